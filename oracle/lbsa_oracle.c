@@ -1,0 +1,444 @@
+/*
+ * lbsa_oracle.c -- plain, slow, obviously-correct CPU oracle for
+ * load-balanced paged decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file; only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no code, header, table or
+ * helper with the HIP library: every number format below is decoded from its
+ * own definition here.
+ *
+ * Sources (the method is described on three web pages; cited by title and
+ * section):
+ *   [vLLM post]   "Tencent Hunyuan HPC-Ops in vLLM" (news.ainew.jp, English
+ *                 text), section "The solution: a per-step, load-balanced
+ *                 decode scheduler", bullets "Assign" and "Compute and
+ *                 combine".
+ *   [SGLang post] "HPC-Ops x SGLang" (Chinese), sections
+ *                 "Attention: load balancing of variable-length decode" and
+ *                 "Scheduling around live KV work".
+ *
+ * Readings taken where the pages are silent (each is also listed with its
+ * reason in the design notes of the repository):
+ *   R1  budget/spill: K = min(P, max(1, floor(T/F))) active bins; the first
+ *       T mod K bins are filled to ceil(T/K) tiles, the rest to floor(T/K),
+ *       in traversal order (fill-to-budget-then-spill with bin sizes that
+ *       differ by at most one tile).
+ *   R2  minimum-work floor F is a parameter (library default 2 tiles).
+ *   R3  "heads" in the tile sum are KV heads; one task covers the whole GQA
+ *       group of one KV head; query head hq reads KV head hq / (Hq/Hkv).
+ *   R5  n_b = ceil(L_b / 64); tokens >= L_b are masked.
+ *   R6  the per-bin terminator is represented as CSR offsets.
+ *   R7  partials are normalised O (per query head, per dim) plus the
+ *       natural-log LSE.
+ *   R9  fp8 is OCP E4M3FN (bias 7, max 448, S.1111.111 is NaN, no inf).
+ *   R10 K/V scales are per token per KV head (fp32), Q scales per request per
+ *       query head; scale arrays are laid out [page][kv_head][slot].
+ *   R11 L_b = 0 is allowed: no tiles, no chunks, output row 0, LSE -inf.
+ *   R12 K/V caches are token-major [page][slot][kv_head][dim].
+ *
+ * Floating point is fp64 throughout; integers in the assign are int64.
+ * Parity of every function here is pinned in tests/ against values that do
+ * not come from this file (library routines, closed forms, brute force and
+ * hand-derived examples).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_TILE 64
+
+/* ------------------------------------------------------------------------ */
+/* Number formats, each from its definition.                                 */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+double oracle_bf16_value(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 7) & 0xFF;
+    int m = bits & 0x7F;
+    double mag;
+    if (e == 0xFF)
+        mag = (m == 0) ? INFINITY : NAN;
+    else if (e == 0)
+        mag = ldexp((double)m / 128.0, -126);           /* subnormal */
+    else
+        mag = ldexp(1.0 + (double)m / 128.0, e - 127);  /* normal */
+    return sign ? -mag : mag;
+}
+
+/* OCP FP8 E4M3FN: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits,
+ * no infinities, exponent=1111 with fraction=111 is NaN, max finite 448. */
+double oracle_e4m3_value(uint8_t bits)
+{
+    int sign = (bits >> 7) & 1;
+    int e = (bits >> 3) & 0xF;
+    int m = bits & 0x7;
+    double mag;
+    if (e == 0xF && m == 0x7)
+        mag = NAN;
+    else if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);              /* subnormal */
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);     /* normal */
+    return sign ? -mag : mag;
+}
+
+void oracle_bf16_values(const uint16_t* bits, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_value(bits[i]);
+}
+
+void oracle_e4m3_values(const uint8_t* bits, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_value(bits[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Assign: the task-map builder.                                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Header words (int32), shared layout with what the GPU map is compared on:
+ *   0 T       total tiles over all (kv_head, request) segments
+ *   1 K       active bins
+ *   2 q       floor(T/K)
+ *   3 r       T mod K
+ *   4 Ndesc   descriptors emitted
+ *   5 P       bins (= persistent workgroups)
+ *   6 F       minimum-work floor (tiles)
+ *   7 B       batch
+ *   8 Hq      query heads
+ *   9 Hkv     KV heads
+ *  10 error   0 ok, 1 = some L_b < 0 or L_b > max_pages*64 (map is empty)
+ *  11 N       tiles per KV head = sum_b n_b
+ *  12 max_pages
+ *  13 page_size (64)
+ *  14,15 zero
+ *
+ * Descriptors are (kv_head, request, tile_begin, tile_end) with tile indices
+ * local to the request.  Steps follow the pages' order:
+ *   1. slice each live KV sequence into 64-token tiles;
+ *   2. sum the tile counts over all KV heads and requests;
+ *   3. derive the per-bin budget from total tiles / bins (reading R1, R2);
+ *   4. walk the tiles head-major, batch-minor, filling the current bin up to
+ *      its budget and then spilling into the next bin; each maximal run of
+ *      tiles of one (kv_head, request) inside one bin is one descriptor
+ *      ("one or more consecutive KV tiles");
+ *   5. count the chunks of each (kv_head, request) for the combine.
+ *
+ * Returns 0, or -1 if an output capacity is too small / arguments invalid.
+ */
+int oracle_assign(const int32_t* seqlens, int32_t B, int32_t Hq, int32_t Hkv,
+                  int32_t P, int32_t F, int32_t max_pages,
+                  int32_t* header, int32_t* bin_desc_begin,
+                  int32_t* desc, int64_t desc_cap,
+                  int32_t* seg_first_desc, int32_t* seg_num_chunks)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || P <= 0 || F <= 0 || max_pages <= 0)
+        return -1;
+    if (Hq % Hkv != 0) return -1;
+
+    int error = 0;
+    for (int32_t b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || (int64_t)seqlens[b] > (int64_t)max_pages * OR_TILE)
+            error = 1;
+
+    /* Step 1: tiles per request. */
+    int64_t* n = (int64_t*)calloc((size_t)B, sizeof(int64_t));
+    int64_t N = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        n[b] = error ? 0 : ((int64_t)seqlens[b] + OR_TILE - 1) / OR_TILE;
+        N += n[b];
+    }
+    /* Step 2: total over all KV heads. */
+    int64_t T = (int64_t)Hkv * N;
+
+    /* Step 3: budget. */
+    int64_t K = 0, q = 0, r = 0;
+    if (T > 0) {
+        int64_t by_floor = T / F;
+        if (by_floor < 1) by_floor = 1;
+        K = by_floor < P ? by_floor : P;
+        q = T / K;
+        r = T % K;
+    }
+
+    /* Step 4: walk tiles head-major, batch-minor; fill and spill. */
+    for (int32_t j = 0; j <= P; ++j) bin_desc_begin[j] = -1;
+    int64_t nd = 0;
+    int64_t bin = 0, fill = 0;
+    int open = 0;  /* is descriptor nd-1 still accepting tiles? */
+    for (int32_t h = 0; h < Hkv; ++h) {
+        for (int32_t b = 0; b < B; ++b) {
+            for (int64_t t = 0; t < n[b]; ++t) {
+                if (fill == 0) bin_desc_begin[bin] = (int32_t)nd;
+                int extend = open && desc[4 * (nd - 1) + 0] == h &&
+                             desc[4 * (nd - 1) + 1] == b &&
+                             desc[4 * (nd - 1) + 3] == t;
+                if (extend) {
+                    desc[4 * (nd - 1) + 3] = (int32_t)(t + 1);
+                } else {
+                    if (nd >= desc_cap) { free(n); return -1; }
+                    desc[4 * nd + 0] = h;
+                    desc[4 * nd + 1] = b;
+                    desc[4 * nd + 2] = (int32_t)t;
+                    desc[4 * nd + 3] = (int32_t)(t + 1);
+                    ++nd;
+                    open = 1;
+                }
+                int64_t budget = (bin < r) ? q + 1 : q;
+                if (++fill == budget) {  /* bin full: spill to the next */
+                    ++bin;
+                    fill = 0;
+                    open = 0;
+                }
+            }
+            open = 0;  /* a new request never extends the previous one */
+        }
+    }
+    for (int64_t j = K; j <= P; ++j) bin_desc_begin[j] = (int32_t)nd;
+
+    /* Step 5: chunk count and first chunk per (kv_head, request). */
+    for (int64_t s = 0; s < (int64_t)Hkv * B; ++s) seg_num_chunks[s] = 0;
+    for (int64_t d = 0; d < nd; ++d)
+        seg_num_chunks[(int64_t)desc[4 * d + 0] * B + desc[4 * d + 1]] += 1;
+    int64_t acc = 0;
+    for (int64_t s = 0; s < (int64_t)Hkv * B; ++s) {
+        seg_first_desc[s] = (int32_t)acc;
+        acc += seg_num_chunks[s];
+    }
+
+    memset(header, 0, 16 * sizeof(int32_t));
+    header[0] = (int32_t)T;
+    header[1] = (int32_t)K;
+    header[2] = (int32_t)q;
+    header[3] = (int32_t)r;
+    header[4] = (int32_t)nd;
+    header[5] = P;
+    header[6] = F;
+    header[7] = B;
+    header[8] = Hq;
+    header[9] = Hkv;
+    header[10] = error;
+    header[11] = (int32_t)N;
+    header[12] = max_pages;
+    header[13] = OR_TILE;
+    free(n);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention: the plain softmax definition over gathered paged K/V.          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const void* q;          /* [B][Hq][D]  bf16 bits (kv_dtype 0) or e4m3 bits (1) */
+    const float* q_scale;   /* [B][Hq]     e4m3 only */
+    const void* k_cache;    /* [pages][64][Hkv][D] */
+    const void* v_cache;
+    const float* k_scale;   /* [pages][Hkv][64]    e4m3 only */
+    const float* v_scale;
+    const int32_t* page_table; /* [B][max_pages] */
+    const int32_t* seqlens;    /* [B] */
+    int32_t kv_dtype;       /* 0 = bf16, 1 = e4m3fn */
+    int32_t B, Hq, Hkv, D, max_pages, num_pages;
+    double softmax_scale;
+} oracle_inputs;
+
+static double q_elem(const oracle_inputs* in, int64_t b, int64_t hq, int64_t d)
+{
+    int64_t i = (b * in->Hq + hq) * in->D + d;
+    if (in->kv_dtype == 0) return oracle_bf16_value(((const uint16_t*)in->q)[i]);
+    return oracle_e4m3_value(((const uint8_t*)in->q)[i]) *
+           (double)in->q_scale[b * in->Hq + hq];
+}
+
+static double kv_elem(const oracle_inputs* in, const void* cache, const float* scale,
+                      int64_t page, int64_t slot, int64_t h, int64_t d)
+{
+    int64_t i = ((page * OR_TILE + slot) * in->Hkv + h) * in->D + d;
+    if (in->kv_dtype == 0) return oracle_bf16_value(((const uint16_t*)cache)[i]);
+    return oracle_e4m3_value(((const uint8_t*)cache)[i]) *
+           (double)scale[(page * in->Hkv + h) * OR_TILE + slot];
+}
+
+/* Attention of query head hq of request b over its tokens [tok0, tok1).
+ * out[D] = sum_t w_t v_t / sum_t w_t with w_t = exp(s_t - max s),
+ * s_t = softmax_scale * <q, k_t>; *lse = max s + ln sum_t w_t.
+ * An empty range gives out = 0 and lse = -inf.  Returns -1 on a bad page. */
+static int attend_range(const oracle_inputs* in, int64_t b, int64_t hq,
+                        int64_t tok0, int64_t tok1, double* out, double* lse,
+                        double* qv, double* s)
+{
+    const int64_t D = in->D;
+    const int64_t h = hq / (in->Hq / in->Hkv);
+    for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+    if (tok1 <= tok0) { *lse = -INFINITY; return 0; }
+    for (int64_t d = 0; d < D; ++d) qv[d] = q_elem(in, b, hq, d);
+
+    double m = -INFINITY;
+    for (int64_t t = tok0; t < tok1; ++t) {
+        int64_t page = in->page_table[b * in->max_pages + t / OR_TILE];
+        if (page < 0 || page >= in->num_pages) return -1;
+        int64_t slot = t % OR_TILE;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            dot += qv[d] * kv_elem(in, in->k_cache, in->k_scale, page, slot, h, d);
+        s[t - tok0] = in->softmax_scale * dot;
+        if (s[t - tok0] > m) m = s[t - tok0];
+    }
+    double wsum = 0.0;
+    for (int64_t t = tok0; t < tok1; ++t) {
+        int64_t page = in->page_table[b * in->max_pages + t / OR_TILE];
+        int64_t slot = t % OR_TILE;
+        double w = exp(s[t - tok0] - m);
+        wsum += w;
+        for (int64_t d = 0; d < D; ++d)
+            out[d] += w * kv_elem(in, in->v_cache, in->v_scale, page, slot, h, d);
+    }
+    for (int64_t d = 0; d < D; ++d) out[d] /= wsum;
+    *lse = m + log(wsum);
+    return 0;
+}
+
+static int64_t max_len(const oracle_inputs* in)
+{
+    int64_t mx = 1;
+    for (int32_t b = 0; b < in->B; ++b)
+        if (in->seqlens[b] > mx) mx = in->seqlens[b];
+    return mx;
+}
+
+/* Full attention for every (request, query head): out [B][Hq][D], lse [B][Hq].
+ * Requests with L_b = 0 give zeros and -inf. */
+int oracle_attention(const oracle_inputs* in, double* out, double* lse, int nthreads)
+{
+    const int64_t rows = (int64_t)in->B * in->Hq;
+    const int64_t D = in->D;
+    const int64_t L = max_len(in);
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double* qv = (double*)malloc((size_t)D * sizeof(double));
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t row = 0; row < rows; ++row) {
+            int64_t b = row / in->Hq, hq = row % in->Hq;
+            if (attend_range(in, b, hq, 0, in->seqlens[b], out + row * D, lse + row, qv, s))
+                bad = 1;
+        }
+        free(qv);
+        free(s);
+    }
+    (void)nthreads;
+    return bad ? -1 : 0;
+}
+
+/* Attention restricted to a subset of rows (request, query head) given as
+ * pairs; used to sample outputs of very large batches. */
+int oracle_attention_rows(const oracle_inputs* in, const int32_t* rows_bh, int64_t nrows,
+                          double* out, double* lse, int nthreads)
+{
+    const int64_t D = in->D;
+    const int64_t L = max_len(in);
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double* qv = (double*)malloc((size_t)D * sizeof(double));
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t b = rows_bh[2 * i], hq = rows_bh[2 * i + 1];
+            if (attend_range(in, b, hq, 0, in->seqlens[b], out + i * D, lse + i, qv, s))
+                bad = 1;
+        }
+        free(qv);
+        free(s);
+    }
+    (void)nthreads;
+    return bad ? -1 : 0;
+}
+
+/* Per-descriptor partials: descriptor i = (h, b, t0, t1) covers tokens
+ * [64 t0, min(64 t1, L_b)) of request b for the G query heads of KV head h.
+ * part_o [n][G][D] is the normalised partial output, part_lse [n][G] its
+ * natural-log LSE (reading R7). */
+int oracle_partials(const oracle_inputs* in, const int32_t* desc, int64_t ndesc,
+                    double* part_o, double* part_lse, int nthreads)
+{
+    const int64_t D = in->D;
+    const int64_t G = in->Hq / in->Hkv;
+    const int64_t L = max_len(in);
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double* qv = (double*)malloc((size_t)D * sizeof(double));
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t i = 0; i < ndesc * G; ++i) {
+            int64_t di = i / G, g = i % G;
+            int64_t h = desc[4 * di], b = desc[4 * di + 1];
+            int64_t tok0 = (int64_t)desc[4 * di + 2] * OR_TILE;
+            int64_t tok1 = (int64_t)desc[4 * di + 3] * OR_TILE;
+            if (tok1 > in->seqlens[b]) tok1 = in->seqlens[b];
+            if (attend_range(in, b, h * G + g, tok0, tok1, part_o + i * D, part_lse + i, qv, s))
+                bad = 1;
+        }
+        free(qv);
+        free(s);
+    }
+    (void)nthreads;
+    return bad ? -1 : 0;
+}
+
+/* Combine: merge n partials (o_c [width], lse_c) of one row under the global
+ * softmax normalisation: M = max lse_c, w_c = exp(lse_c - M),
+ * out = sum w_c o_c / sum w_c, lse = M + ln sum w_c.  n = 0 (or all lse_c
+ * -inf) gives zeros and -inf. */
+void oracle_merge(const double* o, const double* lse, int64_t n, int64_t width,
+                  double* out, double* out_lse)
+{
+    double M = -INFINITY;
+    for (int64_t c = 0; c < n; ++c)
+        if (lse[c] > M) M = lse[c];
+    for (int64_t d = 0; d < width; ++d) out[d] = 0.0;
+    if (M == -INFINITY) { *out_lse = -INFINITY; return; }
+    double wsum = 0.0;
+    for (int64_t c = 0; c < n; ++c) {
+        double w = exp(lse[c] - M);
+        wsum += w;
+        for (int64_t d = 0; d < width; ++d) out[d] += w * o[c * width + d];
+    }
+    for (int64_t d = 0; d < width; ++d) out[d] /= wsum;
+    *out_lse = M + log(wsum);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

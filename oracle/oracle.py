@@ -1,0 +1,230 @@
+"""ctypes/numpy front end of the plain-C CPU oracle (``lbsa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  It shares no code with
+the HIP library and never imports it.
+
+Inputs are plain numpy arrays (or CPU torch tensors, converted here) holding the
+raw bit patterns of bf16 / e4m3 values, exactly as the seeded generator made
+them.  The method it follows is described in the HPC-Ops vLLM integration post,
+section "The solution: a per-step, load-balanced decode scheduler" (bullets
+"Assign" and "Compute and combine").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liblbsa_oracle.so")
+_lib = None
+
+HEADER_FIELDS = ("T", "K", "q", "r", "Ndesc", "P", "F", "B", "Hq", "Hkv",
+                 "error", "N", "max_pages", "page_size")
+TILE = 64
+
+
+class _Inputs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("seqlens", ctypes.c_void_p),
+        ("kv_dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_double),
+    ]
+
+
+def lib():
+    """Load (building if needed) the oracle shared library."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(os.path.join(_HERE, "lbsa_oracle.c"))):
+            from oracle import build as _b  # noqa: PLC0415
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        L.oracle_assign.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, i64, P, P]
+        L.oracle_assign.restype = ctypes.c_int
+        L.oracle_attention.argtypes = [ctypes.POINTER(_Inputs), P, P, ctypes.c_int]
+        L.oracle_attention.restype = ctypes.c_int
+        L.oracle_attention_rows.argtypes = [ctypes.POINTER(_Inputs), P, i64, P, P, ctypes.c_int]
+        L.oracle_attention_rows.restype = ctypes.c_int
+        L.oracle_partials.argtypes = [ctypes.POINTER(_Inputs), P, i64, P, P, ctypes.c_int]
+        L.oracle_partials.restype = ctypes.c_int
+        L.oracle_merge.argtypes = [P, P, i64, i64, P, P]
+        L.oracle_merge.restype = None
+        L.oracle_bf16_values.argtypes = [P, i64, P]
+        L.oracle_e4m3_values.argtypes = [P, i64, P]
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _np(x, dtype=None):
+    """CPU, C-contiguous numpy view of a numpy array or torch tensor."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        import torch  # noqa: PLC0415
+        x = x.detach()
+        if x.device.type != "cpu":
+            x = x.cpu()
+        if x.dtype == torch.bfloat16:
+            x = x.view(torch.int16)
+        elif x.dtype in (torch.float8_e4m3fn,):
+            x = x.view(torch.uint8)
+        x = x.contiguous().numpy()
+    x = np.ascontiguousarray(x)
+    if dtype is not None:
+        x = x.view(dtype) if x.dtype.itemsize == np.dtype(dtype).itemsize else x.astype(dtype)
+    return x
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def bf16_values(bits) -> np.ndarray:
+    """float64 values of bf16 bit patterns (uint16/int16 array)."""
+    a = _np(bits, np.uint16).ravel()
+    out = np.empty(a.size, np.float64)
+    lib().oracle_bf16_values(_ptr(a), a.size, _ptr(out))
+    return out.reshape(np.shape(bits))
+
+
+def e4m3_values(bits) -> np.ndarray:
+    """float64 values of OCP E4M3FN bit patterns (uint8 array)."""
+    a = _np(bits, np.uint8).ravel()
+    out = np.empty(a.size, np.float64)
+    lib().oracle_e4m3_values(_ptr(a), a.size, _ptr(out))
+    return out.reshape(np.shape(bits))
+
+
+# ---------------------------------------------------------------------------
+# assign
+# ---------------------------------------------------------------------------
+
+def assign(seqlens, num_heads: int, num_kv_heads: int, P: int, F: int, max_pages: int) -> dict:
+    """Reference task map.
+
+    Returns a dict with ``header`` int32[16], ``bin_desc_begin`` int32[P+1],
+    ``desc`` int32[Ndesc, 4] (kv_head, request, tile_begin, tile_end),
+    ``seg_first_desc`` / ``seg_num_chunks`` int32[Hkv*B] (index h*B + b) and the
+    header fields by name.
+    """
+    sl = _np(seqlens, None).astype(np.int32).ravel()
+    B = sl.size
+    cap = num_kv_heads * B + P
+    header = np.zeros(16, np.int32)
+    bdb = np.zeros(P + 1, np.int32)
+    desc = np.zeros((cap, 4), np.int32)
+    sfd = np.zeros(num_kv_heads * B, np.int32)
+    snc = np.zeros(num_kv_heads * B, np.int32)
+    rc = lib().oracle_assign(_ptr(sl), B, num_heads, num_kv_heads, P, F, max_pages,
+                             _ptr(header), _ptr(bdb), _ptr(desc), cap, _ptr(sfd), _ptr(snc))
+    if rc != 0:
+        raise ValueError("oracle_assign: invalid arguments")
+    nd = int(header[4])
+    out = {"header": header, "bin_desc_begin": bdb, "desc": desc[:nd].copy(),
+           "seg_first_desc": sfd, "seg_num_chunks": snc}
+    for i, name in enumerate(HEADER_FIELDS):
+        out[name] = int(header[i])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+class _Batch:
+    """Keeps the numpy buffers alive while the C struct points at them."""
+
+    def __init__(self, batch: dict):
+        self.kv_dtype = 0 if batch["kv_dtype"] == "bf16" else 1
+        if self.kv_dtype == 0:
+            self.q = _np(batch["q"], np.uint16)
+            self.k = _np(batch["k_cache"], np.uint16)
+            self.v = _np(batch["v_cache"], np.uint16)
+            self.qs = self.ks = self.vs = None
+        else:
+            self.q = _np(batch["q"], np.uint8)
+            self.k = _np(batch["k_cache"], np.uint8)
+            self.v = _np(batch["v_cache"], np.uint8)
+            self.qs = _np(batch["q_scale"], np.float32)
+            self.ks = _np(batch["k_scale"], np.float32)
+            self.vs = _np(batch["v_scale"], np.float32)
+        self.pt = _np(batch["page_table"], None).astype(np.int32)
+        self.sl = _np(batch["seqlens"], None).astype(np.int32)
+        B, Hq, D = self.q.shape
+        num_pages, page, Hkv, D2 = self.k.shape
+        assert page == TILE and D2 == D
+        self.shape = (B, Hq, Hkv, D)
+        self.s = _Inputs(
+            _ptr(self.q), _ptr(self.qs), _ptr(self.k), _ptr(self.v), _ptr(self.ks), _ptr(self.vs),
+            _ptr(self.pt), _ptr(self.sl), self.kv_dtype, B, Hq, Hkv, D,
+            self.pt.shape[1], num_pages, float(batch["softmax_scale"]))
+
+
+def attention(batch: dict, nthreads: int = 0):
+    """fp64 attention of every (request, query head): returns (out [B,Hq,D], lse [B,Hq])."""
+    bb = _Batch(batch)
+    B, Hq, Hkv, D = bb.shape
+    out = np.zeros((B, Hq, D), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    if lib().oracle_attention(ctypes.byref(bb.s), _ptr(out), _ptr(lse), nthreads) != 0:
+        raise ValueError("oracle_attention: page_table entry out of range")
+    return out, lse
+
+
+def attention_rows(batch: dict, rows, nthreads: int = 0):
+    """fp64 attention for selected (request, query head) rows: rows int[n, 2]."""
+    bb = _Batch(batch)
+    D = bb.shape[3]
+    rows = np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 2))
+    out = np.zeros((rows.shape[0], D), np.float64)
+    lse = np.zeros(rows.shape[0], np.float64)
+    if lib().oracle_attention_rows(ctypes.byref(bb.s), _ptr(rows), rows.shape[0],
+                                   _ptr(out), _ptr(lse), nthreads) != 0:
+        raise ValueError("oracle_attention_rows: page_table entry out of range")
+    return out, lse
+
+
+def partials(batch: dict, desc, nthreads: int = 0):
+    """fp64 partials of descriptors desc int[n, 4]: (part_o [n,G,D], part_lse [n,G])."""
+    bb = _Batch(batch)
+    B, Hq, Hkv, D = bb.shape
+    G = Hq // Hkv
+    desc = np.ascontiguousarray(np.asarray(desc, np.int32).reshape(-1, 4))
+    n = desc.shape[0]
+    po = np.zeros((n, G, D), np.float64)
+    pl = np.zeros((n, G), np.float64)
+    if lib().oracle_partials(ctypes.byref(bb.s), _ptr(desc), n, _ptr(po), _ptr(pl), nthreads) != 0:
+        raise ValueError("oracle_partials: page_table entry out of range")
+    return po, pl
+
+
+def merge(part_o, part_lse):
+    """LSE merge of n partials of one row: part_o [n, width], part_lse [n]."""
+    o = np.ascontiguousarray(np.asarray(part_o, np.float64))
+    n = o.shape[0]
+    o = o.reshape(n, int(np.prod(o.shape[1:])))
+    l = np.ascontiguousarray(np.asarray(part_lse, np.float64).reshape(n))
+    out = np.zeros(o.shape[1], np.float64)
+    out_lse = np.zeros(1, np.float64)
+    lib().oracle_merge(_ptr(o), _ptr(l), n, o.shape[1], _ptr(out), _ptr(out_lse))
+    return out, float(out_lse[0])
