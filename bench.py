@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch already resident
+in HBM: assign (task map) + persistent split + combine.  Before every timed
+step a 512 MiB buffer is streamed through so neither L2 nor the 256 MB Infinity
+Cache still holds K/V from the previous step; HIP events on the launch stream bracket
+each kernel, the flush stays outside them.  The default flush reads the buffer
+(a reduction), so the caches hold clean lines and no write-back competes with
+the timed kernels.
+
+Prints ONE JSON line.  value = achieved HBM GB/s of a step (algorithmic bytes /
+mean step time); the line also carries us_per_step, the per-kernel times, the
+split kernel's roofline, the static split-KV comparison on the skewed batch,
+and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 512 << 20
+SPLIT_SRC = os.path.join(ROOT, "load_balanced_split_assign_amd", "csrc", "lbsa_attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
+
+
+def alg_bytes(seqlens, Hq, Hkv, D, kv_dtype):
+    """Bytes the method must move: live K/V (+ scales), Q (+ scale), bf16 out,
+    page-table entries and lengths.  Partials are overhead, reported apart."""
+    e_kv, s_kv, e_q, s_q = (2, 0, 2, 0) if kv_dtype == "bf16" else (1, 8, 1, 4)
+    B = len(seqlens)
+    n_tiles = sum((L + 63) // 64 for L in seqlens)
+    kv = sum(seqlens) * Hkv * (2 * D * e_kv + s_kv)
+    q = B * Hq * (D * e_q + s_q)
+    out = B * Hq * D * 2
+    meta = 4 * n_tiles + 4 * B
+    return {"kv": kv, "q": q, "out": out, "meta": meta, "layer": kv + q + out + meta, "split": kv + q + meta}
+
+
+def summarize(xs):
+    xs = sorted(xs)
+    return {"mean": statistics.fmean(xs), "median": statistics.median(xs), "min": xs[0],
+            "p90": xs[min(len(xs) - 1, int(math.ceil(0.9 * len(xs))) - 1)]}
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+class Path:
+    """Preallocated buffers for one batch; step() enqueues assign+split+combine."""
+
+    def __init__(self, batch, P, F=0):
+        import torch
+
+        from load_balanced_split_assign_amd import lbsa
+        self.lbsa, self.b, self.P, self.F = lbsa, batch, P, F
+        B, Hq, Hkv = batch["B"], batch["num_heads"], batch["num_kv_heads"]
+        dev = batch["q"].device
+        self.tm = torch.empty(lbsa.task_map_bytes(B, Hkv, P), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(lbsa.workspace_bytes(B, Hq, Hkv, P), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+
+    def assign(self):
+        b = self.b
+        self.lbsa.plan(b["seqlens"], b["num_heads"], b["num_kv_heads"], b["max_pages"], self.P, self.F,
+                       task_map=self.tm)
+
+    def split(self):
+        b = self.b
+        self.lbsa.decode_split(b["q"], b["k_cache"], b["v_cache"], b["page_table"], self.tm, self.P,
+                               b["softmax_scale"], q_scale=b["q_scale"], k_scale=b["k_scale"],
+                               v_scale=b["v_scale"], workspace=self.ws)
+
+    def combine(self):
+        b = self.b
+        self.lbsa.decode_combine(b["B"], b["num_heads"], b["num_kv_heads"], self.P, self.tm, self.ws,
+                                 out=self.out)
+
+
+def make_flush(mode):
+    """Evicts K/V of the previous step from L2 and the Infinity Cache.  'read'
+    streams a 512 MiB buffer through a reduction (the caches are left holding
+    clean lines, so the next kernel pays no write-back); 'write' rewrites it;
+    'none' leaves the caches warm."""
+    import torch
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    if mode == "read":
+        return lambda i: buf.sum()
+    if mode == "write":
+        return lambda i: buf.fill_(float(i & 7))
+    return lambda i: None
+
+
+def time_steps(path, steps, warmup, flush):
+    """Per-step event times (us) of assign, split, combine and the whole step."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(warmup):
+        flush(i)
+        path.assign(); path.split(); path.combine()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush(i)
+        e = ev[i]
+        e[0].record(stream)
+        path.assign()
+        e[1].record(stream)
+        path.split()
+        e[2].record(stream)
+        path.combine()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    us = lambda a, b: [1000.0 * ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)]  # noqa: E731
+    return {"assign": us(0, 1), "split": us(1, 2), "combine": us(2, 3), "layer": us(1, 3), "step": us(0, 3)}
+
+
+def time_static(batch, S, steps, warmup, flush):
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    B, Hq, Hkv = batch["B"], batch["num_heads"], batch["num_kv_heads"]
+    ws = torch.empty(lbsa.static_workspace_bytes(B, Hq, Hkv, S), dtype=torch.uint8, device=batch["q"].device)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=batch["q"].device)
+
+    def run():
+        lbsa.decode_static(batch["q"], batch["k_cache"], batch["v_cache"], batch["page_table"], batch["seqlens"],
+                           S, batch["softmax_scale"], q_scale=batch["q_scale"], k_scale=batch["k_scale"],
+                           v_scale=batch["v_scale"], workspace=ws, out=out)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        flush(i)
+        run()
+    times = []
+    for i in range(steps):
+        flush(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(1000.0 * a.elapsed_time(b))
+    return summarize(times)
+
+
+def gpu_batch(name, tail="normal"):
+    import torch
+
+    from load_balanced_split_assign_amd import workload as wl
+    b = wl.make_batch(name, tail=tail, device="cuda:0")
+    torch.cuda.synchronize()
+    return b
+
+
+def cpu_baseline(name, budget_s):
+    """The CPU oracle (as it stands) timed on this host: assign + fp64 attention
+    over a bounded sample of the workload's (request, query head) rows."""
+    import numpy as np
+
+    from load_balanced_split_assign_amd import workload as wl
+    from oracle import oracle
+    b = wl.make_batch(name, tail="normal", device="cpu")
+    B, Hq, Hkv = b["B"], b["num_heads"], b["num_kv_heads"]
+    sl = [int(x) for x in b["seqlens"]]
+    threads = oracle.num_threads()
+    # rows are taken in (request, head) order until the estimated work fits the budget,
+    # using a rate measured on one row of the first request
+    t0 = time.perf_counter()
+    oracle.attention_rows(b, np.array([[0, 0]], np.int32))
+    per_token_s = max(1e-9, (time.perf_counter() - t0) / max(1, sl[0]))
+    rows, tokens = [], 0
+    for r in range(B * Hq):
+        req = r // Hq
+        if rows and (tokens + sl[req]) * per_token_s / threads > budget_s:
+            break
+        rows.append((req, r % Hq))
+        tokens += sl[req]
+    rows = np.array(rows, np.int32)
+    t0 = time.perf_counter()
+    oracle.attention_rows(b, rows)
+    t_attn = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.assign(b["seqlens"], Hq, Hkv, 1024, 2, b["max_pages"])
+    t_assign = time.perf_counter() - t0
+    full = len(rows) == B * Hq
+    # each row is charged its own Q and output plus 1/G of its segment's K/V bytes
+    G = Hq // Hkv
+    e_kv, s_kv, e_q, s_q = (2, 0, 2, 0) if b["kv_dtype"] == "bf16" else (1, 8, 1, 4)
+    row_tokens = sum(sl[r] for r, _ in rows)
+    sample_bytes = row_tokens * (2 * 128 * e_kv + s_kv) / G + len(rows) * (128 * e_q + s_q + 128 * 2)
+    return {"value": round(sample_bytes / (t_attn + t_assign) / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": (f"{'all' if full else len(rows)} of {B * Hq} (request, query head) rows of '{name}'"
+                       f" ({row_tokens} token-rows), fp64 attention + assign"),
+            "attn_s": round(t_attn, 3), "assign_us": round(1e6 * t_assign, 1)}
+
+
+def traffic_from_profile():
+    """HBM bytes per split launch from committed PMC counters, if they were taken
+    on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("source_sha256") != source_sha(SPLIT_SRC):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="tp8_share")
+    ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0 = CUs x occupancy)")
+    ap.add_argument("--no-static", action="store_true", help="skip the static split-KV comparison")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
+                    help="cache eviction before each timed step")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (bounded sample)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path needs no collectives; "
+              "KV-head or request sharding across GPUs runs independent copies of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    from load_balanced_split_assign_amd import workload as wl
+
+    name = args.workload
+    w = wl.WORKLOADS[name]
+    batch = gpu_batch(name)
+    P = args.workgroups or w.num_workgroups or lbsa.default_workgroups(0, w.kv_dtype)
+    sl = [int(x) for x in batch["seqlens"].cpu()]
+    ab = alg_bytes(sl, batch["num_heads"], batch["num_kv_heads"], 128, w.kv_dtype)
+    flush = make_flush(args.flush)
+
+    path = Path(batch, P)
+    torch.cuda.synchronize()
+    t = time_steps(path, args.steps, args.warmup, flush)
+    m = lbsa.read_task_map(path.tm, batch["B"], batch["num_kv_heads"], P)
+    st = {k: summarize(v) for k, v in t.items()}
+    step_us, split_us = st["step"]["mean"], st["split"]["mean"]
+    value = ab["layer"] / (step_us * 1e-6) / 1e9
+    split_gbs = ab["split"] / (split_us * 1e-6) / 1e9
+    traffic = traffic_from_profile()
+
+    rec = {
+        "metric": "decode-attn µs/step + achieved HBM GB/s (% of peak), mixed-length paged KV batch",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1000.0, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 (bf16 MFMA)",
+        "data": "synthetic",
+        "config": {"workload": name, "desc": w.note, "batch": batch["B"], "num_heads": batch["num_heads"],
+                   "num_kv_heads": batch["num_kv_heads"], "head_dim": 128, "page_size": 64,
+                   "kv_dtype": w.kv_dtype, "seed": w.seed, "live_tokens": sum(sl), "P": P, "T": m["T"],
+                   "K": m["K"], "Ndesc": m["Ndesc"]},
+        "us_per_step": round(step_us, 3),
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "times_us": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in st.items()},
+        "alg_bytes": ab,
+        "partial_bytes": 2 * m["Ndesc"] * 8 * (128 + 1) * 4,
+        "roofline": {"kernel": "split_kernel", "bound": "hbm", "achieved": round(split_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": ab["split"],
+                     "avg_launch_us": round(split_us, 3)},
+    }
+
+    if not args.no_static:
+        sk = gpu_batch("skewed")
+        Pk = lbsa.default_workgroups(0, "bf16")
+        dyn = summarize(time_steps(Path(sk, Pk), 20, 3, flush)["layer"])
+        heur = max(1, -(-Pk // (sk["B"] * sk["num_kv_heads"])))
+        sweep = {S: time_static(sk, S, 10, 2, flush)["mean"] for S in (1, 2, 4, 8, 16, 32, 64)}
+        heur_t = sweep.get(heur) or time_static(sk, heur, 10, 2, flush)["mean"]
+        best_S = min(sweep, key=sweep.get)
+        rec["static_baseline"] = {
+            "workload": "skewed", "P": Pk, "dynamic_layer_us": round(dyn["mean"], 2),
+            "static_heuristic_S": heur, "static_heuristic_us": round(heur_t, 2),
+            "static_best_S": best_S, "static_best_us": round(sweep[best_S], 2),
+            "static_sweep_us": {str(k): round(v, 2) for k, v in sweep.items()},
+            "speedup_vs_static_heuristic": round(heur_t / dyn["mean"], 3),
+            "speedup_vs_static_best": round(sweep[best_S] / dyn["mean"], 3)}
+        del sk
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(name, args.cpu_budget)
+
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

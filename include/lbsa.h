@@ -1,0 +1,211 @@
+/*
+ * lbsa.h -- C ABI of the MI355X (gfx950) load-balanced paged decode attention
+ * library (liblbsa.so).
+ *
+ * The method (HPC-Ops attention backend, described in the HPC-Ops vLLM
+ * integration post, section "The solution: a per-step, load-balanced decode
+ * scheduler", and in the SGLang post, section "Scheduling around live KV
+ * work"):
+ *   1. an assign kernel slices every live KV sequence into 64-token tiles,
+ *      walks them head-major / batch-minor, and fills persistent-workgroup
+ *      bins up to a budget (total tiles / workgroups, with a minimum-work
+ *      floor), spilling into the next bin -- the task map, built once per
+ *      decode step from device-side lengths and reused by every layer;
+ *   2. a persistent split kernel: each workgroup drains its bin, computing
+ *      attention over each descriptor's consecutive tiles and writing a
+ *      partial output with its log-sum-exp;
+ *   3. a combine kernel reads the chunk count of each (request, head) and
+ *      merges the partials under the global softmax normalisation into bf16.
+ * A static split-KV kernel (fixed split count per request; the posts' "static
+ * split-KV" comparison point, section "The challenge: mixed-length decode in
+ * every batch") is exported as the scheduling baseline.
+ *
+ * Conventions for every entry point:
+ *   - all pointers named *_d are DEVICE pointers allocated by the caller; the
+ *     library never allocates, frees or synchronises; work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the null stream) and returns at once;
+ *   - argument errors are detected on the host BEFORE anything is enqueued and
+ *     reported as a negative status; nothing is written in that case;
+ *   - data errors only visible on the device (a length outside
+ *     [0, max_pages_per_seq * 64]) are reported in the task-map header word
+ *     LBSA_HDR_ERROR and give an empty map (output rows zero); a page-table
+ *     entry outside [0, num_pages) poisons the affected rows with NaN instead
+ *     of reading out of bounds;
+ *   - supported shapes: head_dim 128, page_size 64, query-group size
+ *     num_heads / num_kv_heads = 8.
+ *
+ * Tensor layouts (row-major, contiguous):
+ *   q           [batch][num_heads][128]          bf16, or e4m3fn with q_scale
+ *   q_scale     [batch][num_heads]               fp32 (fp8 only)
+ *   k/v cache   [num_pages][64][num_kv_heads][128] bf16 or e4m3fn (token-major)
+ *   k/v scale   [num_pages][num_kv_heads][64]    fp32 (fp8 only)
+ *   page_table  [batch][max_pages_per_seq]       int32 physical page ids
+ *   seqlens     [batch]                          int32 live KV lengths
+ *   out         [batch][num_heads][128]          bf16
+ * Query head hq reads KV head hq / (num_heads / num_kv_heads).
+ */
+#ifndef LBSA_H
+#define LBSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define LBSA_OK 0
+#define LBSA_ERR_INVALID_ARGUMENT (-1) /* null pointer, size <= 0, buffer too small, Hq % Hkv != 0 */
+#define LBSA_ERR_UNSUPPORTED (-2)      /* head_dim != 128, page_size != 64, group != 8, too large */
+#define LBSA_ERR_HIP (-3)              /* a HIP runtime call or launch failed */
+
+/* ---- constants ---------------------------------------------------------- */
+#define LBSA_KV_BF16 0
+#define LBSA_KV_FP8_E4M3 1       /* OCP E4M3FN codes with fp32 per-token-per-head scales */
+#define LBSA_PAGE_SIZE 64        /* tokens per page = tokens per tile */
+#define LBSA_HEAD_DIM 128
+#define LBSA_GROUP 8             /* query heads per KV head */
+#define LBSA_DEFAULT_MIN_TILES 2 /* default minimum-work floor, tiles per active bin */
+
+/* Task-map header words (int32), see lbsa_plan. */
+#define LBSA_HDR_T 0        /* total tiles over all (kv_head, request) segments */
+#define LBSA_HDR_K 1        /* active bins = min(P, max(1, floor(T / F))), 0 if T = 0 */
+#define LBSA_HDR_Q 2        /* floor(T / K) */
+#define LBSA_HDR_R 3        /* T mod K: bins [0, R) hold Q + 1 tiles, the rest Q */
+#define LBSA_HDR_NDESC 4    /* descriptors in the map */
+#define LBSA_HDR_P 5        /* bins = persistent workgroups of the split kernel */
+#define LBSA_HDR_F 6        /* minimum-work floor (tiles) */
+#define LBSA_HDR_B 7
+#define LBSA_HDR_HQ 8
+#define LBSA_HDR_HKV 9
+#define LBSA_HDR_ERROR 10   /* 0 ok; 1 = a length outside [0, max_pages * 64] (map empty) */
+#define LBSA_HDR_N 11       /* tiles per KV head = sum_b ceil(L_b / 64) */
+#define LBSA_HDR_MAX_PAGES 12
+#define LBSA_HDR_PAGE_SIZE 13
+#define LBSA_HDR_WORDS 16
+
+/* Byte offsets of the arrays inside a task map (all from the map base). */
+typedef struct {
+    size_t header;          /* int32[16] */
+    size_t bin_desc_begin;  /* int32[P + 1]: bin j owns descriptors [begin[j], begin[j+1]) */
+    size_t desc;            /* int32x4[Hkv*B + P]: (kv_head, request, tile_begin, tile_end),
+                               request-local tile indices; descriptor d writes partial slot d */
+    size_t seg_first_desc;  /* int32[Hkv*B], index h*B + b: first descriptor of the segment */
+    size_t seg_num_chunks;  /* int32[Hkv*B]: descriptors (chunks) of the segment */
+    size_t seqlens;         /* int32[B]: copy of the lengths the map was built from */
+    size_t total;           /* bytes */
+} lbsa_task_map_layout;
+
+/* Byte offsets inside the decode workspace. */
+typedef struct {
+    size_t part_lse;        /* fp32 [Hkv*B + P][8]: natural-log LSE of each partial */
+    size_t part_o;          /* fp32 [Hkv*B + P][8][128]: normalised partial outputs */
+    size_t total;
+} lbsa_workspace_layout;
+
+/* Human-readable name of a status code (static storage). */
+const char* lbsa_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int lbsa_version(void);
+
+/* Default number of persistent workgroups on `device` for `kv_dtype`:
+ * compute units x resident workgroups per CU of the split kernel (occupancy
+ * query), so every bin is resident at once.  Writes *out_P. */
+int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_P);
+
+/* Layout and size of the task map for (batch, num_kv_heads, P). */
+int lbsa_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32_t P,
+                             lbsa_task_map_layout* out);
+int lbsa_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t P, size_t* out_bytes);
+
+/* Layout and size of the split/combine workspace (partials). */
+int lbsa_workspace_layout_get(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t P, lbsa_workspace_layout* out);
+int lbsa_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t P, size_t* out_bytes);
+
+/*
+ * Assign: build the task map on the device (one launch, no host sync).
+ * Source: vLLM post, "The solution: ..." bullet "Assign"; SGLang post,
+ * "Scheduling around live KV work".
+ *   seqlens_d          int32[batch] live KV lengths (device)
+ *   num_workgroups     P >= 1, the split kernel's grid (see lbsa_default_workgroups)
+ *   min_tiles_per_bin  F >= 1, or 0 for LBSA_DEFAULT_MIN_TILES
+ *   task_map_d         caller buffer of >= lbsa_task_map_bytes bytes, 16-byte aligned
+ * Bins: T = Hkv * sum_b ceil(L_b/64) tiles in head-major, batch-minor order;
+ * K = min(P, max(1, floor(T/F))) active bins; the first T mod K bins hold
+ * ceil(T/K) tiles, the rest floor(T/K); each maximal run of one (kv_head,
+ * request) inside a bin is one descriptor.  Limits: (batch + Hkv*batch) <= 16382
+ * (LDS of the single assign workgroup), batch * max_pages_per_seq * Hkv < 2^30.
+ */
+int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+              int32_t page_size, int32_t max_pages_per_seq, int32_t num_workgroups,
+              int32_t min_tiles_per_bin, void* task_map_d, size_t task_map_bytes, void* stream);
+
+/*
+ * Decode = split + combine with a task map from lbsa_plan (same batch,
+ * num_heads, num_kv_heads and P).  Source: vLLM post, bullet "Compute and
+ * combine"; SGLang post, "Scheduling around live KV work".
+ *   q_d, q_scale_d            query (bf16, or e4m3 codes + fp32 scales for fp8)
+ *   k_cache_d, v_cache_d      paged caches, kv_dtype LBSA_KV_BF16 or LBSA_KV_FP8_E4M3
+ *   k_scale_d, v_scale_d      fp32 scales (fp8 only, else NULL)
+ *   page_table_d              int32 [batch][max_pages_per_seq]
+ *   num_pages                 pages in each cache (page ids are checked against it)
+ *   softmax_scale             multiplier of q.k (e.g. 1/sqrt(128))
+ *   workspace_d               >= lbsa_workspace_bytes bytes, 256-byte aligned
+ *   out_d                     bf16 [batch][num_heads][128]
+ * The q/k/v/out dtypes follow kv_dtype: bf16 path = bf16 q, bf16 caches; fp8
+ * path = e4m3 q with q_scale, e4m3 caches with k/v scales.  Output is bf16
+ * (round to nearest even) in both.
+ */
+int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
+                const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
+                int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t num_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                int32_t max_pages_per_seq, int64_t num_pages, int32_t num_workgroups,
+                float softmax_scale, const void* task_map_d, size_t task_map_bytes,
+                void* workspace_d, size_t workspace_bytes, void* out_d, void* stream);
+
+/* The split half of lbsa_decode alone: fills the workspace partials (slot d =
+ * descriptor d).  Same arguments as lbsa_decode without out_d. */
+int lbsa_decode_split(const void* q_d, const float* q_scale_d, const void* k_cache_d,
+                      const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
+                      int32_t kv_dtype, const int32_t* page_table_d, int32_t batch,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t max_pages_per_seq, int64_t num_pages, int32_t num_workgroups,
+                      float softmax_scale, const void* task_map_d, size_t task_map_bytes,
+                      void* workspace_d, size_t workspace_bytes, void* stream);
+
+/* The combine half of lbsa_decode alone: merges the workspace partials of each
+ * (request, query head) into out_d (bf16). */
+int lbsa_decode_combine(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t num_workgroups, const void* task_map_d, size_t task_map_bytes,
+                        const void* workspace_d, size_t workspace_bytes, void* out_d,
+                        void* stream);
+
+/* Workspace bytes of the static baseline: batch * Hkv * num_splits partials. */
+int lbsa_static_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t num_splits, size_t* out_bytes);
+
+/*
+ * Static split-KV baseline (no task map): a grid of num_splits x batch x Hkv
+ * workgroups; split s of request b covers tiles [floor(s*n_b/S), floor((s+1)*n_b/S))
+ * of every KV head, followed by a fixed-S combine.  This is the "fixed number
+ * of splits" static policy of the vLLM post, section "The challenge:
+ * mixed-length decode in every batch".  Same tensors as lbsa_decode plus the
+ * device lengths; workspace >= lbsa_static_workspace_bytes.
+ */
+int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_cache_d,
+                       const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
+                       int32_t kv_dtype, const int32_t* page_table_d, const int32_t* seqlens_d,
+                       int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
+                       int32_t num_splits, float softmax_scale, void* workspace_d,
+                       size_t workspace_bytes, void* out_d, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LBSA_H */

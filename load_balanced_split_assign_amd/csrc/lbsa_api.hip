@@ -1,0 +1,305 @@
+// C ABI of liblbsa.so: host-side argument validation and kernel launches.
+// Every check runs before anything is enqueued; the library never allocates,
+// frees or synchronises.
+#include <limits.h>
+
+#include "lbsa_internal.h"
+
+#define LBSA_API extern "C" __attribute__((visibility("default")))
+
+using namespace lbsa;
+
+namespace {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+int check_shape(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t page_size) {
+    if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0)
+        return LBSA_ERR_INVALID_ARGUMENT;
+    if (num_heads % num_kv_heads != 0) return LBSA_ERR_INVALID_ARGUMENT;
+    if (head_dim != kHeadDim || page_size != kTile || num_heads / num_kv_heads != kGroup)
+        return LBSA_ERR_UNSUPPORTED;
+    if ((long long)num_kv_heads * batch > (long long)INT_MAX / 4) return LBSA_ERR_UNSUPPORTED;
+    return LBSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LBSA_OK : LBSA_ERR_HIP; }
+
+struct DecodeCommon {
+    int status;
+    AttnArgs a;
+    bool fp8;
+};
+
+DecodeCommon check_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
+                          const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
+                          int32_t kv_dtype, const int32_t* page_table_d, int32_t batch,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
+                          float softmax_scale) {
+    DecodeCommon c{};
+    c.status = check_shape(batch, num_heads, num_kv_heads, head_dim, page_size);
+    if (c.status != LBSA_OK) return c;
+    if (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3) {
+        c.status = LBSA_ERR_INVALID_ARGUMENT;
+        return c;
+    }
+    c.fp8 = kv_dtype == LBSA_KV_FP8_E4M3;
+    if (!q_d || !k_cache_d || !v_cache_d || !page_table_d || max_pages_per_seq <= 0 ||
+        num_pages <= 0 || !(softmax_scale == softmax_scale)) {
+        c.status = LBSA_ERR_INVALID_ARGUMENT;
+        return c;
+    }
+    if (c.fp8 && (!q_scale_d || !k_scale_d || !v_scale_d)) {
+        c.status = LBSA_ERR_INVALID_ARGUMENT;
+        return c;
+    }
+    // 128-bit loads of K/V rows and Q, 64-bit loads of fp8 Q, 128-bit scale loads.
+    if (!aligned(q_d, c.fp8 ? 8 : 16) || !aligned(k_cache_d, 16) || !aligned(v_cache_d, 16) ||
+        (c.fp8 && (!aligned(k_scale_d, 16) || !aligned(v_scale_d, 16) || !aligned(q_scale_d, 4))) ||
+        !aligned(page_table_d, 4)) {
+        c.status = LBSA_ERR_INVALID_ARGUMENT;
+        return c;
+    }
+    if ((long long)max_pages_per_seq * kTile > INT_MAX / 2) {
+        c.status = LBSA_ERR_UNSUPPORTED;
+        return c;
+    }
+    AttnArgs& a = c.a;
+    a.q = q_d;
+    a.q_scale = q_scale_d;
+    a.k_cache = k_cache_d;
+    a.v_cache = v_cache_d;
+    a.k_scale = k_scale_d;
+    a.v_scale = v_scale_d;
+    a.page_table = page_table_d;
+    a.num_pages = num_pages;
+    a.B = batch;
+    a.Hq = num_heads;
+    a.Hkv = num_kv_heads;
+    a.max_pages = max_pages_per_seq;
+    a.scale_log2 = softmax_scale * kLog2eHost;
+    return c;
+}
+
+}  // namespace
+
+LBSA_API const char* lbsa_status_string(int status) {
+    switch (status) {
+        case LBSA_OK: return "ok";
+        case LBSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case LBSA_ERR_UNSUPPORTED: return "unsupported shape";
+        case LBSA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+LBSA_API int lbsa_version(void) { return 100; }
+
+LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_P) {
+    if (!out_P || (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return LBSA_ERR_HIP;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return LBSA_ERR_HIP;
+    if (cur != device && hipSetDevice(device) != hipSuccess) return LBSA_ERR_HIP;
+    int per_cu = 0;
+    const hipError_t e = split_occupancy(kv_dtype == LBSA_KV_FP8_E4M3, &per_cu);
+    if (cur != device) (void)hipSetDevice(cur);
+    if (e != hipSuccess || per_cu <= 0 || cus <= 0) return LBSA_ERR_HIP;
+    *out_P = cus * per_cu;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32_t P,
+                                      lbsa_task_map_layout* out) {
+    if (!out || batch <= 0 || num_kv_heads <= 0 || P <= 0) return LBSA_ERR_INVALID_ARGUMENT;
+    const MapLayout m = map_layout(batch, num_kv_heads, P);
+    out->header = m.header;
+    out->bin_desc_begin = m.bin_desc_begin;
+    out->desc = m.desc;
+    out->seg_first_desc = m.seg_first_desc;
+    out->seg_num_chunks = m.seg_num_chunks;
+    out->seqlens = m.seqlens;
+    out->total = m.total;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t P, size_t* out_bytes) {
+    if (!out_bytes) return LBSA_ERR_INVALID_ARGUMENT;
+    lbsa_task_map_layout l;
+    const int s = lbsa_task_map_layout_get(batch, num_kv_heads, P, &l);
+    if (s == LBSA_OK) *out_bytes = l.total;
+    return s;
+}
+
+LBSA_API int lbsa_workspace_layout_get(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t P, lbsa_workspace_layout* out) {
+    if (!out || P <= 0) return LBSA_ERR_INVALID_ARGUMENT;
+    const int s = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile);
+    if (s != LBSA_OK) return s;
+    const WsLayout w = ws_layout((size_t)num_kv_heads * batch + P);
+    out->part_lse = w.part_lse;
+    out->part_o = w.part_o;
+    out->total = w.total;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t P, size_t* out_bytes) {
+    if (!out_bytes) return LBSA_ERR_INVALID_ARGUMENT;
+    lbsa_workspace_layout l;
+    const int s = lbsa_workspace_layout_get(batch, num_heads, num_kv_heads, head_dim, P, &l);
+    if (s == LBSA_OK) *out_bytes = l.total;
+    return s;
+}
+
+LBSA_API int lbsa_static_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t num_splits, size_t* out_bytes) {
+    if (!out_bytes || num_splits <= 0) return LBSA_ERR_INVALID_ARGUMENT;
+    const int s = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile);
+    if (s != LBSA_OK) return s;
+    *out_bytes = ws_layout((size_t)num_kv_heads * batch * num_splits).total;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t page_size, int32_t max_pages_per_seq,
+                       int32_t num_workgroups, int32_t min_tiles_per_bin, void* task_map_d,
+                       size_t task_map_bytes, void* stream) {
+    int s = check_shape(batch, num_heads, num_kv_heads, kHeadDim, page_size);
+    if (s != LBSA_OK) return s;
+    if (!seqlens_d || !task_map_d || max_pages_per_seq <= 0 || num_workgroups <= 0 ||
+        min_tiles_per_bin < 0 || !aligned(task_map_d, 16) || !aligned(seqlens_d, 4))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    // the single assign workgroup keeps (B + 1) + (Hkv*B + 1) ints in LDS
+    if ((long long)batch + 1 + (long long)num_kv_heads * batch + 1 > kMaxAssignLdsWords)
+        return LBSA_ERR_UNSUPPORTED;
+    // every tile index and prefix stays far from int32 overflow
+    if ((long long)batch * max_pages_per_seq * num_kv_heads >= (1LL << 30) ||
+        (long long)max_pages_per_seq * kTile >= (1LL << 30) || num_workgroups >= (1 << 24))
+        return LBSA_ERR_UNSUPPORTED;
+    size_t need = 0;
+    lbsa_task_map_bytes(batch, num_kv_heads, num_workgroups, &need);
+    if (task_map_bytes < need) return LBSA_ERR_INVALID_ARGUMENT;
+    const int F = min_tiles_per_bin == 0 ? LBSA_DEFAULT_MIN_TILES : min_tiles_per_bin;
+    return hip_status(launch_assign(seqlens_d, batch, num_heads, num_kv_heads, num_workgroups, F,
+                                    max_pages_per_seq, task_map_d,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+static int decode_prepare(DecodeCommon& c, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t num_workgroups, const void* task_map_d,
+                          size_t task_map_bytes, void* workspace_d, size_t workspace_bytes) {
+    if (c.status != LBSA_OK) return c.status;
+    if (!task_map_d || !workspace_d || num_workgroups <= 0 || !aligned(task_map_d, 16) ||
+        !aligned(workspace_d, 256))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    size_t map_need = 0, ws_need = 0;
+    lbsa_task_map_bytes(batch, num_kv_heads, num_workgroups, &map_need);
+    const int s = lbsa_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, num_workgroups, &ws_need);
+    if (s != LBSA_OK) return s;
+    if (task_map_bytes < map_need || workspace_bytes < ws_need) return LBSA_ERR_INVALID_ARGUMENT;
+    const WsLayout w = ws_layout((size_t)num_kv_heads * batch + num_workgroups);
+    c.a.map = static_cast<const uint8_t*>(task_map_d);
+    c.a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) + w.part_lse);
+    c.a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) + w.part_o);
+    c.a.P = num_workgroups;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_decode_split(const void* q_d, const float* q_scale_d, const void* k_cache_d,
+                               const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
+                               int32_t kv_dtype, const int32_t* page_table_d, int32_t batch,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
+                               int32_t num_workgroups, float softmax_scale, const void* task_map_d,
+                               size_t task_map_bytes, void* workspace_d, size_t workspace_bytes,
+                               void* stream) {
+    DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
+                                  kv_dtype, page_table_d, batch, num_heads, num_kv_heads, head_dim,
+                                  page_size, max_pages_per_seq, num_pages, softmax_scale);
+    const int s = decode_prepare(c, batch, num_heads, num_kv_heads, head_dim, num_workgroups,
+                                 task_map_d, task_map_bytes, workspace_d, workspace_bytes);
+    if (s != LBSA_OK) return s;
+    return hip_status(launch_split(c.a, c.fp8, static_cast<hipStream_t>(stream)));
+}
+
+LBSA_API int lbsa_decode_combine(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t num_workgroups, const void* task_map_d,
+                                 size_t task_map_bytes, const void* workspace_d,
+                                 size_t workspace_bytes, void* out_d, void* stream) {
+    DecodeCommon c{};
+    c.status = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile);
+    if (c.status != LBSA_OK) return c.status;
+    if (!out_d || !aligned(out_d, 8)) return LBSA_ERR_INVALID_ARGUMENT;
+    c.a.B = batch;
+    c.a.Hq = num_heads;
+    c.a.Hkv = num_kv_heads;
+    const int s = decode_prepare(c, batch, num_heads, num_kv_heads, head_dim, num_workgroups,
+                                 task_map_d, task_map_bytes, const_cast<void*>(workspace_d),
+                                 workspace_bytes);
+    if (s != LBSA_OK) return s;
+    c.a.out = out_d;
+    return hip_status(launch_combine(c.a, false, static_cast<hipStream_t>(stream)));
+}
+
+LBSA_API int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
+                         const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
+                         int32_t kv_dtype, const int32_t* page_table_d, int32_t batch,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
+                         int32_t num_workgroups, float softmax_scale, const void* task_map_d,
+                         size_t task_map_bytes, void* workspace_d, size_t workspace_bytes,
+                         void* out_d, void* stream) {
+    DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
+                                  kv_dtype, page_table_d, batch, num_heads, num_kv_heads, head_dim,
+                                  page_size, max_pages_per_seq, num_pages, softmax_scale);
+    int s = decode_prepare(c, batch, num_heads, num_kv_heads, head_dim, num_workgroups, task_map_d,
+                           task_map_bytes, workspace_d, workspace_bytes);
+    if (s != LBSA_OK) return s;
+    if (!out_d || !aligned(out_d, 8)) return LBSA_ERR_INVALID_ARGUMENT;
+    c.a.out = out_d;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    s = hip_status(launch_split(c.a, c.fp8, st));
+    if (s != LBSA_OK) return s;
+    return hip_status(launch_combine(c.a, false, st));
+}
+
+LBSA_API int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_cache_d,
+                                const void* v_cache_d, const float* k_scale_d,
+                                const float* v_scale_d, int32_t kv_dtype,
+                                const int32_t* page_table_d, const int32_t* seqlens_d,
+                                int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t page_size, int32_t max_pages_per_seq,
+                                int64_t num_pages, int32_t num_splits, float softmax_scale,
+                                void* workspace_d, size_t workspace_bytes, void* out_d,
+                                void* stream) {
+    DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
+                                  kv_dtype, page_table_d, batch, num_heads, num_kv_heads, head_dim,
+                                  page_size, max_pages_per_seq, num_pages, softmax_scale);
+    if (c.status != LBSA_OK) return c.status;
+    if (!seqlens_d || !workspace_d || !out_d || num_splits <= 0 || !aligned(workspace_d, 256) ||
+        !aligned(out_d, 8) || !aligned(seqlens_d, 4))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    if ((long long)num_splits * batch * num_kv_heads >= (1LL << 31)) return LBSA_ERR_UNSUPPORTED;
+    size_t need = 0;
+    const int s = lbsa_static_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, num_splits, &need);
+    if (s != LBSA_OK) return s;
+    if (workspace_bytes < need) return LBSA_ERR_INVALID_ARGUMENT;
+    const WsLayout w = ws_layout((size_t)num_kv_heads * batch * num_splits);
+    c.a.seqlens = seqlens_d;
+    c.a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) + w.part_lse);
+    c.a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) + w.part_o);
+    c.a.out = out_d;
+    c.a.P = num_splits;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int r = hip_status(launch_static(c.a, c.fp8, st));
+    if (r != LBSA_OK) return r;
+    return hip_status(launch_combine(c.a, true, st));
+}

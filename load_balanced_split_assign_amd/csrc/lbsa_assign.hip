@@ -1,0 +1,206 @@
+// Assign kernel: builds the per-step task map on the device.
+//
+// Method: HPC-Ops vLLM post, section "The solution: a per-step, load-balanced
+// decode scheduler", bullet "Assign" (and the SGLang post's "Scheduling around
+// live KV work"): every live KV sequence is cut into 64-token tiles, tiles are
+// walked head-major / batch-minor, a per-workgroup budget comes from total
+// tiles / workgroups with a minimum-work floor, and bins are filled to the
+// budget and then spill into the next bin.  The map is built from device-side
+// lengths once per decode step and reused by every layer.
+//
+// Budget reading: K = min(P, max(1, floor(T/F))) active bins, the first T mod K
+// bins hold ceil(T/K) tiles and the rest floor(T/K) -- fill-then-spill with
+// bin sizes that differ by at most one tile.
+//
+// GPU formulation (one workgroup, integer only, no atomics, so the map is
+// bit-reproducible).  The sequential fill-and-spill walk is equivalent to
+// cutting the global tile range [0, T) at two sets of points: segment starts
+// and bin starts bin_start(j) = j*q + min(j, r).  Hence
+//   chunks(s) = bin_of(last tile of s) - bin_of(first tile of s) + 1,
+// descriptor slots are the exclusive prefix of chunks(s) in (h, b) order, and
+// descriptor d is reconstructed independently by a binary search over that
+// prefix.  Every step is a scan or a search, so 1024 threads share the work.
+#include "lbsa_internal.h"
+
+namespace lbsa {
+namespace {
+
+// Block-wide exclusive scan of one int per thread; returns the prefix and
+// writes the block total to *total (all threads).  `red` holds 16 ints.
+__device__ int block_exclusive_scan(int v, int* red, int* total) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) red[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < (kAssignThreads / 64) ? red[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            int y = __shfl_up(w, o, 64);
+            if (lane >= o) w += y;
+        }
+        if (lane < (kAssignThreads / 64)) red[16 + lane] = w;  // inclusive wave totals
+    }
+    __syncthreads();
+    const int before = wave ? red[16 + wave - 1] : 0;
+    *total = red[16 + kAssignThreads / 64 - 1];
+    __syncthreads();  // red is reused by the next scan
+    return before + x - v;
+}
+
+struct Bins {
+    int K, q, r;
+    __device__ int start(int j) const { return j * q + min(j, r); }
+    // bin holding global tile x (0 <= x < T)
+    __device__ int of(int x) const {
+        const int big = r * (q + 1);
+        return x < big ? x / (q + 1) : r + (x - big) / q;
+    }
+};
+
+// first index i in [0, n] with a[i] > x (a non-decreasing, length n + 1)
+__device__ int upper_bound(const int* a, int n, int x) {
+    int lo = 0, hi = n + 1;
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (a[mid] > x) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(kAssignThreads) void assign_kernel(
+    const int32_t* __restrict__ seqlens, int B, int Hq, int Hkv, int P, int F, int max_pages,
+    uint8_t* __restrict__ map) {
+    extern __shared__ int smem[];
+    __shared__ int red[32];
+    const MapLayout L = map_layout(B, Hkv, P);
+    int32_t* hdr = reinterpret_cast<int32_t*>(map + L.header);
+    int32_t* bdb = reinterpret_cast<int32_t*>(map + L.bin_desc_begin);
+    int4* desc = reinterpret_cast<int4*>(map + L.desc);
+    int32_t* sfd_g = reinterpret_cast<int32_t*>(map + L.seg_first_desc);
+    int32_t* snc_g = reinterpret_cast<int32_t*>(map + L.seg_num_chunks);
+    int32_t* sl_g = reinterpret_cast<int32_t*>(map + L.seqlens);
+
+    const int S = Hkv * B;
+    int* prefix = smem;            // [B + 1]  exclusive prefix of n_b
+    int* sfd = smem + B + 1;       // [S + 1]  exclusive prefix of chunks(s)
+    const int tid = threadIdx.x;
+
+    // ---- validate lengths (a bad length empties the map) -------------------
+    int bad = 0;
+    for (int b = tid; b < B; b += kAssignThreads) {
+        const int len = seqlens[b];
+        sl_g[b] = len;
+        bad |= (len < 0) || ((long long)len > (long long)max_pages * kTile);
+    }
+    const int error = __syncthreads_or(bad);
+
+    // ---- tile census: n_b = ceil(L_b / 64), exclusive prefix over b ---------
+    const int per = (B + kAssignThreads - 1) / kAssignThreads;
+    const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += error ? 0 : (seqlens[b] + kTile - 1) / kTile;
+    int N;
+    int run = block_exclusive_scan(local, red, &N);
+    for (int b = b0; b < b1; ++b) {
+        prefix[b] = run;
+        run += error ? 0 : (seqlens[b] + kTile - 1) / kTile;
+    }
+    if (tid == 0) prefix[B] = N;
+    __syncthreads();
+
+    // ---- budget ------------------------------------------------------------
+    const int T = Hkv * N;
+    Bins bins;
+    bins.K = 0; bins.q = 0; bins.r = 0;
+    if (T > 0) {
+        bins.K = min(P, max(1, T / F));
+        bins.q = T / bins.K;
+        bins.r = T % bins.K;
+    }
+
+    // ---- chunks per segment s = h*B + b and their exclusive prefix ---------
+    const int sper = (S + kAssignThreads - 1) / kAssignThreads;
+    const int s0 = min(S, tid * sper), s1 = min(S, s0 + sper);
+    auto chunks = [&](int s) -> int {
+        const int h = s / B, b = s - h * B;
+        const int a = h * N + prefix[b];
+        const int n = prefix[b + 1] - prefix[b];
+        return n ? bins.of(a + n - 1) - bins.of(a) + 1 : 0;
+    };
+    local = 0;
+    for (int s = s0; s < s1; ++s) local += chunks(s);
+    int ndesc;
+    run = block_exclusive_scan(local, red, &ndesc);
+    for (int s = s0; s < s1; ++s) {
+        const int c = chunks(s);
+        sfd[s] = run;
+        sfd_g[s] = run;
+        snc_g[s] = c;
+        run += c;
+    }
+    if (tid == 0) sfd[S] = ndesc;
+    __syncthreads();
+
+    // ---- descriptors: slot d belongs to the segment whose prefix covers d ---
+    for (int d = tid; d < ndesc; d += kAssignThreads) {
+        const int s = upper_bound(sfd, S, d) - 1;
+        const int h = s / B, b = s - h * B;
+        const int a = h * N + prefix[b];
+        const int n = prefix[b + 1] - prefix[b];
+        const int j = bins.of(a) + (d - sfd[s]);
+        const int g0 = max(a, bins.start(j));
+        const int g1 = min(a + n, bins.start(j + 1));
+        desc[d] = make_int4(h, b, g0 - a, g1 - a);
+    }
+
+    // ---- bin CSR: the first descriptor of bin j starts at bin_start(j) ------
+    for (int j = tid; j <= P; j += kAssignThreads) {
+        int v = ndesc;
+        if (j < bins.K) {
+            const int x = bins.start(j);
+            const int h = x / N;
+            const int b = upper_bound(prefix, B, x - h * N) - 1;
+            const int s = h * B + b;
+            v = sfd[s] + (j - bins.of(h * N + prefix[b]));
+        }
+        bdb[j] = v;
+    }
+
+    if (tid == 0) {
+        hdr[0] = T;
+        hdr[1] = bins.K;
+        hdr[2] = bins.q;
+        hdr[3] = bins.r;
+        hdr[4] = ndesc;
+        hdr[5] = P;
+        hdr[6] = F;
+        hdr[7] = B;
+        hdr[8] = Hq;
+        hdr[9] = Hkv;
+        hdr[10] = error;
+        hdr[11] = N;
+        hdr[12] = max_pages;
+        hdr[13] = kTile;
+        hdr[14] = 0;
+        hdr[15] = 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_assign(const int32_t* seqlens, int B, int Hq, int Hkv, int P, int F,
+                         int max_pages, void* map, hipStream_t stream) {
+    const size_t lds = sizeof(int) * ((size_t)B + 1 + (size_t)Hkv * B + 1);
+    hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), lds, stream, seqlens, B, Hq,
+                       Hkv, P, F, max_pages, static_cast<uint8_t*>(map));
+    return hipGetLastError();
+}
+
+}  // namespace lbsa

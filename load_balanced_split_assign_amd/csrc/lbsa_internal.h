@@ -1,0 +1,82 @@
+// Internal declarations shared by the HIP translation units of liblbsa.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lbsa.h"
+
+namespace lbsa {
+
+constexpr int kTile = 64;       // tokens per tile = tokens per page
+constexpr int kHeadDim = 128;
+constexpr int kGroup = 8;       // query heads per KV head
+constexpr int kSplitThreads = 256;   // 4 wave64 per split workgroup
+constexpr int kAssignThreads = 1024;
+constexpr int kCombineThreads = 256;
+constexpr int kMaxAssignLdsWords = 16384;  // (B + 1) + (Hkv*B + 1) int32 in 64 KiB
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Byte offsets of the task-map arrays for (B, Hkv, P).
+struct MapLayout {
+    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seqlens, total;
+};
+
+__host__ __device__ inline MapLayout map_layout(int B, int Hkv, int P) {
+    MapLayout m;
+    const size_t S = (size_t)Hkv * (size_t)B;
+    const size_t cap = S + (size_t)P;
+    m.header = 0;
+    m.bin_desc_begin = 64;
+    m.desc = align_up(m.bin_desc_begin + 4 * ((size_t)P + 1), 16);
+    m.seg_first_desc = m.desc + 16 * cap;
+    m.seg_num_chunks = m.seg_first_desc + 4 * S;
+    m.seqlens = m.seg_num_chunks + 4 * S;
+    m.total = align_up(m.seqlens + 4 * (size_t)B, 256);
+    return m;
+}
+
+// Byte offsets of the partial buffers for `slots` partials of G x D.
+struct WsLayout {
+    size_t part_lse, part_o, total;
+};
+
+__host__ __device__ inline WsLayout ws_layout(size_t slots) {
+    WsLayout w;
+    w.part_lse = 0;
+    w.part_o = align_up(4 * slots * kGroup, 256);
+    w.total = align_up(w.part_o + 4 * slots * kGroup * kHeadDim, 256);
+    return w;
+}
+
+// Arguments of the attention kernels (passed by value).
+struct AttnArgs {
+    const void* q;
+    const float* q_scale;
+    const void* k_cache;
+    const void* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* page_table;
+    const int32_t* seqlens;      // static path only (the split path reads the map copy)
+    const uint8_t* map;          // task map base (split / combine)
+    float* part_lse;
+    float* part_o;
+    void* out;
+    int64_t num_pages;
+    int32_t B, Hq, Hkv, max_pages;
+    int32_t P;                   // split: bins; static: number of splits
+    float scale_log2;            // softmax_scale * log2(e)
+};
+
+// Host launchers (defined in the .hip files).
+hipError_t launch_assign(const int32_t* seqlens, int B, int Hq, int Hkv, int P, int F,
+                         int max_pages, void* map, hipStream_t stream);
+hipError_t launch_split(const AttnArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream);
+hipError_t split_occupancy(bool fp8, int* blocks_per_cu);
+
+}  // namespace lbsa

@@ -1,0 +1,271 @@
+"""Thin ctypes binding of liblbsa.so (see include/lbsa.h for the C ABI).
+
+Argument marshalling only: every step of the path (assign, split, combine and
+the static baseline) runs in the library's HIP kernels.  PyTorch provides the
+device memory and the stream.  If the shared library is missing this module
+raises at first use -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblbsa.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+KV_BF16, KV_FP8_E4M3 = 0, 1
+PAGE_SIZE, HEAD_DIM, GROUP, DEFAULT_MIN_TILES = 64, 128, 8, 2
+HEADER_FIELDS = ("T", "K", "q", "r", "Ndesc", "P", "F", "B", "Hq", "Hkv",
+                 "error", "N", "max_pages", "page_size")
+
+_lib = None
+
+
+class LbsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+class _MapLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("header", "bin_desc_begin", "desc", "seg_first_desc", "seg_num_chunks", "seqlens", "total")]
+
+
+class _WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("part_lse", "part_o", "total")]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded liblbsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m load_balanced_split_assign_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        f32 = ctypes.c_float
+        L.lbsa_status_string.argtypes = [ctypes.c_int]
+        L.lbsa_status_string.restype = ctypes.c_char_p
+        L.lbsa_version.restype = ctypes.c_int
+        L.lbsa_default_workgroups.argtypes = [ctypes.c_int, i32, ctypes.POINTER(i32)]
+        L.lbsa_task_map_layout_get.argtypes = [i32, i32, i32, ctypes.POINTER(_MapLayout)]
+        L.lbsa_task_map_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.lbsa_workspace_layout_get.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_WsLayout)]
+        L.lbsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.lbsa_static_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.lbsa_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        attn = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i64, i32, f32, vp, sz, vp, sz]
+        L.lbsa_decode.argtypes = attn + [vp, vp]
+        L.lbsa_decode_split.argtypes = attn + [vp]
+        L.lbsa_decode_combine.argtypes = [i32, i32, i32, i32, i32, vp, sz, vp, sz, vp, vp]
+        L.lbsa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                         i32, i64, i32, f32, vp, sz, vp, vp]
+        for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes",
+                   "lbsa_workspace_layout_get", "lbsa_workspace_bytes", "lbsa_static_workspace_bytes",
+                   "lbsa_plan", "lbsa_decode", "lbsa_decode_split", "lbsa_decode_combine",
+                   "lbsa_decode_static"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().lbsa_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise LbsaError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def kv_dtype_code(kv_dtype: str) -> int:
+    return {"bf16": KV_BF16, "fp8": KV_FP8_E4M3}[kv_dtype]
+
+
+# ---------------------------------------------------------------------------
+# sizes and layouts
+# ---------------------------------------------------------------------------
+
+def default_workgroups(device: int = 0, kv_dtype: str = "bf16") -> int:
+    out = ctypes.c_int32()
+    _check("lbsa_default_workgroups", lib().lbsa_default_workgroups(int(device), kv_dtype_code(kv_dtype),
+                                                                    ctypes.byref(out)))
+    return int(out.value)
+
+
+def task_map_layout(batch: int, num_kv_heads: int, P: int) -> dict:
+    m = _MapLayout()
+    _check("lbsa_task_map_layout_get", lib().lbsa_task_map_layout_get(batch, num_kv_heads, P, ctypes.byref(m)))
+    return {n: int(getattr(m, n)) for n, _ in m._fields_}
+
+
+def task_map_bytes(batch: int, num_kv_heads: int, P: int) -> int:
+    out = ctypes.c_size_t()
+    _check("lbsa_task_map_bytes", lib().lbsa_task_map_bytes(batch, num_kv_heads, P, ctypes.byref(out)))
+    return int(out.value)
+
+
+def workspace_layout(batch: int, num_heads: int, num_kv_heads: int, P: int, head_dim: int = HEAD_DIM) -> dict:
+    w = _WsLayout()
+    _check("lbsa_workspace_layout_get",
+           lib().lbsa_workspace_layout_get(batch, num_heads, num_kv_heads, head_dim, P, ctypes.byref(w)))
+    return {n: int(getattr(w, n)) for n, _ in w._fields_}
+
+
+def workspace_bytes(batch: int, num_heads: int, num_kv_heads: int, P: int, head_dim: int = HEAD_DIM) -> int:
+    out = ctypes.c_size_t()
+    _check("lbsa_workspace_bytes",
+           lib().lbsa_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, P, ctypes.byref(out)))
+    return int(out.value)
+
+
+def static_workspace_bytes(batch: int, num_heads: int, num_kv_heads: int, num_splits: int,
+                           head_dim: int = HEAD_DIM) -> int:
+    out = ctypes.c_size_t()
+    _check("lbsa_static_workspace_bytes",
+           lib().lbsa_static_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, num_splits,
+                                             ctypes.byref(out)))
+    return int(out.value)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def plan(seqlens: torch.Tensor, num_heads: int, num_kv_heads: int, max_pages: int, num_workgroups: int,
+         min_tiles_per_bin: int = 0, page_size: int = PAGE_SIZE, task_map: torch.Tensor | None = None):
+    """Run the assign kernel; returns the task map (uint8 device tensor)."""
+    B = int(seqlens.numel())
+    nbytes = task_map_bytes(B, num_kv_heads, num_workgroups)
+    if task_map is None:
+        task_map = torch.empty(nbytes, dtype=torch.uint8, device=seqlens.device)
+    assert seqlens.dtype == torch.int32 and seqlens.is_contiguous()
+    _check("lbsa_plan", lib().lbsa_plan(_ptr(seqlens), B, num_heads, num_kv_heads, page_size, max_pages,
+                                        num_workgroups, min_tiles_per_bin, _ptr(task_map),
+                                        task_map.numel() * task_map.element_size(), _stream(seqlens.device)))
+    return task_map
+
+
+def _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table):
+    fp8 = k_cache.dtype == torch.float8_e4m3fn
+    if fp8:
+        assert q.dtype == torch.float8_e4m3fn and v_cache.dtype == torch.float8_e4m3fn
+        assert q_scale is not None and k_scale is not None and v_scale is not None
+    else:
+        assert q.dtype == torch.bfloat16 and k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16
+    for t in (q, k_cache, v_cache, page_table, q_scale, k_scale, v_scale):
+        assert t is None or t.is_contiguous()
+    B, Hq, D = q.shape
+    num_pages, page, Hkv, D2 = k_cache.shape
+    assert page == PAGE_SIZE and D2 == D and tuple(v_cache.shape) == tuple(k_cache.shape)
+    assert page_table.dtype == torch.int32 and page_table.shape[0] == B
+    return [_ptr(q), _ptr(q_scale) if fp8 else None, _ptr(k_cache), _ptr(v_cache),
+            _ptr(k_scale) if fp8 else None, _ptr(v_scale) if fp8 else None,
+            KV_FP8_E4M3 if fp8 else KV_BF16, _ptr(page_table), B, Hq, Hkv, D, page,
+            int(page_table.shape[1]), int(num_pages)], (B, Hq, Hkv, D)
+
+
+def decode(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softmax_scale: float,
+           q_scale=None, k_scale=None, v_scale=None, workspace=None, out=None):
+    """Split + combine with a task map from :func:`plan`; returns bf16 [B, Hq, D]."""
+    args, (B, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(B, Hq, Hkv, num_workgroups, D), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _check("lbsa_decode", lib().lbsa_decode(*args, num_workgroups, float(softmax_scale), _ptr(task_map),
+                                            task_map.numel(), _ptr(workspace), workspace.numel(), _ptr(out),
+                                            _stream(q.device)))
+    return out
+
+
+def decode_split(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softmax_scale: float,
+                 q_scale=None, k_scale=None, v_scale=None, workspace=None):
+    """Split kernel only; returns the workspace holding the partials."""
+    args, (B, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(B, Hq, Hkv, num_workgroups, D), dtype=torch.uint8, device=q.device)
+    _check("lbsa_decode_split", lib().lbsa_decode_split(*args, num_workgroups, float(softmax_scale),
+                                                        _ptr(task_map), task_map.numel(), _ptr(workspace),
+                                                        workspace.numel(), _stream(q.device)))
+    return workspace
+
+
+def decode_combine(batch: int, num_heads: int, num_kv_heads: int, num_workgroups: int, task_map, workspace,
+                   out=None, head_dim: int = HEAD_DIM):
+    """Combine kernel only; returns bf16 [B, Hq, D]."""
+    if out is None:
+        out = torch.empty((batch, num_heads, head_dim), dtype=torch.bfloat16, device=workspace.device)
+    _check("lbsa_decode_combine", lib().lbsa_decode_combine(batch, num_heads, num_kv_heads, head_dim,
+                                                            num_workgroups, _ptr(task_map), task_map.numel(),
+                                                            _ptr(workspace), workspace.numel(), _ptr(out),
+                                                            _stream(workspace.device)))
+    return out
+
+
+def decode_static(q, k_cache, v_cache, page_table, seqlens, num_splits: int, softmax_scale: float,
+                  q_scale=None, k_scale=None, v_scale=None, workspace=None, out=None):
+    """Static split-KV baseline (fixed split count per request)."""
+    args, (B, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
+    assert seqlens.dtype == torch.int32 and seqlens.is_contiguous()
+    if workspace is None:
+        workspace = torch.empty(static_workspace_bytes(B, Hq, Hkv, num_splits, D), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    a = args
+    _check("lbsa_decode_static", lib().lbsa_decode_static(*a[:8], _ptr(seqlens), *a[8:], num_splits,
+                                                          float(softmax_scale), _ptr(workspace),
+                                                          workspace.numel(), _ptr(out), _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# reading results back (host side, for checks and reports)
+# ---------------------------------------------------------------------------
+
+def read_task_map(task_map: torch.Tensor, batch: int, num_kv_heads: int, P: int) -> dict:
+    """Copy a task map to the host and split it into its arrays (library layout)."""
+    lay = task_map_layout(batch, num_kv_heads, P)
+    raw = task_map.detach().cpu().numpy()[:lay["total"]]
+    S = batch * num_kv_heads
+    cap = S + P
+
+    def arr(off, n, shape=None):
+        a = raw[off:off + 4 * n].view(np.int32).copy()
+        return a if shape is None else a.reshape(shape)
+
+    header = arr(lay["header"], 16)
+    out = {"header": header, "bin_desc_begin": arr(lay["bin_desc_begin"], P + 1),
+           "desc_all": arr(lay["desc"], 4 * cap, (cap, 4)),
+           "seg_first_desc": arr(lay["seg_first_desc"], S), "seg_num_chunks": arr(lay["seg_num_chunks"], S),
+           "seqlens": arr(lay["seqlens"], batch)}
+    for i, name in enumerate(HEADER_FIELDS):
+        out[name] = int(header[i])
+    nd = max(0, min(out["Ndesc"], cap))
+    out["desc"] = out["desc_all"][:nd].copy()
+    return out
+
+
+def read_partials(workspace: torch.Tensor, batch: int, num_heads: int, num_kv_heads: int, P: int,
+                  ndesc: int):
+    """(part_o [ndesc, 8, 128], part_lse [ndesc, 8]) as float32 numpy arrays."""
+    lay = workspace_layout(batch, num_heads, num_kv_heads, P)
+    raw = workspace.detach().cpu().numpy()
+    lse = raw[lay["part_lse"]:lay["part_lse"] + 4 * GROUP * ndesc].view(np.float32).reshape(ndesc, GROUP)
+    o = raw[lay["part_o"]:lay["part_o"] + 4 * GROUP * HEAD_DIM * ndesc].view(np.float32)
+    return o.reshape(ndesc, GROUP, HEAD_DIM).copy(), lse.copy()

@@ -1,0 +1,110 @@
+"""The C ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before anything is enqueued (no GPU needed: these calls
+return before touching the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from load_balanced_split_assign_amd import lbsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lbsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lbsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    L = lbsa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert getattr(L, n) is not None
+
+
+def test_version_and_status_strings():
+    assert lbsa.lib().lbsa_version() == 100
+    assert lbsa.status_string(0) == "ok"
+    assert "invalid" in lbsa.status_string(-1)
+    assert "unsupported" in lbsa.status_string(-2)
+
+
+def test_task_map_layout_is_aligned_and_sized():
+    for B, Hkv, P in [(4, 1, 32), (64, 8, 768), (1, 8, 2048), (8, 8, 512)]:
+        lay = lbsa.task_map_layout(B, Hkv, P)
+        S, cap = B * Hkv, B * Hkv + P
+        assert lay["header"] == 0 and lay["bin_desc_begin"] == 64
+        assert lay["desc"] % 16 == 0 and lay["desc"] >= 64 + 4 * (P + 1)
+        assert lay["seg_first_desc"] == lay["desc"] + 16 * cap
+        assert lay["seg_num_chunks"] == lay["seg_first_desc"] + 4 * S
+        assert lay["seqlens"] == lay["seg_num_chunks"] + 4 * S
+        assert lay["total"] >= lay["seqlens"] + 4 * B and lay["total"] % 256 == 0
+        assert lbsa.task_map_bytes(B, Hkv, P) == lay["total"]
+
+
+def test_workspace_layout():
+    w = lbsa.workspace_layout(64, 64, 8, 768)
+    cap = 64 * 8 + 768
+    assert w["part_o"] >= 4 * 8 * cap and w["part_o"] % 256 == 0
+    assert w["total"] >= w["part_o"] + 4 * 8 * 128 * cap
+    assert lbsa.static_workspace_bytes(64, 64, 8, 4) >= 4 * 8 * 129 * 64 * 8 * 4
+
+
+def _plan_status(**kw):
+    a = dict(seqlens=ctypes.c_void_p(16), B=4, Hq=8, Hkv=1, page=64, mp=65, P=32, F=0,
+             map=ctypes.c_void_p(256), nbytes=1 << 20, stream=None)
+    a.update(kw)
+    return lbsa.lib().lbsa_plan(a["seqlens"], a["B"], a["Hq"], a["Hkv"], a["page"], a["mp"], a["P"], a["F"],
+                                a["map"], a["nbytes"], a["stream"])
+
+
+def test_plan_rejects_bad_arguments_on_host():
+    assert _plan_status(seqlens=None) == lbsa.ERR_INVALID_ARGUMENT
+    assert _plan_status(map=None) == lbsa.ERR_INVALID_ARGUMENT
+    assert _plan_status(B=0) == lbsa.ERR_INVALID_ARGUMENT
+    assert _plan_status(Hq=12, Hkv=8) == lbsa.ERR_INVALID_ARGUMENT      # Hq % Hkv != 0
+    assert _plan_status(Hq=16, Hkv=1) == lbsa.ERR_UNSUPPORTED           # group 16
+    assert _plan_status(page=32) == lbsa.ERR_UNSUPPORTED
+    assert _plan_status(P=0) == lbsa.ERR_INVALID_ARGUMENT
+    assert _plan_status(F=-1) == lbsa.ERR_INVALID_ARGUMENT
+    assert _plan_status(nbytes=100) == lbsa.ERR_INVALID_ARGUMENT        # map too small
+    assert _plan_status(map=ctypes.c_void_p(8)) == lbsa.ERR_INVALID_ARGUMENT   # misaligned
+    assert _plan_status(B=9000, Hq=8, Hkv=1) == lbsa.ERR_UNSUPPORTED    # LDS of the assign workgroup
+
+
+def _decode_status(**kw):
+    a = dict(q=16, qs=None, k=256, v=512, ks=None, vs=None, dt=0, pt=1024, B=4, Hq=8, Hkv=1, D=128, page=64,
+             mp=65, npages=100, P=32, scale=0.088, map=4096, mapb=1 << 20, ws=1 << 16, wsb=1 << 30, out=8192)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lbsa.lib().lbsa_decode(vp(a["q"]), vp(a["qs"]), vp(a["k"]), vp(a["v"]), vp(a["ks"]), vp(a["vs"]),
+                                  a["dt"], vp(a["pt"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["page"], a["mp"],
+                                  a["npages"], a["P"], a["scale"], vp(a["map"]), a["mapb"], vp(a["ws"]),
+                                  a["wsb"], vp(a["out"]), None)
+
+
+def test_decode_rejects_bad_arguments_on_host():
+    assert _decode_status(q=None) == lbsa.ERR_INVALID_ARGUMENT
+    assert _decode_status(D=64) == lbsa.ERR_UNSUPPORTED
+    assert _decode_status(dt=7) == lbsa.ERR_INVALID_ARGUMENT
+    assert _decode_status(dt=1) == lbsa.ERR_INVALID_ARGUMENT              # fp8 without scales
+    assert _decode_status(mapb=64) == lbsa.ERR_INVALID_ARGUMENT           # map too small
+    assert _decode_status(wsb=64) == lbsa.ERR_INVALID_ARGUMENT            # workspace too small
+    assert _decode_status(ws=(1 << 16) + 4) == lbsa.ERR_INVALID_ARGUMENT  # misaligned workspace
+    assert _decode_status(k=260) == lbsa.ERR_INVALID_ARGUMENT             # misaligned cache
+    assert _decode_status(npages=0) == lbsa.ERR_INVALID_ARGUMENT
+    assert _decode_status(out=None) == lbsa.ERR_INVALID_ARGUMENT
+    assert _decode_status(scale=float("nan")) == lbsa.ERR_INVALID_ARGUMENT
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(lbsa, "_lib", None)
+    monkeypatch.setattr(lbsa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        lbsa.lib()

@@ -1,0 +1,178 @@
+"""GPU split + combine vs the fp64 oracle, and properties of the path.
+
+Tolerances: max |out - oracle| <= 2e-2 for bf16 KV and <= 6e-2 for fp8-e4m3 KV
+(bf16 output); partials: O within the same bound, LSE within 1e-3.  Every
+input comes from the seeded generator with NaN in the tail slots of each last
+page, so a masked token that leaks shows up as NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import _gpu_helpers as H
+from _gpu_helpers import requires_gpu
+from load_balanced_split_assign_amd import lbsa
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def check_full(oracle_mod, batch, out, what):
+    ref, _ = oracle_mod.attention(batch)
+    got = H.out_np(out)
+    assert np.isfinite(got).all(), what
+    err = np.abs(got - ref).max()
+    assert err <= H.tol(batch), (what, err)
+    return err
+
+
+def check_rows(oracle_mod, batch, out, rows, what):
+    ref, _ = oracle_mod.attention_rows(batch, rows)
+    got = H.out_np(out)[rows[:, 0], rows[:, 1]]
+    assert np.isfinite(got).all(), what
+    err = np.abs(got - ref).max()
+    assert err <= H.tol(batch), (what, err)
+    return err
+
+
+@pytest.mark.parametrize("name", ["tiny", "floor", "t3_32x0.125K+32x4K", "t3_1x64K+15x4K"])
+def test_small_workloads_full_parity(oracle_mod, name):
+    batch = H.batch_on_gpu(name)
+    P = H.workgroups(batch)
+    tm = H.plan(batch, P)
+    out = H.decode(batch, tm, P)
+    check_full(oracle_mod, batch, out, name)
+
+
+def test_tp8_share_full_parity(oracle_mod):
+    batch = H.batch_on_gpu("tp8_share")
+    P = H.workgroups(batch)
+    out = H.decode(batch, H.plan(batch, P), P)
+    check_full(oracle_mod, batch, out, "tp8_share")
+
+
+@pytest.mark.parametrize("name", ["skewed", "fp8", "long"])
+def test_large_workloads_sampled_parity(oracle_mod, name):
+    batch = H.batch_on_gpu(name, gen_device="cuda:0")
+    P = H.workgroups(batch)
+    out = H.decode(batch, H.plan(batch, P), P)
+    got = H.out_np(out)
+    assert np.isfinite(got).all()
+    rows = H.sample_rows(batch, n_requests=5 if name == "long" else 8)
+    check_rows(oracle_mod, batch, out, rows, name)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_partials_match_oracle(oracle_mod, kv):
+    batch = H.batch_on_gpu(dict(seqlens=[37, 64, 1000, 4097, 1, 130], num_heads=16, num_kv_heads=2,
+                                kv_dtype=kv, seed=21))
+    P = 29
+    tm = H.plan(batch, P)
+    ws = H.decode_split(batch, tm, P)
+    m = lbsa.read_task_map(tm, batch["B"], batch["num_kv_heads"], P)
+    po, pl = lbsa.read_partials(ws, batch["B"], batch["num_heads"], batch["num_kv_heads"], P, m["Ndesc"])
+    ro, rl = oracle_mod.partials(batch, m["desc"])
+    assert np.isfinite(po).all() and np.isfinite(pl).all()
+    assert np.abs(po - ro).max() <= H.tol(batch)
+    assert np.abs(pl - rl).max() <= H.LSE_TOL
+
+
+@pytest.mark.parametrize("P", [1, 3, 64, 1000, 4096])
+@pytest.mark.parametrize("F", [0, 1, 5])
+def test_any_workgroup_count_and_floor(oracle_mod, P, F):
+    batch = H.batch_on_gpu(dict(seqlens=[5, 3000, 64, 700, 0, 129], num_heads=16, num_kv_heads=2,
+                                kv_dtype="bf16", seed=22))
+    out = H.decode(batch, H.plan(batch, P, F), P)
+    check_full(oracle_mod, batch, out, (P, F))
+
+
+def test_fp8_mixed_lengths(oracle_mod):
+    batch = H.batch_on_gpu(dict(seqlens=[1, 63, 64, 65, 2047, 5000, 130, 17], num_heads=64, num_kv_heads=8,
+                                kv_dtype="fp8", seed=23))
+    P = H.workgroups(batch)
+    out = H.decode(batch, H.plan(batch, P), P)
+    check_full(oracle_mod, batch, out, "fp8 mixed")
+
+
+def test_empty_requests_give_zero_rows(oracle_mod):
+    batch = H.batch_on_gpu(dict(seqlens=[0, 100, 0, 7], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=24))
+    P = 40
+    out = H.decode(batch, H.plan(batch, P), P)
+    got = H.out_np(out)
+    assert (got[0] == 0).all() and (got[2] == 0).all()
+    check_full(oracle_mod, batch, out, "empty rows")
+
+
+def test_deterministic_and_workspace_fully_overwritten():
+    batch = H.batch_on_gpu("tp8_share")
+    P = H.workgroups(batch)
+    tm = H.plan(batch, P)
+    ws = torch.full((lbsa.workspace_bytes(batch["B"], 8, 1, P) // 4,), float("nan"), device="cuda:0")
+    a = H.decode(batch, tm, P, workspace=ws.view(torch.uint8)).clone()
+    ws.fill_(float("nan"))
+    b = H.decode(batch, tm, P, workspace=ws.view(torch.uint8)).clone()
+    c = H.decode(batch, tm, P).clone()
+    torch.cuda.synchronize()
+    assert torch.isfinite(a.float()).all()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_page_permutation_invariance():
+    batch = H.batch_on_gpu(dict(seqlens=[300, 4097, 64, 1], num_heads=16, num_kv_heads=2, kv_dtype="fp8",
+                                seed=25))
+    P = 50
+    tm = H.plan(batch, P)
+    a = H.decode(batch, tm, P).clone()
+    perm = torch.randperm(batch["num_pages"], generator=torch.Generator().manual_seed(5)).to("cuda:0")
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(perm.numel(), device="cuda:0")
+    b2 = dict(batch)
+    for k in ("k_cache", "v_cache", "k_scale", "v_scale"):
+        b2[k] = batch[k][perm].contiguous()
+    pt = batch["page_table"].clone()
+    m = pt >= 0
+    pt[m] = inv[pt[m].long()].to(torch.int32)
+    b2["page_table"] = pt
+    b = H.decode(b2, tm, P)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_map_reused_across_layers(oracle_mod):
+    """One plan per step, many layers: two layers with different K/V."""
+    l1 = H.batch_on_gpu(dict(seqlens=[900, 33, 2000], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=26))
+    l2 = H.batch_on_gpu(dict(seqlens=[900, 33, 2000], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=27))
+    P = 70
+    tm = H.plan(l1, P)
+    o1 = H.decode(l1, tm, P).clone()
+    o2 = H.decode(l2, tm, P).clone()
+    check_full(oracle_mod, l1, o1, "layer 1")
+    check_full(oracle_mod, l2, o2, "layer 2")
+
+
+def test_bad_page_id_poisons_only_its_rows():
+    batch = H.batch_on_gpu(dict(seqlens=[200, 300, 100], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=28))
+    batch["page_table"][1, 2] = batch["num_pages"] + 5          # out of range: never read
+    P = 9
+    out = H.out_np(H.decode(batch, H.plan(batch, P), P))
+    assert np.isnan(out[1]).all()
+    assert np.isfinite(out[0]).all() and np.isfinite(out[2]).all()
+
+
+def test_bad_length_gives_error_flag_and_zero_output():
+    batch = H.batch_on_gpu(dict(seqlens=[200, 300], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=29))
+    batch["seqlens"][1] = 64 * batch["max_pages"] + 1
+    P = 9
+    tm = H.plan(batch, P)
+    out = H.out_np(H.decode(batch, tm, P))
+    assert lbsa.read_task_map(tm, 2, 1, P)["error"] == 1
+    assert (out == 0).all()
+
+
+def test_mismatched_map_poisons_output():
+    batch = H.batch_on_gpu(dict(seqlens=[200, 300], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=30))
+    tm = H.plan(batch, 16)
+    big = torch.zeros(lbsa.task_map_bytes(2, 1, 32), dtype=torch.uint8, device="cuda:0")
+    big[:tm.numel()] = tm                                          # map built for P = 16, used with P = 32
+    out = H.out_np(H.decode(batch, big, 32))
+    assert np.isnan(out).all()
