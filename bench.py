@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
+CALIB_BYTES = 256 << 20
 SPLIT_SRC = os.path.join(ROOT, "load_balanced_split_assign_amd", "csrc", "lbsa_attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
 
@@ -125,6 +126,29 @@ def time_steps(path, steps, warmup, flush):
     torch.cuda.synchronize()
     us = lambda a, b: [1000.0 * ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)]  # noqa: E731
     return {"assign": us(0, 1), "split": us(1, 2), "combine": us(2, 3), "layer": us(1, 3), "step": us(0, 3)}
+
+
+def time_steps_graph(path, steps, warmup, flush):
+    """Per-step times (us) of the assign + split + combine sequence captured in
+    one HIP graph and replayed (the flush runs eagerly between replays)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        path.assign(); path.split(); path.combine()
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        flush(i)
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        flush(i)
+        ev[i][0].record(stream)
+        g.replay()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [1000.0 * a.elapsed_time(b) for a, b in ev]
 
 
 def time_static(batch, S, steps, warmup, flush):
@@ -229,6 +253,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
                     help="cache eviction before each timed step")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 256 MiB device copy first (reference for PMC byte counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (bounded sample)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -240,6 +266,14 @@ def main():
 
     from load_balanced_split_assign_amd import lbsa
     from load_balanced_split_assign_amd import workload as wl
+
+    if args.calib_copy:   # a plain copy of known size: FETCH_SIZE / WRITE_SIZE reference
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     name = args.workload
     w = wl.WORKLOADS[name]

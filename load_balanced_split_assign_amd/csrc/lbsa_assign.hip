@@ -19,7 +19,7 @@
 //   chunks(s) = bin_of(last tile of s) - bin_of(first tile of s) + 1,
 // descriptor slots are the exclusive prefix of chunks(s) in (h, b) order, and
 // descriptor d is reconstructed independently by a binary search over that
-// prefix.  Every step is a scan or a search, so 1024 threads share the work.
+// prefix.  Every step is a scan or a search, so the 256 threads share the work.
 #include "lbsa_internal.h"
 
 namespace lbsa {
@@ -92,25 +92,28 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     int* sfd = smem + B + 1;       // [S + 1]  exclusive prefix of chunks(s)
     const int tid = threadIdx.x;
 
-    // ---- validate lengths (a bad length empties the map) -------------------
-    int bad = 0;
-    for (int b = tid; b < B; b += kAssignThreads) {
-        const int len = seqlens[b];
-        sl_g[b] = len;
-        bad |= (len < 0) || ((long long)len > (long long)max_pages * kTile);
-    }
-    const int error = __syncthreads_or(bad);
-
-    // ---- tile census: n_b = ceil(L_b / 64), exclusive prefix over b ---------
+    // ---- tile census: n_b = ceil(L_b / 64) (one pass over the lengths, n_b
+    // stashed in LDS), validation, exclusive prefix over b -------------------
     const int per = (B + kAssignThreads - 1) / kAssignThreads;
     const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-    int local = 0;
-    for (int b = b0; b < b1; ++b) local += error ? 0 : (seqlens[b] + kTile - 1) / kTile;
+    int bad = 0, local = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int len = seqlens[b];
+        sl_g[b] = len;
+        const bool ok = len >= 0 && (long long)len <= (long long)max_pages * kTile;
+        bad |= !ok;
+        const int nb = ok ? (len + kTile - 1) / kTile : 0;
+        prefix[b] = nb;
+        local += nb;
+    }
+    const int error = __syncthreads_or(bad);   // a bad length empties the map
+    if (error) local = 0;
     int N;
     int run = block_exclusive_scan(local, red, &N);
     for (int b = b0; b < b1; ++b) {
+        const int nb = error ? 0 : prefix[b];
         prefix[b] = run;
-        run += error ? 0 : (seqlens[b] + kTile - 1) / kTile;
+        run += nb;
     }
     if (tid == 0) prefix[B] = N;
     __syncthreads();

@@ -12,30 +12,33 @@
 // gfx950 mapping.  One split workgroup = 4 wave64 serving all 8 query heads of
 // one KV head; wave w owns tokens [16w, 16w + 16) of every 64-token tile.
 //   * Tile stream: a workgroup's bin is one stream of tiles across all of its
-//     descriptors.  Each wave keeps a private ring of kStages LDS stages and
-//     fills it with asynchronous global->LDS loads (global_load_lds_dwordx4):
-//     while tile k is computed, tiles k+1 .. k+kStages-1 are in flight, also
-//     across descriptor boundaries, so the memory pipe never drains inside a
-//     bin.  The compiler does not track these LDS writes; the kernel waits
-//     for each stage itself with s_waitcnt vmcnt(N), N = loads issued after
-//     that stage (vector memory operations complete in order).
-//   * Loads are coalesced: each 64-lane load moves whole 256-byte K/V rows
-//     (4 rows per instruction for bf16, 8 rows of 128 B for fp8).  Inside a
-//     row the 16-byte chunks are XOR-swizzled by the row index, so the MFMA
-//     operand reads (16 rows, same column) hit 16 different LDS bank groups.
-//   * Rows past the live length are fetched from the tile's first row (always
+//     descriptors.  Each wave keeps a private ring of LDS stages and fills it
+//     with asynchronous global->LDS loads (global_load_lds): while tile k is
+//     computed, the next stages' tiles are in flight, also across descriptor
+//     boundaries, so the memory pipe never drains inside a bin.  The kernel
+//     waits for each stage itself with s_waitcnt vmcnt(N), N = loads issued
+//     after that stage (vector memory operations complete in order).
+//   * Loads are coalesced: each 64-lane load moves whole K/V rows (4 rows of
+//     256 B for bf16, 8 rows of 128 B for fp8) from a uniform page base plus a
+//     per-lane offset fixed for the whole stream.  Inside a row the 16-byte
+//     chunks are XOR-swizzled by the row index, so the MFMA operand reads (16
+//     rows, same column) hit 16 different LDS bank groups.
+//   * Rows past the live length are fetched from the page's first row (always
 //     live) instead, so no tail garbage or NaN ever reaches LDS; their scores
 //     are masked to -inf, so they contribute nothing.
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows = 16 tokens, columns =
-//     16 query heads of which 8 are real), fp32 accumulation; online softmax
-//     per wave in the exp2 domain.
-//   * O^T += V^T P^T with v_mfma_f32_16x16x16_bf16: V^T comes from LDS through
+//   * S^T = K Q^T with MFMA 16x16x32 (rows = 16 tokens, columns = 16 query
+//     heads of which 8 are real), fp32 accumulation in two independent
+//     chains: bf16 operands for bf16 KV, the fp8 MFMA on the raw e4m3 codes of
+//     K and Q for fp8 KV (the per-token K scale and per-head Q scale multiply
+//     the score).
+//   * Online softmax in the exp2 domain with a lazy running max: a tile whose
+//     scores stay within kSlack of the running max is exponentiated against
+//     it directly; only when a wave-wide ballot finds a larger score does the
+//     wave reduce the max across lanes and rescale its accumulators.
+//   * O^T += V^T P^T with MFMA 16x16x16 bf16: V^T comes from LDS through
 //     ds_read_b64_tr_b16, P straight from the S^T accumulator registers (its
-//     layout is already the B operand).
-//   * fp8 (OCP e4m3fn) K is widened to bf16 in registers (v_cvt_f32_fp8 +
-//     v_perm_b32, exact), fp8 V is widened into a bf16 LDS area before the
-//     transposed reads; the per-token K scale multiplies the score column and
-//     the per-token V scale is folded into p before PV.
+//     layout is already the B operand).  fp8 V is widened exactly into a bf16
+//     LDS copy first; the per-token V scale is folded into p.
 //   * At the end of a descriptor the 4 waves merge (max, sum, O) through LDS
 //     and one partial (fp32 O normalised, natural-log LSE) is written.
 #include "lbsa_internal.h"
@@ -49,23 +52,23 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) float lds_float;
 
 constexpr int kWaves = kSplitThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kSlack = 8.0f;   // log2 headroom of the lazy running max (p <= 256)
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline uint4 lds_load16(const lds_char* p) {
     return __builtin_bit_cast(uint4, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p));
 }
-__device__ inline uint2 lds_load8(const lds_char* p) {
-    return __builtin_bit_cast(uint2, *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(p));
-}
 __device__ inline void lds_store16(lds_char* p, uint4 v) {
     *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(p) = __builtin_bit_cast(u32x4, v);
 }
+__device__ inline uint32_t lds_addr(const lds_char* p) { return (uint32_t)(size_t)p; }
 
 __device__ inline uint32_t bf16x2_bits(float lo, float hi) {
     __bf16 a = (__bf16)lo, b = (__bf16)hi;          // round to nearest even
@@ -73,23 +76,23 @@ __device__ inline uint32_t bf16x2_bits(float lo, float hi) {
 }
 
 // 4 e4m3fn codes (one dword) -> 4 bf16 (two dwords); exact, since every e4m3
-// value has at most 4 significant bits.  Each byte is widened on its own
-// (v_cvt_f32_fp8 with a byte select) and the upper halves of two fp32 results
-// are packed with v_perm_b32.  (Taking the second element of the packed
-// two-byte convert and masking it was miscompiled by this toolchain: the
-// packing read element 0 twice.)
+// value has at most 4 significant bits.  Two packed converts (bytes 0-1 and
+// 2-3 to fp32 pairs) and two byte permutes keeping the upper halves.  The
+// converts are written as asm: through the builtin, this toolchain
+// miscompiled the use of the pair's second element (it read element 0 twice).
 __device__ inline uint2 fp8x4_to_bf16x4(uint32_t w) {
-    const uint32_t f0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 0));
-    const uint32_t f1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 1));
-    const uint32_t f2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 2));
-    const uint32_t f3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 3));
+    uint64_t lo, hi;
+    __asm__("v_cvt_pk_f32_fp8_e32 %0, %2\n\t"
+            "v_cvt_pk_f32_fp8_sdwa %1, %2 src0_sel:WORD_1"
+            : "=&v"(lo), "=&v"(hi)
+            : "v"(w));
     uint2 r;
-    r.x = __builtin_amdgcn_perm(f1, f0, 0x07060302u);   // {f0.hi16, f1.hi16}
-    r.y = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    r.x = __builtin_amdgcn_perm((uint32_t)(lo >> 32), (uint32_t)lo, 0x07060302u);   // {e0.hi16, e1.hi16}
+    r.y = __builtin_amdgcn_perm((uint32_t)(hi >> 32), (uint32_t)hi, 0x07060302u);
     return r;
 }
 
-// 8 e4m3 codes (two dwords) -> 8 bf16 (one 16-byte operand).
+// 8 e4m3 codes (two dwords) -> 8 bf16 (16 bytes).
 __device__ inline uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
     uint2 a = fp8x4_to_bf16x4(w0), b = fp8x4_to_bf16x4(w1);
     return make_uint4(a.x, a.y, b.x, b.y);
@@ -104,61 +107,25 @@ __device__ inline const __attribute__((address_space(4))) T* uniform_ptr(const v
     return (const __attribute__((address_space(4))) T*)(p);
 }
 
-// s_waitcnt vmcnt(n) with the LDS and export counters left unconstrained,
-// followed by a compiler barrier so no LDS access moves above it.
+// s_waitcnt vmcnt(N) with the LDS and export counters left unconstrained,
+// fenced for the compiler so no LDS access moves above it.
 template <int N>
 __device__ inline void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
     __asm__ volatile("" ::: "memory");
 }
 
-// ---------------------------------------------------------------------------
-// Per-wave LDS ring stage.  bf16: K 16 x 256 B, V 16 x 256 B; fp8: K 16 x 128 B,
-// V 16 x 128 B, scales (k[16], v[16], q[8]).  The group's Q rows (8 x 256 B or
-// 8 x 128 B) of each stage live in a separate array.
-// ---------------------------------------------------------------------------
-template <bool FP8> struct Stage {
-    static constexpr int kRow = FP8 ? 128 : 256;        // bytes of one K/V/Q row
-    static constexpr int K = 0;
-    static constexpr int V = 16 * kRow;
-    static constexpr int SC = 32 * kRow;                // fp8 only
-    static constexpr int BYTES = SC + (FP8 ? 256 : 0);   // 8192 (bf16) / 4352 (fp8)
-    static constexpr int Q_BYTES = 8 * kRow;              // Q rows of the group, own array per stage
-    static constexpr int LOADS = FP8 ? 6 : 10;          // Q, K, V (and scale) loads issued per tile
-    static constexpr int STAGES = FP8 ? 4 : 3;          // ring depth
-    static constexpr int VB = FP8 ? 16 * 256 : 0;       // fp8: bf16 copy of the V slice
-};
-
-// 16-byte chunk swizzle inside a row: LDS chunk c' holds row chunk c' ^ f(row).
-template <bool FP8> __device__ inline int swz(int row) { return FP8 ? ((row >> 1) & 7) : (row & 15); }
-__device__ inline int swz_bf16(int row) { return row & 15; }
-
-// LDS of one split / static workgroup.  Every ring stage is its own
-// __shared__ object: the compiler's wait-count insertion can then tell which
-// asynchronous load an LDS read depends on (distinct underlying objects) and
-// does not fall back to waiting for all of them.
-constexpr int kMergeWave = (kGroup * kHeadDim + 2 * kGroup + 4) * 4;   // O, m, l, flag per wave
-constexpr int kMergeBytes = kWaves * kMergeWave;
-template <bool FP8> struct Smem {
-    lds_char* stage[4];   // [kWaves][Stage::BYTES] each; the first STAGES are used
-    lds_char* qst[4];     // [kWaves][Stage::Q_BYTES] each
-    lds_char* vb;         // fp8: [kWaves][4096] bf16 copy of the V slice
-    lds_char* merge;      // [kMergeBytes]
-};
-template <bool FP8> constexpr int stage_array_bytes(int u) {
-    return u < Stage<FP8>::STAGES ? kWaves * Stage<FP8>::BYTES : 16;
+// Workgroup barrier for LDS exchange only.  __syncthreads() also fences
+// global memory, which would wait for every asynchronous load in flight; the
+// merge only needs this wave's LDS writes done (lgkmcnt(0)) before s_barrier.
+__device__ inline void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0), vmcnt(63)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
 }
-template <bool FP8> constexpr int q_array_bytes(int u) {
-    return u < Stage<FP8>::STAGES ? kWaves * Stage<FP8>::Q_BYTES : 16;
-}
-constexpr int kVbBytes = kWaves * 16 * 256;
-
-// One descriptor of the tile stream (all fields wave-uniform).
-struct Desc {
-    int h, b, t0, t1, L;
-    int64_t slot;
-};
 
 // Asynchronous global -> LDS loads: lane i's 16 (or 4) bytes land at
 // lds + 16 i (or 4 i).  Non-template wrappers keep the target builtin out of
@@ -170,56 +137,14 @@ __device__ inline void dma4(const void* g, lds_char* l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
 }
 
-// Issue the asynchronous loads of one tile into `st` (this wave's 16-token
-// slice of page `page`): K and V rows (whole rows, chunk-swizzled), the fp8
-// scales, and -- for the first tile of a descriptor -- the group's Q rows.
-template <bool FP8>
-__device__ inline void issue_tile(const AttnArgs& a, lds_char* __restrict__ st, lds_char* __restrict__ qs,
-                                  int64_t page, const Desc& d, int tile, int w, int lane) {
-    using SL = Stage<FP8>;
-    constexpr size_t kRow = SL::kRow;
-    const int tok0 = 64 * tile;
-    const char* kc = static_cast<const char*>(a.k_cache);
-    const char* vc = static_cast<const char*>(a.v_cache);
-    {   // the group's Q rows, every tile (uniform load count; only a descriptor's first tile reads them)
-        const char* q = static_cast<const char*>(a.q) + ((size_t)d.b * a.Hq + (size_t)d.h * kGroup) * kRow;
-        if constexpr (!FP8) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)      // 4 heads x 256 B per load
-                dma16(q + 1024 * s + 16 * lane, qs + 1024 * s);
-        } else {                             // 8 heads x 128 B
-            dma16(q + 16 * lane, qs);
-        }
-    }
-    constexpr int kRowsPerLoad = 1024 / kRow;          // 4 (bf16) or 8 (fp8)
-    constexpr int kChunks = kRow / 16;
-#pragma unroll
-    for (int s = 0; s < 16 / kRowsPerLoad; ++s) {
-        const int row = kRowsPerLoad * s + lane / kChunks;        // row of this wave's slice
-        const int cl = lane % kChunks;                            // LDS chunk
-        const int trow = (tok0 + 16 * w + row < d.L) ? 16 * w + row : 0;   // dead rows read row 0
-        const size_t goff = (((size_t)page * kTile + trow) * a.Hkv + d.h) * kRow + 16 * (cl ^ swz<FP8>(row));
-        dma16(kc + goff, st + SL::K + 1024 * s);
-        dma16(vc + goff, st + SL::V + 1024 * s);
-    }
-    if constexpr (FP8) {
-        // lanes 0-15: k scale of rows 0-15, 16-31: v scale, 32-39: q scale of the group
-        const int row = lane & 15;
-        const int trow = (tok0 + 16 * w + row < d.L) ? 16 * w + row : 0;
-        const size_t sidx = ((size_t)page * a.Hkv + d.h) * kTile + trow;
-        const float* src = lane < 16 ? a.k_scale + sidx
-                         : lane < 32 ? a.v_scale + sidx
-                                     : a.q_scale + (size_t)d.b * a.Hq + (size_t)d.h * kGroup + (lane & 7);
-        dma4(src, st + SL::SC);
-    }
-}
-
-// The 8 transposed V reads of one tile (one per 16-wide d block), issued
-// together and completed (lgkmcnt(0)) before returning.  Written as one asm
-// block: the compiler models the transposed-read intrinsic without the LDS
-// alias information it uses for ordinary LDS loads, and would otherwise wait
-// for every asynchronous load in flight before each of them.  The LDS data
-// they read is ordered by the caller's explicit vmcnt wait (memory clobber).
+// LDS accesses to the ring are written as small asm blocks that complete
+// before returning (s_waitcnt lgkmcnt(0)).  The compiler does not see them as
+// LDS accesses, so it adds no wait of its own for the asynchronous loads in
+// flight (its alias reasoning about those loads is conservative and falls
+// back to waiting for all of them); their ordering after the loads is the
+// caller's explicit vmcnt wait, and the memory clobbers keep program order.
+//
+// The 8 transposed V reads of one tile (one per 16-wide d block).
 __device__ inline void vt_read8(s16x4 (&va)[8], const uint32_t (&addr)[8]) {
     typedef short s16x4_v __attribute__((ext_vector_type(4)));
     s16x4_v o0, o1, o2, o3, o4, o5, o6, o7;
@@ -247,9 +172,7 @@ __device__ inline void vt_read8(s16x4 (&va)[8], const uint32_t (&addr)[8]) {
     va[7] = __builtin_bit_cast(s16x4, o7);
 }
 
-// Two 16-byte LDS reads completed before returning (asm for the same reason
-// as vt_read8: the fp8 V rows come from asynchronous loads ordered by the
-// caller's explicit vmcnt wait).
+// Two 16-byte LDS reads completed before returning.
 __device__ inline void lds_read2x16(uint4& x, uint4& y, uint32_t ax, uint32_t ay) {
     u32x4 ox, oy;
     __asm__ volatile(
@@ -263,75 +186,301 @@ __device__ inline void lds_read2x16(uint4& x, uint4& y, uint32_t ax, uint32_t ay
     y = __builtin_bit_cast(uint4, oy);
 }
 
+// Four 16-byte LDS reads completed before returning.
+__device__ inline void lds_read4x16(uint4 (&o)[4], const uint32_t (&addr)[4]) {
+    u32x4 o0, o1, o2, o3;
+    __asm__ volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3)
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+        : "memory");
+    o[0] = __builtin_bit_cast(uint4, o0);
+    o[1] = __builtin_bit_cast(uint4, o1);
+    o[2] = __builtin_bit_cast(uint4, o2);
+    o[3] = __builtin_bit_cast(uint4, o3);
+}
+
+// One 4-byte LDS read completed before returning.
+__device__ inline float lds_read_f32(uint32_t addr) {
+    float o;
+    __asm__ volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(o) : "v"(addr) : "memory");
+    return o;
+}
+
+// Four 16-byte LDS writes (the fp8 V copy), ordered by program order with the
+// asm reads around them.
+__device__ inline void lds_write4x16(const uint32_t (&addr)[4], const uint4 (&v)[4]) {
+    __asm__ volatile(
+        "ds_write_b128 %0, %4\n\t"
+        "ds_write_b128 %1, %5\n\t"
+        "ds_write_b128 %2, %6\n\t"
+        "ds_write_b128 %3, %7"
+        :
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(__builtin_bit_cast(u32x4, v[0])),
+          "v"(__builtin_bit_cast(u32x4, v[1])), "v"(__builtin_bit_cast(u32x4, v[2])),
+          "v"(__builtin_bit_cast(u32x4, v[3]))
+        : "memory");
+}
+
+// bf16 tile: the 4 K-operand reads and the 8 transposed V reads in one block.
+__device__ inline void lds_read_tile_bf16(uint4 (&k)[4], s16x4 (&va)[8], const uint32_t (&ka)[4],
+                                          const uint32_t (&va_addr)[8]) {
+    typedef short s16x4_v __attribute__((ext_vector_type(4)));
+    u32x4 k0, k1, k2, k3;
+    s16x4_v o0, o1, o2, o3, o4, o5, o6, o7;
+    __asm__ volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\t"
+        "ds_read_b64_tr_b16 %4, %16\n\t"
+        "ds_read_b64_tr_b16 %5, %17\n\t"
+        "ds_read_b64_tr_b16 %6, %18\n\t"
+        "ds_read_b64_tr_b16 %7, %19\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %21\n\t"
+        "ds_read_b64_tr_b16 %10, %22\n\t"
+        "ds_read_b64_tr_b16 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3), "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3), "=&v"(o4),
+          "=&v"(o5), "=&v"(o6), "=&v"(o7)
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va_addr[0]), "v"(va_addr[1]), "v"(va_addr[2]),
+          "v"(va_addr[3]), "v"(va_addr[4]), "v"(va_addr[5]), "v"(va_addr[6]), "v"(va_addr[7])
+        : "memory");
+    k[0] = __builtin_bit_cast(uint4, k0);
+    k[1] = __builtin_bit_cast(uint4, k1);
+    k[2] = __builtin_bit_cast(uint4, k2);
+    k[3] = __builtin_bit_cast(uint4, k3);
+    va[0] = __builtin_bit_cast(s16x4, o0);
+    va[1] = __builtin_bit_cast(s16x4, o1);
+    va[2] = __builtin_bit_cast(s16x4, o2);
+    va[3] = __builtin_bit_cast(s16x4, o3);
+    va[4] = __builtin_bit_cast(s16x4, o4);
+    va[5] = __builtin_bit_cast(s16x4, o5);
+    va[6] = __builtin_bit_cast(s16x4, o6);
+    va[7] = __builtin_bit_cast(s16x4, o7);
+}
+
+// fp8 tile: the two K chunks, the two V chunks and the k/v scales in one block.
+__device__ inline void lds_read_tile_fp8(uint4 (&o)[6], const uint32_t (&addr)[6]) {
+    u32x4 o0, o1, o2, o3, o4, o5;
+    __asm__ volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b128 %2, %8\n\t"
+        "ds_read_b128 %3, %9\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3), "=&v"(o4), "=&v"(o5)
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5])
+        : "memory");
+    o[0] = __builtin_bit_cast(uint4, o0);
+    o[1] = __builtin_bit_cast(uint4, o1);
+    o[2] = __builtin_bit_cast(uint4, o2);
+    o[3] = __builtin_bit_cast(uint4, o3);
+    o[4] = __builtin_bit_cast(uint4, o4);
+    o[5] = __builtin_bit_cast(uint4, o5);
+}
+
+// ---------------------------------------------------------------------------
+// Per-wave LDS ring stage.  bf16: K 16 x 256 B, V 16 x 256 B.  fp8: K 16 x 128
+// B, V 16 x 128 B, k scales (256 B: rows 0-15, then copies), v scales (256 B).
+// ---------------------------------------------------------------------------
+template <bool FP8> struct Stage {
+    static constexpr int kRow = FP8 ? 128 : 256;        // bytes of one K/V row
+    static constexpr int K = 0;
+    static constexpr int V = 16 * kRow;
+    static constexpr int KS = 32 * kRow;                // fp8 only
+    static constexpr int VS = KS + 256;                 // fp8 only
+    static constexpr int BYTES = FP8 ? VS + 256 : 32 * kRow;      // 4608 (fp8) / 8192 (bf16)
+    static constexpr int KV_LOADS = 16 * kRow / 1024;   // loads per K (or V) slice: 4 (bf16) / 2 (fp8)
+    static constexpr int LOADS = 2 * KV_LOADS + (FP8 ? 2 : 0);   // ring loads issued per tile
+    static constexpr int STAGES = FP8 ? 6 : 4;          // ring depth: STAGES - 1 tiles in flight
+};
+static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt range");
+static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
+
+// 16-byte chunk swizzle inside a row: LDS chunk c' holds row chunk c' ^ f(row).
+template <bool FP8> __device__ inline int swz(int row) { return FP8 ? ((row >> 1) & 7) : (row & 15); }
+__device__ inline int swz_bf16(int row) { return row & 15; }
+
+// LDS of one split / static workgroup.  Every ring stage is its own
+// __shared__ object: the compiler's wait-count insertion can then tell which
+// asynchronous load an LDS read depends on (distinct underlying objects) and
+// does not fall back to waiting for all of them.
+constexpr int kMergeWave = (kGroup * kHeadDim + 2 * kGroup + 4) * 4;   // O, m, l, flag per wave
+constexpr int kMergeBytes = kWaves * kMergeWave;
+constexpr int kVbBytes = kWaves * 16 * 256;
+constexpr int kMaxStages = 6;
+template <bool FP8> struct Smem {
+    lds_char* stage[kMaxStages];   // [kWaves][Stage::BYTES] each; the first STAGES are used
+    lds_char* vb;                  // fp8: [kWaves][16 x 256 B] bf16 copy of the V slice
+    lds_char* merge;               // [kMergeBytes]
+};
+template <bool FP8> constexpr int stage_array_bytes(int u) {
+    return u < Stage<FP8>::STAGES ? kWaves * Stage<FP8>::BYTES : 16;
+}
+static_assert(kWaves * Stage<false>::BYTES * Stage<false>::STAGES + kMergeBytes <= 160 * 1024, "LDS");
+static_assert(kWaves * Stage<true>::BYTES * Stage<true>::STAGES + kVbBytes + kMergeBytes <= 160 * 1024, "LDS");
+
+// One descriptor of the tile stream (all fields wave-uniform).
+struct Desc {
+    int h, b, t0, t1, L;
+    int64_t slot;
+};
+
+// Per-lane constants of the asynchronous loads (fixed for a wave's stream).
+template <bool FP8> struct LaneLoads {
+    uint32_t kv_live[Stage<FP8>::KV_LOADS];   // byte offset in a page of this lane's 16 B (h = 0)
+    uint32_t kv_dead[Stage<FP8>::KV_LOADS];   // same chunk of the page's row 0
+    int row[Stage<FP8>::KV_LOADS];            // slice row loaded by this lane
+    int scale_row;                            // fp8: slice row of this lane's scale (lane % 16)
+    __device__ void init(int Hkv, int w, int lane) {
+        using SL = Stage<FP8>;
+        constexpr int kRowsPerLoad = 1024 / SL::kRow;
+        constexpr int kChunks = SL::kRow / 16;
+#pragma unroll
+        for (int s = 0; s < SL::KV_LOADS; ++s) {
+            row[s] = kRowsPerLoad * s + lane / kChunks;
+            const uint32_t chunk = 16u * (uint32_t)((lane % kChunks) ^ swz<FP8>(row[s]));
+            kv_live[s] = (uint32_t)(16 * w + row[s]) * (uint32_t)Hkv * SL::kRow + chunk;
+            kv_dead[s] = chunk;
+        }
+        scale_row = lane & 15;
+    }
+};
+
+// Issue the asynchronous loads of one tile into stage `st`: this wave's 16 K
+// and V rows of page `page` and, for fp8, their k/v scales.
+template <bool FP8>
+__device__ inline void issue_tile(const AttnArgs& a, const LaneLoads<FP8>& ll, lds_char* __restrict__ st,
+                                  int64_t page, const Desc& d, int tile, int w) {
+    using SL = Stage<FP8>;
+    const size_t pbase = ((size_t)page * kTile * a.Hkv + d.h) * SL::kRow;
+    const char* kb = static_cast<const char*>(a.k_cache) + pbase;
+    const char* vb = static_cast<const char*>(a.v_cache) + pbase;
+    const int tok0 = 64 * tile + 16 * w;
+    const bool full = tok0 + 16 <= d.L;                 // every row of this slice is live
+#pragma unroll
+    for (int s = 0; s < SL::KV_LOADS; ++s) {
+        const uint32_t off = (full || tok0 + ll.row[s] < d.L) ? ll.kv_live[s] : ll.kv_dead[s];
+        dma16(kb + off, st + SL::K + 1024 * s);
+        dma16(vb + off, st + SL::V + 1024 * s);
+    }
+    if constexpr (FP8) {
+        const size_t sbase = ((size_t)page * a.Hkv + d.h) * kTile;
+        const int srow = (full || tok0 + ll.scale_row < d.L) ? 16 * w + ll.scale_row : 0;
+        dma4(a.k_scale + sbase + srow, st + SL::KS);
+        dma4(a.v_scale + sbase + srow, st + SL::VS);
+    }
+}
+
 // Running state of one wave over one descriptor.
 struct WaveState {
     f32x4 acc[8];     // O^T[d = 16 db + 4 g + i][head r]
-    float m;          // running max (log2 domain) of head r, uniform over g
+    float m;          // running reference max (log2 domain) of head r, uniform over g
     float l;          // this lane's share of the running sum of head r
 };
 
-// Q operand of a descriptor (B of S^T = K Q^T) from the stage of its first
-// tile: head r of the group, zero for r >= 8.  Also returns the score scale.
+// Q operand of a descriptor (B of S^T = K Q^T): head r of the group (zero for
+// r >= 8), as bf16 (bf16 KV) or raw e4m3 codes (fp8 KV), plus the Q scale.
+template <bool FP8> struct QOp;
+template <> struct QOp<false> { uint4 v[4]; };
+template <> struct QOp<true> { uint4 v[2]; float scale; };
+
+// Plain loads into registers, issued when the load cursor enters a descriptor
+// (its first tile), several tiles before the compute cursor needs them.
 template <bool FP8>
-__device__ inline void read_q(const lds_char* __restrict__ qs, const lds_char* __restrict__ st, int r, int g,
-                              float scale_log2, bf16x8 (&q)[4], float& sl2) {
-    using SL = Stage<FP8>;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const int hr = r & 7;
-    sl2 = scale_log2;
+__device__ inline void load_q(const AttnArgs& a, const Desc& d, int r, int g, QOp<FP8>& q) {
+    const size_t row = (size_t)d.b * a.Hq + (size_t)d.h * kGroup + (r & 7);
+    if constexpr (!FP8) {
+        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + row * 256);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        uint4 v;
-        if constexpr (!FP8) {
-            v = lds_load16(qs + hr * 256 + 16 * (g + 4 * ks));
-        } else {
-            const uint2 c = lds_load8(qs + hr * 128 + 16 * (g + 4 * (ks >> 1)) + 8 * (ks & 1));
-            v = fp8x8_to_bf16x8(c.x, c.y);
-        }
-        q[ks] = as_bf16x8(r < kGroup ? v : z);
+        for (int ks = 0; ks < 4; ++ks) q.v[ks] = qp[g + 4 * ks];
+    } else {
+        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + row * 128);
+        q.v[0] = qp[g];            // k-steps 0, 1
+        q.v[1] = qp[g + 4];        // k-steps 2, 3
+        q.scale = a.q_scale[row];
     }
-    if constexpr (FP8) sl2 *= *reinterpret_cast<const __attribute__((address_space(3))) float*>(st + SL::SC + 4 * (32 + hr));
 }
 
 // QK^T, online softmax and PV of one tile held in stage `st`.
 template <bool FP8>
-__device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* __restrict__ vb, const bf16x8 (&q)[4], float sl2, int tok0,
-                                    int L, int w, int r, int g, WaveState& ws) {
+__device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* __restrict__ vb, const QOp<FP8>& q,
+                                    float sl2, int tok0, int L, int w, int r, int g, WaveState& ws) {
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    const bool qlive = r < kGroup;
     using SL = Stage<FP8>;
-    // ---- S^T = K Q^T: rows = this wave's 16 tokens, cols = 16 heads --------
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    // ---- operands from LDS, then S^T = K Q^T (rows = 16 tokens, cols = 16 heads)
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    const int vrow = 4 * g + (r >> 2);            // transposed-read row of this lane
+    s16x4 va[8];
+    f32x4 ks4, vs4;
     if constexpr (!FP8) {
+        uint32_t ka[4], vaddr[8];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const uint4 k = lds_load16(st + SL::K + r * 256 + 16 * ((g + 4 * ks) ^ swz<false>(r)));
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k), q[ks], s, 0, 0, 0);
-        }
+        for (int ks = 0; ks < 4; ++ks) ka[ks] = lds_addr(st + SL::K + r * 256 + 16 * ((g + 4 * ks) ^ swz<false>(r)));
+        const uint32_t vr = lds_addr(st + SL::V + vrow * 256 + 8 * (r & 1));
+#pragma unroll
+        for (int db = 0; db < 8; ++db) vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_bf16(vrow));
+        uint4 k[4];
+        lds_read_tile_bf16(k, va, ka, vaddr);
+        bf16x8 qv[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qv[ks] = as_bf16x8(qlive ? q.v[ks] : z4);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[0]), qv[0], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[1]), qv[1], sb, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[2]), qv[2], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[3]), qv[3], sb, 0, 0, 0);
     } else {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const uint4 c = lds_load16(st + SL::K + r * 128 + 16 * ((g + 4 * p) ^ swz<true>(r)));
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fp8x8_to_bf16x8(c.x, c.y)), q[2 * p], s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fp8x8_to_bf16x8(c.z, c.w)), q[2 * p + 1], s, 0, 0, 0);
-        }
-        // widen this lane's two V chunks of row r into the bf16 copy (same swizzle as bf16 V)
-        uint4 raw[2];
-        lds_read2x16(raw[0], raw[1], (uint32_t)(size_t)(st + SL::V + r * 128 + 16 * (g ^ swz<true>(r))),
-                     (uint32_t)(size_t)(st + SL::V + r * 128 + 16 * ((g + 4) ^ swz<true>(r))));
+        uint32_t addr[6];
+        addr[0] = lds_addr(st + SL::K + r * 128 + 16 * (g ^ swz<true>(r)));         // K k-steps 0, 1
+        addr[1] = lds_addr(st + SL::K + r * 128 + 16 * ((g + 4) ^ swz<true>(r)));   // K k-steps 2, 3
+        addr[2] = lds_addr(st + SL::V + r * 128 + 16 * (g ^ swz<true>(r)));         // V chunk g
+        addr[3] = lds_addr(st + SL::V + r * 128 + 16 * ((g + 4) ^ swz<true>(r)));   // V chunk g + 4
+        addr[4] = lds_addr(st + SL::KS + 16 * g);                                   // k scales, rows 4g..
+        addr[5] = lds_addr(st + SL::VS + 16 * g);                                   // v scales, rows 4g..
+        uint4 o[6];
+        lds_read_tile_fp8(o, addr);
+        const uint4 c0 = o[0], c1 = o[1];
+        ks4 = __builtin_bit_cast(f32x4, o[4]);
+        vs4 = __builtin_bit_cast(f32x4, o[5]);
+        const uint4 q0 = qlive ? q.v[0] : z4, q1 = qlive ? q.v[1] : z4;
+        auto lo = [](uint4 x) { return (long)(((uint64_t)x.y << 32) | x.x); };
+        auto hi = [](uint4 x) { return (long)(((uint64_t)x.w << 32) | x.z); };
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(lo(c0), lo(q0), sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(hi(c0), hi(q0), sb, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(lo(c1), lo(q1), sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(hi(c1), hi(q1), sb, 0, 0, 0);
+        // widen this lane's two V chunks of row r into the bf16 copy (same swizzle as bf16 V),
+        // then read it back transposed
+        uint32_t waddr[4];
+        uint4 wv[4];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int c = g + 4 * p;
-            lds_store16(vb + r * 256 + 16 * ((2 * c) ^ swz_bf16(r)), fp8x8_to_bf16x8(raw[p].x, raw[p].y));
-            lds_store16(vb + r * 256 + 16 * ((2 * c + 1) ^ swz_bf16(r)), fp8x8_to_bf16x8(raw[p].z, raw[p].w));
+            waddr[2 * p] = lds_addr(vb + r * 256 + 16 * ((2 * c) ^ swz_bf16(r)));
+            waddr[2 * p + 1] = lds_addr(vb + r * 256 + 16 * ((2 * c + 1) ^ swz_bf16(r)));
+            wv[2 * p] = fp8x8_to_bf16x8(o[2 + p].x, o[2 + p].y);
+            wv[2 * p + 1] = fp8x8_to_bf16x8(o[2 + p].z, o[2 + p].w);
         }
+        lds_write4x16(waddr, wv);
+        const uint32_t vr = lds_addr(vb + vrow * 256 + 8 * (r & 1));
+        uint32_t vaddr[8];
+#pragma unroll
+        for (int db = 0; db < 8; ++db) vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_bf16(vrow));
+        vt_read8(va, vaddr);
     }
+    const f32x4 s = sa + sb;
 
     // ---- online softmax over the 4 score rows of this lane ------------------
     const int pos0 = tok0 + 16 * w + 4 * g;       // token of score row i is pos0 + i
-    f32x4 ks4, vs4;
-    if constexpr (FP8) {
-        ks4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(st + SL::SC + 16 * g);
-        vs4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(st + SL::SC + 64 + 16 * g);
-    }
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -339,21 +488,25 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
         if constexpr (FP8) x *= ks4[i];
         sc[i] = (pos0 + i < L) ? x : kNegInf;
     }
-    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(ws.m, mt);
-    const bool none = (m_new == kNegInf);        // no live token seen yet
-    const float alpha = none ? 1.f : exp2_fast(ws.m - m_new);
+    const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (__builtin_amdgcn_ballot_w64(lmax > ws.m + kSlack) != 0) {
+        // a score above the reference: new reference = max over the 16 tokens
+        float mt = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(ws.m, mt);
+        const float alpha = exp2_fast(ws.m - m_new);      // 0 when nothing was accumulated yet
+        ws.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) ws.acc[db] *= alpha;
+        ws.m = m_new;
+    }
+    const float mref = (ws.m == kNegInf) ? 0.f : ws.m;   // all scores -inf so far: p = 0
     float p[4];
-    float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        p[i] = none ? 0.f : exp2_fast(sc[i] - m_new);
-        psum += p[i];
+        p[i] = exp2_fast(sc[i] - mref);
+        ws.l += p[i];
     }
-    ws.l = ws.l * alpha + psum;
-    ws.m = m_new;
     if constexpr (FP8) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] *= vs4[i];
@@ -364,40 +517,19 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
     // ds_read_b64_tr_b16: in each 16-lane group, lane k supplies the address of
     // 4 consecutive d of token row 4g + k/4; lane i = 4a + c then receives
     // V[4g + j][16 db + i] for j = 0..3 -- the A operand (d x tokens).
-    const lds_char* vbase = FP8 ? (const lds_char*)vb : st + SL::V;
-    const int vrow = 4 * g + (r >> 2);
-    const uint32_t vr = (uint32_t)(size_t)(vbase + vrow * 256 + 8 * (r & 1));   // LDS byte address
-    uint32_t addr[8];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) addr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_bf16(vrow));
-    s16x4 va[8];
-    vt_read8(va, addr);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        ws.acc[db] = ws.acc[db] * alpha;
+    for (int db = 0; db < 8; ++db)
         ws.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], pb, ws.acc[db], 0, 0, 0);
-    }
-}
-
-// Workgroup barrier for LDS exchange only.  __syncthreads() also fences
-// global memory, which would wait for every asynchronous load in flight; the
-// merge only needs this wave's LDS writes done (lgkmcnt(0)) before s_barrier.
-__device__ inline void lds_barrier() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0), vmcnt(63)
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
 }
 
 // End of a descriptor: merge the 4 waves' (max, sum, O) through LDS and write
-// the partial (normalised O, natural-log LSE) of slot d.slot.
+// the partial (normalised O, natural-log LSE) of `slot`.
 __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const WaveState& ws, bool bad,
                                    int64_t slot, int w, int lane, int r, int g) {
     float lsum = ws.l;
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
-    __attribute__((address_space(3))) float* o_w =
-        reinterpret_cast<__attribute__((address_space(3))) float*>(merge + w * kMergeWave);
+    lds_float* o_w = reinterpret_cast<lds_float*>(merge + w * kMergeWave);
     if (r < kGroup) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
@@ -416,8 +548,7 @@ __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const Wav
         bool any_bad = false;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const __attribute__((address_space(3))) float* ow =
-                reinterpret_cast<const __attribute__((address_space(3))) float*>(merge + ww * kMergeWave);
+            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * kMergeWave);
             M = fmaxf(M, ow[kGroup * kHeadDim + hh]);
             any_bad |= ow[kGroup * kHeadDim + 2 * kGroup] != 0.f;
         }
@@ -425,15 +556,14 @@ __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const Wav
         float lt = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const __attribute__((address_space(3))) float* ow =
-                reinterpret_cast<const __attribute__((address_space(3))) float*>(merge + ww * kMergeWave);
+            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * kMergeWave);
             const float mw = ow[kGroup * kHeadDim + hh];
             const float sw = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
             lt += sw * ow[kGroup * kHeadDim + kGroup + hh];
             o += sw * *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(ow + hh * kHeadDim + d4);
         }
         float lse;
-        if (any_bad || M == kNegInf) {
+        if (any_bad || M == kNegInf || !(lt > 0.f)) {
             const float nan = __builtin_nanf("");
             o = f32x4{nan, nan, nan, nan};
             lse = nan;
@@ -497,15 +627,23 @@ struct Cursor {
     }
 };
 
-// Issue the next tile of the load cursor into ring stage `slot`.
+// Issue the next tile of the load cursor into ring stage `slot` (and, when it
+// is the first tile of a descriptor, that descriptor's Q into qslot).  Past
+// the last tile it re-issues the last tile into a stage that is never read, so
+// every step issues the same number of ring loads.  `page` is the page id of
+// the cursor's tile, loaded one step ahead; the next one is fetched here.
 template <bool FP8, class Src>
-__device__ inline void issue_step(const AttnArgs& a, Cursor<Src>& lc, int& issued, int ntiles, uint32_t& bad_bits,
-                                  lds_char* st, lds_char* qs, int slot, int w, int lane) {
-    const int64_t pg = (int64_t)uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
-    const bool ok = pg >= 0 && pg < a.num_pages;
+__device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, Cursor<Src>& lc, int& issued,
+                                  int ntiles, int64_t& page, uint32_t& bad_bits, lds_char* st, QOp<FP8>& qslot,
+                                  int slot, int w, int r, int g) {
+    const bool ok = page >= 0 && page < a.num_pages;
     bad_bits = (bad_bits & ~(1u << slot)) | ((uint32_t)(!ok) << slot);
-    issue_tile<FP8>(a, st, qs, ok ? pg : 0, lc.d, lc.t, w, lane);
-    if (++issued < ntiles) lc.next();
+    if (issued < ntiles && lc.t == lc.d.t0) load_q<FP8>(a, lc.d, r, g, qslot);
+    issue_tile<FP8>(a, ll, st, ok ? page : 0, lc.d, lc.t, w);
+    if (++issued < ntiles) {
+        lc.next();
+        page = (int64_t)uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
+    }
 }
 
 // Stream every tile of `src` through this workgroup (see the header comment).
@@ -516,37 +654,39 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     auto stage = [&](int u) -> lds_char* { return sm.stage[u] + w * SL::BYTES; };
-    auto qstage = [&](int u) -> lds_char* { return sm.qst[u] + w * SL::Q_BYTES; };
     lds_char* vb = sm.vb + w * (16 * 256);
-    lds_char* merge = sm.merge;
+    LaneLoads<FP8> ll;
+    ll.init(a.Hkv, w, lane);
 
-    // load cursor: runs S-1 tiles ahead; past the last tile it re-issues the
-    // last tile (into a free stage, never read) so every step issues the same
-    // number of loads and the vmcnt bound below stays exact.
+    // load cursor: runs S-1 tiles ahead of the compute cursor
     Cursor<Src> lc;
     lc.begin(&src);
     int issued = 0;
+    int64_t page = (int64_t)uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
     uint32_t bad_bits = 0;          // bit u: the tile in stage u has an out-of-range page id
+    QOp<FP8> qring[S];              // Q of the descriptor whose first tile sits in stage u
 #pragma unroll
-    for (int u = 0; u < S - 1; ++u) issue_step<FP8>(a, lc, issued, ntiles, bad_bits, stage(u), qstage(u), u, w, lane);
+    for (int u = 0; u < S - 1; ++u)
+        issue_step<FP8>(a, ll, lc, issued, ntiles, page, bad_bits, stage(u), qring[u], u, w, r, g);
 
     Cursor<Src> cc;
     cc.begin(&src);
     WaveState ws;
-    bf16x8 q[4];
+    QOp<FP8> q;
     float sl2 = 0.f;
     bool bad = false;
     for (int k = 0; k < ntiles; k += S) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
             const int kk = k + u;
-            issue_step<FP8>(a, lc, issued, ntiles, bad_bits, stage((u + S - 1) % S), qstage((u + S - 1) % S),
-                            (u + S - 1) % S, w, lane);                  // tile kk + S - 1
-            wait_vmcnt<(S - 1) * SL::LOADS>();                // tile kk has landed
+            issue_step<FP8>(a, ll, lc, issued, ntiles, page, bad_bits, stage((u + S - 1) % S), qring[(u + S - 1) % S],
+                            (u + S - 1) % S, w, r, g);                     // tile kk + S - 1
+            wait_vmcnt<(S - 1) * SL::LOADS>();                             // tile kk has landed
             if (kk < ntiles) {
-                const lds_char* st = stage(u);
-                if (cc.t == cc.d.t0) {                            // first tile of a descriptor
-                    read_q<FP8>(qstage(u), st, r, g, a.scale_log2, q, sl2);
+                if (cc.t == cc.d.t0) {                                     // first tile of a descriptor
+                    q = qring[u];
+                    sl2 = a.scale_log2;
+                    if constexpr (FP8) sl2 *= q.scale;
 #pragma unroll
                     for (int db = 0; db < 8; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
                     ws.m = kNegInf;
@@ -554,38 +694,37 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
                     bad = false;
                 }
                 bad |= (bad_bits >> u) & 1u;
-                tile_compute<FP8>(st, vb, q, sl2, 64 * cc.t, cc.d.L, w, r, g, ws);
-                if (cc.t + 1 == cc.d.t1) finish_desc(a, merge, ws, bad, cc.d.slot, w, lane, r, g);
+                tile_compute<FP8>(stage(u), vb, q, sl2, 64 * cc.t, cc.d.L, w, r, g, ws);
+                if (cc.t + 1 == cc.d.t1) finish_desc(a, sm.merge, ws, bad, cc.d.slot, w, lane, r, g);
                 cc.next();
             }
         }
     }
-    wait_vmcnt<0>();   // no load may still target LDS when the workgroup retires
+    wait_vmcnt<0>();   // no load may still target LDS when the workgroup moves on
 }
+
+#define LBSA_DECLARE_SMEM(FP8)                                                 \
+    __shared__ __attribute__((aligned(16))) char s0[stage_array_bytes<FP8>(0)]; \
+    __shared__ __attribute__((aligned(16))) char s1[stage_array_bytes<FP8>(1)]; \
+    __shared__ __attribute__((aligned(16))) char s2[stage_array_bytes<FP8>(2)]; \
+    __shared__ __attribute__((aligned(16))) char s3[stage_array_bytes<FP8>(3)]; \
+    __shared__ __attribute__((aligned(16))) char s4[stage_array_bytes<FP8>(4)]; \
+    __shared__ __attribute__((aligned(16))) char s5[stage_array_bytes<FP8>(5)]; \
+    __shared__ __attribute__((aligned(16))) char svb[FP8 ? kVbBytes : 16];      \
+    __shared__ __attribute__((aligned(16))) char smerge[kMergeBytes];           \
+    Smem<FP8> sm; /* address-space casts to LDS */                             \
+    sm.stage[0] = (lds_char*)s0;                                               \
+    sm.stage[1] = (lds_char*)s1;                                               \
+    sm.stage[2] = (lds_char*)s2;                                               \
+    sm.stage[3] = (lds_char*)s3;                                               \
+    sm.stage[4] = (lds_char*)s4;                                               \
+    sm.stage[5] = (lds_char*)s5;                                               \
+    sm.vb = (lds_char*)svb;                                                    \
+    sm.merge = (lds_char*)smerge
 
 template <bool FP8>
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) char s0[stage_array_bytes<FP8>(0)];
-    __shared__ __attribute__((aligned(16))) char s1[stage_array_bytes<FP8>(1)];
-    __shared__ __attribute__((aligned(16))) char s2[stage_array_bytes<FP8>(2)];
-    __shared__ __attribute__((aligned(16))) char s3[stage_array_bytes<FP8>(3)];
-    __shared__ __attribute__((aligned(16))) char q0[q_array_bytes<FP8>(0)];
-    __shared__ __attribute__((aligned(16))) char q1[q_array_bytes<FP8>(1)];
-    __shared__ __attribute__((aligned(16))) char q2[q_array_bytes<FP8>(2)];
-    __shared__ __attribute__((aligned(16))) char q3[q_array_bytes<FP8>(3)];
-    __shared__ __attribute__((aligned(16))) char svb[FP8 ? kVbBytes : 16];
-    __shared__ __attribute__((aligned(16))) char smerge[kMergeBytes];
-    Smem<FP8> sm;   // address-space casts to LDS
-    sm.stage[0] = (lds_char*)s0;
-    sm.stage[1] = (lds_char*)s1;
-    sm.stage[2] = (lds_char*)s2;
-    sm.stage[3] = (lds_char*)s3;
-    sm.qst[0] = (lds_char*)q0;
-    sm.qst[1] = (lds_char*)q1;
-    sm.qst[2] = (lds_char*)q2;
-    sm.qst[3] = (lds_char*)q3;
-    sm.vb = (lds_char*)svb;
-    sm.merge = (lds_char*)smerge;
+    LBSA_DECLARE_SMEM(FP8);
     const MapLayout ML = map_layout(a.B, a.Hkv, a.P);
     const auto* hdr = uniform_ptr<int32_t>(a.map + ML.header);
     if (hdr[LBSA_HDR_ERROR] != 0 || hdr[LBSA_HDR_P] != a.P || hdr[LBSA_HDR_B] != a.B ||
@@ -613,27 +752,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
 
 template <bool FP8>
 __global__ __launch_bounds__(kSplitThreads) void static_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) char s0[stage_array_bytes<FP8>(0)];
-    __shared__ __attribute__((aligned(16))) char s1[stage_array_bytes<FP8>(1)];
-    __shared__ __attribute__((aligned(16))) char s2[stage_array_bytes<FP8>(2)];
-    __shared__ __attribute__((aligned(16))) char s3[stage_array_bytes<FP8>(3)];
-    __shared__ __attribute__((aligned(16))) char q0[q_array_bytes<FP8>(0)];
-    __shared__ __attribute__((aligned(16))) char q1[q_array_bytes<FP8>(1)];
-    __shared__ __attribute__((aligned(16))) char q2[q_array_bytes<FP8>(2)];
-    __shared__ __attribute__((aligned(16))) char q3[q_array_bytes<FP8>(3)];
-    __shared__ __attribute__((aligned(16))) char svb[FP8 ? kVbBytes : 16];
-    __shared__ __attribute__((aligned(16))) char smerge[kMergeBytes];
-    Smem<FP8> sm;   // address-space casts to LDS
-    sm.stage[0] = (lds_char*)s0;
-    sm.stage[1] = (lds_char*)s1;
-    sm.stage[2] = (lds_char*)s2;
-    sm.stage[3] = (lds_char*)s3;
-    sm.qst[0] = (lds_char*)q0;
-    sm.qst[1] = (lds_char*)q1;
-    sm.qst[2] = (lds_char*)q2;
-    sm.qst[3] = (lds_char*)q3;
-    sm.vb = (lds_char*)svb;
-    sm.merge = (lds_char*)smerge;
+    LBSA_DECLARE_SMEM(FP8);
     const int S = a.P;
     const int split = blockIdx.x % S;
     const int rest = blockIdx.x / S;
@@ -669,18 +788,37 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// One workgroup per (request, query head): 8 slices of 32 threads stride over
-// the chunks, each thread owns 4 consecutive d.
+// Online LSE merge of one chunk into a running (max, weight sum, weighted O).
+__device__ inline void merge_chunk(float l, f32x4 x, float& m, float& wsum, f32x4& o, bool& nan_seen) {
+    if (l != l) { nan_seen = true; return; }
+    if (l == kNegInf) return;                           // empty chunk (static split)
+    if (l > m) {
+        const float sc = exp2_fast((m - l) * kLog2e);   // 0 when m = -inf
+        wsum *= sc;
+        o *= sc;
+        m = l;
+    }
+    const float wgt = exp2_fast((l - m) * kLog2e);
+    wsum += wgt;
+    o += wgt * x;
+}
+
+// One workgroup per (request, query head).  Its 256 threads form 8 slices of
+// 32 (4 consecutive d per thread); slice c0 merges chunks c0, c0 + 8, ... of
+// the row in one pass with a running (max LSE, weight sum, weighted O), four
+// chunks' loads in flight at a time, and the 8 slice states are merged
+// through LDS under the global maximum.
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, int static_mode) {
-    __shared__ float red_m[8];
-    __shared__ float red_w[8];
-    __shared__ __attribute__((aligned(16))) float red_o[8][kHeadDim];
+    constexpr int kSlices = 8;
+    __shared__ float red_m[kSlices];
+    __shared__ float red_w[kSlices];
+    __shared__ int red_nan;
+    __shared__ __attribute__((aligned(16))) float red_o[kSlices][kHeadDim];
     const int row = blockIdx.x;
     const int b = row / a.Hq, hq = row - b * a.Hq;
     const int h = hq / kGroup, gq = hq - h * kGroup;
     const int64_t seg = (int64_t)h * a.B + b;
-    const int tid = threadIdx.x, cs = tid >> 5, d4 = (tid & 31) * 4;
-    uint16_t* out = static_cast<uint16_t*>(a.out) + ((size_t)b * a.Hq + hq) * kHeadDim + d4;
+    const int tid = threadIdx.x, slice = tid >> 5, d4 = (tid & 31) * 4;
 
     int64_t d0 = 0;
     int n = 0;
@@ -700,45 +838,55 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
             if (d0 < 0 || n < 0 || d0 + n > cap) { poison = true; n = 0; }
         }
     }
+    if (tid == 0) red_nan = 0;
 
-    // pass 1: global max of the chunk LSEs
-    float m = kNegInf;
-    for (int c = cs; c < n; c += 8) m = fmaxf(m, a.part_lse[(d0 + c) * kGroup + gq]);
-    if ((tid & 31) == 0) red_m[cs] = m;
-    __syncthreads();
-    float M = red_m[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) M = fmaxf(M, red_m[i]);
-
-    // pass 2: weighted sum of the partial outputs
+    float m = kNegInf, wsum = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    float ws = 0.f;
-    if (M != kNegInf) {
-#pragma unroll 4
-        for (int c = cs; c < n; c += 8) {
-            const float l = a.part_lse[(d0 + c) * kGroup + gq];
-            const float wgt = exp2_fast((l - M) * kLog2e);
-            ws += wgt;
-            o += wgt * *reinterpret_cast<const f32x4*>(a.part_o + ((d0 + c) * kGroup + gq) * kHeadDim + d4);
-        }
-    }
-    if ((tid & 31) == 0) red_w[cs] = ws;
-    *reinterpret_cast<f32x4*>(&red_o[cs][d4]) = o;
-    __syncthreads();
-    if (cs == 0) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        float wt = 0.f;
+    bool nan_seen = false;
+    auto pr = [&](int c) { return (d0 + c) * kGroup + gq; };
+    int c = slice;
+    for (; c + 3 * kSlices < n; c += 4 * kSlices) {     // four chunks' loads in flight
+        float l[4];
+        f32x4 x[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            acc += *reinterpret_cast<const f32x4*>(&red_o[i][d4]);
-            wt += red_w[i];
+        for (int u = 0; u < 4; ++u) {
+            l[u] = a.part_lse[pr(c + u * kSlices)];
+            x[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr(c + u * kSlices) * kHeadDim + d4);
         }
-        if (M == kNegInf || n == 0) acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        else acc *= 1.f / wt;
-        if (poison || M != M) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) merge_chunk(l[u], x[u], m, wsum, o, nan_seen);
+    }
+    for (; c < n; c += kSlices)
+        merge_chunk(a.part_lse[pr(c)], *reinterpret_cast<const f32x4*>(a.part_o + pr(c) * kHeadDim + d4), m, wsum,
+                    o, nan_seen);
+    __syncthreads();                                    // red_nan initialised
+    if (nan_seen) red_nan = 1;
+    if ((tid & 31) == 0) {
+        red_m[slice] = m;
+        red_w[slice] = wsum;
+    }
+    *reinterpret_cast<f32x4*>(&red_o[slice][d4]) = o;
+    __syncthreads();
+    if (slice == 0) {
+        float M = kNegInf;
+#pragma unroll
+        for (int i = 0; i < kSlices; ++i) M = fmaxf(M, red_m[i]);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        float W = 0.f;
+        if (M != kNegInf) {
+#pragma unroll
+            for (int i = 0; i < kSlices; ++i) {
+                const float sc = exp2_fast((red_m[i] - M) * kLog2e);   // 0 for empty slices
+                W += sc * red_w[i];
+                acc += sc * *reinterpret_cast<const f32x4*>(&red_o[i][d4]);
+            }
+            acc *= 1.f / W;
+        }
+        if (poison || red_nan) {
             const float nan = __builtin_nanf("");
             acc = f32x4{nan, nan, nan, nan};
         }
+        uint16_t* out = static_cast<uint16_t*>(a.out) + ((size_t)b * a.Hq + hq) * kHeadDim + d4;
         uint2 packed;
         packed.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
         packed.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);

@@ -13,7 +13,7 @@ constexpr int kTile = 64;       // tokens per tile = tokens per page
 constexpr int kHeadDim = 128;
 constexpr int kGroup = 8;       // query heads per KV head
 constexpr int kSplitThreads = 256;   // 4 wave64 per split workgroup
-constexpr int kAssignThreads = 1024;
+constexpr int kAssignThreads = 256;
 constexpr int kCombineThreads = 256;
 constexpr int kMaxAssignLdsWords = 16384;  // (B + 1) + (Hkv*B + 1) int32 in 64 KiB
 
