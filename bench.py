@@ -188,14 +188,17 @@ def gpu_batch(name, tail="normal"):
     return b
 
 
-def cpu_baseline(name, budget_s):
+def cpu_baseline(batch, out, P, budget_s):
     """The CPU oracle (as it stands) timed on this host: assign + fp64 attention
-    over a bounded sample of the workload's (request, query head) rows."""
+    over a bounded sample of the workload's (request, query head) rows, on a
+    host copy of the very batch the GPU ran.  The sampled rows and the task map
+    are also checked against the GPU results (max abs error, bit-exact map)."""
     import numpy as np
+    import torch
 
-    from load_balanced_split_assign_amd import workload as wl
+    from load_balanced_split_assign_amd import lbsa
     from oracle import oracle
-    b = wl.make_batch(name, tail="normal", device="cpu")
+    b = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in batch.items()}
     B, Hq, Hkv = b["B"], b["num_heads"], b["num_kv_heads"]
     sl = [int(x) for x in b["seqlens"]]
     threads = oracle.num_threads()
@@ -213,10 +216,10 @@ def cpu_baseline(name, budget_s):
         tokens += sl[req]
     rows = np.array(rows, np.int32)
     t0 = time.perf_counter()
-    oracle.attention_rows(b, rows)
+    ref, _ = oracle.attention_rows(b, rows)
     t_attn = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.assign(b["seqlens"], Hq, Hkv, 1024, 2, b["max_pages"])
+    om = oracle.assign(b["seqlens"], Hq, Hkv, P, 2, b["max_pages"])
     t_assign = time.perf_counter() - t0
     full = len(rows) == B * Hq
     # each row is charged its own Q and output plus 1/G of its segment's K/V bytes
@@ -224,11 +227,56 @@ def cpu_baseline(name, budget_s):
     e_kv, s_kv, e_q, s_q = (2, 0, 2, 0) if b["kv_dtype"] == "bf16" else (1, 8, 1, 4)
     row_tokens = sum(sl[r] for r, _ in rows)
     sample_bytes = row_tokens * (2 * 128 * e_kv + s_kv) / G + len(rows) * (128 * e_q + s_q + 128 * 2)
+    got = out.float().cpu().numpy()[rows[:, 0], rows[:, 1]].astype(np.float64)
+    err = float(np.max(np.abs(got - ref))) if len(rows) else 0.0
+    gm = lbsa.read_task_map(batch["_tm"], B, Hkv, P)
+    same = all(np.array_equal(np.asarray(gm[k]), np.asarray(om[k]))
+               for k in ("bin_desc_begin", "desc", "seg_first_desc", "seg_num_chunks"))
+    same = same and all(int(gm[k]) == int(om[k]) for k in ("T", "K", "q", "r", "Ndesc"))
     return {"value": round(sample_bytes / (t_attn + t_assign) / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
-            "sample": (f"{'all' if full else len(rows)} of {B * Hq} (request, query head) rows of '{name}'"
+            "sample": (f"{'all' if full else len(rows)} of {B * Hq} (request, query head) rows"
                        f" ({row_tokens} token-rows), fp64 attention + assign"),
-            "attn_s": round(t_attn, 3), "assign_us": round(1e6 * t_assign, 1)}
+            "attn_s": round(t_attn, 3), "assign_us": round(1e6 * t_assign, 1),
+            "check": {"rows": len(rows), "max_abs_err": err, "map_bitexact": bool(same)}}
+
+
+def _pmc_rows(run_dir, counter):
+    """(kernel name, value in KiB) per dispatch, in dispatch order, from the
+    counter_collection CSV files of one rocprofv3 --pmc run."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, v) for _, k, v in rows]
+
+
+def write_traffic(fetch_dir, write_dir):
+    """HBM bytes per split launch = FETCH_SIZE + WRITE_SIZE of the split kernel,
+    each scaled by CALIB_BYTES / what the same counter reads for the calibration
+    copy (the first device-to-device copy dispatch of a --calib-copy run)."""
+    rec = {"source_sha256": source_sha(SPLIT_SRC), "kernel": "split_kernel", "calib_bytes": CALIB_BYTES}
+    total = 0.0
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(d, counter)
+        calib = next(v for k, v in rows if "copyBuffer" in k)
+        split = [v for k, v in rows if "split_kernel" in k]
+        factor = CALIB_BYTES / (calib * 1024.0)
+        mean_kib = statistics.fmean(split)
+        rec[key] = {"counter": counter, "calib_kib": calib, "factor": round(factor, 4),
+                    "split_kib_mean": round(mean_kib, 2), "launches": len(split),
+                    "bytes_per_launch": round(mean_kib * 1024.0 * factor)}
+        total += mean_kib * 1024.0 * factor
+    rec["bytes_per_launch"] = round(total)
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def traffic_from_profile():
@@ -245,7 +293,7 @@ def traffic_from_profile():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="tp8_share")
     ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0 = CUs x occupancy)")
@@ -256,7 +304,13 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device copy first (reference for PMC byte counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (bounded sample)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; each with "
+                         "--calib-copy) into the split kernel's HBM bytes per launch")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path needs no collectives; "
               "KV-head or request sharding across GPUs runs independent copies of it.", file=sys.stderr)
@@ -290,6 +344,8 @@ def main():
     st = {k: summarize(v) for k, v in t.items()}
     step_us, split_us = st["step"]["mean"], st["split"]["mean"]
     value = ab["layer"] / (step_us * 1e-6) / 1e9
+    layer_us = st["layer"]["mean"]
+    layer_gbs = ab["layer"] / (layer_us * 1e-6) / 1e9
     split_gbs = ab["split"] / (split_us * 1e-6) / 1e9
     traffic = traffic_from_profile()
 
@@ -305,6 +361,8 @@ def main():
                    "K": m["K"], "Ndesc": m["Ndesc"]},
         "us_per_step": round(step_us, 3),
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "layer_GBps": round(layer_gbs, 2), "pct_of_peak_layer": round(100.0 * layer_gbs / HBM_PEAK_GBS, 2),
+        "occupancy": {"workgroups": P, "per_cu": P // 256},
         "times_us": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in st.items()},
         "alg_bytes": ab,
         "partial_bytes": 2 * m["Ndesc"] * 8 * (128 + 1) * 4,
@@ -332,7 +390,8 @@ def main():
         del sk
 
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(name, args.cpu_budget)
+        batch["_tm"] = path.tm
+        rec["cpu_baseline"] = cpu_baseline(batch, path.out, P, args.cpu_budget)
 
     print(json.dumps(rec), flush=True)
 
