@@ -94,6 +94,11 @@ typedef struct {
     size_t seg_first_desc;  /* int32[Hkv*B], index h*B + b: first descriptor of the segment */
     size_t seg_num_chunks;  /* int32[Hkv*B]: descriptors (chunks) of the segment */
     size_t seqlens;         /* int32[B]: copy of the lengths the map was built from */
+    size_t bin_head;        /* int32[P][8], 32-byte records: (kv_head, request, tile_begin,
+                               tile_end) of bin j's first descriptor, that descriptor's index,
+                               the bin's descriptor count, the request's length, 0; all zero
+                               but the index (= Ndesc) for a bin without descriptors */
+    size_t desc_len;        /* int32[Hkv*B + P]: length of descriptor d's request */
     size_t total;           /* bytes */
 } lbsa_task_map_layout;
 

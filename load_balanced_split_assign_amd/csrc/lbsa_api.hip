@@ -97,7 +97,7 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 100; }
+LBSA_API int lbsa_version(void) { return 101; }
 
 LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_P) {
     if (!out_P || (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3))
@@ -126,6 +126,8 @@ LBSA_API int lbsa_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32
     out->seg_first_desc = m.seg_first_desc;
     out->seg_num_chunks = m.seg_num_chunks;
     out->seqlens = m.seqlens;
+    out->bin_head = m.bin_head;
+    out->desc_len = m.desc_len;
     out->total = m.total;
     return LBSA_OK;
 }

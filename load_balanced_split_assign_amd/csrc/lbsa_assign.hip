@@ -26,8 +26,10 @@ namespace lbsa {
 namespace {
 
 // Block-wide exclusive scan of one int per thread; returns the prefix and
-// writes the block total to *total (all threads).  `red` holds 16 ints.
+// writes the block total to *total (all threads).  `red` holds one int per
+// wave and must not be reused by the next scan (one barrier per scan).
 __device__ int block_exclusive_scan(int v, int* red, int* total) {
+    constexpr int kWaves = kAssignThreads / 64;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     int x = v;
@@ -38,19 +40,14 @@ __device__ int block_exclusive_scan(int v, int* red, int* total) {
     }
     if (lane == 63) red[wave] = x;
     __syncthreads();
-    if (wave == 0) {
-        int w = lane < (kAssignThreads / 64) ? red[lane] : 0;
+    int before = 0, all = 0;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            int y = __shfl_up(w, o, 64);
-            if (lane >= o) w += y;
-        }
-        if (lane < (kAssignThreads / 64)) red[16 + lane] = w;  // inclusive wave totals
+    for (int i = 0; i < kWaves; ++i) {
+        const int t = red[i];
+        before += i < wave ? t : 0;
+        all += t;
     }
-    __syncthreads();
-    const int before = wave ? red[16 + wave - 1] : 0;
-    *total = red[16 + kAssignThreads / 64 - 1];
-    __syncthreads();  // red is reused by the next scan
+    *total = all;
     return before + x - v;
 }
 
@@ -78,7 +75,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     const int32_t* __restrict__ seqlens, int B, int Hq, int Hkv, int P, int F, int max_pages,
     uint8_t* __restrict__ map) {
     extern __shared__ int smem[];
-    __shared__ int red[32];
+    __shared__ int red[2][kAssignThreads / 64];
     const MapLayout L = map_layout(B, Hkv, P);
     int32_t* hdr = reinterpret_cast<int32_t*>(map + L.header);
     int32_t* bdb = reinterpret_cast<int32_t*>(map + L.bin_desc_begin);
@@ -86,6 +83,8 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     int32_t* sfd_g = reinterpret_cast<int32_t*>(map + L.seg_first_desc);
     int32_t* snc_g = reinterpret_cast<int32_t*>(map + L.seg_num_chunks);
     int32_t* sl_g = reinterpret_cast<int32_t*>(map + L.seqlens);
+    int4* head = reinterpret_cast<int4*>(map + L.bin_head);
+    int32_t* dlen = reinterpret_cast<int32_t*>(map + L.desc_len);
 
     const int S = Hkv * B;
     int* prefix = smem;            // [B + 1]  exclusive prefix of n_b
@@ -109,7 +108,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     const int error = __syncthreads_or(bad);   // a bad length empties the map
     if (error) local = 0;
     int N;
-    int run = block_exclusive_scan(local, red, &N);
+    int run = block_exclusive_scan(local, red[0], &N);
     for (int b = b0; b < b1; ++b) {
         const int nb = error ? 0 : prefix[b];
         prefix[b] = run;
@@ -129,20 +128,22 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     }
 
     // ---- chunks per segment s = h*B + b and their exclusive prefix ---------
+    // (chunk counts are parked in sfd[] until the scan turns them into offsets)
     const int sper = (S + kAssignThreads - 1) / kAssignThreads;
     const int s0 = min(S, tid * sper), s1 = min(S, s0 + sper);
-    auto chunks = [&](int s) -> int {
+    local = 0;
+    for (int s = s0; s < s1; ++s) {
         const int h = s / B, b = s - h * B;
         const int a = h * N + prefix[b];
         const int n = prefix[b + 1] - prefix[b];
-        return n ? bins.of(a + n - 1) - bins.of(a) + 1 : 0;
-    };
-    local = 0;
-    for (int s = s0; s < s1; ++s) local += chunks(s);
+        const int c = n ? bins.of(a + n - 1) - bins.of(a) + 1 : 0;
+        sfd[s] = c;
+        local += c;
+    }
     int ndesc;
-    run = block_exclusive_scan(local, red, &ndesc);
+    run = block_exclusive_scan(local, red[1], &ndesc);
     for (int s = s0; s < s1; ++s) {
-        const int c = chunks(s);
+        const int c = sfd[s];
         sfd[s] = run;
         sfd_g[s] = run;
         snc_g[s] = c;
@@ -151,29 +152,51 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     if (tid == 0) sfd[S] = ndesc;
     __syncthreads();
 
-    // ---- descriptors: slot d belongs to the segment whose prefix covers d ---
-    for (int d = tid; d < ndesc; d += kAssignThreads) {
-        const int s = upper_bound(sfd, S, d) - 1;
-        const int h = s / B, b = s - h * B;
-        const int a = h * N + prefix[b];
-        const int n = prefix[b + 1] - prefix[b];
-        const int j = bins.of(a) + (d - sfd[s]);
-        const int g0 = max(a, bins.start(j));
-        const int g1 = min(a + n, bins.start(j + 1));
-        desc[d] = make_int4(h, b, g0 - a, g1 - a);
-    }
-
-    // ---- bin CSR: the first descriptor of bin j starts at bin_start(j) ------
-    for (int j = tid; j <= P; j += kAssignThreads) {
-        int v = ndesc;
-        if (j < bins.K) {
-            const int x = bins.start(j);
-            const int h = x / N;
-            const int b = upper_bound(prefix, B, x - h * N) - 1;
-            const int s = h * B + b;
-            v = sfd[s] + (j - bins.of(h * N + prefix[b]));
+    // ---- descriptors, bin CSR and bin heads (independent; one pass) --------
+    // Slot d belongs to the segment whose prefix covers d.  The first
+    // descriptor of bin j starts at global tile bin_start(j).
+    const int nwork = max(ndesc, P + 1);
+    for (int i = tid; i < nwork; i += kAssignThreads) {
+        if (i < ndesc) {
+            const int d = i;
+            const int s = upper_bound(sfd, S, d) - 1;
+            const int h = s / B, b = s - h * B;
+            const int a = h * N + prefix[b];
+            const int n = prefix[b + 1] - prefix[b];
+            const int j = bins.of(a) + (d - sfd[s]);
+            const int g0 = max(a, bins.start(j));
+            const int g1 = min(a + n, bins.start(j + 1));
+            desc[d] = make_int4(h, b, g0 - a, g1 - a);
+            dlen[d] = seqlens[b];
         }
-        bdb[j] = v;
+        if (i <= P) {
+            const int j = i;
+            int v = ndesc;
+            int4 rec0 = make_int4(0, 0, 0, 0);
+            int len = 0;
+            if (j < bins.K) {
+                const int x = bins.start(j), xe = bins.start(j + 1);
+                const int h = x / N;
+                const int b = upper_bound(prefix, B, x - h * N) - 1;
+                const int a = h * N + prefix[b];
+                v = sfd[h * B + b] + (j - bins.of(a));
+                rec0 = make_int4(h, b, x - a, min(prefix[b + 1] + h * N, xe) - a);
+                len = seqlens[b];
+            }
+            bdb[j] = v;
+            if (j < P) {
+                // descriptors of bin j: up to the first descriptor of bin j + 1
+                int v1 = ndesc;
+                if (j + 1 < bins.K) {
+                    const int x = bins.start(j + 1);
+                    const int h = x / N;
+                    const int b = upper_bound(prefix, B, x - h * N) - 1;
+                    v1 = sfd[h * B + b] + (j + 1 - bins.of(h * N + prefix[b]));
+                }
+                head[2 * j] = rec0;
+                head[2 * j + 1] = make_int4(v, v1 - v, len, 0);
+            }
+        }
     }
 
     if (tid == 0) {

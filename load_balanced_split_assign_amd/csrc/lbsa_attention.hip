@@ -578,26 +578,32 @@ __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const Wav
 }
 
 // Descriptor sources of the tile stream.
-struct MapDescs {           // descriptors [d0, d1) of a task-map bin
+// A descriptor as loaded from the map, before validation.
+struct RawDesc {
+    int h, b, t0, t1, L;
+};
+
+struct MapDescs {           // descriptors [d0, d0 + n) of a task-map bin
     const __attribute__((address_space(4))) int32_t* desc;
-    const __attribute__((address_space(4))) int32_t* seqlens;
-    int d0, d1, Hkv, B, max_pages;
-    __device__ int count() const { return d1 - d0; }
+    const __attribute__((address_space(4))) int32_t* dlen;
+    RawDesc head;           // descriptor d0, from the bin's head record
+    int d0, n, Hkv, B, max_pages;
+    __device__ int count() const { return n; }
     // descriptor i (0-based in the bin); an invalid one (corrupt map) has no tiles
     __device__ Desc get(int i) const {
+        RawDesc x = head;
         const int d = d0 + i;
-        Desc x;
-        x.h = desc[4 * d];
-        x.b = desc[4 * d + 1];
-        x.t0 = desc[4 * d + 2];
-        x.t1 = desc[4 * d + 3];
-        x.slot = d;
-        if (x.h < 0 || x.h >= Hkv || x.b < 0 || x.b >= B || x.t0 < 0 || x.t1 <= x.t0 || x.t1 > max_pages) {
-            x.h = 0; x.b = 0; x.t0 = 0; x.t1 = 0; x.L = 0;
+        if (i != 0) x = RawDesc{desc[4 * d], desc[4 * d + 1], desc[4 * d + 2], desc[4 * d + 3], dlen[d]};
+        Desc y;
+        y.slot = d;
+        if (x.h < 0 || x.h >= Hkv || x.b < 0 || x.b >= B || x.t0 < 0 || x.t1 <= x.t0 || x.t1 > max_pages ||
+            x.L < 0) {
+            y.h = 0; y.b = 0; y.t0 = 0; y.t1 = 0; y.L = 0;
         } else {
-            x.L = min(seqlens[x.b], max_pages * kTile);
+            y.h = x.h; y.b = x.b; y.t0 = x.t0; y.t1 = x.t1;
+            y.L = min(x.L, max_pages * kTile);
         }
-        return x;
+        return y;
     }
 };
 
@@ -607,7 +613,9 @@ struct OneDesc {            // the static kernel's single chunk
     __device__ Desc get(int) const { return d; }
 };
 
-// Cursor over the tiles of a descriptor source (wave-uniform).
+// Cursor over the tiles of a descriptor source (wave-uniform).  Past the last
+// tile it parks on that tile (or on tile 0 of an empty descriptor), so every
+// page-table index it yields stays in bounds whatever the map holds.
 template <class Src>
 struct Cursor {
     const Src* src;
@@ -616,12 +624,18 @@ struct Cursor {
     Desc d;
     __device__ void seek_valid() {      // skip descriptors without tiles
         while (i < src->count()) {
-            d = src->get(i);
-            if (d.t1 > d.t0) { t = d.t0; return; }
+            const Desc x = src->get(i);
+            if (x.t1 > x.t0) { d = x; t = x.t0; return; }
             ++i;
         }
+        t = max(d.t0, d.t1 - 1);
     }
-    __device__ void begin(const Src* s) { src = s; i = 0; seek_valid(); }
+    __device__ void begin(const Src* s) {
+        src = s;
+        i = 0;
+        d = Desc{0, 0, 0, 0, 0, 0};
+        seek_valid();
+    }
     __device__ void next() {
         if (++t >= d.t1) { ++i; seek_valid(); }
     }
@@ -646,7 +660,9 @@ __device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, C
     }
 }
 
-// Stream every tile of `src` through this workgroup (see the header comment).
+// Stream the tiles of `src` through this workgroup (see the header comment).
+// `ntiles` is the number of tiles the source holds (at least 1); with a
+// corrupt map that holds fewer, the cursors repeat their last tile.
 template <bool FP8, class Src>
 __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const Smem<FP8>& sm) {
     using SL = Stage<FP8>;
@@ -722,32 +738,35 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     sm.vb = (lds_char*)svb;                                                    \
     sm.merge = (lds_char*)smerge
 
+// One workgroup per bin (grid = P).  The header words and the bin's head
+// record are independent loads, so the first page-table and K/V loads follow
+// after a single round trip to the map.
 template <bool FP8>
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
     LBSA_DECLARE_SMEM(FP8);
     const MapLayout ML = map_layout(a.B, a.Hkv, a.P);
+    const int j = blockIdx.x;
     const auto* hdr = uniform_ptr<int32_t>(a.map + ML.header);
-    if (hdr[LBSA_HDR_ERROR] != 0 || hdr[LBSA_HDR_P] != a.P || hdr[LBSA_HDR_B] != a.B ||
-        hdr[LBSA_HDR_HKV] != a.Hkv)
-        return;
-    const auto* bdb = uniform_ptr<int32_t>(a.map + ML.bin_desc_begin);
+    const auto* rec = uniform_ptr<int32_t>(a.map + ML.bin_head) + (size_t)kBinHeadWords * j;
+    const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
+    const int h_k = hdr[LBSA_HDR_K], h_q = hdr[LBSA_HDR_Q], h_r = hdr[LBSA_HDR_R];
+    const int r_h = rec[BH_H], r_b = rec[BH_B], r_t0 = rec[BH_T0], r_t1 = rec[BH_T1];
+    const int r_first = rec[BH_FIRST], r_count = rec[BH_COUNT], r_len = rec[BH_L];
+    if (h_err != 0 || h_p != a.P || h_b != a.B || h_hkv != a.Hkv) return;
     const int cap = a.Hkv * a.B + a.P;
-    for (int j = blockIdx.x; j < a.P; j += gridDim.x) {
-        MapDescs src;
-        src.desc = uniform_ptr<int32_t>(a.map + ML.desc);
-        src.seqlens = uniform_ptr<int32_t>(a.map + ML.seqlens);
-        src.d0 = max(0, min(bdb[j], cap));
-        src.d1 = max(src.d0, min(bdb[j + 1], cap));
-        src.Hkv = a.Hkv;
-        src.B = a.B;
-        src.max_pages = a.max_pages;
-        int ntiles = 0;
-        for (int i = 0; i < src.count(); ++i) {
-            const Desc d = src.get(i);
-            ntiles += d.t1 - d.t0;
-        }
-        if (ntiles > 0) run_stream<FP8>(a, src, ntiles, sm);
-    }
+    if (r_count <= 0 || r_first < 0 || r_count > cap - r_first) return;
+    MapDescs src;
+    src.desc = uniform_ptr<int32_t>(a.map + ML.desc);
+    src.dlen = uniform_ptr<int32_t>(a.map + ML.desc_len);
+    src.d0 = r_first;
+    src.n = r_count;
+    src.Hkv = a.Hkv;
+    src.B = a.B;
+    src.max_pages = a.max_pages;
+    src.head = RawDesc{r_h, r_b, r_t0, r_t1, r_len};
+    // tiles of bin j from the header's bin sizes (the descriptors' tiles sum to it)
+    const int ntiles = j < h_k ? min(h_q + (j < h_r ? 1 : 0), a.B * a.max_pages) : 0;
+    if (ntiles > 0) run_stream<FP8>(a, src, ntiles, sm);
 }
 
 template <bool FP8>
@@ -827,14 +846,20 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
         d0 = seg * a.P;
         n = a.P;
     } else {
+        // header words and the segment's chunk range are independent loads
+        // (the segment index is in range for any map of this shape)
         const MapLayout ML = map_layout(a.B, a.Hkv, a.P);
-        const int32_t* hdr = reinterpret_cast<const int32_t*>(a.map + ML.header);
-        if (hdr[LBSA_HDR_P] != a.P || hdr[LBSA_HDR_B] != a.B || hdr[LBSA_HDR_HKV] != a.Hkv) {
+        const auto* hdr = uniform_ptr<int32_t>(a.map + ML.header);
+        const int h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
+        const int h_err = hdr[LBSA_HDR_ERROR];
+        const int sd0 = uniform_ptr<int32_t>(a.map + ML.seg_first_desc)[seg];
+        const int sn = uniform_ptr<int32_t>(a.map + ML.seg_num_chunks)[seg];
+        if (h_p != a.P || h_b != a.B || h_hkv != a.Hkv) {
             poison = true;
-        } else if (hdr[LBSA_HDR_ERROR] == 0) {
+        } else if (h_err == 0) {
             const int cap = a.Hkv * a.B + a.P;
-            d0 = reinterpret_cast<const int32_t*>(a.map + ML.seg_first_desc)[seg];
-            n = reinterpret_cast<const int32_t*>(a.map + ML.seg_num_chunks)[seg];
+            d0 = sd0;
+            n = sn;
             if (d0 < 0 || n < 0 || d0 + n > cap) { poison = true; n = 0; }
         }
     }

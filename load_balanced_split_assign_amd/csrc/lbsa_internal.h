@@ -21,8 +21,14 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // Byte offsets of the task-map arrays for (B, Hkv, P).
 struct MapLayout {
-    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seqlens, total;
+    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seqlens, bin_head, desc_len, total;
 };
+
+// Words of one bin_head record: the bin's first descriptor, its slot, the
+// bin's descriptor count and the request's length (everything a split
+// workgroup needs to start streaming).
+constexpr int kBinHeadWords = 8;
+enum { BH_H = 0, BH_B = 1, BH_T0 = 2, BH_T1 = 3, BH_FIRST = 4, BH_COUNT = 5, BH_L = 6 };
 
 __host__ __device__ inline MapLayout map_layout(int B, int Hkv, int P) {
     MapLayout m;
@@ -34,7 +40,9 @@ __host__ __device__ inline MapLayout map_layout(int B, int Hkv, int P) {
     m.seg_first_desc = m.desc + 16 * cap;
     m.seg_num_chunks = m.seg_first_desc + 4 * S;
     m.seqlens = m.seg_num_chunks + 4 * S;
-    m.total = align_up(m.seqlens + 4 * (size_t)B, 256);
+    m.bin_head = align_up(m.seqlens + 4 * (size_t)B, 32);
+    m.desc_len = m.bin_head + 4 * kBinHeadWords * (size_t)P;
+    m.total = align_up(m.desc_len + 4 * cap, 256);
     return m;
 }
 

@@ -33,7 +33,8 @@ class LbsaError(RuntimeError):
 
 class _MapLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("header", "bin_desc_begin", "desc", "seg_first_desc", "seg_num_chunks", "seqlens", "total")]
+                ("header", "bin_desc_begin", "desc", "seg_first_desc", "seg_num_chunks", "seqlens", "bin_head",
+                 "desc_len", "total")]
 
 
 class _WsLayout(ctypes.Structure):
@@ -253,11 +254,13 @@ def read_task_map(task_map: torch.Tensor, batch: int, num_kv_heads: int, P: int)
     out = {"header": header, "bin_desc_begin": arr(lay["bin_desc_begin"], P + 1),
            "desc_all": arr(lay["desc"], 4 * cap, (cap, 4)),
            "seg_first_desc": arr(lay["seg_first_desc"], S), "seg_num_chunks": arr(lay["seg_num_chunks"], S),
-           "seqlens": arr(lay["seqlens"], batch)}
+           "seqlens": arr(lay["seqlens"], batch), "bin_head": arr(lay["bin_head"], 8 * P, (P, 8)),
+           "desc_len_all": arr(lay["desc_len"], cap)}
     for i, name in enumerate(HEADER_FIELDS):
         out[name] = int(header[i])
     nd = max(0, min(out["Ndesc"], cap))
     out["desc"] = out["desc_all"][:nd].copy()
+    out["desc_len"] = out["desc_len_all"][:nd].copy()
     return out
 
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 100
+    assert lbsa.lib().lbsa_version() == 101
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -44,7 +44,9 @@ def test_task_map_layout_is_aligned_and_sized():
         assert lay["seg_first_desc"] == lay["desc"] + 16 * cap
         assert lay["seg_num_chunks"] == lay["seg_first_desc"] + 4 * S
         assert lay["seqlens"] == lay["seg_num_chunks"] + 4 * S
-        assert lay["total"] >= lay["seqlens"] + 4 * B and lay["total"] % 256 == 0
+        assert lay["bin_head"] % 32 == 0 and lay["bin_head"] >= lay["seqlens"] + 4 * B
+        assert lay["desc_len"] == lay["bin_head"] + 32 * P
+        assert lay["total"] >= lay["desc_len"] + 4 * cap and lay["total"] % 256 == 0
         assert lbsa.task_map_bytes(B, Hkv, P) == lay["total"]
 
 

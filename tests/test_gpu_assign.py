@@ -1,8 +1,9 @@
 """GPU assign kernel vs the oracle's assign: the task map must be bit-exact.
 
 Compared: header words 0..13, bin CSR (P + 1 entries), descriptors [0, Ndesc),
-per-segment first descriptor and chunk count, and the length copy.  Slots of
-the descriptor array past Ndesc are unspecified and not compared.
+per-segment first descriptor and chunk count, the length copy, and the per-bin
+head records (expected values built from the oracle's descriptors and CSR).
+Slots of the descriptor array past Ndesc are unspecified and not compared.
 """
 import numpy as np
 import pytest
@@ -32,7 +33,27 @@ def assert_same_map(oracle_mod, seqlens, Hq, Hkv, P, F, max_pages, what=""):
     np.testing.assert_array_equal(g["seg_first_desc"], o["seg_first_desc"], err_msg=str(ctx))
     np.testing.assert_array_equal(g["seg_num_chunks"], o["seg_num_chunks"], err_msg=str(ctx))
     np.testing.assert_array_equal(g["seqlens"], np.asarray(seqlens, np.int32), err_msg=str(ctx))
+    sl = np.asarray(seqlens, np.int32)
+    np.testing.assert_array_equal(g["bin_head"], expected_bin_head(o, P, sl), err_msg=str(ctx))
+    np.testing.assert_array_equal(g["desc_len"], sl[np.asarray(o["desc"], np.int64)[:, 1]] if len(o["desc"]) else
+                                  np.zeros(0, np.int32), err_msg=str(ctx))
     return g
+
+
+def expected_bin_head(o, P, seqlens):
+    """Head record of each bin from the oracle's map: first descriptor of the
+    bin (zeros if none), its index, the bin's descriptor count, the length of
+    the descriptor's request, 0."""
+    bdb = np.asarray(o["bin_desc_begin"], np.int64)
+    head = np.zeros((P, 8), np.int32)
+    for j in range(P):
+        d0, d1 = int(bdb[j]), int(bdb[j + 1])
+        head[j, 4] = d0
+        head[j, 5] = d1 - d0
+        if d1 > d0:
+            head[j, :4] = o["desc"][d0]
+            head[j, 6] = seqlens[o["desc"][d0][1]]
+    return head
 
 
 @pytest.mark.parametrize("name", ["tiny", "tp8_share", "skewed", "fp8", "long", "floor",
