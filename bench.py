@@ -4,8 +4,9 @@
 A step is one pass of the whole path over one synthetic batch already resident
 in HBM: assign (task map) + persistent split + combine.  Before every timed
 step a 512 MiB buffer is streamed through so neither L2 nor the 256 MB Infinity
-Cache still holds K/V from the previous step; HIP events on the launch stream bracket
-each kernel, the flush stays outside them.  The default flush reads the buffer
+Cache still holds K/V from the previous step.  HIP events on the launch stream
+bracket each step (one pair, nothing between the kernels) and, in a second
+pass, each kernel; the flush stays outside them.  The default flush reads the buffer
 (a reduction), so the caches hold clean lines and no write-back competes with
 the timed kernels.
 
@@ -105,14 +106,23 @@ def make_flush(mode):
 
 
 def time_steps(path, steps, warmup, flush):
-    """Per-step event times (us) of assign, split, combine and the whole step."""
+    """Per-step event times (us).  Pass 1 brackets each whole step with one
+    event pair (no markers between the kernels, as in real use); pass 2 adds an
+    event between the kernels for the per-kernel split (each marker adds a
+    dispatch gap of its own, so pass 2's sum exceeds pass 1's step)."""
     import torch
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(warmup):
         flush(i)
         path.assign(); path.split(); path.combine()
     torch.cuda.synchronize()
+    whole = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        flush(i)
+        whole[i][0].record(stream)
+        path.assign(); path.split(); path.combine()
+        whole[i][1].record(stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         flush(i)
         e = ev[i]
@@ -125,7 +135,8 @@ def time_steps(path, steps, warmup, flush):
         e[3].record(stream)
     torch.cuda.synchronize()
     us = lambda a, b: [1000.0 * ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)]  # noqa: E731
-    return {"assign": us(0, 1), "split": us(1, 2), "combine": us(2, 3), "layer": us(1, 3), "step": us(0, 3)}
+    return {"assign": us(0, 1), "split": us(1, 2), "combine": us(2, 3), "layer": us(1, 3),
+            "step_markers": us(0, 3), "step": [1000.0 * a.elapsed_time(b) for a, b in whole]}
 
 
 def time_steps_graph(path, steps, warmup, flush):
