@@ -142,7 +142,7 @@ int lbsa_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
  * Bins: T = Hkv * sum_b ceil(L_b/64) tiles in head-major, batch-minor order;
  * K = min(P, max(1, floor(T/F))) active bins; the first T mod K bins hold
  * ceil(T/K) tiles, the rest floor(T/K); each maximal run of one (kv_head,
- * request) inside a bin is one descriptor.  Limits: (batch + Hkv*batch) <= 16382
+ * request) inside a bin is one descriptor.  Limits: (2*batch + Hkv*batch) <= 16382
  * (LDS of the single assign workgroup), batch * max_pages_per_seq * Hkv < 2^30.
  */
 int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_heads, int32_t num_kv_heads,

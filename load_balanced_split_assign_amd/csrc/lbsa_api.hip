@@ -179,8 +179,8 @@ LBSA_API int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_head
     if (!seqlens_d || !task_map_d || max_pages_per_seq <= 0 || num_workgroups <= 0 ||
         min_tiles_per_bin < 0 || !aligned(task_map_d, 16) || !aligned(seqlens_d, 4))
         return LBSA_ERR_INVALID_ARGUMENT;
-    // the single assign workgroup keeps (B + 1) + (Hkv*B + 1) ints in LDS
-    if ((long long)batch + 1 + (long long)num_kv_heads * batch + 1 > kMaxAssignLdsWords)
+    // the single assign workgroup keeps (B + 1) + (Hkv*B + 1) + B ints in LDS
+    if (2LL * batch + 1 + (long long)num_kv_heads * batch + 1 > kMaxAssignLdsWords)
         return LBSA_ERR_UNSUPPORTED;
     // every tile index and prefix stays far from int32 overflow
     if ((long long)batch * max_pages_per_seq * num_kv_heads >= (1LL << 30) ||

@@ -18,8 +18,9 @@
 // and bin starts bin_start(j) = j*q + min(j, r).  Hence
 //   chunks(s) = bin_of(last tile of s) - bin_of(first tile of s) + 1,
 // descriptor slots are the exclusive prefix of chunks(s) in (h, b) order, and
-// descriptor d is reconstructed independently by a binary search over that
-// prefix.  Every step is a scan or a search, so the 256 threads share the work.
+// each bin's descriptors are emitted by one thread walking the bin's tile range
+// from its first slot.  Every step is a scan, a search or a short walk, so the
+// 256 threads share the work.
 #include "lbsa_internal.h"
 
 namespace lbsa {
@@ -89,6 +90,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     const int S = Hkv * B;
     int* prefix = smem;            // [B + 1]  exclusive prefix of n_b
     int* sfd = smem + B + 1;       // [S + 1]  exclusive prefix of chunks(s)
+    int* lens = sfd + S + 1;       // [B]      the lengths (read once from global)
     const int tid = threadIdx.x;
 
     // ---- tile census: n_b = ceil(L_b / 64) (one pass over the lengths, n_b
@@ -99,6 +101,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     for (int b = b0; b < b1; ++b) {
         const int len = seqlens[b];
         sl_g[b] = len;
+        lens[b] = len;
         const bool ok = len >= 0 && (long long)len <= (long long)max_pages * kTile;
         bad |= !ok;
         const int nb = ok ? (len + kTile - 1) / kTile : 0;
@@ -152,50 +155,49 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     if (tid == 0) sfd[S] = ndesc;
     __syncthreads();
 
-    // ---- descriptors, bin CSR and bin heads (independent; one pass) --------
-    // Slot d belongs to the segment whose prefix covers d.  The first
-    // descriptor of bin j starts at global tile bin_start(j).
-    const int nwork = max(ndesc, P + 1);
-    for (int i = tid; i < nwork; i += kAssignThreads) {
-        if (i < ndesc) {
-            const int d = i;
-            const int s = upper_bound(sfd, S, d) - 1;
-            const int h = s / B, b = s - h * B;
-            const int a = h * N + prefix[b];
-            const int n = prefix[b + 1] - prefix[b];
-            const int j = bins.of(a) + (d - sfd[s]);
-            const int g0 = max(a, bins.start(j));
-            const int g1 = min(a + n, bins.start(j + 1));
-            desc[d] = make_int4(h, b, g0 - a, g1 - a);
-            dlen[d] = seqlens[b];
-        }
-        if (i <= P) {
-            const int j = i;
-            int v = ndesc;
-            int4 rec0 = make_int4(0, 0, 0, 0);
-            int len = 0;
-            if (j < bins.K) {
-                const int x = bins.start(j), xe = bins.start(j + 1);
-                const int h = x / N;
-                const int b = upper_bound(prefix, B, x - h * N) - 1;
-                const int a = h * N + prefix[b];
-                v = sfd[h * B + b] + (j - bins.of(a));
-                rec0 = make_int4(h, b, x - a, min(prefix[b + 1] + h * N, xe) - a);
-                len = seqlens[b];
-            }
-            bdb[j] = v;
-            if (j < P) {
-                // descriptors of bin j: up to the first descriptor of bin j + 1
-                int v1 = ndesc;
-                if (j + 1 < bins.K) {
-                    const int x = bins.start(j + 1);
-                    const int h = x / N;
-                    const int b = upper_bound(prefix, B, x - h * N) - 1;
-                    v1 = sfd[h * B + b] + (j + 1 - bins.of(h * N + prefix[b]));
+    // ---- bins: thread j walks bin j's tile range [bin_start(j), bin_start(j+1))
+    // segment by segment and emits its descriptors, which take consecutive
+    // slots from the bin's first one (the first slot of bin j counts every
+    // chunk of earlier segments plus the chunks of its first segment that lie
+    // in earlier bins) -------------------------------------------------------
+    for (int j = tid; j <= P; j += kAssignThreads) {
+        int v = ndesc;
+        int4 rec0 = make_int4(0, 0, 0, 0);
+        int len0 = 0, count = 0;
+        if (j < bins.K) {
+            int x = bins.start(j);
+            const int xe = bins.start(j + 1);
+            int h = x / N;
+            int b = upper_bound(prefix, B, x - h * N) - 1;
+            int a = h * N + prefix[b];
+            v = sfd[h * B + b] + (j - bins.of(a));
+            const int cap = S + P;                             // descriptor slots in the map
+            for (int d = v; d < cap; ++d) {
+                const int e = h * N + prefix[b + 1];          // end of segment (h, b)
+                const int t1 = min(e, xe);
+                const int4 dd = make_int4(h, b, x - a, t1 - a);
+                desc[d] = dd;
+                dlen[d] = lens[b];
+                if (d == v) { rec0 = dd; len0 = lens[b]; }
+                ++count;
+                if (t1 >= xe) break;
+                // next non-empty segment: step over a few empty requests, else search
+                x = t1;
+                int k = 0;
+                do {
+                    if (++b == B) { b = 0; ++h; }
+                } while (prefix[b + 1] == prefix[b] && ++k < 4);
+                if (prefix[b + 1] == prefix[b]) {
+                    h = x / N;
+                    b = upper_bound(prefix, B, x - h * N) - 1;
                 }
-                head[2 * j] = rec0;
-                head[2 * j + 1] = make_int4(v, v1 - v, len, 0);
+                a = h * N + prefix[b];
             }
+        }
+        bdb[j] = v;
+        if (j < P) {
+            head[2 * j] = rec0;
+            head[2 * j + 1] = make_int4(v, count, len0, 0);
         }
     }
 
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
 
 hipError_t launch_assign(const int32_t* seqlens, int B, int Hq, int Hkv, int P, int F,
                          int max_pages, void* map, hipStream_t stream) {
-    const size_t lds = sizeof(int) * ((size_t)B + 1 + (size_t)Hkv * B + 1);
+    const size_t lds = sizeof(int) * (2 * (size_t)B + 1 + (size_t)Hkv * B + 1);
     hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), lds, stream, seqlens, B, Hq,
                        Hkv, P, F, max_pages, static_cast<uint8_t*>(map));
     return hipGetLastError();

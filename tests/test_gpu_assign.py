@@ -75,8 +75,8 @@ def test_random_maps_bitexact(oracle_mod):
     for it in range(150):
         B = int(rng.integers(1, 400))
         Hkv = int(rng.choice([1, 2, 4, 8]))
-        if B + 1 + Hkv * B + 1 > 16382:
-            B = 16380 // (Hkv + 1)
+        if 2 * B + 1 + Hkv * B + 1 > 16384:
+            B = 16382 // (Hkv + 2)
         sl = rng.integers(0, 5000, B)
         sl[rng.random(B) < 0.1] = 0
         sl[rng.random(B) < 0.1] = 64 * rng.integers(1, 40)
@@ -90,10 +90,10 @@ def test_random_maps_bitexact(oracle_mod):
 
 def test_large_batch_and_segment_count(oracle_mod):
     rng = np.random.default_rng(7)
-    sl = rng.integers(0, 3000, 1800).astype(np.int32).tolist()       # 1800 + 14400 + 2 ints of LDS
-    assert_same_map(oracle_mod, sl, 64, 8, 1024, 0, 47, "B=1800 Hkv=8")
-    sl = rng.integers(1, 9000, 8000).astype(np.int32).tolist()       # Hkv = 1, batch 8000
-    assert_same_map(oracle_mod, sl, 8, 1, 2048, 0, 141, "B=8000 Hkv=1")
+    sl = rng.integers(0, 3000, 1630).astype(np.int32).tolist()       # 2*1630 + 13040 + 2 ints of LDS
+    assert_same_map(oracle_mod, sl, 64, 8, 1024, 0, 47, "B=1630 Hkv=8")
+    sl = rng.integers(1, 9000, 5400).astype(np.int32).tolist()       # Hkv = 1, batch 5400
+    assert_same_map(oracle_mod, sl, 8, 1, 2048, 0, 141, "B=5400 Hkv=1")
 
 
 def test_bad_lengths_set_error_and_empty_map(oracle_mod):
