@@ -190,6 +190,73 @@ def time_static(batch, S, steps, warmup, flush):
     return summarize(times)
 
 
+def time_layer(path, steps, warmup, flush, with_assign=False):
+    """Event time (us) of split + combine (plus assign if asked) with one event
+    pair around them, as a layer (or a step) runs in use."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def run():
+        if with_assign:
+            path.assign()
+        path.split()
+        path.combine()
+    path.assign()            # the map the layers reuse
+    for i in range(warmup):
+        flush(i)
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        flush(i)
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return summarize([1000.0 * a.elapsed_time(b) for a, b in ev])
+
+
+def static_sweep(batch, P, steps, warmup, flush, splits=(1, 2, 4, 8, 16, 32, 64)):
+    """Static split-KV at the heuristic S = ceil(P / (B * Hkv)) and over a sweep of S."""
+    heur = max(1, -(-P // (batch["B"] * batch["num_kv_heads"])))
+    sweep = {S: time_static(batch, S, steps, warmup, flush)["mean"] for S in splits}
+    heur_t = sweep.get(heur) or time_static(batch, heur, steps, warmup, flush)["mean"]
+    best = min(sweep, key=sweep.get)
+    return heur, heur_t, best, sweep
+
+
+def table3(args):
+    """The six KV-length mixes of the vLLM post's Table 3 (fp8 KV, 8 query heads /
+    1 KV head): dynamic (map reused: split + combine; and with assign) against
+    the static split-KV kernel."""
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    from load_balanced_split_assign_amd import workload as wl
+    flush = make_flush(args.flush)
+    rows = []
+    for name in wl.TABLE3:
+        b = gpu_batch(name)
+        w = wl.WORKLOADS[name]
+        P = args.workgroups or lbsa.default_workgroups(0, w.kv_dtype)
+        sl = [int(x) for x in b["seqlens"].cpu()]
+        ab = alg_bytes(sl, b["num_heads"], b["num_kv_heads"], 128, w.kv_dtype)
+        path = Path(b, P)
+        layer = time_layer(path, args.steps, args.warmup, flush)["mean"]
+        step = time_layer(path, args.steps, args.warmup, flush, with_assign=True)["mean"]
+        heur, heur_t, best, sweep = static_sweep(b, P, max(10, args.steps // 2), 3, flush)
+        rows.append({"mix": name[3:], "batch": b["B"], "live_tokens": sum(sl), "alg_bytes": ab["layer"],
+                     "dynamic_layer_us": round(layer, 2), "dynamic_step_us": round(step, 2),
+                     "layer_GBps": round(ab["layer"] / layer / 1e3, 1),
+                     "static_heuristic_S": heur, "static_heuristic_us": round(heur_t, 2),
+                     "static_best_S": best, "static_best_us": round(sweep[best], 2),
+                     "speedup_vs_static_best": round(sweep[best] / layer, 3),
+                     "speedup_vs_static_heuristic": round(heur_t / layer, 3)})
+        del b, path
+        torch.cuda.empty_cache()
+    print(json.dumps({"table3": rows, "P": P, "unit": "us", "flush": args.flush}), flush=True)
+
+
 def gpu_batch(name, tail="normal"):
     import torch
 
@@ -315,6 +382,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device copy first (reference for PMC byte counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (bounded sample)")
+    ap.add_argument("--table3", action="store_true",
+                    help="instead of the headline line: the six fp8 KV-length mixes, dynamic vs static")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; each with "
                          "--calib-copy) into the split kernel's HBM bytes per launch")
@@ -331,6 +400,10 @@ def main():
 
     from load_balanced_split_assign_amd import lbsa
     from load_balanced_split_assign_amd import workload as wl
+
+    if args.table3:
+        table3(args)
+        return
 
     if args.calib_copy:   # a plain copy of known size: FETCH_SIZE / WRITE_SIZE reference
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
@@ -386,11 +459,8 @@ def main():
     if not args.no_static:
         sk = gpu_batch("skewed")
         Pk = lbsa.default_workgroups(0, "bf16")
-        dyn = summarize(time_steps(Path(sk, Pk), 20, 3, flush)["layer"])
-        heur = max(1, -(-Pk // (sk["B"] * sk["num_kv_heads"])))
-        sweep = {S: time_static(sk, S, 10, 2, flush)["mean"] for S in (1, 2, 4, 8, 16, 32, 64)}
-        heur_t = sweep.get(heur) or time_static(sk, heur, 10, 2, flush)["mean"]
-        best_S = min(sweep, key=sweep.get)
+        dyn = time_layer(Path(sk, Pk), 20, 3, flush)
+        heur, heur_t, best_S, sweep = static_sweep(sk, Pk, 10, 2, flush)
         rec["static_baseline"] = {
             "workload": "skewed", "P": Pk, "dynamic_layer_us": round(dyn["mean"], 2),
             "static_heuristic_S": heur, "static_heuristic_us": round(heur_t, 2),
