@@ -289,18 +289,27 @@ __device__ inline void lds_read_tile_fp8(uint4 (&o)[6], const uint32_t (&addr)[6
 
 // ---------------------------------------------------------------------------
 // Per-wave LDS ring stage.  bf16: K 16 x 256 B, V 16 x 256 B.  fp8: K 16 x 128
-// B, V 16 x 128 B, k scales (256 B: rows 0-15, then copies), v scales (256 B).
+// B, V 16 x 128 B, k scales (256 B: rows 0-15, then copies), v scales (256 B),
+// the q scales of the tile's descriptor (256 B: heads 0-7, then copies) and,
+// on a descriptor's first tile, its Q codes (8 heads x 128 B).  Q and its
+// scales travel through the ring so that reading them needs no wait on a
+// register load (which the compiler turns into a wait for the whole ring).
 // ---------------------------------------------------------------------------
 template <bool FP8> struct Stage {
     static constexpr int kRow = FP8 ? 128 : 256;        // bytes of one K/V row
     static constexpr int K = 0;
     static constexpr int V = 16 * kRow;
-    static constexpr int KS = 32 * kRow;                // fp8 only
-    static constexpr int VS = KS + 256;                 // fp8 only
-    static constexpr int BYTES = FP8 ? VS + 256 : 32 * kRow;      // 4608 (fp8) / 8192 (bf16)
+    static constexpr int KS = 32 * kRow;                // fp8 only: k scales
+    static constexpr int VS = KS + 256;                 // fp8 only: v scales
+    static constexpr int QS = VS + 256;                 // fp8 only: the 8 q scales of the descriptor
+    static constexpr int QD = QS + 256;                 // fp8 only: Q codes, 8 heads x 128 B (first tiles)
+    static constexpr int BYTES = FP8 ? QD + 1024 : 32 * kRow;     // 5888 (fp8) / 8192 (bf16)
     static constexpr int KV_LOADS = 16 * kRow / 1024;   // loads per K (or V) slice: 4 (bf16) / 2 (fp8)
-    static constexpr int LOADS = 2 * KV_LOADS + (FP8 ? 2 : 0);   // ring loads issued per tile
-    static constexpr int STAGES = FP8 ? 6 : 4;          // ring depth: STAGES - 1 tiles in flight
+    // ring loads issued for every tile (fp8 adds one more, the Q codes, on a
+    // descriptor's first tile; the waits count only the fixed ones, which can
+    // only make them wait for a little more than the stage)
+    static constexpr int LOADS = 2 * KV_LOADS + (FP8 ? 3 : 0);
+    static constexpr int STAGES = FP8 ? 5 : 4;          // ring depth: STAGES - 1 tiles in flight
 };
 static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt range");
 static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
@@ -313,20 +322,28 @@ __device__ inline int swz_bf16(int row) { return row & 15; }
 // __shared__ object: the compiler's wait-count insertion can then tell which
 // asynchronous load an LDS read depends on (distinct underlying objects) and
 // does not fall back to waiting for all of them.
+//
+// Each wave has one slot (kWaveSlot bytes) that holds its bf16 copy of the
+// fp8 V slice during a tile and its (O, m, l, flag) for the merge at the end of
+// a descriptor; the two uses of a slot never overlap in time (program order
+// within the wave, and the merge's closing barrier before any wave's next
+// tile), so for fp8 they share the memory.
 constexpr int kMergeWave = (kGroup * kHeadDim + 2 * kGroup + 4) * 4;   // O, m, l, flag per wave
-constexpr int kMergeBytes = kWaves * kMergeWave;
-constexpr int kVbBytes = kWaves * 16 * 256;
+constexpr int kVbWave = 16 * 256;                                      // 16 V rows as bf16
+constexpr int kWaveSlot = 17 * 256;                                    // >= both, 256-aligned
+static_assert(kWaveSlot >= kMergeWave && kWaveSlot >= kVbWave, "wave slot");
+constexpr int kSlotBytes = kWaves * kWaveSlot;
 constexpr int kMaxStages = 6;
 template <bool FP8> struct Smem {
     lds_char* stage[kMaxStages];   // [kWaves][Stage::BYTES] each; the first STAGES are used
-    lds_char* vb;                  // fp8: [kWaves][16 x 256 B] bf16 copy of the V slice
-    lds_char* merge;               // [kMergeBytes]
+    lds_char* vb;                  // fp8: [kWaves][kWaveSlot], the bf16 copy of the V slice
+    lds_char* merge;               // [kWaves][kWaveSlot] (for fp8 the same memory as vb)
 };
 template <bool FP8> constexpr int stage_array_bytes(int u) {
     return u < Stage<FP8>::STAGES ? kWaves * Stage<FP8>::BYTES : 16;
 }
-static_assert(kWaves * Stage<false>::BYTES * Stage<false>::STAGES + kMergeBytes <= 160 * 1024, "LDS");
-static_assert(kWaves * Stage<true>::BYTES * Stage<true>::STAGES + kVbBytes + kMergeBytes <= 160 * 1024, "LDS");
+static_assert(kWaves * Stage<false>::BYTES * Stage<false>::STAGES + kSlotBytes <= 160 * 1024, "LDS");
+static_assert(kWaves * Stage<true>::BYTES * Stage<true>::STAGES + kSlotBytes <= 160 * 1024, "LDS");
 
 // One descriptor of the tile stream (all fields wave-uniform).
 struct Desc {
@@ -377,6 +394,7 @@ __device__ inline void issue_tile(const AttnArgs& a, const LaneLoads<FP8>& ll, l
         const int srow = (full || tok0 + ll.scale_row < d.L) ? 16 * w + ll.scale_row : 0;
         dma4(a.k_scale + sbase + srow, st + SL::KS);
         dma4(a.v_scale + sbase + srow, st + SL::VS);
+        dma4(a.q_scale + ((size_t)d.b * a.Hq + (size_t)d.h * kGroup) + (threadIdx.x & 7), st + SL::QS);
     }
 }
 
@@ -388,25 +406,26 @@ struct WaveState {
 };
 
 // Q operand of a descriptor (B of S^T = K Q^T): head r of the group (zero for
-// r >= 8), as bf16 (bf16 KV) or raw e4m3 codes (fp8 KV), plus the Q scale.
+// r >= 8), as bf16 (bf16 KV: register loads) or raw e4m3 codes (fp8 KV: read
+// from the ring stage of the descriptor's first tile).
 template <bool FP8> struct QOp;
 template <> struct QOp<false> { uint4 v[4]; };
-template <> struct QOp<true> { uint4 v[2]; float scale; };
+template <> struct QOp<true> { uint4 v[2]; };
 
-// Plain loads into registers, issued when the load cursor enters a descriptor
-// (its first tile), several tiles before the compute cursor needs them.
+// bf16: plain loads into registers, issued when the load cursor enters a
+// descriptor (its first tile), several tiles before the compute cursor needs
+// them.  fp8: the 8 x 128 B of Q codes go into the stage with that first tile
+// (lane i moves bytes [16 i, 16 i + 16) of the row-major block).
 template <bool FP8>
-__device__ inline void load_q(const AttnArgs& a, const Desc& d, int r, int g, QOp<FP8>& q) {
-    const size_t row = (size_t)d.b * a.Hq + (size_t)d.h * kGroup + (r & 7);
+__device__ inline void load_q(const AttnArgs& a, const Desc& d, int r, int g, QOp<FP8>& q, lds_char* st) {
     if constexpr (!FP8) {
+        const size_t row = (size_t)d.b * a.Hq + (size_t)d.h * kGroup + (r & 7);
         const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + row * 256);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) q.v[ks] = qp[g + 4 * ks];
     } else {
-        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + row * 128);
-        q.v[0] = qp[g];            // k-steps 0, 1
-        q.v[1] = qp[g + 4];        // k-steps 2, 3
-        q.scale = a.q_scale[row];
+        const size_t row0 = (size_t)d.b * a.Hq + (size_t)d.h * kGroup;
+        dma16(static_cast<const char*>(a.q) + row0 * 128 + 16 * (threadIdx.x & 63), st + Stage<true>::QD);
     }
 }
 
@@ -529,7 +548,7 @@ __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const Wav
     float lsum = ws.l;
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
-    lds_float* o_w = reinterpret_cast<lds_float*>(merge + w * kMergeWave);
+    lds_float* o_w = reinterpret_cast<lds_float*>(merge + w * kWaveSlot);
     if (r < kGroup) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
@@ -548,7 +567,7 @@ __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const Wav
         bool any_bad = false;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * kMergeWave);
+            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * kWaveSlot);
             M = fmaxf(M, ow[kGroup * kHeadDim + hh]);
             any_bad |= ow[kGroup * kHeadDim + 2 * kGroup] != 0.f;
         }
@@ -556,7 +575,7 @@ __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const Wav
         float lt = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * kMergeWave);
+            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * kWaveSlot);
             const float mw = ow[kGroup * kHeadDim + hh];
             const float sw = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
             lt += sw * ow[kGroup * kHeadDim + kGroup + hh];
@@ -652,7 +671,7 @@ __device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, C
                                   int slot, int w, int r, int g) {
     const bool ok = page >= 0 && page < a.num_pages;
     bad_bits = (bad_bits & ~(1u << slot)) | ((uint32_t)(!ok) << slot);
-    if (issued < ntiles && lc.t == lc.d.t0) load_q<FP8>(a, lc.d, r, g, qslot);
+    if (issued < ntiles && lc.t == lc.d.t0) load_q<FP8>(a, lc.d, r, g, qslot, st);
     issue_tile<FP8>(a, ll, st, ok ? page : 0, lc.d, lc.t, w);
     if (++issued < ntiles) {
         lc.next();
@@ -670,7 +689,7 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     auto stage = [&](int u) -> lds_char* { return sm.stage[u] + w * SL::BYTES; };
-    lds_char* vb = sm.vb + w * (16 * 256);
+    lds_char* vb = sm.vb + w * kWaveSlot;
     LaneLoads<FP8> ll;
     ll.init(a.Hkv, w, lane);
 
@@ -700,9 +719,13 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
             wait_vmcnt<(S - 1) * SL::LOADS>();                             // tile kk has landed
             if (kk < ntiles) {
                 if (cc.t == cc.d.t0) {                                     // first tile of a descriptor
-                    q = qring[u];
+                    if constexpr (FP8)
+                        lds_read2x16(q.v[0], q.v[1], lds_addr(stage(u) + SL::QD) + 128 * (r & 7) + 16 * g,
+                                     lds_addr(stage(u) + SL::QD) + 128 * (r & 7) + 16 * g + 64);
+                    else
+                        q = qring[u];
                     sl2 = a.scale_log2;
-                    if constexpr (FP8) sl2 *= q.scale;
+                    if constexpr (FP8) sl2 *= lds_read_f32(lds_addr(stage(u) + SL::QS) + 4 * (r & 7));
 #pragma unroll
                     for (int db = 0; db < 8; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
                     ws.m = kNegInf;
@@ -726,8 +749,7 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     __shared__ __attribute__((aligned(16))) char s3[stage_array_bytes<FP8>(3)]; \
     __shared__ __attribute__((aligned(16))) char s4[stage_array_bytes<FP8>(4)]; \
     __shared__ __attribute__((aligned(16))) char s5[stage_array_bytes<FP8>(5)]; \
-    __shared__ __attribute__((aligned(16))) char svb[FP8 ? kVbBytes : 16];      \
-    __shared__ __attribute__((aligned(16))) char smerge[kMergeBytes];           \
+    __shared__ __attribute__((aligned(16))) char sslot[kSlotBytes];             \
     Smem<FP8> sm; /* address-space casts to LDS */                             \
     sm.stage[0] = (lds_char*)s0;                                               \
     sm.stage[1] = (lds_char*)s1;                                               \
@@ -735,8 +757,8 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     sm.stage[3] = (lds_char*)s3;                                               \
     sm.stage[4] = (lds_char*)s4;                                               \
     sm.stage[5] = (lds_char*)s5;                                               \
-    sm.vb = (lds_char*)svb;                                                    \
-    sm.merge = (lds_char*)smerge
+    sm.vb = (lds_char*)sslot;                                                  \
+    sm.merge = (lds_char*)sslot
 
 // One workgroup per bin (grid = P).  The header words and the bin's head
 // record are independent loads, so the first page-table and K/V loads follow
