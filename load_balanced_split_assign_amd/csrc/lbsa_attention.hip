@@ -309,7 +309,7 @@ template <bool FP8> struct Stage {
     // descriptor's first tile; the waits count only the fixed ones, which can
     // only make them wait for a little more than the stage)
     static constexpr int LOADS = 2 * KV_LOADS + (FP8 ? 3 : 0);
-    static constexpr int STAGES = FP8 ? 5 : 4;          // ring depth: STAGES - 1 tiles in flight
+    static constexpr int STAGES = FP8 ? 5 : 3;          // ring depth: STAGES - 1 tiles in flight
 };
 static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt range");
 static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
