@@ -7,15 +7,15 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "lbsa_oracle.c")
+SRCS = [os.path.join(HERE, "lbsa_oracle.c"), os.path.join(HERE, "prologue_oracle.c")]
 LIB = os.path.join(HERE, "liblbsa_oracle.so")
 
 
 def build(verbose: bool = False) -> str:
-    """Compile oracle/lbsa_oracle.c into oracle/liblbsa_oracle.so and return its path."""
+    """Compile the oracle's C sources into oracle/liblbsa_oracle.so and return its path."""
     tmp = LIB + ".tmp"
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
-           "-Wall", "-Wextra", "-Wno-unused-parameter", SRC, "-o", tmp, "-lm"]
+           "-Wall", "-Wextra", "-Wno-unused-parameter", *SRCS, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

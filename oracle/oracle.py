@@ -43,8 +43,9 @@ def lib():
     """Load (building if needed) the oracle shared library."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or (
-                os.path.getmtime(_LIB_PATH) < os.path.getmtime(os.path.join(_HERE, "lbsa_oracle.c"))):
+        if not os.path.exists(_LIB_PATH) or any(
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(os.path.join(_HERE, f))
+                for f in ("lbsa_oracle.c", "prologue_oracle.c")):
             from oracle import build as _b  # noqa: PLC0415
             _b.build()
         L = ctypes.CDLL(_LIB_PATH)
@@ -63,6 +64,17 @@ def lib():
         L.oracle_bf16_values.argtypes = [P, i64, P]
         L.oracle_e4m3_values.argtypes = [P, i64, P]
         L.oracle_num_threads.restype = ctypes.c_int
+        d = ctypes.c_double
+        L.oracle_rmsnorm.argtypes = [P, P, ctypes.c_int, d, P]
+        L.oracle_rmsnorm.restype = None
+        L.oracle_rope.argtypes = [P, ctypes.c_int, d, d]
+        L.oracle_rope.restype = None
+        L.oracle_quant_e4m3.argtypes = [P, ctypes.c_int, P, P]
+        L.oracle_quant_e4m3.restype = None
+        L.oracle_bf16_nearest.argtypes = [d]
+        L.oracle_bf16_nearest.restype = ctypes.c_uint16
+        L.oracle_prologue.argtypes = [P, i32, i32, i32, i32, P, P, P, d, d, P, P, P]
+        L.oracle_prologue.restype = None
         _lib = L
     return _lib
 
@@ -228,3 +240,70 @@ def merge(part_o, part_lse):
     out_lse = np.zeros(1, np.float64)
     lib().oracle_merge(_ptr(o), _ptr(l), n, o.shape[1], _ptr(out), _ptr(out_lse))
     return out, float(out_lse[0])
+
+
+# ---------------------------------------------------------------------------
+# fused prologue (QK-Norm -> RoPE -> Q as bf16 or fp8 + scale; K/V to the cache)
+# ---------------------------------------------------------------------------
+
+def rmsnorm(x, w, eps: float) -> np.ndarray:
+    """RMSNorm of the last axis of x (float64) with weight w."""
+    x = np.ascontiguousarray(np.asarray(x, np.float64))
+    w = np.ascontiguousarray(np.asarray(w, np.float64))
+    n = x.shape[-1]
+    flat = x.reshape(-1, n)
+    out = np.empty_like(flat)
+    for i in range(flat.shape[0]):
+        lib().oracle_rmsnorm(_ptr(flat[i]), _ptr(w), n, float(eps), _ptr(out[i]))
+    return out.reshape(x.shape)
+
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """RoPE of the last axis of x (float64) at positions pos (one per row)."""
+    x = np.array(np.asarray(x, np.float64), copy=True, order="C")
+    n = x.shape[-1]
+    flat = x.reshape(-1, n)
+    pos = np.broadcast_to(np.asarray(pos, np.float64).ravel(), (flat.shape[0],))
+    for i in range(flat.shape[0]):
+        lib().oracle_rope(_ptr(flat[i]), n, float(pos[i]), float(theta))
+    return flat.reshape(x.shape)
+
+
+def quant_e4m3(x):
+    """fp8 codes (uint8) and scale of the last axis of x (float64), per row."""
+    x = np.ascontiguousarray(np.asarray(x, np.float64))
+    n = x.shape[-1]
+    flat = x.reshape(-1, n)
+    codes = np.empty(flat.shape, np.uint8)
+    scales = np.empty(flat.shape[0], np.float64)
+    sc = ctypes.c_double()
+    for i in range(flat.shape[0]):
+        lib().oracle_quant_e4m3(_ptr(flat[i]), n, _ptr(codes[i]), ctypes.byref(sc))
+        scales[i] = sc.value
+    return codes.reshape(x.shape), scales.reshape(x.shape[:-1])
+
+
+def bf16_nearest(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) nearest to the float64 values x (ties to even)."""
+    x = np.asarray(x, np.float64)
+    f = lib().oracle_bf16_nearest
+    return np.array([f(float(v)) for v in x.ravel()], np.uint16).reshape(x.shape)
+
+
+def prologue(qkv, positions, q_weight, k_weight, num_heads: int, num_kv_heads: int, theta: float,
+             eps: float):
+    """float64 (q [T,Hq,D], k [T,Hkv,D], v [T,Hkv,D]) of the prologue of T tokens;
+    qkv holds bf16 bits [T, (Hq + 2 Hkv) * D]."""
+    a = _np(qkv, np.uint16)
+    T = a.shape[0]
+    D = np.asarray(q_weight).size
+    Hq, Hkv = int(num_heads), int(num_kv_heads)
+    pos = _np(positions, None).astype(np.int32).ravel()
+    qw = np.ascontiguousarray(np.asarray(q_weight, np.float64))
+    kw = np.ascontiguousarray(np.asarray(k_weight, np.float64))
+    q = np.zeros((T, Hq, D), np.float64)
+    k = np.zeros((T, Hkv, D), np.float64)
+    v = np.zeros((T, Hkv, D), np.float64)
+    lib().oracle_prologue(_ptr(a), T, Hq, Hkv, D, _ptr(pos), _ptr(qw), _ptr(kw), float(theta), float(eps),
+                          _ptr(q), _ptr(k), _ptr(v))
+    return q, k, v
