@@ -210,6 +210,38 @@ int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_ca
                        int32_t num_splits, float softmax_scale, void* workspace_d,
                        size_t workspace_bytes, void* out_d, void* stream);
 
+/*
+ * Fused attention prologue: from the fused QKV projection of num_tokens tokens
+ * to the decode path's inputs, in one launch.  Source: vLLM post, section "A
+ * fused attention prologue"; SGLang post, the attention prologue section
+ * (QK-Norm before RoPE, K and V written straight into the paged cache, in fp8
+ * the query emitted as fp8 with a per-token, per-head scale).
+ *   qkv_d            bf16 [num_tokens][(num_heads + 2 num_kv_heads) * 128]: per token the
+ *                    query heads, then the key heads, then the value heads
+ *   positions_d      int32 [num_tokens] position of each token in its sequence (RoPE)
+ *   slot_mapping_d   int64 [num_tokens] cache slot page * 64 + row; a slot < 0 or
+ *                    >= num_pages * 64 is not written (padding tokens)
+ *   q_norm_weight_d, k_norm_weight_d   fp32 [128] RMSNorm weights (all query heads
+ *                    share one, all KV heads the other)
+ *   rope_theta, eps  RoPE base (> 1) and the RMSNorm epsilon (>= 0)
+ *   kv_dtype         LBSA_KV_BF16: q_out bf16 [num_tokens][num_heads][128], bf16 caches;
+ *                    LBSA_KV_FP8_E4M3: q_out e4m3 codes of the same shape plus
+ *                    q_scale_out fp32 [num_tokens][num_heads], e4m3 caches plus
+ *                    k_scale_d / v_scale_d fp32 [num_pages][num_kv_heads][64]
+ *   k_cache_d, v_cache_d   [num_pages][64][num_kv_heads][128], updated in place
+ * Per query and key head: y = x * w / sqrt(mean(x^2) + eps), then the pairs
+ * (d, d + 64) rotate by pos * rope_theta^(-2d/128).  V is copied.  fp8: scale =
+ * max|y| / 448 per token and head (1 for an all-zero head), codes rounded to
+ * nearest even.  head_dim must be 128 and page_size 64; num_heads must be a
+ * multiple of num_kv_heads.  num_tokens = 0 is a no-op.
+ */
+int lbsa_prologue(const void* qkv_d, const int32_t* positions_d, const int64_t* slot_mapping_d,
+                  const float* q_norm_weight_d, const float* k_norm_weight_d, double rope_theta,
+                  float eps, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t page_size, int32_t kv_dtype, void* q_out_d,
+                  float* q_scale_out_d, void* k_cache_d, void* v_cache_d, float* k_scale_d,
+                  float* v_scale_d, int64_t num_pages, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

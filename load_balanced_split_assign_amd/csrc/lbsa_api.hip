@@ -305,3 +305,35 @@ LBSA_API int lbsa_decode_static(const void* q_d, const float* q_scale_d, const v
     if (r != LBSA_OK) return r;
     return hip_status(launch_combine(c.a, true, st));
 }
+
+LBSA_API int lbsa_prologue(const void* qkv_d, const int32_t* positions_d, const int64_t* slot_mapping_d,
+                           const float* q_norm_weight_d, const float* k_norm_weight_d, double rope_theta,
+                           float eps, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t page_size, int32_t kv_dtype, void* q_out_d,
+                           float* q_scale_out_d, void* k_cache_d, void* v_cache_d, float* k_scale_d,
+                           float* v_scale_d, int64_t num_pages, void* stream) {
+    if (num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+        num_pages <= 0)
+        return LBSA_ERR_INVALID_ARGUMENT;
+    if (head_dim != kHeadDim || page_size != kTile) return LBSA_ERR_UNSUPPORTED;
+    if (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3) return LBSA_ERR_INVALID_ARGUMENT;
+    const bool fp8 = kv_dtype == LBSA_KV_FP8_E4M3;
+    if (!(rope_theta > 1.0) || !(eps >= 0.f)) return LBSA_ERR_INVALID_ARGUMENT;
+    if ((long long)num_tokens * (num_heads + 2 * num_kv_heads) >= (1LL << 31) / 4) return LBSA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return LBSA_OK;
+    if (!qkv_d || !positions_d || !slot_mapping_d || !q_norm_weight_d || !k_norm_weight_d || !q_out_d ||
+        !k_cache_d || !v_cache_d)
+        return LBSA_ERR_INVALID_ARGUMENT;
+    if (fp8 && (!q_scale_out_d || !k_scale_d || !v_scale_d)) return LBSA_ERR_INVALID_ARGUMENT;
+    // 8-byte bf16 loads / stores (4-byte fp8 stores), 16-byte weight loads
+    if (!aligned(qkv_d, 8) || !aligned(positions_d, 4) || !aligned(slot_mapping_d, 8) ||
+        !aligned(q_norm_weight_d, 16) || !aligned(k_norm_weight_d, 16) || !aligned(q_out_d, fp8 ? 4 : 8) ||
+        !aligned(k_cache_d, fp8 ? 4 : 8) || !aligned(v_cache_d, fp8 ? 4 : 8) ||
+        (fp8 && (!aligned(q_scale_out_d, 4) || !aligned(k_scale_d, 4) || !aligned(v_scale_d, 4))))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_prologue(static_cast<const uint16_t*>(qkv_d), positions_d, slot_mapping_d,
+                                      q_norm_weight_d, k_norm_weight_d, rope_theta, eps, num_tokens,
+                                      num_heads, num_kv_heads, fp8, q_out_d, q_scale_out_d, k_cache_d,
+                                      v_cache_d, k_scale_d, v_scale_d, num_pages,
+                                      static_cast<hipStream_t>(stream)));
+}

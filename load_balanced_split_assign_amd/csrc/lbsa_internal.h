@@ -86,5 +86,9 @@ hipError_t launch_split(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream);
 hipError_t split_occupancy(bool fp8, int* blocks_per_cu);
+hipError_t launch_prologue(const uint16_t* qkv, const int32_t* positions, const int64_t* slots,
+                           const float* qw, const float* kw, double theta, float eps, int T, int Hq,
+                           int Hkv, bool fp8, void* q_out, float* q_scale, void* k_cache, void* v_cache,
+                           float* k_scale, float* v_scale, int64_t num_pages, hipStream_t stream);
 
 }  // namespace lbsa

@@ -67,7 +67,9 @@ def lib() -> ctypes.CDLL:
         L.lbsa_decode_combine.argtypes = [i32, i32, i32, i32, i32, vp, sz, vp, sz, vp, vp]
         L.lbsa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                          i32, i64, i32, f32, vp, sz, vp, vp]
-        for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes",
+        L.lbsa_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, f32, i32, i32, i32, i32, i32, i32,
+                                    vp, vp, vp, vp, vp, vp, i64, vp]
+        for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes", "lbsa_prologue",
                    "lbsa_workspace_layout_get", "lbsa_workspace_bytes", "lbsa_static_workspace_bytes",
                    "lbsa_plan", "lbsa_decode", "lbsa_decode_split", "lbsa_decode_combine",
                    "lbsa_decode_static"):
@@ -272,3 +274,25 @@ def read_partials(workspace: torch.Tensor, batch: int, num_heads: int, num_kv_he
     lse = raw[lay["part_lse"]:lay["part_lse"] + 4 * GROUP * ndesc].view(np.float32).reshape(ndesc, GROUP)
     o = raw[lay["part_o"]:lay["part_o"] + 4 * GROUP * HEAD_DIM * ndesc].view(np.float32)
     return o.reshape(ndesc, GROUP, HEAD_DIM).copy(), lse.copy()
+
+
+def prologue(qkv, positions, slot_mapping, q_norm_weight, k_norm_weight, num_heads: int, num_kv_heads: int,
+             k_cache, v_cache, rope_theta: float = 10000.0, eps: float = 1e-6, k_scale=None, v_scale=None,
+             q_out=None, q_scale_out=None):
+    """Fused QK-Norm -> RoPE -> Q out (bf16, or fp8 + scale when the caches are
+    fp8) and K / V written into the paged caches.  Returns (q_out, q_scale_out)."""
+    T = int(qkv.shape[0])
+    fp8 = k_cache.dtype == torch.float8_e4m3fn
+    dev = qkv.device
+    if q_out is None:
+        q_out = torch.empty((T, num_heads, HEAD_DIM), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16,
+                            device=dev)
+    if fp8 and q_scale_out is None:
+        q_scale_out = torch.empty((T, num_heads), dtype=torch.float32, device=dev)
+    _check("lbsa_prologue", lib().lbsa_prologue(
+        _ptr(qkv), _ptr(positions), _ptr(slot_mapping), _ptr(q_norm_weight), _ptr(k_norm_weight),
+        float(rope_theta), float(eps), T, int(num_heads), int(num_kv_heads), int(qkv.shape[1]) // (
+            int(num_heads) + 2 * int(num_kv_heads)), int(k_cache.shape[1]), KV_FP8_E4M3 if fp8 else KV_BF16,
+        _ptr(q_out), _ptr(q_scale_out), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        int(k_cache.shape[0]), _stream(dev)))
+    return q_out, q_scale_out

@@ -211,3 +211,71 @@ def _poison_tails(sl, pt, k_cache, v_cache, k_scale, v_scale):
         for sc in (k_scale, v_scale):
             if sc is not None:
                 sc[page, :, s0:] = float("nan")
+
+
+# ---------------------------------------------------------------------------
+# inputs of the fused attention prologue (random draws only)
+# ---------------------------------------------------------------------------
+
+PROLOGUE_WORKLOADS = {
+    # decode step of the tp8_share batch: one new token per request
+    "decode_8_1": dict(tokens=32, num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=31),
+    # decode step of the full 64/8-head model, fp8 cache
+    "decode_64_8_fp8": dict(tokens=64, num_heads=64, num_kv_heads=8, kv_dtype="fp8", seed=32),
+    # a prefill chunk: 8192 tokens, 64/8 heads
+    "prefill_64_8": dict(tokens=8192, num_heads=64, num_kv_heads=8, kv_dtype="bf16", seed=33),
+    "prefill_64_8_fp8": dict(tokens=8192, num_heads=64, num_kv_heads=8, kv_dtype="fp8", seed=34),
+}
+
+
+def make_prologue_inputs(tokens: int, num_heads: int, num_kv_heads: int, kv_dtype: str = "bf16", seed: int = 0,
+                         num_pages: int | None = None, max_position: int = 262143, padding: int = 0,
+                         zero_heads: int = 0, magnitude: float = 16.0, device="cpu") -> dict:
+    """Seeded inputs of the prologue.
+
+    * qkv bf16 [T, (Hq + 2 Hkv) * 128] ~ N(0, 1) times a per-(token, head)
+      magnitude log-uniform in [1/magnitude, magnitude]; ``zero_heads`` head
+      vectors are zero;
+    * positions int32 uniform in [0, max_position];
+    * slot_mapping int64: distinct random slots of a pool of ``num_pages`` pages
+      (default: just enough), the last ``padding`` tokens get -1;
+    * norm weights fp32 ~ 1 + 0.2 N(0, 1);
+    * caches pre-filled with random contents (bf16 N(0, 1), or fp8 codes that
+      are not NaN and scales in [0.5, 2)), so a write to a wrong slot shows.
+    """
+    gen = torch.Generator().manual_seed(seed)
+    D, NV = HEAD_DIM, num_heads + 2 * num_kv_heads
+    mag = torch.exp(math.log(magnitude) * (2 * torch.rand((tokens, NV, 1), generator=gen, dtype=torch.float64) - 1))
+    x = torch.randn((tokens, NV, D), generator=gen, dtype=torch.float64) * mag
+    if zero_heads:
+        idx = torch.randperm(tokens * NV, generator=gen)[:zero_heads]
+        x.view(tokens * NV, D)[idx] = 0.0
+    qkv = x.to(torch.float32).to(torch.bfloat16).reshape(tokens, NV * D)
+    positions = torch.randint(0, max_position + 1, (tokens,), generator=gen, dtype=torch.int64).to(torch.int32)
+    pages = num_pages or max(1, (tokens + TILE - 1) // TILE + 2)
+    slots = torch.randperm(pages * TILE, generator=gen)[:tokens].to(torch.int64)
+    if padding:
+        slots[tokens - padding:] = -1
+    qw = (1.0 + 0.2 * torch.randn(D, generator=gen, dtype=torch.float64)).to(torch.float32)
+    kw = (1.0 + 0.2 * torch.randn(D, generator=gen, dtype=torch.float64)).to(torch.float32)
+    shape = (pages, TILE, num_kv_heads, D)
+    if kv_dtype == "bf16":
+        k_cache = torch.randn(shape, generator=gen).to(torch.bfloat16)
+        v_cache = torch.randn(shape, generator=gen).to(torch.bfloat16)
+        k_scale = v_scale = None
+    elif kv_dtype == "fp8":
+        codes = torch.randint(0, 256, (2,) + shape, generator=gen, dtype=torch.int64).to(torch.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x7E                      # no NaN codes
+        k_cache, v_cache = codes[0].view(torch.float8_e4m3fn), codes[1].view(torch.float8_e4m3fn)
+        k_scale = 0.5 + 1.5 * torch.rand((pages, num_kv_heads, TILE), generator=gen)
+        v_scale = 0.5 + 1.5 * torch.rand((pages, num_kv_heads, TILE), generator=gen)
+    else:
+        raise ValueError("kv_dtype must be 'bf16' or 'fp8'")
+    out = {"qkv": qkv, "positions": positions, "slot_mapping": slots, "q_weight": qw, "k_weight": kw,
+           "k_cache": k_cache.contiguous(), "v_cache": v_cache.contiguous(), "k_scale": k_scale,
+           "v_scale": v_scale, "num_heads": num_heads, "num_kv_heads": num_kv_heads, "kv_dtype": kv_dtype,
+           "tokens": tokens, "num_pages": pages, "theta": 10000.0, "eps": 1e-6}
+    for k, v in list(out.items()):
+        if isinstance(v, torch.Tensor):
+            out[k] = v.to(device)
+    return out

@@ -105,6 +105,32 @@ def test_decode_rejects_bad_arguments_on_host():
     assert _decode_status(scale=float("nan")) == lbsa.ERR_INVALID_ARGUMENT
 
 
+def _prologue_status(**kw):
+    a = dict(qkv=16, pos=32, slots=64, qw=128, kw=256, theta=10000.0, eps=1e-6, T=4, Hq=8, Hkv=1, D=128,
+             page=64, dt=0, q=4096, qs=None, k=8192, v=16384, ks=None, vs=None, npages=10)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lbsa.lib().lbsa_prologue(vp(a["qkv"]), vp(a["pos"]), vp(a["slots"]), vp(a["qw"]), vp(a["kw"]),
+                                    a["theta"], a["eps"], a["T"], a["Hq"], a["Hkv"], a["D"], a["page"], a["dt"],
+                                    vp(a["q"]), vp(a["qs"]), vp(a["k"]), vp(a["v"]), vp(a["ks"]), vp(a["vs"]),
+                                    a["npages"], None)
+
+
+def test_prologue_rejects_bad_arguments_on_host():
+    assert _prologue_status(qkv=None) == lbsa.ERR_INVALID_ARGUMENT
+    assert _prologue_status(D=64) == lbsa.ERR_UNSUPPORTED
+    assert _prologue_status(page=16) == lbsa.ERR_UNSUPPORTED
+    assert _prologue_status(Hq=12, Hkv=8) == lbsa.ERR_INVALID_ARGUMENT
+    assert _prologue_status(dt=1) == lbsa.ERR_INVALID_ARGUMENT             # fp8 without scales
+    assert _prologue_status(theta=1.0) == lbsa.ERR_INVALID_ARGUMENT
+    assert _prologue_status(eps=-1.0) == lbsa.ERR_INVALID_ARGUMENT
+    assert _prologue_status(qw=130) == lbsa.ERR_INVALID_ARGUMENT           # misaligned weights
+    assert _prologue_status(slots=68) == lbsa.ERR_INVALID_ARGUMENT         # misaligned int64
+    assert _prologue_status(T=-1) == lbsa.ERR_INVALID_ARGUMENT
+    assert _prologue_status(npages=0) == lbsa.ERR_INVALID_ARGUMENT
+    assert _prologue_status(T=0, qkv=None) == lbsa.OK                      # nothing to do
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lbsa, "_lib", None)
     monkeypatch.setattr(lbsa, "LIB_PATH", str(tmp_path / "missing.so"))
