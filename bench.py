@@ -257,6 +257,79 @@ def table3(args):
     print(json.dumps({"table3": rows, "P": P, "unit": "us", "flush": args.flush}), flush=True)
 
 
+def prologue_bytes(T, Hq, Hkv, fp8):
+    """Bytes the prologue must move: the fused QKV rows in, positions and slots,
+    the two norm weights, Q out (+ scale) and the K / V cache rows (+ scales)."""
+    e = 1 if fp8 else 2
+    s = 4 if fp8 else 0
+    return (T * (Hq + 2 * Hkv) * 128 * 2 + T * 12 + 2 * 128 * 4
+            + T * Hq * (128 * e + s) + 2 * T * Hkv * (128 * e + s))
+
+
+def prologue_bench(args):
+    """The fused prologue on the decode- and prefill-shaped inputs: mean event
+    time and achieved GB/s per workload (cache flush before every launch)."""
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    from load_balanced_split_assign_amd import workload as wl
+    flush = make_flush(args.flush)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for name, kw in wl.PROLOGUE_WORKLOADS.items():
+        g = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v)
+             for k, v in wl.make_prologue_inputs(**kw).items()}
+        fp8 = g["kv_dtype"] == "fp8"
+        T, Hq, Hkv = g["tokens"], g["num_heads"], g["num_kv_heads"]
+        q = torch.empty((T, Hq, 128), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16, device="cuda:0")
+        qs = torch.empty((T, Hq), dtype=torch.float32, device="cuda:0") if fp8 else None
+
+        def run():
+            lbsa.prologue(g["qkv"], g["positions"], g["slot_mapping"], g["q_weight"], g["k_weight"], Hq, Hkv,
+                          g["k_cache"], g["v_cache"], rope_theta=g["theta"], eps=g["eps"], k_scale=g["k_scale"],
+                          v_scale=g["v_scale"], q_out=q, q_scale_out=qs)
+        for i in range(args.warmup):
+            flush(i)
+            run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush(i)
+            ev[i][0].record(stream)
+            run()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = summarize([1000.0 * a.elapsed_time(b) for a, b in ev])
+        nbytes = prologue_bytes(T, Hq, Hkv, fp8)
+        rows.append({"workload": name, "tokens": T, "num_heads": Hq, "num_kv_heads": Hkv,
+                     "kv_dtype": g["kv_dtype"], "bytes": nbytes, "us_mean": round(t["mean"], 3),
+                     "us_median": round(t["median"], 3), "GBps": round(nbytes / t["mean"] / 1e3, 1),
+                     "pct_of_peak": round(100 * nbytes / t["mean"] / 1e3 / HBM_PEAK_GBS, 2)})
+        del g, q, qs
+        torch.cuda.empty_cache()
+    # a plain device copy that moves as many bytes as the bf16 prefill (half
+    # read, half written): the streaming rate these compare with in practice
+    big = max(rows, key=lambda r: r["bytes"])
+    src = torch.empty(big["bytes"] // 8, dtype=torch.int32, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for i in range(args.warmup):
+        flush(i)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush(i)
+        ev[i][0].record(stream)
+        dst.copy_(src)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = summarize([1000.0 * a.elapsed_time(b) for a, b in ev])
+    nbytes = 2 * src.numel() * 4
+    copy = {"bytes": nbytes, "us_mean": round(t["mean"], 3), "GBps": round(nbytes / t["mean"] / 1e3, 1),
+            "pct_of_peak": round(100 * nbytes / t["mean"] / 1e3 / HBM_PEAK_GBS, 2)}
+    print(json.dumps({"prologue": rows, "device_copy": copy, "unit": "us", "flush": args.flush}), flush=True)
+
+
 def gpu_batch(name, tail="normal"):
     import torch
 
@@ -382,6 +455,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device copy first (reference for PMC byte counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (bounded sample)")
+    ap.add_argument("--prologue", action="store_true",
+                    help="instead of the headline line: the fused QK-Norm/RoPE/KV-write prologue")
     ap.add_argument("--table3", action="store_true",
                     help="instead of the headline line: the six fp8 KV-length mixes, dynamic vs static")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -403,6 +478,9 @@ def main():
 
     if args.table3:
         table3(args)
+        return
+    if args.prologue:
+        prologue_bench(args)
         return
 
     if args.calib_copy:   # a plain copy of known size: FETCH_SIZE / WRITE_SIZE reference

@@ -232,8 +232,13 @@ int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_ca
  * Per query and key head: y = x * w / sqrt(mean(x^2) + eps), then the pairs
  * (d, d + 64) rotate by pos * rope_theta^(-2d/128).  V is copied.  fp8: scale =
  * max|y| / 448 per token and head (1 for an all-zero head), codes rounded to
- * nearest even.  head_dim must be 128 and page_size 64; num_heads must be a
- * multiple of num_kv_heads.  num_tokens = 0 is a no-op.
+ * nearest even.  head_dim must be 128 and page_size 64 (else
+ * LBSA_ERR_UNSUPPORTED); num_heads must be a multiple of num_kv_heads.
+ * Alignment: qkv_d and the two weights 16 B; q_out_d, k_cache_d and v_cache_d
+ * 16 B in bf16, 8 B in fp8; the rest their element size (else
+ * LBSA_ERR_INVALID_ARGUMENT, as for a null pointer, theta <= 1 or eps < 0).
+ * num_tokens = 0 is a no-op.  All buffers are the caller's; the call only
+ * enqueues one kernel on the stream.
  */
 int lbsa_prologue(const void* qkv_d, const int32_t* positions_d, const int64_t* slot_mapping_d,
                   const float* q_norm_weight_d, const float* k_norm_weight_d, double rope_theta,

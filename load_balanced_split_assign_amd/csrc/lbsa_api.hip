@@ -325,10 +325,10 @@ LBSA_API int lbsa_prologue(const void* qkv_d, const int32_t* positions_d, const 
         !k_cache_d || !v_cache_d)
         return LBSA_ERR_INVALID_ARGUMENT;
     if (fp8 && (!q_scale_out_d || !k_scale_d || !v_scale_d)) return LBSA_ERR_INVALID_ARGUMENT;
-    // 8-byte bf16 loads / stores (4-byte fp8 stores), 16-byte weight loads
-    if (!aligned(qkv_d, 8) || !aligned(positions_d, 4) || !aligned(slot_mapping_d, 8) ||
-        !aligned(q_norm_weight_d, 16) || !aligned(k_norm_weight_d, 16) || !aligned(q_out_d, fp8 ? 4 : 8) ||
-        !aligned(k_cache_d, fp8 ? 4 : 8) || !aligned(v_cache_d, fp8 ? 4 : 8) ||
+    // 16-byte loads of the projection and the weights, 16-byte bf16 / 8-byte fp8 stores
+    if (!aligned(qkv_d, 16) || !aligned(positions_d, 4) || !aligned(slot_mapping_d, 8) ||
+        !aligned(q_norm_weight_d, 16) || !aligned(k_norm_weight_d, 16) || !aligned(q_out_d, fp8 ? 8 : 16) ||
+        !aligned(k_cache_d, fp8 ? 8 : 16) || !aligned(v_cache_d, fp8 ? 8 : 16) ||
         (fp8 && (!aligned(q_scale_out_d, 4) || !aligned(k_scale_d, 4) || !aligned(v_scale_d, 4))))
         return LBSA_ERR_INVALID_ARGUMENT;
     return hip_status(launch_prologue(static_cast<const uint16_t*>(qkv_d), positions_d, slot_mapping_d,

@@ -126,6 +126,9 @@ def test_prologue_rejects_bad_arguments_on_host():
     assert _prologue_status(eps=-1.0) == lbsa.ERR_INVALID_ARGUMENT
     assert _prologue_status(qw=130) == lbsa.ERR_INVALID_ARGUMENT           # misaligned weights
     assert _prologue_status(slots=68) == lbsa.ERR_INVALID_ARGUMENT         # misaligned int64
+    assert _prologue_status(qkv=24) == lbsa.ERR_INVALID_ARGUMENT           # 16-byte loads
+    assert _prologue_status(q=4104) == lbsa.ERR_INVALID_ARGUMENT           # 16-byte bf16 stores
+    assert _prologue_status(k=8196, dt=1, qs=512, ks=1024, vs=2048) == lbsa.ERR_INVALID_ARGUMENT  # 8 B fp8
     assert _prologue_status(T=-1) == lbsa.ERR_INVALID_ARGUMENT
     assert _prologue_status(npages=0) == lbsa.ERR_INVALID_ARGUMENT
     assert _prologue_status(T=0, qkv=None) == lbsa.OK                      # nothing to do
