@@ -476,13 +476,6 @@ def main():
     from load_balanced_split_assign_amd import lbsa
     from load_balanced_split_assign_amd import workload as wl
 
-    if args.table3:
-        table3(args)
-        return
-    if args.prologue:
-        prologue_bench(args)
-        return
-
     if args.calib_copy:   # a plain copy of known size: FETCH_SIZE / WRITE_SIZE reference
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -490,6 +483,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.table3:
+        table3(args)
+        return
+    if args.prologue:
+        prologue_bench(args)
+        return
 
     name = args.workload
     w = wl.WORKLOADS[name]
