@@ -18,8 +18,9 @@ order: sequence lengths -> physical page permutation -> Q -> K -> V.
 * tail slots past L_b in a request's last page hold NaN (``tail="nan"``, parity
   runs: they must never reach the output) or N(0, 1) (``tail="normal"``).
 
-Layouts: q [B, Hq, D]; k_cache / v_cache [pages, 64, Hkv, D] (token-major);
-k_scale / v_scale [pages, Hkv, 64] fp32; q_scale [B, Hq] fp32; page_table
+Layouts: q [B, Hq, D] (or [B, q_len, Hq, D] with q_len > 1 query tokens per
+request, multi-token decode); k_cache / v_cache [pages, 64, Hkv, D] (token-major);
+k_scale / v_scale [pages, Hkv, 64] fp32; q_scale [B, Hq] (or [B, q_len, Hq]) fp32; page_table
 [B, max_pages] int32; seqlens [B] int32.
 """
 from __future__ import annotations
@@ -46,6 +47,7 @@ class Workload:
     dist: tuple = ()                 # ("loguniform", a, b) | ("uniform_int", a, b)
     num_workgroups: int = 0          # 0 = library default (CUs x occupancy)
     head_dim: int = HEAD_DIM
+    q_len: int = 1                   # query tokens per request (> 1: multi-token decode)
     note: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -124,11 +126,12 @@ def _to_fp8(x: torch.Tensor):
 
 def make_batch(w: Workload | str | None = None, *, seqlens=None, num_heads=None, num_kv_heads=None,
                kv_dtype=None, seed=None, tail: str = "nan", device="cpu", max_pages=None,
-               head_dim=HEAD_DIM) -> dict:
+               head_dim=HEAD_DIM, q_len=None) -> dict:
     """Build one synthetic decode batch.
 
     Either pass a workload (object or name) or explicit ``seqlens`` with
-    ``num_heads``, ``num_kv_heads``, ``kv_dtype`` and ``seed``.  Returns a dict of
+    ``num_heads``, ``num_kv_heads``, ``kv_dtype`` and ``seed``.  ``q_len``
+    (default: the workload's, 1) query tokens per request.  Returns a dict of
     tensors on ``device`` plus scalar metadata.
     """
     if isinstance(w, str):
@@ -143,6 +146,7 @@ def make_batch(w: Workload | str | None = None, *, seqlens=None, num_heads=None,
 
     sl = draw_seqlens(w, gen_cpu)
     B, Hq, Hkv, D = int(sl.numel()), w.num_heads, w.num_kv_heads, w.head_dim
+    QL = int(q_len or w.q_len)
     n = (sl.to(torch.int64) + TILE - 1) // TILE
     n_pages = int(n.sum())
     pool = max(1, n_pages)
@@ -155,7 +159,7 @@ def make_batch(w: Workload | str | None = None, *, seqlens=None, num_heads=None,
         pt[b, :nb] = perm[off:off + nb]
         off += nb
 
-    q32 = _normal((B, Hq, D), gen, dev)
+    q32 = _normal((B, Hq, D) if QL == 1 else (B, QL, Hq, D), gen, dev)
     k32 = _normal((pool, TILE, Hkv, D), gen, dev)
     k_cache, k_scale = _finish_cache(k32, w.kv_dtype)
     del k32
@@ -178,7 +182,7 @@ def make_batch(w: Workload | str | None = None, *, seqlens=None, num_heads=None,
         "q": q, "q_scale": q_scale, "k_cache": k_cache, "v_cache": v_cache,
         "k_scale": k_scale, "v_scale": v_scale,
         "page_table": pt.to(dev), "seqlens": sl.to(dev),
-        "B": B, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+        "B": B, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "q_len": QL,
         "max_pages": mp, "num_pages": pool,
         "softmax_scale": 1.0 / math.sqrt(D),
         "num_workgroups": w.num_workgroups,

@@ -36,6 +36,13 @@
  *       query head; scale arrays are laid out [page][kv_head][slot].
  *   R11 L_b = 0 is allowed: no tiles, no chunks, output row 0, LSE -inf.
  *   R12 K/V caches are token-major [page][slot][kv_head][dim].
+ *   M1  multi-token decode (q_len > 1, Hy3's MTP speculative layer in the
+ *       vLLM post's model paragraph): the q_len new tokens of a request are
+ *       the last q_len of its L_b cached tokens; query i (0-based) sits at
+ *       position L_b - q_len + i and sees tokens [0, L_b - q_len + i], i.e.
+ *       causal among the new tokens.  A query that sees no token gives 0.
+ *       q is [B][q_len][Hq][D], q_scale [B][q_len][Hq], out like q; a
+ *       descriptor's partial has one row per (query i, head g), row i*G + g.
  *
  * Floating point is fp64 throughout; integers in the assign are int64.
  * Parity of every function here is pinned in tests/ against values that do
@@ -238,8 +245,8 @@ int oracle_assign(const int32_t* seqlens, int32_t B, int32_t Hq, int32_t Hkv,
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
-    const void* q;          /* [B][Hq][D]  bf16 bits (kv_dtype 0) or e4m3 bits (1) */
-    const float* q_scale;   /* [B][Hq]     e4m3 only */
+    const void* q;          /* [B][q_len][Hq][D]  bf16 bits (kv_dtype 0) or e4m3 bits (1) */
+    const float* q_scale;   /* [B][q_len][Hq]     e4m3 only */
     const void* k_cache;    /* [pages][64][Hkv][D] */
     const void* v_cache;
     const float* k_scale;   /* [pages][Hkv][64]    e4m3 only */
@@ -249,14 +256,22 @@ typedef struct {
     int32_t kv_dtype;       /* 0 = bf16, 1 = e4m3fn */
     int32_t B, Hq, Hkv, D, max_pages, num_pages;
     double softmax_scale;
+    int32_t q_len;          /* query tokens per request (M1), >= 1 */
 } oracle_inputs;
 
-static double q_elem(const oracle_inputs* in, int64_t b, int64_t hq, int64_t d)
+/* Element d of query i of request b, head hq. */
+static double q_elem(const oracle_inputs* in, int64_t b, int64_t i, int64_t hq, int64_t d)
 {
-    int64_t i = (b * in->Hq + hq) * in->D + d;
-    if (in->kv_dtype == 0) return oracle_bf16_value(((const uint16_t*)in->q)[i]);
-    return oracle_e4m3_value(((const uint8_t*)in->q)[i]) *
-           (double)in->q_scale[b * in->Hq + hq];
+    const int64_t row = (b * in->q_len + i) * in->Hq + hq;
+    if (in->kv_dtype == 0) return oracle_bf16_value(((const uint16_t*)in->q)[row * in->D + d]);
+    return oracle_e4m3_value(((const uint8_t*)in->q)[row * in->D + d]) * (double)in->q_scale[row];
+}
+
+/* M1: tokens [0, visible) of request b are seen by its query i. */
+static int64_t visible(const oracle_inputs* in, int64_t b, int64_t i)
+{
+    const int64_t v = (int64_t)in->seqlens[b] - in->q_len + 1 + i;
+    return v > 0 ? v : 0;
 }
 
 static double kv_elem(const oracle_inputs* in, const void* cache, const float* scale,
@@ -268,19 +283,21 @@ static double kv_elem(const oracle_inputs* in, const void* cache, const float* s
            (double)scale[(page * in->Hkv + h) * OR_TILE + slot];
 }
 
-/* Attention of query head hq of request b over its tokens [tok0, tok1).
+/* Attention of query i, head hq of request b over its tokens [tok0, tok1)
+ * (cut at what the query sees, M1).
  * out[D] = sum_t w_t v_t / sum_t w_t with w_t = exp(s_t - max s),
  * s_t = softmax_scale * <q, k_t>; *lse = max s + ln sum_t w_t.
  * An empty range gives out = 0 and lse = -inf.  Returns -1 on a bad page. */
-static int attend_range(const oracle_inputs* in, int64_t b, int64_t hq,
+static int attend_range(const oracle_inputs* in, int64_t b, int64_t i, int64_t hq,
                         int64_t tok0, int64_t tok1, double* out, double* lse,
                         double* qv, double* s)
 {
     const int64_t D = in->D;
     const int64_t h = hq / (in->Hq / in->Hkv);
+    if (tok1 > visible(in, b, i)) tok1 = visible(in, b, i);
     for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
     if (tok1 <= tok0) { *lse = -INFINITY; return 0; }
-    for (int64_t d = 0; d < D; ++d) qv[d] = q_elem(in, b, hq, d);
+    for (int64_t d = 0; d < D; ++d) qv[d] = q_elem(in, b, i, hq, d);
 
     double m = -INFINITY;
     for (int64_t t = tok0; t < tok1; ++t) {
@@ -315,11 +332,11 @@ static int64_t max_len(const oracle_inputs* in)
     return mx;
 }
 
-/* Full attention for every (request, query head): out [B][Hq][D], lse [B][Hq].
- * Requests with L_b = 0 give zeros and -inf. */
+/* Full attention for every (request, query, head): out [B][q_len][Hq][D],
+ * lse [B][q_len][Hq].  Requests with L_b = 0 give zeros and -inf. */
 int oracle_attention(const oracle_inputs* in, double* out, double* lse, int nthreads)
 {
-    const int64_t rows = (int64_t)in->B * in->Hq;
+    const int64_t rows = (int64_t)in->B * in->q_len * in->Hq;
     const int64_t D = in->D;
     const int64_t L = max_len(in);
     int bad = 0;
@@ -334,8 +351,9 @@ int oracle_attention(const oracle_inputs* in, double* out, double* lse, int nthr
 #pragma omp for schedule(dynamic, 1)
 #endif
         for (int64_t row = 0; row < rows; ++row) {
-            int64_t b = row / in->Hq, hq = row % in->Hq;
-            if (attend_range(in, b, hq, 0, in->seqlens[b], out + row * D, lse + row, qv, s))
+            const int64_t b = row / ((int64_t)in->q_len * in->Hq);
+            const int64_t i = row / in->Hq % in->q_len, hq = row % in->Hq;
+            if (attend_range(in, b, i, hq, 0, in->seqlens[b], out + row * D, lse + row, qv, s))
                 bad = 1;
         }
         free(qv);
@@ -345,8 +363,9 @@ int oracle_attention(const oracle_inputs* in, double* out, double* lse, int nthr
     return bad ? -1 : 0;
 }
 
-/* Attention restricted to a subset of rows (request, query head) given as
- * pairs; used to sample outputs of very large batches. */
+/* Attention restricted to a subset of rows given as pairs (request, j) with
+ * j = i * Hq + hq (query i, head hq); used to sample outputs of very large
+ * batches. */
 int oracle_attention_rows(const oracle_inputs* in, const int32_t* rows_bh, int64_t nrows,
                           double* out, double* lse, int nthreads)
 {
@@ -364,8 +383,9 @@ int oracle_attention_rows(const oracle_inputs* in, const int32_t* rows_bh, int64
 #pragma omp for schedule(dynamic, 1)
 #endif
         for (int64_t i = 0; i < nrows; ++i) {
-            int64_t b = rows_bh[2 * i], hq = rows_bh[2 * i + 1];
-            if (attend_range(in, b, hq, 0, in->seqlens[b], out + i * D, lse + i, qv, s))
+            const int64_t b = rows_bh[2 * i], qi = rows_bh[2 * i + 1] / in->Hq;
+            const int64_t hq = rows_bh[2 * i + 1] % in->Hq;
+            if (attend_range(in, b, qi, hq, 0, in->seqlens[b], out + i * D, lse + i, qv, s))
                 bad = 1;
         }
         free(qv);
@@ -376,9 +396,10 @@ int oracle_attention_rows(const oracle_inputs* in, const int32_t* rows_bh, int64
 }
 
 /* Per-descriptor partials: descriptor i = (h, b, t0, t1) covers tokens
- * [64 t0, min(64 t1, L_b)) of request b for the G query heads of KV head h.
- * part_o [n][G][D] is the normalised partial output, part_lse [n][G] its
- * natural-log LSE (reading R7). */
+ * [64 t0, min(64 t1, L_b)) of request b for the G query heads of KV head h
+ * and each of the q_len queries (cut at what each sees, M1).
+ * part_o [n][q_len * G][D] is the normalised partial output (row qi * G + g),
+ * part_lse [n][q_len * G] its natural-log LSE (reading R7). */
 int oracle_partials(const oracle_inputs* in, const int32_t* desc, int64_t ndesc,
                     double* part_o, double* part_lse, int nthreads)
 {
@@ -396,13 +417,13 @@ int oracle_partials(const oracle_inputs* in, const int32_t* desc, int64_t ndesc,
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 1)
 #endif
-        for (int64_t i = 0; i < ndesc * G; ++i) {
-            int64_t di = i / G, g = i % G;
-            int64_t h = desc[4 * di], b = desc[4 * di + 1];
-            int64_t tok0 = (int64_t)desc[4 * di + 2] * OR_TILE;
+        for (int64_t i = 0; i < ndesc * in->q_len * G; ++i) {
+            const int64_t di = i / (in->q_len * G), qi = i / G % in->q_len, g = i % G;
+            const int64_t h = desc[4 * di], b = desc[4 * di + 1];
+            const int64_t tok0 = (int64_t)desc[4 * di + 2] * OR_TILE;
             int64_t tok1 = (int64_t)desc[4 * di + 3] * OR_TILE;
             if (tok1 > in->seqlens[b]) tok1 = in->seqlens[b];
-            if (attend_range(in, b, h * G + g, tok0, tok1, part_o + i * D, part_lse + i, qv, s))
+            if (attend_range(in, b, qi, h * G + g, tok0, tok1, part_o + i * D, part_lse + i, qv, s))
                 bad = 1;
         }
         free(qv);

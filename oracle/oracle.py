@@ -36,6 +36,7 @@ class _Inputs(ctypes.Structure):
         ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
         ("D", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
         ("softmax_scale", ctypes.c_double),
+        ("q_len", ctypes.c_int32),
     ]
 
 
@@ -182,29 +183,35 @@ class _Batch:
             self.vs = _np(batch["v_scale"], np.float32)
         self.pt = _np(batch["page_table"], None).astype(np.int32)
         self.sl = _np(batch["seqlens"], None).astype(np.int32)
-        B, Hq, D = self.q.shape
+        # q [B, Hq, D] (one query per request) or [B, q_len, Hq, D]
+        if self.q.ndim == 3:
+            (B, Hq, D), QL = self.q.shape, 1
+        else:
+            B, QL, Hq, D = self.q.shape
         num_pages, page, Hkv, D2 = self.k.shape
         assert page == TILE and D2 == D
         self.shape = (B, Hq, Hkv, D)
+        self.q_len = QL
         self.s = _Inputs(
             _ptr(self.q), _ptr(self.qs), _ptr(self.k), _ptr(self.v), _ptr(self.ks), _ptr(self.vs),
             _ptr(self.pt), _ptr(self.sl), self.kv_dtype, B, Hq, Hkv, D,
-            self.pt.shape[1], num_pages, float(batch["softmax_scale"]))
+            self.pt.shape[1], num_pages, float(batch["softmax_scale"]), QL)
 
 
 def attention(batch: dict, nthreads: int = 0):
-    """fp64 attention of every (request, query head): returns (out [B,Hq,D], lse [B,Hq])."""
+    """fp64 attention of every (request, query head): returns (out, lse) shaped like q
+    without / with its last axis: [B,Hq,D] and [B,Hq], or [B,q_len,Hq,D] and [B,q_len,Hq]."""
     bb = _Batch(batch)
     B, Hq, Hkv, D = bb.shape
-    out = np.zeros((B, Hq, D), np.float64)
-    lse = np.zeros((B, Hq), np.float64)
+    out = np.zeros(bb.q.shape, np.float64)
+    lse = np.zeros(bb.q.shape[:-1], np.float64)
     if lib().oracle_attention(ctypes.byref(bb.s), _ptr(out), _ptr(lse), nthreads) != 0:
         raise ValueError("oracle_attention: page_table entry out of range")
     return out, lse
 
 
 def attention_rows(batch: dict, rows, nthreads: int = 0):
-    """fp64 attention for selected (request, query head) rows: rows int[n, 2]."""
+    """fp64 attention for selected rows int[n, 2] = (request, j), j = query * Hq + head."""
     bb = _Batch(batch)
     D = bb.shape[3]
     rows = np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 2))
@@ -217,10 +224,11 @@ def attention_rows(batch: dict, rows, nthreads: int = 0):
 
 
 def partials(batch: dict, desc, nthreads: int = 0):
-    """fp64 partials of descriptors desc int[n, 4]: (part_o [n,G,D], part_lse [n,G])."""
+    """fp64 partials of descriptors desc int[n, 4]: (part_o [n, q_len*G, D], part_lse [n, q_len*G]),
+    row i*G + g for query i, head g of the group."""
     bb = _Batch(batch)
     B, Hq, Hkv, D = bb.shape
-    G = Hq // Hkv
+    G = Hq // Hkv * bb.q_len
     desc = np.ascontiguousarray(np.asarray(desc, np.int32).reshape(-1, 4))
     n = desc.shape[0]
     po = np.zeros((n, G, D), np.float64)
