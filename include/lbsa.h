@@ -32,16 +32,23 @@
  *     entry outside [0, num_pages) poisons the affected rows with NaN instead
  *     of reading out of bounds;
  *   - supported shapes: head_dim 128, page_size 64, query-group size
- *     num_heads / num_kv_heads = 8.
+ *     num_heads / num_kv_heads = 8, q_len 1 or 2 query tokens per request.
+ *
+ * Multi-token decode (q_len = 2: verifying the draft token of Hy3's MTP
+ * speculative layer, vLLM post, the Hy3 model paragraph): the q_len new
+ * tokens of a request are the last q_len of its L cached tokens, and query i
+ * (0-based) attends to tokens [0, L - q_len + i] -- causal among the new
+ * tokens; a query that sees no token (L < q_len) gives a zero row.  The task
+ * map does not depend on q_len (tiles count KV tokens).
  *
  * Tensor layouts (row-major, contiguous):
- *   q           [batch][num_heads][128]          bf16, or e4m3fn with q_scale
- *   q_scale     [batch][num_heads]               fp32 (fp8 only)
+ *   q           [batch][q_len][num_heads][128]   bf16, or e4m3fn with q_scale
+ *   q_scale     [batch][q_len][num_heads]        fp32 (fp8 only)
  *   k/v cache   [num_pages][64][num_kv_heads][128] bf16 or e4m3fn (token-major)
  *   k/v scale   [num_pages][num_kv_heads][64]    fp32 (fp8 only)
  *   page_table  [batch][max_pages_per_seq]       int32 physical page ids
  *   seqlens     [batch]                          int32 live KV lengths
- *   out         [batch][num_heads][128]          bf16
+ *   out         [batch][q_len][num_heads][128]   bf16
  * Query head hq reads KV head hq / (num_heads / num_kv_heads).
  */
 #ifndef LBSA_H
@@ -57,7 +64,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------- */
 #define LBSA_OK 0
 #define LBSA_ERR_INVALID_ARGUMENT (-1) /* null pointer, size <= 0, buffer too small, Hq % Hkv != 0 */
-#define LBSA_ERR_UNSUPPORTED (-2)      /* head_dim != 128, page_size != 64, group != 8, too large */
+#define LBSA_ERR_UNSUPPORTED (-2)      /* head_dim != 128, page_size != 64, group != 8, q_len > 2, too large */
 #define LBSA_ERR_HIP (-3)              /* a HIP runtime call or launch failed */
 
 /* ---- constants ---------------------------------------------------------- */
@@ -67,6 +74,7 @@ extern "C" {
 #define LBSA_HEAD_DIM 128
 #define LBSA_GROUP 8             /* query heads per KV head */
 #define LBSA_DEFAULT_MIN_TILES 2 /* default minimum-work floor, tiles per active bin */
+#define LBSA_MAX_Q_LEN 2         /* query tokens per request the decode entry points take */
 
 /* Task-map header words (int32), see lbsa_plan. */
 #define LBSA_HDR_T 0        /* total tiles over all (kv_head, request) segments */
@@ -102,10 +110,10 @@ typedef struct {
     size_t total;           /* bytes */
 } lbsa_task_map_layout;
 
-/* Byte offsets inside the decode workspace. */
+/* Byte offsets inside the decode workspace (row 8 * query + head of the group). */
 typedef struct {
-    size_t part_lse;        /* fp32 [Hkv*B + P][8]: natural-log LSE of each partial */
-    size_t part_o;          /* fp32 [Hkv*B + P][8][128]: normalised partial outputs */
+    size_t part_lse;        /* fp32 [Hkv*B + P][q_len * 8]: natural-log LSE of each partial */
+    size_t part_o;          /* fp32 [Hkv*B + P][q_len * 8][128]: normalised partial outputs */
     size_t total;
 } lbsa_workspace_layout;
 
@@ -117,7 +125,9 @@ int lbsa_version(void);
 
 /* Default number of persistent workgroups on `device` for `kv_dtype`:
  * compute units x resident workgroups per CU of the split kernel (occupancy
- * query), so every bin is resident at once.  Writes *out_P. */
+ * query), so every bin is resident at once; the split kernels of q_len 1 and
+ * 2 have the same occupancy (one workgroup per CU, bound by LDS).  Writes
+ * *out_P. */
 int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_P);
 
 /* Layout and size of the task map for (batch, num_kv_heads, P). */
@@ -126,9 +136,9 @@ int lbsa_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32_t P,
 int lbsa_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t P, size_t* out_bytes);
 
 /* Layout and size of the split/combine workspace (partials). */
-int lbsa_workspace_layout_get(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+int lbsa_workspace_layout_get(int32_t batch, int32_t q_len, int32_t num_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t P, lbsa_workspace_layout* out);
-int lbsa_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+int lbsa_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t P, size_t* out_bytes);
 
 /*
@@ -153,6 +163,7 @@ int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_heads, int32_
  * Decode = split + combine with a task map from lbsa_plan (same batch,
  * num_heads, num_kv_heads and P).  Source: vLLM post, bullet "Compute and
  * combine"; SGLang post, "Scheduling around live KV work".
+ *   q_len                     query tokens per request, 1 or 2 (multi-token decode)
  *   q_d, q_scale_d            query (bf16, or e4m3 codes + fp32 scales for fp8)
  *   k_cache_d, v_cache_d      paged caches, kv_dtype LBSA_KV_BF16 or LBSA_KV_FP8_E4M3
  *   k_scale_d, v_scale_d      fp32 scales (fp8 only, else NULL)
@@ -160,14 +171,14 @@ int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_heads, int32_
  *   num_pages                 pages in each cache (page ids are checked against it)
  *   softmax_scale             multiplier of q.k (e.g. 1/sqrt(128))
  *   workspace_d               >= lbsa_workspace_bytes bytes, 256-byte aligned
- *   out_d                     bf16 [batch][num_heads][128]
+ *   out_d                     bf16 [batch][q_len][num_heads][128]
  * The q/k/v/out dtypes follow kv_dtype: bf16 path = bf16 q, bf16 caches; fp8
  * path = e4m3 q with q_scale, e4m3 caches with k/v scales.  Output is bf16
  * (round to nearest even) in both.
  */
 int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                 const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
-                int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t num_heads,
+                int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t q_len, int32_t num_heads,
                 int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                 int32_t max_pages_per_seq, int64_t num_pages, int32_t num_workgroups,
                 float softmax_scale, const void* task_map_d, size_t task_map_bytes,
@@ -177,21 +188,21 @@ int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
  * descriptor d).  Same arguments as lbsa_decode without out_d. */
 int lbsa_decode_split(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                       const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
-                      int32_t kv_dtype, const int32_t* page_table_d, int32_t batch,
+                      int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t q_len,
                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                       int32_t max_pages_per_seq, int64_t num_pages, int32_t num_workgroups,
                       float softmax_scale, const void* task_map_d, size_t task_map_bytes,
                       void* workspace_d, size_t workspace_bytes, void* stream);
 
 /* The combine half of lbsa_decode alone: merges the workspace partials of each
- * (request, query head) into out_d (bf16). */
-int lbsa_decode_combine(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+ * (request, query token, query head) into out_d (bf16). */
+int lbsa_decode_combine(int32_t batch, int32_t q_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t num_workgroups, const void* task_map_d, size_t task_map_bytes,
                         const void* workspace_d, size_t workspace_bytes, void* out_d,
                         void* stream);
 
 /* Workspace bytes of the static baseline: batch * Hkv * num_splits partials. */
-int lbsa_static_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+int lbsa_static_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t num_splits, size_t* out_bytes);
 
 /*
@@ -205,7 +216,7 @@ int lbsa_static_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv
 int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                        const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
                        int32_t kv_dtype, const int32_t* page_table_d, const int32_t* seqlens_d,
-                       int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t batch, int32_t q_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
                        int32_t num_splits, float softmax_scale, void* workspace_d,
                        size_t workspace_bytes, void* out_d, void* stream);

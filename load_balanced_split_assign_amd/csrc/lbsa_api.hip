@@ -14,13 +14,16 @@ namespace {
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 int check_shape(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                int32_t page_size) {
-    if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0)
+                int32_t page_size, int32_t q_len = 1) {
+    if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 || q_len <= 0)
         return LBSA_ERR_INVALID_ARGUMENT;
+    if (q_len > kMaxQLen) return LBSA_ERR_UNSUPPORTED;
     if (num_heads % num_kv_heads != 0) return LBSA_ERR_INVALID_ARGUMENT;
     if (head_dim != kHeadDim || page_size != kTile || num_heads / num_kv_heads != kGroup)
         return LBSA_ERR_UNSUPPORTED;
-    if ((long long)num_kv_heads * batch > (long long)INT_MAX / 4) return LBSA_ERR_UNSUPPORTED;
+    if ((long long)num_kv_heads * batch > (long long)INT_MAX / 4 ||
+        (long long)num_heads * batch * q_len > (long long)INT_MAX / 4)
+        return LBSA_ERR_UNSUPPORTED;
     return LBSA_OK;
 }
 
@@ -36,12 +39,12 @@ struct DecodeCommon {
 
 DecodeCommon check_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                           const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
-                          int32_t kv_dtype, const int32_t* page_table_d, int32_t batch,
+                          int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t q_len,
                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
                           float softmax_scale) {
     DecodeCommon c{};
-    c.status = check_shape(batch, num_heads, num_kv_heads, head_dim, page_size);
+    c.status = check_shape(batch, num_heads, num_kv_heads, head_dim, page_size, q_len);
     if (c.status != LBSA_OK) return c;
     if (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3) {
         c.status = LBSA_ERR_INVALID_ARGUMENT;
@@ -78,6 +81,7 @@ DecodeCommon check_decode(const void* q_d, const float* q_scale_d, const void* k
     a.page_table = page_table_d;
     a.num_pages = num_pages;
     a.B = batch;
+    a.QL = q_len;
     a.Hq = num_heads;
     a.Hkv = num_kv_heads;
     a.max_pages = max_pages_per_seq;
@@ -97,7 +101,7 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 101; }
+LBSA_API int lbsa_version(void) { return 200; }
 
 LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_P) {
     if (!out_P || (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3))
@@ -109,7 +113,7 @@ LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_
     if (hipGetDevice(&cur) != hipSuccess) return LBSA_ERR_HIP;
     if (cur != device && hipSetDevice(device) != hipSuccess) return LBSA_ERR_HIP;
     int per_cu = 0;
-    const hipError_t e = split_occupancy(kv_dtype == LBSA_KV_FP8_E4M3, &per_cu);
+    const hipError_t e = split_occupancy(kv_dtype == LBSA_KV_FP8_E4M3, 1, &per_cu);
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess || per_cu <= 0 || cus <= 0) return LBSA_ERR_HIP;
     *out_P = cus * per_cu;
@@ -140,33 +144,35 @@ LBSA_API int lbsa_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t P,
     return s;
 }
 
-LBSA_API int lbsa_workspace_layout_get(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t P, lbsa_workspace_layout* out) {
+LBSA_API int lbsa_workspace_layout_get(int32_t batch, int32_t q_len, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t P,
+                                       lbsa_workspace_layout* out) {
     if (!out || P <= 0) return LBSA_ERR_INVALID_ARGUMENT;
-    const int s = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile);
+    const int s = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile, q_len);
     if (s != LBSA_OK) return s;
-    const WsLayout w = ws_layout((size_t)num_kv_heads * batch + P);
+    const WsLayout w = ws_layout((size_t)num_kv_heads * batch + P, q_len);
     out->part_lse = w.part_lse;
     out->part_o = w.part_o;
     out->total = w.total;
     return LBSA_OK;
 }
 
-LBSA_API int lbsa_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+LBSA_API int lbsa_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t P, size_t* out_bytes) {
     if (!out_bytes) return LBSA_ERR_INVALID_ARGUMENT;
     lbsa_workspace_layout l;
-    const int s = lbsa_workspace_layout_get(batch, num_heads, num_kv_heads, head_dim, P, &l);
+    const int s = lbsa_workspace_layout_get(batch, q_len, num_heads, num_kv_heads, head_dim, P, &l);
     if (s == LBSA_OK) *out_bytes = l.total;
     return s;
 }
 
-LBSA_API int lbsa_static_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
-                                         int32_t head_dim, int32_t num_splits, size_t* out_bytes) {
+LBSA_API int lbsa_static_workspace_bytes(int32_t batch, int32_t q_len, int32_t num_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t num_splits,
+                                         size_t* out_bytes) {
     if (!out_bytes || num_splits <= 0) return LBSA_ERR_INVALID_ARGUMENT;
-    const int s = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile);
+    const int s = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile, q_len);
     if (s != LBSA_OK) return s;
-    *out_bytes = ws_layout((size_t)num_kv_heads * batch * num_splits).total;
+    *out_bytes = ws_layout((size_t)num_kv_heads * batch * num_splits, q_len).total;
     return LBSA_OK;
 }
 
@@ -195,19 +201,21 @@ LBSA_API int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_head
                                     static_cast<hipStream_t>(stream)));
 }
 
-static int decode_prepare(DecodeCommon& c, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
-                          int32_t head_dim, int32_t num_workgroups, const void* task_map_d,
-                          size_t task_map_bytes, void* workspace_d, size_t workspace_bytes) {
+static int decode_prepare(DecodeCommon& c, int32_t batch, int32_t q_len, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t num_workgroups,
+                          const void* task_map_d, size_t task_map_bytes, void* workspace_d,
+                          size_t workspace_bytes) {
     if (c.status != LBSA_OK) return c.status;
     if (!task_map_d || !workspace_d || num_workgroups <= 0 || !aligned(task_map_d, 16) ||
         !aligned(workspace_d, 256))
         return LBSA_ERR_INVALID_ARGUMENT;
     size_t map_need = 0, ws_need = 0;
     lbsa_task_map_bytes(batch, num_kv_heads, num_workgroups, &map_need);
-    const int s = lbsa_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, num_workgroups, &ws_need);
+    const int s = lbsa_workspace_bytes(batch, q_len, num_heads, num_kv_heads, head_dim, num_workgroups,
+                                       &ws_need);
     if (s != LBSA_OK) return s;
     if (task_map_bytes < map_need || workspace_bytes < ws_need) return LBSA_ERR_INVALID_ARGUMENT;
-    const WsLayout w = ws_layout((size_t)num_kv_heads * batch + num_workgroups);
+    const WsLayout w = ws_layout((size_t)num_kv_heads * batch + num_workgroups, q_len);
     c.a.map = static_cast<const uint8_t*>(task_map_d);
     c.a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) + w.part_lse);
     c.a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) + w.part_o);
@@ -218,32 +226,33 @@ static int decode_prepare(DecodeCommon& c, int32_t batch, int32_t num_heads, int
 LBSA_API int lbsa_decode_split(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                                const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
                                int32_t kv_dtype, const int32_t* page_table_d, int32_t batch,
-                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t q_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
                                int32_t num_workgroups, float softmax_scale, const void* task_map_d,
                                size_t task_map_bytes, void* workspace_d, size_t workspace_bytes,
                                void* stream) {
     DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
-                                  kv_dtype, page_table_d, batch, num_heads, num_kv_heads, head_dim,
+                                  kv_dtype, page_table_d, batch, q_len, num_heads, num_kv_heads, head_dim,
                                   page_size, max_pages_per_seq, num_pages, softmax_scale);
-    const int s = decode_prepare(c, batch, num_heads, num_kv_heads, head_dim, num_workgroups,
+    const int s = decode_prepare(c, batch, q_len, num_heads, num_kv_heads, head_dim, num_workgroups,
                                  task_map_d, task_map_bytes, workspace_d, workspace_bytes);
     if (s != LBSA_OK) return s;
     return hip_status(launch_split(c.a, c.fp8, static_cast<hipStream_t>(stream)));
 }
 
-LBSA_API int lbsa_decode_combine(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+LBSA_API int lbsa_decode_combine(int32_t batch, int32_t q_len, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t num_workgroups, const void* task_map_d,
                                  size_t task_map_bytes, const void* workspace_d,
                                  size_t workspace_bytes, void* out_d, void* stream) {
     DecodeCommon c{};
-    c.status = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile);
+    c.status = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile, q_len);
     if (c.status != LBSA_OK) return c.status;
     if (!out_d || !aligned(out_d, 8)) return LBSA_ERR_INVALID_ARGUMENT;
     c.a.B = batch;
+    c.a.QL = q_len;
     c.a.Hq = num_heads;
     c.a.Hkv = num_kv_heads;
-    const int s = decode_prepare(c, batch, num_heads, num_kv_heads, head_dim, num_workgroups,
+    const int s = decode_prepare(c, batch, q_len, num_heads, num_kv_heads, head_dim, num_workgroups,
                                  task_map_d, task_map_bytes, const_cast<void*>(workspace_d),
                                  workspace_bytes);
     if (s != LBSA_OK) return s;
@@ -253,16 +262,16 @@ LBSA_API int lbsa_decode_combine(int32_t batch, int32_t num_heads, int32_t num_k
 
 LBSA_API int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                          const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
-                         int32_t kv_dtype, const int32_t* page_table_d, int32_t batch,
+                         int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t q_len,
                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                          int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
                          int32_t num_workgroups, float softmax_scale, const void* task_map_d,
                          size_t task_map_bytes, void* workspace_d, size_t workspace_bytes,
                          void* out_d, void* stream) {
     DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
-                                  kv_dtype, page_table_d, batch, num_heads, num_kv_heads, head_dim,
+                                  kv_dtype, page_table_d, batch, q_len, num_heads, num_kv_heads, head_dim,
                                   page_size, max_pages_per_seq, num_pages, softmax_scale);
-    int s = decode_prepare(c, batch, num_heads, num_kv_heads, head_dim, num_workgroups, task_map_d,
+    int s = decode_prepare(c, batch, q_len, num_heads, num_kv_heads, head_dim, num_workgroups, task_map_d,
                            task_map_bytes, workspace_d, workspace_bytes);
     if (s != LBSA_OK) return s;
     if (!out_d || !aligned(out_d, 8)) return LBSA_ERR_INVALID_ARGUMENT;
@@ -277,13 +286,13 @@ LBSA_API int lbsa_decode_static(const void* q_d, const float* q_scale_d, const v
                                 const void* v_cache_d, const float* k_scale_d,
                                 const float* v_scale_d, int32_t kv_dtype,
                                 const int32_t* page_table_d, const int32_t* seqlens_d,
-                                int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t batch, int32_t q_len, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t page_size, int32_t max_pages_per_seq,
                                 int64_t num_pages, int32_t num_splits, float softmax_scale,
                                 void* workspace_d, size_t workspace_bytes, void* out_d,
                                 void* stream) {
     DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
-                                  kv_dtype, page_table_d, batch, num_heads, num_kv_heads, head_dim,
+                                  kv_dtype, page_table_d, batch, q_len, num_heads, num_kv_heads, head_dim,
                                   page_size, max_pages_per_seq, num_pages, softmax_scale);
     if (c.status != LBSA_OK) return c.status;
     if (!seqlens_d || !workspace_d || !out_d || num_splits <= 0 || !aligned(workspace_d, 256) ||
@@ -291,10 +300,11 @@ LBSA_API int lbsa_decode_static(const void* q_d, const float* q_scale_d, const v
         return LBSA_ERR_INVALID_ARGUMENT;
     if ((long long)num_splits * batch * num_kv_heads >= (1LL << 31)) return LBSA_ERR_UNSUPPORTED;
     size_t need = 0;
-    const int s = lbsa_static_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, num_splits, &need);
+    const int s = lbsa_static_workspace_bytes(batch, q_len, num_heads, num_kv_heads, head_dim, num_splits,
+                                              &need);
     if (s != LBSA_OK) return s;
     if (workspace_bytes < need) return LBSA_ERR_INVALID_ARGUMENT;
-    const WsLayout w = ws_layout((size_t)num_kv_heads * batch * num_splits);
+    const WsLayout w = ws_layout((size_t)num_kv_heads * batch * num_splits, q_len);
     c.a.seqlens = seqlens_d;
     c.a.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) + w.part_lse);
     c.a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) + w.part_o);

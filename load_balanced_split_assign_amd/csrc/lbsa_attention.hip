@@ -27,10 +27,13 @@
 //     live) instead, so no tail garbage or NaN ever reaches LDS; their scores
 //     are masked to -inf, so they contribute nothing.
 //   * S^T = K Q^T with MFMA 16x16x32 (rows = 16 tokens, columns = 16 query
-//     heads of which 8 are real), fp32 accumulation in two independent
-//     chains: bf16 operands for bf16 KV, the fp8 MFMA on the raw e4m3 codes of
-//     K and Q for fp8 KV (the per-token K scale and per-head Q scale multiply
-//     the score).
+//     rows: the 8 heads of the group for one query token per request, of
+//     which 8 columns are real, or 8 heads x 2 query tokens for multi-token
+//     decode, all 16 real), fp32 accumulation in two independent chains:
+//     bf16 operands for bf16 KV, the fp8 MFMA on the raw e4m3 codes of K and
+//     Q for fp8 KV (the per-token K scale and per-head Q scale multiply the
+//     score).  With 2 query tokens the later one sees one token more (causal
+//     among the new tokens): a per-column length limit in the score mask.
 //   * Online softmax in the exp2 domain with a lazy running max: a tile whose
 //     scores stay within kSlack of the running max is exponentiated against
 //     it directly; only when a wave-wide ballot finds a larger score does the
@@ -295,21 +298,24 @@ __device__ inline void lds_read_tile_fp8(uint4 (&o)[6], const uint32_t (&addr)[6
 // scales travel through the ring so that reading them needs no wait on a
 // register load (which the compiler turns into a wait for the whole ring).
 // ---------------------------------------------------------------------------
-template <bool FP8> struct Stage {
+// QL = query tokens per request (1, or 2 for multi-token decode): the Q codes
+// of a descriptor are QL x 8 heads x 128 B, and with QL = 2 the fp8 ring is
+// one stage shallower to leave LDS for the larger merge slots.
+template <bool FP8, int QL = 1> struct Stage {
     static constexpr int kRow = FP8 ? 128 : 256;        // bytes of one K/V row
     static constexpr int K = 0;
     static constexpr int V = 16 * kRow;
     static constexpr int KS = 32 * kRow;                // fp8 only: k scales
     static constexpr int VS = KS + 256;                 // fp8 only: v scales
-    static constexpr int QS = VS + 256;                 // fp8 only: the 8 q scales of the descriptor
-    static constexpr int QD = QS + 256;                 // fp8 only: Q codes, 8 heads x 128 B (first tiles)
-    static constexpr int BYTES = FP8 ? QD + 1024 : 32 * kRow;     // 5888 (fp8) / 8192 (bf16)
+    static constexpr int QS = VS + 256;                 // fp8 only: the 8 QL q scales of the descriptor
+    static constexpr int QD = QS + 256;                 // fp8 only: Q codes, QL x 8 heads x 128 B (first tiles)
+    static constexpr int BYTES = FP8 ? QD + 1024 * QL : 32 * kRow;   // 5888 / 6912 (fp8), 8192 (bf16)
     static constexpr int KV_LOADS = 16 * kRow / 1024;   // loads per K (or V) slice: 4 (bf16) / 2 (fp8)
     // ring loads issued for every tile (fp8 adds one more, the Q codes, on a
     // descriptor's first tile; the waits count only the fixed ones, which can
     // only make them wait for a little more than the stage)
     static constexpr int LOADS = 2 * KV_LOADS + (FP8 ? 3 : 0);
-    static constexpr int STAGES = FP8 ? 5 : 3;          // ring depth: STAGES - 1 tiles in flight
+    static constexpr int STAGES = FP8 ? (QL == 1 ? 5 : 4) : 3;   // ring depth: STAGES - 1 tiles in flight
 };
 static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt range");
 static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
@@ -323,27 +329,33 @@ __device__ inline int swz_bf16(int row) { return row & 15; }
 // asynchronous load an LDS read depends on (distinct underlying objects) and
 // does not fall back to waiting for all of them.
 //
-// Each wave has one slot (kWaveSlot bytes) that holds its bf16 copy of the
+// Each wave has one slot (Slot<QL>::kWave bytes) that holds its bf16 copy of the
 // fp8 V slice during a tile and its (O, m, l, flag) for the merge at the end of
 // a descriptor; the two uses of a slot never overlap in time (program order
 // within the wave, and the merge's closing barrier before any wave's next
 // tile), so for fp8 they share the memory.
-constexpr int kMergeWave = (kGroup * kHeadDim + 2 * kGroup + 4) * 4;   // O, m, l, flag per wave
 constexpr int kVbWave = 16 * 256;                                      // 16 V rows as bf16
-constexpr int kWaveSlot = 17 * 256;                                    // >= both, 256-aligned
-static_assert(kWaveSlot >= kMergeWave && kWaveSlot >= kVbWave, "wave slot");
-constexpr int kSlotBytes = kWaves * kWaveSlot;
+template <int QL> struct Slot {
+    static constexpr int kRows = kGroup * QL;                          // query rows of a descriptor
+    static constexpr int kMerge = (kRows * kHeadDim + 2 * kRows + 4) * 4;   // O, m, l, flag per wave
+    static constexpr int kWave = QL == 1 ? 17 * 256 : 33 * 256;        // >= both uses, 256-aligned
+    static constexpr int kBytes = kWaves * kWave;
+    static_assert(kWave >= kMerge && kWave >= kVbWave, "wave slot");
+};
 constexpr int kMaxStages = 6;
 template <bool FP8> struct Smem {
     lds_char* stage[kMaxStages];   // [kWaves][Stage::BYTES] each; the first STAGES are used
-    lds_char* vb;                  // fp8: [kWaves][kWaveSlot], the bf16 copy of the V slice
-    lds_char* merge;               // [kWaves][kWaveSlot] (for fp8 the same memory as vb)
+    lds_char* vb;                  // fp8: [kWaves][Slot::kWave], the bf16 copy of the V slice
+    lds_char* merge;               // [kWaves][Slot::kWave] (for fp8 the same memory as vb)
 };
-template <bool FP8> constexpr int stage_array_bytes(int u) {
-    return u < Stage<FP8>::STAGES ? kWaves * Stage<FP8>::BYTES : 16;
+template <bool FP8, int QL> constexpr int stage_array_bytes(int u) {
+    return u < Stage<FP8, QL>::STAGES ? kWaves * Stage<FP8, QL>::BYTES : 16;
 }
-static_assert(kWaves * Stage<false>::BYTES * Stage<false>::STAGES + kSlotBytes <= 160 * 1024, "LDS");
-static_assert(kWaves * Stage<true>::BYTES * Stage<true>::STAGES + kSlotBytes <= 160 * 1024, "LDS");
+template <bool FP8, int QL> constexpr int smem_bytes() {
+    return kWaves * Stage<FP8, QL>::BYTES * Stage<FP8, QL>::STAGES + Slot<QL>::kBytes;
+}
+static_assert(smem_bytes<false, 1>() <= 160 * 1024 && smem_bytes<true, 1>() <= 160 * 1024, "LDS");
+static_assert(smem_bytes<false, 2>() <= 160 * 1024 && smem_bytes<true, 2>() <= 160 * 1024, "LDS");
 
 // One descriptor of the tile stream (all fields wave-uniform).
 struct Desc {
@@ -374,10 +386,10 @@ template <bool FP8> struct LaneLoads {
 
 // Issue the asynchronous loads of one tile into stage `st`: this wave's 16 K
 // and V rows of page `page` and, for fp8, their k/v scales.
-template <bool FP8>
+template <bool FP8, int QL>
 __device__ inline void issue_tile(const AttnArgs& a, const LaneLoads<FP8>& ll, lds_char* __restrict__ st,
                                   int64_t page, const Desc& d, int tile, int w) {
-    using SL = Stage<FP8>;
+    using SL = Stage<FP8, QL>;
     const size_t pbase = ((size_t)page * kTile * a.Hkv + d.h) * SL::kRow;
     const char* kb = static_cast<const char*>(a.k_cache) + pbase;
     const char* vb = static_cast<const char*>(a.v_cache) + pbase;
@@ -394,7 +406,9 @@ __device__ inline void issue_tile(const AttnArgs& a, const LaneLoads<FP8>& ll, l
         const int srow = (full || tok0 + ll.scale_row < d.L) ? 16 * w + ll.scale_row : 0;
         dma4(a.k_scale + sbase + srow, st + SL::KS);
         dma4(a.v_scale + sbase + srow, st + SL::VS);
-        dma4(a.q_scale + ((size_t)d.b * a.Hq + (size_t)d.h * kGroup) + (threadIdx.x & 7), st + SL::QS);
+        // lane i brings the scale of query (i / 8) % QL, head i % 8 (q_scale [B][QL][Hq])
+        const int qi = QL == 1 ? 0 : (threadIdx.x >> 3) & (QL - 1);
+        dma4(a.q_scale + ((size_t)(d.b * QL + qi) * a.Hq + (size_t)d.h * kGroup) + (threadIdx.x & 7), st + SL::QS);
     }
 }
 
@@ -414,28 +428,35 @@ template <> struct QOp<true> { uint4 v[2]; };
 
 // bf16: plain loads into registers, issued when the load cursor enters a
 // descriptor (its first tile), several tiles before the compute cursor needs
-// them.  fp8: the 8 x 128 B of Q codes go into the stage with that first tile
-// (lane i moves bytes [16 i, 16 i + 16) of the row-major block).
-template <bool FP8>
+// them; column r holds query r / 8, head r % 8 (q [B][QL][Hq][128]).  fp8:
+// the QL x 8 x 128 B of Q codes go into the stage with that first tile (lane
+// i moves bytes [16 i, 16 i + 16) of each query's row-major block).
+template <bool FP8, int QL>
 __device__ inline void load_q(const AttnArgs& a, const Desc& d, int r, int g, QOp<FP8>& q, lds_char* st) {
     if constexpr (!FP8) {
-        const size_t row = (size_t)d.b * a.Hq + (size_t)d.h * kGroup + (r & 7);
+        const int qi = QL == 1 ? 0 : (r >> 3) & (QL - 1);
+        const size_t row = (size_t)(d.b * QL + qi) * a.Hq + (size_t)d.h * kGroup + (r & 7);
         const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + row * 256);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) q.v[ks] = qp[g + 4 * ks];
     } else {
-        const size_t row0 = (size_t)d.b * a.Hq + (size_t)d.h * kGroup;
-        dma16(static_cast<const char*>(a.q) + row0 * 128 + 16 * (threadIdx.x & 63), st + Stage<true>::QD);
+#pragma unroll
+        for (int qi = 0; qi < QL; ++qi) {
+            const size_t row0 = (size_t)(d.b * QL + qi) * a.Hq + (size_t)d.h * kGroup;
+            dma16(static_cast<const char*>(a.q) + row0 * 128 + 16 * (threadIdx.x & 63),
+                  st + Stage<true, QL>::QD + 1024 * qi);
+        }
     }
 }
 
-// QK^T, online softmax and PV of one tile held in stage `st`.
-template <bool FP8>
+// QK^T, online softmax and PV of one tile held in stage `st`.  `lim` is the
+// token limit of this lane's column (its query sees tokens < lim).
+template <bool FP8, int QL>
 __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* __restrict__ vb, const QOp<FP8>& q,
-                                    float sl2, int tok0, int L, int w, int r, int g, WaveState& ws) {
+                                    float sl2, int tok0, int lim, int w, int r, int g, WaveState& ws) {
     const uint4 z4 = make_uint4(0, 0, 0, 0);
-    const bool qlive = r < kGroup;
-    using SL = Stage<FP8>;
+    const bool qlive = r < kGroup * QL;
+    using SL = Stage<FP8, QL>;
     // ---- operands from LDS, then S^T = K Q^T (rows = 16 tokens, cols = 16 heads)
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
     const int vrow = 4 * g + (r >> 2);            // transposed-read row of this lane
@@ -505,7 +526,7 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
     for (int i = 0; i < 4; ++i) {
         float x = s[i] * sl2;
         if constexpr (FP8) x *= ks4[i];
-        sc[i] = (pos0 + i < L) ? x : kNegInf;
+        sc[i] = (pos0 + i < lim) ? x : kNegInf;
     }
     const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if (__builtin_amdgcn_ballot_w64(lmax > ws.m + kSlack) != 0) {
@@ -513,7 +534,10 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
         float mt = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(ws.m, mt);
-        const float alpha = exp2_fast(ws.m - m_new);      // 0 when nothing was accumulated yet
+        // 0 when nothing was accumulated yet (also when this column is still
+        // fully masked, m_new = -inf: a wave-wide rescale may come from another
+        // column, and -inf - -inf would give NaN)
+        const float alpha = ws.m == kNegInf ? 0.f : exp2_fast(ws.m - m_new);
         ws.l *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; ++db) ws.acc[db] *= alpha;
@@ -542,47 +566,57 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
 }
 
 // End of a descriptor: merge the 4 waves' (max, sum, O) through LDS and write
-// the partial (normalised O, natural-log LSE) of `slot`.
+// the partial (normalised O, natural-log LSE) of `slot`: QL x 8 rows, row
+// r = 8 query + head.  Every descriptor holds a token the last query sees, so
+// a row of that query with nothing accumulated means bad data (NaN); an
+// earlier query may legitimately see none of the descriptor's tokens, which
+// gives an empty partial (O = 0, LSE = -inf) that the combine skips.
+template <int QL>
 __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const WaveState& ws, bool bad,
                                    int64_t slot, int w, int lane, int r, int g) {
+    constexpr int R = Slot<QL>::kRows;
     float lsum = ws.l;
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
-    lds_float* o_w = reinterpret_cast<lds_float*>(merge + w * kWaveSlot);
-    if (r < kGroup) {
+    lds_float* o_w = reinterpret_cast<lds_float*>(merge + w * Slot<QL>::kWave);
+    if (r < R) {
 #pragma unroll
         for (int db = 0; db < 8; ++db)
             *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(o_w + r * kHeadDim + 16 * db + 4 * g) = ws.acc[db];
         if (g == 0) {
-            o_w[kGroup * kHeadDim + r] = ws.m;
-            o_w[kGroup * kHeadDim + kGroup + r] = lsum;
+            o_w[R * kHeadDim + r] = ws.m;
+            o_w[R * kHeadDim + R + r] = lsum;
         }
     }
-    if (lane == 0) o_w[kGroup * kHeadDim + 2 * kGroup] = bad ? 1.f : 0.f;
+    if (lane == 0) o_w[R * kHeadDim + 2 * R] = bad ? 1.f : 0.f;
     lds_barrier();
-    {
+#pragma unroll
+    for (int pass = 0; pass < QL; ++pass) {
         const int tid = threadIdx.x;
-        const int hh = tid >> 5, d4 = (tid & 31) * 4;
+        const int hh = kGroup * pass + (tid >> 5), d4 = (tid & 31) * 4;
         float M = kNegInf;
         bool any_bad = false;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * kWaveSlot);
-            M = fmaxf(M, ow[kGroup * kHeadDim + hh]);
-            any_bad |= ow[kGroup * kHeadDim + 2 * kGroup] != 0.f;
+            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * Slot<QL>::kWave);
+            M = fmaxf(M, ow[R * kHeadDim + hh]);
+            any_bad |= ow[R * kHeadDim + 2 * R] != 0.f;
         }
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
         float lt = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * kWaveSlot);
-            const float mw = ow[kGroup * kHeadDim + hh];
+            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * Slot<QL>::kWave);
+            const float mw = ow[R * kHeadDim + hh];
             const float sw = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
-            lt += sw * ow[kGroup * kHeadDim + kGroup + hh];
+            lt += sw * ow[R * kHeadDim + R + hh];
             o += sw * *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(ow + hh * kHeadDim + d4);
         }
         float lse;
-        if (any_bad || M == kNegInf || !(lt > 0.f)) {
+        if (!any_bad && M == kNegInf && pass < QL - 1) {
+            o = f32x4{0.f, 0.f, 0.f, 0.f};                 // an earlier query that sees none of it
+            lse = kNegInf;
+        } else if (any_bad || M == kNegInf || !(lt > 0.f)) {
             const float nan = __builtin_nanf("");
             o = f32x4{nan, nan, nan, nan};
             lse = nan;
@@ -590,8 +624,8 @@ __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const Wav
             o *= 1.f / lt;
             lse = (M + __builtin_log2f(lt)) * kLn2;
         }
-        *reinterpret_cast<f32x4*>(a.part_o + ((size_t)slot * kGroup + hh) * kHeadDim + d4) = o;
-        if ((tid & 31) == 0) a.part_lse[(size_t)slot * kGroup + hh] = lse;
+        *reinterpret_cast<f32x4*>(a.part_o + ((size_t)slot * R + hh) * kHeadDim + d4) = o;
+        if ((tid & 31) == 0) a.part_lse[(size_t)slot * R + hh] = lse;
     }
     lds_barrier();   // the merge area is reused by the next descriptor
 }
@@ -665,14 +699,14 @@ struct Cursor {
 // the last tile it re-issues the last tile into a stage that is never read, so
 // every step issues the same number of ring loads.  `page` is the page id of
 // the cursor's tile, loaded one step ahead; the next one is fetched here.
-template <bool FP8, class Src>
+template <bool FP8, int QL, class Src>
 __device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, Cursor<Src>& lc, int& issued,
                                   int ntiles, int64_t& page, uint32_t& bad_bits, lds_char* st, QOp<FP8>& qslot,
                                   int slot, int w, int r, int g) {
     const bool ok = page >= 0 && page < a.num_pages;
     bad_bits = (bad_bits & ~(1u << slot)) | ((uint32_t)(!ok) << slot);
-    if (issued < ntiles && lc.t == lc.d.t0) load_q<FP8>(a, lc.d, r, g, qslot, st);
-    issue_tile<FP8>(a, ll, st, ok ? page : 0, lc.d, lc.t, w);
+    if (issued < ntiles && lc.t == lc.d.t0) load_q<FP8, QL>(a, lc.d, r, g, qslot, st);
+    issue_tile<FP8, QL>(a, ll, st, ok ? page : 0, lc.d, lc.t, w);
     if (++issued < ntiles) {
         lc.next();
         page = (int64_t)uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
@@ -682,14 +716,16 @@ __device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, C
 // Stream the tiles of `src` through this workgroup (see the header comment).
 // `ntiles` is the number of tiles the source holds (at least 1); with a
 // corrupt map that holds fewer, the cursors repeat their last tile.
-template <bool FP8, class Src>
+template <bool FP8, int QL, class Src>
 __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const Smem<FP8>& sm) {
-    using SL = Stage<FP8>;
+    using SL = Stage<FP8, QL>;
     constexpr int S = SL::STAGES;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
+    // column r's query sees the request's tokens below L - (QL - 1 - query)
+    const int lim_off = (QL == 1 ? 0 : min(r >> 3, QL - 1)) - (QL - 1);
     auto stage = [&](int u) -> lds_char* { return sm.stage[u] + w * SL::BYTES; };
-    lds_char* vb = sm.vb + w * kWaveSlot;
+    lds_char* vb = sm.vb + w * Slot<QL>::kWave;
     LaneLoads<FP8> ll;
     ll.init(a.Hkv, w, lane);
 
@@ -702,7 +738,7 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     QOp<FP8> qring[S];              // Q of the descriptor whose first tile sits in stage u
 #pragma unroll
     for (int u = 0; u < S - 1; ++u)
-        issue_step<FP8>(a, ll, lc, issued, ntiles, page, bad_bits, stage(u), qring[u], u, w, r, g);
+        issue_step<FP8, QL>(a, ll, lc, issued, ntiles, page, bad_bits, stage(u), qring[u], u, w, r, g);
 
     Cursor<Src> cc;
     cc.begin(&src);
@@ -714,18 +750,20 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
 #pragma unroll
         for (int u = 0; u < S; ++u) {
             const int kk = k + u;
-            issue_step<FP8>(a, ll, lc, issued, ntiles, page, bad_bits, stage((u + S - 1) % S), qring[(u + S - 1) % S],
-                            (u + S - 1) % S, w, r, g);                     // tile kk + S - 1
+            issue_step<FP8, QL>(a, ll, lc, issued, ntiles, page, bad_bits, stage((u + S - 1) % S),
+                                qring[(u + S - 1) % S], (u + S - 1) % S, w, r, g);   // tile kk + S - 1
             wait_vmcnt<(S - 1) * SL::LOADS>();                             // tile kk has landed
             if (kk < ntiles) {
                 if (cc.t == cc.d.t0) {                                     // first tile of a descriptor
+                    // column r: row r of the QL x 8 Q block, scale r of the 8 QL scales
+                    constexpr int kColMask = kGroup * QL - 1;
                     if constexpr (FP8)
-                        lds_read2x16(q.v[0], q.v[1], lds_addr(stage(u) + SL::QD) + 128 * (r & 7) + 16 * g,
-                                     lds_addr(stage(u) + SL::QD) + 128 * (r & 7) + 16 * g + 64);
+                        lds_read2x16(q.v[0], q.v[1], lds_addr(stage(u) + SL::QD) + 128 * (r & kColMask) + 16 * g,
+                                     lds_addr(stage(u) + SL::QD) + 128 * (r & kColMask) + 16 * g + 64);
                     else
                         q = qring[u];
                     sl2 = a.scale_log2;
-                    if constexpr (FP8) sl2 *= lds_read_f32(lds_addr(stage(u) + SL::QS) + 4 * (r & 7));
+                    if constexpr (FP8) sl2 *= lds_read_f32(lds_addr(stage(u) + SL::QS) + 4 * (r & kColMask));
 #pragma unroll
                     for (int db = 0; db < 8; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
                     ws.m = kNegInf;
@@ -733,8 +771,8 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
                     bad = false;
                 }
                 bad |= (bad_bits >> u) & 1u;
-                tile_compute<FP8>(stage(u), vb, q, sl2, 64 * cc.t, cc.d.L, w, r, g, ws);
-                if (cc.t + 1 == cc.d.t1) finish_desc(a, sm.merge, ws, bad, cc.d.slot, w, lane, r, g);
+                tile_compute<FP8, QL>(stage(u), vb, q, sl2, 64 * cc.t, cc.d.L + lim_off, w, r, g, ws);
+                if (cc.t + 1 == cc.d.t1) finish_desc<QL>(a, sm.merge, ws, bad, cc.d.slot, w, lane, r, g);
                 cc.next();
             }
         }
@@ -742,14 +780,14 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     wait_vmcnt<0>();   // no load may still target LDS when the workgroup moves on
 }
 
-#define LBSA_DECLARE_SMEM(FP8)                                                 \
-    __shared__ __attribute__((aligned(16))) char s0[stage_array_bytes<FP8>(0)]; \
-    __shared__ __attribute__((aligned(16))) char s1[stage_array_bytes<FP8>(1)]; \
-    __shared__ __attribute__((aligned(16))) char s2[stage_array_bytes<FP8>(2)]; \
-    __shared__ __attribute__((aligned(16))) char s3[stage_array_bytes<FP8>(3)]; \
-    __shared__ __attribute__((aligned(16))) char s4[stage_array_bytes<FP8>(4)]; \
-    __shared__ __attribute__((aligned(16))) char s5[stage_array_bytes<FP8>(5)]; \
-    __shared__ __attribute__((aligned(16))) char sslot[kSlotBytes];             \
+#define LBSA_DECLARE_SMEM(FP8, QL)                                                  \
+    __shared__ __attribute__((aligned(16))) char s0[stage_array_bytes<FP8, QL>(0)]; \
+    __shared__ __attribute__((aligned(16))) char s1[stage_array_bytes<FP8, QL>(1)]; \
+    __shared__ __attribute__((aligned(16))) char s2[stage_array_bytes<FP8, QL>(2)]; \
+    __shared__ __attribute__((aligned(16))) char s3[stage_array_bytes<FP8, QL>(3)]; \
+    __shared__ __attribute__((aligned(16))) char s4[stage_array_bytes<FP8, QL>(4)]; \
+    __shared__ __attribute__((aligned(16))) char s5[stage_array_bytes<FP8, QL>(5)]; \
+    __shared__ __attribute__((aligned(16))) char sslot[Slot<QL>::kBytes];           \
     Smem<FP8> sm; /* address-space casts to LDS */                             \
     sm.stage[0] = (lds_char*)s0;                                               \
     sm.stage[1] = (lds_char*)s1;                                               \
@@ -763,9 +801,9 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
 // One workgroup per bin (grid = P).  The header words and the bin's head
 // record are independent loads, so the first page-table and K/V loads follow
 // after a single round trip to the map.
-template <bool FP8>
+template <bool FP8, int QL>
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
-    LBSA_DECLARE_SMEM(FP8);
+    LBSA_DECLARE_SMEM(FP8, QL);
     const MapLayout ML = map_layout(a.B, a.Hkv, a.P);
     const int j = blockIdx.x;
     const auto* hdr = uniform_ptr<int32_t>(a.map + ML.header);
@@ -788,12 +826,12 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
     src.head = RawDesc{r_h, r_b, r_t0, r_t1, r_len};
     // tiles of bin j from the header's bin sizes (the descriptors' tiles sum to it)
     const int ntiles = j < h_k ? min(h_q + (j < h_r ? 1 : 0), a.B * a.max_pages) : 0;
-    if (ntiles > 0) run_stream<FP8>(a, src, ntiles, sm);
+    if (ntiles > 0) run_stream<FP8, QL>(a, src, ntiles, sm);
 }
 
-template <bool FP8>
+template <bool FP8, int QL>
 __global__ __launch_bounds__(kSplitThreads) void static_kernel(AttnArgs a) {
-    LBSA_DECLARE_SMEM(FP8);
+    LBSA_DECLARE_SMEM(FP8, QL);
     const int S = a.P;
     const int split = blockIdx.x % S;
     const int rest = blockIdx.x / S;
@@ -806,10 +844,14 @@ __global__ __launch_bounds__(kSplitThreads) void static_kernel(AttnArgs a) {
     const int t0 = (int)((int64_t)split * n / S);
     const int t1 = (int)((int64_t)(split + 1) * n / S);
     if (t1 <= t0) {   // empty split: weight 0 in the combine (NaN if the length was invalid)
+        constexpr int R = Slot<QL>::kRows;
         const int tid = threadIdx.x;
-        const int hh = tid >> 5, d4 = (tid & 31) * 4;
-        *reinterpret_cast<f32x4*>(a.part_o + ((size_t)slot * kGroup + hh) * kHeadDim + d4) = f32x4{0.f, 0.f, 0.f, 0.f};
-        if ((tid & 31) == 0) a.part_lse[(size_t)slot * kGroup + hh] = len_ok ? kNegInf : __builtin_nanf("");
+#pragma unroll
+        for (int pass = 0; pass < QL; ++pass) {
+            const int hh = kGroup * pass + (tid >> 5), d4 = (tid & 31) * 4;
+            *reinterpret_cast<f32x4*>(a.part_o + ((size_t)slot * R + hh) * kHeadDim + d4) = f32x4{0.f, 0.f, 0.f, 0.f};
+            if ((tid & 31) == 0) a.part_lse[(size_t)slot * R + hh] = len_ok ? kNegInf : __builtin_nanf("");
+        }
         return;
     }
     OneDesc src;
@@ -819,7 +861,7 @@ __global__ __launch_bounds__(kSplitThreads) void static_kernel(AttnArgs a) {
     src.d.t1 = t1;
     src.d.L = L;
     src.d.slot = slot;
-    run_stream<FP8>(a, src, t1 - t0, sm);
+    run_stream<FP8, QL>(a, src, t1 - t0, sm);
 }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
@@ -844,7 +886,7 @@ __device__ inline void merge_chunk(float l, f32x4 x, float& m, float& wsum, f32x
     o += wgt * x;
 }
 
-// One workgroup per (request, query head).  Its 256 threads form 8 slices of
+// One workgroup per (request, query token, query head).  Its 256 threads form 8 slices of
 // 32 (4 consecutive d per thread); slice c0 merges chunks c0, c0 + 8, ... of
 // the row in one pass with a running (max LSE, weight sum, weighted O), four
 // chunks' loads in flight at a time, and the 8 slice states are merged
@@ -855,9 +897,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
     __shared__ float red_w[kSlices];
     __shared__ int red_nan;
     __shared__ __attribute__((aligned(16))) float red_o[kSlices][kHeadDim];
-    const int row = blockIdx.x;
-    const int b = row / a.Hq, hq = row - b * a.Hq;
+    const int row = blockIdx.x;                         // (b * QL + query) * Hq + hq
+    const int bq = row / a.Hq, hq = row - bq * a.Hq;
+    const int b = bq / a.QL, qi = bq - b * a.QL;
     const int h = hq / kGroup, gq = hq - h * kGroup;
+    const int R = kGroup * a.QL;                        // partial rows per slot
     const int64_t seg = (int64_t)h * a.B + b;
     const int tid = threadIdx.x, slice = tid >> 5, d4 = (tid & 31) * 4;
 
@@ -890,7 +934,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
     float m = kNegInf, wsum = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     bool nan_seen = false;
-    auto pr = [&](int c) { return (d0 + c) * kGroup + gq; };
+    auto pr = [&](int c) { return (d0 + c) * R + kGroup * qi + gq; };
     int c = slice;
     for (; c + 3 * kSlices < n; c += 4 * kSlices) {     // four chunks' loads in flight
         float l[4];
@@ -933,7 +977,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
             const float nan = __builtin_nanf("");
             acc = f32x4{nan, nan, nan, nan};
         }
-        uint16_t* out = static_cast<uint16_t*>(a.out) + ((size_t)b * a.Hq + hq) * kHeadDim + d4;
+        uint16_t* out = static_cast<uint16_t*>(a.out) + (size_t)row * kHeadDim + d4;
         uint2 packed;
         packed.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
         packed.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
@@ -944,29 +988,45 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
 }  // namespace
 
 hipError_t launch_split(const AttnArgs& a, bool fp8, hipStream_t stream) {
-    if (fp8) hipLaunchKernelGGL(split_kernel<true>, dim3(a.P), dim3(kSplitThreads), 0, stream, a);
-    else hipLaunchKernelGGL(split_kernel<false>, dim3(a.P), dim3(kSplitThreads), 0, stream, a);
+    const dim3 grid(a.P), block(kSplitThreads);
+    if (a.QL == 2) {
+        if (fp8) hipLaunchKernelGGL((split_kernel<true, 2>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((split_kernel<false, 2>), grid, block, 0, stream, a);
+    } else {
+        if (fp8) hipLaunchKernelGGL((split_kernel<true, 1>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((split_kernel<false, 1>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
-    const long long grid = (long long)a.P * a.B * a.Hkv;
-    if (fp8) hipLaunchKernelGGL(static_kernel<true>, dim3((unsigned)grid), dim3(kSplitThreads), 0, stream, a);
-    else hipLaunchKernelGGL(static_kernel<false>, dim3((unsigned)grid), dim3(kSplitThreads), 0, stream, a);
+    const dim3 grid((unsigned)((long long)a.P * a.B * a.Hkv)), block(kSplitThreads);
+    if (a.QL == 2) {
+        if (fp8) hipLaunchKernelGGL((static_kernel<true, 2>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((static_kernel<false, 2>), grid, block, 0, stream, a);
+    } else {
+        if (fp8) hipLaunchKernelGGL((static_kernel<true, 1>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((static_kernel<false, 1>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream) {
-    const long long grid = (long long)a.B * a.Hq;
+    const long long grid = (long long)a.B * a.QL * a.Hq;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a,
                        static_mode ? 1 : 0);
     return hipGetLastError();
 }
 
-hipError_t split_occupancy(bool fp8, int* blocks_per_cu) {
+hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu) {
+    if (q_len == 2) {
+        if (fp8)
+            return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, split_kernel<true, 2>, kSplitThreads, 0);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, split_kernel<false, 2>, kSplitThreads, 0);
+    }
     if (fp8)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, split_kernel<true>, kSplitThreads, 0);
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, split_kernel<false>, kSplitThreads, 0);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, split_kernel<true, 1>, kSplitThreads, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, split_kernel<false, 1>, kSplitThreads, 0);
 }
 
 }  // namespace lbsa

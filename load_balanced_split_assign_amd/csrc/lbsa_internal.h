@@ -46,18 +46,22 @@ __host__ __device__ inline MapLayout map_layout(int B, int Hkv, int P) {
     return m;
 }
 
-// Byte offsets of the partial buffers for `slots` partials of G x D.
+// Byte offsets of the partial buffers for `slots` partials of (q_len x G) x D
+// (one row per query token and head of the group).
 struct WsLayout {
     size_t part_lse, part_o, total;
 };
 
-__host__ __device__ inline WsLayout ws_layout(size_t slots) {
+__host__ __device__ inline WsLayout ws_layout(size_t slots, int q_len) {
+    const size_t rows = slots * (size_t)kGroup * (size_t)q_len;
     WsLayout w;
     w.part_lse = 0;
-    w.part_o = align_up(4 * slots * kGroup, 256);
-    w.total = align_up(w.part_o + 4 * slots * kGroup * kHeadDim, 256);
+    w.part_o = align_up(4 * rows, 256);
+    w.total = align_up(w.part_o + 4 * rows * kHeadDim, 256);
     return w;
 }
+
+constexpr int kMaxQLen = 2;     // query tokens per request the decode kernels take
 
 // Arguments of the attention kernels (passed by value).
 struct AttnArgs {
@@ -76,6 +80,7 @@ struct AttnArgs {
     int64_t num_pages;
     int32_t B, Hq, Hkv, max_pages;
     int32_t P;                   // split: bins; static: number of splits
+    int32_t QL;                  // query tokens per request (1 .. kMaxQLen)
     float scale_log2;            // softmax_scale * log2(e)
 };
 
@@ -85,7 +90,7 @@ hipError_t launch_assign(const int32_t* seqlens, int B, int Hq, int Hkv, int P, 
 hipError_t launch_split(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream);
-hipError_t split_occupancy(bool fp8, int* blocks_per_cu);
+hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu);
 hipError_t launch_prologue(const uint16_t* qkv, const int32_t* positions, const int64_t* slots,
                            const float* qw, const float* kw, double theta, float eps, int T, int Hq,
                            int Hkv, bool fp8, void* q_out, float* q_scale, void* k_cache, void* v_cache,

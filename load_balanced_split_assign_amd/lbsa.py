@@ -57,15 +57,16 @@ def lib() -> ctypes.CDLL:
         L.lbsa_default_workgroups.argtypes = [ctypes.c_int, i32, ctypes.POINTER(i32)]
         L.lbsa_task_map_layout_get.argtypes = [i32, i32, i32, ctypes.POINTER(_MapLayout)]
         L.lbsa_task_map_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
-        L.lbsa_workspace_layout_get.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_WsLayout)]
-        L.lbsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
-        L.lbsa_static_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.lbsa_workspace_layout_get.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(_WsLayout)]
+        L.lbsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.lbsa_static_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.lbsa_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
-        attn = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i64, i32, f32, vp, sz, vp, sz]
+        attn = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, i64, i32, f32, vp, sz, vp,
+                sz]
         L.lbsa_decode.argtypes = attn + [vp, vp]
         L.lbsa_decode_split.argtypes = attn + [vp]
-        L.lbsa_decode_combine.argtypes = [i32, i32, i32, i32, i32, vp, sz, vp, sz, vp, vp]
-        L.lbsa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+        L.lbsa_decode_combine.argtypes = [i32, i32, i32, i32, i32, i32, vp, sz, vp, sz, vp, vp]
+        L.lbsa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, i64, i32, f32, vp, sz, vp, vp]
         L.lbsa_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, f32, i32, i32, i32, i32, i32, i32,
                                     vp, vp, vp, vp, vp, vp, i64, vp]
@@ -122,25 +123,27 @@ def task_map_bytes(batch: int, num_kv_heads: int, P: int) -> int:
     return int(out.value)
 
 
-def workspace_layout(batch: int, num_heads: int, num_kv_heads: int, P: int, head_dim: int = HEAD_DIM) -> dict:
+def workspace_layout(batch: int, num_heads: int, num_kv_heads: int, P: int, head_dim: int = HEAD_DIM,
+                     q_len: int = 1) -> dict:
     w = _WsLayout()
     _check("lbsa_workspace_layout_get",
-           lib().lbsa_workspace_layout_get(batch, num_heads, num_kv_heads, head_dim, P, ctypes.byref(w)))
+           lib().lbsa_workspace_layout_get(batch, q_len, num_heads, num_kv_heads, head_dim, P, ctypes.byref(w)))
     return {n: int(getattr(w, n)) for n, _ in w._fields_}
 
 
-def workspace_bytes(batch: int, num_heads: int, num_kv_heads: int, P: int, head_dim: int = HEAD_DIM) -> int:
+def workspace_bytes(batch: int, num_heads: int, num_kv_heads: int, P: int, head_dim: int = HEAD_DIM,
+                    q_len: int = 1) -> int:
     out = ctypes.c_size_t()
     _check("lbsa_workspace_bytes",
-           lib().lbsa_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, P, ctypes.byref(out)))
+           lib().lbsa_workspace_bytes(batch, q_len, num_heads, num_kv_heads, head_dim, P, ctypes.byref(out)))
     return int(out.value)
 
 
 def static_workspace_bytes(batch: int, num_heads: int, num_kv_heads: int, num_splits: int,
-                           head_dim: int = HEAD_DIM) -> int:
+                           head_dim: int = HEAD_DIM, q_len: int = 1) -> int:
     out = ctypes.c_size_t()
     _check("lbsa_static_workspace_bytes",
-           lib().lbsa_static_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, num_splits,
+           lib().lbsa_static_workspace_bytes(batch, q_len, num_heads, num_kv_heads, head_dim, num_splits,
                                              ctypes.byref(out)))
     return int(out.value)
 
@@ -172,24 +175,31 @@ def _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table):
         assert q.dtype == torch.bfloat16 and k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16
     for t in (q, k_cache, v_cache, page_table, q_scale, k_scale, v_scale):
         assert t is None or t.is_contiguous()
-    B, Hq, D = q.shape
+    # q [B, Hq, D]: one query token per request; [B, q_len, Hq, D]: multi-token decode
+    if q.dim() == 3:
+        (B, Hq, D), QL = q.shape, 1
+    else:
+        B, QL, Hq, D = q.shape
     num_pages, page, Hkv, D2 = k_cache.shape
     assert page == PAGE_SIZE and D2 == D and tuple(v_cache.shape) == tuple(k_cache.shape)
     assert page_table.dtype == torch.int32 and page_table.shape[0] == B
+    if fp8:
+        assert q_scale.numel() == B * QL * Hq
     return [_ptr(q), _ptr(q_scale) if fp8 else None, _ptr(k_cache), _ptr(v_cache),
             _ptr(k_scale) if fp8 else None, _ptr(v_scale) if fp8 else None,
-            KV_FP8_E4M3 if fp8 else KV_BF16, _ptr(page_table), B, Hq, Hkv, D, page,
-            int(page_table.shape[1]), int(num_pages)], (B, Hq, Hkv, D)
+            KV_FP8_E4M3 if fp8 else KV_BF16, _ptr(page_table), B, QL, Hq, Hkv, D, page,
+            int(page_table.shape[1]), int(num_pages)], (B, QL, Hq, Hkv, D)
 
 
 def decode(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softmax_scale: float,
            q_scale=None, k_scale=None, v_scale=None, workspace=None, out=None):
-    """Split + combine with a task map from :func:`plan`; returns bf16 [B, Hq, D]."""
-    args, (B, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
+    """Split + combine with a task map from :func:`plan`; returns bf16 shaped like q."""
+    args, (B, QL, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
     if workspace is None:
-        workspace = torch.empty(workspace_bytes(B, Hq, Hkv, num_workgroups, D), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(workspace_bytes(B, Hq, Hkv, num_workgroups, D, QL), dtype=torch.uint8,
+                                device=q.device)
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
     _check("lbsa_decode", lib().lbsa_decode(*args, num_workgroups, float(softmax_scale), _ptr(task_map),
                                             task_map.numel(), _ptr(workspace), workspace.numel(), _ptr(out),
                                             _stream(q.device)))
@@ -199,9 +209,10 @@ def decode(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softm
 def decode_split(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softmax_scale: float,
                  q_scale=None, k_scale=None, v_scale=None, workspace=None):
     """Split kernel only; returns the workspace holding the partials."""
-    args, (B, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
+    args, (B, QL, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
     if workspace is None:
-        workspace = torch.empty(workspace_bytes(B, Hq, Hkv, num_workgroups, D), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(workspace_bytes(B, Hq, Hkv, num_workgroups, D, QL), dtype=torch.uint8,
+                                device=q.device)
     _check("lbsa_decode_split", lib().lbsa_decode_split(*args, num_workgroups, float(softmax_scale),
                                                         _ptr(task_map), task_map.numel(), _ptr(workspace),
                                                         workspace.numel(), _stream(q.device)))
@@ -209,11 +220,12 @@ def decode_split(q, k_cache, v_cache, page_table, task_map, num_workgroups: int,
 
 
 def decode_combine(batch: int, num_heads: int, num_kv_heads: int, num_workgroups: int, task_map, workspace,
-                   out=None, head_dim: int = HEAD_DIM):
-    """Combine kernel only; returns bf16 [B, Hq, D]."""
+                   out=None, head_dim: int = HEAD_DIM, q_len: int = 1):
+    """Combine kernel only; returns bf16 [B, Hq, D] (or [B, q_len, Hq, D] for q_len > 1)."""
     if out is None:
-        out = torch.empty((batch, num_heads, head_dim), dtype=torch.bfloat16, device=workspace.device)
-    _check("lbsa_decode_combine", lib().lbsa_decode_combine(batch, num_heads, num_kv_heads, head_dim,
+        shape = (batch, num_heads, head_dim) if q_len == 1 else (batch, q_len, num_heads, head_dim)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=workspace.device)
+    _check("lbsa_decode_combine", lib().lbsa_decode_combine(batch, q_len, num_heads, num_kv_heads, head_dim,
                                                             num_workgroups, _ptr(task_map), task_map.numel(),
                                                             _ptr(workspace), workspace.numel(), _ptr(out),
                                                             _stream(workspace.device)))
@@ -223,13 +235,13 @@ def decode_combine(batch: int, num_heads: int, num_kv_heads: int, num_workgroups
 def decode_static(q, k_cache, v_cache, page_table, seqlens, num_splits: int, softmax_scale: float,
                   q_scale=None, k_scale=None, v_scale=None, workspace=None, out=None):
     """Static split-KV baseline (fixed split count per request)."""
-    args, (B, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
+    args, (B, QL, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
     assert seqlens.dtype == torch.int32 and seqlens.is_contiguous()
     if workspace is None:
-        workspace = torch.empty(static_workspace_bytes(B, Hq, Hkv, num_splits, D), dtype=torch.uint8,
+        workspace = torch.empty(static_workspace_bytes(B, Hq, Hkv, num_splits, D, QL), dtype=torch.uint8,
                                 device=q.device)
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
     a = args
     _check("lbsa_decode_static", lib().lbsa_decode_static(*a[:8], _ptr(seqlens), *a[8:], num_splits,
                                                           float(softmax_scale), _ptr(workspace),
@@ -267,13 +279,15 @@ def read_task_map(task_map: torch.Tensor, batch: int, num_kv_heads: int, P: int)
 
 
 def read_partials(workspace: torch.Tensor, batch: int, num_heads: int, num_kv_heads: int, P: int,
-                  ndesc: int):
-    """(part_o [ndesc, 8, 128], part_lse [ndesc, 8]) as float32 numpy arrays."""
-    lay = workspace_layout(batch, num_heads, num_kv_heads, P)
+                  ndesc: int, q_len: int = 1):
+    """(part_o [ndesc, q_len*8, 128], part_lse [ndesc, q_len*8]) as float32 numpy arrays
+    (row 8 * query + head)."""
+    lay = workspace_layout(batch, num_heads, num_kv_heads, P, q_len=q_len)
     raw = workspace.detach().cpu().numpy()
-    lse = raw[lay["part_lse"]:lay["part_lse"] + 4 * GROUP * ndesc].view(np.float32).reshape(ndesc, GROUP)
-    o = raw[lay["part_o"]:lay["part_o"] + 4 * GROUP * HEAD_DIM * ndesc].view(np.float32)
-    return o.reshape(ndesc, GROUP, HEAD_DIM).copy(), lse.copy()
+    R = GROUP * q_len
+    lse = raw[lay["part_lse"]:lay["part_lse"] + 4 * R * ndesc].view(np.float32).reshape(ndesc, R)
+    o = raw[lay["part_o"]:lay["part_o"] + 4 * R * HEAD_DIM * ndesc].view(np.float32)
+    return o.reshape(ndesc, R, HEAD_DIM).copy(), lse.copy()
 
 
 def prologue(qkv, positions, slot_mapping, q_norm_weight, k_norm_weight, num_heads: int, num_kv_heads: int,

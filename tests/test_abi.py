@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 101
+    assert lbsa.lib().lbsa_version() == 200
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -56,6 +56,10 @@ def test_workspace_layout():
     assert w["part_o"] >= 4 * 8 * cap and w["part_o"] % 256 == 0
     assert w["total"] >= w["part_o"] + 4 * 8 * 128 * cap
     assert lbsa.static_workspace_bytes(64, 64, 8, 4) >= 4 * 8 * 129 * 64 * 8 * 4
+    # two query tokens per request: twice the partial rows
+    w2 = lbsa.workspace_layout(64, 64, 8, 768, q_len=2)
+    assert w2["part_o"] >= 4 * 16 * cap and w2["total"] >= w2["part_o"] + 4 * 16 * 128 * cap
+    assert lbsa.static_workspace_bytes(64, 64, 8, 4, q_len=2) >= 4 * 16 * 129 * 64 * 8 * 4
 
 
 def _plan_status(**kw):
@@ -81,13 +85,14 @@ def test_plan_rejects_bad_arguments_on_host():
 
 
 def _decode_status(**kw):
-    a = dict(q=16, qs=None, k=256, v=512, ks=None, vs=None, dt=0, pt=1024, B=4, Hq=8, Hkv=1, D=128, page=64,
-             mp=65, npages=100, P=32, scale=0.088, map=4096, mapb=1 << 20, ws=1 << 16, wsb=1 << 30, out=8192)
+    a = dict(q=16, qs=None, k=256, v=512, ks=None, vs=None, dt=0, pt=1024, B=4, QL=1, Hq=8, Hkv=1, D=128,
+             page=64, mp=65, npages=100, P=32, scale=0.088, map=4096, mapb=1 << 20, ws=1 << 16, wsb=1 << 30,
+             out=8192)
     a.update(kw)
     vp = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
     return lbsa.lib().lbsa_decode(vp(a["q"]), vp(a["qs"]), vp(a["k"]), vp(a["v"]), vp(a["ks"]), vp(a["vs"]),
-                                  a["dt"], vp(a["pt"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["page"], a["mp"],
-                                  a["npages"], a["P"], a["scale"], vp(a["map"]), a["mapb"], vp(a["ws"]),
+                                  a["dt"], vp(a["pt"]), a["B"], a["QL"], a["Hq"], a["Hkv"], a["D"], a["page"],
+                                  a["mp"], a["npages"], a["P"], a["scale"], vp(a["map"]), a["mapb"], vp(a["ws"]),
                                   a["wsb"], vp(a["out"]), None)
 
 
@@ -103,6 +108,9 @@ def test_decode_rejects_bad_arguments_on_host():
     assert _decode_status(npages=0) == lbsa.ERR_INVALID_ARGUMENT
     assert _decode_status(out=None) == lbsa.ERR_INVALID_ARGUMENT
     assert _decode_status(scale=float("nan")) == lbsa.ERR_INVALID_ARGUMENT
+    assert _decode_status(QL=0) == lbsa.ERR_INVALID_ARGUMENT
+    assert _decode_status(QL=3) == lbsa.ERR_UNSUPPORTED                   # at most 2 query tokens
+    assert _decode_status(QL=2, wsb=lbsa.workspace_bytes(4, 8, 1, 32)) == lbsa.ERR_INVALID_ARGUMENT  # sized for 1
 
 
 def _prologue_status(**kw):
