@@ -37,15 +37,17 @@ SPLIT_SRC = os.path.join(ROOT, "load_balanced_split_assign_amd", "csrc", "lbsa_a
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
 
 
-def alg_bytes(seqlens, Hq, Hkv, D, kv_dtype):
+def alg_bytes(seqlens, Hq, Hkv, D, kv_dtype, q_len=1):
     """Bytes the method must move: live K/V (+ scales), Q (+ scale), bf16 out,
-    page-table entries and lengths.  Partials are overhead, reported apart."""
+    page-table entries and lengths.  Partials are overhead, reported apart.
+    With q_len query tokens per request, Q and out scale with q_len; K/V is
+    read once for all of them."""
     e_kv, s_kv, e_q, s_q = (2, 0, 2, 0) if kv_dtype == "bf16" else (1, 8, 1, 4)
     B = len(seqlens)
     n_tiles = sum((L + 63) // 64 for L in seqlens)
     kv = sum(seqlens) * Hkv * (2 * D * e_kv + s_kv)
-    q = B * Hq * (D * e_q + s_q)
-    out = B * Hq * D * 2
+    q = B * q_len * Hq * (D * e_q + s_q)
+    out = B * q_len * Hq * D * 2
     meta = 4 * n_tiles + 4 * B
     return {"kv": kv, "q": q, "out": out, "meta": meta, "layer": kv + q + out + meta, "split": kv + q + meta}
 
@@ -69,10 +71,11 @@ class Path:
         from load_balanced_split_assign_amd import lbsa
         self.lbsa, self.b, self.P, self.F = lbsa, batch, P, F
         B, Hq, Hkv = batch["B"], batch["num_heads"], batch["num_kv_heads"]
+        self.q_len = batch.get("q_len", 1)
         dev = batch["q"].device
         self.tm = torch.empty(lbsa.task_map_bytes(B, Hkv, P), dtype=torch.uint8, device=dev)
-        self.ws = torch.empty(lbsa.workspace_bytes(B, Hq, Hkv, P), dtype=torch.uint8, device=dev)
-        self.out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(lbsa.workspace_bytes(B, Hq, Hkv, P, q_len=self.q_len), dtype=torch.uint8, device=dev)
+        self.out = torch.empty(tuple(batch["q"].shape), dtype=torch.bfloat16, device=dev)
 
     def assign(self):
         b = self.b
@@ -88,7 +91,7 @@ class Path:
     def combine(self):
         b = self.b
         self.lbsa.decode_combine(b["B"], b["num_heads"], b["num_kv_heads"], self.P, self.tm, self.ws,
-                                 out=self.out)
+                                 out=self.out, q_len=self.q_len)
 
 
 def make_flush(mode):
@@ -255,6 +258,35 @@ def table3(args):
         del b, path
         torch.cuda.empty_cache()
     print(json.dumps({"table3": rows, "P": P, "unit": "us", "flush": args.flush}), flush=True)
+
+
+def mtp_bench(args):
+    """Multi-token decode (2 query tokens per request: verifying one draft token
+    of a multi-token-prediction layer) against one-token decode on the same
+    lengths: layer time (split + combine, map reused) for each."""
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    from load_balanced_split_assign_amd import workload as wl
+    flush = make_flush(args.flush)
+    rows = []
+    for name in ("tp8_share", "skewed", "fp8"):
+        w = wl.WORKLOADS[name]
+        P = args.workgroups or w.num_workgroups or lbsa.default_workgroups(0, w.kv_dtype)
+        row = {"workload": name, "kv_dtype": w.kv_dtype, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads}
+        for ql in (1, 2):
+            b = wl.make_batch(name, tail="normal", device="cuda:0", q_len=ql)
+            sl = [int(x) for x in b["seqlens"].cpu()]
+            ab = alg_bytes(sl, b["num_heads"], b["num_kv_heads"], 128, w.kv_dtype, q_len=ql)
+            t = time_layer(Path(b, P), args.steps, args.warmup, flush)["mean"]
+            row[f"q{ql}_layer_us"] = round(t, 2)
+            row[f"q{ql}_GBps"] = round(ab["layer"] / t / 1e3, 1)
+            row["batch"] = b["B"]
+            del b
+            torch.cuda.empty_cache()
+        row["q2_over_q1"] = round(row["q2_layer_us"] / row["q1_layer_us"], 3)
+        rows.append(row)
+    print(json.dumps({"multi_token_decode": rows, "unit": "us", "flush": args.flush}), flush=True)
 
 
 def prologue_bytes(T, Hq, Hkv, fp8):
@@ -455,6 +487,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device copy first (reference for PMC byte counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (bounded sample)")
+    ap.add_argument("--mtp", action="store_true",
+                    help="instead of the headline line: 2-query-token decode vs 1-token decode")
     ap.add_argument("--prologue", action="store_true",
                     help="instead of the headline line: the fused QK-Norm/RoPE/KV-write prologue")
     ap.add_argument("--table3", action="store_true",
@@ -489,6 +523,9 @@ def main():
         return
     if args.prologue:
         prologue_bench(args)
+        return
+    if args.mtp:
+        mtp_bench(args)
         return
 
     name = args.workload
