@@ -289,6 +289,74 @@ def mtp_bench(args):
     print(json.dumps({"multi_token_decode": rows, "unit": "us", "flush": args.flush}), flush=True)
 
 
+# HPC-Ops latency (ms) on one H20 from the vLLM post's Table 4: context for the
+# same shapes here, not a target measured on this machine
+TABLE4_H20_MS = {"q512": 0.047, "q1ks2k": 0.406, "q2k": 0.530, "q4k": 2.002, "q8k": 7.883, "2q1ks4k": 1.835,
+                 "8q1s1k": 0.019, "16q1s2k": 0.054, "32q1s1k": 0.057, "64q1s4k": 0.299}
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def causal_flops(B, QL, L, Hq, D=128):
+    """2 matmuls x 2 flops per multiply-add over the (query, token) pairs the
+    causal rule keeps: query i of a request sees L - QL + i + 1 tokens."""
+    seen = sum(max(0, min(L, L - QL + i + 1)) for i in range(QL))
+    return 4 * B * Hq * D * seen
+
+
+def table4(args):
+    """The attention shapes of the vLLM post's Table 4 at 64 query / 8 KV heads,
+    bf16: prefill and extend through lbsa_prefill (TFLOP/s of the causal
+    work), decode through the load-balanced path (assign + split + combine)."""
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    from load_balanced_split_assign_amd import workload as wl
+    flush = make_flush(args.flush)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for name, (kind, B, QL, L) in wl.TABLE4.items():
+        b = wl.make_table4_batch(name, device="cuda:0")
+        torch.cuda.synchronize()
+        row = {"shape": name, "kind": kind, "batch": B, "q_len": QL, "kv_len": L,
+               "pages_h20_ms": TABLE4_H20_MS[name]}
+        if kind == "decode":
+            P = args.workgroups or lbsa.default_workgroups(0, "bf16")
+            path = Path(b, P)
+            t = time_layer(path, args.steps, args.warmup, flush, with_assign=True)["mean"]
+            ab = alg_bytes([L] * B, 64, 8, 128, "bf16")
+            row.update({"us": round(t, 2), "GBps": round(ab["layer"] / t / 1e3, 1),
+                        "pct_of_hbm_peak": round(100 * ab["layer"] / t / 1e3 / HBM_PEAK_GBS, 2)})
+            del path
+        else:
+            out = torch.empty_like(b["q"])
+
+            def run():
+                lbsa.prefill(b["q"], b["k_cache"], b["v_cache"], b["page_table"], b["seqlens"],
+                             b["softmax_scale"], out=out)
+            for i in range(args.warmup):
+                flush(i)
+                run()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for i in range(args.steps):
+                flush(i)
+                ev[i][0].record(stream)
+                run()
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            t = summarize([1000.0 * x.elapsed_time(y) for x, y in ev])["mean"]
+            fl = causal_flops(B, QL, L, 64)
+            row.update({"us": round(t, 2), "TFLOPs": round(fl / t / 1e6, 1),
+                        "pct_of_mfma_peak": round(100 * fl / t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2)})
+            del out
+        row["speedup_vs_pages_h20"] = round(row["pages_h20_ms"] * 1000.0 / row["us"], 2)
+        rows.append(row)
+        del b
+        torch.cuda.empty_cache()
+    print(json.dumps({"table4": rows, "unit": "us", "flush": args.flush}), flush=True)
+
+
 def prologue_bytes(T, Hq, Hkv, fp8):
     """Bytes the prologue must move: the fused QKV rows in, positions and slots,
     the two norm weights, Q out (+ scale) and the K / V cache rows (+ scales)."""
@@ -487,6 +555,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 256 MiB device copy first (reference for PMC byte counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (bounded sample)")
+    ap.add_argument("--table4", action="store_true",
+                    help="instead of the headline line: Table 4 prefill / extend / decode shapes (64/8 heads)")
     ap.add_argument("--mtp", action="store_true",
                     help="instead of the headline line: 2-query-token decode vs 1-token decode")
     ap.add_argument("--prologue", action="store_true",
@@ -526,6 +596,9 @@ def main():
         return
     if args.mtp:
         mtp_bench(args)
+        return
+    if args.table4:
+        table4(args)
         return
 
     name = args.workload

@@ -222,6 +222,34 @@ int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_ca
                        size_t workspace_bytes, void* out_d, void* stream);
 
 /*
+ * Prefill / extend attention over the paged cache (vLLM post, Table 4:
+ * prefill and extend shapes of the same backend).  The q_len new tokens of each
+ * request are the last q_len of its seqlens[b] cached tokens (already written,
+ * e.g. by lbsa_prologue); query i attends to tokens [0, seqlens[b] - q_len + i]
+ * (causal), the same rule as multi-token decode.
+ *   q_d            bf16 [batch][q_len][num_heads][128]
+ *   k/v_cache_d    bf16 [num_pages][64][num_kv_heads][128]; kv_dtype must be
+ *                  LBSA_KV_BF16 (LBSA_ERR_UNSUPPORTED for fp8)
+ *   page_table_d   int32 [batch][max_pages_per_seq]; seqlens_d int32 [batch]
+ *   out_d          bf16 [batch][q_len][num_heads][128]; a query that sees no
+ *                  token (seqlens[b] < q_len) gives a zero row; a length outside
+ *                  [0, max_pages_per_seq * 64] gives NaN rows for that request;
+ *                  a page id outside [0, num_pages) is never dereferenced and
+ *                  gives NaN rows for the queries that see that page
+ * One launch, no workspace, no task map: every workgroup owns one (request,
+ * KV head, block of query positions) and streams that KV head's pages itself;
+ * the grid starts with the blocks that see the most tiles.  Alignment: q_d and
+ * the caches 16 B, out_d 8 B, the int32 arrays 4 B (else
+ * LBSA_ERR_INVALID_ARGUMENT).  q_len >= 1, any size; head_dim 128, page 64,
+ * group 8 as for decode.
+ */
+int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, int32_t kv_dtype,
+                 const int32_t* page_table_d, const int32_t* seqlens_d, int32_t batch, int32_t q_len,
+                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                 int32_t max_pages_per_seq, int64_t num_pages, float softmax_scale, void* out_d,
+                 void* stream);
+
+/*
  * Fused attention prologue: from the fused QKV projection of num_tokens tokens
  * to the decode path's inputs, in one launch.  Source: vLLM post, section "A
  * fused attention prologue"; SGLang post, the attention prologue section

@@ -316,6 +316,30 @@ LBSA_API int lbsa_decode_static(const void* q_d, const float* q_scale_d, const v
     return hip_status(launch_combine(c.a, true, st));
 }
 
+LBSA_API int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, int32_t kv_dtype,
+                          const int32_t* page_table_d, const int32_t* seqlens_d, int32_t batch, int32_t q_len,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                          int32_t max_pages_per_seq, int64_t num_pages, float softmax_scale, void* out_d,
+                          void* stream) {
+    const int s = check_shape(batch, num_heads, num_kv_heads, head_dim, page_size);
+    if (s != LBSA_OK) return s;
+    if (kv_dtype == LBSA_KV_FP8_E4M3) return LBSA_ERR_UNSUPPORTED;
+    if (kv_dtype != LBSA_KV_BF16 || q_len <= 0) return LBSA_ERR_INVALID_ARGUMENT;
+    if ((long long)batch * q_len * num_heads >= (1LL << 31) / kHeadDim ||
+        (long long)max_pages_per_seq * kTile > INT_MAX / 2)
+        return LBSA_ERR_UNSUPPORTED;
+    if (!q_d || !k_cache_d || !v_cache_d || !page_table_d || !seqlens_d || !out_d || max_pages_per_seq <= 0 ||
+        num_pages <= 0 || !(softmax_scale == softmax_scale))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    // 16-byte Q and K/V loads, 8-byte output stores
+    if (!aligned(q_d, 16) || !aligned(k_cache_d, 16) || !aligned(v_cache_d, 16) || !aligned(out_d, 8) ||
+        !aligned(page_table_d, 4) || !aligned(seqlens_d, 4))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_prefill(q_d, k_cache_d, v_cache_d, page_table_d, seqlens_d, batch, q_len, num_heads,
+                                     num_kv_heads, max_pages_per_seq, num_pages, softmax_scale * kLog2eHost, out_d,
+                                     0, static_cast<hipStream_t>(stream)));
+}
+
 LBSA_API int lbsa_prologue(const void* qkv_d, const int32_t* positions_d, const int64_t* slot_mapping_d,
                            const float* q_norm_weight_d, const float* k_norm_weight_d, double rope_theta,
                            float eps, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,

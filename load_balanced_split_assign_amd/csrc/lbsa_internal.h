@@ -91,6 +91,9 @@ hipError_t launch_split(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream);
 hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu);
+hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
+                          const int32_t* seqlens, int B, int QL, int Hq, int Hkv, int max_pages,
+                          int64_t num_pages, float scale_log2, void* out, int cb, hipStream_t stream);
 hipError_t launch_prologue(const uint16_t* qkv, const int32_t* positions, const int64_t* slots,
                            const float* qw, const float* kw, double theta, float eps, int T, int Hq,
                            int Hkv, bool fp8, void* q_out, float* q_scale, void* k_cache, void* v_cache,

@@ -1,0 +1,300 @@
+// Prefill / extend attention over the paged KV cache for gfx950 (bf16).
+//
+// Method: the vLLM post's Table 4 ("Attention latency vs FlashAttention,
+// Triton and FlashInfer") measures the same attention backend on prefill and
+// extend shapes; the SGLang post's "Attention" section frames decode and
+// prefill as one backend over the paged store.  Prefill and extend are causal
+// attention of a request's q_len new tokens (the last q_len of its L cached
+// tokens, written into the cache beforehand) over the cache: query i sees
+// tokens [0, L - q_len + i].
+//
+// gfx950 mapping.  The work is a dense contraction, so it is built around the
+// MFMA tiles the decode kernel already uses, with K/V reuse across many query
+// columns:
+//   * A workgroup (4 wave64) owns one KV head of one request and a block of
+//     query positions; every query column is a (position, head of the group)
+//     pair, 16 columns per MFMA block, CB blocks per wave (CB = 1, 2, 4, i.e.
+//     2, 4 or 8 positions per wave).  Q stays in registers for the whole run.
+//   * The 64-token K/V tiles (one page of the KV head) stream through a
+//     3-stage LDS ring shared by the 4 waves: each wave issues the async
+//     global->LDS loads of 16 of the 64 rows, waits for them with its own
+//     vmcnt, and one workgroup barrier per tile publishes the tile and frees
+//     the stage written next.
+//   * Per 16-token sub-tile: S^T = K Q^T (MFMA 16x16x32 bf16, K from LDS is
+//     read once per wave for all CB blocks), a masked online softmax per
+//     column in the exp2 domain with a lazy running max, then O^T += V^T P^T
+//     (MFMA 16x16x16 bf16, V^T through ds_read_b64_tr_b16, P straight from the
+//     S^T accumulators), again one V read for all CB blocks.
+//   * Causality: column limits mask the diagonal tiles; a wave skips the tiles
+//     past its own last position; the grid starts with the query blocks that
+//     see the most tiles (longest first), and the blocks of one (request, KV
+//     head) share an XCD whenever batch * Hkv is a multiple of 8, so their K/V
+//     reuse stays in one L2.
+#include "lbsa_device.h"
+
+namespace lbsa {
+namespace {
+
+using namespace dev;
+
+constexpr int kPfStages = 3;
+constexpr int kPfRow = 256;                         // bytes of one bf16 K/V row
+constexpr int kPfSlice = 16 * kPfRow;               // one wave's 16 rows of a tile
+constexpr int kPfHalf = 64 * kPfRow;                // K (or V) of one 64-token tile
+constexpr int kPfStageBytes = 2 * kPfHalf;          // 32 KiB: K then V
+constexpr int kPfLoads = 8;                         // ring loads per lane per tile (4 K + 4 V)
+constexpr float kPfSlack = 8.0f;                    // log2 headroom of the lazy running max
+static_assert(kPfStages * kPfStageBytes <= 160 * 1024, "LDS");
+static_assert((kPfStages - 2) * kPfLoads < 64, "vmcnt range");
+
+struct PrefillArgs {
+    const uint16_t* q;           // [B][QL][Hq][128]
+    const uint16_t* k_cache;     // [pages][64][Hkv][128]
+    const uint16_t* v_cache;
+    const int32_t* page_table;   // [B][max_pages]
+    const int32_t* seqlens;      // [B]
+    uint16_t* out;               // [B][QL][Hq][128]
+    int64_t num_pages;
+    int32_t B, QL, Hq, Hkv, max_pages;
+    int32_t qblocks;             // query blocks per (request, KV head)
+    float scale_log2;            // softmax_scale * log2(e)
+};
+
+__device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+template <int CB>
+__global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) char ring_mem[kPfStages * kPfStageBytes];
+    lds_char* const ring = (lds_char*)ring_mem;         // stage u at u * kPfStageBytes
+    constexpr int kPosWave = 2 * CB, kPosBlock = kWaves * kPosWave;
+
+    // heaviest query blocks first; consecutive workgroups take different
+    // (request, KV head) pairs of the same query block
+    const int nbh = a.B * a.Hkv;
+    const int qb = a.qblocks - 1 - (int)(blockIdx.x / (unsigned)nbh);
+    const int bh = (int)(blockIdx.x % (unsigned)nbh);
+    const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+
+    int L = uniform_ptr<int32_t>(a.seqlens)[b];
+    const bool len_ok = L >= 0 && L <= a.max_pages * kTile;
+    if (!len_ok) L = 0;
+    const int off = L - a.QL;                             // query i sees tokens < off + i + 1
+
+    // columns of this lane: position p0 + 2 cb + r / 8, head r % 8
+    const int p0 = qb * kPosBlock + w * kPosWave;
+    int pos[CB], lim[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        pos[cb] = p0 + 2 * cb + (r >> 3);
+        lim[cb] = pos[cb] < a.QL ? clampi(off + pos[cb] + 1, 0, L) : 0;
+    }
+    const int pw_last = min(p0 + kPosWave, a.QL) - 1;     // this wave's last live position
+    const int lim_wave = pw_last >= p0 ? clampi(off + pw_last + 1, 0, L) : 0;
+    const int pb_last = min(qb * kPosBlock + kPosBlock, a.QL) - 1;
+    const int lim_blk = pb_last >= qb * kPosBlock ? clampi(off + pb_last + 1, 0, L) : 0;
+    const int ntiles = (lim_blk + kTile - 1) / kTile;
+
+    f32x4 acc[CB][8];
+    float m[CB], l[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[cb] = kNegInf;
+        l[cb] = 0.f;
+    }
+    bool bad = !len_ok;
+
+    if (ntiles > 0) {
+        // Q of every column of this lane (B operand: 8 dims per k-step), then
+        // wait for it once before the ring starts
+        uint4 q[CB][4];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const bool live = pos[cb] < a.QL;
+            const int p = live ? pos[cb] : 0;
+            const uint4* qp = reinterpret_cast<const uint4*>(
+                a.q + ((size_t)(b * a.QL + p) * a.Hq + (size_t)h * kGroup + (r & 7)) * kHeadDim);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) q[cb][ks] = live ? qp[g + 4 * ks] : make_uint4(0, 0, 0, 0);
+        }
+        wait_vmcnt<0>();
+
+        // this lane's 4 K and 4 V chunks of every tile: rows 16 w + 4 s + lane / 16,
+        // chunk lane % 16, XOR-swizzled by the row inside the wave's 16
+        uint32_t live_off[4], dead_off[4];
+        int lrow[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            lrow[s] = 4 * s + (lane >> 4);
+            const uint32_t chunk = 16u * (uint32_t)((lane & 15) ^ lrow[s]);
+            live_off[s] = (uint32_t)(16 * w + lrow[s]) * (uint32_t)a.Hkv * kPfRow + chunk;
+            dead_off[s] = chunk;                          // row 0 of the page: always live
+        }
+        const auto* pt = uniform_ptr<int32_t>(a.page_table) + (size_t)b * a.max_pages;
+        auto issue = [&](int t, lds_char* st) {
+            int64_t page = pt[t];
+            if (page < 0 || page >= a.num_pages) {
+                bad = true;
+                page = 0;
+            }
+            const size_t pbase = ((size_t)page * kTile * a.Hkv + h) * kPfRow;
+            const char* kb = reinterpret_cast<const char*>(a.k_cache) + pbase;
+            const char* vb = reinterpret_cast<const char*>(a.v_cache) + pbase;
+            const int tok0 = kTile * t + 16 * w;
+            const bool full = tok0 + 16 <= L;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t o = (full || tok0 + lrow[s] < L) ? live_off[s] : dead_off[s];
+                dma16(kb + o, st + w * kPfSlice + 1024 * s);
+                dma16(vb + o, st + kPfHalf + w * kPfSlice + 1024 * s);
+            }
+        };
+        for (int u = 0; u < kPfStages - 1; ++u) issue(min(u, ntiles - 1), ring + u * kPfStageBytes);
+
+        // every tile issues the same number of loads (past the end the last tile
+        // is loaded again into a stage nobody reads), so one wait count fits all
+        int u = 0;                                                  // stage of tile k
+        for (int k = 0; k < ntiles; ++k) {
+            {
+                wait_vmcnt<(kPfStages - 2) * kPfLoads>();             // this wave's rows of tile k
+                lds_barrier();                                      // everyone's rows; stage of k-1 free
+                const int un = u == 0 ? kPfStages - 1 : u - 1;      // = (k + kPfStages - 1) % kPfStages
+                issue(min(k + kPfStages - 1, ntiles - 1), ring + un * kPfStageBytes);
+                const lds_char* st = ring + u * kPfStageBytes;
+                u = u == kPfStages - 1 ? 0 : u + 1;
+                if (kTile * k >= lim_wave) continue;                // nothing of it is visible here
+#pragma unroll 1
+                for (int sub = 0; sub < 4; ++sub) {
+                    // ---- K (A operand) and V^T reads of 16 tokens, shared by all blocks
+                    const int row = 16 * sub + r;
+                    uint32_t ka[4], vaddr[8];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) ka[ks] = lds_addr(st + row * kPfRow + 16 * ((g + 4 * ks) ^ r));
+                    const int vrow = 4 * g + (r >> 2);
+                    const uint32_t vr = lds_addr(st + kPfHalf + (16 * sub + vrow) * kPfRow + 8 * (r & 1));
+#pragma unroll
+                    for (int db = 0; db < 8; ++db)
+                        vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ vrow);
+                    uint4 kk[4];
+                    s16x4 va[8];
+                    lds_read_tile_bf16(kk, va, ka, vaddr);
+
+                    // ---- S^T = K Q^T per block, masked scores in the log2 domain
+                    const int tok = kTile * k + 16 * sub + 4 * g;       // token of score row i: tok + i
+                    float sc[CB][4], lmax[CB];
+                    bool need = false;
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+                        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
+                        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[1]), as_bf16x8(q[cb][1]), sb, 0, 0, 0);
+                        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
+                        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[3]), as_bf16x8(q[cb][3]), sb, 0, 0, 0);
+                        const f32x4 s = sa + sb;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sc[cb][i] = (tok + i < lim[cb]) ? s[i] * a.scale_log2 : kNegInf;
+                        lmax[cb] = fmaxf(fmaxf(sc[cb][0], sc[cb][1]), fmaxf(sc[cb][2], sc[cb][3]));
+                        need |= lmax[cb] > m[cb] + kPfSlack;
+                    }
+                    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                        // a score above a column's reference: new reference = max over
+                        // the column's 16 tokens (0 rescale for a column still fully masked)
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb) {
+                            float mt = fmaxf(lmax[cb], __shfl_xor(lmax[cb], 16, 64));
+                            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                            const float m_new = fmaxf(m[cb], mt);
+                            const float alpha = m[cb] == kNegInf ? 0.f : exp2_fast(m[cb] - m_new);
+                            l[cb] *= alpha;
+#pragma unroll
+                            for (int db = 0; db < 8; ++db) acc[cb][db] *= alpha;
+                            m[cb] = m_new;
+                        }
+                    }
+                    // ---- P and O^T += V^T P^T
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const float mref = m[cb] == kNegInf ? 0.f : m[cb];
+                        float p[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            p[i] = exp2_fast(sc[cb][i] - mref);
+                            l[cb] += p[i];
+                        }
+                        const s16x4 pb = __builtin_bit_cast(
+                            s16x4, make_uint2(bf16x2_bits(p[0], p[1]), bf16x2_bits(p[2], p[3])));
+#pragma unroll
+                        for (int db = 0; db < 8; ++db)
+                            acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], pb, acc[cb][db], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
+    }
+
+    // ---- normalise and store: lane (g, r) holds dims 16 db + 4 g .. + 3 of column r
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        float lt = l[cb];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        if (pos[cb] >= a.QL) continue;
+        float inv = lt > 0.f ? 1.f / lt : 0.f;            // a query that sees nothing: zeros
+        if (bad) inv = __builtin_nanf("");
+        uint16_t* o = a.out + ((size_t)(b * a.QL + pos[cb]) * a.Hq + (size_t)h * kGroup + (r & 7)) * kHeadDim + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const f32x4 v = acc[cb][db] * inv;
+            *reinterpret_cast<uint2*>(o + 16 * db) = make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
+        }
+    }
+}
+
+template <int CB>
+hipError_t launch_cb(PrefillArgs a, hipStream_t stream) {
+    constexpr int kPosBlock = kWaves * 2 * CB;
+    a.qblocks = (a.QL + kPosBlock - 1) / kPosBlock;
+    const long long grid = (long long)a.qblocks * a.B * a.Hkv;
+    hipLaunchKernelGGL((prefill_kernel<CB>), dim3((unsigned)grid), dim3(kSplitThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
+                          const int32_t* seqlens, int B, int QL, int Hq, int Hkv, int max_pages,
+                          int64_t num_pages, float scale_log2, void* out, int cb, hipStream_t stream) {
+    PrefillArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint16_t*>(k_cache);
+    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.page_table = page_table;
+    a.seqlens = seqlens;
+    a.out = static_cast<uint16_t*>(out);
+    a.num_pages = num_pages;
+    a.B = B;
+    a.QL = QL;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.max_pages = max_pages;
+    a.qblocks = 0;
+    a.scale_log2 = scale_log2;
+    if (cb <= 0) {
+        // the most query columns per wave (K/V reuse) that still leaves two
+        // workgroups per compute unit
+        const long long bh = (long long)B * Hkv;
+        cb = 4;
+        while (cb > 1 && bh * ((QL + kWaves * 2 * cb - 1) / (kWaves * 2 * cb)) < 512) cb /= 2;
+    }
+    switch (cb) {
+        case 4: return launch_cb<4>(a, stream);
+        case 2: return launch_cb<2>(a, stream);
+        default: return launch_cb<1>(a, stream);
+    }
+}
+
+}  // namespace lbsa

@@ -68,12 +68,13 @@ def lib() -> ctypes.CDLL:
         L.lbsa_decode_combine.argtypes = [i32, i32, i32, i32, i32, i32, vp, sz, vp, sz, vp, vp]
         L.lbsa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, i64, i32, f32, vp, sz, vp, vp]
+        L.lbsa_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32, vp, vp]
         L.lbsa_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, f32, i32, i32, i32, i32, i32, i32,
                                     vp, vp, vp, vp, vp, vp, i64, vp]
         for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes", "lbsa_prologue",
                    "lbsa_workspace_layout_get", "lbsa_workspace_bytes", "lbsa_static_workspace_bytes",
                    "lbsa_plan", "lbsa_decode", "lbsa_decode_split", "lbsa_decode_combine",
-                   "lbsa_decode_static"):
+                   "lbsa_decode_static", "lbsa_prefill"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -246,6 +247,28 @@ def decode_static(q, k_cache, v_cache, page_table, seqlens, num_splits: int, sof
     _check("lbsa_decode_static", lib().lbsa_decode_static(*a[:8], _ptr(seqlens), *a[8:], num_splits,
                                                           float(softmax_scale), _ptr(workspace),
                                                           workspace.numel(), _ptr(out), _stream(q.device)))
+    return out
+
+
+def prefill(q, k_cache, v_cache, page_table, seqlens, softmax_scale: float, out=None):
+    """Prefill / extend attention: q bf16 [B, q_len, Hq, D] are the last q_len tokens of each
+    request's seqlens[b] cached tokens (causal); returns bf16 [B, q_len, Hq, D]."""
+    assert q.dtype == torch.bfloat16 and k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16
+    for t in (q, k_cache, v_cache, page_table, seqlens):
+        assert t.is_contiguous()
+    if q.dim() == 3:                                   # [B, Hq, D]: one new token per request
+        (B, Hq, D), QL = q.shape, 1
+    else:
+        B, QL, Hq, D = q.shape
+    num_pages, page, Hkv, D2 = k_cache.shape
+    assert page == PAGE_SIZE and D2 == D and tuple(v_cache.shape) == tuple(k_cache.shape)
+    assert page_table.dtype == torch.int32 and page_table.shape[0] == B
+    assert seqlens.dtype == torch.int32 and seqlens.numel() == B
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
+    _check("lbsa_prefill", lib().lbsa_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), KV_BF16, _ptr(page_table),
+                                              _ptr(seqlens), B, QL, Hq, Hkv, D, page, int(page_table.shape[1]),
+                                              int(num_pages), float(softmax_scale), _ptr(out), _stream(q.device)))
     return out
 
 

@@ -221,6 +221,32 @@ def _poison_tails(sl, pt, k_cache, v_cache, k_scale, v_scale):
 # inputs of the fused attention prologue (random draws only)
 # ---------------------------------------------------------------------------
 
+# The attention shapes of the vLLM post's Table 4 ("Attention latency (ms) vs
+# FlashAttention, Triton and FlashInfer"), read as (batch, q_len new tokens per
+# request, L cached tokens per request including the new ones): "q512" is a
+# 512-token prefill, "q1ks2k" 1K new tokens over a 2K sequence, "8q1s1k" 8
+# decode requests at 1K.  Full Hy3 attention: 64 query / 8 KV heads, bf16.
+TABLE4 = {
+    "q512": ("prefill", 1, 512, 512),
+    "q1ks2k": ("extend", 1, 1024, 2048),
+    "q2k": ("prefill", 1, 2048, 2048),
+    "q4k": ("prefill", 1, 4096, 4096),
+    "q8k": ("prefill", 1, 8192, 8192),
+    "2q1ks4k": ("extend", 2, 1024, 4096),
+    "8q1s1k": ("decode", 8, 1, 1024),
+    "16q1s2k": ("decode", 16, 1, 2048),
+    "32q1s1k": ("decode", 32, 1, 1024),
+    "64q1s4k": ("decode", 64, 1, 4096),
+}
+
+
+def make_table4_batch(name: str, tail: str = "normal", device="cpu", seed: int = 80) -> dict:
+    """Seeded batch of one Table 4 shape (q [B, q_len, Hq, D] for prefill / extend)."""
+    kind, B, QL, L = TABLE4[name]
+    return make_batch(seqlens=[L] * B, num_heads=64, num_kv_heads=8, kv_dtype="bf16", seed=seed, tail=tail,
+                      device=device, q_len=None if kind == "decode" else QL)
+
+
 PROLOGUE_WORKLOADS = {
     # decode step of the tp8_share batch: one new token per request
     "decode_8_1": dict(tokens=32, num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=31),

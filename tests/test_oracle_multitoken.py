@@ -140,3 +140,31 @@ def test_rows_sample_matches_full(oracle_mod):
     for k, (b, j) in enumerate(rows):
         np.testing.assert_array_equal(o[k], out[b, j // 16, j % 16])
         assert l[k] == lse[b, j // 16, j % 16]
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_prefill_and_extend_match_masked_sdpa(oracle_mod, kv_dtype):
+    """Prefill (q_len = L: plain causal attention) and extend (q_len < L) are
+    the same rule at larger q_len."""
+    for seed, sl, ql in ((48, [130, 130], 130), (49, [300, 77], 77), (50, [64, 200], 64)):
+        batch = wl.make_batch(seqlens=sl, num_heads=16, num_kv_heads=2, kv_dtype=kv_dtype, seed=seed, q_len=ql,
+                              tail="nan")
+        out, lse = oracle_mod.attention(batch)
+        ref_out, ref_lse = masked_sdpa_reference(batch)
+        np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
+        fin = np.isfinite(ref_lse)
+        np.testing.assert_array_equal(np.isfinite(lse), fin)
+        np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-13, atol=1e-12)
+
+
+def test_prefill_is_torch_causal_attention(oracle_mod):
+    """q_len = L: the first query sees only token 0, the mask is torch's own
+    is_causal (top-left aligned, which coincides with M1 when q_len = L)."""
+    batch = wl.make_batch(seqlens=[96], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=51, q_len=96)
+    out, _ = oracle_mod.attention(batch)
+    k, v = gather_dense(batch, 0)
+    q = q_dense_multi(batch, 0).permute(1, 0, 2)                        # [Hq, 96, D]
+    ref = F.scaled_dot_product_attention(q, k.repeat_interleave(8, 0), v.repeat_interleave(8, 0), is_causal=True,
+                                         scale=batch["softmax_scale"])
+    np.testing.assert_allclose(out[0], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(out[0, 0], np.repeat(v[:, 0, :].numpy(), 8, axis=0))
