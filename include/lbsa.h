@@ -240,8 +240,8 @@ int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_ca
  * KV head, block of query positions) and streams that KV head's pages itself;
  * the grid starts with the blocks that see the most tiles.  Alignment: q_d and
  * the caches 16 B, out_d 8 B, the int32 arrays 4 B (else
- * LBSA_ERR_INVALID_ARGUMENT).  q_len >= 1, any size; head_dim 128, page 64,
- * group 8 as for decode.
+ * LBSA_ERR_INVALID_ARGUMENT, as for softmax_scale <= 0 or not finite).
+ * q_len >= 1, any size; head_dim 128, page 64, group 8 as for decode.
  */
 int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, int32_t kv_dtype,
                  const int32_t* page_table_d, const int32_t* seqlens_d, int32_t batch, int32_t q_len,

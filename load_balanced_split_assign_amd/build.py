@@ -30,9 +30,15 @@ CFLAGS = [
 ]
 
 
+# per-source flags: the prefill kernel keeps its MFMA accumulators in VGPRs
+# (the softmax rescale touches them with VALU instructions, which cannot read
+# AGPRs; without this the compiler copies every accumulator through AGPRs)
+EXTRA = {"lbsa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -2,6 +2,7 @@
 // Every check runs before anything is enqueued; the library never allocates,
 // frees or synchronises.
 #include <limits.h>
+#include <math.h>
 
 #include "lbsa_internal.h"
 
@@ -329,7 +330,7 @@ LBSA_API int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_
         (long long)max_pages_per_seq * kTile > INT_MAX / 2)
         return LBSA_ERR_UNSUPPORTED;
     if (!q_d || !k_cache_d || !v_cache_d || !page_table_d || !seqlens_d || !out_d || max_pages_per_seq <= 0 ||
-        num_pages <= 0 || !(softmax_scale == softmax_scale))
+        num_pages <= 0 || !(softmax_scale > 0.f) || !(softmax_scale < INFINITY))
         return LBSA_ERR_INVALID_ARGUMENT;
     // 16-byte Q and K/V loads, 8-byte output stores
     if (!aligned(q_d, 16) || !aligned(k_cache_d, 16) || !aligned(v_cache_d, 16) || !aligned(out_d, 8) ||

@@ -32,6 +32,14 @@ __device__ inline void lds_store16(lds_char* p, uint4 v) {
 }
 __device__ inline uint32_t lds_addr(const lds_char* p) { return (uint32_t)(size_t)p; }
 
+// Two floats -> two bf16 (round to nearest even) in one dword through one
+// packed convert (v_cvt_pk_bf16_f32), low half first.
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t bf16x2_pack(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){lo, hi}, bf16x2_v));
+}
+
 __device__ inline uint32_t bf16x2_bits(float lo, float hi) {
     __bf16 a = (__bf16)lo, b = (__bf16)hi;          // round to nearest even
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);

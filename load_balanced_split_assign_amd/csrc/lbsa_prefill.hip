@@ -13,18 +13,27 @@
 // columns:
 //   * A workgroup (4 wave64) owns one KV head of one request and a block of
 //     query positions; every query column is a (position, head of the group)
-//     pair, 16 columns per MFMA block, CB blocks per wave (CB = 1, 2, 4, i.e.
-//     2, 4 or 8 positions per wave).  Q stays in registers for the whole run.
+//     pair, 16 columns per MFMA block, CB blocks per wave (CB = 1 or 2, i.e.
+//     2 or 4 positions per wave).  Q stays in registers for the whole run.
 //   * The 64-token K/V tiles (one page of the KV head) stream through a
-//     3-stage LDS ring shared by the 4 waves: each wave issues the async
-//     global->LDS loads of 16 of the 64 rows, waits for them with its own
-//     vmcnt, and one workgroup barrier per tile publishes the tile and frees
-//     the stage written next.
-//   * Per 16-token sub-tile: S^T = K Q^T (MFMA 16x16x32 bf16, K from LDS is
-//     read once per wave for all CB blocks), a masked online softmax per
-//     column in the exp2 domain with a lazy running max, then O^T += V^T P^T
-//     (MFMA 16x16x16 bf16, V^T through ds_read_b64_tr_b16, P straight from the
-//     S^T accumulators), again one V read for all CB blocks.
+//     2-stage LDS ring (64 KiB) shared by the 4 waves: each wave issues the
+//     async global->LDS loads of 16 of the 64 rows, waits for them with its
+//     own vmcnt, and one workgroup barrier per tile publishes the tile and
+//     frees the stage written next.  At 64 KiB of LDS and under 256 VGPRs two
+//     workgroups share a compute unit, so one's softmax (VALU) overlaps the
+//     other's MFMAs; that overlap outweighs the larger K/V reuse of 4 blocks
+//     per wave or a deeper ring, which both leave one wave per SIMD.
+//   * Per 32-token half-tile: S^T = K Q^T (MFMA 16x16x32 bf16, one chain of 4
+//     per 16 tokens and block; K is read from LDS once per wave for all CB
+//     blocks), a masked online softmax per column in the exp2 domain with a
+//     lazy running max, then O^T += V^T P^T with MFMA 16x16x32 bf16 over the
+//     32 tokens (V^T through ds_read_b64_tr_b16, P straight from the S^T
+//     accumulators).  Tiles below every column's limit skip the mask: the
+//     softmax scale folds into one fma before each exp2.
+//   * Built with the MFMA accumulators in VGPRs (-amdgpu-mfma-vgpr-form): the
+//     rescale of the online softmax multiplies them with VALU instructions,
+//     which cannot address AGPRs, and the AGPR form copied every accumulator
+//     on every step.
 //   * Causality: column limits mask the diagonal tiles; a wave skips the tiles
 //     past its own last position; the grid starts with the query blocks that
 //     see the most tiles (longest first), and the blocks of one (request, KV
@@ -37,14 +46,14 @@ namespace {
 
 using namespace dev;
 
-constexpr int kPfStages = 3;
+constexpr int kPfStages = 2;
 constexpr int kPfRow = 256;                         // bytes of one bf16 K/V row
 constexpr int kPfSlice = 16 * kPfRow;               // one wave's 16 rows of a tile
 constexpr int kPfHalf = 64 * kPfRow;                // K (or V) of one 64-token tile
 constexpr int kPfStageBytes = 2 * kPfHalf;          // 32 KiB: K then V
 constexpr int kPfLoads = 8;                         // ring loads per lane per tile (4 K + 4 V)
 constexpr float kPfSlack = 8.0f;                    // log2 headroom of the lazy running max
-static_assert(kPfStages * kPfStageBytes <= 160 * 1024, "LDS");
+static_assert(kPfStages * kPfStageBytes <= 80 * 1024, "two workgroups per compute unit");
 static_assert((kPfStages - 2) * kPfLoads < 64, "vmcnt range");
 
 struct PrefillArgs {
@@ -90,6 +99,9 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
         pos[cb] = p0 + 2 * cb + (r >> 3);
         lim[cb] = pos[cb] < a.QL ? clampi(off + pos[cb] + 1, 0, L) : 0;
     }
+    // smallest limit over this wave's live columns (its first position): tokens
+    // below it are visible to every live column
+    const int lim_lo = p0 < a.QL ? clampi(off + p0 + 1, 0, L) : 0;
     const int pw_last = min(p0 + kPosWave, a.QL) - 1;     // this wave's last live position
     const int lim_wave = pw_last >= p0 ? clampi(off + pw_last + 1, 0, L) : 0;
     const int pb_last = min(qb * kPosBlock + kPosBlock, a.QL) - 1;
@@ -167,41 +179,76 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
                 u = u == kPfStages - 1 ? 0 : u + 1;
                 if (kTile * k >= lim_wave) continue;                // nothing of it is visible here
 #pragma unroll 1
-                for (int sub = 0; sub < 4; ++sub) {
-                    // ---- K (A operand) and V^T reads of 16 tokens, shared by all blocks
-                    const int row = 16 * sub + r;
-                    uint32_t ka[4], vaddr[8];
+                for (int half = 0; half < 2; ++half) {
+                    // ---- K (A operand of S^T) and V^T reads of 32 tokens, two
+                    // 16-token sub-tiles, shared by all CB blocks
+                    uint4 kk[2][4];
+                    s16x4 va[2][8];
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) ka[ks] = lds_addr(st + row * kPfRow + 16 * ((g + 4 * ks) ^ r));
-                    const int vrow = 4 * g + (r >> 2);
-                    const uint32_t vr = lds_addr(st + kPfHalf + (16 * sub + vrow) * kPfRow + 8 * (r & 1));
+                    for (int sub = 0; sub < 2; ++sub) {
+                        const int row = 32 * half + 16 * sub + r;
+                        uint32_t ka[4], vaddr[8];
 #pragma unroll
-                    for (int db = 0; db < 8; ++db)
-                        vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ vrow);
-                    uint4 kk[4];
-                    s16x4 va[8];
-                    lds_read_tile_bf16(kk, va, ka, vaddr);
+                        for (int ks = 0; ks < 4; ++ks) ka[ks] = lds_addr(st + row * kPfRow + 16 * ((g + 4 * ks) ^ r));
+                        const int vrow = 4 * g + (r >> 2);
+                        const uint32_t vr =
+                            lds_addr(st + kPfHalf + (32 * half + 16 * sub + vrow) * kPfRow + 8 * (r & 1));
+#pragma unroll
+                        for (int db = 0; db < 8; ++db)
+                            vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ vrow);
+                        lds_read_tile_bf16(kk[sub], va[sub], ka, vaddr);
+                    }
 
-                    // ---- S^T = K Q^T per block, masked scores in the log2 domain
-                    const int tok = kTile * k + 16 * sub + 4 * g;       // token of score row i: tok + i
-                    float sc[CB][4], lmax[CB];
-                    bool need = false;
+                    // ---- S^T = K Q^T: s[cb][sub][i] is token 32 half + 16 sub + 4 g + i
+                    f32x4 s[CB][2];
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
-                        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-                        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
-                        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[1]), as_bf16x8(q[cb][1]), sb, 0, 0, 0);
-                        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
-                        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[3]), as_bf16x8(q[cb][3]), sb, 0, 0, 0);
-                        const f32x4 s = sa + sb;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) sc[cb][i] = (tok + i < lim[cb]) ? s[i] * a.scale_log2 : kNegInf;
-                        lmax[cb] = fmaxf(fmaxf(sc[cb][0], sc[cb][1]), fmaxf(sc[cb][2], sc[cb][3]));
-                        need |= lmax[cb] > m[cb] + kPfSlack;
+                        for (int sub = 0; sub < 2; ++sub) {
+                            f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
+                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][1]), as_bf16x8(q[cb][1]), sa, 0, 0, 0);
+                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
+                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][3]), as_bf16x8(q[cb][3]), sa, 0, 0, 0);
+                            s[cb][sub] = sa;
+                        }
+                    }
+
+                    // ---- online softmax over the 8 scores of this lane per block.
+                    // Tiles below every live column's limit need no mask: the scale
+                    // folds into one fma before the exp2, and the block maximum is
+                    // the scale times the raw maximum (the scale is positive).
+                    const int tok = kTile * k + 32 * half + 4 * g;
+                    const bool masked = kTile * k + 32 * half + 31 >= lim_lo;     // uniform
+                    float lmax[CB];
+                    bool need = false;
+                    if (masked) {
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb) {
+                            float mx = kNegInf;
+#pragma unroll
+                            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const float x = (tok + 16 * sub + i < lim[cb]) ? s[cb][sub][i] * a.scale_log2 : kNegInf;
+                                    s[cb][sub][i] = x;
+                                    mx = fmaxf(mx, x);
+                                }
+                            lmax[cb] = mx;
+                            need |= mx > m[cb] + kPfSlack;
+                        }
+                    } else {
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb) {
+                            const float mx = fmaxf(fmaxf(fmaxf(s[cb][0][0], s[cb][0][1]), fmaxf(s[cb][0][2], s[cb][0][3])),
+                                                   fmaxf(fmaxf(s[cb][1][0], s[cb][1][1]), fmaxf(s[cb][1][2], s[cb][1][3])));
+                            lmax[cb] = mx * a.scale_log2;
+                            need |= lmax[cb] > m[cb] + kPfSlack;
+                        }
                     }
                     if (__builtin_amdgcn_ballot_w64(need) != 0) {
                         // a score above a column's reference: new reference = max over
-                        // the column's 16 tokens (0 rescale for a column still fully masked)
+                        // the column's 32 tokens (0 rescale for a column still fully masked)
 #pragma unroll
                         for (int cb = 0; cb < CB; ++cb) {
                             float mt = fmaxf(lmax[cb], __shfl_xor(lmax[cb], 16, 64));
@@ -214,21 +261,34 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
                             m[cb] = m_new;
                         }
                     }
-                    // ---- P and O^T += V^T P^T
+
+                    // ---- P and O^T += V^T P^T with MFMA 16x16x32: k = the 32 tokens,
+                    // lane group g holding tokens 4g .. 4g + 3 of both sub-tiles, in the
+                    // same order in the V^T operand (two transposed reads) and in P
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
                         const float mref = m[cb] == kNegInf ? 0.f : m[cb];
-                        float p[4];
+                        float p[8];
+                        if (masked) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            p[i] = exp2_fast(sc[cb][i] - mref);
-                            l[cb] += p[i];
+                            for (int j = 0; j < 8; ++j) p[j] = exp2_fast(s[cb][j >> 2][j & 3] - mref);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(s[cb][j >> 2][j & 3], a.scale_log2, -mref));
                         }
-                        const s16x4 pb = __builtin_bit_cast(
-                            s16x4, make_uint2(bf16x2_bits(p[0], p[1]), bf16x2_bits(p[2], p[3])));
+                        l[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+                        const bf16x8 pb = __builtin_bit_cast(
+                            bf16x8, make_uint4(bf16x2_pack(p[0], p[1]), bf16x2_pack(p[2], p[3]),
+                                               bf16x2_pack(p[4], p[5]), bf16x2_pack(p[6], p[7])));
 #pragma unroll
-                        for (int db = 0; db < 8; ++db)
-                            acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], pb, acc[cb][db], 0, 0, 0);
+                        for (int db = 0; db < 8; ++db) {
+                            const bf16x8 vt = __builtin_bit_cast(
+                                bf16x8, make_uint4(__builtin_bit_cast(uint2, va[0][db]).x,
+                                                   __builtin_bit_cast(uint2, va[0][db]).y,
+                                                   __builtin_bit_cast(uint2, va[1][db]).x,
+                                                   __builtin_bit_cast(uint2, va[1][db]).y));
+                            acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, acc[cb][db], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -249,7 +309,7 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             const f32x4 v = acc[cb][db] * inv;
-            *reinterpret_cast<uint2*>(o + 16 * db) = make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
+            *reinterpret_cast<uint2*>(o + 16 * db) = make_uint2(bf16x2_pack(v[0], v[1]), bf16x2_pack(v[2], v[3]));
         }
     }
 }
@@ -284,17 +344,12 @@ hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cach
     a.qblocks = 0;
     a.scale_log2 = scale_log2;
     if (cb <= 0) {
-        // the most query columns per wave (K/V reuse) that still leaves two
-        // workgroups per compute unit
+        // two query blocks per wave (K/V reuse) while that still leaves two
+        // workgroups per compute unit in the grid, else one
         const long long bh = (long long)B * Hkv;
-        cb = 4;
-        while (cb > 1 && bh * ((QL + kWaves * 2 * cb - 1) / (kWaves * 2 * cb)) < 512) cb /= 2;
+        cb = bh * ((QL + kWaves * 4 - 1) / (kWaves * 4)) >= 512 ? 2 : 1;
     }
-    switch (cb) {
-        case 4: return launch_cb<4>(a, stream);
-        case 2: return launch_cb<2>(a, stream);
-        default: return launch_cb<1>(a, stream);
-    }
+    return cb == 2 ? launch_cb<2>(a, stream) : launch_cb<1>(a, stream);
 }
 
 }  // namespace lbsa
