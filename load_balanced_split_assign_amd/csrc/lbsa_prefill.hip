@@ -71,6 +71,13 @@ struct PrefillArgs {
 
 __device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// 16-byte chunk swizzle of a V row inside its 16-row slice.  A transposed read
+// pass covers 8 rows (4 g + r / 4 for g = 0, 1, or g = 2, 3), each lane group
+// of a row reading one aligned 32-byte chunk pair; the swizzle puts the 8 rows'
+// pairs on 8 different bank groups.  (K keeps chunk ^ row, which spreads the
+// 16 rows of a 16-byte read over all 64 banks.)
+__device__ inline int vswz(int row) { return ((row << 1) & 14) | ((row >> 3) & 1); }
+
 template <int CB>
 __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char ring_mem[kPfStages * kPfStageBytes];
@@ -136,14 +143,17 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
 
         // this lane's 4 K and 4 V chunks of every tile: rows 16 w + 4 s + lane / 16,
         // chunk lane % 16, XOR-swizzled by the row inside the wave's 16
-        uint32_t live_off[4], dead_off[4];
+        uint32_t live_off[4], live_off_v[4], dead_off[4];
         int lrow[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             lrow[s] = 4 * s + (lane >> 4);
             const uint32_t chunk = 16u * (uint32_t)((lane & 15) ^ lrow[s]);
-            live_off[s] = (uint32_t)(16 * w + lrow[s]) * (uint32_t)a.Hkv * kPfRow + chunk;
-            dead_off[s] = chunk;                          // row 0 of the page: always live
+            const uint32_t chunk_v = 16u * (uint32_t)((lane & 15) ^ vswz(lrow[s]));
+            const uint32_t row_off = (uint32_t)(16 * w + lrow[s]) * (uint32_t)a.Hkv * kPfRow;
+            live_off[s] = row_off + chunk;
+            live_off_v[s] = row_off + chunk_v;
+            dead_off[s] = 16u * (uint32_t)(lane & 15);    // row 0 of the page: always live
         }
         const auto* pt = uniform_ptr<int32_t>(a.page_table) + (size_t)b * a.max_pages;
         auto issue = [&](int t, lds_char* st) {
@@ -159,9 +169,9 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
             const bool full = tok0 + 16 <= L;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const uint32_t o = (full || tok0 + lrow[s] < L) ? live_off[s] : dead_off[s];
-                dma16(kb + o, st + w * kPfSlice + 1024 * s);
-                dma16(vb + o, st + kPfHalf + w * kPfSlice + 1024 * s);
+                const bool live = full || tok0 + lrow[s] < L;
+                dma16(kb + (live ? live_off[s] : dead_off[s]), st + w * kPfSlice + 1024 * s);
+                dma16(vb + (live ? live_off_v[s] : dead_off[s]), st + kPfHalf + w * kPfSlice + 1024 * s);
             }
         };
         for (int u = 0; u < kPfStages - 1; ++u) issue(min(u, ntiles - 1), ring + u * kPfStageBytes);
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
                             lds_addr(st + kPfHalf + (32 * half + 16 * sub + vrow) * kPfRow + 8 * (r & 1));
 #pragma unroll
                         for (int db = 0; db < 8; ++db)
-                            vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ vrow);
+                            vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ vswz(vrow));
                         lds_read_tile_bf16(kk[sub], va[sub], ka, vaddr);
                     }
 
