@@ -84,8 +84,10 @@ static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt rang
 static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
 
 // 16-byte chunk swizzle inside a row: LDS chunk c' holds row chunk c' ^ f(row).
+// K rows (and fp8 V rows) use swz; bf16 V rows, which are read transposed, and
+// the bf16 copy of fp8 V use swz_v (no bank conflicts in a transposed pass).
 template <bool FP8> __device__ inline int swz(int row) { return FP8 ? ((row >> 1) & 7) : (row & 15); }
-__device__ inline int swz_bf16(int row) { return row & 15; }
+template <bool FP8> __device__ inline int swz_vrow(int row) { return FP8 ? swz<true>(row) : swz_v(row); }
 
 // LDS of one split / static workgroup.  Every ring stage is its own
 // __shared__ object: the compiler's wait-count insertion can then tell which
@@ -128,8 +130,9 @@ struct Desc {
 
 // Per-lane constants of the asynchronous loads (fixed for a wave's stream).
 template <bool FP8> struct LaneLoads {
-    uint32_t kv_live[Stage<FP8>::KV_LOADS];   // byte offset in a page of this lane's 16 B (h = 0)
-    uint32_t kv_dead[Stage<FP8>::KV_LOADS];   // same chunk of the page's row 0
+    uint32_t kv_live[Stage<FP8>::KV_LOADS];   // byte offset in a page of this lane's 16 B of K (h = 0)
+    uint32_t v_live[Stage<FP8>::KV_LOADS];    // the same for V (its own swizzle)
+    uint32_t kv_dead[Stage<FP8>::KV_LOADS];   // a chunk of the page's row 0
     int row[Stage<FP8>::KV_LOADS];            // slice row loaded by this lane
     int scale_row;                            // fp8: slice row of this lane's scale (lane % 16)
     __device__ void init(int Hkv, int w, int lane) {
@@ -140,7 +143,10 @@ template <bool FP8> struct LaneLoads {
         for (int s = 0; s < SL::KV_LOADS; ++s) {
             row[s] = kRowsPerLoad * s + lane / kChunks;
             const uint32_t chunk = 16u * (uint32_t)((lane % kChunks) ^ swz<FP8>(row[s]));
-            kv_live[s] = (uint32_t)(16 * w + row[s]) * (uint32_t)Hkv * SL::kRow + chunk;
+            const uint32_t chunk_v = 16u * (uint32_t)((lane % kChunks) ^ swz_vrow<FP8>(row[s]));
+            const uint32_t row_off = (uint32_t)(16 * w + row[s]) * (uint32_t)Hkv * SL::kRow;
+            kv_live[s] = row_off + chunk;
+            v_live[s] = row_off + chunk_v;
             kv_dead[s] = chunk;
         }
         scale_row = lane & 15;
@@ -160,9 +166,9 @@ __device__ inline void issue_tile(const AttnArgs& a, const LaneLoads<FP8>& ll, l
     const bool full = tok0 + 16 <= d.L;                 // every row of this slice is live
 #pragma unroll
     for (int s = 0; s < SL::KV_LOADS; ++s) {
-        const uint32_t off = (full || tok0 + ll.row[s] < d.L) ? ll.kv_live[s] : ll.kv_dead[s];
-        dma16(kb + off, st + SL::K + 1024 * s);
-        dma16(vb + off, st + SL::V + 1024 * s);
+        const bool live = full || tok0 + ll.row[s] < d.L;
+        dma16(kb + (live ? ll.kv_live[s] : ll.kv_dead[s]), st + SL::K + 1024 * s);
+        dma16(vb + (live ? ll.v_live[s] : ll.kv_dead[s]), st + SL::V + 1024 * s);
     }
     if constexpr (FP8) {
         const size_t sbase = ((size_t)page * a.Hkv + d.h) * kTile;
@@ -231,7 +237,7 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
         for (int ks = 0; ks < 4; ++ks) ka[ks] = lds_addr(st + SL::K + r * 256 + 16 * ((g + 4 * ks) ^ swz<false>(r)));
         const uint32_t vr = lds_addr(st + SL::V + vrow * 256 + 8 * (r & 1));
 #pragma unroll
-        for (int db = 0; db < 8; ++db) vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_bf16(vrow));
+        for (int db = 0; db < 8; ++db) vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_v(vrow));
         uint4 k[4];
         lds_read_tile_bf16(k, va, ka, vaddr);
         bf16x8 qv[4];
@@ -268,8 +274,8 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int c = g + 4 * p;
-            waddr[2 * p] = lds_addr(vb + r * 256 + 16 * ((2 * c) ^ swz_bf16(r)));
-            waddr[2 * p + 1] = lds_addr(vb + r * 256 + 16 * ((2 * c + 1) ^ swz_bf16(r)));
+            waddr[2 * p] = lds_addr(vb + r * 256 + 16 * ((2 * c) ^ swz_v(r)));
+            waddr[2 * p + 1] = lds_addr(vb + r * 256 + 16 * ((2 * c + 1) ^ swz_v(r)));
             wv[2 * p] = fp8x8_to_bf16x8(o[2 + p].x, o[2 + p].y);
             wv[2 * p + 1] = fp8x8_to_bf16x8(o[2 + p].z, o[2 + p].w);
         }
@@ -277,7 +283,7 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
         const uint32_t vr = lds_addr(vb + vrow * 256 + 8 * (r & 1));
         uint32_t vaddr[8];
 #pragma unroll
-        for (int db = 0; db < 8; ++db) vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_bf16(vrow));
+        for (int db = 0; db < 8; ++db) vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_v(vrow));
         vt_read8(va, vaddr);
     }
     const f32x4 s = sa + sb;

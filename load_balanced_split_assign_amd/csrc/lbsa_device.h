@@ -32,6 +32,14 @@ __device__ inline void lds_store16(lds_char* p, uint4 v) {
 }
 __device__ inline uint32_t lds_addr(const lds_char* p) { return (uint32_t)(size_t)p; }
 
+// 16-byte chunk swizzle of a bf16 V row (16 chunks) inside its 16-row slice,
+// for the transposed reads of V^T (ds_read_b64_tr_b16).  One pass of such a
+// read covers 8 rows (4 g + r / 4 for g = 0, 1, or g = 2, 3), each row's
+// lanes reading one aligned 32-byte chunk pair; this swizzle puts the 8 rows'
+// pairs on 8 different 32-byte bank groups, so the pass has no bank conflict
+// (chunk ^ row would pair rows 2k and 2k + 1 on the same banks).
+__device__ inline int swz_v(int row) { return ((row << 1) & 14) | ((row >> 3) & 1); }
+
 // Two floats -> two bf16 (round to nearest even) in one dword through one
 // packed convert (v_cvt_pk_bf16_f32), low half first.
 typedef float f32x2_v __attribute__((ext_vector_type(2)));

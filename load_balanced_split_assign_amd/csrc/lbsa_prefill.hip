@@ -71,12 +71,7 @@ struct PrefillArgs {
 
 __device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// 16-byte chunk swizzle of a V row inside its 16-row slice.  A transposed read
-// pass covers 8 rows (4 g + r / 4 for g = 0, 1, or g = 2, 3), each lane group
-// of a row reading one aligned 32-byte chunk pair; the swizzle puts the 8 rows'
-// pairs on 8 different bank groups.  (K keeps chunk ^ row, which spreads the
-// 16 rows of a 16-byte read over all 64 banks.)
-__device__ inline int vswz(int row) { return ((row << 1) & 14) | ((row >> 3) & 1); }
+
 
 template <int CB>
 __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
@@ -149,7 +144,7 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
         for (int s = 0; s < 4; ++s) {
             lrow[s] = 4 * s + (lane >> 4);
             const uint32_t chunk = 16u * (uint32_t)((lane & 15) ^ lrow[s]);
-            const uint32_t chunk_v = 16u * (uint32_t)((lane & 15) ^ vswz(lrow[s]));
+            const uint32_t chunk_v = 16u * (uint32_t)((lane & 15) ^ swz_v(lrow[s]));
             const uint32_t row_off = (uint32_t)(16 * w + lrow[s]) * (uint32_t)a.Hkv * kPfRow;
             live_off[s] = row_off + chunk;
             live_off_v[s] = row_off + chunk_v;
@@ -205,7 +200,7 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
                             lds_addr(st + kPfHalf + (32 * half + 16 * sub + vrow) * kPfRow + 8 * (r & 1));
 #pragma unroll
                         for (int db = 0; db < 8; ++db)
-                            vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ vswz(vrow));
+                            vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_v(vrow));
                         lds_read_tile_bf16(kk[sub], va[sub], ka, vaddr);
                     }
 
