@@ -315,6 +315,8 @@ def table4(args):
     stream = torch.cuda.current_stream()
     rows = []
     for name, (kind, B, QL, L) in wl.TABLE4.items():
+        if args.shapes and name not in args.shapes.split(","):
+            continue
         b = wl.make_table4_batch(name, device="cuda:0")
         torch.cuda.synchronize()
         row = {"shape": name, "kind": kind, "batch": B, "q_len": QL, "kv_len": L,
@@ -557,6 +559,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (bounded sample)")
     ap.add_argument("--table4", action="store_true",
                     help="instead of the headline line: Table 4 prefill / extend / decode shapes (64/8 heads)")
+    ap.add_argument("--shapes", default="", help="with --table4: comma-separated subset of the shapes")
     ap.add_argument("--mtp", action="store_true",
                     help="instead of the headline line: 2-query-token decode vs 1-token decode")
     ap.add_argument("--prologue", action="store_true",
