@@ -359,6 +359,67 @@ def table4(args):
     print(json.dumps({"table4": rows, "unit": "us", "flush": args.flush}), flush=True)
 
 
+ROUTER_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def router_bench(args):
+    """Split-bf16 router GEMM on the SGLang post's K = 4096, N = 192 sweep over M
+    tokens, against an fp32 GEMM of the same scores (torch / hipBLASLt, with and
+    without the bf16 -> fp32 cast of X), each timed with its own event pair
+    (flush before each launch); the max |error| of both against fp64 on the
+    exact fp32 weights."""
+    import numpy as np
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    flush = make_flush(args.flush)
+    stream = torch.cuda.current_stream()
+    K, N = 4096, 192
+    g = torch.Generator(device="cuda:0").manual_seed(120)
+    w = torch.randn(N, K, generator=g, device="cuda:0") * 0.02
+    wt = w.t().contiguous()
+    hi, lo = lbsa.router_split_weights(w)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            flush(i)
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush(i)
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return summarize([1000.0 * a.elapsed_time(b) for a, b in ev])["mean"]
+
+    rows = []
+    w64 = w.double()
+    for M in ROUTER_M:
+        x = torch.randn(M, K, generator=g, device="cuda:0").to(torch.bfloat16)
+        xf = x.float()
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        need = lbsa.router_workspace_bytes(M, N, K)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda:0")
+        t_ours = timed(lambda: lbsa.router_gemm(x, hi, lo, out=out, workspace=ws))
+        t_f32 = timed(lambda: torch.mm(xf, wt))
+        t_f32_cast = timed(lambda: torch.mm(x.float(), wt))
+        exact = x.double() @ w64.t()
+        lbsa.router_gemm(x, hi, lo, out=out, workspace=ws)
+        err = float((out.double() - exact).abs().max())
+        err_f32 = float((torch.mm(xf, wt).double() - exact).abs().max())
+        flops = 2 * 2 * M * N * K
+        nbytes = M * K * 2 + 2 * N * K * 2 + M * N * 4
+        rows.append({"M": M, "us": round(t_ours, 2), "fp32_gemm_us": round(t_f32, 2),
+                     "fp32_cast_gemm_us": round(t_f32_cast, 2), "speedup_vs_fp32": round(t_f32 / t_ours, 2),
+                     "speedup_vs_fp32_cast": round(t_f32_cast / t_ours, 2),
+                     "TFLOPs": round(flops / t_ours / 1e6, 2), "GBps": round(nbytes / t_ours / 1e3, 1),
+                     "max_abs_err": err, "fp32_max_abs_err": err_f32})
+        del x, xf, out, ws
+    print(json.dumps({"router_gemm": rows, "K": K, "N": N, "unit": "us", "flush": args.flush}), flush=True)
+
+
 def prologue_bytes(T, Hq, Hkv, fp8):
     """Bytes the prologue must move: the fused QKV rows in, positions and slots,
     the two norm weights, Q out (+ scale) and the K / V cache rows (+ scales)."""
@@ -560,6 +621,8 @@ def main():
     ap.add_argument("--table4", action="store_true",
                     help="instead of the headline line: Table 4 prefill / extend / decode shapes (64/8 heads)")
     ap.add_argument("--shapes", default="", help="with --table4: comma-separated subset of the shapes")
+    ap.add_argument("--router", action="store_true",
+                    help="instead of the headline line: split-bf16 router GEMM, K 4096, N 192, M sweep")
     ap.add_argument("--mtp", action="store_true",
                     help="instead of the headline line: 2-query-token decode vs 1-token decode")
     ap.add_argument("--prologue", action="store_true",
@@ -602,6 +665,9 @@ def main():
         return
     if args.table4:
         table4(args)
+        return
+    if args.router:
+        router_bench(args)
         return
 
     name = args.workload

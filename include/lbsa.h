@@ -250,6 +250,32 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
                  void* stream);
 
 /*
+ * Split-bf16 router GEMM (SGLang post, section "Router GEMM: balancing routing
+ * precision and throughput"): router scores from bf16 hidden states and fp32
+ * router weights, run on bf16 MFMA with the weights' low mantissa bits kept.
+ *
+ * lbsa_router_split_weights, once per weight matrix:
+ *   w_d        fp32 [n][k] (one row per expert)
+ *   w_high_d   bf16 [n][k]: w truncated to bf16 (its low 16 bits dropped)
+ *   w_low_d    bf16 [n][k]: (w - w_high) * 256 rounded to nearest even
+ * so that w ~ w_high + w_low / 256 within 2^-16 |w|.
+ *
+ * lbsa_router_gemm, per call:
+ *   x_d        bf16 [m][k] hidden states (m = 0 is a no-op)
+ *   scores_d   fp32 [m][n] = x w_high^T + (x w_low^T) / 256, fp32 accumulation
+ *   workspace  >= lbsa_router_workspace_bytes(m, n, k) bytes (partials of a
+ *              split of k; 0 bytes for large m), 16-byte aligned
+ * Shapes: n a multiple of 16, k of 128 (else LBSA_ERR_UNSUPPORTED); every
+ * pointer 16-byte aligned (else LBSA_ERR_INVALID_ARGUMENT).  The scores are
+ * deterministic: splits of k are added in a fixed order.  All buffers are the
+ * caller's; the calls only enqueue kernels on the stream.
+ */
+int lbsa_router_split_weights(const float* w_d, int32_t n, int32_t k, void* w_high_d, void* w_low_d, void* stream);
+int lbsa_router_workspace_bytes(int32_t m, int32_t n, int32_t k, size_t* out_bytes);
+int lbsa_router_gemm(const void* x_d, const void* w_high_d, const void* w_low_d, int32_t m, int32_t n, int32_t k,
+                     float* scores_d, void* workspace_d, size_t workspace_bytes, void* stream);
+
+/*
  * Fused attention prologue: from the fused QKV projection of num_tokens tokens
  * to the decode path's inputs, in one launch.  Source: vLLM post, section "A
  * fused attention prologue"; SGLang post, the attention prologue section

@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "lbsa")
 LIB = os.path.join(HERE, "liblbsa.so")
-SOURCES = ["lbsa_assign.hip", "lbsa_attention.hip", "lbsa_prefill.hip", "lbsa_prologue.hip", "lbsa_api.hip"]
+SOURCES = ["lbsa_assign.hip", "lbsa_attention.hip", "lbsa_prefill.hip", "lbsa_prologue.hip", "lbsa_router.hip",
+           "lbsa_api.hip"]
 ARCH = os.environ.get("LBSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

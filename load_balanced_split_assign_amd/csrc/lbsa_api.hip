@@ -341,6 +341,46 @@ LBSA_API int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_
                                      0, static_cast<hipStream_t>(stream)));
 }
 
+static int router_shape(int32_t m, int32_t n, int32_t k) {
+    if (m < 0 || n <= 0 || k <= 0) return LBSA_ERR_INVALID_ARGUMENT;
+    if (n % 16 != 0 || k % 128 != 0) return LBSA_ERR_UNSUPPORTED;
+    if ((long long)m * k >= (1LL << 31) || (long long)n * k >= (1LL << 31) || (long long)m * n * 32 >= (1LL << 31))
+        return LBSA_ERR_UNSUPPORTED;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_router_split_weights(const float* w_d, int32_t n, int32_t k, void* w_high_d, void* w_low_d,
+                                       void* stream) {
+    const int s = router_shape(0, n, k);
+    if (s != LBSA_OK) return s;
+    if (!w_d || !w_high_d || !w_low_d || !aligned(w_d, 16) || !aligned(w_high_d, 16) || !aligned(w_low_d, 16))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_router_split(w_d, w_high_d, w_low_d, (long long)n * k, static_cast<hipStream_t>(stream)));
+}
+
+LBSA_API int lbsa_router_workspace_bytes(int32_t m, int32_t n, int32_t k, size_t* out_bytes) {
+    if (!out_bytes) return LBSA_ERR_INVALID_ARGUMENT;
+    const int s = router_shape(m, n, k);
+    if (s != LBSA_OK) return s;
+    *out_bytes = m == 0 ? 0 : router_plan(m, n, k).workspace;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_router_gemm(const void* x_d, const void* w_high_d, const void* w_low_d, int32_t m, int32_t n,
+                              int32_t k, float* scores_d, void* workspace_d, size_t workspace_bytes, void* stream) {
+    const int s = router_shape(m, n, k);
+    if (s != LBSA_OK) return s;
+    if (m == 0) return LBSA_OK;
+    if (!x_d || !w_high_d || !w_low_d || !scores_d || !aligned(x_d, 16) || !aligned(w_high_d, 16) ||
+        !aligned(w_low_d, 16) || !aligned(scores_d, 16))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    const RouterPlan p = router_plan(m, n, k);
+    if (p.workspace > 0 && (!workspace_d || workspace_bytes < p.workspace || !aligned(workspace_d, 16)))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_router_gemm(x_d, w_high_d, w_low_d, m, n, k, scores_d, workspace_d,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 LBSA_API int lbsa_prologue(const void* qkv_d, const int32_t* positions_d, const int64_t* slot_mapping_d,
                            const float* q_norm_weight_d, const float* k_norm_weight_d, double rope_theta,
                            float eps, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,

@@ -94,6 +94,17 @@ hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu);
 hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                           const int32_t* seqlens, int B, int QL, int Hq, int Hkv, int max_pages,
                           int64_t num_pages, float scale_log2, void* out, int cb, hipStream_t stream);
+// Router GEMM launch plan: MT token tiles of 16 per wave, S splits of K, and
+// the workspace the splits' partials need (0 when S = 1).
+struct RouterPlan {
+    int MT, S;
+    bool wide;          // up to 64 tokens: one launch, K split over the waves of a workgroup
+    size_t workspace;
+};
+RouterPlan router_plan(int M, int N, int K);
+hipError_t launch_router_split(const float* w, void* hi, void* lo, long long count, hipStream_t stream);
+hipError_t launch_router_gemm(const void* x, const void* w_hi, const void* w_lo, int M, int N, int K, float* out,
+                              void* workspace, hipStream_t stream);
 hipError_t launch_prologue(const uint16_t* qkv, const int32_t* positions, const int64_t* slots,
                            const float* qw, const float* kw, double theta, float eps, int T, int Hq,
                            int Hkv, bool fp8, void* q_out, float* q_scale, void* k_cache, void* v_cache,

@@ -69,12 +69,16 @@ def lib() -> ctypes.CDLL:
         L.lbsa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, i64, i32, f32, vp, sz, vp, vp]
         L.lbsa_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32, vp, vp]
+        L.lbsa_router_split_weights.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.lbsa_router_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.lbsa_router_gemm.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
         L.lbsa_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, f32, i32, i32, i32, i32, i32, i32,
                                     vp, vp, vp, vp, vp, vp, i64, vp]
         for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes", "lbsa_prologue",
                    "lbsa_workspace_layout_get", "lbsa_workspace_bytes", "lbsa_static_workspace_bytes",
                    "lbsa_plan", "lbsa_decode", "lbsa_decode_split", "lbsa_decode_combine",
-                   "lbsa_decode_static", "lbsa_prefill"):
+                   "lbsa_decode_static", "lbsa_prefill", "lbsa_router_split_weights",
+                   "lbsa_router_workspace_bytes", "lbsa_router_gemm"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -269,6 +273,46 @@ def prefill(q, k_cache, v_cache, page_table, seqlens, softmax_scale: float, out=
     _check("lbsa_prefill", lib().lbsa_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), KV_BF16, _ptr(page_table),
                                               _ptr(seqlens), B, QL, Hq, Hkv, D, page, int(page_table.shape[1]),
                                               int(num_pages), float(softmax_scale), _ptr(out), _stream(q.device)))
+    return out
+
+
+def router_split_weights(w, w_high=None, w_low=None):
+    """fp32 router weights [N, K] -> (w_high, w_low) bf16 [N, K]: truncation and
+    the bf16 of the residual x 256."""
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous()
+    N, K = w.shape
+    if w_high is None:
+        w_high = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    if w_low is None:
+        w_low = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    _check("lbsa_router_split_weights", lib().lbsa_router_split_weights(_ptr(w), N, K, _ptr(w_high), _ptr(w_low),
+                                                                        _stream(w.device)))
+    return w_high, w_low
+
+
+def router_workspace_bytes(m: int, n: int, k: int) -> int:
+    out = ctypes.c_size_t()
+    _check("lbsa_router_workspace_bytes", lib().lbsa_router_workspace_bytes(m, n, k, ctypes.byref(out)))
+    return int(out.value)
+
+
+def router_gemm(x, w_high, w_low, out=None, workspace=None):
+    """fp32 scores [M, N] = x w_high^T + (x w_low^T) / 256 for bf16 x [M, K]."""
+    assert x.dtype == torch.bfloat16 and w_high.dtype == torch.bfloat16 and w_low.dtype == torch.bfloat16
+    for t in (x, w_high, w_low):
+        assert t.is_contiguous()
+    M, K = x.shape
+    N = w_high.shape[0]
+    assert tuple(w_high.shape) == (N, K) and tuple(w_low.shape) == (N, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = router_workspace_bytes(M, N, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check("lbsa_router_gemm", lib().lbsa_router_gemm(_ptr(x), _ptr(w_high), _ptr(w_low), M, N, K, _ptr(out),
+                                                      _ptr(workspace) if workspace is not None else None,
+                                                      0 if workspace is None else workspace.numel(),
+                                                      _stream(x.device)))
     return out
 
 

@@ -147,3 +147,23 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lbsa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         lbsa.lib()
+
+
+def test_router_rejects_bad_arguments_on_host():
+    L = lbsa.lib()
+    vp = ctypes.c_void_p
+    out = ctypes.c_size_t()
+    assert L.lbsa_router_workspace_bytes(4, 192, 4096, ctypes.byref(out)) == lbsa.OK
+    assert L.lbsa_router_workspace_bytes(4, 100, 4096, ctypes.byref(out)) == lbsa.ERR_UNSUPPORTED    # n % 16
+    assert L.lbsa_router_workspace_bytes(4, 192, 4000, ctypes.byref(out)) == lbsa.ERR_UNSUPPORTED    # k % 128
+    assert L.lbsa_router_workspace_bytes(-1, 192, 4096, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_router_workspace_bytes(0, 192, 4096, ctypes.byref(out)) == lbsa.OK and out.value == 0
+    assert L.lbsa_router_split_weights(None, 192, 4096, vp(256), vp(512), None) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_router_split_weights(vp(8), 192, 4096, vp(256), vp(512), None) == lbsa.ERR_INVALID_ARGUMENT
+    # (every call below must fail validation: none may reach a launch with these fake pointers)
+    assert L.lbsa_router_workspace_bytes(100, 192, 4096, ctypes.byref(out)) == lbsa.OK and out.value > 0
+    assert L.lbsa_router_gemm(vp(256), vp(512), vp(1024), 100, 192, 4096, vp(2048), None, 0, None) == \
+        lbsa.ERR_INVALID_ARGUMENT                                                              # workspace needed
+    assert L.lbsa_router_gemm(None, vp(512), vp(1024), 4, 192, 4096, vp(2048), vp(4096), 1 << 30, None) == \
+        lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_router_gemm(None, None, None, 0, 192, 4096, None, None, 0, None) == lbsa.OK       # nothing to do
