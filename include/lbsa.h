@@ -256,19 +256,28 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
  *
  * lbsa_router_split_weights, once per weight matrix:
  *   w_d        fp32 [n][k] (one row per expert)
- *   w_high_d   bf16 [n][k]: w truncated to bf16 (its low 16 bits dropped)
- *   w_low_d    bf16 [n][k]: (w - w_high) * 256 rounded to nearest even
- * so that w ~ w_high + w_low / 256 within 2^-16 |w|.
+ *   w_high_d   bf16, n * k elements: w truncated to bf16 (its low 16 bits dropped)
+ *   w_low_d    bf16, n * k elements: (w - w_high) * 256 rounded to nearest even
+ * so that w ~ w_high + w_low / 256 within 2^-16 |w|.  Both parts are stored
+ * blocked for the GEMM's loads: element (e, c) (expert e, input feature c)
+ * sits at index ((e / 16) * (k / 64) + c / 64) * 1024 + b * 512 + lane * 8 + i
+ * with c % 64 = 16 g + 8 b + i and lane = 16 g + e % 16 (per 16 experts
+ * and 64 features a 2 KiB block; each wave's load of a block half is one
+ * contiguous 1 KiB read).
  *
  * lbsa_router_gemm, per call:
  *   x_d        bf16 [m][k] hidden states (m = 0 is a no-op)
+ *   w_*_d      the two blocked parts from lbsa_router_split_weights
  *   scores_d   fp32 [m][n] = x w_high^T + (x w_low^T) / 256, fp32 accumulation
- *   workspace  >= lbsa_router_workspace_bytes(m, n, k) bytes (partials of a
- *              split of k; 0 bytes for large m), 16-byte aligned
- * Shapes: n a multiple of 16, k of 128 (else LBSA_ERR_UNSUPPORTED); every
- * pointer 16-byte aligned (else LBSA_ERR_INVALID_ARGUMENT).  The scores are
- * deterministic: splits of k are added in a fixed order.  All buffers are the
- * caller's; the calls only enqueue kernels on the stream.
+ *   workspace  >= lbsa_router_workspace_bytes(m, n, k) bytes, 16-byte aligned,
+ *              any contents (0 bytes, and the pointer may be NULL, when k is
+ *              not split): the fp32 partial scores of the parts of k.  Calls
+ *              that share one workspace must not overlap in time.
+ * Shapes: n a multiple of 16, k a multiple of 256 and at most 2^20 (else
+ * LBSA_ERR_UNSUPPORTED); every pointer 16-byte aligned (else
+ * LBSA_ERR_INVALID_ARGUMENT).  The scores are deterministic: the parts of a
+ * split of k are added in a fixed order.  All buffers are the caller's; the
+ * calls only enqueue kernels on the stream.
  */
 int lbsa_router_split_weights(const float* w_d, int32_t n, int32_t k, void* w_high_d, void* w_low_d, void* stream);
 int lbsa_router_workspace_bytes(int32_t m, int32_t n, int32_t k, size_t* out_bytes);

@@ -31,10 +31,13 @@ CFLAGS = [
 ]
 
 
-# per-source flags: the prefill kernel keeps its MFMA accumulators in VGPRs
-# (the softmax rescale touches them with VALU instructions, which cannot read
-# AGPRs; without this the compiler copies every accumulator through AGPRs)
-EXTRA = {"lbsa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source flags: the prefill and router kernels keep their MFMA
+# accumulators in VGPRs.  Prefill: the softmax rescale touches them with VALU
+# instructions, which cannot read AGPRs.  Router: with AGPR accumulators
+# carried around the k loop, the allocator reshuffles them with accvgpr moves
+# on every iteration.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"lbsa_prefill.hip": _VGPR_FORM, "lbsa_router.hip": _VGPR_FORM}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -102,7 +102,7 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 200; }
+LBSA_API int lbsa_version(void) { return 201; }
 
 LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_P) {
     if (!out_P || (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3))
@@ -343,8 +343,8 @@ LBSA_API int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_
 
 static int router_shape(int32_t m, int32_t n, int32_t k) {
     if (m < 0 || n <= 0 || k <= 0) return LBSA_ERR_INVALID_ARGUMENT;
-    if (n % 16 != 0 || k % 128 != 0) return LBSA_ERR_UNSUPPORTED;
-    if ((long long)m * k >= (1LL << 31) || (long long)n * k >= (1LL << 31) || (long long)m * n * 32 >= (1LL << 31))
+    if (n % 16 != 0 || k % kRouterKAlign != 0 || k > (1 << 20)) return LBSA_ERR_UNSUPPORTED;
+    if ((long long)m * k >= (1LL << 31) || (long long)n * k >= (1LL << 31) || (long long)m * n >= (1LL << 31))
         return LBSA_ERR_UNSUPPORTED;
     return LBSA_OK;
 }
@@ -355,7 +355,7 @@ LBSA_API int lbsa_router_split_weights(const float* w_d, int32_t n, int32_t k, v
     if (s != LBSA_OK) return s;
     if (!w_d || !w_high_d || !w_low_d || !aligned(w_d, 16) || !aligned(w_high_d, 16) || !aligned(w_low_d, 16))
         return LBSA_ERR_INVALID_ARGUMENT;
-    return hip_status(launch_router_split(w_d, w_high_d, w_low_d, (long long)n * k, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_router_split(w_d, w_high_d, w_low_d, n, k, static_cast<hipStream_t>(stream)));
 }
 
 LBSA_API int lbsa_router_workspace_bytes(int32_t m, int32_t n, int32_t k, size_t* out_bytes) {

@@ -94,15 +94,23 @@ hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu);
 hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                           const int32_t* seqlens, int B, int QL, int Hq, int Hkv, int max_pages,
                           int64_t num_pages, float scale_log2, void* out, int cb, hipStream_t stream);
-// Router GEMM launch plan: MT token tiles of 16 per wave, S splits of K, and
-// the workspace the splits' partials need (0 when S = 1).
+// Router GEMM launch plan.  Thin form (few tokens): MT 16-token tiles per
+// workgroup of 16 experts, K split in S = K / 256 parts.  Tile form: 64 tokens
+// x 192 experts per workgroup, S parts of K of at most kRouterTileMaxK each.
+// S > 1: the parts' fp32 partial planes [S][M][N] go to the workspace and a
+// second kernel adds them.
+constexpr int kRouterKAlign = 256;          // K granularity of both forms
+constexpr int kRouterThinMaxM = 256;        // thin form up to this many tokens
+constexpr int kRouterTileMaxK = 1024;       // k per tile workgroup (its X tile in LDS)
+constexpr int kRouterTileMaxS = 16;         // parts of K a tile-form split aims at, at most
+constexpr int kRouterTileTarget = 256;      // tile-form workgroups aimed at (one per CU)
 struct RouterPlan {
-    int MT, S;
-    bool wide;          // up to 64 tokens: one launch, K split over the waves of a workgroup
+    bool tile;
+    int MT, S, tiles_n;
     size_t workspace;
 };
 RouterPlan router_plan(int M, int N, int K);
-hipError_t launch_router_split(const float* w, void* hi, void* lo, long long count, hipStream_t stream);
+hipError_t launch_router_split(const float* w, void* hi, void* lo, int N, int K, hipStream_t stream);
 hipError_t launch_router_gemm(const void* x, const void* w_hi, const void* w_lo, int M, int N, int K, float* out,
                               void* workspace, hipStream_t stream);
 hipError_t launch_prologue(const uint16_t* qkv, const int32_t* positions, const int64_t* slots,

@@ -276,18 +276,34 @@ def prefill(q, k_cache, v_cache, page_table, seqlens, softmax_scale: float, out=
     return out
 
 
+def router_weight_shape(n: int, k: int) -> tuple:
+    """Shape of one blocked weight part: [n/16][k/64][2][64][8] bf16 (per 16
+    experts and 64 k, the halves b of the lanes' 16 k: lane = 16 g + n % 16
+    holds k % 64 = 16 g + 8 b + e at [b][lane][e])."""
+    return (n // 16, k // 64, 2, 64, 8)
+
+
 def router_split_weights(w, w_high=None, w_low=None):
-    """fp32 router weights [N, K] -> (w_high, w_low) bf16 [N, K]: truncation and
-    the bf16 of the residual x 256."""
+    """fp32 router weights [N, K] -> (w_high, w_low): truncation and the bf16
+    of the residual x 256, both blocked (router_weight_shape)."""
     assert w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous()
     N, K = w.shape
+    shape = router_weight_shape(N, K)
     if w_high is None:
-        w_high = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+        w_high = torch.empty(shape, dtype=torch.bfloat16, device=w.device)
     if w_low is None:
-        w_low = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+        w_low = torch.empty(shape, dtype=torch.bfloat16, device=w.device)
+    assert w_high.numel() == N * K and w_low.numel() == N * K
     _check("lbsa_router_split_weights", lib().lbsa_router_split_weights(_ptr(w), N, K, _ptr(w_high), _ptr(w_low),
                                                                         _stream(w.device)))
     return w_high, w_low
+
+
+def router_unpack_weights(part) -> torch.Tensor:
+    """A blocked weight part -> the same values as [N, K] (a copy, for checks)."""
+    nt, ks = part.shape[0], part.shape[1]
+    t = part.reshape(nt, ks, 2, 4, 16, 8)                     # [n/16][k/64][b][g][r][e]
+    return t.permute(0, 4, 1, 3, 2, 5).reshape(16 * nt, 64 * ks)
 
 
 def router_workspace_bytes(m: int, n: int, k: int) -> int:
@@ -297,13 +313,14 @@ def router_workspace_bytes(m: int, n: int, k: int) -> int:
 
 
 def router_gemm(x, w_high, w_low, out=None, workspace=None):
-    """fp32 scores [M, N] = x w_high^T + (x w_low^T) / 256 for bf16 x [M, K]."""
+    """fp32 scores [M, N] = x w_high^T + (x w_low^T) / 256 for bf16 x [M, K] and
+    the blocked weight parts of router_split_weights."""
     assert x.dtype == torch.bfloat16 and w_high.dtype == torch.bfloat16 and w_low.dtype == torch.bfloat16
     for t in (x, w_high, w_low):
         assert t.is_contiguous()
     M, K = x.shape
-    N = w_high.shape[0]
-    assert tuple(w_high.shape) == (N, K) and tuple(w_low.shape) == (N, K)
+    N = 16 * w_high.shape[0]
+    assert tuple(w_high.shape) == router_weight_shape(N, K) and tuple(w_low.shape) == router_weight_shape(N, K)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     need = router_workspace_bytes(M, N, K)

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 200
+    assert lbsa.lib().lbsa_version() == 201
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -155,7 +155,17 @@ def test_router_rejects_bad_arguments_on_host():
     out = ctypes.c_size_t()
     assert L.lbsa_router_workspace_bytes(4, 192, 4096, ctypes.byref(out)) == lbsa.OK
     assert L.lbsa_router_workspace_bytes(4, 100, 4096, ctypes.byref(out)) == lbsa.ERR_UNSUPPORTED    # n % 16
-    assert L.lbsa_router_workspace_bytes(4, 192, 4000, ctypes.byref(out)) == lbsa.ERR_UNSUPPORTED    # k % 128
+    assert L.lbsa_router_workspace_bytes(4, 192, 4000, ctypes.byref(out)) == lbsa.ERR_UNSUPPORTED    # k % 256
+    assert L.lbsa_router_workspace_bytes(4, 192, 384, ctypes.byref(out)) == lbsa.ERR_UNSUPPORTED
+    assert L.lbsa_router_workspace_bytes(4, 16, 1 << 21, ctypes.byref(out)) == lbsa.ERR_UNSUPPORTED   # k > 2^20
+    # a split of k: one fp32 plane of scores per part
+    assert L.lbsa_router_workspace_bytes(4, 192, 4096, ctypes.byref(out)) == lbsa.OK
+    assert out.value == 16 * 4 * 192 * 4
+    assert L.lbsa_router_workspace_bytes(4, 192, 256, ctypes.byref(out)) == lbsa.OK and out.value == 0
+    # many tokens: k in parts of at most 1024 (the X tile of a workgroup sits in LDS)
+    assert L.lbsa_router_workspace_bytes(65536, 192, 1024, ctypes.byref(out)) == lbsa.OK and out.value == 0
+    assert L.lbsa_router_workspace_bytes(65536, 192, 4096, ctypes.byref(out)) == lbsa.OK
+    assert out.value == 4 * 65536 * 192 * 4
     assert L.lbsa_router_workspace_bytes(-1, 192, 4096, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT
     assert L.lbsa_router_workspace_bytes(0, 192, 4096, ctypes.byref(out)) == lbsa.OK and out.value == 0
     assert L.lbsa_router_split_weights(None, 192, 4096, vp(256), vp(512), None) == lbsa.ERR_INVALID_ARGUMENT
