@@ -569,11 +569,13 @@ def _pmc_rows(run_dir, counter):
     return [(k, v) for _, k, v in rows]
 
 
-def write_traffic(fetch_dir, write_dir):
-    """HBM bytes per split launch = FETCH_SIZE + WRITE_SIZE of the split kernel,
-    each scaled by CALIB_BYTES / what the same counter reads for the calibration
-    copy (the first device-to-device copy dispatch of a --calib-copy run)."""
-    rec = {"source_sha256": source_sha(SPLIT_SRC), "kernel": "split_kernel", "calib_bytes": CALIB_BYTES}
+def write_traffic(fetch_dir, write_dir, workload):
+    """HBM bytes per split launch on `workload` = FETCH_SIZE + WRITE_SIZE of the
+    split kernel, each scaled by CALIB_BYTES / what the same counter reads for
+    the calibration copy (the first device-to-device copy dispatch of a
+    --calib-copy run)."""
+    rec = {"source_sha256": source_sha(SPLIT_SRC), "kernel": "split_kernel", "workload": workload,
+           "calib_bytes": CALIB_BYTES}
     total = 0.0
     for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _pmc_rows(d, counter)
@@ -593,13 +595,13 @@ def write_traffic(fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
-def traffic_from_profile():
+def traffic_from_profile(workload):
     """HBM bytes per split launch from committed PMC counters, if they were taken
-    on the current kernel source (else None)."""
+    on the current kernel source and on this workload (else None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    if rec.get("source_sha256") != source_sha(SPLIT_SRC):
+    if rec.get("source_sha256") != source_sha(SPLIT_SRC) or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -634,7 +636,7 @@ def main():
                          "--calib-copy) into the split kernel's HBM bytes per launch")
     args = ap.parse_args()
     if args.traffic_from:
-        write_traffic(*args.traffic_from)
+        write_traffic(*args.traffic_from, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path needs no collectives; "
@@ -688,7 +690,7 @@ def main():
     layer_us = st["layer"]["mean"]
     layer_gbs = ab["layer"] / (layer_us * 1e-6) / 1e9
     split_gbs = ab["split"] / (split_us * 1e-6) / 1e9
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile(name)
 
     rec = {
         "metric": "decode-attn µs/step + achieved HBM GB/s (% of peak), mixed-length paged KV batch",
