@@ -21,7 +21,7 @@ def resident(batch):
     return lbsa.default_workgroups(0, batch["kv_dtype"])
 
 
-def counters(tm):
+def reserved_words(tm):
     h = tm[:64].cpu().numpy().view(np.int32)
     return tuple(int(h[i]) for i in HDR_RESERVED)
 
@@ -43,12 +43,12 @@ def test_multiwave_matches_oracle_and_repeats(oracle_mod, mult):
                                 num_heads=16, num_kv_heads=2, kv_dtype="bf16", seed=41))
     P = mult * resident(batch)
     tm = H.plan(batch, P)
-    assert counters(tm) == (0, 0)
+    assert reserved_words(tm) == (0, 0)
     outs = []
     for _ in range(3):
         outs.append(H.decode(batch, tm, P).clone())
         torch.cuda.synchronize()
-        assert counters(tm) == (0, 0)
+        assert reserved_words(tm) == (0, 0)
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     assert max_err(oracle_mod, batch, outs[0]) <= H.tol(batch)
@@ -61,7 +61,7 @@ def test_multiwave_fp8(oracle_mod):
     tm = H.plan(batch, P)
     out = H.decode(batch, tm, P)
     torch.cuda.synchronize()
-    assert counters(tm) == (0, 0)
+    assert reserved_words(tm) == (0, 0)
     assert max_err(oracle_mod, batch, out) <= H.tol(batch)
 
 
@@ -74,7 +74,7 @@ def test_multiwave_full_size_sampled(oracle_mod, name):
         tm = H.plan(batch, P)
         out = H.decode(batch, tm, P)
         torch.cuda.synchronize()
-        assert counters(tm) == (0, 0), (name, P)
+        assert reserved_words(tm) == (0, 0), (name, P)
         assert max_err(oracle_mod, batch, out, rows) <= H.tol(batch), (name, P)
 
 
@@ -98,4 +98,4 @@ def test_multiwave_partials_repeat_bitwise():
     for a, b in zip(p1, p2):
         assert np.isfinite(a).all()
         assert np.array_equal(a.view(np.int32), b.view(np.int32))
-    assert counters(tm) == (0, 0)
+    assert reserved_words(tm) == (0, 0)
