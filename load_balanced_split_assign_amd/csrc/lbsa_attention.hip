@@ -154,7 +154,8 @@ template <bool FP8> struct LaneLoads {
 };
 
 // Issue the asynchronous loads of one tile into stage `st`: this wave's 16 K
-// and V rows of page `page` and, for fp8, their k/v scales.
+// and V rows of page `page` and, for fp8, their k/v scales, all non-temporal
+// (a step reads each page once).
 template <bool FP8, int QL>
 __device__ inline void issue_tile(const AttnArgs& a, const LaneLoads<FP8>& ll, lds_char* __restrict__ st,
                                   int64_t page, const Desc& d, int tile, int w) {
@@ -167,14 +168,14 @@ __device__ inline void issue_tile(const AttnArgs& a, const LaneLoads<FP8>& ll, l
 #pragma unroll
     for (int s = 0; s < SL::KV_LOADS; ++s) {
         const bool live = full || tok0 + ll.row[s] < d.L;
-        dma16(kb + (live ? ll.kv_live[s] : ll.kv_dead[s]), st + SL::K + 1024 * s);
-        dma16(vb + (live ? ll.v_live[s] : ll.kv_dead[s]), st + SL::V + 1024 * s);
+        dma16_nt(kb + (live ? ll.kv_live[s] : ll.kv_dead[s]), st + SL::K + 1024 * s);
+        dma16_nt(vb + (live ? ll.v_live[s] : ll.kv_dead[s]), st + SL::V + 1024 * s);
     }
     if constexpr (FP8) {
         const size_t sbase = ((size_t)page * a.Hkv + d.h) * kTile;
         const int srow = (full || tok0 + ll.scale_row < d.L) ? 16 * w + ll.scale_row : 0;
-        dma4(a.k_scale + sbase + srow, st + SL::KS);
-        dma4(a.v_scale + sbase + srow, st + SL::VS);
+        dma4_nt(a.k_scale + sbase + srow, st + SL::KS);
+        dma4_nt(a.v_scale + sbase + srow, st + SL::VS);
         // lane i brings the scale of query (i / 8) % QL, head i % 8 (q_scale [B][QL][Hq])
         const int qi = QL == 1 ? 0 : (threadIdx.x >> 3) & (QL - 1);
         dma4(a.q_scale + ((size_t)(d.b * QL + qi) * a.Hq + (size_t)d.h * kGroup) + (threadIdx.x & 7), st + SL::QS);

@@ -114,6 +114,15 @@ __device__ inline void dma16(const void* g, lds_char* l) {
 __device__ inline void dma4(const void* g, lds_char* l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
 }
+// The same with the non-temporal hint (cache policy NT): for data read once,
+// such as a decode step's K/V pages.  A global->LDS stream of 512 MiB reads at
+// about 6.9 TB/s with it against 6.0 TB/s without, on MI355X.
+__device__ inline void dma16_nt(const void* g, lds_char* l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 2);
+}
+__device__ inline void dma4_nt(const void* g, lds_char* l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 2);
+}
 
 // LDS accesses to the ring are written as small asm blocks that complete
 // before returning (s_waitcnt lgkmcnt(0)).  The compiler does not see them as
