@@ -272,9 +272,10 @@ def mtp_bench(args):
     rows = []
     for name in ("tp8_share", "skewed", "fp8"):
         w = wl.WORKLOADS[name]
-        P = args.workgroups or w.num_workgroups or lbsa.default_workgroups(0, w.kv_dtype)
         row = {"workload": name, "kv_dtype": w.kv_dtype, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads}
         for ql in (1, 2):
+            P = args.workgroups or w.num_workgroups or lbsa.default_workgroups(0, w.kv_dtype, ql)
+            row[f"q{ql}_P"] = P
             b = wl.make_batch(name, tail="normal", device="cuda:0", q_len=ql)
             sl = [int(x) for x in b["seqlens"].cpu()]
             ab = alg_bytes(sl, b["num_heads"], b["num_kv_heads"], 128, w.kv_dtype, q_len=ql)

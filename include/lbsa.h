@@ -123,12 +123,13 @@ const char* lbsa_status_string(int status);
 /* Library ABI version (major * 100 + minor). */
 int lbsa_version(void);
 
-/* Default number of persistent workgroups on `device` for `kv_dtype`:
- * compute units x resident workgroups per CU of the split kernel (occupancy
- * query), so every bin is resident at once; the split kernels of q_len 1 and
- * 2 have the same occupancy (one workgroup per CU, bound by LDS).  Writes
- * *out_P. */
-int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_P);
+/* Default number of persistent workgroups on `device` for `kv_dtype` and
+ * q_len (1 or 2): compute units x resident workgroups per CU of that split
+ * kernel (occupancy query), so every bin is resident at once.  On MI355X the
+ * fp8 q_len 1 kernel holds two workgroups per CU (P = 512), the others one
+ * (P = 256); a task map planned for one P serves either q_len, and a larger
+ * P than resident runs in waves of workgroups.  Writes *out_P. */
+int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t q_len, int32_t* out_P);
 
 /* Layout and size of the task map for (batch, num_kv_heads, P). */
 int lbsa_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32_t P,

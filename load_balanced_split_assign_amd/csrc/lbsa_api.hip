@@ -102,10 +102,10 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 201; }
+LBSA_API int lbsa_version(void) { return 202; }
 
-LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_P) {
-    if (!out_P || (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3))
+LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t q_len, int32_t* out_P) {
+    if (!out_P || (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3) || q_len < 1 || q_len > kMaxQLen)
         return LBSA_ERR_INVALID_ARGUMENT;
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
@@ -114,7 +114,7 @@ LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t* out_
     if (hipGetDevice(&cur) != hipSuccess) return LBSA_ERR_HIP;
     if (cur != device && hipSetDevice(device) != hipSuccess) return LBSA_ERR_HIP;
     int per_cu = 0;
-    const hipError_t e = split_occupancy(kv_dtype == LBSA_KV_FP8_E4M3, 1, &per_cu);
+    const hipError_t e = split_occupancy(kv_dtype == LBSA_KV_FP8_E4M3, q_len, &per_cu);
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess || per_cu <= 0 || cus <= 0) return LBSA_ERR_HIP;
     *out_P = cus * per_cu;

@@ -62,8 +62,14 @@ constexpr float kSlack = 8.0f;   // log2 headroom of the lazy running max (p <= 
 // register load (which the compiler turns into a wait for the whole ring).
 // ---------------------------------------------------------------------------
 // QL = query tokens per request (1, or 2 for multi-token decode): the Q codes
-// of a descriptor are QL x 8 heads x 128 B, and with QL = 2 the fp8 ring is
-// one stage shallower to leave LDS for the larger merge slots.
+// of a descriptor are QL x 8 heads x 128 B.  fp8 with QL = 1 runs a 2-stage
+// ring, so a workgroup needs under 80 KiB of LDS and two share a CU: an fp8
+// tile carries half the bytes of a bf16 one for the same work, and the second
+// workgroup computes while the first waits on its LDS round trips and loads
+// (16% faster than one workgroup per CU with a 5-stage ring).  bf16 keeps one
+// workgroup per CU and 3 stages (two per CU, with half-size bins and twice
+// the descriptors, was slower on the small batches and no faster on the
+// large ones).  With QL = 2 the merge slots are larger: one workgroup per CU.
 template <bool FP8, int QL = 1> struct Stage {
     static constexpr int kRow = FP8 ? 128 : 256;        // bytes of one K/V row
     static constexpr int K = 0;
@@ -78,7 +84,7 @@ template <bool FP8, int QL = 1> struct Stage {
     // descriptor's first tile; the waits count only the fixed ones, which can
     // only make them wait for a little more than the stage)
     static constexpr int LOADS = 2 * KV_LOADS + (FP8 ? 3 : 0);
-    static constexpr int STAGES = FP8 ? (QL == 1 ? 5 : 4) : 3;   // ring depth: STAGES - 1 tiles in flight
+    static constexpr int STAGES = FP8 ? (QL == 1 ? 2 : 4) : 3;   // ring depth: STAGES - 1 tiles in flight
 };
 static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt range");
 static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
@@ -119,7 +125,7 @@ template <bool FP8, int QL> constexpr int stage_array_bytes(int u) {
 template <bool FP8, int QL> constexpr int smem_bytes() {
     return kWaves * Stage<FP8, QL>::BYTES * Stage<FP8, QL>::STAGES + Slot<QL>::kBytes;
 }
-static_assert(smem_bytes<false, 1>() <= 160 * 1024 && smem_bytes<true, 1>() <= 160 * 1024, "LDS");
+static_assert(smem_bytes<false, 1>() <= 160 * 1024 && smem_bytes<true, 1>() <= 80 * 1024, "LDS (fp8: 2 per CU)");
 static_assert(smem_bytes<false, 2>() <= 160 * 1024 && smem_bytes<true, 2>() <= 160 * 1024, "LDS");
 
 // One descriptor of the tile stream (all fields wave-uniform).

@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
         L.lbsa_status_string.argtypes = [ctypes.c_int]
         L.lbsa_status_string.restype = ctypes.c_char_p
         L.lbsa_version.restype = ctypes.c_int
-        L.lbsa_default_workgroups.argtypes = [ctypes.c_int, i32, ctypes.POINTER(i32)]
+        L.lbsa_default_workgroups.argtypes = [ctypes.c_int, i32, i32, ctypes.POINTER(i32)]
         L.lbsa_task_map_layout_get.argtypes = [i32, i32, i32, ctypes.POINTER(_MapLayout)]
         L.lbsa_task_map_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.lbsa_workspace_layout_get.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(_WsLayout)]
@@ -109,10 +109,10 @@ def kv_dtype_code(kv_dtype: str) -> int:
 # sizes and layouts
 # ---------------------------------------------------------------------------
 
-def default_workgroups(device: int = 0, kv_dtype: str = "bf16") -> int:
+def default_workgroups(device: int = 0, kv_dtype: str = "bf16", q_len: int = 1) -> int:
     out = ctypes.c_int32()
     _check("lbsa_default_workgroups", lib().lbsa_default_workgroups(int(device), kv_dtype_code(kv_dtype),
-                                                                    ctypes.byref(out)))
+                                                                    int(q_len), ctypes.byref(out)))
     return int(out.value)
 
 

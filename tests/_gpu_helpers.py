@@ -37,7 +37,7 @@ def workgroups(batch, P=None) -> int:
         return int(P)
     if batch.get("num_workgroups"):
         return int(batch["num_workgroups"])
-    return lbsa.default_workgroups(0, batch["kv_dtype"])
+    return lbsa.default_workgroups(0, batch["kv_dtype"], batch.get("q_len", 1))
 
 
 def plan(batch, P, F=0):

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 201
+    assert lbsa.lib().lbsa_version() == 202
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -177,3 +177,11 @@ def test_router_rejects_bad_arguments_on_host():
     assert L.lbsa_router_gemm(None, vp(512), vp(1024), 4, 192, 4096, vp(2048), vp(4096), 1 << 30, None) == \
         lbsa.ERR_INVALID_ARGUMENT
     assert L.lbsa_router_gemm(None, None, None, 0, 192, 4096, None, None, 0, None) == lbsa.OK       # nothing to do
+
+def test_default_workgroups_rejects_bad_arguments_on_host():
+    L = lbsa.lib()
+    out = ctypes.c_int32()
+    assert L.lbsa_default_workgroups(0, 0, 3, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT     # q_len 3
+    assert L.lbsa_default_workgroups(0, 0, 0, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_default_workgroups(0, 7, 1, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT     # kv dtype
+    assert L.lbsa_default_workgroups(0, 0, 1, None) == lbsa.ERR_INVALID_ARGUMENT

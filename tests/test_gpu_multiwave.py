@@ -18,7 +18,7 @@ HDR_RESERVED = (14, 15)
 
 
 def resident(batch):
-    return lbsa.default_workgroups(0, batch["kv_dtype"])
+    return lbsa.default_workgroups(0, batch["kv_dtype"], batch.get("q_len", 1))
 
 
 def reserved_words(tm):
