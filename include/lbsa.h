@@ -126,7 +126,7 @@ int lbsa_version(void);
 /* Default number of persistent workgroups on `device` for `kv_dtype` and
  * q_len (1 or 2): compute units x resident workgroups per CU of that split
  * kernel (occupancy query), so every bin is resident at once.  On MI355X the
- * fp8 q_len 1 kernel holds two workgroups per CU (P = 512), the others one
+ * fp8 kernels hold two workgroups per CU (P = 512), the bf16 ones one
  * (P = 256); a task map planned for one P serves either q_len, and a larger
  * P than resident runs in waves of workgroups.  Writes *out_P. */
 int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t q_len, int32_t* out_P);

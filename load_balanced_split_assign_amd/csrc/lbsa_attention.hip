@@ -62,14 +62,15 @@ constexpr float kSlack = 8.0f;   // log2 headroom of the lazy running max (p <= 
 // register load (which the compiler turns into a wait for the whole ring).
 // ---------------------------------------------------------------------------
 // QL = query tokens per request (1, or 2 for multi-token decode): the Q codes
-// of a descriptor are QL x 8 heads x 128 B.  fp8 with QL = 1 runs a 2-stage
-// ring, so a workgroup needs under 80 KiB of LDS and two share a CU: an fp8
-// tile carries half the bytes of a bf16 one for the same work, and the second
-// workgroup computes while the first waits on its LDS round trips and loads
-// (16% faster than one workgroup per CU with a 5-stage ring).  bf16 keeps one
+// of a descriptor are QL x 8 heads x 128 B.  fp8 runs a 2-stage ring, so a
+// workgroup needs under 80 KiB of LDS and two share a CU: an fp8 tile carries
+// half the bytes of a bf16 one for the same work, and the second workgroup
+// computes while the first waits on its LDS round trips and loads (16% faster
+// than one workgroup per CU with a 5-stage ring).  With QL = 2 its merge slot
+// holds half of O at a time (two passes of 64 dims) to fit.  bf16 keeps one
 // workgroup per CU and 3 stages (two per CU, with half-size bins and twice
 // the descriptors, was slower on the small batches and no faster on the
-// large ones).  With QL = 2 the merge slots are larger: one workgroup per CU.
+// large ones).
 template <bool FP8, int QL = 1> struct Stage {
     static constexpr int kRow = FP8 ? 128 : 256;        // bytes of one K/V row
     static constexpr int K = 0;
@@ -84,7 +85,7 @@ template <bool FP8, int QL = 1> struct Stage {
     // descriptor's first tile; the waits count only the fixed ones, which can
     // only make them wait for a little more than the stage)
     static constexpr int LOADS = 2 * KV_LOADS + (FP8 ? 3 : 0);
-    static constexpr int STAGES = FP8 ? (QL == 1 ? 2 : 4) : 3;   // ring depth: STAGES - 1 tiles in flight
+    static constexpr int STAGES = FP8 ? 2 : 3;   // ring depth: STAGES - 1 tiles in flight
 };
 static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt range");
 static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
@@ -100,18 +101,21 @@ template <bool FP8> __device__ inline int swz_vrow(int row) { return FP8 ? swz<t
 // asynchronous load an LDS read depends on (distinct underlying objects) and
 // does not fall back to waiting for all of them.
 //
-// Each wave has one slot (Slot<QL>::kWave bytes) that holds its bf16 copy of the
+// Each wave has one slot (Slot::kWave bytes) that holds its bf16 copy of the
 // fp8 V slice during a tile and its (O, m, l, flag) for the merge at the end of
 // a descriptor; the two uses of a slot never overlap in time (program order
 // within the wave, and the merge's closing barrier before any wave's next
-// tile), so for fp8 they share the memory.
+// tile), so for fp8 they share the memory.  fp8 with QL = 2 merges O in two
+// passes of 64 dims (the slot holds half of O).
 constexpr int kVbWave = 16 * 256;                                      // 16 V rows as bf16
-template <int QL> struct Slot {
+template <bool FP8, int QL> struct Slot {
     static constexpr int kRows = kGroup * QL;                          // query rows of a descriptor
-    static constexpr int kMerge = (kRows * kHeadDim + 2 * kRows + 4) * 4;   // O, m, l, flag per wave
-    static constexpr int kWave = QL == 1 ? 17 * 256 : 33 * 256;        // >= both uses, 256-aligned
+    static constexpr int kPasses = (FP8 && QL == 2) ? 2 : 1;           // passes over the 128 dims
+    static constexpr int kDims = kHeadDim / kPasses;                   // dims of O per pass
+    static constexpr int kMerge = (kRows * kDims + 2 * kRows + 4) * 4;   // O (one pass), m, l, flag per wave
+    static constexpr int kUse = FP8 && kVbWave > kMerge ? kVbWave : kMerge;
+    static constexpr int kWave = (kUse + 255) / 256 * 256;             // 256-aligned
     static constexpr int kBytes = kWaves * kWave;
-    static_assert(kWave >= kMerge && kWave >= kVbWave, "wave slot");
 };
 constexpr int kMaxStages = 6;
 template <bool FP8> struct Smem {
@@ -123,10 +127,10 @@ template <bool FP8, int QL> constexpr int stage_array_bytes(int u) {
     return u < Stage<FP8, QL>::STAGES ? kWaves * Stage<FP8, QL>::BYTES : 16;
 }
 template <bool FP8, int QL> constexpr int smem_bytes() {
-    return kWaves * Stage<FP8, QL>::BYTES * Stage<FP8, QL>::STAGES + Slot<QL>::kBytes;
+    return kWaves * Stage<FP8, QL>::BYTES * Stage<FP8, QL>::STAGES + Slot<FP8, QL>::kBytes;
 }
 static_assert(smem_bytes<false, 1>() <= 160 * 1024 && smem_bytes<true, 1>() <= 80 * 1024, "LDS (fp8: 2 per CU)");
-static_assert(smem_bytes<false, 2>() <= 160 * 1024 && smem_bytes<true, 2>() <= 160 * 1024, "LDS");
+static_assert(smem_bytes<false, 2>() <= 160 * 1024 && smem_bytes<true, 2>() <= 80 * 1024, "LDS (fp8: 2 per CU)");
 
 // One descriptor of the tile stream (all fields wave-uniform).
 struct Desc {
@@ -347,63 +351,70 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
 // a row of that query with nothing accumulated means bad data (NaN); an
 // earlier query may legitimately see none of the descriptor's tokens, which
 // gives an empty partial (O = 0, LSE = -inf) that the combine skips.
-template <int QL>
+template <bool FP8, int QL>
 __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const WaveState& ws, bool bad,
                                    int64_t slot, int w, int lane, int r, int g) {
-    constexpr int R = Slot<QL>::kRows;
+    using SM = Slot<FP8, QL>;
+    constexpr int R = SM::kRows, DW = SM::kDims, DBP = DW / 16;   // rows, dims and d blocks per pass
     float lsum = ws.l;
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
-    lds_float* o_w = reinterpret_cast<lds_float*>(merge + w * Slot<QL>::kWave);
-    if (r < R) {
+    lds_float* o_w = reinterpret_cast<lds_float*>(merge + w * SM::kWave);
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(o_w + r * kHeadDim + 16 * db + 4 * g) = ws.acc[db];
-        if (g == 0) {
-            o_w[R * kHeadDim + r] = ws.m;
-            o_w[R * kHeadDim + R + r] = lsum;
+    for (int dp = 0; dp < SM::kPasses; ++dp) {
+        if (r < R) {
+#pragma unroll
+            for (int e = 0; e < DBP; ++e)
+                *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(o_w + r * DW + 16 * e + 4 * g) =
+                    ws.acc[DBP * dp + e];
+            if (dp == 0 && g == 0) {
+                o_w[R * DW + r] = ws.m;
+                o_w[R * DW + R + r] = lsum;
+            }
         }
+        if (dp == 0 && lane == 0) o_w[R * DW + 2 * R] = bad ? 1.f : 0.f;
+        lds_barrier();
+#pragma unroll
+        for (int pass = 0; pass < QL; ++pass) {
+            const int tid = threadIdx.x;
+            const int hh = kGroup * pass + (tid >> 5), d4 = (tid & 31) * 4;
+            if (d4 < DW) {
+                float M = kNegInf;
+                bool any_bad = false;
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * SM::kWave);
+                    M = fmaxf(M, ow[R * DW + hh]);
+                    any_bad |= ow[R * DW + 2 * R] != 0.f;
+                }
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                float lt = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * SM::kWave);
+                    const float mw = ow[R * DW + hh];
+                    const float sw = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
+                    lt += sw * ow[R * DW + R + hh];
+                    o += sw * *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(ow + hh * DW + d4);
+                }
+                float lse;
+                if (!any_bad && M == kNegInf && pass < QL - 1) {
+                    o = f32x4{0.f, 0.f, 0.f, 0.f};                 // an earlier query that sees none of it
+                    lse = kNegInf;
+                } else if (any_bad || M == kNegInf || !(lt > 0.f)) {
+                    const float nan = __builtin_nanf("");
+                    o = f32x4{nan, nan, nan, nan};
+                    lse = nan;
+                } else {
+                    o *= 1.f / lt;
+                    lse = (M + __builtin_log2f(lt)) * kLn2;
+                }
+                *reinterpret_cast<f32x4*>(a.part_o + ((size_t)slot * R + hh) * kHeadDim + DW * dp + d4) = o;
+                if (dp == 0 && (tid & 31) == 0) a.part_lse[(size_t)slot * R + hh] = lse;
+            }
+        }
+        lds_barrier();   // the merge area is reused by the next pass / descriptor
     }
-    if (lane == 0) o_w[R * kHeadDim + 2 * R] = bad ? 1.f : 0.f;
-    lds_barrier();
-#pragma unroll
-    for (int pass = 0; pass < QL; ++pass) {
-        const int tid = threadIdx.x;
-        const int hh = kGroup * pass + (tid >> 5), d4 = (tid & 31) * 4;
-        float M = kNegInf;
-        bool any_bad = false;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * Slot<QL>::kWave);
-            M = fmaxf(M, ow[R * kHeadDim + hh]);
-            any_bad |= ow[R * kHeadDim + 2 * R] != 0.f;
-        }
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        float lt = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const lds_float* ow = reinterpret_cast<const lds_float*>(merge + ww * Slot<QL>::kWave);
-            const float mw = ow[R * kHeadDim + hh];
-            const float sw = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
-            lt += sw * ow[R * kHeadDim + R + hh];
-            o += sw * *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(ow + hh * kHeadDim + d4);
-        }
-        float lse;
-        if (!any_bad && M == kNegInf && pass < QL - 1) {
-            o = f32x4{0.f, 0.f, 0.f, 0.f};                 // an earlier query that sees none of it
-            lse = kNegInf;
-        } else if (any_bad || M == kNegInf || !(lt > 0.f)) {
-            const float nan = __builtin_nanf("");
-            o = f32x4{nan, nan, nan, nan};
-            lse = nan;
-        } else {
-            o *= 1.f / lt;
-            lse = (M + __builtin_log2f(lt)) * kLn2;
-        }
-        *reinterpret_cast<f32x4*>(a.part_o + ((size_t)slot * R + hh) * kHeadDim + d4) = o;
-        if ((tid & 31) == 0) a.part_lse[(size_t)slot * R + hh] = lse;
-    }
-    lds_barrier();   // the merge area is reused by the next descriptor
 }
 
 // Descriptor sources of the tile stream.
@@ -501,7 +512,7 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     // column r's query sees the request's tokens below L - (QL - 1 - query)
     const int lim_off = (QL == 1 ? 0 : min(r >> 3, QL - 1)) - (QL - 1);
     auto stage = [&](int u) -> lds_char* { return sm.stage[u] + w * SL::BYTES; };
-    lds_char* vb = sm.vb + w * Slot<QL>::kWave;
+    lds_char* vb = sm.vb + w * Slot<FP8, QL>::kWave;
     LaneLoads<FP8> ll;
     ll.init(a.Hkv, w, lane);
 
@@ -548,7 +559,7 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
                 }
                 bad |= (bad_bits >> u) & 1u;
                 tile_compute<FP8, QL>(stage(u), vb, q, sl2, 64 * cc.t, cc.d.L + lim_off, w, r, g, ws);
-                if (cc.t + 1 == cc.d.t1) finish_desc<QL>(a, sm.merge, ws, bad, cc.d.slot, w, lane, r, g);
+                if (cc.t + 1 == cc.d.t1) finish_desc<FP8, QL>(a, sm.merge, ws, bad, cc.d.slot, w, lane, r, g);
                 cc.next();
             }
         }
@@ -563,7 +574,7 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     __shared__ __attribute__((aligned(16))) char s3[stage_array_bytes<FP8, QL>(3)]; \
     __shared__ __attribute__((aligned(16))) char s4[stage_array_bytes<FP8, QL>(4)]; \
     __shared__ __attribute__((aligned(16))) char s5[stage_array_bytes<FP8, QL>(5)]; \
-    __shared__ __attribute__((aligned(16))) char sslot[Slot<QL>::kBytes];           \
+    __shared__ __attribute__((aligned(16))) char sslot[Slot<FP8, QL>::kBytes];      \
     Smem<FP8> sm; /* address-space casts to LDS */                             \
     sm.stage[0] = (lds_char*)s0;                                               \
     sm.stage[1] = (lds_char*)s1;                                               \
@@ -620,7 +631,7 @@ __global__ __launch_bounds__(kSplitThreads) void static_kernel(AttnArgs a) {
     const int t0 = (int)((int64_t)split * n / S);
     const int t1 = (int)((int64_t)(split + 1) * n / S);
     if (t1 <= t0) {   // empty split: weight 0 in the combine (NaN if the length was invalid)
-        constexpr int R = Slot<QL>::kRows;
+        constexpr int R = Slot<FP8, QL>::kRows;
         const int tid = threadIdx.x;
 #pragma unroll
         for (int pass = 0; pass < QL; ++pass) {
