@@ -123,6 +123,19 @@ const char* lbsa_status_string(int status);
 /* Library ABI version (major * 100 + minor). */
 int lbsa_version(void);
 
+/* Kernel timing hook.  Arms two caller-owned HIP events (hipEvent_t, created
+ * with timing enabled) for the next kernel that this host thread launches
+ * through the library: that launch goes through hipExtLaunchKernel, which
+ * records `start_event` when the kernel begins and `stop_event` when it ends,
+ * so hipEventElapsedTime(start, stop) is the kernel's own duration, without the
+ * dispatch gap that a marker recorded between launches adds.  An entry point
+ * that launches several kernels stamps its first one.  The hook stays armed
+ * until a kernel is launched (an entry point that rejects its arguments
+ * launches nothing and leaves it armed); NULL, NULL disarms it.  Either event
+ * may be NULL.  The library never creates, waits on or destroys the events.
+ * Thread-local; returns LBSA_OK. */
+int lbsa_time_next_kernel(void* start_event, void* stop_event);
+
 /* Default number of persistent workgroups on `device` for `kv_dtype` and
  * q_len (1 or 2): compute units x resident workgroups per CU of that split
  * kernel (occupancy query), so every bin is resident at once.  On MI355X the

@@ -102,7 +102,24 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 202; }
+LBSA_API int lbsa_version(void) { return 203; }
+
+namespace {
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+}
+
+KernelEvents lbsa::take_kernel_events() {
+    const KernelEvents e{t_ev_start, t_ev_stop};
+    t_ev_start = nullptr;
+    t_ev_stop = nullptr;
+    return e;
+}
+
+LBSA_API int lbsa_time_next_kernel(void* start_event, void* stop_event) {
+    t_ev_start = static_cast<hipEvent_t>(start_event);
+    t_ev_stop = static_cast<hipEvent_t>(stop_event);
+    return LBSA_OK;
+}
 
 LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t q_len, int32_t* out_P) {
     if (!out_P || (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3) || q_len < 1 || q_len > kMaxQLen)

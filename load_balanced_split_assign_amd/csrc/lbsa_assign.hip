@@ -226,9 +226,8 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
 hipError_t launch_assign(const int32_t* seqlens, int B, int Hq, int Hkv, int P, int F,
                          int max_pages, void* map, hipStream_t stream) {
     const size_t lds = sizeof(int) * (2 * (size_t)B + 1 + (size_t)Hkv * B + 1);
-    hipLaunchKernelGGL(assign_kernel, dim3(1), dim3(kAssignThreads), lds, stream, seqlens, B, Hq,
-                       Hkv, P, F, max_pages, static_cast<uint8_t*>(map));
-    return hipGetLastError();
+    return launch(assign_kernel, dim3(1), dim3(kAssignThreads), (uint32_t)lds, stream, seqlens, B, Hq, Hkv, P, F,
+                  max_pages, static_cast<uint8_t*>(map));
 }
 
 }  // namespace lbsa

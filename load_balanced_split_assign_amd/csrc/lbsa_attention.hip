@@ -776,33 +776,25 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
 
 hipError_t launch_split(const AttnArgs& a, bool fp8, hipStream_t stream) {
     const dim3 grid(a.P), block(kSplitThreads);
-    if (a.QL == 2) {
-        if (fp8) hipLaunchKernelGGL((split_kernel<true, 2>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((split_kernel<false, 2>), grid, block, 0, stream, a);
-    } else {
-        if (fp8) hipLaunchKernelGGL((split_kernel<true, 1>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((split_kernel<false, 1>), grid, block, 0, stream, a);
-    }
-    return hipGetLastError();
+    if (a.QL == 2)
+        return fp8 ? launch(split_kernel<true, 2>, grid, block, 0, stream, a)
+                   : launch(split_kernel<false, 2>, grid, block, 0, stream, a);
+    return fp8 ? launch(split_kernel<true, 1>, grid, block, 0, stream, a)
+               : launch(split_kernel<false, 1>, grid, block, 0, stream, a);
 }
 
 hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
     const dim3 grid((unsigned)((long long)a.P * a.B * a.Hkv)), block(kSplitThreads);
-    if (a.QL == 2) {
-        if (fp8) hipLaunchKernelGGL((static_kernel<true, 2>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((static_kernel<false, 2>), grid, block, 0, stream, a);
-    } else {
-        if (fp8) hipLaunchKernelGGL((static_kernel<true, 1>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((static_kernel<false, 1>), grid, block, 0, stream, a);
-    }
-    return hipGetLastError();
+    if (a.QL == 2)
+        return fp8 ? launch(static_kernel<true, 2>, grid, block, 0, stream, a)
+                   : launch(static_kernel<false, 2>, grid, block, 0, stream, a);
+    return fp8 ? launch(static_kernel<true, 1>, grid, block, 0, stream, a)
+               : launch(static_kernel<false, 1>, grid, block, 0, stream, a);
 }
 
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream) {
     const long long grid = (long long)a.B * a.QL * a.Hq;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a,
-                       static_mode ? 1 : 0);
-    return hipGetLastError();
+    return launch(combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a, static_mode ? 1 : 0);
 }
 
 hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu) {

@@ -1,6 +1,7 @@
 // Internal declarations shared by the HIP translation units of liblbsa.so.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -18,6 +19,26 @@ constexpr int kCombineThreads = 256;
 constexpr int kMaxAssignLdsWords = 16384;  // (B + 1) + (Hkv*B + 1) + B int32 in 64 KiB
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Events armed by lbsa_time_next_kernel for the next launch on this host
+// thread; taking them disarms the hook.
+struct KernelEvents {
+    hipEvent_t start, stop;
+};
+KernelEvents take_kernel_events();
+
+// Every kernel of the library is launched here: through hipExtLaunchKernelGGL,
+// which stamps the armed events at the kernel's own start and end, when the
+// timing hook is armed, else as a plain launch.
+template <class F, class... Args>
+inline hipError_t launch(F kernel, dim3 grid, dim3 block, uint32_t lds_bytes, hipStream_t stream, Args... args) {
+    const KernelEvents ev = take_kernel_events();
+    if (ev.start != nullptr || ev.stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, ev.start, ev.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
+    return hipGetLastError();
+}
 
 // Byte offsets of the task-map arrays for (B, Hkv, P).
 struct MapLayout {

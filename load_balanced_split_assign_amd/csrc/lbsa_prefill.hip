@@ -324,8 +324,7 @@ hipError_t launch_cb(PrefillArgs a, hipStream_t stream) {
     constexpr int kPosBlock = kWaves * 2 * CB;
     a.qblocks = (a.QL + kPosBlock - 1) / kPosBlock;
     const long long grid = (long long)a.qblocks * a.B * a.Hkv;
-    hipLaunchKernelGGL((prefill_kernel<CB>), dim3((unsigned)grid), dim3(kSplitThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch(prefill_kernel<CB>, dim3((unsigned)grid), dim3(kSplitThreads), 0, stream, a);
 }
 
 }  // namespace

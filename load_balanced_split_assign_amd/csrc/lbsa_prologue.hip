@@ -278,11 +278,8 @@ __global__ __launch_bounds__(kPrologueThreads) void prologue_kernel(PrologueArgs
 
 template <int K>
 hipError_t launch_k(const PrologueArgs& a, bool fp8, unsigned grid, hipStream_t stream) {
-    if (fp8)
-        hipLaunchKernelGGL((prologue_kernel<K, true>), dim3(grid), dim3(kPrologueThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((prologue_kernel<K, false>), dim3(grid), dim3(kPrologueThreads), 0, stream, a);
-    return hipGetLastError();
+    return fp8 ? launch(prologue_kernel<K, true>, dim3(grid), dim3(kPrologueThreads), 0, stream, a)
+               : launch(prologue_kernel<K, false>, dim3(grid), dim3(kPrologueThreads), 0, stream, a);
 }
 
 }  // namespace

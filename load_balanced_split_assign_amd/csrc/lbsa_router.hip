@@ -363,9 +363,8 @@ RouterPlan router_plan(int M, int N, int K) {
 hipError_t launch_router_split(const float* w, void* hi, void* lo, int N, int K, hipStream_t stream) {
     const long long n8 = (long long)N * K / 8;
     if (n8 == 0) return hipSuccess;
-    hipLaunchKernelGGL(split_weights_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, w,
-                       static_cast<uint16_t*>(hi), static_cast<uint16_t*>(lo), n8, K);
-    return hipGetLastError();
+    return launch(split_weights_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, w,
+                  static_cast<uint16_t*>(hi), static_cast<uint16_t*>(lo), n8, K);
 }
 
 hipError_t launch_router_gemm(const void* x, const void* w_hi, const void* w_lo, int M, int N, int K, float* out,
@@ -382,23 +381,22 @@ hipError_t launch_router_gemm(const void* x, const void* w_hi, const void* w_lo,
     a.K = K;
     a.S = p.S;
     a.tiles_n = p.tiles_n;
+    hipError_t e;
     if (p.tile) {
         a.tiles = p.tiles_n * ceil_div(M, kTileRows);
         const long long grid = 8 % p.S == 0 ? 8LL * ceil_div(a.tiles, 8 / p.S) : (long long)a.tiles * p.S;
-        hipLaunchKernelGGL(router_tile_kernel, dim3((unsigned)grid), dim3(64 * kTileWaves), 0, stream, a);
+        e = launch(router_tile_kernel, dim3((unsigned)grid), dim3(64 * kTileWaves), 0, stream, a);
     } else {
         a.tiles = p.tiles_n * ceil_div(M, 16 * p.MT);
         const dim3 grid(p.tiles_n, a.tiles / p.tiles_n, p.S);
-        if (p.MT == 1) hipLaunchKernelGGL((router_thin_kernel<1>), grid, dim3(64 * kThinWaves), 0, stream, a);
-        else if (p.MT == 2) hipLaunchKernelGGL((router_thin_kernel<2>), grid, dim3(64 * kThinWaves), 0, stream, a);
-        else hipLaunchKernelGGL((router_thin_kernel<4>), grid, dim3(64 * kThinWaves), 0, stream, a);
+        if (p.MT == 1) e = launch(router_thin_kernel<1>, grid, dim3(64 * kThinWaves), 0, stream, a);
+        else if (p.MT == 2) e = launch(router_thin_kernel<2>, grid, dim3(64 * kThinWaves), 0, stream, a);
+        else e = launch(router_thin_kernel<4>, grid, dim3(64 * kThinWaves), 0, stream, a);
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.S == 1) return e;
     const long long n4 = (long long)M * N / 4;
-    hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                       static_cast<const f32x4*>(workspace), reinterpret_cast<f32x4*>(out), n4, p.S);
-    return hipGetLastError();
+    return launch(router_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                  static_cast<const f32x4*>(workspace), reinterpret_cast<f32x4*>(out), n4, p.S);
 }
 
 }  // namespace lbsa

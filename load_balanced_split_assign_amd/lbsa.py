@@ -72,13 +72,14 @@ def lib() -> ctypes.CDLL:
         L.lbsa_router_split_weights.argtypes = [vp, i32, i32, vp, vp, vp]
         L.lbsa_router_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.lbsa_router_gemm.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+        L.lbsa_time_next_kernel.argtypes = [vp, vp]
         L.lbsa_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, f32, i32, i32, i32, i32, i32, i32,
                                     vp, vp, vp, vp, vp, vp, i64, vp]
         for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes", "lbsa_prologue",
                    "lbsa_workspace_layout_get", "lbsa_workspace_bytes", "lbsa_static_workspace_bytes",
                    "lbsa_plan", "lbsa_decode", "lbsa_decode_split", "lbsa_decode_combine",
                    "lbsa_decode_static", "lbsa_prefill", "lbsa_router_split_weights",
-                   "lbsa_router_workspace_bytes", "lbsa_router_gemm"):
+                   "lbsa_router_workspace_bytes", "lbsa_router_gemm", "lbsa_time_next_kernel"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -108,6 +109,22 @@ def kv_dtype_code(kv_dtype: str) -> int:
 # ---------------------------------------------------------------------------
 # sizes and layouts
 # ---------------------------------------------------------------------------
+
+def time_next_kernel(start=None, stop=None) -> None:
+    """Arm the library's kernel timing hook: the next kernel that this thread
+    launches through the library stamps `start` and `stop` (torch.cuda.Event
+    with enable_timing=True) at its own start and end, so
+    start.elapsed_time(stop) is that kernel's duration without a dispatch
+    gap.  torch creates an event at its first record: an event never recorded
+    is recorded once here, on the current stream, to create it."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:
+            ev.record()
+        return ctypes.c_void_p(ev.cuda_event)
+    _check("lbsa_time_next_kernel", lib().lbsa_time_next_kernel(handle(start), handle(stop)))
+
 
 def default_workgroups(device: int = 0, kv_dtype: str = "bf16", q_len: int = 1) -> int:
     out = ctypes.c_int32()
