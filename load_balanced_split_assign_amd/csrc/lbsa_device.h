@@ -252,6 +252,49 @@ __device__ inline void lds_read_tile_bf16(uint4 (&k)[4], s16x4 (&va)[8], const u
     va[7] = __builtin_bit_cast(s16x4, o7);
 }
 
+// The same reads at a compile-time byte offset OFF from every address (the
+// DS offset field), so that a caller's lane addresses stay fixed across ring
+// stages and sub-tiles.
+template <int OFF>
+__device__ inline void lds_read_tile_bf16_at(uint4 (&k)[4], s16x4 (&va)[8], const uint32_t (&ka)[4],
+                                             const uint32_t (&va_addr)[8]) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+    typedef short s16x4_v __attribute__((ext_vector_type(4)));
+    u32x4 k0, k1, k2, k3;
+    s16x4_v o0, o1, o2, o3, o4, o5, o6, o7;
+    __asm__ volatile(
+        "ds_read_b128 %0, %12 offset:%24\n\t"
+        "ds_read_b128 %1, %13 offset:%24\n\t"
+        "ds_read_b128 %2, %14 offset:%24\n\t"
+        "ds_read_b128 %3, %15 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %10, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %11, %23 offset:%24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3), "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3), "=&v"(o4),
+          "=&v"(o5), "=&v"(o6), "=&v"(o7)
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va_addr[0]), "v"(va_addr[1]), "v"(va_addr[2]),
+          "v"(va_addr[3]), "v"(va_addr[4]), "v"(va_addr[5]), "v"(va_addr[6]), "v"(va_addr[7]), "i"(OFF)
+        : "memory");
+    k[0] = __builtin_bit_cast(uint4, k0);
+    k[1] = __builtin_bit_cast(uint4, k1);
+    k[2] = __builtin_bit_cast(uint4, k2);
+    k[3] = __builtin_bit_cast(uint4, k3);
+    va[0] = __builtin_bit_cast(s16x4, o0);
+    va[1] = __builtin_bit_cast(s16x4, o1);
+    va[2] = __builtin_bit_cast(s16x4, o2);
+    va[3] = __builtin_bit_cast(s16x4, o3);
+    va[4] = __builtin_bit_cast(s16x4, o4);
+    va[5] = __builtin_bit_cast(s16x4, o5);
+    va[6] = __builtin_bit_cast(s16x4, o6);
+    va[7] = __builtin_bit_cast(s16x4, o7);
+}
+
 // fp8 tile: the two K chunks, the two V chunks and the k/v scales in one block.
 __device__ inline void lds_read_tile_fp8(uint4 (&o)[6], const uint32_t (&addr)[6]) {
     u32x4 o0, o1, o2, o3, o4, o5;

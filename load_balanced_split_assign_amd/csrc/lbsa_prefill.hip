@@ -25,11 +25,15 @@
 //     per wave or a deeper ring, which both leave one wave per SIMD.
 //   * Per 32-token half-tile: S^T = K Q^T (MFMA 16x16x32 bf16, one chain of 4
 //     per 16 tokens and block; K is read from LDS once per wave for all CB
-//     blocks), a masked online softmax per column in the exp2 domain with a
-//     lazy running max, then O^T += V^T P^T with MFMA 16x16x32 bf16 over the
-//     32 tokens (V^T through ds_read_b64_tr_b16, P straight from the S^T
-//     accumulators).  Tiles below every column's limit skip the mask: the
-//     softmax scale folds into one fma before each exp2.
+//     blocks), an online softmax per column in the exp2 domain with a lazy
+//     running max, then O^T += V^T P^T with MFMA 16x16x32 bf16 over the 32
+//     tokens (V^T through ds_read_b64_tr_b16, P straight from the S^T
+//     accumulators).  Half-tiles that reach a column's limit set the scores
+//     above it to -inf; the softmax scale folds into one fma before each
+//     exp2; the denominator is one more MFMA with an all-ones A operand over
+//     the same bf16 P as the numerator.
+//   * The tile loop is unrolled over the 2 ring stages and the 2 halves, so
+//     each LDS read is a per-lane base address plus an immediate offset.
 //   * Built with the MFMA accumulators in VGPRs (-amdgpu-mfma-vgpr-form): the
 //     rescale of the online softmax multiplies them with VALU instructions,
 //     which cannot address AGPRs, and the AGPR form copied every accumulator
@@ -39,6 +43,8 @@
 //     see the most tiles (longest first), and the blocks of one (request, KV
 //     head) share an XCD whenever batch * Hkv is a multiple of 8, so their K/V
 //     reuse stays in one L2.
+#include <type_traits>
+
 #include "lbsa_device.h"
 
 namespace lbsa {
@@ -111,13 +117,14 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
     const int ntiles = (lim_blk + kTile - 1) / kTile;
 
     f32x4 acc[CB][8];
-    float m[CB], l[CB];
+    float m[CB];
+    f32x4 l[CB];        // column sums of P, from an MFMA with an all-ones A: every element holds it
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[cb] = kNegInf;
-        l[cb] = 0.f;
+        l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     bool bad = !len_ok;
 
@@ -171,132 +178,133 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
         };
         for (int u = 0; u < kPfStages - 1; ++u) issue(min(u, ntiles - 1), ring + u * kPfStageBytes);
 
-        // every tile issues the same number of loads (past the end the last tile
-        // is loaded again into a stage nobody reads), so one wait count fits all
-        int u = 0;                                                  // stage of tile k
-        for (int k = 0; k < ntiles; ++k) {
-            {
-                wait_vmcnt<(kPfStages - 2) * kPfLoads>();             // this wave's rows of tile k
-                lds_barrier();                                      // everyone's rows; stage of k-1 free
-                const int un = u == 0 ? kPfStages - 1 : u - 1;      // = (k + kPfStages - 1) % kPfStages
-                issue(min(k + kPfStages - 1, ntiles - 1), ring + un * kPfStageBytes);
-                const lds_char* st = ring + u * kPfStageBytes;
-                u = u == kPfStages - 1 ? 0 : u + 1;
-                if (kTile * k >= lim_wave) continue;                // nothing of it is visible here
-#pragma unroll 1
-                for (int half = 0; half < 2; ++half) {
-                    // ---- K (A operand of S^T) and V^T reads of 32 tokens, two
-                    // 16-token sub-tiles, shared by all CB blocks
-                    uint4 kk[2][4];
-                    s16x4 va[2][8];
+        // lane parts of the ring read addresses (stage 0, first 16 rows); the
+        // stage and the 16-row sub-tile are the reads' immediate offsets
+        uint32_t ka[4], vaddr[8];
+        {
+            const uint32_t rb = lds_addr(ring);
 #pragma unroll
-                    for (int sub = 0; sub < 2; ++sub) {
-                        const int row = 32 * half + 16 * sub + r;
-                        uint32_t ka[4], vaddr[8];
+            for (int ks = 0; ks < 4; ++ks) ka[ks] = rb + r * kPfRow + 16 * ((g + 4 * ks) ^ r);
+            const int vrow = 4 * g + (r >> 2);
+            const uint32_t vr = rb + kPfHalf + vrow * kPfRow + 8 * (r & 1);
 #pragma unroll
-                        for (int ks = 0; ks < 4; ++ks) ka[ks] = lds_addr(st + row * kPfRow + 16 * ((g + 4 * ks) ^ r));
-                        const int vrow = 4 * g + (r >> 2);
-                        const uint32_t vr =
-                            lds_addr(st + kPfHalf + (32 * half + 16 * sub + vrow) * kPfRow + 8 * (r & 1));
-#pragma unroll
-                        for (int db = 0; db < 8; ++db)
-                            vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_v(vrow));
-                        lds_read_tile_bf16(kk[sub], va[sub], ka, vaddr);
-                    }
+            for (int db = 0; db < 8; ++db)
+                vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_v(vrow));
+        }
 
-                    // ---- S^T = K Q^T: s[cb][sub][i] is token 32 half + 16 sub + 4 g + i
-                    f32x4 s[CB][2];
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-                        for (int sub = 0; sub < 2; ++sub) {
-                            f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
-                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][1]), as_bf16x8(q[cb][1]), sa, 0, 0, 0);
-                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
-                            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][3]), as_bf16x8(q[cb][3]), sa, 0, 0, 0);
-                            s[cb][sub] = sa;
-                        }
-                    }
+        const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+        // 32 tokens [t32, t32 + 32) of the tile whose rows start at ring byte OFF
+        auto half_step = [&](auto off_c, int t32) {
+            constexpr int OFF = decltype(off_c)::value;
+            // ---- K (A operand of S^T) and V^T reads of 32 tokens, two 16-token
+            // sub-tiles, shared by all CB blocks
+            uint4 kk[2][4];
+            s16x4 va[2][8];
+            lds_read_tile_bf16_at<OFF>(kk[0], va[0], ka, vaddr);
+            lds_read_tile_bf16_at<OFF + 16 * kPfRow>(kk[1], va[1], ka, vaddr);
 
-                    // ---- online softmax over the 8 scores of this lane per block.
-                    // Tiles below every live column's limit need no mask: the scale
-                    // folds into one fma before the exp2, and the block maximum is
-                    // the scale times the raw maximum (the scale is positive).
-                    const int tok = kTile * k + 32 * half + 4 * g;
-                    const bool masked = kTile * k + 32 * half + 31 >= lim_lo;     // uniform
-                    float lmax[CB];
-                    bool need = false;
-                    if (masked) {
+            // ---- S^T = K Q^T: s[cb][sub][i] is token t32 + 16 sub + 4 g + i
+            f32x4 s[CB][2];
 #pragma unroll
-                        for (int cb = 0; cb < CB; ++cb) {
-                            float mx = kNegInf;
+            for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-                            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) {
-                                    const float x = (tok + 16 * sub + i < lim[cb]) ? s[cb][sub][i] * a.scale_log2 : kNegInf;
-                                    s[cb][sub][i] = x;
-                                    mx = fmaxf(mx, x);
-                                }
-                            lmax[cb] = mx;
-                            need |= mx > m[cb] + kPfSlack;
-                        }
-                    } else {
-#pragma unroll
-                        for (int cb = 0; cb < CB; ++cb) {
-                            const float mx = fmaxf(fmaxf(fmaxf(s[cb][0][0], s[cb][0][1]), fmaxf(s[cb][0][2], s[cb][0][3])),
-                                                   fmaxf(fmaxf(s[cb][1][0], s[cb][1][1]), fmaxf(s[cb][1][2], s[cb][1][3])));
-                            lmax[cb] = mx * a.scale_log2;
-                            need |= lmax[cb] > m[cb] + kPfSlack;
-                        }
-                    }
-                    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                        // a score above a column's reference: new reference = max over
-                        // the column's 32 tokens (0 rescale for a column still fully masked)
-#pragma unroll
-                        for (int cb = 0; cb < CB; ++cb) {
-                            float mt = fmaxf(lmax[cb], __shfl_xor(lmax[cb], 16, 64));
-                            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-                            const float m_new = fmaxf(m[cb], mt);
-                            const float alpha = m[cb] == kNegInf ? 0.f : exp2_fast(m[cb] - m_new);
-                            l[cb] *= alpha;
-#pragma unroll
-                            for (int db = 0; db < 8; ++db) acc[cb][db] *= alpha;
-                            m[cb] = m_new;
-                        }
-                    }
-
-                    // ---- P and O^T += V^T P^T with MFMA 16x16x32: k = the 32 tokens,
-                    // lane group g holding tokens 4g .. 4g + 3 of both sub-tiles, in the
-                    // same order in the V^T operand (two transposed reads) and in P
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        const float mref = m[cb] == kNegInf ? 0.f : m[cb];
-                        float p[8];
-                        if (masked) {
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) p[j] = exp2_fast(s[cb][j >> 2][j & 3] - mref);
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(s[cb][j >> 2][j & 3], a.scale_log2, -mref));
-                        }
-                        l[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-                        const bf16x8 pb = __builtin_bit_cast(
-                            bf16x8, make_uint4(bf16x2_pack(p[0], p[1]), bf16x2_pack(p[2], p[3]),
-                                               bf16x2_pack(p[4], p[5]), bf16x2_pack(p[6], p[7])));
-#pragma unroll
-                        for (int db = 0; db < 8; ++db) {
-                            const bf16x8 vt = __builtin_bit_cast(
-                                bf16x8, make_uint4(__builtin_bit_cast(uint2, va[0][db]).x,
-                                                   __builtin_bit_cast(uint2, va[0][db]).y,
-                                                   __builtin_bit_cast(uint2, va[1][db]).x,
-                                                   __builtin_bit_cast(uint2, va[1][db]).y));
-                            acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, acc[cb][db], 0, 0, 0);
-                        }
-                    }
+                for (int sub = 0; sub < 2; ++sub) {
+                    f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
+                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][1]), as_bf16x8(q[cb][1]), sa, 0, 0, 0);
+                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
+                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][3]), as_bf16x8(q[cb][3]), sa, 0, 0, 0);
+                    s[cb][sub] = sa;
                 }
             }
+
+            // ---- online softmax over the 8 scores of this lane per block.  Half-
+            // tiles that reach a live column's limit get -inf above it (raw score
+            // domain); then one path for all: the scale folds into the fma before
+            // each exp2 (exp2(-inf) = 0), and the block maximum is the scale times
+            // the raw maximum (the scale is positive).  The maximum propagates NaN
+            // (v_maximum3), which needs no canonicalising of the MFMA results.
+            const int tok = t32 + 4 * g;
+            if (t32 + 31 >= lim_lo) {                                     // uniform
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (tok + 16 * sub + i >= lim[cb]) s[cb][sub][i] = kNegInf;
+            }
+            float lmax[CB];
+            bool need = false;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const f32x4 x0 = s[cb][0], x1 = s[cb][1];
+                float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x0[0], x0[1]), x0[2]);
+                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, x0[3]), x1[0]);
+                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, x1[1]), x1[2]);
+                mx = __builtin_elementwise_maximum(mx, x1[3]);
+                lmax[cb] = mx * a.scale_log2;
+                need |= lmax[cb] > m[cb] + kPfSlack;
+            }
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                // a score above a column's reference: new reference = max over
+                // the column's 32 tokens (0 rescale for a column still fully masked)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    float mt = fmaxf(lmax[cb], __shfl_xor(lmax[cb], 16, 64));
+                    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                    const float m_new = fmaxf(m[cb], mt);
+                    const float alpha = m[cb] == kNegInf ? 0.f : exp2_fast(m[cb] - m_new);
+                    l[cb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) acc[cb][db] *= alpha;
+                    m[cb] = m_new;
+                }
+            }
+
+            // ---- P and O^T += V^T P^T with MFMA 16x16x32: k = the 32 tokens,
+            // lane group g holding tokens 4g .. 4g + 3 of both sub-tiles, in the
+            // same order in the V^T operand (two transposed reads) and in P
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const float mref = m[cb] == kNegInf ? 0.f : m[cb];
+                float p[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(s[cb][j >> 2][j & 3], a.scale_log2, -mref));
+                const bf16x8 pb = __builtin_bit_cast(
+                    bf16x8, make_uint4(bf16x2_pack(p[0], p[1]), bf16x2_pack(p[2], p[3]),
+                                       bf16x2_pack(p[4], p[5]), bf16x2_pack(p[6], p[7])));
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const bf16x8 vt = __builtin_bit_cast(
+                        bf16x8, make_uint4(__builtin_bit_cast(uint2, va[0][db]).x,
+                                           __builtin_bit_cast(uint2, va[0][db]).y,
+                                           __builtin_bit_cast(uint2, va[1][db]).x,
+                                           __builtin_bit_cast(uint2, va[1][db]).y));
+                    acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, acc[cb][db], 0, 0, 0);
+                }
+                // the softmax denominator over the same bf16 P as the numerator
+                l[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, l[cb], 0, 0, 0);
+            }
+        };
+
+        // tile k sits in ring stage U = k % 2.  Every tile issues the same number
+        // of loads (past the end the last tile is loaded again into a stage
+        // nobody reads), so one wait count fits all
+        auto tile_step = [&](auto u_c, int k) {
+            constexpr int U = decltype(u_c)::value;
+            wait_vmcnt<(kPfStages - 2) * kPfLoads>();                 // this wave's rows of tile k
+            lds_barrier();                                          // everyone's rows; stage of k-1 free
+            issue(min(k + kPfStages - 1, ntiles - 1), ring + (1 - U) * kPfStageBytes);
+            if (kTile * k >= lim_wave) return;                      // nothing of it is visible here
+            half_step(std::integral_constant<int, U * kPfStageBytes>{}, kTile * k);
+            if (kTile * k + 32 < lim_wave)
+                half_step(std::integral_constant<int, U * kPfStageBytes + 32 * kPfRow>{}, kTile * k + 32);
+        };
+        static_assert(kPfStages == 2, "tile_step alternates two stages");
+        for (int k = 0; k < ntiles; k += 2) {
+            tile_step(std::integral_constant<int, 0>{}, k);
+            if (k + 1 < ntiles) tile_step(std::integral_constant<int, 1>{}, k + 1);
         }
         wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
     }
@@ -304,9 +312,7 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
     // ---- normalise and store: lane (g, r) holds dims 16 db + 4 g .. + 3 of column r
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        float lt = l[cb];
-        lt += __shfl_xor(lt, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
+        const float lt = l[cb][0];
         if (pos[cb] >= a.QL) continue;
         float inv = lt > 0.f ? 1.f / lt : 0.f;            // a query that sees nothing: zeros
         if (bad) inv = __builtin_nanf("");
