@@ -483,7 +483,8 @@ struct Cursor {
 
 // Issue the next tile of the load cursor into ring stage `slot` (and, when it
 // is the first tile of a descriptor, that descriptor's Q into qslot).  Past
-// the last tile it re-issues the last tile into a stage that is never read, so
+// the last tile it issues the same number of loads, of row 0 of the last page
+// only (one cache line per row chunk), into a stage that is never read, so
 // every step issues the same number of ring loads.  `page` is the page id of
 // the cursor's tile, loaded one step ahead; the next one is fetched here.
 template <bool FP8, int QL, class Src>
@@ -492,8 +493,11 @@ __device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, C
                                   int slot, int w, int r, int g) {
     const bool ok = page >= 0 && page < a.num_pages;
     bad_bits = (bad_bits & ~(1u << slot)) | ((uint32_t)(!ok) << slot);
-    if (issued < ntiles && lc.t == lc.d.t0) load_q<FP8, QL>(a, lc.d, r, g, qslot, st);
-    issue_tile<FP8, QL>(a, ll, st, ok ? page : 0, lc.d, lc.t, w);
+    const bool real = issued < ntiles;
+    if (real && lc.t == lc.d.t0) load_q<FP8, QL>(a, lc.d, r, g, qslot, st);
+    Desc d = lc.d;
+    if (!real) d.L = 0;     // past the end: every row counts as dead, so only row 0 of the page is read
+    issue_tile<FP8, QL>(a, ll, st, ok ? page : 0, d, lc.t, w);
     if (++issued < ntiles) {
         lc.next();
         page = (int64_t)uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
