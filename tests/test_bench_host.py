@@ -1,0 +1,65 @@
+"""Host logic of bench.py (no GPU): the algorithmic-byte count behind every
+GB/s figure, the timing summaries, and the rule that keeps PMC traffic tied to
+the kernel source and workload it was measured on."""
+import json
+import os
+
+import pytest
+
+import bench
+
+
+def test_alg_bytes_tiny_bf16_by_hand():
+    # lengths 37, 64, 1000, 4097 -> 1 + 1 + 16 + 65 = 83 tiles; 8 query / 1 KV head
+    ab = bench.alg_bytes([37, 64, 1000, 4097], 8, 1, 128, "bf16")
+    live = 37 + 64 + 1000 + 4097
+    assert ab["kv"] == live * 1 * (2 * 128 * 2)            # K and V rows, bf16
+    assert ab["q"] == 4 * 8 * 128 * 2
+    assert ab["out"] == 4 * 8 * 128 * 2
+    assert ab["meta"] == 4 * 83 + 4 * 4                     # page-table words + lengths
+    assert ab["layer"] == 2678108                           # 2.68 MB
+    assert ab["split"] == ab["layer"] - ab["out"]
+
+
+def test_alg_bytes_fp8_counts_scales_and_query_tokens():
+    ab = bench.alg_bytes([64, 65], 64, 8, 128, "fp8", q_len=2)
+    assert ab["kv"] == (64 + 65) * 8 * (2 * 128 * 1 + 8)    # e4m3 K and V plus their fp32 scales
+    assert ab["q"] == 2 * 2 * 64 * (128 + 4)                # e4m3 Q plus its scale, per query token
+    assert ab["out"] == 2 * 2 * 64 * 128 * 2                # bf16 out, per query token
+    assert ab["meta"] == 4 * (1 + 2) + 4 * 2
+
+
+def test_alg_bytes_empty_request_moves_no_kv():
+    ab = bench.alg_bytes([0, 64], 8, 1, 128, "bf16")
+    assert ab["kv"] == 64 * 512
+    assert ab["meta"] == 4 * 1 + 4 * 2
+
+
+def test_summarize_statistics():
+    s = bench.summarize([5.0, 1.0, 3.0, 2.0, 4.0, 6.0, 7.0, 8.0, 9.0, 10.0])
+    assert s["min"] == 1.0 and s["median"] == 5.5 and s["mean"] == 5.5
+    assert s["p90"] == 9.0                                  # 9th of 10 sorted values
+
+
+def test_traffic_reported_only_for_its_source_and_workload(tmp_path, monkeypatch):
+    rec = {"source_sha256": bench.source_sha(bench.SPLIT_SRC), "kernel": "split_kernel", "workload": "tp8_share",
+           "bytes_per_launch": 123}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.traffic_from_profile("tp8_share") == 123
+    assert bench.traffic_from_profile("skewed") is None
+    rec["source_sha256"] = "0" * 64
+    f.write_text(json.dumps(rec))
+    assert bench.traffic_from_profile("tp8_share") is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
+    assert bench.traffic_from_profile("tp8_share") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
