@@ -187,6 +187,26 @@ def time_steps_graph(path, steps, warmup, flush):
     return [1000.0 * a.elapsed_time(b) for a, b in ev]
 
 
+def graph_bench(args):
+    """The step (assign + split + combine) launched eagerly against the same
+    three launches captured in one HIP graph and replayed, on tp8_share, the
+    smallest Table 3 mix and skewed (medians, us)."""
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    flush = make_flush(args.flush)
+    rows = []
+    for name in ("tp8_share", "t3_64x0.5K", "skewed"):
+        b = gpu_batch(name)
+        path = Path(b, lbsa.default_workgroups(0, b["kv_dtype"]))
+        eager = summarize(time_steps(path, args.steps, args.warmup, flush)["step"])["median"]
+        graph = summarize(time_steps_graph(path, args.steps, args.warmup, flush))["median"]
+        rows.append({"workload": name, "eager_step_us": round(eager, 2), "graph_step_us": round(graph, 2)})
+        del b, path
+        torch.cuda.empty_cache()
+    print(json.dumps({"graph_vs_eager": rows, "unit": "us", "flush": args.flush}), flush=True)
+
+
 def time_static(batch, S, steps, warmup, flush):
     import torch
 
@@ -652,6 +672,8 @@ def main():
                     help="instead of the headline line: 2-query-token decode vs 1-token decode")
     ap.add_argument("--prologue", action="store_true",
                     help="instead of the headline line: the fused QK-Norm/RoPE/KV-write prologue")
+    ap.add_argument("--graph", action="store_true",
+                    help="eager launches against one HIP graph of assign + split + combine (step times)")
     ap.add_argument("--table3", action="store_true",
                     help="instead of the headline line: the six fp8 KV-length mixes, dynamic vs static")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -693,6 +715,9 @@ def main():
         return
     if args.router:
         router_bench(args)
+        return
+    if args.graph:
+        graph_bench(args)
         return
 
     name = args.workload
