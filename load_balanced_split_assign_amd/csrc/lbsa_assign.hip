@@ -26,6 +26,20 @@
 namespace lbsa {
 namespace {
 
+// Inclusive scan of one int per lane over the 64-lane wave with DPP moves:
+// shifts by 1, 2, 4 and 8 inside each 16-lane row (lanes without a source
+// add 0), then lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into
+// rows 2 and 3.
+__device__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);    // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);    // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
 // Block-wide exclusive scan of one int per thread; returns the prefix and
 // writes the block total to *total (all threads).  `red` holds one int per
 // wave and must not be reused by the next scan (one barrier per scan).
@@ -33,12 +47,7 @@ __device__ int block_exclusive_scan(int v, int* red, int* total) {
     constexpr int kWaves = kAssignThreads / 64;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_inclusive_scan(v);
     if (lane == 63) red[wave] = x;
     __syncthreads();
     int before = 0, all = 0;
