@@ -2,18 +2,24 @@
 """Decode-attention benchmark on one MI355X.
 
 A step is one pass of the whole path over one synthetic batch already resident
-in HBM: assign (task map) + persistent split + combine.  Before every timed
-step a 512 MiB buffer is streamed through so neither L2 nor the 256 MB Infinity
-Cache still holds K/V from the previous step.  HIP events on the launch stream
-bracket each step (one pair, nothing between the kernels) and, in a second
-pass, each kernel; the flush stays outside them.  The default flush reads the buffer
-(a reduction), so the caches hold clean lines and no write-back competes with
-the timed kernels.
+in HBM: assign (task map) + persistent split + combine.  A layer is split +
+combine with the step's task map reused, as every layer of the model reuses
+it.  Before every timed step or layer a 512 MiB buffer is streamed through so
+neither L2 nor the 256 MB Infinity Cache still holds K/V from the previous one.
+HIP events on the launch stream bracket each step (one pair, nothing between
+the kernels), each layer (one pair), and -- through the library's timing hook --
+each kernel's own start and end.  The default flush reads the buffer (a
+reduction), so the caches hold clean lines and no write-back competes with the
+timed kernels.
 
-Prints ONE JSON line.  value = achieved HBM GB/s of a step (algorithmic bytes /
-mean step time); the line also carries us_per_step, the per-kernel times, the
-split kernel's roofline, the static split-KV comparison on the skewed batch,
-and the CPU oracle timed on the host.
+Prints ONE JSON line.  The headline workload is the long-context batch (8
+requests of 64K-256K tokens, 64/8 heads, bf16: the largest single-GPU
+configuration).  value = achieved HBM GB/s of a layer (algorithmic bytes /
+mean layer time); ms_per_step is the whole step with assign.  The line also
+carries the per-kernel times, the split kernel's roofline, a block with the
+same figures for the other configurations (one GPU's TP8 share, the skewed
+batch, the fp8 batch, the minimum-work-floor case), the static split-KV
+comparison on the skewed batch, and the CPU oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -63,7 +69,9 @@ def source_sha(path):
 
 
 class Path:
-    """Preallocated buffers for one batch; step() enqueues assign+split+combine."""
+    """Preallocated buffers for one batch: assign() enqueues the assign kernel,
+    layer() the split + combine of lbsa_decode (single-chunk segments written by
+    the split kernel), split()/combine() the two halves as separate calls."""
 
     def __init__(self, batch, P, F=0):
         import torch
@@ -81,6 +89,12 @@ class Path:
         b = self.b
         self.lbsa.plan(b["seqlens"], b["num_heads"], b["num_kv_heads"], b["max_pages"], self.P, self.F,
                        task_map=self.tm)
+
+    def layer(self):
+        b = self.b
+        self.lbsa.decode(b["q"], b["k_cache"], b["v_cache"], b["page_table"], self.tm, self.P, b["softmax_scale"],
+                         q_scale=b["q_scale"], k_scale=b["k_scale"], v_scale=b["v_scale"], workspace=self.ws,
+                         out=self.out)
 
     def split(self):
         b = self.b
@@ -108,60 +122,52 @@ def make_flush(mode):
     return lambda i: None
 
 
+def _pairs(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
 def time_steps(path, steps, warmup, flush):
-    """Per-step event times (us).  Pass 1 brackets each whole step with one
-    event pair (no markers between the kernels, as in real use); pass 2 adds an
-    event between the kernels for the per-kernel split (each marker adds a
-    dispatch gap of its own, so pass 2's sum exceeds pass 1's step); pass 3
-    arms the library's timing hook so that each kernel stamps its own start and
-    end (`*_kernel`: the kernels' durations, as rocprofv3 reports them)."""
+    """Per-step times (us) in three passes, the flush outside every event pair:
+    `step` = assign + split + combine under one pair (as a decode step runs);
+    `layer` = split + combine under one pair with the map built beforehand (as
+    every layer runs); `*_kernel` = each kernel's own start-to-end stamps from the
+    library's timing hook (no marker packets between the launches, so no added
+    dispatch gaps: the durations rocprofv3 reports)."""
     import torch
 
     from load_balanced_split_assign_amd import lbsa
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         flush(i)
-        path.assign(); path.split(); path.combine()
+        path.assign(); path.layer()
     torch.cuda.synchronize()
-    whole = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    whole = _pairs(steps)
     for i in range(steps):
         flush(i)
         whole[i][0].record(stream)
-        path.assign(); path.split(); path.combine()
+        path.assign(); path.layer()
         whole[i][1].record(stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    lay = _pairs(steps)
+    path.assign()
     for i in range(steps):
         flush(i)
-        e = ev[i]
-        e[0].record(stream)
-        path.assign()
-        e[1].record(stream)
-        path.split()
-        e[2].record(stream)
-        path.combine()
-        e[3].record(stream)
-    # pass 3: the library's timing hook stamps each kernel's own start and end
-    # (no marker packets between the launches, so no added dispatch gaps)
-    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        lay[i][0].record(stream)
+        path.layer()
+        lay[i][1].record(stream)
+    kev = [_pairs(3) for _ in range(steps)]
     for e in kev:
-        for x in e:
-            x.record(stream)        # torch creates an event at its first record
+        for a, b in e:
+            a.record(stream); b.record(stream)      # torch creates an event at its first record
     torch.cuda.synchronize()
     for i in range(steps):
         flush(i)
-        e = kev[i]
-        lbsa.time_next_kernel(e[0], e[1])
-        path.assign()
-        lbsa.time_next_kernel(e[2], e[3])
-        path.split()
-        lbsa.time_next_kernel(e[4], e[5])
-        path.combine()
+        lbsa.time_next_kernels(kev[i])              # assign, then the split and the combine of decode
+        path.assign(); path.layer()
     torch.cuda.synchronize()
-    us = lambda a, b: [1000.0 * ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)]  # noqa: E731
-    kus = lambda a: [1000.0 * kev[i][a].elapsed_time(kev[i][a + 1]) for i in range(steps)]  # noqa: E731
-    return {"assign": us(0, 1), "split": us(1, 2), "combine": us(2, 3), "layer": us(1, 3),
-            "step_markers": us(0, 3), "step": [1000.0 * a.elapsed_time(b) for a, b in whole],
-            "assign_kernel": kus(0), "split_kernel": kus(2), "combine_kernel": kus(4)}
+    us = lambda ps: [1000.0 * a.elapsed_time(b) for a, b in ps]  # noqa: E731
+    return {"step": us(whole), "layer": us(lay), "assign_kernel": us([e[0] for e in kev]),
+            "split_kernel": us([e[1] for e in kev]), "combine_kernel": us([e[2] for e in kev])}
 
 
 def time_steps_graph(path, steps, warmup, flush):
@@ -171,7 +177,7 @@ def time_steps_graph(path, steps, warmup, flush):
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        path.assign(); path.split(); path.combine()
+        path.assign(); path.layer()
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         flush(i)
@@ -207,7 +213,9 @@ def graph_bench(args):
     print(json.dumps({"graph_vs_eager": rows, "unit": "us", "flush": args.flush}), flush=True)
 
 
-def time_static(batch, S, steps, warmup, flush):
+def time_static(batch, S, steps, warmup, flush, stamps=False):
+    """Static split-KV (split + fixed-S combine) under one event pair per call;
+    with stamps=True also each kernel's own start/end (summaries in us)."""
     import torch
 
     from load_balanced_split_assign_amd import lbsa
@@ -223,35 +231,47 @@ def time_static(batch, S, steps, warmup, flush):
     for i in range(warmup):
         flush(i)
         run()
-    times = []
+    torch.cuda.synchronize()
+    ev = _pairs(steps)
     for i in range(steps):
         flush(i)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+        ev[i][0].record(stream)
         run()
-        b.record(stream)
+        ev[i][1].record(stream)
+    res = summarize([1000.0 * a.elapsed_time(b) for a, b in ev])
+    if stamps:
+        kev = [_pairs(2) for _ in range(steps)]
+        for e in kev:
+            for a, b in e:
+                a.record(stream); b.record(stream)
         torch.cuda.synchronize()
-        times.append(1000.0 * a.elapsed_time(b))
-    return summarize(times)
+        for i in range(steps):
+            flush(i)
+            lbsa.time_next_kernels(kev[i])
+            run()
+        torch.cuda.synchronize()
+        res["split_kernel"] = statistics.fmean(1000.0 * e[0][0].elapsed_time(e[0][1]) for e in kev)
+        res["combine_kernel"] = statistics.fmean(1000.0 * e[1][0].elapsed_time(e[1][1]) for e in kev)
+    torch.cuda.synchronize()
+    return res
 
 
 def time_layer(path, steps, warmup, flush, with_assign=False):
-    """Event time (us) of split + combine (plus assign if asked) with one event
-    pair around them, as a layer (or a step) runs in use."""
+    """Event time (us) of split + combine (lbsa_decode; plus assign if asked) with
+    one event pair around them, as a layer (or a step) runs in use."""
     import torch
     stream = torch.cuda.current_stream()
 
     def run():
         if with_assign:
             path.assign()
-        path.split()
-        path.combine()
+        path.layer()
     path.assign()            # the map the layers reuse
     for i in range(warmup):
         flush(i)
         run()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = _pairs(steps)
     for i in range(steps):
         flush(i)
         ev[i][0].record(stream)
@@ -273,7 +293,8 @@ def static_sweep(batch, P, steps, warmup, flush, splits=(1, 2, 4, 8, 16, 32, 64)
 def table3(args):
     """The six KV-length mixes of the vLLM post's Table 3 (fp8 KV, 8 query heads /
     1 KV head): dynamic (map reused: split + combine; and with assign) against
-    the static split-KV kernel."""
+    the static split-KV kernel at the heuristic S and at the best S of a sweep,
+    each with its kernels' own start/end stamps."""
     import torch
 
     from load_balanced_split_assign_amd import lbsa
@@ -287,14 +308,23 @@ def table3(args):
         sl = [int(x) for x in b["seqlens"].cpu()]
         ab = alg_bytes(sl, b["num_heads"], b["num_kv_heads"], 128, w.kv_dtype)
         path = Path(b, P)
-        layer = time_layer(path, args.steps, args.warmup, flush)["mean"]
-        step = time_layer(path, args.steps, args.warmup, flush, with_assign=True)["mean"]
+        t = {k: summarize(v)["mean"] for k, v in time_steps(path, args.steps, args.warmup, flush).items()}
+        m = lbsa.read_task_map(path.tm, b["B"], b["num_kv_heads"], P)
         heur, heur_t, best, sweep = static_sweep(b, P, max(10, args.steps // 2), 3, flush)
+        st = time_static(b, best, max(10, args.steps // 2), 3, flush, stamps=True)
+        layer = t["layer"]
         rows.append({"mix": name[3:], "batch": b["B"], "live_tokens": sum(sl), "alg_bytes": ab["layer"],
-                     "dynamic_layer_us": round(layer, 2), "dynamic_step_us": round(step, 2),
+                     "K": m["K"], "Ndesc": m["Ndesc"], "single_chunk_segments": int((m["seg_num_chunks"] == 1).sum()),
+                     "dynamic_layer_us": round(layer, 2), "dynamic_step_us": round(t["step"], 2),
+                     "dynamic_split_kernel_us": round(t["split_kernel"], 2),
+                     "dynamic_combine_kernel_us": round(t["combine_kernel"], 2),
+                     "assign_kernel_us": round(t["assign_kernel"], 2),
                      "layer_GBps": round(ab["layer"] / layer / 1e3, 1),
                      "static_heuristic_S": heur, "static_heuristic_us": round(heur_t, 2),
                      "static_best_S": best, "static_best_us": round(sweep[best], 2),
+                     "static_best_split_kernel_us": round(st["split_kernel"], 2),
+                     "static_best_combine_kernel_us": round(st["combine_kernel"], 2),
+                     "static_sweep_us": {str(k): round(v, 2) for k, v in sweep.items()},
                      "speedup_vs_static_best": round(sweep[best] / layer, 3),
                      "speedup_vs_static_heuristic": round(heur_t / layer, 3)})
         del b, path
@@ -612,11 +642,19 @@ def _pmc_rows(run_dir, counter):
     return [(k, v) for _, k, v in rows]
 
 
+def _load_traffic():
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    rec = json.load(open(TRAFFIC_FILE))
+    return rec.get("workloads", {})
+
+
 def write_traffic(fetch_dir, write_dir, workload):
     """HBM bytes per split launch on `workload` = FETCH_SIZE + WRITE_SIZE of the
     split kernel, each scaled by CALIB_BYTES / what the same counter reads for
     the calibration copy (the first device-to-device copy dispatch of a
-    --calib-copy run)."""
+    --calib-copy run).  The file keeps one entry per workload, each stamped with
+    the kernel source it was taken on."""
     rec = {"source_sha256": source_sha(SPLIT_SRC), "kernel": "split_kernel", "workload": workload,
            "calib_bytes": CALIB_BYTES}
     total = 0.0
@@ -631,9 +669,11 @@ def write_traffic(fetch_dir, write_dir, workload):
                     "bytes_per_launch": round(mean_kib * 1024.0 * factor)}
         total += mean_kib * 1024.0 * factor
     rec["bytes_per_launch"] = round(total)
+    entries = _load_traffic()
+    entries[workload] = rec
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump({"kernel": "split_kernel", "workloads": dict(sorted(entries.items()))}, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
 
@@ -641,12 +681,43 @@ def write_traffic(fetch_dir, write_dir, workload):
 def traffic_from_profile(workload):
     """HBM bytes per split launch from committed PMC counters, if they were taken
     on the current kernel source and on this workload (else None)."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    rec = json.load(open(TRAFFIC_FILE))
-    if rec.get("source_sha256") != source_sha(SPLIT_SRC) or rec.get("workload") != workload:
+    rec = _load_traffic().get(workload)
+    if not rec or rec.get("source_sha256") != source_sha(SPLIT_SRC):
         return None
     return rec.get("bytes_per_launch")
+
+
+def measure_workload(name, steps, warmup, flush, workgroups=0):
+    """Step, layer and per-kernel times of one workload; returns (record, batch, path)."""
+    from load_balanced_split_assign_amd import lbsa
+    from load_balanced_split_assign_amd import workload as wl
+    w = wl.WORKLOADS[name]
+    batch = gpu_batch(name)
+    P = workgroups or w.num_workgroups or lbsa.default_workgroups(0, w.kv_dtype)
+    sl = [int(x) for x in batch["seqlens"].cpu()]
+    ab = alg_bytes(sl, batch["num_heads"], batch["num_kv_heads"], 128, w.kv_dtype)
+    path = Path(batch, P)
+    t = time_steps(path, steps, warmup, flush)
+    m = lbsa.read_task_map(path.tm, batch["B"], batch["num_kv_heads"], P)
+    st = {k: summarize(v) for k, v in t.items()}
+    gbs = lambda nbytes, us: nbytes / (us * 1e-6) / 1e9  # noqa: E731
+    layer_us, step_us, split_us = st["layer"]["mean"], st["step"]["mean"], st["split_kernel"]["mean"]
+    single = int((m["seg_num_chunks"] == 1).sum())
+    rec = {"workload": name, "desc": w.note, "batch": batch["B"], "num_heads": batch["num_heads"],
+           "num_kv_heads": batch["num_kv_heads"], "kv_dtype": w.kv_dtype, "seed": w.seed, "live_tokens": sum(sl),
+           "P": P, "T": m["T"], "K": m["K"], "Ndesc": m["Ndesc"], "single_chunk_segments": single,
+           "alg_bytes_layer": ab["layer"], "alg_bytes_split": ab["split"],
+           "t_step_us": round(step_us, 3), "t_layer_us": round(layer_us, 3),
+           "t_assign_kernel_us": round(st["assign_kernel"]["mean"], 3),
+           "t_split_kernel_us": round(split_us, 3), "t_combine_kernel_us": round(st["combine_kernel"]["mean"], 3),
+           "layer_GBps": round(gbs(ab["layer"], layer_us), 1),
+           "pct_of_peak_layer": round(100.0 * gbs(ab["layer"], layer_us) / HBM_PEAK_GBS, 2),
+           "step_GBps": round(gbs(ab["layer"], step_us), 1),
+           "pct_of_peak_step": round(100.0 * gbs(ab["layer"], step_us) / HBM_PEAK_GBS, 2),
+           "split_GBps": round(gbs(ab["split"], split_us), 1),
+           "pct_of_peak_split": round(100.0 * gbs(ab["split"], split_us) / HBM_PEAK_GBS, 2),
+           "partial_bytes": 2 * (m["Ndesc"] - single) * 8 * (128 + 1) * 4}
+    return rec, st, batch, path, ab
 
 
 def main():
@@ -654,7 +725,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="tp8_share")
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline workload alone (no other configs, static sweep or CPU baseline)")
     ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0 = CUs x occupancy)")
     ap.add_argument("--no-static", action="store_true", help="skip the static split-KV comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -722,49 +795,54 @@ def main():
 
     name = args.workload
     w = wl.WORKLOADS[name]
-    batch = gpu_batch(name)
-    P = args.workgroups or w.num_workgroups or lbsa.default_workgroups(0, w.kv_dtype)
-    sl = [int(x) for x in batch["seqlens"].cpu()]
-    ab = alg_bytes(sl, batch["num_heads"], batch["num_kv_heads"], 128, w.kv_dtype)
     flush = make_flush(args.flush)
-
-    path = Path(batch, P)
-    torch.cuda.synchronize()
-    t = time_steps(path, args.steps, args.warmup, flush)
-    m = lbsa.read_task_map(path.tm, batch["B"], batch["num_kv_heads"], P)
-    st = {k: summarize(v) for k, v in t.items()}
-    step_us, split_us = st["step"]["mean"], st["split_kernel"]["mean"]
-    value = ab["layer"] / (step_us * 1e-6) / 1e9
-    layer_us = st["layer"]["mean"]
-    layer_gbs = ab["layer"] / (layer_us * 1e-6) / 1e9
+    head, st, batch, path, ab = measure_workload(name, args.steps, args.warmup, flush, args.workgroups)
+    P = head["P"]
+    layer_us, step_us, split_us = st["layer"]["mean"], st["step"]["mean"], st["split_kernel"]["mean"]
+    value = ab["layer"] / (layer_us * 1e-6) / 1e9
     split_gbs = ab["split"] / (split_us * 1e-6) / 1e9
-    traffic = traffic_from_profile(name)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    dtype = "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 (fp8 MFMA QK^T, bf16 MFMA PV)"
 
     rec = {
         "metric": "decode-attn µs/step + achieved HBM GB/s (% of peak), mixed-length paged KV batch",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(step_us / 1000.0, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 (bf16 MFMA)",
-        "data": "synthetic",
-        "config": {"workload": name, "desc": w.note, "batch": batch["B"], "num_heads": batch["num_heads"],
-                   "num_kv_heads": batch["num_kv_heads"], "head_dim": 128, "page_size": 64,
-                   "kv_dtype": w.kv_dtype, "seed": w.seed, "live_tokens": sum(sl), "P": P, "T": m["T"],
-                   "K": m["K"], "Ndesc": m["Ndesc"]},
-        "us_per_step": round(step_us, 3),
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {k: head[k] for k in ("workload", "desc", "batch", "num_heads", "num_kv_heads", "kv_dtype",
+                                        "seed", "live_tokens", "P", "T", "K", "Ndesc")},
+        "value_is": "layer GB/s = algorithmic bytes / t_layer (split + combine, the step's task map reused)",
+        "us_per_step": round(step_us, 3), "us_per_layer": round(layer_us, 3),
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "layer_GBps": round(layer_gbs, 2), "pct_of_peak_layer": round(100.0 * layer_gbs / HBM_PEAK_GBS, 2),
-        "occupancy": {"workgroups": P, "per_cu": P // 256},
+        "step_GBps": head["step_GBps"], "pct_of_peak_step": head["pct_of_peak_step"],
+        "occupancy": {"workgroups": P, "compute_units": cus, "per_cu": round(P / cus, 3)},
         "times_us": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in st.items()},
         "alg_bytes": ab,
-        "partial_bytes": 2 * m["Ndesc"] * 8 * (128 + 1) * 4,
+        "partial_bytes": head["partial_bytes"],
         "roofline": {"kernel": "split_kernel", "bound": "hbm", "achieved": round(split_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "alg_bytes_per_launch": ab["split"],
-                     "avg_launch_us": round(split_us, 3), "timing": "kernel start/end events (hipExtLaunchKernel)",
-                     "marker_pair_us": round(st["split"]["mean"], 3)},
+                     "traffic": traffic_from_profile(name), "alg_bytes_per_launch": ab["split"],
+                     "avg_launch_us": round(split_us, 3), "workload": name,
+                     "timing": "kernel start/end events (hipExtLaunchKernel), live in this run"},
     }
+    if not args.no_cpu_baseline and not args.only:
+        batch["_tm"] = path.tm                       # the map and output of the last timed layer
+        rec["cpu_baseline"] = cpu_baseline(batch, path.out, P, args.cpu_budget)
+    del batch, path
+    torch.cuda.empty_cache()
 
-    if not args.no_static:
+    if not args.only:
+        configs = []
+        for other in ("tp8_share", "skewed", "fp8", "floor"):
+            if other == name:
+                continue
+            r, _, b2, p2, _ = measure_workload(other, min(args.steps, 50), min(args.warmup, 5), flush)
+            configs.append(r)
+            del b2, p2
+            torch.cuda.empty_cache()
+        rec["configs"] = configs
+
+    if not args.no_static and not args.only:
         sk = gpu_batch("skewed")
         Pk = lbsa.default_workgroups(0, "bf16")
         dyn = time_layer(Path(sk, Pk), 20, 3, flush)
@@ -777,10 +855,7 @@ def main():
             "speedup_vs_static_heuristic": round(heur_t / dyn["mean"], 3),
             "speedup_vs_static_best": round(sweep[best_S] / dyn["mean"], 3)}
         del sk
-
-    if not args.no_cpu_baseline:
-        batch["_tm"] = path.tm
-        rec["cpu_baseline"] = cpu_baseline(batch, path.out, P, args.cpu_budget)
+        torch.cuda.empty_cache()
 
     print(json.dumps(rec), flush=True)
 

@@ -28,9 +28,9 @@
  *     reported as a negative status; nothing is written in that case;
  *   - data errors only visible on the device (a length outside
  *     [0, max_pages_per_seq * 64]) are reported in the task-map header word
- *     LBSA_HDR_ERROR and give an empty map (output rows zero); a page-table
- *     entry outside [0, num_pages) poisons the affected rows with NaN instead
- *     of reading out of bounds;
+ *     LBSA_HDR_ERROR and give an empty map, and a decode with that map writes
+ *     NaN in every output row; a page-table entry outside [0, num_pages)
+ *     poisons the affected rows with NaN instead of reading out of bounds;
  *   - supported shapes: head_dim 128, page_size 64, query-group size
  *     num_heads / num_kv_heads = 8, q_len 1 or 2 query tokens per request.
  *
@@ -123,17 +123,24 @@ const char* lbsa_status_string(int status);
 /* Library ABI version (major * 100 + minor). */
 int lbsa_version(void);
 
-/* Kernel timing hook.  Arms two caller-owned HIP events (hipEvent_t, created
- * with timing enabled) for the next kernel that this host thread launches
- * through the library: that launch goes through hipExtLaunchKernel, which
- * records `start_event` when the kernel begins and `stop_event` when it ends,
- * so hipEventElapsedTime(start, stop) is the kernel's own duration, without the
- * dispatch gap that a marker recorded between launches adds.  An entry point
- * that launches several kernels stamps its first one.  The hook stays armed
- * until a kernel is launched (an entry point that rejects its arguments
- * launches nothing and leaves it armed); NULL, NULL disarms it.  Either event
- * may be NULL.  The library never creates, waits on or destroys the events.
- * Thread-local; returns LBSA_OK. */
+/* Kernel timing hook.  Arms caller-owned HIP events (hipEvent_t, created with
+ * timing enabled) for the next kernels that this host thread launches through
+ * the library: such a launch goes through hipExtLaunchKernel, which records its
+ * start event when the kernel begins and its stop event when it ends, so
+ * hipEventElapsedTime(start, stop) is the kernel's own duration, without the
+ * dispatch gap that a marker recorded between launches adds.
+ *   lbsa_time_next_kernels: the next n launches (0 <= n <= 8) stamp
+ *     (start_events[i], stop_events[i]) in launch order; an entry point that
+ *     launches several kernels (lbsa_decode: split, then combine) uses one pair
+ *     per kernel.  n = 0 disarms.  Either event of a pair may be NULL.
+ *   lbsa_time_next_kernel: the same for one launch; NULL, NULL disarms.
+ * Arming replaces whatever was armed before.  Pairs left over stay armed for
+ * the following launches, except that an entry point which returns without
+ * launching anything (an argument it rejected, nothing to do) disarms the hook,
+ * so no event is ever stamped by an unrelated later launch.  The library never
+ * creates, waits on or destroys the events.  Thread-local; returns LBSA_OK, or
+ * LBSA_ERR_INVALID_ARGUMENT for n outside [0, 8] or NULL arrays with n > 0. */
+int lbsa_time_next_kernels(int32_t n, void* const* start_events, void* const* stop_events);
 int lbsa_time_next_kernel(void* start_event, void* stop_event);
 
 /* Default number of persistent workgroups on `device` for `kv_dtype` and
@@ -188,7 +195,10 @@ int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_heads, int32_
  *   out_d                     bf16 [batch][q_len][num_heads][128]
  * The q/k/v/out dtypes follow kv_dtype: bf16 path = bf16 q, bf16 caches; fp8
  * path = e4m3 q with q_scale, e4m3 caches with k/v scales.  Output is bf16
- * (round to nearest even) in both.
+ * (round to nearest even) in both.  A (kv_head, request) segment served by a
+ * single descriptor needs no merge: the split kernel writes its output rows
+ * itself and the combine leaves them alone, so lbsa_decode writes no partial
+ * for such a segment (lbsa_decode_split, which has no output, writes them all).
  */
 int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                 const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
@@ -198,8 +208,9 @@ int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                 float softmax_scale, const void* task_map_d, size_t task_map_bytes,
                 void* workspace_d, size_t workspace_bytes, void* out_d, void* stream);
 
-/* The split half of lbsa_decode alone: fills the workspace partials (slot d =
- * descriptor d).  Same arguments as lbsa_decode without out_d. */
+/* The split half of lbsa_decode alone: fills the workspace partials of every
+ * descriptor (slot d = descriptor d), single-chunk segments included.  Same
+ * arguments as lbsa_decode without out_d. */
 int lbsa_decode_split(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                       const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
                       int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t q_len,

@@ -80,7 +80,7 @@ DecodeCommon check_decode(const void* q_d, const float* q_scale_d, const void* k
     a.k_scale = k_scale_d;
     a.v_scale = v_scale_d;
     a.page_table = page_table_d;
-    a.num_pages = num_pages;
+    a.num_pages = num_pages > INT32_MAX ? INT32_MAX : (int32_t)num_pages;   // every int32 page id fits
     a.B = batch;
     a.QL = q_len;
     a.Hq = num_heads;
@@ -102,23 +102,55 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 203; }
+LBSA_API int lbsa_version(void) { return 204; }
 
 namespace {
-thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
-}
+// Events armed for the next launches on this host thread, used in order.
+constexpr int kMaxArmed = 8;
+thread_local hipEvent_t t_ev[kMaxArmed][2];
+thread_local int t_armed = 0, t_used = 0;
+thread_local unsigned long long t_launches = 0;   // launches made by this thread
+
+void disarm() { t_armed = t_used = 0; }
+
+// Guards a public entry point: if it returns without launching a kernel (an
+// argument it rejected, or nothing to do), the timing hook is disarmed, so the
+// armed events are never stamped by some later, unrelated launch.
+struct HookGuard {
+    unsigned long long n0 = t_launches;
+    ~HookGuard() {
+        if (t_launches == n0) disarm();
+    }
+};
+}  // namespace
 
 KernelEvents lbsa::take_kernel_events() {
-    const KernelEvents e{t_ev_start, t_ev_stop};
-    t_ev_start = nullptr;
-    t_ev_stop = nullptr;
-    return e;
+    ++t_launches;
+    if (t_used < t_armed) {
+        const KernelEvents e{t_ev[t_used][0], t_ev[t_used][1]};
+        if (++t_used == t_armed) disarm();
+        return e;
+    }
+    return KernelEvents{nullptr, nullptr};
+}
+
+LBSA_API int lbsa_time_next_kernels(int32_t n, void* const* start_events, void* const* stop_events) {
+    if (n < 0 || n > kMaxArmed || (n > 0 && (!start_events || !stop_events))) return LBSA_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < n; ++i) {
+        t_ev[i][0] = static_cast<hipEvent_t>(start_events[i]);
+        t_ev[i][1] = static_cast<hipEvent_t>(stop_events[i]);
+    }
+    t_armed = n;
+    t_used = 0;
+    return LBSA_OK;
 }
 
 LBSA_API int lbsa_time_next_kernel(void* start_event, void* stop_event) {
-    t_ev_start = static_cast<hipEvent_t>(start_event);
-    t_ev_stop = static_cast<hipEvent_t>(stop_event);
-    return LBSA_OK;
+    if (!start_event && !stop_event) {
+        disarm();
+        return LBSA_OK;
+    }
+    return lbsa_time_next_kernels(1, &start_event, &stop_event);
 }
 
 LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t q_len, int32_t* out_P) {
@@ -198,6 +230,7 @@ LBSA_API int lbsa_plan(const int32_t* seqlens_d, int32_t batch, int32_t num_head
                        int32_t num_kv_heads, int32_t page_size, int32_t max_pages_per_seq,
                        int32_t num_workgroups, int32_t min_tiles_per_bin, void* task_map_d,
                        size_t task_map_bytes, void* stream) {
+    HookGuard guard;
     int s = check_shape(batch, num_heads, num_kv_heads, kHeadDim, page_size);
     if (s != LBSA_OK) return s;
     if (!seqlens_d || !task_map_d || max_pages_per_seq <= 0 || num_workgroups <= 0 ||
@@ -249,6 +282,7 @@ LBSA_API int lbsa_decode_split(const void* q_d, const float* q_scale_d, const vo
                                int32_t num_workgroups, float softmax_scale, const void* task_map_d,
                                size_t task_map_bytes, void* workspace_d, size_t workspace_bytes,
                                void* stream) {
+    HookGuard guard;
     DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
                                   kv_dtype, page_table_d, batch, q_len, num_heads, num_kv_heads, head_dim,
                                   page_size, max_pages_per_seq, num_pages, softmax_scale);
@@ -262,6 +296,7 @@ LBSA_API int lbsa_decode_combine(int32_t batch, int32_t q_len, int32_t num_heads
                                  int32_t head_dim, int32_t num_workgroups, const void* task_map_d,
                                  size_t task_map_bytes, const void* workspace_d,
                                  size_t workspace_bytes, void* out_d, void* stream) {
+    HookGuard guard;
     DecodeCommon c{};
     c.status = check_shape(batch, num_heads, num_kv_heads, head_dim, kTile, q_len);
     if (c.status != LBSA_OK) return c.status;
@@ -278,6 +313,18 @@ LBSA_API int lbsa_decode_combine(int32_t batch, int32_t q_len, int32_t num_heads
     return hip_status(launch_combine(c.a, false, static_cast<hipStream_t>(stream)));
 }
 
+// Split + combine of lbsa_decode on prepared arguments (single-chunk segments
+// written by the split kernel).
+static int decode_launch(DecodeCommon& c, void* out_d, void* stream) {
+    if (!out_d || !aligned(out_d, 8)) return LBSA_ERR_INVALID_ARGUMENT;
+    c.a.out = out_d;
+    c.a.direct_out = 1;   // single-chunk segments: the split kernel writes their rows itself
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int s = hip_status(launch_split(c.a, c.fp8, st));
+    if (s != LBSA_OK) return s;
+    return hip_status(launch_combine(c.a, false, st));
+}
+
 LBSA_API int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                          const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
                          int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t q_len,
@@ -286,19 +333,16 @@ LBSA_API int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_
                          int32_t num_workgroups, float softmax_scale, const void* task_map_d,
                          size_t task_map_bytes, void* workspace_d, size_t workspace_bytes,
                          void* out_d, void* stream) {
+    HookGuard guard;
     DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
                                   kv_dtype, page_table_d, batch, q_len, num_heads, num_kv_heads, head_dim,
                                   page_size, max_pages_per_seq, num_pages, softmax_scale);
-    int s = decode_prepare(c, batch, q_len, num_heads, num_kv_heads, head_dim, num_workgroups, task_map_d,
-                           task_map_bytes, workspace_d, workspace_bytes);
+    const int s = decode_prepare(c, batch, q_len, num_heads, num_kv_heads, head_dim, num_workgroups, task_map_d,
+                                 task_map_bytes, workspace_d, workspace_bytes);
     if (s != LBSA_OK) return s;
-    if (!out_d || !aligned(out_d, 8)) return LBSA_ERR_INVALID_ARGUMENT;
-    c.a.out = out_d;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    s = hip_status(launch_split(c.a, c.fp8, st));
-    if (s != LBSA_OK) return s;
-    return hip_status(launch_combine(c.a, false, st));
+    return decode_launch(c, out_d, stream);
 }
+
 
 LBSA_API int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                                 const void* v_cache_d, const float* k_scale_d,
@@ -309,6 +353,7 @@ LBSA_API int lbsa_decode_static(const void* q_d, const float* q_scale_d, const v
                                 int64_t num_pages, int32_t num_splits, float softmax_scale,
                                 void* workspace_d, size_t workspace_bytes, void* out_d,
                                 void* stream) {
+    HookGuard guard;
     DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d,
                                   kv_dtype, page_table_d, batch, q_len, num_heads, num_kv_heads, head_dim,
                                   page_size, max_pages_per_seq, num_pages, softmax_scale);
@@ -339,6 +384,7 @@ LBSA_API int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_
                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                           int32_t max_pages_per_seq, int64_t num_pages, float softmax_scale, void* out_d,
                           void* stream) {
+    HookGuard guard;
     const int s = check_shape(batch, num_heads, num_kv_heads, head_dim, page_size);
     if (s != LBSA_OK) return s;
     if (kv_dtype == LBSA_KV_FP8_E4M3) return LBSA_ERR_UNSUPPORTED;
@@ -368,6 +414,7 @@ static int router_shape(int32_t m, int32_t n, int32_t k) {
 
 LBSA_API int lbsa_router_split_weights(const float* w_d, int32_t n, int32_t k, void* w_high_d, void* w_low_d,
                                        void* stream) {
+    HookGuard guard;
     const int s = router_shape(0, n, k);
     if (s != LBSA_OK) return s;
     if (!w_d || !w_high_d || !w_low_d || !aligned(w_d, 16) || !aligned(w_high_d, 16) || !aligned(w_low_d, 16))
@@ -385,6 +432,7 @@ LBSA_API int lbsa_router_workspace_bytes(int32_t m, int32_t n, int32_t k, size_t
 
 LBSA_API int lbsa_router_gemm(const void* x_d, const void* w_high_d, const void* w_low_d, int32_t m, int32_t n,
                               int32_t k, float* scores_d, void* workspace_d, size_t workspace_bytes, void* stream) {
+    HookGuard guard;
     const int s = router_shape(m, n, k);
     if (s != LBSA_OK) return s;
     if (m == 0) return LBSA_OK;
@@ -404,6 +452,7 @@ LBSA_API int lbsa_prologue(const void* qkv_d, const int32_t* positions_d, const 
                            int32_t head_dim, int32_t page_size, int32_t kv_dtype, void* q_out_d,
                            float* q_scale_out_d, void* k_cache_d, void* v_cache_d, float* k_scale_d,
                            float* v_scale_d, int64_t num_pages, void* stream) {
+    HookGuard guard;
     if (num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_pages <= 0)
         return LBSA_ERR_INVALID_ARGUMENT;

@@ -39,9 +39,11 @@
 //     it directly; only when a wave-wide ballot finds a larger score does the
 //     wave reduce the max across lanes and rescale its accumulators.
 //   * O^T += V^T P^T with MFMA 16x16x16 bf16: V^T comes from LDS through
-//     ds_read_b64_tr_b16, P straight from the S^T accumulator registers (its
-//     layout is already the B operand).  fp8 V is widened exactly into a bf16
-//     LDS copy first; the per-token V scale is folded into p.
+//     transposed reads, P straight from the S^T accumulator registers (its
+//     layout is already the B operand).  bf16 V: ds_read_b64_tr_b16.  fp8 V:
+//     ds_read_b64_tr_b8 straight from the ring stage, each read giving a lane
+//     the 4 tokens of two d blocks, widened exactly to bf16 in registers; the
+//     per-token V scale is folded into p.
 //   * At the end of a descriptor the 4 waves merge (max, sum, O) through LDS
 //     and one partial (fp32 O normalised, natural-log LSE) is written.
 #include "lbsa_device.h"
@@ -91,37 +93,37 @@ static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt rang
 static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
 
 // 16-byte chunk swizzle inside a row: LDS chunk c' holds row chunk c' ^ f(row).
-// K rows (and fp8 V rows) use swz; bf16 V rows, which are read transposed, and
-// the bf16 copy of fp8 V use swz_v (no bank conflicts in a transposed pass).
+// K rows use swz; V rows, which are read transposed, use swz_v (bf16) or
+// swz_v8 (fp8), chosen so that a transposed pass has no bank conflict.
 template <bool FP8> __device__ inline int swz(int row) { return FP8 ? ((row >> 1) & 7) : (row & 15); }
-template <bool FP8> __device__ inline int swz_vrow(int row) { return FP8 ? swz<true>(row) : swz_v(row); }
+// fp8 V: one 16-lane pass of ds_read_b64_tr_b8 reads chunks 2c and 2c + 1 of the
+// 4 rows 4g .. 4g + 3 (8 B per lane, 128 B).  A 128-byte row spans half of the
+// 32 four-byte banks, so the bank group of a chunk is its swizzled index alone;
+// 2 (row & 3) sends the four rows' chunk pairs to four different pairs of bank
+// groups.
+__device__ inline int swz_v8(int row) { return 2 * (row & 3); }
+template <bool FP8> __device__ inline int swz_vrow(int row) { return FP8 ? swz_v8(row) : swz_v(row); }
 
 // LDS of one split / static workgroup.  Every ring stage is its own
 // __shared__ object: the compiler's wait-count insertion can then tell which
 // asynchronous load an LDS read depends on (distinct underlying objects) and
 // does not fall back to waiting for all of them.
 //
-// Each wave has one slot (Slot::kWave bytes) that holds its bf16 copy of the
-// fp8 V slice during a tile and its (O, m, l, flag) for the merge at the end of
-// a descriptor; the two uses of a slot never overlap in time (program order
-// within the wave, and the merge's closing barrier before any wave's next
-// tile), so for fp8 they share the memory.  fp8 with QL = 2 merges O in two
-// passes of 64 dims (the slot holds half of O).
-constexpr int kVbWave = 16 * 256;                                      // 16 V rows as bf16
+// Each wave has one slot (Slot::kWave bytes) that holds its (O, m, l, flag) for
+// the merge at the end of a descriptor.  fp8 with QL = 2 merges O in two passes
+// of 64 dims (the slot holds half of O), so that two workgroups fit a CU.
 template <bool FP8, int QL> struct Slot {
     static constexpr int kRows = kGroup * QL;                          // query rows of a descriptor
     static constexpr int kPasses = (FP8 && QL == 2) ? 2 : 1;           // passes over the 128 dims
     static constexpr int kDims = kHeadDim / kPasses;                   // dims of O per pass
     static constexpr int kMerge = (kRows * kDims + 2 * kRows + 4) * 4;   // O (one pass), m, l, flag per wave
-    static constexpr int kUse = FP8 && kVbWave > kMerge ? kVbWave : kMerge;
-    static constexpr int kWave = (kUse + 255) / 256 * 256;             // 256-aligned
+    static constexpr int kWave = (kMerge + 255) / 256 * 256;           // 256-aligned
     static constexpr int kBytes = kWaves * kWave;
 };
 constexpr int kMaxStages = 6;
 template <bool FP8> struct Smem {
     lds_char* stage[kMaxStages];   // [kWaves][Stage::BYTES] each; the first STAGES are used
-    lds_char* vb;                  // fp8: [kWaves][Slot::kWave], the bf16 copy of the V slice
-    lds_char* merge;               // [kWaves][Slot::kWave] (for fp8 the same memory as vb)
+    lds_char* merge;               // [kWaves][Slot::kWave]
 };
 template <bool FP8, int QL> constexpr int stage_array_bytes(int u) {
     return u < Stage<FP8, QL>::STAGES ? kWaves * Stage<FP8, QL>::BYTES : 16;
@@ -135,7 +137,7 @@ static_assert(smem_bytes<false, 2>() <= 160 * 1024 && smem_bytes<true, 2>() <= 8
 // One descriptor of the tile stream (all fields wave-uniform).
 struct Desc {
     int h, b, t0, t1, L;
-    int64_t slot;
+    int slot;        // partial slot (< Hkv * B + P, or the static grid size: both below 2^31)
 };
 
 // Per-lane constants of the asynchronous loads (fixed for a wave's stream).
@@ -192,6 +194,22 @@ __device__ inline void issue_tile(const AttnArgs& a, const LaneLoads<FP8>& ll, l
     }
 }
 
+// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Four fp32 -> four bf16 in one 8-byte store.
+__device__ inline void store_bf16x4(uint16_t* p, f32x4 v) {
+    uint2 packed;
+    packed.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+    packed.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = packed;
+}
+
 // Running state of one wave over one descriptor.
 struct WaveState {
     f32x4 acc[8];     // O^T[d = 16 db + 4 g + i][head r]
@@ -232,8 +250,8 @@ __device__ inline void load_q(const AttnArgs& a, const Desc& d, int r, int g, QO
 // QK^T, online softmax and PV of one tile held in stage `st`.  `lim` is the
 // token limit of this lane's column (its query sees tokens < lim).
 template <bool FP8, int QL>
-__device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* __restrict__ vb, const QOp<FP8>& q,
-                                    float sl2, int tok0, int lim, int w, int r, int g, WaveState& ws) {
+__device__ inline void tile_compute(const lds_char* __restrict__ st, const QOp<FP8>& q, float sl2, int tok0,
+                                    int lim, int w, int r, int g, WaveState& ws) {
     const uint4 z4 = make_uint4(0, 0, 0, 0);
     const bool qlive = r < kGroup * QL;
     using SL = Stage<FP8, QL>;
@@ -259,18 +277,25 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
         sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[2]), qv[2], sa, 0, 0, 0);
         sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[3]), qv[3], sb, 0, 0, 0);
     } else {
-        uint32_t addr[6];
+        uint32_t addr[4], vaddr[4];
         addr[0] = lds_addr(st + SL::K + r * 128 + 16 * (g ^ swz<true>(r)));         // K k-steps 0, 1
         addr[1] = lds_addr(st + SL::K + r * 128 + 16 * ((g + 4) ^ swz<true>(r)));   // K k-steps 2, 3
-        addr[2] = lds_addr(st + SL::V + r * 128 + 16 * (g ^ swz<true>(r)));         // V chunk g
-        addr[3] = lds_addr(st + SL::V + r * 128 + 16 * ((g + 4) ^ swz<true>(r)));   // V chunk g + 4
-        addr[4] = lds_addr(st + SL::KS + 16 * g);                                   // k scales, rows 4g..
-        addr[5] = lds_addr(st + SL::VS + 16 * g);                                   // v scales, rows 4g..
-        uint4 o[6];
-        lds_read_tile_fp8(o, addr);
+        addr[2] = lds_addr(st + SL::KS + 16 * g);                                   // k scales, rows 4g..
+        addr[3] = lds_addr(st + SL::VS + 16 * g);                                   // v scales, rows 4g..
+        // V^T by transposed byte reads: in the 16-lane group g, lanes 2j and 2j + 1
+        // name the two halves of "row" j = (token 4g + j % 4, chunk 2 db + j / 4);
+        // lane i then receives byte i of each of the 8 rows: the 4 tokens of dim
+        // 32 db + i (bytes 0-3) and of dim 32 db + 16 + i (bytes 4-7).
+        const int vt = 4 * g + ((r >> 1) & 3);
+        const uint32_t vrow = lds_addr(st + SL::V + vt * 128 + 8 * (r & 1));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) vaddr[db] = vrow + 16u * (uint32_t)((2 * db + (r >> 3)) ^ swz_v8(vt));
+        uint4 o[4];
+        uint2 vv[4];
+        lds_read_tile_fp8_tr(o, vv, addr, vaddr);
         const uint4 c0 = o[0], c1 = o[1];
-        ks4 = __builtin_bit_cast(f32x4, o[4]);
-        vs4 = __builtin_bit_cast(f32x4, o[5]);
+        ks4 = __builtin_bit_cast(f32x4, o[2]);
+        vs4 = __builtin_bit_cast(f32x4, o[3]);
         const uint4 q0 = qlive ? q.v[0] : z4, q1 = qlive ? q.v[1] : z4;
         auto lo = [](uint4 x) { return (long)(((uint64_t)x.y << 32) | x.x); };
         auto hi = [](uint4 x) { return (long)(((uint64_t)x.w << 32) | x.z); };
@@ -278,24 +303,12 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
         sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(hi(c0), hi(q0), sb, 0, 0, 0);
         sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(lo(c1), lo(q1), sa, 0, 0, 0);
         sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(hi(c1), hi(q1), sb, 0, 0, 0);
-        // widen this lane's two V chunks of row r into the bf16 copy (same swizzle as bf16 V),
-        // then read it back transposed
-        uint32_t waddr[4];
-        uint4 wv[4];
+        // the 4 tokens of each d block as bf16, in token order (exact widening)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int c = g + 4 * p;
-            waddr[2 * p] = lds_addr(vb + r * 256 + 16 * ((2 * c) ^ swz_v(r)));
-            waddr[2 * p + 1] = lds_addr(vb + r * 256 + 16 * ((2 * c + 1) ^ swz_v(r)));
-            wv[2 * p] = fp8x8_to_bf16x8(o[2 + p].x, o[2 + p].y);
-            wv[2 * p + 1] = fp8x8_to_bf16x8(o[2 + p].z, o[2 + p].w);
+        for (int db = 0; db < 4; ++db) {
+            va[2 * db] = __builtin_bit_cast(s16x4, fp8x4_to_bf16x4(vv[db].x));
+            va[2 * db + 1] = __builtin_bit_cast(s16x4, fp8x4_to_bf16x4(vv[db].y));
         }
-        lds_write4x16(waddr, wv);
-        const uint32_t vr = lds_addr(vb + vrow * 256 + 8 * (r & 1));
-        uint32_t vaddr[8];
-#pragma unroll
-        for (int db = 0; db < 8; ++db) vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_v(vrow));
-        vt_read8(va, vaddr);
     }
     const f32x4 s = sa + sb;
 
@@ -346,14 +359,20 @@ __device__ inline void tile_compute(const lds_char* __restrict__ st, lds_char* _
 }
 
 // End of a descriptor: merge the 4 waves' (max, sum, O) through LDS and write
-// the partial (normalised O, natural-log LSE) of `slot`: QL x 8 rows, row
+// the partial (normalised O, natural-log LSE) of its slot: QL x 8 rows, row
 // r = 8 query + head.  Every descriptor holds a token the last query sees, so
 // a row of that query with nothing accumulated means bad data (NaN); an
 // earlier query may legitimately see none of the descriptor's tokens, which
 // gives an empty partial (O = 0, LSE = -inf) that the combine skips.
+// With a.direct_out set, a descriptor that covers its whole (kv_head, request)
+// segment -- the segment's only chunk -- is already the final result: its
+// normalised O goes straight to the bf16 output rows (the merge of a single
+// chunk is the identity) and the combine leaves those rows alone.
 template <bool FP8, int QL>
 __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const WaveState& ws, bool bad,
-                                   int64_t slot, int w, int lane, int r, int g) {
+                                   const Desc& dd, int w, int lane, int r, int g) {
+    const size_t slot = (size_t)dd.slot;
+    const bool whole = a.direct_out != 0 && dd.t0 == 0 && dd.t1 == (dd.L + kTile - 1) / kTile;
     using SM = Slot<FP8, QL>;
     constexpr int R = SM::kRows, DW = SM::kDims, DBP = DW / 16;   // rows, dims and d blocks per pass
     float lsum = ws.l;
@@ -409,8 +428,14 @@ __device__ inline void finish_desc(const AttnArgs& a, lds_char* merge, const Wav
                     o *= 1.f / lt;
                     lse = (M + __builtin_log2f(lt)) * kLn2;
                 }
-                *reinterpret_cast<f32x4*>(a.part_o + ((size_t)slot * R + hh) * kHeadDim + DW * dp + d4) = o;
-                if (dp == 0 && (tid & 31) == 0) a.part_lse[(size_t)slot * R + hh] = lse;
+                if (whole) {
+                    // row (request, query pass, head h * 8 + tid / 32) of out [B][QL][Hq][128]
+                    const size_t orow = ((size_t)dd.b * QL + pass) * a.Hq + (size_t)dd.h * kGroup + (tid >> 5);
+                    store_bf16x4(static_cast<uint16_t*>(a.out) + orow * kHeadDim + DW * dp + d4, o);
+                } else {
+                    *reinterpret_cast<f32x4*>(a.part_o + ((size_t)slot * R + hh) * kHeadDim + DW * dp + d4) = o;
+                    if (dp == 0 && (tid & 31) == 0) a.part_lse[(size_t)slot * R + hh] = lse;
+                }
             }
         }
         lds_barrier();   // the merge area is reused by the next pass / descriptor
@@ -429,11 +454,17 @@ struct MapDescs {           // descriptors [d0, d0 + n) of a task-map bin
     RawDesc head;           // descriptor d0, from the bin's head record
     int d0, n, Hkv, B, max_pages;
     __device__ int count() const { return n; }
-    // descriptor i (0-based in the bin); an invalid one (corrupt map) has no tiles
+    // the bin's first descriptor (from the head record; no load)
+    __device__ Desc first() const { return check(0, head); }
+    // descriptor i >= 1 of the bin (loaded from the map).  The cursors read the
+    // head record only in first(), so it is dead inside the stream loop.
     __device__ Desc get(int i) const {
-        RawDesc x = head;
         const int d = d0 + i;
-        if (i != 0) x = RawDesc{desc[4 * d], desc[4 * d + 1], desc[4 * d + 2], desc[4 * d + 3], dlen[d]};
+        return check(i, RawDesc{desc[4 * d], desc[4 * d + 1], desc[4 * d + 2], desc[4 * d + 3], dlen[d]});
+    }
+    // an invalid descriptor (corrupt map) has no tiles
+    __device__ Desc check(int i, RawDesc x) const {
+        const int d = d0 + i;
         Desc y;
         y.slot = d;
         if (x.h < 0 || x.h >= Hkv || x.b < 0 || x.b >= B || x.t0 < 0 || x.t1 <= x.t0 || x.t1 > max_pages ||
@@ -450,6 +481,7 @@ struct MapDescs {           // descriptors [d0, d0 + n) of a task-map bin
 struct OneDesc {            // the static kernel's single chunk
     Desc d;
     __device__ int count() const { return 1; }
+    __device__ Desc first() const { return d; }
     __device__ Desc get(int) const { return d; }
 };
 
@@ -462,7 +494,7 @@ struct Cursor {
     int i;          // descriptor ordinal
     int t;          // tile of that descriptor
     Desc d;
-    __device__ void seek_valid() {      // skip descriptors without tiles
+    __device__ void seek_valid() {      // skip descriptors without tiles, from descriptor i >= 1
         while (i < src->count()) {
             const Desc x = src->get(i);
             if (x.t1 > x.t0) { d = x; t = x.t0; return; }
@@ -473,8 +505,12 @@ struct Cursor {
     __device__ void begin(const Src* s) {
         src = s;
         i = 0;
-        d = Desc{0, 0, 0, 0, 0, 0};
-        seek_valid();
+        d = s->first();
+        t = d.t0;
+        if (d.t1 <= d.t0) {
+            ++i;
+            seek_valid();
+        }
     }
     __device__ void next() {
         if (++t >= d.t1) { ++i; seek_valid(); }
@@ -489,7 +525,7 @@ struct Cursor {
 // the cursor's tile, loaded one step ahead; the next one is fetched here.
 template <bool FP8, int QL, class Src>
 __device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, Cursor<Src>& lc, int& issued,
-                                  int ntiles, int64_t& page, uint32_t& bad_bits, lds_char* st, QOp<FP8>& qslot,
+                                  int ntiles, int& page, uint32_t& bad_bits, lds_char* st, QOp<FP8>& qslot,
                                   int slot, int w, int r, int g) {
     const bool ok = page >= 0 && page < a.num_pages;
     bad_bits = (bad_bits & ~(1u << slot)) | ((uint32_t)(!ok) << slot);
@@ -500,7 +536,7 @@ __device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, C
     issue_tile<FP8, QL>(a, ll, st, ok ? page : 0, d, lc.t, w);
     if (++issued < ntiles) {
         lc.next();
-        page = (int64_t)uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
+        page = uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
     }
 }
 
@@ -516,7 +552,6 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     // column r's query sees the request's tokens below L - (QL - 1 - query)
     const int lim_off = (QL == 1 ? 0 : min(r >> 3, QL - 1)) - (QL - 1);
     auto stage = [&](int u) -> lds_char* { return sm.stage[u] + w * SL::BYTES; };
-    lds_char* vb = sm.vb + w * Slot<FP8, QL>::kWave;
     LaneLoads<FP8> ll;
     ll.init(a.Hkv, w, lane);
 
@@ -524,7 +559,7 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     Cursor<Src> lc;
     lc.begin(&src);
     int issued = 0;
-    int64_t page = (int64_t)uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
+    int page = uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
     uint32_t bad_bits = 0;          // bit u: the tile in stage u has an out-of-range page id
     QOp<FP8> qring[S];              // Q of the descriptor whose first tile sits in stage u
 #pragma unroll
@@ -562,8 +597,8 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
                     bad = false;
                 }
                 bad |= (bad_bits >> u) & 1u;
-                tile_compute<FP8, QL>(stage(u), vb, q, sl2, 64 * cc.t, cc.d.L + lim_off, w, r, g, ws);
-                if (cc.t + 1 == cc.d.t1) finish_desc<FP8, QL>(a, sm.merge, ws, bad, cc.d.slot, w, lane, r, g);
+                tile_compute<FP8, QL>(stage(u), q, sl2, 64 * cc.t, cc.d.L + lim_off, w, r, g, ws);
+                if (cc.t + 1 == cc.d.t1) finish_desc<FP8, QL>(a, sm.merge, ws, bad, cc.d, w, lane, r, g);
                 cc.next();
             }
         }
@@ -586,7 +621,6 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
     sm.stage[3] = (lds_char*)s3;                                               \
     sm.stage[4] = (lds_char*)s4;                                               \
     sm.stage[5] = (lds_char*)s5;                                               \
-    sm.vb = (lds_char*)sslot;                                                  \
     sm.merge = (lds_char*)sslot
 
 // One workgroup per bin (grid = P).  The header words and the bin's head
@@ -627,7 +661,7 @@ __global__ __launch_bounds__(kSplitThreads) void static_kernel(AttnArgs a) {
     const int split = blockIdx.x % S;
     const int rest = blockIdx.x / S;
     const int b = rest % a.B, h = rest / a.B;
-    const int64_t slot = ((int64_t)h * a.B + b) * S + split;
+    const int slot = (h * a.B + b) * S + split;
     int L = uniform_ptr<int32_t>(a.seqlens)[b];
     const bool len_ok = L >= 0 && L <= a.max_pages * kTile;
     if (!len_ok) L = 0;
@@ -655,17 +689,10 @@ __global__ __launch_bounds__(kSplitThreads) void static_kernel(AttnArgs a) {
     run_stream<FP8, QL>(a, src, t1 - t0, sm);
 }
 
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 // Online LSE merge of one chunk into a running (max, weight sum, weighted O).
 __device__ inline void merge_chunk(float l, f32x4 x, float& m, float& wsum, f32x4& o, bool& nan_seen) {
     if (l != l) { nan_seen = true; return; }
-    if (l == kNegInf) return;                           // empty chunk (static split)
+    if (l == kNegInf) return;                           // empty chunk (static split) or padding
     if (l > m) {
         const float sc = exp2_fast((m - l) * kLog2e);   // 0 when m = -inf
         wsum *= sc;
@@ -677,11 +704,16 @@ __device__ inline void merge_chunk(float l, f32x4 x, float& m, float& wsum, f32x
     o += wgt * x;
 }
 
-// One workgroup per (request, query token, query head).  Its 256 threads form 8 slices of
-// 32 (4 consecutive d per thread); slice c0 merges chunks c0, c0 + 8, ... of
-// the row in one pass with a running (max LSE, weight sum, weighted O), four
-// chunks' loads in flight at a time, and the 8 slice states are merged
-// through LDS under the global maximum.
+// One workgroup per output row (request, query token, query head).  Its 256
+// threads form 8 slices of 32 (4 consecutive d per thread); slice c0 merges
+// chunks c0, c0 + 8, ... of the row with a running (max LSE, weight sum,
+// weighted O).  The loads of up to kCombineUnroll chunks per slice (64 per
+// row) are all issued before the first of them is used, so a row of up to 64
+// chunks costs one round trip to the partials after the one to the map.  The 8
+// slice states are then merged through LDS under the global maximum.  With
+// a.direct_out, a row whose segment has a single chunk was written by the split
+// kernel, and its workgroup stops after reading the chunk count.
+constexpr int kCombineUnroll = 8;
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, int static_mode) {
     constexpr int kSlices = 8;
     __shared__ float red_m[kSlices];
@@ -711,13 +743,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
         const int h_err = hdr[LBSA_HDR_ERROR];
         const int sd0 = uniform_ptr<int32_t>(a.map + ML.seg_first_desc)[seg];
         const int sn = uniform_ptr<int32_t>(a.map + ML.seg_num_chunks)[seg];
-        if (h_p != a.P || h_b != a.B || h_hkv != a.Hkv) {
+        const int cap = a.Hkv * a.B + a.P;
+        if (h_p != a.P || h_b != a.B || h_hkv != a.Hkv || h_err != 0 || sd0 < 0 || sn < 0 || sn > cap - sd0) {
+            // a map built for another shape, or one whose lengths were invalid
+            // (the split kernel computed nothing): every row is NaN
             poison = true;
-        } else if (h_err == 0) {
-            const int cap = a.Hkv * a.B + a.P;
+        } else {
             d0 = sd0;
             n = sn;
-            if (d0 < 0 || n < 0 || d0 + n > cap) { poison = true; n = 0; }
+            if (a.direct_out && n == 1) return;         // the split kernel wrote this row
         }
     }
     if (tid == 0) red_nan = 0;
@@ -726,21 +760,22 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     bool nan_seen = false;
     auto pr = [&](int c) { return (d0 + c) * R + kGroup * qi + gq; };
-    int c = slice;
-    for (; c + 3 * kSlices < n; c += 4 * kSlices) {     // four chunks' loads in flight
-        float l[4];
-        f32x4 x[4];
+    for (int c0 = slice; c0 < n; c0 += kCombineUnroll * kSlices) {
+        float l[kCombineUnroll];
+        f32x4 x[kCombineUnroll];
+        // unconditional loads (a chunk past the row's last one re-reads the last
+        // one, in bounds, and is then dropped), so the compiler emits them as
+        // one straight run with no branch between them
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            l[u] = a.part_lse[pr(c + u * kSlices)];
-            x[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr(c + u * kSlices) * kHeadDim + d4);
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const int c = min(c0 + u * kSlices, n - 1);
+            l[u] = a.part_lse[pr(c)];
+            x[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr(c) * kHeadDim + d4);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) merge_chunk(l[u], x[u], m, wsum, o, nan_seen);
+        for (int u = 0; u < kCombineUnroll; ++u)
+            merge_chunk(c0 + u * kSlices < n ? l[u] : kNegInf, x[u], m, wsum, o, nan_seen);
     }
-    for (; c < n; c += kSlices)
-        merge_chunk(a.part_lse[pr(c)], *reinterpret_cast<const f32x4*>(a.part_o + pr(c) * kHeadDim + d4), m, wsum,
-                    o, nan_seen);
     __syncthreads();                                    // red_nan initialised
     if (nan_seen) red_nan = 1;
     if ((tid & 31) == 0) {
@@ -768,11 +803,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
             const float nan = __builtin_nanf("");
             acc = f32x4{nan, nan, nan, nan};
         }
-        uint16_t* out = static_cast<uint16_t*>(a.out) + (size_t)row * kHeadDim + d4;
-        uint2 packed;
-        packed.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-        packed.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-        *reinterpret_cast<uint2*>(out) = packed;
+        store_bf16x4(static_cast<uint16_t*>(a.out) + (size_t)row * kHeadDim + d4, acc);
     }
 }
 

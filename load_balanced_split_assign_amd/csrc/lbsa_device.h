@@ -295,6 +295,36 @@ __device__ inline void lds_read_tile_bf16_at(uint4 (&k)[4], s16x4 (&va)[8], cons
     va[7] = __builtin_bit_cast(s16x4, o7);
 }
 
+// fp8 tile: the two K chunks and the k/v scales (ds_read_b128), and the four
+// transposed byte reads of V^T (ds_read_b64_tr_b8), in one block.
+__device__ inline void lds_read_tile_fp8_tr(uint4 (&o)[4], uint2 (&v)[4], const uint32_t (&addr)[4],
+                                            const uint32_t (&vaddr)[4]) {
+    u32x4 o0, o1, o2, o3;
+    u32x2 v0, v1, v2, v3;
+    __asm__ volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b64_tr_b8 %4, %12\n\t"
+        "ds_read_b64_tr_b8 %5, %13\n\t"
+        "ds_read_b64_tr_b8 %6, %14\n\t"
+        "ds_read_b64_tr_b8 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3), "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(vaddr[0]), "v"(vaddr[1]), "v"(vaddr[2]),
+          "v"(vaddr[3])
+        : "memory");
+    o[0] = __builtin_bit_cast(uint4, o0);
+    o[1] = __builtin_bit_cast(uint4, o1);
+    o[2] = __builtin_bit_cast(uint4, o2);
+    o[3] = __builtin_bit_cast(uint4, o3);
+    v[0] = __builtin_bit_cast(uint2, v0);
+    v[1] = __builtin_bit_cast(uint2, v1);
+    v[2] = __builtin_bit_cast(uint2, v2);
+    v[3] = __builtin_bit_cast(uint2, v3);
+}
+
 // fp8 tile: the two K chunks, the two V chunks and the k/v scales in one block.
 __device__ inline void lds_read_tile_fp8(uint4 (&o)[6], const uint32_t (&addr)[6]) {
     u32x4 o0, o1, o2, o3, o4, o5;

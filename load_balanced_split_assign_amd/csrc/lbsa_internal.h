@@ -98,10 +98,12 @@ struct AttnArgs {
     float* part_lse;
     float* part_o;
     void* out;
-    int64_t num_pages;
+    int32_t num_pages;           // pages in each cache (capped at INT32_MAX: page ids are int32)
     int32_t B, Hq, Hkv, max_pages;
     int32_t P;                   // split: bins; static: number of splits
     int32_t QL;                  // query tokens per request (1 .. kMaxQLen)
+    int32_t direct_out;          // split: a segment's only chunk goes straight to out (bf16); combine:
+                                 // skip the rows of single-chunk segments (map path only)
     float scale_log2;            // softmax_scale * log2(e)
 };
 

@@ -73,13 +73,15 @@ def lib() -> ctypes.CDLL:
         L.lbsa_router_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.lbsa_router_gemm.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
         L.lbsa_time_next_kernel.argtypes = [vp, vp]
+        L.lbsa_time_next_kernels.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.lbsa_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, f32, i32, i32, i32, i32, i32, i32,
                                     vp, vp, vp, vp, vp, vp, i64, vp]
         for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes", "lbsa_prologue",
                    "lbsa_workspace_layout_get", "lbsa_workspace_bytes", "lbsa_static_workspace_bytes",
                    "lbsa_plan", "lbsa_decode", "lbsa_decode_split", "lbsa_decode_combine",
                    "lbsa_decode_static", "lbsa_prefill", "lbsa_router_split_weights",
-                   "lbsa_router_workspace_bytes", "lbsa_router_gemm", "lbsa_time_next_kernel"):
+                   "lbsa_router_workspace_bytes", "lbsa_router_gemm", "lbsa_time_next_kernel",
+                   "lbsa_time_next_kernels"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -110,20 +112,33 @@ def kv_dtype_code(kv_dtype: str) -> int:
 # sizes and layouts
 # ---------------------------------------------------------------------------
 
+def _event_handle(ev):
+    """hipEvent_t of a torch.cuda.Event (None stays None).  torch creates an
+    event at its first record: an event never recorded is recorded once here,
+    on the current stream, to create it."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
+
+
 def time_next_kernel(start=None, stop=None) -> None:
     """Arm the library's kernel timing hook: the next kernel that this thread
     launches through the library stamps `start` and `stop` (torch.cuda.Event
     with enable_timing=True) at its own start and end, so
     start.elapsed_time(stop) is that kernel's duration without a dispatch
-    gap.  torch creates an event at its first record: an event never recorded
-    is recorded once here, on the current stream, to create it."""
-    def handle(ev):
-        if ev is None:
-            return None
-        if not ev.cuda_event:
-            ev.record()
-        return ctypes.c_void_p(ev.cuda_event)
-    _check("lbsa_time_next_kernel", lib().lbsa_time_next_kernel(handle(start), handle(stop)))
+    gap.  (None, None) disarms."""
+    _check("lbsa_time_next_kernel", lib().lbsa_time_next_kernel(_event_handle(start), _event_handle(stop)))
+
+
+def time_next_kernels(pairs) -> None:
+    """Arm the hook for the next len(pairs) launches, in order: launch i stamps
+    pairs[i] = (start, stop).  An empty list disarms."""
+    n = len(pairs)
+    starts = (ctypes.c_void_p * max(1, n))(*[_event_handle(a) for a, _ in pairs])
+    stops = (ctypes.c_void_p * max(1, n))(*[_event_handle(b) for _, b in pairs])
+    _check("lbsa_time_next_kernels", lib().lbsa_time_next_kernels(n, starts, stops))
 
 
 def default_workgroups(device: int = 0, kv_dtype: str = "bf16", q_len: int = 1) -> int:
@@ -189,14 +204,18 @@ def plan(seqlens: torch.Tensor, num_heads: int, num_kv_heads: int, max_pages: in
 
 
 def _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table):
+    """Checks the decode tensors against each other (the C ABI takes no sizes for
+    the scales, so a mis-sized tensor here would mean reads out of bounds) and
+    returns the leading C arguments and (B, q_len, Hq, Hkv, D)."""
     fp8 = k_cache.dtype == torch.float8_e4m3fn
     if fp8:
         assert q.dtype == torch.float8_e4m3fn and v_cache.dtype == torch.float8_e4m3fn
         assert q_scale is not None and k_scale is not None and v_scale is not None
     else:
         assert q.dtype == torch.bfloat16 and k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16
+    dev = q.device
     for t in (q, k_cache, v_cache, page_table, q_scale, k_scale, v_scale):
-        assert t is None or t.is_contiguous()
+        assert t is None or (t.is_contiguous() and t.device == dev)
     # q [B, Hq, D]: one query token per request; [B, q_len, Hq, D]: multi-token decode
     if q.dim() == 3:
         (B, Hq, D), QL = q.shape, 1
@@ -204,13 +223,26 @@ def _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table):
         B, QL, Hq, D = q.shape
     num_pages, page, Hkv, D2 = k_cache.shape
     assert page == PAGE_SIZE and D2 == D and tuple(v_cache.shape) == tuple(k_cache.shape)
-    assert page_table.dtype == torch.int32 and page_table.shape[0] == B
+    assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.shape[0] == B
     if fp8:
-        assert q_scale.numel() == B * QL * Hq
+        assert q_scale.dtype == torch.float32 and q_scale.numel() == B * QL * Hq
+        for sc in (k_scale, v_scale):
+            assert sc.dtype == torch.float32 and sc.numel() == num_pages * Hkv * PAGE_SIZE
     return [_ptr(q), _ptr(q_scale) if fp8 else None, _ptr(k_cache), _ptr(v_cache),
             _ptr(k_scale) if fp8 else None, _ptr(v_scale) if fp8 else None,
             KV_FP8_E4M3 if fp8 else KV_BF16, _ptr(page_table), B, QL, Hq, Hkv, D, page,
             int(page_table.shape[1]), int(num_pages)], (B, QL, Hq, Hkv, D)
+
+
+def _check_out(out, q):
+    """A caller's output tensor: bf16, contiguous, on q's device, shaped like q."""
+    assert out.dtype == torch.bfloat16 and out.is_contiguous() and out.device == q.device
+    assert tuple(out.shape) == tuple(q.shape), (tuple(out.shape), tuple(q.shape))
+
+
+def _check_bytes(buf, device, what):
+    """A caller's byte buffer (workspace, task map): uint8, contiguous, on `device`."""
+    assert buf.dtype == torch.uint8 and buf.is_contiguous() and buf.device == device, what
 
 
 def decode(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softmax_scale: float,
@@ -222,6 +254,9 @@ def decode(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softm
                                 device=q.device)
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, q)
+    _check_bytes(workspace, q.device, "workspace")
+    _check_bytes(task_map, q.device, "task map")
     _check("lbsa_decode", lib().lbsa_decode(*args, num_workgroups, float(softmax_scale), _ptr(task_map),
                                             task_map.numel(), _ptr(workspace), workspace.numel(), _ptr(out),
                                             _stream(q.device)))
@@ -235,6 +270,8 @@ def decode_split(q, k_cache, v_cache, page_table, task_map, num_workgroups: int,
     if workspace is None:
         workspace = torch.empty(workspace_bytes(B, Hq, Hkv, num_workgroups, D, QL), dtype=torch.uint8,
                                 device=q.device)
+    _check_bytes(workspace, q.device, "workspace")
+    _check_bytes(task_map, q.device, "task map")
     _check("lbsa_decode_split", lib().lbsa_decode_split(*args, num_workgroups, float(softmax_scale),
                                                         _ptr(task_map), task_map.numel(), _ptr(workspace),
                                                         workspace.numel(), _stream(q.device)))
@@ -247,6 +284,11 @@ def decode_combine(batch: int, num_heads: int, num_kv_heads: int, num_workgroups
     if out is None:
         shape = (batch, num_heads, head_dim) if q_len == 1 else (batch, q_len, num_heads, head_dim)
         out = torch.empty(shape, dtype=torch.bfloat16, device=workspace.device)
+    shape = (batch, num_heads, head_dim) if q_len == 1 else (batch, q_len, num_heads, head_dim)
+    assert out.dtype == torch.bfloat16 and out.is_contiguous() and out.device == workspace.device
+    assert out.numel() == batch * q_len * num_heads * head_dim, (tuple(out.shape), shape)
+    _check_bytes(workspace, workspace.device, "workspace")
+    _check_bytes(task_map, workspace.device, "task map")
     _check("lbsa_decode_combine", lib().lbsa_decode_combine(batch, q_len, num_heads, num_kv_heads, head_dim,
                                                             num_workgroups, _ptr(task_map), task_map.numel(),
                                                             _ptr(workspace), workspace.numel(), _ptr(out),
@@ -264,6 +306,9 @@ def decode_static(q, k_cache, v_cache, page_table, seqlens, num_splits: int, sof
                                 device=q.device)
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, q)
+    _check_bytes(workspace, q.device, "workspace")
+    assert seqlens.device == q.device and seqlens.numel() == B
     a = args
     _check("lbsa_decode_static", lib().lbsa_decode_static(*a[:8], _ptr(seqlens), *a[8:], num_splits,
                                                           float(softmax_scale), _ptr(workspace),
@@ -287,6 +332,7 @@ def prefill(q, k_cache, v_cache, page_table, seqlens, softmax_scale: float, out=
     assert seqlens.dtype == torch.int32 and seqlens.numel() == B
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, q)
     _check("lbsa_prefill", lib().lbsa_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), KV_BF16, _ptr(page_table),
                                               _ptr(seqlens), B, QL, Hq, Hkv, D, page, int(page_table.shape[1]),
                                               int(num_pages), float(softmax_scale), _ptr(out), _stream(q.device)))

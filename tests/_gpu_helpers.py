@@ -11,13 +11,19 @@ from load_balanced_split_assign_amd import workload as wl
 
 requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")
 
-BF16_TOL = 2e-2     # max |out - oracle| for bf16 KV
-FP8_TOL = 6e-2      # max |out - oracle| for fp8-e4m3 KV
-LSE_TOL = 1e-3      # |partial LSE - oracle| (natural log)
+from parity import BF16_TOL, FP8_TOL, LSE_TOL, REL_TOL, assert_parity  # noqa: F401  (the bar, tests/parity.py)
 
 
 def tol(batch) -> float:
     return FP8_TOL if batch["kv_dtype"] == "fp8" else BF16_TOL
+
+
+def check(batch, got, ref, what=""):
+    """Both bounds of the bar on every row (absolute, and relative to the row's
+    largest oracle entry); prints the figures so a run shows the margins."""
+    err, ratio = assert_parity(got, ref, tol(batch), REL_TOL, what)
+    print(f"parity {what}: max abs err {err:.2e}, worst row ratio {ratio:.2e}", flush=True)
+    return err
 
 
 def batch_on_gpu(name_or_kw, tail="nan", gen_device="cpu"):
@@ -65,15 +71,3 @@ def decode_static(batch, S, **kw):
 def out_np(out: torch.Tensor) -> np.ndarray:
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
-
-
-def sample_rows(batch, n_requests=6, heads=(0, 7, 8, 63), seed=0):
-    """(request, query head) rows for sampled parity at full size: the longest
-    and shortest requests plus random ones, heads across group boundaries."""
-    sl = batch["seqlens"].cpu().numpy()
-    rng = np.random.default_rng(seed)
-    reqs = {int(np.argmax(sl)), int(np.argmin(sl))}
-    while len(reqs) < min(n_requests, len(sl)):
-        reqs.add(int(rng.integers(0, len(sl))))
-    hq = [h for h in heads if h < batch["num_heads"]]
-    return np.array([(b, h) for b in sorted(reqs) for h in hq], np.int32)

@@ -1,0 +1,96 @@
+"""The parity bar of the attention outputs, in one place (no GPU needed).
+
+Two bounds hold for every output row (the last axis, 128 dims, is a row):
+
+* the absolute bound of the target: max |got - ref| <= 2e-2 with bf16 K/V and
+  <= 6e-2 with fp8-e4m3 K/V;
+* a scale-aware bound: max |got - ref| <= REL_TOL * max |ref| over the row.
+
+Why the second one.  With N(0, 1) values an attention row averages L value
+rows, so its entries shrink like sqrt(e / L): at L = 131072 the largest entry of
+a row is about 0.02, and an all-zero output would pass the absolute bound alone.
+The relative bound scales with the row and rejects that.
+
+Where REL_TOL comes from.  The kernels compute the scores in fp32 from exact
+products, exponentiate in fp32 and sum the weights p_t in fp32; the rounding
+that matters is the one of p_t to bf16 for the P.V matrix product, and the
+final rounding of the output to bf16:
+
+* output rounding: |bf16(x) - x| <= 2^-9 |x| <= 2^-9 max|ref| per entry;
+* P rounding: with p~_t = p_t (1 + d_t), |d_t| <= 2^-9 (round to nearest
+  even, unbiased), the output moves by e = sum_t p_t d_t v_t / sum_t p_t.  The
+  same weighted sum without d_t is the output itself, and for independent
+  values its typical size is sqrt(sum p^2 v^2) / sum p, so e is about
+  2^-9 / sqrt(3) = 1.1e-3 of the row's typical entry; a 5-sigma excursion of e
+  over 4096 rows x 128 dims is 5.6e-3 of a typical entry, and a row's largest
+  entry is at least twice its typical one, which gives 2.8e-3 max|ref|.
+
+The two add up to 4.8e-3 max|ref|; REL_TOL = 2^-7 = 7.8e-3 keeps a factor 1.6
+above that.  The fp32 accumulation (relative 2^-24 per add), the fp32 exp2
+(about 1 ulp) and the fp32 LSE merge are three orders of magnitude smaller.
+fp8 K/V change none of this: the oracle works on the same dequantised values,
+and the per-token V scale is folded into p before the same bf16 rounding.
+tests/test_parity_checker.py pins the bound on the CPU: a model of exactly
+these roundings passes it with room on long rows, while a zeroed row, a row
+scaled by 0.97 and a row missing one of its chunks fail it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BF16_TOL = 2e-2     # max |out - oracle| for bf16 KV (the target's bound)
+FP8_TOL = 6e-2      # max |out - oracle| for fp8-e4m3 KV (the target's bound)
+REL_TOL = 2.0 ** -7  # per row: max |out - oracle| <= REL_TOL * max |oracle| (derivation above)
+LSE_TOL = 1e-3      # |partial LSE - oracle| (natural log)
+
+
+def abs_tol(kv_dtype: str) -> float:
+    return FP8_TOL if kv_dtype == "fp8" else BF16_TOL
+
+
+def row_stats(got, ref):
+    """(per-row max |got - ref|, per-row max |ref|) over the last axis."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    n = ref.shape[-1]
+    g = got.reshape(-1, n)
+    r = ref.reshape(-1, n)
+    return np.abs(g - r).max(axis=1), np.abs(r).max(axis=1)
+
+
+def parity_failures(got, ref, atol: float, rtol: float = REL_TOL):
+    """Description of every way `got` misses the bar (empty list = parity)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    fails = []
+    if not np.isfinite(got).all():
+        fails.append(f"{int((~np.isfinite(got)).sum())} non-finite entries")
+        return fails
+    err, scale = row_stats(got, ref)
+    if err.size == 0:
+        return fails
+    if err.max() > atol:
+        fails.append(f"max abs err {err.max():.3e} > {atol:.1e}")
+    bad = err > rtol * scale
+    if bad.any():
+        i = int(np.argmax(np.where(bad, err / np.maximum(scale, 1e-300), 0.0)))
+        fails.append(f"{int(bad.sum())} of {err.size} rows over the relative bound; worst row {i}: "
+                     f"err {err[i]:.3e} vs max|ref| {scale[i]:.3e} (ratio {err[i] / max(scale[i], 1e-300):.3e} > "
+                     f"{rtol:.3e})")
+    return fails
+
+
+def worst_ratio(got, ref) -> float:
+    """max over rows of max|got - ref| / max|ref| (0 for exactly equal zero rows)."""
+    err, scale = row_stats(got, ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(scale > 0, err / scale, np.where(err > 0, np.inf, 0.0))
+    return float(r.max()) if r.size else 0.0
+
+
+def assert_parity(got, ref, atol: float, rtol: float = REL_TOL, what=""):
+    fails = parity_failures(got, ref, atol, rtol)
+    assert not fails, (what, fails)
+    err, _ = row_stats(got, ref)
+    return float(err.max()) if err.size else 0.0, worst_ratio(got, ref)

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 203
+    assert lbsa.lib().lbsa_version() == 204
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -193,3 +193,11 @@ def test_timing_hook_arms_and_disarms_without_a_gpu():
     L = lbsa.lib()
     assert L.lbsa_time_next_kernel(None, None) == 0
     lbsa.time_next_kernel(None, None)
+    vp = ctypes.c_void_p
+    arr = (vp * 9)()
+    assert L.lbsa_time_next_kernels(0, None, None) == 0
+    assert L.lbsa_time_next_kernels(9, arr, arr) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_time_next_kernels(-1, arr, arr) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_time_next_kernels(2, None, arr) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_time_next_kernels(2, arr, arr) == 0       # NULL events: armed, nothing stamped
+    lbsa.time_next_kernels([])

@@ -42,18 +42,44 @@ def test_summarize_statistics():
 
 
 def test_traffic_reported_only_for_its_source_and_workload(tmp_path, monkeypatch):
-    rec = {"source_sha256": bench.source_sha(bench.SPLIT_SRC), "kernel": "split_kernel", "workload": "tp8_share",
-           "bytes_per_launch": 123}
+    ok = bench.source_sha(bench.SPLIT_SRC)
     f = tmp_path / "traffic.json"
-    f.write_text(json.dumps(rec))
+    doc = {"kernel": "split_kernel", "workloads": {
+        "long": {"source_sha256": ok, "workload": "long", "bytes_per_launch": 123},
+        "tp8_share": {"source_sha256": "0" * 64, "workload": "tp8_share", "bytes_per_launch": 7}}}
+    f.write_text(json.dumps(doc))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.traffic_from_profile("tp8_share") == 123
-    assert bench.traffic_from_profile("skewed") is None
-    rec["source_sha256"] = "0" * 64
-    f.write_text(json.dumps(rec))
-    assert bench.traffic_from_profile("tp8_share") is None
+    assert bench.traffic_from_profile("long") == 123
+    assert bench.traffic_from_profile("tp8_share") is None      # taken on another kernel source
+    assert bench.traffic_from_profile("skewed") is None         # never taken
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
-    assert bench.traffic_from_profile("tp8_share") is None
+    assert bench.traffic_from_profile("long") is None
+
+
+def test_write_traffic_keeps_one_entry_per_workload(tmp_path, monkeypatch):
+    """Two PMC runs (FETCH_SIZE, WRITE_SIZE) become one entry; an entry of
+    another workload already in the file is kept."""
+    def run_dir(name, counter, calib_kib, split_kib):
+        d = tmp_path / name
+        d.mkdir()
+        rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value",
+                f'1,"__amd_rocclr_copyBuffer",{counter},{calib_kib}',
+                f'2,"void lbsa::split_kernel<false, 1>(lbsa::AttnArgs)",{counter},{split_kib}',
+                f'3,"void lbsa::split_kernel<false, 1>(lbsa::AttnArgs)",{counter},{split_kib}']
+        (d / "x_counter_collection.csv").write_text("\n".join(rows) + "\n")
+        return str(d)
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps({"kernel": "split_kernel", "workloads": {"tp8_share": {"bytes_per_launch": 1}}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    calib = bench.CALIB_BYTES / 1024.0
+    bench.write_traffic(run_dir("fetch", "FETCH_SIZE", 2 * calib, 1000.0),
+                        run_dir("write", "WRITE_SIZE", calib, 10.0), "long")
+    doc = json.loads(f.read_text())
+    assert set(doc["workloads"]) == {"tp8_share", "long"}
+    e = doc["workloads"]["long"]
+    assert e["fetch"]["factor"] == 0.5 and e["write"]["factor"] == 1.0
+    assert e["bytes_per_launch"] == round(1000.0 * 1024 * 0.5 + 10.0 * 1024)
+    assert bench.traffic_from_profile("long") == e["bytes_per_launch"]
 
 
 def test_more_than_one_gpu_is_refused():

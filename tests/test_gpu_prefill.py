@@ -49,8 +49,7 @@ def test_prefill_matches_oracle(oracle_mod, sl, ql, Hq, Hkv):
     got = run(batch)
     ref, _ = oracle_mod.attention(batch)
     assert got.shape == ref.shape
-    assert np.isfinite(got).all()
-    assert np.abs(got - ref).max() <= H.BF16_TOL
+    H.check(batch, got, ref, ("prefill", ql, Hq, Hkv))
 
 
 @pytest.mark.parametrize("B,Hkv,QL,expect_cb", [(4, 8, 256, 2), (8, 8, 100, 1), (2, 2, 96, 1)])
@@ -61,8 +60,7 @@ def test_prefill_each_block_width(oracle_mod, B, Hkv, QL, expect_cb):
                                 q_len=QL), gen_device="cuda:0")
     got = run(batch)
     ref, _ = oracle_mod.attention(batch)
-    assert np.isfinite(got).all()
-    assert np.abs(got - ref).max() <= H.BF16_TOL
+    H.check(batch, got, ref, ("prefill block width", B, Hkv, QL))
 
 
 def test_queries_that_see_nothing_and_empty_requests(oracle_mod):
@@ -72,7 +70,7 @@ def test_queries_that_see_nothing_and_empty_requests(oracle_mod):
     got = run(batch)
     ref, _ = oracle_mod.attention(batch)
     assert (got[0, :5] == 0).all() and (got[1] == 0).all()
-    assert np.abs(got - ref).max() <= H.BF16_TOL
+    H.check(batch, got, ref, "prefill empty queries")
 
 
 def test_one_token_prefill_equals_decode(oracle_mod):
@@ -95,10 +93,10 @@ def test_table4_shapes_sampled(oracle_mod, name):
     rng = np.random.default_rng(7)
     # first, last and random queries, heads across group boundaries
     qs = sorted({0, QL - 1, *rng.integers(0, QL, 4).tolist()})
-    rows = np.array([(b, qi * Hq + hq) for b in range(B) for qi in qs for hq in (0, 7, 8, 63)], np.int32)
+    rows = np.array([(b, qi * Hq + hq) for b in range(B) for qi in qs for hq in range(Hq)], np.int32)
     ref, _ = oracle_mod.attention_rows(batch, rows)
     sub = got.reshape(B, QL * Hq, 128)[rows[:, 0], rows[:, 1]]
-    assert np.abs(sub - ref).max() <= H.BF16_TOL
+    H.check(batch, sub, ref, ("table4", name))
 
 
 def test_bad_page_poisons_the_queries_that_read_it():

@@ -147,9 +147,7 @@ def test_prologue_feeds_decode(oracle_mod, kv_dtype):
     out = H.decode(batch, H.plan(batch, P), P)
     torch.cuda.synchronize()
     ref, _ = oracle_mod.attention(batch)
-    got = H.out_np(out)
-    assert np.isfinite(got).all()
-    assert np.abs(got - ref).max() <= H.tol(batch)
+    H.check(batch, H.out_np(out), ref, f"prologue -> decode {kv_dtype}")
     # the written K row of each request is the rotated, normalised key
     _, k_ref, _ = oracle_mod.prologue(inp["qkv"], pos.to(torch.int32), inp["q_weight"].double().numpy(),
                                       inp["k_weight"].double().numpy(), Hq, Hkv, inp["theta"], inp["eps"])

@@ -49,7 +49,9 @@ def test_stamped_split_and_combine_match_plain_launches():
     assert ev[3].elapsed_time(ev[4]) == comb_ms
 
 
-def test_rejected_call_leaves_hook_armed_for_the_next_launch():
+def test_rejected_call_disarms_the_hook():
+    """An entry point that rejects its arguments launches nothing and disarms
+    the hook: the next, valid launch does not stamp the events."""
     batch = H.batch_on_gpu("tp8_share")
     P = H.workgroups(batch)
     tm = H.plan(batch, P)
@@ -58,10 +60,31 @@ def test_rejected_call_leaves_hook_armed_for_the_next_launch():
     for e in ev:
         e.record(stream)
     torch.cuda.synchronize()
+    before = ev[0].elapsed_time(ev[1])
     lbsa.time_next_kernel(ev[0], ev[1])
     with pytest.raises(lbsa.LbsaError):
         H.decode_split(batch, tm, P, workspace=torch.empty(16, dtype=torch.uint8, device="cuda:0"))
     H.decode_split(batch, tm, P)
     torch.cuda.synchronize()
-    assert ev[0].elapsed_time(ev[1]) > 0.010     # the split kernel's own ~30 us, not two adjacent markers
-    lbsa.time_next_kernel(None, None)
+    assert ev[0].elapsed_time(ev[1]) == before       # the split launch left the events alone
+
+
+def test_one_call_stamps_split_and_combine():
+    """lbsa_decode launches two kernels; two armed pairs stamp one each, in order."""
+    batch = H.batch_on_gpu("tp8_share")
+    P = H.workgroups(batch)
+    tm = H.plan(batch, P)
+    ref = H.decode(batch, tm, P).clone()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record(stream)
+    torch.cuda.synchronize()
+    lbsa.time_next_kernels([(ev[0], ev[1]), (ev[2], ev[3])])
+    out = H.decode(batch, tm, P)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    split_ms, comb_ms = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    print(f"split {1000 * split_ms:.2f} us, combine {1000 * comb_ms:.2f} us", flush=True)
+    assert split_ms > 0.005 and comb_ms > 0.0
+    assert ev[1].elapsed_time(ev[2]) >= 0.0          # the combine starts after the split ends

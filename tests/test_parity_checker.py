@@ -1,0 +1,125 @@
+"""CPU pins of the parity bar (tests/parity.py) on long rows.
+
+At L = 131072 every entry of an attention row of N(0, 1) values is below 2e-2,
+so the absolute bound alone cannot tell a correct row from a zeroed one.  These
+tests show that the scale-aware bound can, and that it is not too tight: a
+model of exactly the roundings the kernels make (p in fp32, p rounded to bf16
+for P.V, fp32 denominator, bf16 output) passes with room to spare, while a
+zeroed row, a row off by 3% and a row merged without one of its chunks fail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import parity
+from load_balanced_split_assign_amd import workload as wl
+
+
+def _bf16(x):
+    """bf16 rounding (to nearest even) of fp32 values, back as float64."""
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _dense(oracle_mod, batch, b=0):
+    """Request b's live K and V (float64 values; fp8: codes times scales) and its
+    V scales [L, Hkv] (ones for bf16)."""
+    L = int(batch["seqlens"][b])
+    pt = batch["page_table"][b].numpy()
+    pages = pt[: (L + 63) // 64]
+    if batch["kv_dtype"] == "bf16":
+        k = oracle_mod.bf16_values(batch["k_cache"].view(torch.int16)[pages])
+        v = oracle_mod.bf16_values(batch["v_cache"].view(torch.int16)[pages])
+        vs = np.ones(k.shape[:3])
+    else:
+        k = oracle_mod.e4m3_values(batch["k_cache"].view(torch.uint8)[pages])
+        v = oracle_mod.e4m3_values(batch["v_cache"].view(torch.uint8)[pages])
+        ks = batch["k_scale"][pages].numpy().transpose(0, 2, 1)      # [pages, 64, Hkv]
+        vs = batch["v_scale"][pages].numpy().transpose(0, 2, 1)
+        k = k * ks[..., None]
+        v = v.copy()                                                   # codes: the scale goes into p
+    Hkv = k.shape[2]
+    k = k.reshape(-1, Hkv, 128)[:L]
+    v = v.reshape(-1, Hkv, 128)[:L]
+    vs = np.asarray(vs).reshape(-1, Hkv)[:L]
+    return k, v, vs
+
+
+def _q(oracle_mod, batch, b=0):
+    if batch["kv_dtype"] == "bf16":
+        return oracle_mod.bf16_values(batch["q"].view(torch.int16)[b])
+    return oracle_mod.e4m3_values(batch["q"].view(torch.uint8)[b]) * batch["q_scale"][b].numpy()[:, None]
+
+
+def rounding_model(oracle_mod, batch, b=0):
+    """Output rows of request b with the kernels' roundings: fp32 p, bf16 p (times
+    the V scale for fp8) in P.V, fp32 weight sum, bf16 output."""
+    k, v, vs = _dense(oracle_mod, batch, b)
+    q = _q(oracle_mod, batch, b)
+    Hq, Hkv = q.shape[0], k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((Hq, 128))
+    for hq in range(Hq):
+        h = hq // G
+        s = batch["softmax_scale"] * (k[:, h, :] @ q[hq])
+        p32 = np.exp(s - s.max()).astype(np.float32).astype(np.float64)
+        pb = _bf16(p32 * vs[:, h])
+        out[hq] = _bf16((pb @ v[:, h, :]) / p32.sum())
+    return out
+
+
+@pytest.fixture(scope="module")
+def long_row(oracle_mod):
+    batch = wl.make_batch(seqlens=[131072], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=40, tail="nan")
+    ref, _ = oracle_mod.attention(batch)
+    return batch, ref[0]
+
+
+def test_absolute_bound_alone_cannot_see_a_zeroed_long_row(long_row):
+    _, ref = long_row
+    assert np.abs(ref).max() < parity.BF16_TOL          # every entry below the absolute bound
+    assert not parity.parity_failures(np.zeros_like(ref), ref, parity.BF16_TOL, rtol=np.inf)
+
+
+def test_zeroed_long_row_is_rejected(long_row):
+    _, ref = long_row
+    fails = parity.parity_failures(np.zeros_like(ref), ref, parity.BF16_TOL)
+    assert fails and "relative bound" in fails[-1]
+
+
+def test_three_percent_off_is_rejected(long_row):
+    _, ref = long_row
+    assert parity.parity_failures(0.97 * ref, ref, parity.BF16_TOL)
+
+
+def test_kernel_rounding_model_passes_with_room(oracle_mod, long_row):
+    batch, ref = long_row
+    got = rounding_model(oracle_mod, batch)
+    assert not parity.parity_failures(got, ref, parity.BF16_TOL)
+    ratio = parity.worst_ratio(got, ref)
+    print(f"rounding model, L = 131072 bf16: worst row ratio {ratio:.2e} (bound {parity.REL_TOL:.2e})")
+    assert ratio < 0.6 * parity.REL_TOL
+
+
+@pytest.mark.parametrize("L,kv", [(37, "bf16"), (4097, "bf16"), (65536, "fp8"), (700, "fp8")])
+def test_kernel_rounding_model_passes_other_lengths(oracle_mod, L, kv):
+    batch = wl.make_batch(seqlens=[L], num_heads=64, num_kv_heads=8, kv_dtype=kv, seed=41, tail="nan")
+    ref, _ = oracle_mod.attention(batch)
+    got = rounding_model(oracle_mod, batch)
+    assert not parity.parity_failures(got, ref[0], parity.abs_tol(kv))
+    print(f"rounding model, L = {L} {kv}: worst row ratio {parity.worst_ratio(got, ref[0]):.2e}")
+
+
+def test_row_missing_one_chunk_is_rejected(oracle_mod, long_row):
+    """The long request cut into 26 chunks as a bin walk would cut it; merging all
+    but one of them is a plausible combine mistake, and the bar must see it."""
+    batch, ref = long_row
+    n = 131072 // 64
+    cuts = np.linspace(0, n, 27).astype(int)
+    desc = np.array([(0, 0, cuts[i], cuts[i + 1]) for i in range(26)], np.int32)
+    po, pl = oracle_mod.partials(batch, desc)
+    full = np.stack([oracle_mod.merge(po[:, g], pl[:, g])[0] for g in range(8)])
+    assert not parity.parity_failures(full, ref, parity.BF16_TOL, rtol=1e-9)   # the merge itself is exact
+    for drop in (0, 13, 25):
+        keep = [i for i in range(26) if i != drop]
+        part = np.stack([oracle_mod.merge(po[keep, g], pl[keep, g])[0] for g in range(8)])
+        assert parity.parity_failures(part, ref, parity.BF16_TOL), drop
