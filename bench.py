@@ -238,6 +238,7 @@ def time_static(batch, S, steps, warmup, flush, stamps=False):
         ev[i][0].record(stream)
         run()
         ev[i][1].record(stream)
+    torch.cuda.synchronize()
     res = summarize([1000.0 * a.elapsed_time(b) for a, b in ev])
     if stamps:
         kev = [_pairs(2) for _ in range(steps)]

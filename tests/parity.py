@@ -12,27 +12,35 @@ a row is about 0.02, and an all-zero output would pass the absolute bound alone.
 The relative bound scales with the row and rejects that.
 
 Where REL_TOL comes from.  The kernels compute the scores in fp32 from exact
-products, exponentiate in fp32 and sum the weights p_t in fp32; the rounding
-that matters is the one of p_t to bf16 for the P.V matrix product, and the
+products, exponentiate in fp32 and sum the weights p_t in fp32; the roundings
+that matter are the one of p_t to bf16 for the P.V matrix product and the
 final rounding of the output to bf16:
 
 * output rounding: |bf16(x) - x| <= 2^-9 |x| <= 2^-9 max|ref| per entry;
 * P rounding: with p~_t = p_t (1 + d_t), |d_t| <= 2^-9 (round to nearest
-  even, unbiased), the output moves by e = sum_t p_t d_t v_t / sum_t p_t.  The
-  same weighted sum without d_t is the output itself, and for independent
-  values its typical size is sqrt(sum p^2 v^2) / sum p, so e is about
-  2^-9 / sqrt(3) = 1.1e-3 of the row's typical entry; a 5-sigma excursion of e
-  over 4096 rows x 128 dims is 5.6e-3 of a typical entry, and a row's largest
-  entry is at least twice its typical one, which gives 2.8e-3 max|ref|.
+  even, unbiased, standard deviation 2^-9 / sqrt(3) = 1.13e-3), the output
+  moves by e = sum_t p_t d_t v_t / sum_t p_t.  The same weighted sum without
+  d_t is the output itself, so for independent values e is close to normal
+  with a standard deviation of 1.13e-3 times the row's typical entry.  Over
+  the ~10^6 entries of a full-size test its largest excursion is about 5.5
+  standard deviations, and a row's largest entry is at least ~1.8 times its
+  typical one (the largest of 128 near-normal values), which bounds this term
+  by 5.5 x 1.13e-3 / 1.8 = 3.5e-3 max|ref|.
+* prefill also sums the rounded p~_t for its denominator, which adds a term of
+  the same size (partly cancelling): up to about 7.5e-3 max|ref| there.
 
-The two add up to 4.8e-3 max|ref|; REL_TOL = 2^-7 = 7.8e-3 keeps a factor 1.6
-above that.  The fp32 accumulation (relative 2^-24 per add), the fp32 exp2
-(about 1 ulp) and the fp32 LSE merge are three orders of magnitude smaller.
-fp8 K/V change none of this: the oracle works on the same dequantised values,
-and the per-token V scale is folded into p before the same bf16 rounding.
-tests/test_parity_checker.py pins the bound on the CPU: a model of exactly
-these roundings passes it with room on long rows, while a zeroed row, a row
-scaled by 0.97 and a row missing one of its chunks fail it.
+Decode then stays below 5.4e-3 max|ref| and prefill below 7.5e-3;
+REL_TOL = 2^-6 = 1.56e-2 keeps a factor 2 above both.  On MI355X the decode
+kernels' per-row ratios follow a model of exactly these roundings (skewed
+batch, 4096 rows: median 2.67e-3 against the model's 2.60e-3, 99.9th
+percentile 4.84e-3 against 4.62e-3, worst 5.5e-3; worst over every decode test
+6.5e-3, over the prefill tests 7.3e-3).  The fp32 accumulation (relative 2^-24
+per add), the fp32 exp2 (about 1 ulp) and the fp32 LSE merge are three orders
+of magnitude smaller.  fp8 K/V change none of this: the oracle works on the
+same dequantised values, and the per-token V scale is folded into p before the
+same bf16 rounding.  tests/test_parity_checker.py pins the bound on the CPU: a
+model of exactly these roundings passes it with room, while a zeroed row, a
+row off by 3% and a row merged without one of its chunks fail it.
 """
 from __future__ import annotations
 
@@ -40,7 +48,7 @@ import numpy as np
 
 BF16_TOL = 2e-2     # max |out - oracle| for bf16 KV (the target's bound)
 FP8_TOL = 6e-2      # max |out - oracle| for fp8-e4m3 KV (the target's bound)
-REL_TOL = 2.0 ** -7  # per row: max |out - oracle| <= REL_TOL * max |oracle| (derivation above)
+REL_TOL = 2.0 ** -6  # per row: max |out - oracle| <= REL_TOL * max |oracle| (derivation above)
 LSE_TOL = 1e-3      # |partial LSE - oracle| (natural log)
 
 
