@@ -208,6 +208,34 @@ int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                 float softmax_scale, const void* task_map_d, size_t task_map_bytes,
                 void* workspace_d, size_t workspace_bytes, void* out_d, void* stream);
 
+/*
+ * lbsa_decode with no workspace argument, for callers that cannot allocate
+ * device memory themselves (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split and combine kernels are
+ * lbsa_decode's; their partials live in a static device array of
+ * LBSA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates and frees nothing.
+ *   Arguments: those of lbsa_decode minus workspace_d / workspace_bytes; the
+ *   caller still owns q, the caches, the page table, the task map and out_d.
+ *   Limit: lbsa_workspace_bytes(batch, q_len, num_heads, num_kv_heads, 128, P)
+ *   must not exceed LBSA_NOALLOC_SCRATCH_BYTES, else LBSA_ERR_UNSUPPORTED and
+ *   nothing is enqueued (16 MiB: e.g. batch 64 x 8 KV heads with P = 1024 at
+ *   q_len 2).
+ *   The array is shared by every call on one GPU and keeps the last call's
+ *   partials: calls that overlap in time on one GPU (two streams, or two host
+ *   threads) race on it and must be serialised by the caller.  Nothing in it
+ *   needs to start at zero (every partial a call reads, it wrote first).
+ * The first call on a device looks the array's device address up
+ * (hipGetSymbolAddress); LBSA_ERR_HIP if that fails.
+ */
+#define LBSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int lbsa_decode_noalloc(const void* q_d, const float* q_scale_d, const void* k_cache_d, const void* v_cache_d,
+                        const float* k_scale_d, const float* v_scale_d, int32_t kv_dtype,
+                        const int32_t* page_table_d, int32_t batch, int32_t q_len, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t max_pages_per_seq,
+                        int64_t num_pages, int32_t num_workgroups, float softmax_scale, const void* task_map_d,
+                        size_t task_map_bytes, void* out_d, void* stream);
+
 /* The split half of lbsa_decode alone: fills the workspace partials of every
  * descriptor (slot d = descriptor d), single-chunk segments included.  Same
  * arguments as lbsa_decode without out_d. */

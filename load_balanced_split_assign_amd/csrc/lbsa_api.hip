@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "lbsa_internal.h"
 
 #define LBSA_API extern "C" __attribute__((visibility("default")))
@@ -343,6 +345,67 @@ LBSA_API int lbsa_decode(const void* q_d, const float* q_scale_d, const void* k_
     return decode_launch(c, out_d, stream);
 }
 
+// ---------------------------------------------------------------------------
+// lbsa_decode without a workspace argument, for callers that cannot allocate.
+// The partials live in `scratch`, a file-scope device array: every GPU the
+// library runs on holds its own copy until the process ends.  In host code the
+// name `scratch` is only a host-side stand-in; the kernels get the device
+// address that hipGetSymbolAddress returns for the stream's device, looked up
+// once per device (with that device current) and kept in scratch_ptr.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[LBSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];   // device address of `scratch` per device; nullptr until looked up
+
+// Device address of `scratch` on the device that runs `stream`.
+int scratch_address(hipStream_t stream, void** out) {
+    int dev = -1, cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return LBSA_ERR_HIP;
+    dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return LBSA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return LBSA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return LBSA_ERR_HIP;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) return LBSA_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return LBSA_OK;
+}
+}  // namespace
+
+LBSA_API int lbsa_decode_noalloc(const void* q_d, const float* q_scale_d, const void* k_cache_d,
+                                 const void* v_cache_d, const float* k_scale_d, const float* v_scale_d,
+                                 int32_t kv_dtype, const int32_t* page_table_d, int32_t batch, int32_t q_len,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                 int32_t max_pages_per_seq, int64_t num_pages, int32_t num_workgroups,
+                                 float softmax_scale, const void* task_map_d, size_t task_map_bytes, void* out_d,
+                                 void* stream) {
+    HookGuard guard;
+    DecodeCommon c = check_decode(q_d, q_scale_d, k_cache_d, v_cache_d, k_scale_d, v_scale_d, kv_dtype,
+                                  page_table_d, batch, q_len, num_heads, num_kv_heads, head_dim, page_size,
+                                  max_pages_per_seq, num_pages, softmax_scale);
+    if (c.status != LBSA_OK) return c.status;
+    if (num_workgroups <= 0 || !task_map_d || !out_d) return LBSA_ERR_INVALID_ARGUMENT;
+    size_t need = 0;
+    int s = lbsa_workspace_bytes(batch, q_len, num_heads, num_kv_heads, head_dim, num_workgroups, &need);
+    if (s != LBSA_OK) return s;
+    if (need > (size_t)LBSA_NOALLOC_SCRATCH_BYTES) return LBSA_ERR_UNSUPPORTED;   // partials do not fit
+    void* ws = nullptr;
+    s = scratch_address(static_cast<hipStream_t>(stream), &ws);
+    if (s != LBSA_OK) return s;
+    s = decode_prepare(c, batch, q_len, num_heads, num_kv_heads, head_dim, num_workgroups, task_map_d,
+                       task_map_bytes, ws, (size_t)LBSA_NOALLOC_SCRATCH_BYTES);
+    if (s != LBSA_OK) return s;
+    return decode_launch(c, out_d, stream);
+}
 
 LBSA_API int lbsa_decode_static(const void* q_d, const float* q_scale_d, const void* k_cache_d,
                                 const void* v_cache_d, const float* k_scale_d,

@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblbsa.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+NOALLOC_SCRATCH_BYTES = 16 << 20      # LBSA_NOALLOC_SCRATCH_BYTES
 KV_BF16, KV_FP8_E4M3 = 0, 1
 PAGE_SIZE, HEAD_DIM, GROUP, DEFAULT_MIN_TILES = 64, 128, 8, 2
 HEADER_FIELDS = ("T", "K", "q", "r", "Ndesc", "P", "F", "B", "Hq", "Hkv",
@@ -64,6 +65,7 @@ def lib() -> ctypes.CDLL:
         attn = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, i64, i32, f32, vp, sz, vp,
                 sz]
         L.lbsa_decode.argtypes = attn + [vp, vp]
+        L.lbsa_decode_noalloc.argtypes = attn[:-2] + [vp, vp]
         L.lbsa_decode_split.argtypes = attn + [vp]
         L.lbsa_decode_combine.argtypes = [i32, i32, i32, i32, i32, i32, vp, sz, vp, sz, vp, vp]
         L.lbsa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -78,7 +80,7 @@ def lib() -> ctypes.CDLL:
                                     vp, vp, vp, vp, vp, vp, i64, vp]
         for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes", "lbsa_prologue",
                    "lbsa_workspace_layout_get", "lbsa_workspace_bytes", "lbsa_static_workspace_bytes",
-                   "lbsa_plan", "lbsa_decode", "lbsa_decode_split", "lbsa_decode_combine",
+                   "lbsa_plan", "lbsa_decode", "lbsa_decode_noalloc", "lbsa_decode_split", "lbsa_decode_combine",
                    "lbsa_decode_static", "lbsa_prefill", "lbsa_router_split_weights",
                    "lbsa_router_workspace_bytes", "lbsa_router_gemm", "lbsa_time_next_kernel",
                    "lbsa_time_next_kernels"):
@@ -260,6 +262,22 @@ def decode(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softm
     _check("lbsa_decode", lib().lbsa_decode(*args, num_workgroups, float(softmax_scale), _ptr(task_map),
                                             task_map.numel(), _ptr(workspace), workspace.numel(), _ptr(out),
                                             _stream(q.device)))
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softmax_scale: float,
+                   q_scale=None, k_scale=None, v_scale=None, out=None):
+    """lbsa_decode_noalloc: split + combine with the partials in the library's
+    own device scratch array (no workspace; calls on one GPU must not overlap).
+    With `out` given, nothing is allocated on this path either."""
+    args, (B, QL, Hq, Hkv, D) = _attn_args(q, q_scale, k_cache, v_cache, k_scale, v_scale, page_table)
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, q)
+    _check_bytes(task_map, q.device, "task map")
+    _check("lbsa_decode_noalloc", lib().lbsa_decode_noalloc(*args, num_workgroups, float(softmax_scale),
+                                                            _ptr(task_map), task_map.numel(), _ptr(out),
+                                                            _stream(q.device)))
     return out
 
 
