@@ -133,7 +133,8 @@ def time_steps(path, steps, warmup, flush):
     `layer` = split + combine under one pair with the map built beforehand (as
     every layer runs); `*_kernel` = each kernel's own start-to-end stamps from the
     library's timing hook (no marker packets between the launches, so no added
-    dispatch gaps: the durations rocprofv3 reports)."""
+    dispatch gaps: the durations rocprofv3 reports) -- the assign kernel's in a
+    step, the split and combine kernels' in a layer."""
     import torch
 
     from load_balanced_split_assign_amd import lbsa
@@ -155,19 +156,25 @@ def time_steps(path, steps, warmup, flush):
         lay[i][0].record(stream)
         path.layer()
         lay[i][1].record(stream)
-    kev = [_pairs(3) for _ in range(steps)]
-    for e in kev:
+    aev = _pairs(steps)                             # the assign kernel, as in a step
+    kev = [_pairs(2) for _ in range(steps)]         # split and combine, as in a layer (map reused)
+    for e in [aev] + kev:
         for a, b in e:
             a.record(stream); b.record(stream)      # torch creates an event at its first record
     torch.cuda.synchronize()
     for i in range(steps):
         flush(i)
-        lbsa.time_next_kernels(kev[i])              # assign, then the split and the combine of decode
+        lbsa.time_next_kernels([aev[i]])
         path.assign(); path.layer()
+    path.assign()
+    for i in range(steps):
+        flush(i)
+        lbsa.time_next_kernels(kev[i])              # the split and the combine of decode
+        path.layer()
     torch.cuda.synchronize()
     us = lambda ps: [1000.0 * a.elapsed_time(b) for a, b in ps]  # noqa: E731
-    return {"step": us(whole), "layer": us(lay), "assign_kernel": us([e[0] for e in kev]),
-            "split_kernel": us([e[1] for e in kev]), "combine_kernel": us([e[2] for e in kev])}
+    return {"step": us(whole), "layer": us(lay), "assign_kernel": us(aev),
+            "split_kernel": us([e[0] for e in kev]), "combine_kernel": us([e[1] for e in kev])}
 
 
 def time_steps_graph(path, steps, warmup, flush):

@@ -86,6 +86,9 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     uint8_t* __restrict__ map) {
     extern __shared__ int smem[];
     __shared__ int red[2][kAssignThreads / 64];
+    // every kernel argument in one round trip, before anything uses one (else the
+    // compiler fetches them in several dependent rounds)
+    __asm__ volatile("" ::"s"(seqlens), "s"(map), "s"(B), "s"(Hq), "s"(Hkv), "s"(P), "s"(F), "s"(max_pages));
     const MapLayout L = map_layout(B, Hkv, P);
     int32_t* hdr = reinterpret_cast<int32_t*>(map + L.header);
     int32_t* bdb = reinterpret_cast<int32_t*>(map + L.bin_desc_begin);

@@ -87,7 +87,9 @@ template <bool FP8, int QL = 1> struct Stage {
     // descriptor's first tile; the waits count only the fixed ones, which can
     // only make them wait for a little more than the stage)
     static constexpr int LOADS = 2 * KV_LOADS + (FP8 ? 3 : 0);
-    static constexpr int STAGES = FP8 ? 2 : 3;   // ring depth: STAGES - 1 tiles in flight
+    // ring depth: STAGES - 1 tiles in flight per wave (a 3-stage fp8 ring, which
+    // fits once the merge slot lives in the ring, measured 3% slower)
+    static constexpr int STAGES = FP8 ? 2 : 3;
 };
 static_assert((Stage<false>::STAGES - 1) * Stage<false>::LOADS < 64, "vmcnt range");
 static_assert((Stage<true>::STAGES - 1) * Stage<true>::LOADS < 64, "vmcnt range");
@@ -109,17 +111,24 @@ template <bool FP8> __device__ inline int swz_vrow(int row) { return FP8 ? swz_v
 // asynchronous load an LDS read depends on (distinct underlying objects) and
 // does not fall back to waiting for all of them.
 //
-// Each wave has one slot (Slot::kWave bytes) that holds its (O, m, l, flag) for
-// the merge at the end of a descriptor.  fp8 with QL = 2 merges O in two passes
-// of 64 dims (the slot holds half of O), so that two workgroups fit a CU.
+// At the end of a descriptor each wave puts its (O, m, l, flag) in a merge slot.
+// bf16: one slot per wave (Slot::kWave bytes) of its own.  fp8: the wave's slice
+// of the ring stage it has just computed -- that stage is consumed, and no
+// load targets it again before the merge's closing barrier (the next load into
+// it is issued in the following step) -- so the fp8 ring gets one more stage
+// in the same LDS (two workgroups per CU).  fp8 with QL = 2 merges O in two
+// passes of 64 dims (a slot holds half of O).
 template <bool FP8, int QL> struct Slot {
     static constexpr int kRows = kGroup * QL;                          // query rows of a descriptor
     static constexpr int kPasses = (FP8 && QL == 2) ? 2 : 1;           // passes over the 128 dims
     static constexpr int kDims = kHeadDim / kPasses;                   // dims of O per pass
     static constexpr int kMerge = (kRows * kDims + 2 * kRows + 4) * 4;   // O (one pass), m, l, flag per wave
-    static constexpr int kWave = (kMerge + 255) / 256 * 256;           // 256-aligned
-    static constexpr int kBytes = kWaves * kWave;
+    static constexpr bool kInStage = FP8;                              // merge in the consumed ring stage
+    static constexpr int kWave = kInStage ? Stage<FP8, QL>::BYTES : (kMerge + 255) / 256 * 256;   // slot stride
+    static constexpr int kBytes = kInStage ? 16 : kWaves * kWave;      // the separate slot array
 };
+static_assert(Slot<true, 1>::kMerge <= Stage<true, 1>::BYTES && Slot<true, 2>::kMerge <= Stage<true, 2>::BYTES,
+              "an fp8 merge slot fits the wave's stage slice");
 constexpr int kMaxStages = 6;
 template <bool FP8> struct Smem {
     lds_char* stage[kMaxStages];   // [kWaves][Stage::BYTES] each; the first STAGES are used
@@ -458,9 +467,11 @@ struct MapDescs {           // descriptors [d0, d0 + n) of a task-map bin
     __device__ Desc first() const { return check(0, head); }
     // descriptor i >= 1 of the bin (loaded from the map).  The cursors read the
     // head record only in first(), so it is dead inside the stream loop.
-    __device__ Desc get(int i) const {
+    __device__ Desc get(int i) const { return check(i, raw(i)); }
+    // the raw record of descriptor i >= 1 (loads; validated by check)
+    __device__ RawDesc raw(int i) const {
         const int d = d0 + i;
-        return check(i, RawDesc{desc[4 * d], desc[4 * d + 1], desc[4 * d + 2], desc[4 * d + 3], dlen[d]});
+        return RawDesc{desc[4 * d], desc[4 * d + 1], desc[4 * d + 2], desc[4 * d + 3], dlen[d]};
     }
     // an invalid descriptor (corrupt map) has no tiles
     __device__ Desc check(int i, RawDesc x) const {
@@ -483,6 +494,8 @@ struct OneDesc {            // the static kernel's single chunk
     __device__ int count() const { return 1; }
     __device__ Desc first() const { return d; }
     __device__ Desc get(int) const { return d; }
+    __device__ RawDesc raw(int) const { return RawDesc{d.h, d.b, d.t0, d.t1, d.L}; }
+    __device__ Desc check(int, RawDesc) const { return d; }
 };
 
 // Cursor over the tiles of a descriptor source (wave-uniform).  Past the last
@@ -515,6 +528,26 @@ struct Cursor {
     __device__ void next() {
         if (++t >= d.t1) { ++i; seek_valid(); }
     }
+    // The load cursor: the record of descriptor i + 1 is loaded when descriptor
+    // i is entered, so it has arrived -- behind the ring wait of the steps in
+    // between -- by the time the cursor switches to it, and a switch waits for
+    // no map load.
+    RawDesc nx;
+    __device__ void begin_prefetching(const Src* s) {
+        begin(s);
+        if (i + 1 < src->count()) nx = src->raw(i + 1);
+    }
+    __device__ void next_prefetched() {
+        if (++t < d.t1) return;
+        ++i;
+        while (i < src->count()) {
+            const Desc x = src->check(i, nx);
+            if (i + 1 < src->count()) nx = src->raw(i + 1);
+            if (x.t1 > x.t0) { d = x; t = x.t0; return; }
+            ++i;
+        }
+        t = max(d.t0, d.t1 - 1);
+    }
 };
 
 // Issue the next tile of the load cursor into ring stage `slot` (and, when it
@@ -535,7 +568,7 @@ __device__ inline void issue_step(const AttnArgs& a, const LaneLoads<FP8>& ll, C
     if (!real) d.L = 0;     // past the end: every row counts as dead, so only row 0 of the page is read
     issue_tile<FP8, QL>(a, ll, st, ok ? page : 0, d, lc.t, w);
     if (++issued < ntiles) {
-        lc.next();
+        lc.next_prefetched();
         page = uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
     }
 }
@@ -557,7 +590,7 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
 
     // load cursor: runs S-1 tiles ahead of the compute cursor
     Cursor<Src> lc;
-    lc.begin(&src);
+    lc.begin_prefetching(&src);
     int issued = 0;
     int page = uniform_ptr<int32_t>(a.page_table)[(size_t)lc.d.b * a.max_pages + lc.t];
     uint32_t bad_bits = 0;          // bit u: the tile in stage u has an out-of-range page id
@@ -598,7 +631,9 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
                 }
                 bad |= (bad_bits >> u) & 1u;
                 tile_compute<FP8, QL>(stage(u), q, sl2, 64 * cc.t, cc.d.L + lim_off, w, r, g, ws);
-                if (cc.t + 1 == cc.d.t1) finish_desc<FP8, QL>(a, sm.merge, ws, bad, cc.d, w, lane, r, g);
+                if (cc.t + 1 == cc.d.t1)
+                    finish_desc<FP8, QL>(a, Slot<FP8, QL>::kInStage ? sm.stage[u] : sm.merge, ws, bad, cc.d, w, lane,
+                                         r, g);
                 cc.next();
             }
         }
@@ -626,6 +661,35 @@ __device__ void run_stream(const AttnArgs& a, const Src& src, int ntiles, const 
 // One workgroup per bin (grid = P).  The header words and the bin's head
 // record are independent loads, so the first page-table and K/V loads follow
 // after a single round trip to the map.
+// Keeps a loaded value (and so its load) alive up to this point without using
+// it: a compiler-only barrier, no instruction.  Used to make loads that the
+// compiler would otherwise sink into later branches go out together.
+__device__ inline void keep(int x) { __asm__ volatile("" ::"s"(x)); }
+__device__ inline void keep(const void* p) { __asm__ volatile("" ::"s"(p)); }
+__device__ inline void keep(float x) { __asm__ volatile("" ::"s"(x)); }
+
+// The kernel arguments the tile stream reads, fetched in the kernel's first
+// round trip rather than after the map checks.
+template <bool FP8>
+__device__ inline void keep_stream_args(const AttnArgs& a) {
+    keep(a.q);
+    keep(a.k_cache);
+    keep(a.v_cache);
+    keep(a.page_table);
+    keep(a.scale_log2);
+    if constexpr (FP8) {
+        keep(a.q_scale);
+        keep(a.k_scale);
+        keep(a.v_scale);
+    }
+}
+
+// One workgroup per bin (grid = P).  Every map word the start needs -- the
+// header words and the bin's head record -- is loaded up front and checked in a
+// single branch, so the loads go out together and the first page-table and
+// K/V loads follow after one round trip to the map (checked one by one, the
+// compiler sinks each load into the branch that tests it, and the start takes
+// a round trip per check).
 template <bool FP8, int QL>
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
     LBSA_DECLARE_SMEM(FP8, QL);
@@ -633,13 +697,37 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
     const int j = blockIdx.x;
     const auto* hdr = uniform_ptr<int32_t>(a.map + ML.header);
     const auto* rec = uniform_ptr<int32_t>(a.map + ML.bin_head) + (size_t)kBinHeadWords * j;
+    // The combine kernel starts by reading each segment's chunk range: the
+    // workgroups load one word of each 64-byte line of those two arrays (8 bytes
+    // per segment, contiguous; the index is clamped into them) in the same round
+    // trip as their own map words, so that the combine finds them in the
+    // caches.  The load is asm, issued before the map loads (its memory clobber
+    // keeps them after it), so the wait for the map words covers it too; its
+    // register stays live (keep, below) until after that wait, since the load
+    // writes it whenever it returns.
+    const int seg_words = 2 * a.Hkv * a.B;
+    const int32_t* seg_line = reinterpret_cast<const int32_t*>(a.map + ML.seg_first_desc) + min(16 * j, seg_words - 1);
+    int touched;
+    __asm__ volatile("s_load_dword %0, %1, 0x0" : "=s"(touched) : "s"(seg_line) : "memory");
     const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
     const int h_k = hdr[LBSA_HDR_K], h_q = hdr[LBSA_HDR_Q], h_r = hdr[LBSA_HDR_R];
     const int r_h = rec[BH_H], r_b = rec[BH_B], r_t0 = rec[BH_T0], r_t1 = rec[BH_T1];
     const int r_first = rec[BH_FIRST], r_count = rec[BH_COUNT], r_len = rec[BH_L];
-    if (h_err != 0 || h_p != a.P || h_b != a.B || h_hkv != a.Hkv) return;
     const int cap = a.Hkv * a.B + a.P;
-    if (r_count <= 0 || r_first < 0 || r_count > cap - r_first) return;
+    // tiles of bin j from the header's bin sizes (the descriptors' tiles sum to it)
+    const int ntiles = min(h_q + (j < h_r ? 1 : 0), a.B * a.max_pages) * (j < h_k ? 1 : 0);
+    const bool run = (h_err == 0) & (h_p == a.P) & (h_b == a.B) & (h_hkv == a.Hkv) & (r_count > 0) &
+                     (r_first >= 0) & (r_count <= cap - r_first) & (ntiles > 0);
+    keep(h_q);
+    keep(h_r);
+    keep(r_h);
+    keep(r_b);
+    keep(r_t0);
+    keep(r_t1);
+    keep(r_len);
+    keep_stream_args<FP8>(a);
+    keep(touched);   // waited for with the map words: from here its register is the compiler's again
+    if (!run) return;
     MapDescs src;
     src.desc = uniform_ptr<int32_t>(a.map + ML.desc);
     src.dlen = uniform_ptr<int32_t>(a.map + ML.desc_len);
@@ -649,9 +737,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
     src.B = a.B;
     src.max_pages = a.max_pages;
     src.head = RawDesc{r_h, r_b, r_t0, r_t1, r_len};
-    // tiles of bin j from the header's bin sizes (the descriptors' tiles sum to it)
-    const int ntiles = j < h_k ? min(h_q + (j < h_r ? 1 : 0), a.B * a.max_pages) : 0;
-    if (ntiles > 0) run_stream<FP8, QL>(a, src, ntiles, sm);
+    run_stream<FP8, QL>(a, src, ntiles, sm);
 }
 
 template <bool FP8, int QL>
@@ -662,6 +748,10 @@ __global__ __launch_bounds__(kSplitThreads) void static_kernel(AttnArgs a) {
     const int rest = blockIdx.x / S;
     const int b = rest % a.B, h = rest / a.B;
     const int slot = (h * a.B + b) * S + split;
+    // every kernel argument in one round trip, before the length is loaded
+    __asm__ volatile("" ::"s"(a.q), "s"(a.k_cache), "s"(a.v_cache), "s"(a.page_table), "s"(a.seqlens),
+                     "s"(a.part_lse), "s"(a.part_o), "s"(a.scale_log2), "s"(a.num_pages), "s"(a.max_pages));
+    if constexpr (FP8) __asm__ volatile("" ::"s"(a.q_scale), "s"(a.k_scale), "s"(a.v_scale));
     int L = uniform_ptr<int32_t>(a.seqlens)[b];
     const bool len_ok = L >= 0 && L <= a.max_pages * kTile;
     if (!len_ok) L = 0;
@@ -709,17 +799,23 @@ __device__ inline void merge_chunk(float l, f32x4 x, float& m, float& wsum, f32x
 // chunks c0, c0 + 8, ... of the row with a running (max LSE, weight sum,
 // weighted O).  The loads of up to kCombineUnroll chunks per slice (64 per
 // row) are all issued before the first of them is used, so a row of up to 64
-// chunks costs one round trip to the partials after the one to the map.  The 8
+// chunks costs one round trip to the partials after the one to the map (16
+// per slice needed more registers, and the lower occupancy cost more than the
+// round trips it saved).  The 8
 // slice states are then merged through LDS under the global maximum.  With
 // a.direct_out, a row whose segment has a single chunk was written by the split
 // kernel, and its workgroup stops after reading the chunk count.
 constexpr int kCombineUnroll = 8;
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, int static_mode) {
+template <bool STATIC>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
     constexpr int kSlices = 8;
     __shared__ float red_m[kSlices];
     __shared__ float red_w[kSlices];
     __shared__ int red_nan;
     __shared__ __attribute__((aligned(16))) float red_o[kSlices][kHeadDim];
+    // every kernel argument in one round trip, before anything uses one
+    __asm__ volatile("" ::"s"(a.map), "s"(a.part_lse), "s"(a.part_o), "s"(a.out), "s"(a.Hq), "s"(a.QL), "s"(a.B),
+                     "s"(a.Hkv), "s"(a.P), "s"(a.direct_out));
     const int row = blockIdx.x;                         // (b * QL + query) * Hq + hq
     const int bq = row / a.Hq, hq = row - bq * a.Hq;
     const int b = bq / a.QL, qi = bq - b * a.QL;
@@ -731,12 +827,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
     int64_t d0 = 0;
     int n = 0;
     bool poison = false;
-    if (static_mode) {
+    if constexpr (STATIC) {
         d0 = seg * a.P;
         n = a.P;
     } else {
-        // header words and the segment's chunk range are independent loads
-        // (the segment index is in range for any map of this shape)
+        // the header words and the segment's chunk range: independent loads in
+        // one round trip, checked together (the segment index is in range for
+        // any map of this shape)
         const MapLayout ML = map_layout(a.B, a.Hkv, a.P);
         const auto* hdr = uniform_ptr<int32_t>(a.map + ML.header);
         const int h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
@@ -744,11 +841,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
         const int sd0 = uniform_ptr<int32_t>(a.map + ML.seg_first_desc)[seg];
         const int sn = uniform_ptr<int32_t>(a.map + ML.seg_num_chunks)[seg];
         const int cap = a.Hkv * a.B + a.P;
-        if (h_p != a.P || h_b != a.B || h_hkv != a.Hkv || h_err != 0 || sd0 < 0 || sn < 0 || sn > cap - sd0) {
-            // a map built for another shape, or one whose lengths were invalid
-            // (the split kernel computed nothing): every row is NaN
-            poison = true;
-        } else {
+        // a map built for another shape, or one whose lengths were invalid (the
+        // split kernel computed nothing): every row is NaN
+        poison = (h_p != a.P) | (h_b != a.B) | (h_hkv != a.Hkv) | (h_err != 0) | (sd0 < 0) | (sn < 0) |
+                 (sn > cap - sd0);
+        keep(a.direct_out);
+        keep(sd0);
+        keep(sn);
+        if (!poison) {
             d0 = sd0;
             n = sn;
             if (a.direct_out && n == 1) return;         // the split kernel wrote this row
@@ -763,18 +863,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a, in
     for (int c0 = slice; c0 < n; c0 += kCombineUnroll * kSlices) {
         float l[kCombineUnroll];
         f32x4 x[kCombineUnroll];
-        // unconditional loads (a chunk past the row's last one re-reads the last
-        // one, in bounds, and is then dropped), so the compiler emits them as
-        // one straight run with no branch between them
+        // every load first (a slice past the row's last chunk loads nothing), then
+        // the merges
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) {
-            const int c = min(c0 + u * kSlices, n - 1);
-            l[u] = a.part_lse[pr(c)];
-            x[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr(c) * kHeadDim + d4);
+            const int c = c0 + u * kSlices;
+            if (c < n) {
+                l[u] = a.part_lse[pr(c)];
+                x[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr(c) * kHeadDim + d4);
+            } else {
+                l[u] = kNegInf;
+                x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u)
-            merge_chunk(c0 + u * kSlices < n ? l[u] : kNegInf, x[u], m, wsum, o, nan_seen);
+        for (int u = 0; u < kCombineUnroll; ++u) merge_chunk(l[u], x[u], m, wsum, o, nan_seen);
     }
     __syncthreads();                                    // red_nan initialised
     if (nan_seen) red_nan = 1;
@@ -829,7 +932,8 @@ hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
 
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream) {
     const long long grid = (long long)a.B * a.QL * a.Hq;
-    return launch(combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a, static_mode ? 1 : 0);
+    if (static_mode) return launch(combine_kernel<true>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a);
+    return launch(combine_kernel<false>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a);
 }
 
 hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu) {
