@@ -37,7 +37,13 @@ CFLAGS = [
 # carried around the k loop, the allocator reshuffles them with accvgpr moves
 # on every iteration.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA = {"lbsa_prefill.hip": _VGPR_FORM, "lbsa_router.hip": _VGPR_FORM}
+# the decode kernels take the arguments of their first dependent loads (the map
+# pointer and the shape words) as leading scalar parameters, which gfx950
+# preloads into SGPRs before the first instruction: the map loads go out
+# without waiting for a kernel-argument load
+_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=8"]
+EXTRA = {"lbsa_prefill.hip": _VGPR_FORM, "lbsa_router.hip": _VGPR_FORM, "lbsa_attention.hip": _PRELOAD,
+         "lbsa_assign.hip": _PRELOAD}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -691,12 +691,12 @@ __device__ inline void keep_stream_args(const AttnArgs& a) {
 // compiler sinks each load into the branch that tests it, and the start takes
 // a round trip per check).
 template <bool FP8, int QL>
-__global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kSplitThreads) void split_kernel(const uint8_t* map, int B, int Hkv, int P, int max_pages, AttnArgs a) {
     LBSA_DECLARE_SMEM(FP8, QL);
-    const MapLayout ML = map_layout(a.B, a.Hkv, a.P);
+    const MapLayout ML = map_layout(B, Hkv, P);
     const int j = blockIdx.x;
-    const auto* hdr = uniform_ptr<int32_t>(a.map + ML.header);
-    const auto* rec = uniform_ptr<int32_t>(a.map + ML.bin_head) + (size_t)kBinHeadWords * j;
+    const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
+    const auto* rec = uniform_ptr<int32_t>(map + ML.bin_head) + (size_t)kBinHeadWords * j;
     // The combine kernel starts by reading each segment's chunk range: the
     // workgroups load one word of each 64-byte line of those two arrays (8 bytes
     // per segment, contiguous; the index is clamped into them) in the same round
@@ -705,18 +705,18 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
     // keeps them after it), so the wait for the map words covers it too; its
     // register stays live (keep, below) until after that wait, since the load
     // writes it whenever it returns.
-    const int seg_words = 2 * a.Hkv * a.B;
-    const int32_t* seg_line = reinterpret_cast<const int32_t*>(a.map + ML.seg_first_desc) + min(16 * j, seg_words - 1);
+    const int seg_words = 2 * Hkv * B;
+    const int32_t* seg_line = reinterpret_cast<const int32_t*>(map + ML.seg_first_desc) + min(16 * j, seg_words - 1);
     int touched;
     __asm__ volatile("s_load_dword %0, %1, 0x0" : "=s"(touched) : "s"(seg_line) : "memory");
     const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
     const int h_k = hdr[LBSA_HDR_K], h_q = hdr[LBSA_HDR_Q], h_r = hdr[LBSA_HDR_R];
     const int r_h = rec[BH_H], r_b = rec[BH_B], r_t0 = rec[BH_T0], r_t1 = rec[BH_T1];
     const int r_first = rec[BH_FIRST], r_count = rec[BH_COUNT], r_len = rec[BH_L];
-    const int cap = a.Hkv * a.B + a.P;
+    const int cap = Hkv * B + P;
     // tiles of bin j from the header's bin sizes (the descriptors' tiles sum to it)
-    const int ntiles = min(h_q + (j < h_r ? 1 : 0), a.B * a.max_pages) * (j < h_k ? 1 : 0);
-    const bool run = (h_err == 0) & (h_p == a.P) & (h_b == a.B) & (h_hkv == a.Hkv) & (r_count > 0) &
+    const int ntiles = min(h_q + (j < h_r ? 1 : 0), B * max_pages) * (j < h_k ? 1 : 0);
+    const bool run = (h_err == 0) & (h_p == P) & (h_b == B) & (h_hkv == Hkv) & (r_count > 0) &
                      (r_first >= 0) & (r_count <= cap - r_first) & (ntiles > 0);
     keep(h_q);
     keep(h_r);
@@ -729,12 +729,12 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(AttnArgs a) {
     keep(touched);   // waited for with the map words: from here its register is the compiler's again
     if (!run) return;
     MapDescs src;
-    src.desc = uniform_ptr<int32_t>(a.map + ML.desc);
-    src.dlen = uniform_ptr<int32_t>(a.map + ML.desc_len);
+    src.desc = uniform_ptr<int32_t>(map + ML.desc);
+    src.dlen = uniform_ptr<int32_t>(map + ML.desc_len);
     src.d0 = r_first;
     src.n = r_count;
-    src.Hkv = a.Hkv;
-    src.B = a.B;
+    src.Hkv = Hkv;
+    src.B = B;
     src.max_pages = a.max_pages;
     src.head = RawDesc{r_h, r_b, r_t0, r_t1, r_len};
     run_stream<FP8, QL>(a, src, ntiles, sm);
@@ -807,45 +807,46 @@ __device__ inline void merge_chunk(float l, f32x4 x, float& m, float& wsum, f32x
 // kernel, and its workgroup stops after reading the chunk count.
 constexpr int kCombineUnroll = 8;
 template <bool STATIC>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint8_t* map, int B, int Hkv, int P, int Hq,
+                                                                   int QL, AttnArgs a) {
     constexpr int kSlices = 8;
     __shared__ float red_m[kSlices];
     __shared__ float red_w[kSlices];
     __shared__ int red_nan;
     __shared__ __attribute__((aligned(16))) float red_o[kSlices][kHeadDim];
     // every kernel argument in one round trip, before anything uses one
-    __asm__ volatile("" ::"s"(a.map), "s"(a.part_lse), "s"(a.part_o), "s"(a.out), "s"(a.Hq), "s"(a.QL), "s"(a.B),
-                     "s"(a.Hkv), "s"(a.P), "s"(a.direct_out));
     const int row = blockIdx.x;                         // (b * QL + query) * Hq + hq
-    const int bq = row / a.Hq, hq = row - bq * a.Hq;
-    const int b = bq / a.QL, qi = bq - b * a.QL;
+    const int bq = row / Hq, hq = row - bq * Hq;
+    const int b = bq / QL, qi = bq - b * QL;
     const int h = hq / kGroup, gq = hq - h * kGroup;
-    const int R = kGroup * a.QL;                        // partial rows per slot
-    const int64_t seg = (int64_t)h * a.B + b;
+    const int R = kGroup * QL;                        // partial rows per slot
+    const int64_t seg = (int64_t)h * B + b;
     const int tid = threadIdx.x, slice = tid >> 5, d4 = (tid & 31) * 4;
 
     int64_t d0 = 0;
     int n = 0;
     bool poison = false;
     if constexpr (STATIC) {
-        d0 = seg * a.P;
-        n = a.P;
+        d0 = seg * P;
+        n = P;
     } else {
         // the header words and the segment's chunk range: independent loads in
         // one round trip, checked together (the segment index is in range for
         // any map of this shape)
-        const MapLayout ML = map_layout(a.B, a.Hkv, a.P);
-        const auto* hdr = uniform_ptr<int32_t>(a.map + ML.header);
+        const MapLayout ML = map_layout(B, Hkv, P);
+        const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
         const int h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
         const int h_err = hdr[LBSA_HDR_ERROR];
-        const int sd0 = uniform_ptr<int32_t>(a.map + ML.seg_first_desc)[seg];
-        const int sn = uniform_ptr<int32_t>(a.map + ML.seg_num_chunks)[seg];
-        const int cap = a.Hkv * a.B + a.P;
+        const int sd0 = uniform_ptr<int32_t>(map + ML.seg_first_desc)[seg];
+        const int sn = uniform_ptr<int32_t>(map + ML.seg_num_chunks)[seg];
+        const int cap = Hkv * B + P;
         // a map built for another shape, or one whose lengths were invalid (the
         // split kernel computed nothing): every row is NaN
-        poison = (h_p != a.P) | (h_b != a.B) | (h_hkv != a.Hkv) | (h_err != 0) | (sd0 < 0) | (sn < 0) |
+        poison = (h_p != P) | (h_b != B) | (h_hkv != Hkv) | (h_err != 0) | (sd0 < 0) | (sn < 0) |
                  (sn > cap - sd0);
-        keep(a.direct_out);
+        // the remaining kernel arguments go out with the map loads (map, B, Hkv,
+        // P, Hq and QL arrive preloaded in SGPRs): one round trip for both
+        __asm__ volatile("" ::"s"(a.part_lse), "s"(a.part_o), "s"(a.out), "s"(a.direct_out));
         keep(sd0);
         keep(sn);
         if (!poison) {
@@ -915,10 +916,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
 hipError_t launch_split(const AttnArgs& a, bool fp8, hipStream_t stream) {
     const dim3 grid(a.P), block(kSplitThreads);
     if (a.QL == 2)
-        return fp8 ? launch(split_kernel<true, 2>, grid, block, 0, stream, a)
-                   : launch(split_kernel<false, 2>, grid, block, 0, stream, a);
-    return fp8 ? launch(split_kernel<true, 1>, grid, block, 0, stream, a)
-               : launch(split_kernel<false, 1>, grid, block, 0, stream, a);
+        return fp8 ? launch(split_kernel<true, 2>, grid, block, 0, stream, a.map, a.B, a.Hkv, a.P, a.max_pages, a)
+                   : launch(split_kernel<false, 2>, grid, block, 0, stream, a.map, a.B, a.Hkv, a.P, a.max_pages, a);
+    return fp8 ? launch(split_kernel<true, 1>, grid, block, 0, stream, a.map, a.B, a.Hkv, a.P, a.max_pages, a)
+               : launch(split_kernel<false, 1>, grid, block, 0, stream, a.map, a.B, a.Hkv, a.P, a.max_pages, a);
 }
 
 hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
@@ -932,8 +933,11 @@ hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
 
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream) {
     const long long grid = (long long)a.B * a.QL * a.Hq;
-    if (static_mode) return launch(combine_kernel<true>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a);
-    return launch(combine_kernel<false>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a);
+    if (static_mode)
+        return launch(combine_kernel<true>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a.map, a.B, a.Hkv,
+                      a.P, a.Hq, a.QL, a);
+    return launch(combine_kernel<false>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a.map, a.B, a.Hkv,
+                  a.P, a.Hq, a.QL, a);
 }
 
 hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu) {

@@ -46,8 +46,8 @@ def workgroups(batch, P=None) -> int:
     return lbsa.default_workgroups(0, batch["kv_dtype"], batch.get("q_len", 1))
 
 
-def plan(batch, P, F=0):
-    return lbsa.plan(batch["seqlens"], batch["num_heads"], batch["num_kv_heads"], batch["max_pages"], P, F)
+def plan(batch, P, F=0, **kw):
+    return lbsa.plan(batch["seqlens"], batch["num_heads"], batch["num_kv_heads"], batch["max_pages"], P, F, **kw)
 
 
 def decode(batch, task_map, P, **kw):

@@ -204,6 +204,38 @@ def test_direct_rows_match_split_then_combine(kv, q_len):
     assert torch.equal(a.view(torch.int16), b.reshape(a.shape).view(torch.int16))
 
 
+@pytest.mark.parametrize("n", [2, 15, 16, 17, 63, 64, 65, 300])
+def test_combine_of_n_chunks(oracle_mod, n):
+    """One request of n tiles on P = n bins with floor 1: its segment is cut into
+    n one-tile chunks (the combine's slices take 64 per round trip: 63, 64 and 65
+    straddle that)."""
+    batch = H.batch_on_gpu(dict(seqlens=[64 * n - 5], num_heads=8, num_kv_heads=1, kv_dtype="bf16",
+                                seed=40 + n))
+    tm = H.plan(batch, n, F=1)
+    assert int(lbsa.read_task_map(tm, 1, 1, n)["seg_num_chunks"][0]) == n
+    check_full(oracle_mod, batch, H.decode(batch, tm, n), f"{n} chunks")
+
+
+def test_many_cut_segments_two_query_tokens(oracle_mod):
+    """fp8, two query tokens, two KV heads: a 400-tile request cut into about 360
+    chunks per head beside short, empty and mid-size requests."""
+    batch = H.batch_on_gpu(dict(seqlens=[64 * 400, 100, 2600, 0, 7000], num_heads=16, num_kv_heads=2,
+                                kv_dtype="fp8", seed=48, q_len=2))
+    P = 1000
+    tm = H.plan(batch, P, F=1)
+    assert int(lbsa.read_task_map(tm, 5, 2, P)["seg_num_chunks"].max()) > 256
+    check_full(oracle_mod, batch, H.decode(batch, tm, P), "many cut segments")
+
+
+def test_all_requests_empty_gives_zero_rows():
+    """T = 0: no bins and no descriptors; every row is 0, whatever out held."""
+    batch = H.batch_on_gpu(dict(seqlens=[0, 0, 0], num_heads=16, num_kv_heads=2, kv_dtype="bf16", seed=50))
+    P = 32
+    out = H.decode(batch, H.plan(batch, P), P, out=torch.full((3, 16, 128), float("nan"), dtype=torch.bfloat16,
+                                                                device="cuda:0"))
+    assert (H.out_np(out) == 0).all()
+
+
 def test_mismatched_map_poisons_output():
     batch = H.batch_on_gpu(dict(seqlens=[200, 300], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=30))
     tm = H.plan(batch, 16)
