@@ -126,13 +126,15 @@ def _to_fp8(x: torch.Tensor):
 
 def make_batch(w: Workload | str | None = None, *, seqlens=None, num_heads=None, num_kv_heads=None,
                kv_dtype=None, seed=None, tail: str = "nan", device="cpu", max_pages=None,
-               head_dim=HEAD_DIM, q_len=None) -> dict:
+               head_dim=HEAD_DIM, q_len=None, qlens=None) -> dict:
     """Build one synthetic decode batch.
 
     Either pass a workload (object or name) or explicit ``seqlens`` with
     ``num_heads``, ``num_kv_heads``, ``kv_dtype`` and ``seed``.  ``q_len``
-    (default: the workload's, 1) query tokens per request.  Returns a dict of
-    tensors on ``device`` plus scalar metadata.
+    (default: the workload's, 1) query tokens per request.  ``qlens`` (one per
+    request) instead gives each request its own number of new tokens, and q is
+    packed [sum(qlens), Hq, D] in request order (a prefill / extend / decode
+    mix).  Returns a dict of tensors on ``device`` plus scalar metadata.
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -159,7 +161,12 @@ def make_batch(w: Workload | str | None = None, *, seqlens=None, num_heads=None,
         pt[b, :nb] = perm[off:off + nb]
         off += nb
 
-    q32 = _normal((B, Hq, D) if QL == 1 else (B, QL, Hq, D), gen, dev)
+    if qlens is not None:
+        qlens = torch.tensor([int(x) for x in qlens], dtype=torch.int32)
+        assert qlens.numel() == B
+        q32 = _normal((int(qlens.sum()), Hq, D), gen, dev)
+    else:
+        q32 = _normal((B, Hq, D) if QL == 1 else (B, QL, Hq, D), gen, dev)
     k32 = _normal((pool, TILE, Hkv, D), gen, dev)
     k_cache, k_scale = _finish_cache(k32, w.kv_dtype)
     del k32
@@ -186,7 +193,33 @@ def make_batch(w: Workload | str | None = None, *, seqlens=None, num_heads=None,
         "max_pages": mp, "num_pages": pool,
         "softmax_scale": 1.0 / math.sqrt(D),
         "num_workgroups": w.num_workgroups,
+        "qlens": None if qlens is None else qlens.to(dev),
     }
+
+
+# A prefill / extend / decode mix on one map: request 0 extends an 8K-token
+# context by 8K new tokens (the vLLM post's Table 4 extend rows, at q8k's
+# length), 63 decode requests of log-uniform 1K-16K tokens beside it, full Hy3
+# attention (64 query / 8 KV heads), bf16.
+MIXED_EXTEND = dict(extend_len=16384, extend_q=8192, decode_rows=63, decode_lo=1024, decode_hi=16384, seed=90)
+
+
+def mixed_extend_lengths(extend_len=16384, extend_q=8192, decode_rows=63, decode_lo=1024, decode_hi=16384,
+                         seed=90):
+    """(seqlens, qlens) of the mix: the extend request first, then the decode rows."""
+    gen = torch.Generator().manual_seed(seed)
+    u = torch.rand(decode_rows, generator=gen, dtype=torch.float64)
+    dec = torch.exp(math.log(decode_lo) + u * (math.log(decode_hi) - math.log(decode_lo))).floor()
+    dec = dec.clamp(decode_lo, decode_hi).to(torch.int64).tolist()
+    return [int(extend_len)] + [int(x) for x in dec], [int(extend_q)] + [1] * decode_rows
+
+
+def make_mixed_extend_batch(tail: str = "normal", device="cpu", **kw) -> dict:
+    """Seeded batch of the mix (q packed [8192 + 63, 64, 128])."""
+    cfg = dict(MIXED_EXTEND, **kw)
+    sl, ql = mixed_extend_lengths(**cfg)
+    return make_batch(seqlens=sl, qlens=ql, num_heads=64, num_kv_heads=8, kv_dtype="bf16", seed=cfg["seed"],
+                      tail=tail, device=device)
 
 
 def _finish_cache(x32: torch.Tensor, kv_dtype: str):

@@ -43,6 +43,17 @@
  *       causal among the new tokens.  A query that sees no token gives 0.
  *       q is [B][q_len][Hq][D], q_scale [B][q_len][Hq], out like q; a
  *       descriptor's partial has one row per (query i, head g), row i*G + g.
+ *   Q1  prefill / extend on the task map (the survey's query-tile dimension):
+ *       request b brings q_b >= 1 new tokens, the last q_b of its L_b cached
+ *       ones, query i seeing tokens [0, L_b - q_b + i] (M1 with a per-request
+ *       q).  Its queries form blocks of QB consecutive positions; a segment is
+ *       (kv_head, request, query block k) and spans the tiles its last query
+ *       sees: ceil(min(L_b, L_b - q_b + QB (k + 1)) / 64).  Segments are walked
+ *       head-major, batch-minor, query block innermost; budget, fill and spill
+ *       are those of R1 over these tiles.  With q_b = 1 for every request this
+ *       is the decode map.  Q and out are packed [sum q_b][Hq][D] in request
+ *       order (row qstart_b + i); a partial has one row per (block position p,
+ *       head g), row p*G + g, and positions past q_b are empty (0, -inf).
  *
  * Floating point is fp64 throughout; integers in the assign are int64.
  * Parity of every function here is pinned in tests/ against values that do
@@ -240,6 +251,142 @@ int oracle_assign(const int32_t* seqlens, int32_t B, int32_t Hq, int32_t Hkv,
     return 0;
 }
 
+/*
+ * Assign with query blocks (reading Q1).  The same five steps as
+ * oracle_assign, over segments (kv_head, request, query block):
+ *   1. slice: query block k of request b spans n(b, k) =
+ *      ceil(min(L_b, L_b - q_b + QB (k + 1)) / 64) tiles, for k < ceil(q_b / QB);
+ *   2. T = sum of n(b, k) over every KV head, request and query block;
+ *   3. budget from T and the bins (R1, R2);
+ *   4. walk the tiles head-major, batch-minor, query block innermost, fill and
+ *      spill; a maximal run of one segment's tiles inside one bin is a
+ *      descriptor (kv_head, request, query_block, tile_begin, tile_end);
+ *   5. chunk count and first chunk per segment, segment index
+ *      s = h * NQ + (blocks of earlier requests) + k, NQ = sum_b ceil(q_b / QB).
+ * Header as oracle_assign (word 11 N = tiles per KV head), plus 14 NQ and
+ * 15 QB.  An L_b or q_b out of range (L_b < 0, L_b > max_pages * 64, q_b < 1,
+ * q_b > L_b) sets the error word and empties the map.
+ */
+int oracle_assign_varlen(const int32_t* seqlens, const int32_t* qlens, int32_t B, int32_t Hq,
+                         int32_t Hkv, int32_t P, int32_t F, int32_t max_pages, int32_t QB,
+                         int32_t* header, int32_t* bin_desc_begin,
+                         int32_t* desc, int64_t desc_cap,
+                         int32_t* seg_first_desc, int32_t* seg_num_chunks, int64_t seg_cap)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || P <= 0 || F <= 0 || max_pages <= 0 || QB <= 0)
+        return -1;
+    if (Hq % Hkv != 0) return -1;
+
+    int error = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t L = seqlens[b], q = qlens[b];
+        if (L < 0 || L > (int64_t)max_pages * OR_TILE || q < 1 || q > L) error = 1;
+    }
+
+    /* Step 1: query blocks per request and the tiles of each block. */
+    int64_t NQ = 0;
+    int64_t* nq = (int64_t*)calloc((size_t)B, sizeof(int64_t));
+    for (int32_t b = 0; b < B; ++b) {
+        nq[b] = error ? 0 : ((int64_t)qlens[b] + QB - 1) / QB;
+        NQ += nq[b];
+    }
+    if ((int64_t)Hkv * NQ > seg_cap) { free(nq); return -1; }
+    int64_t* ntile = (int64_t*)calloc((size_t)(NQ > 0 ? NQ : 1), sizeof(int64_t));
+    int64_t N = 0;
+    {
+        int64_t s = 0;
+        for (int32_t b = 0; b < B; ++b)
+            for (int64_t k = 0; k < nq[b]; ++k, ++s) {
+                int64_t seen = (int64_t)seqlens[b] - qlens[b] + QB * (k + 1);
+                if (seen > seqlens[b]) seen = seqlens[b];
+                ntile[s] = (seen + OR_TILE - 1) / OR_TILE;
+                N += ntile[s];
+            }
+    }
+    /* Step 2: total over all KV heads. */
+    int64_t T = (int64_t)Hkv * N;
+
+    /* Step 3: budget. */
+    int64_t K = 0, q = 0, r = 0;
+    if (T > 0) {
+        int64_t by_floor = T / F;
+        if (by_floor < 1) by_floor = 1;
+        K = by_floor < P ? by_floor : P;
+        q = T / K;
+        r = T % K;
+    }
+
+    /* Step 4: walk; fill and spill. */
+    for (int32_t j = 0; j <= P; ++j) bin_desc_begin[j] = -1;
+    int64_t nd = 0, bin = 0, fill = 0;
+    int open = 0;
+    for (int32_t h = 0; h < Hkv; ++h) {
+        int64_t s = 0;
+        for (int32_t b = 0; b < B; ++b) {
+            for (int64_t k = 0; k < nq[b]; ++k, ++s) {
+                for (int64_t t = 0; t < ntile[s]; ++t) {
+                    if (fill == 0) bin_desc_begin[bin] = (int32_t)nd;
+                    if (open) {
+                        desc[5 * (nd - 1) + 4] = (int32_t)(t + 1);
+                    } else {
+                        if (nd >= desc_cap) { free(nq); free(ntile); return -1; }
+                        desc[5 * nd + 0] = h;
+                        desc[5 * nd + 1] = b;
+                        desc[5 * nd + 2] = (int32_t)k;
+                        desc[5 * nd + 3] = (int32_t)t;
+                        desc[5 * nd + 4] = (int32_t)(t + 1);
+                        ++nd;
+                        open = 1;
+                    }
+                    int64_t budget = (bin < r) ? q + 1 : q;
+                    if (++fill == budget) {  /* bin full: spill to the next */
+                        ++bin;
+                        fill = 0;
+                        open = 0;
+                    }
+                }
+                open = 0;  /* a new segment never extends the previous one */
+            }
+        }
+    }
+    for (int64_t j = K; j <= P; ++j) bin_desc_begin[j] = (int32_t)nd;
+
+    /* Step 5: chunk count and first chunk per segment. */
+    int64_t* qbase = (int64_t*)calloc((size_t)B + 1, sizeof(int64_t));
+    for (int32_t b = 0; b < B; ++b) qbase[b + 1] = qbase[b] + nq[b];
+    const int64_t S = (int64_t)Hkv * NQ;
+    for (int64_t s = 0; s < S; ++s) seg_num_chunks[s] = 0;
+    for (int64_t d = 0; d < nd; ++d)
+        seg_num_chunks[(int64_t)desc[5 * d] * NQ + qbase[desc[5 * d + 1]] + desc[5 * d + 2]] += 1;
+    int64_t acc = 0;
+    for (int64_t s = 0; s < S; ++s) {
+        seg_first_desc[s] = (int32_t)acc;
+        acc += seg_num_chunks[s];
+    }
+
+    memset(header, 0, 16 * sizeof(int32_t));
+    header[0] = (int32_t)T;
+    header[1] = (int32_t)K;
+    header[2] = (int32_t)q;
+    header[3] = (int32_t)r;
+    header[4] = (int32_t)nd;
+    header[5] = P;
+    header[6] = F;
+    header[7] = B;
+    header[8] = Hq;
+    header[9] = Hkv;
+    header[10] = error;
+    header[11] = (int32_t)N;
+    header[12] = max_pages;
+    header[13] = OR_TILE;
+    header[14] = (int32_t)NQ;
+    header[15] = QB;
+    free(nq);
+    free(ntile);
+    free(qbase);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Attention: the plain softmax definition over gathered paged K/V.          */
 /* ------------------------------------------------------------------------ */
@@ -257,12 +404,25 @@ typedef struct {
     int32_t B, Hq, Hkv, D, max_pages, num_pages;
     double softmax_scale;
     int32_t q_len;          /* query tokens per request (M1), >= 1 */
+    const int32_t* qlens;   /* Q1: per-request q_b, or NULL for q_len everywhere */
+    const int32_t* qstart;  /* Q1: packed row of query 0 of request b (prefix of qlens), [B + 1] */
 } oracle_inputs;
 
 /* Element d of query i of request b, head hq. */
+static int64_t q_of(const oracle_inputs* in, int64_t b)
+{
+    return in->qlens ? in->qlens[b] : in->q_len;
+}
+
+/* Row of query i of request b in q / out: [B][q_len] (M1) or packed (Q1). */
+static int64_t q_row(const oracle_inputs* in, int64_t b, int64_t i)
+{
+    return in->qlens ? (int64_t)in->qstart[b] + i : b * in->q_len + i;
+}
+
 static double q_elem(const oracle_inputs* in, int64_t b, int64_t i, int64_t hq, int64_t d)
 {
-    const int64_t row = (b * in->q_len + i) * in->Hq + hq;
+    const int64_t row = q_row(in, b, i) * in->Hq + hq;
     if (in->kv_dtype == 0) return oracle_bf16_value(((const uint16_t*)in->q)[row * in->D + d]);
     return oracle_e4m3_value(((const uint8_t*)in->q)[row * in->D + d]) * (double)in->q_scale[row];
 }
@@ -270,7 +430,7 @@ static double q_elem(const oracle_inputs* in, int64_t b, int64_t i, int64_t hq, 
 /* M1: tokens [0, visible) of request b are seen by its query i. */
 static int64_t visible(const oracle_inputs* in, int64_t b, int64_t i)
 {
-    const int64_t v = (int64_t)in->seqlens[b] - in->q_len + 1 + i;
+    const int64_t v = (int64_t)in->seqlens[b] - q_of(in, b) + 1 + i;
     return v > 0 ? v : 0;
 }
 
@@ -422,6 +582,114 @@ int oracle_partials(const oracle_inputs* in, const int32_t* desc, int64_t ndesc,
             const int64_t h = desc[4 * di], b = desc[4 * di + 1];
             const int64_t tok0 = (int64_t)desc[4 * di + 2] * OR_TILE;
             int64_t tok1 = (int64_t)desc[4 * di + 3] * OR_TILE;
+            if (tok1 > in->seqlens[b]) tok1 = in->seqlens[b];
+            if (attend_range(in, b, qi, h * G + g, tok0, tok1, part_o + i * D, part_lse + i, qv, s))
+                bad = 1;
+        }
+        free(qv);
+        free(s);
+    }
+    (void)nthreads;
+    return bad ? -1 : 0;
+}
+
+/* Q1: full attention of every packed query row: out [sum q_b][Hq][D], lse
+ * [sum q_b][Hq] (in->qlens and in->qstart set). */
+int oracle_attention_varlen(const oracle_inputs* in, double* out, double* lse, int nthreads)
+{
+    const int64_t D = in->D;
+    const int64_t L = max_len(in);
+    const int64_t rows = (int64_t)in->qstart[in->B] * in->Hq;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double* qv = (double*)malloc((size_t)D * sizeof(double));
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t row = 0; row < rows; ++row) {
+            const int64_t t = row / in->Hq, hq = row % in->Hq;
+            int64_t b = 0;
+            while (in->qstart[b + 1] <= t) ++b;   /* the request that owns packed row t */
+            if (attend_range(in, b, t - in->qstart[b], hq, 0, in->seqlens[b], out + row * D, lse + row, qv, s))
+                bad = 1;
+        }
+        free(qv);
+        free(s);
+    }
+    (void)nthreads;
+    return bad ? -1 : 0;
+}
+
+/* Q1: attention of selected packed rows given as pairs (t, hq): query row t of
+ * q (request b with qstart[b] <= t < qstart[b + 1]), head hq. */
+int oracle_attention_varlen_rows(const oracle_inputs* in, const int32_t* rows, int64_t nrows,
+                                 double* out, double* lse, int nthreads)
+{
+    const int64_t D = in->D;
+    const int64_t L = max_len(in);
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double* qv = (double*)malloc((size_t)D * sizeof(double));
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t t = rows[2 * i], hq = rows[2 * i + 1];
+            int64_t b = 0;
+            while (in->qstart[b + 1] <= t) ++b;
+            if (attend_range(in, b, t - in->qstart[b], hq, 0, in->seqlens[b], out + i * D, lse + i, qv, s))
+                bad = 1;
+        }
+        free(qv);
+        free(s);
+    }
+    (void)nthreads;
+    return bad ? -1 : 0;
+}
+
+/* Q1 partials: descriptor i = (h, b, k, t0, t1) covers tokens [64 t0,
+ * min(64 t1, L_b)) of request b for the G query heads of KV head h and the QB
+ * positions of query block k (each cut at what it sees).  part_o
+ * [n][QB * G][D] (row p * G + g for query QB k + p), part_lse [n][QB * G];
+ * positions at or past q_b give 0 and -inf. */
+int oracle_partials_varlen(const oracle_inputs* in, const int32_t* desc, int64_t ndesc, int32_t QB,
+                           double* part_o, double* part_lse, int nthreads)
+{
+    const int64_t D = in->D;
+    const int64_t G = in->Hq / in->Hkv;
+    const int64_t L = max_len(in);
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double* qv = (double*)malloc((size_t)D * sizeof(double));
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t i = 0; i < ndesc * QB * G; ++i) {
+            const int64_t di = i / (QB * G), p = i / G % QB, g = i % G;
+            const int64_t h = desc[5 * di], b = desc[5 * di + 1], k = desc[5 * di + 2];
+            const int64_t qi = QB * k + p;
+            if (qi >= q_of(in, b)) {
+                for (int64_t d = 0; d < D; ++d) part_o[i * D + d] = 0.0;
+                part_lse[i] = -INFINITY;
+                continue;
+            }
+            const int64_t tok0 = (int64_t)desc[5 * di + 3] * OR_TILE;
+            int64_t tok1 = (int64_t)desc[5 * di + 4] * OR_TILE;
             if (tok1 > in->seqlens[b]) tok1 = in->seqlens[b];
             if (attend_range(in, b, qi, h * G + g, tok0, tok1, part_o + i * D, part_lse + i, qv, s))
                 bad = 1;

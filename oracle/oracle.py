@@ -37,6 +37,7 @@ class _Inputs(ctypes.Structure):
         ("D", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
         ("softmax_scale", ctypes.c_double),
         ("q_len", ctypes.c_int32),
+        ("qlens", ctypes.c_void_p), ("qstart", ctypes.c_void_p),
     ]
 
 
@@ -60,6 +61,14 @@ def lib():
         L.oracle_attention_rows.restype = ctypes.c_int
         L.oracle_partials.argtypes = [ctypes.POINTER(_Inputs), P, i64, P, P, ctypes.c_int]
         L.oracle_partials.restype = ctypes.c_int
+        L.oracle_assign_varlen.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, i64, P, P, i64]
+        L.oracle_assign_varlen.restype = ctypes.c_int
+        L.oracle_attention_varlen.argtypes = [ctypes.POINTER(_Inputs), P, P, ctypes.c_int]
+        L.oracle_attention_varlen.restype = ctypes.c_int
+        L.oracle_attention_varlen_rows.argtypes = [ctypes.POINTER(_Inputs), P, i64, P, P, ctypes.c_int]
+        L.oracle_attention_varlen_rows.restype = ctypes.c_int
+        L.oracle_partials_varlen.argtypes = [ctypes.POINTER(_Inputs), P, i64, i32, P, P, ctypes.c_int]
+        L.oracle_partials_varlen.restype = ctypes.c_int
         L.oracle_merge.argtypes = [P, P, i64, i64, P, P]
         L.oracle_merge.restype = None
         L.oracle_bf16_values.argtypes = [P, i64, P]
@@ -160,6 +169,39 @@ def assign(seqlens, num_heads: int, num_kv_heads: int, P: int, F: int, max_pages
     return out
 
 
+def assign_varlen(seqlens, qlens, num_heads: int, num_kv_heads: int, P: int, F: int, max_pages: int,
+                  QB: int = 16) -> dict:
+    """Reference task map with query blocks (prefill / extend, reading Q1).
+
+    ``desc`` is int32[Ndesc, 5] (kv_head, request, query_block, tile_begin,
+    tile_end); ``seg_first_desc`` / ``seg_num_chunks`` are int32[Hkv * NQ], index
+    h * NQ + (query blocks of earlier requests) + block; header word 14 is NQ,
+    15 is QB."""
+    sl = _np(seqlens, None).astype(np.int32).ravel()
+    ql = _np(qlens, None).astype(np.int32).ravel()
+    B = sl.size
+    nq = int(sum(-(-max(int(x), 0) // QB) for x in ql))
+    seg_cap = max(1, num_kv_heads * nq)
+    cap = seg_cap + P
+    header = np.zeros(16, np.int32)
+    bdb = np.zeros(P + 1, np.int32)
+    desc = np.zeros((cap, 5), np.int32)
+    sfd = np.zeros(seg_cap, np.int32)
+    snc = np.zeros(seg_cap, np.int32)
+    rc = lib().oracle_assign_varlen(_ptr(sl), _ptr(ql), B, num_heads, num_kv_heads, P, F, max_pages, QB,
+                                    _ptr(header), _ptr(bdb), _ptr(desc), cap, _ptr(sfd), _ptr(snc), seg_cap)
+    if rc != 0:
+        raise ValueError("oracle_assign_varlen: invalid arguments")
+    nd = int(header[4])
+    S = num_kv_heads * int(header[14])
+    out = {"header": header, "bin_desc_begin": bdb, "desc": desc[:nd].copy(),
+           "seg_first_desc": sfd[:S].copy(), "seg_num_chunks": snc[:S].copy()}
+    for i, name in enumerate(HEADER_FIELDS):
+        out[name] = int(header[i])
+    out["NQ"], out["QB"] = int(header[14]), int(header[15])
+    return out
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------
@@ -183,8 +225,14 @@ class _Batch:
             self.vs = _np(batch["v_scale"], np.float32)
         self.pt = _np(batch["page_table"], None).astype(np.int32)
         self.sl = _np(batch["seqlens"], None).astype(np.int32)
+        self.ql = self.qs0 = None
+        if batch.get("qlens") is not None:
+            # Q1: q packed [sum q_b, Hq, D], request b's queries from row qstart[b]
+            self.ql = _np(batch["qlens"], None).astype(np.int32).ravel()
+            self.qs0 = np.concatenate([[0], np.cumsum(self.ql)]).astype(np.int32)
+            B, (_, Hq, D), QL = self.sl.size, self.q.shape, 1
         # q [B, Hq, D] (one query per request) or [B, q_len, Hq, D]
-        if self.q.ndim == 3:
+        elif self.q.ndim == 3:
             (B, Hq, D), QL = self.q.shape, 1
         else:
             B, QL, Hq, D = self.q.shape
@@ -195,7 +243,7 @@ class _Batch:
         self.s = _Inputs(
             _ptr(self.q), _ptr(self.qs), _ptr(self.k), _ptr(self.v), _ptr(self.ks), _ptr(self.vs),
             _ptr(self.pt), _ptr(self.sl), self.kv_dtype, B, Hq, Hkv, D,
-            self.pt.shape[1], num_pages, float(batch["softmax_scale"]), QL)
+            self.pt.shape[1], num_pages, float(batch["softmax_scale"]), QL, _ptr(self.ql), _ptr(self.qs0))
 
 
 def attention(batch: dict, nthreads: int = 0):
@@ -235,6 +283,45 @@ def partials(batch: dict, desc, nthreads: int = 0):
     pl = np.zeros((n, G), np.float64)
     if lib().oracle_partials(ctypes.byref(bb.s), _ptr(desc), n, _ptr(po), _ptr(pl), nthreads) != 0:
         raise ValueError("oracle_partials: page_table entry out of range")
+    return po, pl
+
+
+def attention_varlen(batch: dict, nthreads: int = 0):
+    """fp64 attention of every packed query row (reading Q1): (out [sum q_b, Hq, D],
+    lse [sum q_b, Hq])."""
+    bb = _Batch(batch)
+    out = np.zeros(bb.q.shape, np.float64)
+    lse = np.zeros(bb.q.shape[:-1], np.float64)
+    if lib().oracle_attention_varlen(ctypes.byref(bb.s), _ptr(out), _ptr(lse), nthreads) != 0:
+        raise ValueError("oracle_attention_varlen: page_table entry out of range")
+    return out, lse
+
+
+def attention_varlen_rows(batch: dict, rows, nthreads: int = 0):
+    """fp64 attention of selected packed rows int[n, 2] = (query row t, head hq)."""
+    bb = _Batch(batch)
+    D = bb.shape[3]
+    rows = np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 2))
+    out = np.zeros((rows.shape[0], D), np.float64)
+    lse = np.zeros(rows.shape[0], np.float64)
+    if lib().oracle_attention_varlen_rows(ctypes.byref(bb.s), _ptr(rows), rows.shape[0], _ptr(out), _ptr(lse),
+                                          nthreads) != 0:
+        raise ValueError("oracle_attention_varlen_rows: page_table entry out of range")
+    return out, lse
+
+
+def partials_varlen(batch: dict, desc, QB: int = 16, nthreads: int = 0):
+    """fp64 partials of query-block descriptors desc int[n, 5]: (part_o [n, QB*G, D],
+    part_lse [n, QB*G]), row p*G + g for query QB*k + p, head g of the group."""
+    bb = _Batch(batch)
+    B, Hq, Hkv, D = bb.shape
+    G = Hq // Hkv
+    desc = np.ascontiguousarray(np.asarray(desc, np.int32).reshape(-1, 5))
+    n = desc.shape[0]
+    po = np.zeros((n, QB * G, D), np.float64)
+    pl = np.zeros((n, QB * G), np.float64)
+    if lib().oracle_partials_varlen(ctypes.byref(bb.s), _ptr(desc), n, QB, _ptr(po), _ptr(pl), nthreads) != 0:
+        raise ValueError("oracle_partials_varlen: page_table entry out of range")
     return po, pl
 
 
