@@ -303,6 +303,66 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
                  void* stream);
 
 /*
+ * Prefill, extend and decode rows on one task map (vLLM post, Table 4: one
+ * backend over prefill, extend and decode shapes; the map of the section "The
+ * solution: a per-step, load-balanced decode scheduler", bullet "Assign",
+ * with a query-tile dimension).  Request b brings qlens[b] >= 1 new tokens,
+ * the last qlens[b] of its seqlens[b] cached ones (1 for a decode row,
+ * seqlens[b] for a prefill); query i attends to tokens [0, seqlens[b] -
+ * qlens[b] + i].  Its queries form blocks of LBSA_QBLOCK positions, and a
+ * segment is (KV head, request, query block) spanning the 64-token tiles its
+ * last query sees: ceil(min(L, L - q + 16 (k + 1)) / 64) for block k.
+ * Segments are walked head-major, batch-minor, query block innermost, and
+ * binned with the decode budget, fill and spill (lbsa_plan).
+ *   total_q        sum of qlens (host-side: the rows of the packed q and out);
+ *                  the map and the launches are sized by it, and lbsa_plan_varlen
+ *                  sets the error word when the device lengths disagree with it
+ *   q_d / out_d    bf16 [total_q][num_heads][128], request b's queries at rows
+ *                  [sum_{b' < b} qlens[b'], + qlens[b]) (packed, request order)
+ *   map            lbsa_varlen_task_map_bytes(batch, num_kv_heads, P, total_q)
+ *                  bytes: header (words as lbsa_plan's, plus 14 = query blocks
+ *                  per KV head NQ, 15 = LBSA_QBLOCK), bin CSR, 32-byte
+ *                  descriptors (kv_head, request, block, tile_begin, tile_end,
+ *                  L, q, first packed row), per segment s = h * NQ + block (of
+ *                  all requests in order) its first descriptor, chunk count and
+ *                  first partial slot, per block its request and index, the
+ *                  prefixes of blocks and of qlens, and the two length copies
+ *                  (lbsa_varlen_task_map_layout_get)
+ *   workspace      lbsa_varlen_workspace_bytes(num_heads, num_kv_heads, 128, P):
+ *                  2 P partial slots of 16 x 8 rows (position x head), fp32 LSE
+ *                  [2 P][128] then O [2 P][128][128]; only a bin's first and last
+ *                  descriptors can cut a segment, so slot 2 j + (0 first, 1 last)
+ * lbsa_attend_varlen is two launches: a persistent workgroup per bin computes
+ * each descriptor's query block over its tiles (MFMA, K/V through LDS), writing
+ * the bf16 rows of a segment it holds whole and a partial otherwise; then one
+ * workgroup per (KV head, block) merges the chunks of the cut segments.
+ * Errors: shapes as lbsa_plan and lbsa_prefill (bf16 only); maps larger than
+ * one assign workgroup's LDS (about 16K segments) give LBSA_ERR_UNSUPPORTED.
+ * A length or q out of range on the device sets the error word: every output
+ * row is then NaN.  Default P: lbsa_varlen_default_workgroups.
+ */
+#define LBSA_QBLOCK 16
+typedef struct {
+    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seg_slot0, blk_req, blk_k, qbase,
+        qstart, seqlens, qlens, total;
+} lbsa_varlen_task_map_layout;
+int lbsa_varlen_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32_t P, int64_t total_q,
+                                    lbsa_varlen_task_map_layout* out);
+int lbsa_varlen_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t P, int64_t total_q, size_t* out_bytes);
+int lbsa_varlen_workspace_bytes(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t P,
+                                size_t* out_bytes);
+int lbsa_varlen_default_workgroups(int device, int32_t* out_P);
+int lbsa_plan_varlen(const int32_t* seqlens_d, const int32_t* qlens_d, int32_t batch, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t page_size, int32_t max_pages_per_seq, int64_t total_q,
+                     int32_t num_workgroups, int32_t min_tiles_per_bin, void* task_map_d, size_t task_map_bytes,
+                     void* stream);
+int lbsa_attend_varlen(const void* q_d, const void* k_cache_d, const void* v_cache_d, const int32_t* page_table_d,
+                       int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t max_pages_per_seq, int64_t num_pages, int64_t total_q, int32_t num_workgroups,
+                       float softmax_scale, const void* task_map_d, size_t task_map_bytes, void* workspace_d,
+                       size_t workspace_bytes, void* out_d, void* stream);
+
+/*
  * Split-bf16 router GEMM (SGLang post, section "Router GEMM: balancing routing
  * precision and throughput"): router scores from bf16 hidden states and fp32
  * router weights, run on bf16 MFMA with the weights' low mantissa bits kept.

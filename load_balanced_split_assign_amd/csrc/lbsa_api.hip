@@ -104,7 +104,7 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 204; }
+LBSA_API int lbsa_version(void) { return 205; }
 
 namespace {
 // Events armed for the next launches on this host thread, used in order.
@@ -465,6 +465,130 @@ LBSA_API int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_
     return hip_status(launch_prefill(q_d, k_cache_d, v_cache_d, page_table_d, seqlens_d, batch, q_len, num_heads,
                                      num_kv_heads, max_pages_per_seq, num_pages, softmax_scale * kLog2eHost, out_d,
                                      0, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / extend / decode rows on one task map.
+// ---------------------------------------------------------------------------
+static int varlen_shape(int32_t batch, int32_t num_kv_heads, int32_t P, int64_t total_q) {
+    if (batch <= 0 || num_kv_heads <= 0 || P <= 0 || total_q < batch) return LBSA_ERR_INVALID_ARGUMENT;
+    if (total_q > (1 << 24) || P >= (1 << 24)) return LBSA_ERR_UNSUPPORTED;
+    // the single assign workgroup keeps every prefix in LDS
+    if (varlen_assign_lds_words(batch, num_kv_heads, varlen_max_blocks(batch, total_q)) > (size_t)kMaxAssignLdsWords)
+        return LBSA_ERR_UNSUPPORTED;
+    return LBSA_OK;
+}
+
+static const size_t kVarlenSlotBytesLse = 4u * kVarlenRows;
+static const size_t kVarlenSlotBytesO = 4u * kVarlenRows * kHeadDim;
+
+LBSA_API int lbsa_varlen_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32_t P, int64_t total_q,
+                                             lbsa_varlen_task_map_layout* out) {
+    if (!out) return LBSA_ERR_INVALID_ARGUMENT;
+    const int s = varlen_shape(batch, num_kv_heads, P, total_q);
+    if (s != LBSA_OK) return s;
+    const VarlenMapLayout m = varlen_map_layout(batch, num_kv_heads, P, varlen_max_blocks(batch, total_q));
+    out->header = m.header;
+    out->bin_desc_begin = m.bin_desc_begin;
+    out->desc = m.desc;
+    out->seg_first_desc = m.seg_first_desc;
+    out->seg_num_chunks = m.seg_num_chunks;
+    out->seg_slot0 = m.seg_slot0;
+    out->blk_req = m.blk_req;
+    out->blk_k = m.blk_k;
+    out->qbase = m.qbase;
+    out->qstart = m.qstart;
+    out->seqlens = m.seqlens;
+    out->qlens = m.qlens;
+    out->total = m.total;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_varlen_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t P, int64_t total_q,
+                                        size_t* out_bytes) {
+    if (!out_bytes) return LBSA_ERR_INVALID_ARGUMENT;
+    lbsa_varlen_task_map_layout l;
+    const int s = lbsa_varlen_task_map_layout_get(batch, num_kv_heads, P, total_q, &l);
+    if (s == LBSA_OK) *out_bytes = l.total;
+    return s;
+}
+
+LBSA_API int lbsa_varlen_workspace_bytes(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t P,
+                                         size_t* out_bytes) {
+    if (!out_bytes || P <= 0) return LBSA_ERR_INVALID_ARGUMENT;
+    const int s = check_shape(1, num_heads, num_kv_heads, head_dim, kTile);
+    if (s != LBSA_OK) return s;
+    *out_bytes = align_up(2 * (size_t)P * kVarlenSlotBytesLse, 256) + 2 * (size_t)P * kVarlenSlotBytesO;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_varlen_default_workgroups(int device, int32_t* out_P) {
+    if (!out_P) return LBSA_ERR_INVALID_ARGUMENT;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return LBSA_ERR_HIP;
+    if (varlen_occupancy(&per_cu) != hipSuccess || per_cu <= 0) return LBSA_ERR_HIP;
+    *out_P = cus * per_cu;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_plan_varlen(const int32_t* seqlens_d, const int32_t* qlens_d, int32_t batch, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t page_size, int32_t max_pages_per_seq, int64_t total_q,
+                              int32_t num_workgroups, int32_t min_tiles_per_bin, void* task_map_d,
+                              size_t task_map_bytes, void* stream) {
+    HookGuard guard;
+    int s = check_shape(batch, num_heads, num_kv_heads, kHeadDim, page_size);
+    if (s != LBSA_OK) return s;
+    s = varlen_shape(batch, num_kv_heads, num_workgroups, total_q);
+    if (s != LBSA_OK) return s;
+    if (!seqlens_d || !qlens_d || !task_map_d || max_pages_per_seq <= 0 || min_tiles_per_bin < 0 ||
+        !aligned(task_map_d, 32) || !aligned(seqlens_d, 4) || !aligned(qlens_d, 4))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    const int64_t nq = varlen_max_blocks(batch, total_q);
+    // every tile index and prefix stays far from int32 overflow
+    if (nq * max_pages_per_seq * num_kv_heads >= (1LL << 30) || (long long)max_pages_per_seq * kTile >= (1LL << 30))
+        return LBSA_ERR_UNSUPPORTED;
+    size_t need = 0;
+    lbsa_varlen_task_map_bytes(batch, num_kv_heads, num_workgroups, total_q, &need);
+    if (task_map_bytes < need) return LBSA_ERR_INVALID_ARGUMENT;
+    const int F = min_tiles_per_bin == 0 ? LBSA_DEFAULT_MIN_TILES : min_tiles_per_bin;
+    return hip_status(launch_assign_varlen(seqlens_d, qlens_d, batch, num_heads, num_kv_heads, num_workgroups, F,
+                                           max_pages_per_seq, total_q, nq, task_map_d,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+LBSA_API int lbsa_attend_varlen(const void* q_d, const void* k_cache_d, const void* v_cache_d,
+                                const int32_t* page_table_d, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t page_size, int32_t max_pages_per_seq, int64_t num_pages,
+                                int64_t total_q, int32_t num_workgroups, float softmax_scale, const void* task_map_d,
+                                size_t task_map_bytes, void* workspace_d, size_t workspace_bytes, void* out_d,
+                                void* stream) {
+    HookGuard guard;
+    int s = check_shape(batch, num_heads, num_kv_heads, head_dim, page_size);
+    if (s != LBSA_OK) return s;
+    s = varlen_shape(batch, num_kv_heads, num_workgroups, total_q);
+    if (s != LBSA_OK) return s;
+    if (total_q * num_heads >= (1LL << 31) / kHeadDim || (long long)max_pages_per_seq * kTile > INT_MAX / 2)
+        return LBSA_ERR_UNSUPPORTED;
+    if (!q_d || !k_cache_d || !v_cache_d || !page_table_d || !task_map_d || !workspace_d || !out_d ||
+        max_pages_per_seq <= 0 || num_pages <= 0 || !(softmax_scale > 0.f) || !(softmax_scale < INFINITY))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q_d, 16) || !aligned(k_cache_d, 16) || !aligned(v_cache_d, 16) || !aligned(out_d, 8) ||
+        !aligned(page_table_d, 4) || !aligned(task_map_d, 32) || !aligned(workspace_d, 256))
+        return LBSA_ERR_INVALID_ARGUMENT;
+    size_t map_need = 0, ws_need = 0;
+    lbsa_varlen_task_map_bytes(batch, num_kv_heads, num_workgroups, total_q, &map_need);
+    s = lbsa_varlen_workspace_bytes(num_heads, num_kv_heads, head_dim, num_workgroups, &ws_need);
+    if (s != LBSA_OK) return s;
+    if (task_map_bytes < map_need || workspace_bytes < ws_need) return LBSA_ERR_INVALID_ARGUMENT;
+    float* part_lse = static_cast<float*>(workspace_d);
+    float* part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) +
+                                             align_up(2 * (size_t)num_workgroups * kVarlenSlotBytesLse, 256));
+    return hip_status(launch_varlen(q_d, k_cache_d, v_cache_d, page_table_d, task_map_d, batch, num_heads,
+                                    num_kv_heads, num_workgroups, varlen_max_blocks(batch, total_q),
+                                    max_pages_per_seq, num_pages > INT32_MAX ? INT32_MAX : num_pages, total_q,
+                                    softmax_scale * kLog2eHost, part_lse, part_o, out_d,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 static int router_shape(int32_t m, int32_t n, int32_t k) {

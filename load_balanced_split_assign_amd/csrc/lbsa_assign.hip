@@ -233,7 +233,196 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Assign with query blocks (prefill / extend and decode rows on one map).  The
+// same cut of [0, T) at segment starts and bin starts, over segments
+// (h, request, query block): block u of one KV head belongs to request
+// blk_req[u] and spans ntile(u) = ceil(min(L, L - q + 16 (k + 1)) / 64) tiles;
+// segment s = h * NQ + u.  Besides the decode map's arrays it records, per
+// segment, the partial slot of its first chunk (2 * bin, + 1 when the chunk is
+// not its bin's first descriptor: only a bin's first and last descriptors can
+// cut a segment, so partial slots are numbered by bin), and per query block
+// its request and index, for the combine.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
+    const int32_t* __restrict__ seqlens, const int32_t* __restrict__ qlens, int B, int Hq, int Hkv, int P, int F,
+    int max_pages, int total_q, int nq_max, uint8_t* __restrict__ map) {
+    extern __shared__ int smem[];
+    __shared__ int red[4][kAssignThreads / 64];
+    const VarlenMapLayout L = varlen_map_layout(B, Hkv, P, nq_max);
+    int32_t* hdr = reinterpret_cast<int32_t*>(map + L.header);
+    int32_t* bdb = reinterpret_cast<int32_t*>(map + L.bin_desc_begin);
+    int32_t* desc = reinterpret_cast<int32_t*>(map + L.desc);
+    int32_t* sfd_g = reinterpret_cast<int32_t*>(map + L.seg_first_desc);
+    int32_t* snc_g = reinterpret_cast<int32_t*>(map + L.seg_num_chunks);
+    int32_t* slot0_g = reinterpret_cast<int32_t*>(map + L.seg_slot0);
+    int32_t* breq_g = reinterpret_cast<int32_t*>(map + L.blk_req);
+    int32_t* bk_g = reinterpret_cast<int32_t*>(map + L.blk_k);
+    int32_t* qbase_g = reinterpret_cast<int32_t*>(map + L.qbase);
+    int32_t* qstart_g = reinterpret_cast<int32_t*>(map + L.qstart);
+    int32_t* sl_g = reinterpret_cast<int32_t*>(map + L.seqlens);
+    int32_t* ql_g = reinterpret_cast<int32_t*>(map + L.qlens);
+
+    int* lens = smem;                  // [B]
+    int* qls = lens + B;               // [B]
+    int* qbase = qls + B;              // [B + 1] exclusive prefix of the query blocks per request
+    int* qstart = qbase + B + 1;       // [B + 1] exclusive prefix of q_b (packed query rows)
+    int* tpre = qstart + B + 1;        // [nq_max + 1] exclusive prefix of the blocks' tiles
+    int* sfd = tpre + nq_max + 1;      // [Hkv * nq_max + 1] exclusive prefix of chunks(s)
+    const int tid = threadIdx.x;
+
+    // ---- lengths, validation, query blocks and packed rows per request -----
+    const int per = (B + kAssignThreads - 1) / kAssignThreads;
+    const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+    int bad = 0, nq_local = 0, q_local = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int len = seqlens[b], q = qlens[b];
+        sl_g[b] = len;
+        ql_g[b] = q;
+        lens[b] = len;
+        qls[b] = q;
+        bad |= !(len >= 0 && (long long)len <= (long long)max_pages * kTile && q >= 1 && q <= len);
+        nq_local += q >= 1 ? (q + kQBlock - 1) / kQBlock : 0;
+        q_local += q >= 1 ? q : 0;
+    }
+    int NQ, QT;
+    int runb = block_exclusive_scan(nq_local, red[0], &NQ);
+    int runq = block_exclusive_scan(q_local, red[1], &QT);
+    // bad lengths, or query counts that disagree with the packed Q the caller sized
+    const int error = __syncthreads_or(bad) || QT != total_q || NQ > nq_max;
+    if (error) NQ = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int q = qls[b];
+        qbase[b] = error ? 0 : runb;
+        qstart[b] = error ? 0 : runq;
+        runb += q >= 1 ? (q + kQBlock - 1) / kQBlock : 0;
+        runq += q >= 1 ? q : 0;
+    }
+    if (tid == 0) {
+        qbase[B] = NQ;
+        qstart[B] = error ? 0 : QT;
+    }
+    __syncthreads();
+    for (int b = tid; b <= B; b += kAssignThreads) {
+        qbase_g[b] = qbase[b];
+        qstart_g[b] = qstart[b];
+    }
+
+    // ---- tiles of every query block: request by search over qbase ----------
+    const int uper = (NQ + kAssignThreads - 1) / kAssignThreads;
+    const int u0 = min(NQ, tid * uper), u1 = min(NQ, u0 + uper);
+    int t_local = 0;
+    for (int u = u0; u < u1; ++u) {
+        const int b = upper_bound(qbase, B, u) - 1;
+        const int k = u - qbase[b];
+        breq_g[u] = b;
+        bk_g[u] = k;
+        const int seen = lens[b] - qls[b] + min(qls[b], kQBlock * (k + 1));
+        const int nt = (seen + kTile - 1) / kTile;
+        tpre[u] = nt;
+        t_local += nt;
+    }
+    int N;
+    int run = block_exclusive_scan(t_local, red[2], &N);
+    for (int u = u0; u < u1; ++u) {
+        const int nt = tpre[u];
+        tpre[u] = run;
+        run += nt;
+    }
+    if (tid == 0) tpre[NQ] = N;
+    __syncthreads();
+
+    // ---- budget -------------------------------------------------------------
+    const int T = Hkv * N;
+    Bins bins;
+    bins.K = 0; bins.q = 0; bins.r = 0;
+    if (T > 0) {
+        bins.K = min(P, max(1, T / F));
+        bins.q = T / bins.K;
+        bins.r = T % bins.K;
+    }
+
+    // ---- chunks per segment s = h * NQ + u, their prefix, first-chunk slots --
+    const int S = Hkv * NQ;
+    const int sper = (S + kAssignThreads - 1) / kAssignThreads;
+    const int s0 = min(S, tid * sper), s1 = min(S, s0 + sper);
+    int c_local = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int h = s / NQ, u = s - h * NQ;
+        const int a = h * N + tpre[u], n = tpre[u + 1] - tpre[u];
+        const int c = n ? bins.of(a + n - 1) - bins.of(a) + 1 : 0;
+        sfd[s] = c;
+        c_local += c;
+        const int j0 = n ? bins.of(a) : 0;
+        slot0_g[s] = 2 * j0 + (n && a != bins.start(j0) ? 1 : 0);
+    }
+    int ndesc;
+    run = block_exclusive_scan(c_local, red[3], &ndesc);
+    for (int s = s0; s < s1; ++s) {
+        const int c = sfd[s];
+        sfd[s] = run;
+        sfd_g[s] = run;
+        snc_g[s] = c;
+        run += c;
+    }
+    if (tid == 0) sfd[S] = ndesc;
+    __syncthreads();
+
+    // ---- bins: thread j walks bin j's tile range segment by segment ---------
+    for (int j = tid; j <= P; j += kAssignThreads) {
+        int v = ndesc;
+        if (j < bins.K) {
+            int x = bins.start(j);
+            const int xe = bins.start(j + 1);
+            int h = x / N;
+            int u = upper_bound(tpre, NQ, x - h * N) - 1;
+            int a = h * N + tpre[u];
+            v = sfd[h * NQ + u] + (j - bins.of(a));
+            const int cap = S + P;
+            for (int d = v; d < cap; ++d) {
+                const int e = h * N + tpre[u + 1];            // end of segment (h, u)
+                const int t1 = min(e, xe);
+                const int b = upper_bound(qbase, B, u) - 1;
+                int32_t* rec = desc + (size_t)kVarlenDescWords * d;
+                *reinterpret_cast<int4*>(rec) = make_int4(h, b, u - qbase[b], x - a);
+                *reinterpret_cast<int4*>(rec + 4) = make_int4(t1 - a, lens[b], qls[b], qstart[b]);
+                if (t1 >= xe) break;
+                x = t1;                                       // blocks are never empty: the next one
+                if (++u == NQ) { u = 0; ++h; }
+                a = h * N + tpre[u];
+            }
+        }
+        bdb[j] = v;
+    }
+
+    if (tid == 0) {
+        hdr[0] = T;
+        hdr[1] = bins.K;
+        hdr[2] = bins.q;
+        hdr[3] = bins.r;
+        hdr[4] = ndesc;
+        hdr[5] = P;
+        hdr[6] = F;
+        hdr[7] = B;
+        hdr[8] = Hq;
+        hdr[9] = Hkv;
+        hdr[10] = error;
+        hdr[11] = N;
+        hdr[12] = max_pages;
+        hdr[13] = kTile;
+        hdr[14] = NQ;
+        hdr[15] = kQBlock;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_assign_varlen(const int32_t* seqlens, const int32_t* qlens, int B, int Hq, int Hkv, int P, int F,
+                                int max_pages, int64_t total_q, int64_t nq_max, void* map, hipStream_t stream) {
+    const size_t lds = sizeof(int) * varlen_assign_lds_words(B, Hkv, nq_max);
+    return launch(assign_varlen_kernel, dim3(1), dim3(kAssignThreads), (uint32_t)lds, stream, seqlens, qlens, B, Hq,
+                  Hkv, P, F, max_pages, (int)total_q, (int)nq_max, static_cast<uint8_t*>(map));
+}
 
 hipError_t launch_assign(const int32_t* seqlens, int B, int Hq, int Hkv, int P, int F,
                          int max_pages, void* map, hipStream_t stream) {

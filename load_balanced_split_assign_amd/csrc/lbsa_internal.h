@@ -67,6 +67,56 @@ __host__ __device__ inline MapLayout map_layout(int B, int Hkv, int P) {
     return m;
 }
 
+// ---------------------------------------------------------------------------
+// Prefill / extend on the task map.  Request b brings q_b new tokens (the last
+// q_b of its L_b cached ones); its queries form blocks of kQBlock positions,
+// and a segment is (KV head, request, query block) spanning the tiles that the
+// block's last query sees.  Segments are walked head-major, batch-minor, query
+// block innermost, with the decode budget, fill and spill.  Q and out are
+// packed [sum q_b][Hq][128].
+// ---------------------------------------------------------------------------
+constexpr int kQBlock = 16;                 // query positions per block (one split workgroup's columns)
+constexpr int kVarlenDescWords = 8;         // h, b, k, t0, t1, L, q, qstart: one 32-byte record
+enum { VD_H = 0, VD_B = 1, VD_K = 2, VD_T0 = 3, VD_T1 = 4, VD_L = 5, VD_Q = 6, VD_QS = 7 };
+constexpr int kVarlenRows = kQBlock * kGroup;   // partial rows per slot: position p, head g -> p * 8 + g
+
+// Query blocks a map must hold: sum_b ceil(q_b / 16) <= B + total_q / 16.
+__host__ __device__ inline int64_t varlen_max_blocks(int B, int64_t total_q) { return B + total_q / kQBlock; }
+
+// Byte offsets of a prefill / extend task map for B requests, Hkv KV heads, P
+// bins and at most NQ query blocks per KV head.
+struct VarlenMapLayout {
+    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seg_slot0, blk_req, blk_k, qbase,
+        qstart, seqlens, qlens, total;
+};
+
+__host__ __device__ inline VarlenMapLayout varlen_map_layout(int B, int Hkv, int P, int64_t NQ) {
+    VarlenMapLayout m;
+    const size_t S = (size_t)Hkv * (size_t)NQ;
+    const size_t cap = S + (size_t)P;
+    m.header = 0;
+    m.bin_desc_begin = 64;
+    m.desc = align_up(m.bin_desc_begin + 4 * ((size_t)P + 1), 32);
+    m.seg_first_desc = m.desc + 4 * kVarlenDescWords * cap;
+    m.seg_num_chunks = m.seg_first_desc + 4 * S;
+    m.seg_slot0 = m.seg_num_chunks + 4 * S;
+    m.blk_req = m.seg_slot0 + 4 * S;
+    m.blk_k = m.blk_req + 4 * (size_t)NQ;
+    m.qbase = m.blk_k + 4 * (size_t)NQ;
+    m.qstart = m.qbase + 4 * ((size_t)B + 1);
+    m.seqlens = m.qstart + 4 * ((size_t)B + 1);
+    m.qlens = m.seqlens + 4 * (size_t)B;
+    m.total = align_up(m.qlens + 4 * (size_t)B, 256);
+    return m;
+}
+
+// LDS words the varlen assign kernel needs: lengths, q lengths, their two
+// prefixes, the tile prefix over query blocks and the chunk prefix over
+// segments.
+__host__ __device__ inline size_t varlen_assign_lds_words(int B, int Hkv, int64_t NQ) {
+    return 4 * (size_t)B + 2 + ((size_t)NQ + 1) + ((size_t)Hkv * NQ + 1);
+}
+
 // Byte offsets of the partial buffers for `slots` partials of (q_len x G) x D
 // (one row per query token and head of the group).
 struct WsLayout {
@@ -110,10 +160,17 @@ struct AttnArgs {
 // Host launchers (defined in the .hip files).
 hipError_t launch_assign(const int32_t* seqlens, int B, int Hq, int Hkv, int P, int F,
                          int max_pages, void* map, hipStream_t stream);
+hipError_t launch_assign_varlen(const int32_t* seqlens, const int32_t* qlens, int B, int Hq, int Hkv, int P, int F,
+                                int max_pages, int64_t total_q, int64_t nq_max, void* map, hipStream_t stream);
 hipError_t launch_split(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream);
 hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu);
+hipError_t launch_varlen(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
+                         const void* map, int B, int Hq, int Hkv, int P, int64_t nq_max, int max_pages,
+                         int64_t num_pages, int64_t total_q, float scale_log2, float* part_lse, float* part_o,
+                         void* out, hipStream_t stream);
+hipError_t varlen_occupancy(int* blocks_per_cu);
 hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                           const int32_t* seqlens, int B, int QL, int Hq, int Hkv, int max_pages,
                           int64_t num_pages, float scale_log2, void* out, int cb, hipStream_t stream);

@@ -79,6 +79,244 @@ __device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > 
 
 
 
+// One query block of one (request, KV head) over the KV tiles [t0, t1) of the
+// request: what a prefill workgroup computes for its block, and what a
+// persistent workgroup computes for one descriptor of a prefill / extend map.
+struct QBlock {
+    const uint16_t* q0;          // row of the block's first position, head 0 (row p at q0 + p * Hq * 128)
+    const uint16_t* k_cache;     // [pages][64][Hkv][128]
+    const uint16_t* v_cache;
+    const int32_t* pt;           // the request's page-table row
+    int64_t num_pages;
+    int Hq, Hkv, h;
+    int L;                       // the request's cached tokens (0 if invalid)
+    int live;                    // positions of the block that are real queries
+    int off;                     // block position p sees tokens [0, off + p]
+    float scale_log2;
+};
+
+// Column state of one wave after a block: acc[cb][db] = O^T (unnormalised),
+// m[cb] the log2-domain reference maximum, l[cb] the column sums of P (every
+// element holds the sum).  Position of block column (cb, r): kPosWave w + 2 cb + r / 8.
+template <int CB>
+struct QBlockState {
+    f32x4 acc[CB][8];
+    float m[CB];
+    f32x4 l[CB];
+    bool bad;
+};
+
+template <int CB>
+__device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock& a, lds_char* ring, int t0, int t1,
+                                                                    QBlockState<CB>& st) {
+    constexpr int kPosWave = 2 * CB;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int L = a.L;
+
+    // columns of this lane: block position p0 + 2 cb + r / 8, head r % 8
+    const int p0 = w * kPosWave;
+    int pos[CB], lim[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        pos[cb] = p0 + 2 * cb + (r >> 3);
+        lim[cb] = pos[cb] < a.live ? clampi(a.off + pos[cb] + 1, 0, L) : 0;
+    }
+    // smallest limit over this wave's live columns (its first position): tokens
+    // below it are visible to every live column
+    const int lim_lo = p0 < a.live ? clampi(a.off + p0 + 1, 0, L) : 0;
+    const int pw_last = min(p0 + kPosWave, a.live) - 1;   // this wave's last live position
+    const int lim_wave = pw_last >= p0 ? clampi(a.off + pw_last + 1, 0, L) : 0;
+
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) st.acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m[cb] = kNegInf;
+        st.l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (t1 <= t0) return;
+
+    // Q of every column of this lane (B operand: 8 dims per k-step), then wait
+    // for it once before the ring starts
+    uint4 q[CB][4];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const bool live = pos[cb] < a.live;
+        const int p = live ? pos[cb] : 0;
+        const uint4* qp =
+            reinterpret_cast<const uint4*>(a.q0 + ((size_t)p * a.Hq + (size_t)a.h * kGroup + (r & 7)) * kHeadDim);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) q[cb][ks] = live ? qp[g + 4 * ks] : make_uint4(0, 0, 0, 0);
+    }
+    wait_vmcnt<0>();
+
+    // this lane's 4 K and 4 V chunks of every tile: rows 16 w + 4 s + lane / 16,
+    // chunk lane % 16, XOR-swizzled by the row inside the wave's 16
+    uint32_t live_off[4], live_off_v[4], dead_off[4];
+    int lrow[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        lrow[s] = 4 * s + (lane >> 4);
+        const uint32_t chunk = 16u * (uint32_t)((lane & 15) ^ lrow[s]);
+        const uint32_t chunk_v = 16u * (uint32_t)((lane & 15) ^ swz_v(lrow[s]));
+        const uint32_t row_off = (uint32_t)(16 * w + lrow[s]) * (uint32_t)a.Hkv * kPfRow;
+        live_off[s] = row_off + chunk;
+        live_off_v[s] = row_off + chunk_v;
+        dead_off[s] = 16u * (uint32_t)(lane & 15);    // row 0 of the page: always live
+    }
+    const auto* pt = uniform_ptr<int32_t>(a.pt);
+    auto issue = [&](int t, lds_char* stg) {
+        int64_t page = pt[t];
+        if (page < 0 || page >= a.num_pages) {
+            st.bad = true;
+            page = 0;
+        }
+        const size_t pbase = ((size_t)page * kTile * a.Hkv + a.h) * kPfRow;
+        const char* kb = reinterpret_cast<const char*>(a.k_cache) + pbase;
+        const char* vb = reinterpret_cast<const char*>(a.v_cache) + pbase;
+        const int tok0 = kTile * t + 16 * w;
+        const bool full = tok0 + 16 <= L;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const bool live = full || tok0 + lrow[s] < L;
+            dma16(kb + (live ? live_off[s] : dead_off[s]), stg + w * kPfSlice + 1024 * s);
+            dma16(vb + (live ? live_off_v[s] : dead_off[s]), stg + kPfHalf + w * kPfSlice + 1024 * s);
+        }
+    };
+    for (int u = 0; u < kPfStages - 1; ++u) issue(min(t0 + u, t1 - 1), ring + u * kPfStageBytes);
+
+    // lane parts of the ring read addresses (stage 0, first 16 rows); the
+    // stage and the 16-row sub-tile are the reads' immediate offsets
+    uint32_t ka[4], vaddr[8];
+    {
+        const uint32_t rb = lds_addr(ring);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ka[ks] = rb + r * kPfRow + 16 * ((g + 4 * ks) ^ r);
+        const int vrow = 4 * g + (r >> 2);
+        const uint32_t vr = rb + kPfHalf + vrow * kPfRow + 8 * (r & 1);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_v(vrow));
+    }
+
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    // 32 tokens [t32, t32 + 32) of the tile whose rows start at ring byte OFF
+    auto half_step = [&](auto off_c, int t32) {
+        constexpr int OFF = decltype(off_c)::value;
+        // ---- K (A operand of S^T) and V^T reads of 32 tokens, two 16-token
+        // sub-tiles, shared by all CB blocks
+        uint4 kk[2][4];
+        s16x4 va[2][8];
+        lds_read_tile_bf16_at<OFF>(kk[0], va[0], ka, vaddr);
+        lds_read_tile_bf16_at<OFF + 16 * kPfRow>(kk[1], va[1], ka, vaddr);
+
+        // ---- S^T = K Q^T: s[cb][sub][i] is token t32 + 16 sub + 4 g + i
+        f32x4 s[CB][2];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+                f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][1]), as_bf16x8(q[cb][1]), sa, 0, 0, 0);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][3]), as_bf16x8(q[cb][3]), sa, 0, 0, 0);
+                s[cb][sub] = sa;
+            }
+        }
+
+        // ---- online softmax over the 8 scores of this lane per block.  Half-
+        // tiles that reach a live column's limit get -inf above it (raw score
+        // domain); then one path for all: the scale folds into the fma before
+        // each exp2 (exp2(-inf) = 0), and the block maximum is the scale times
+        // the raw maximum (the scale is positive).  The maximum propagates NaN
+        // (v_maximum3), which needs no canonicalising of the MFMA results.
+        const int tok = t32 + 4 * g;
+        if (t32 + 31 >= lim_lo) {                                     // uniform
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (tok + 16 * sub + i >= lim[cb]) s[cb][sub][i] = kNegInf;
+        }
+        float lmax[CB];
+        bool need = false;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const f32x4 x0 = s[cb][0], x1 = s[cb][1];
+            float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x0[0], x0[1]), x0[2]);
+            mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, x0[3]), x1[0]);
+            mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, x1[1]), x1[2]);
+            mx = __builtin_elementwise_maximum(mx, x1[3]);
+            lmax[cb] = mx * a.scale_log2;
+            need |= lmax[cb] > st.m[cb] + kPfSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            // a score above a column's reference: new reference = max over
+            // the column's 32 tokens (0 rescale for a column still fully masked)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                float mt = fmaxf(lmax[cb], __shfl_xor(lmax[cb], 16, 64));
+                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                const float m_new = fmaxf(st.m[cb], mt);
+                const float alpha = st.m[cb] == kNegInf ? 0.f : exp2_fast(st.m[cb] - m_new);
+                st.l[cb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) st.acc[cb][db] *= alpha;
+                st.m[cb] = m_new;
+            }
+        }
+
+        // ---- P and O^T += V^T P^T with MFMA 16x16x32: k = the 32 tokens,
+        // lane group g holding tokens 4g .. 4g + 3 of both sub-tiles, in the
+        // same order in the V^T operand (two transposed reads) and in P
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const float mref = st.m[cb] == kNegInf ? 0.f : st.m[cb];
+            float p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(s[cb][j >> 2][j & 3], a.scale_log2, -mref));
+            const bf16x8 pb = __builtin_bit_cast(
+                bf16x8, make_uint4(bf16x2_pack(p[0], p[1]), bf16x2_pack(p[2], p[3]),
+                                   bf16x2_pack(p[4], p[5]), bf16x2_pack(p[6], p[7])));
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const bf16x8 vt = __builtin_bit_cast(
+                    bf16x8, make_uint4(__builtin_bit_cast(uint2, va[0][db]).x,
+                                       __builtin_bit_cast(uint2, va[0][db]).y,
+                                       __builtin_bit_cast(uint2, va[1][db]).x,
+                                       __builtin_bit_cast(uint2, va[1][db]).y));
+                st.acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, st.acc[cb][db], 0, 0, 0);
+            }
+            // the softmax denominator over the same bf16 P as the numerator
+            st.l[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, st.l[cb], 0, 0, 0);
+        }
+    };
+
+    // tile k sits in ring stage U = (k - t0) % 2.  Every tile issues the same
+    // number of loads (past the end the last tile is loaded again into a stage
+    // nobody reads), so one wait count fits all
+    auto tile_step = [&](auto u_c, int k) {
+        constexpr int U = decltype(u_c)::value;
+        wait_vmcnt<(kPfStages - 2) * kPfLoads>();                 // this wave's rows of tile k
+        lds_barrier();                                          // everyone's rows; stage of k-1 free
+        issue(min(k + kPfStages - 1, t1 - 1), ring + (1 - U) * kPfStageBytes);
+        if (kTile * k >= lim_wave) return;                      // nothing of it is visible here
+        half_step(std::integral_constant<int, U * kPfStageBytes>{}, kTile * k);
+        if (kTile * k + 32 < lim_wave)
+            half_step(std::integral_constant<int, U * kPfStageBytes + 32 * kPfRow>{}, kTile * k + 32);
+    };
+    static_assert(kPfStages == 2, "tile_step alternates two stages");
+    for (int k = t0; k < t1; k += 2) {
+        tile_step(std::integral_constant<int, 0>{}, k);
+        if (k + 1 < t1) tile_step(std::integral_constant<int, 1>{}, k + 1);
+    }
+    wait_vmcnt<0>();   // no load may still target LDS when the block ends
+}
+
 template <int CB>
 __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char ring_mem[kPfStages * kPfStageBytes];
@@ -97,231 +335,232 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
     int L = uniform_ptr<int32_t>(a.seqlens)[b];
     const bool len_ok = L >= 0 && L <= a.max_pages * kTile;
     if (!len_ok) L = 0;
-    const int off = L - a.QL;                             // query i sees tokens < off + i + 1
-
-    // columns of this lane: position p0 + 2 cb + r / 8, head r % 8
-    const int p0 = qb * kPosBlock + w * kPosWave;
-    int pos[CB], lim[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        pos[cb] = p0 + 2 * cb + (r >> 3);
-        lim[cb] = pos[cb] < a.QL ? clampi(off + pos[cb] + 1, 0, L) : 0;
-    }
-    // smallest limit over this wave's live columns (its first position): tokens
-    // below it are visible to every live column
-    const int lim_lo = p0 < a.QL ? clampi(off + p0 + 1, 0, L) : 0;
-    const int pw_last = min(p0 + kPosWave, a.QL) - 1;     // this wave's last live position
-    const int lim_wave = pw_last >= p0 ? clampi(off + pw_last + 1, 0, L) : 0;
-    const int pb_last = min(qb * kPosBlock + kPosBlock, a.QL) - 1;
-    const int lim_blk = pb_last >= qb * kPosBlock ? clampi(off + pb_last + 1, 0, L) : 0;
+    const int pos0 = qb * kPosBlock;
+    QBlock blk;
+    blk.q0 = a.q + (size_t)(b * a.QL + pos0) * a.Hq * kHeadDim;
+    blk.k_cache = a.k_cache;
+    blk.v_cache = a.v_cache;
+    blk.pt = a.page_table + (size_t)b * a.max_pages;
+    blk.num_pages = a.num_pages;
+    blk.Hq = a.Hq;
+    blk.Hkv = a.Hkv;
+    blk.h = h;
+    blk.L = L;
+    blk.live = max(0, min(kPosBlock, a.QL - pos0));
+    blk.off = L - a.QL + pos0;                            // block position p sees tokens < off + p + 1
+    blk.scale_log2 = a.scale_log2;
+    const int pb_last = blk.live - 1;
+    const int lim_blk = pb_last >= 0 ? clampi(blk.off + pb_last + 1, 0, L) : 0;
     const int ntiles = (lim_blk + kTile - 1) / kTile;
 
-    f32x4 acc[CB][8];
-    float m[CB];
-    f32x4 l[CB];        // column sums of P, from an MFMA with an all-ones A: every element holds it
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m[cb] = kNegInf;
-        l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    bool bad = !len_ok;
-
-    if (ntiles > 0) {
-        // Q of every column of this lane (B operand: 8 dims per k-step), then
-        // wait for it once before the ring starts
-        uint4 q[CB][4];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const bool live = pos[cb] < a.QL;
-            const int p = live ? pos[cb] : 0;
-            const uint4* qp = reinterpret_cast<const uint4*>(
-                a.q + ((size_t)(b * a.QL + p) * a.Hq + (size_t)h * kGroup + (r & 7)) * kHeadDim);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) q[cb][ks] = live ? qp[g + 4 * ks] : make_uint4(0, 0, 0, 0);
-        }
-        wait_vmcnt<0>();
-
-        // this lane's 4 K and 4 V chunks of every tile: rows 16 w + 4 s + lane / 16,
-        // chunk lane % 16, XOR-swizzled by the row inside the wave's 16
-        uint32_t live_off[4], live_off_v[4], dead_off[4];
-        int lrow[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            lrow[s] = 4 * s + (lane >> 4);
-            const uint32_t chunk = 16u * (uint32_t)((lane & 15) ^ lrow[s]);
-            const uint32_t chunk_v = 16u * (uint32_t)((lane & 15) ^ swz_v(lrow[s]));
-            const uint32_t row_off = (uint32_t)(16 * w + lrow[s]) * (uint32_t)a.Hkv * kPfRow;
-            live_off[s] = row_off + chunk;
-            live_off_v[s] = row_off + chunk_v;
-            dead_off[s] = 16u * (uint32_t)(lane & 15);    // row 0 of the page: always live
-        }
-        const auto* pt = uniform_ptr<int32_t>(a.page_table) + (size_t)b * a.max_pages;
-        auto issue = [&](int t, lds_char* st) {
-            int64_t page = pt[t];
-            if (page < 0 || page >= a.num_pages) {
-                bad = true;
-                page = 0;
-            }
-            const size_t pbase = ((size_t)page * kTile * a.Hkv + h) * kPfRow;
-            const char* kb = reinterpret_cast<const char*>(a.k_cache) + pbase;
-            const char* vb = reinterpret_cast<const char*>(a.v_cache) + pbase;
-            const int tok0 = kTile * t + 16 * w;
-            const bool full = tok0 + 16 <= L;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bool live = full || tok0 + lrow[s] < L;
-                dma16(kb + (live ? live_off[s] : dead_off[s]), st + w * kPfSlice + 1024 * s);
-                dma16(vb + (live ? live_off_v[s] : dead_off[s]), st + kPfHalf + w * kPfSlice + 1024 * s);
-            }
-        };
-        for (int u = 0; u < kPfStages - 1; ++u) issue(min(u, ntiles - 1), ring + u * kPfStageBytes);
-
-        // lane parts of the ring read addresses (stage 0, first 16 rows); the
-        // stage and the 16-row sub-tile are the reads' immediate offsets
-        uint32_t ka[4], vaddr[8];
-        {
-            const uint32_t rb = lds_addr(ring);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) ka[ks] = rb + r * kPfRow + 16 * ((g + 4 * ks) ^ r);
-            const int vrow = 4 * g + (r >> 2);
-            const uint32_t vr = rb + kPfHalf + vrow * kPfRow + 8 * (r & 1);
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-                vaddr[db] = vr + 16u * (uint32_t)((2 * db + ((r >> 1) & 1)) ^ swz_v(vrow));
-        }
-
-        const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-        // 32 tokens [t32, t32 + 32) of the tile whose rows start at ring byte OFF
-        auto half_step = [&](auto off_c, int t32) {
-            constexpr int OFF = decltype(off_c)::value;
-            // ---- K (A operand of S^T) and V^T reads of 32 tokens, two 16-token
-            // sub-tiles, shared by all CB blocks
-            uint4 kk[2][4];
-            s16x4 va[2][8];
-            lds_read_tile_bf16_at<OFF>(kk[0], va[0], ka, vaddr);
-            lds_read_tile_bf16_at<OFF + 16 * kPfRow>(kk[1], va[1], ka, vaddr);
-
-            // ---- S^T = K Q^T: s[cb][sub][i] is token t32 + 16 sub + 4 g + i
-            f32x4 s[CB][2];
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
-                    f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
-                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][1]), as_bf16x8(q[cb][1]), sa, 0, 0, 0);
-                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
-                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][3]), as_bf16x8(q[cb][3]), sa, 0, 0, 0);
-                    s[cb][sub] = sa;
-                }
-            }
-
-            // ---- online softmax over the 8 scores of this lane per block.  Half-
-            // tiles that reach a live column's limit get -inf above it (raw score
-            // domain); then one path for all: the scale folds into the fma before
-            // each exp2 (exp2(-inf) = 0), and the block maximum is the scale times
-            // the raw maximum (the scale is positive).  The maximum propagates NaN
-            // (v_maximum3), which needs no canonicalising of the MFMA results.
-            const int tok = t32 + 4 * g;
-            if (t32 + 31 >= lim_lo) {                                     // uniform
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (tok + 16 * sub + i >= lim[cb]) s[cb][sub][i] = kNegInf;
-            }
-            float lmax[CB];
-            bool need = false;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const f32x4 x0 = s[cb][0], x1 = s[cb][1];
-                float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x0[0], x0[1]), x0[2]);
-                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, x0[3]), x1[0]);
-                mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, x1[1]), x1[2]);
-                mx = __builtin_elementwise_maximum(mx, x1[3]);
-                lmax[cb] = mx * a.scale_log2;
-                need |= lmax[cb] > m[cb] + kPfSlack;
-            }
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                // a score above a column's reference: new reference = max over
-                // the column's 32 tokens (0 rescale for a column still fully masked)
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    float mt = fmaxf(lmax[cb], __shfl_xor(lmax[cb], 16, 64));
-                    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-                    const float m_new = fmaxf(m[cb], mt);
-                    const float alpha = m[cb] == kNegInf ? 0.f : exp2_fast(m[cb] - m_new);
-                    l[cb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < 8; ++db) acc[cb][db] *= alpha;
-                    m[cb] = m_new;
-                }
-            }
-
-            // ---- P and O^T += V^T P^T with MFMA 16x16x32: k = the 32 tokens,
-            // lane group g holding tokens 4g .. 4g + 3 of both sub-tiles, in the
-            // same order in the V^T operand (two transposed reads) and in P
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const float mref = m[cb] == kNegInf ? 0.f : m[cb];
-                float p[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(s[cb][j >> 2][j & 3], a.scale_log2, -mref));
-                const bf16x8 pb = __builtin_bit_cast(
-                    bf16x8, make_uint4(bf16x2_pack(p[0], p[1]), bf16x2_pack(p[2], p[3]),
-                                       bf16x2_pack(p[4], p[5]), bf16x2_pack(p[6], p[7])));
-#pragma unroll
-                for (int db = 0; db < 8; ++db) {
-                    const bf16x8 vt = __builtin_bit_cast(
-                        bf16x8, make_uint4(__builtin_bit_cast(uint2, va[0][db]).x,
-                                           __builtin_bit_cast(uint2, va[0][db]).y,
-                                           __builtin_bit_cast(uint2, va[1][db]).x,
-                                           __builtin_bit_cast(uint2, va[1][db]).y));
-                    acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, acc[cb][db], 0, 0, 0);
-                }
-                // the softmax denominator over the same bf16 P as the numerator
-                l[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, l[cb], 0, 0, 0);
-            }
-        };
-
-        // tile k sits in ring stage U = k % 2.  Every tile issues the same number
-        // of loads (past the end the last tile is loaded again into a stage
-        // nobody reads), so one wait count fits all
-        auto tile_step = [&](auto u_c, int k) {
-            constexpr int U = decltype(u_c)::value;
-            wait_vmcnt<(kPfStages - 2) * kPfLoads>();                 // this wave's rows of tile k
-            lds_barrier();                                          // everyone's rows; stage of k-1 free
-            issue(min(k + kPfStages - 1, ntiles - 1), ring + (1 - U) * kPfStageBytes);
-            if (kTile * k >= lim_wave) return;                      // nothing of it is visible here
-            half_step(std::integral_constant<int, U * kPfStageBytes>{}, kTile * k);
-            if (kTile * k + 32 < lim_wave)
-                half_step(std::integral_constant<int, U * kPfStageBytes + 32 * kPfRow>{}, kTile * k + 32);
-        };
-        static_assert(kPfStages == 2, "tile_step alternates two stages");
-        for (int k = 0; k < ntiles; k += 2) {
-            tile_step(std::integral_constant<int, 0>{}, k);
-            if (k + 1 < ntiles) tile_step(std::integral_constant<int, 1>{}, k + 1);
-        }
-        wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
-    }
+    QBlockState<CB> st;
+    st.bad = !len_ok;
+    attend_qblock<CB>(blk, ring, 0, ntiles, st);
 
     // ---- normalise and store: lane (g, r) holds dims 16 db + 4 g .. + 3 of column r
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        const float lt = l[cb][0];
-        if (pos[cb] >= a.QL) continue;
+        const int p = w * kPosWave + 2 * cb + (r >> 3);
+        const float lt = st.l[cb][0];
+        if (p >= blk.live) continue;
         float inv = lt > 0.f ? 1.f / lt : 0.f;            // a query that sees nothing: zeros
-        if (bad) inv = __builtin_nanf("");
-        uint16_t* o = a.out + ((size_t)(b * a.QL + pos[cb]) * a.Hq + (size_t)h * kGroup + (r & 7)) * kHeadDim + 4 * g;
+        if (st.bad) inv = __builtin_nanf("");
+        uint16_t* o = a.out + ((size_t)(b * a.QL + pos0 + p) * a.Hq + (size_t)h * kGroup + (r & 7)) * kHeadDim + 4 * g;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-            const f32x4 v = acc[cb][db] * inv;
+            const f32x4 v = st.acc[cb][db] * inv;
             *reinterpret_cast<uint2*>(o + 16 * db) = make_uint2(bf16x2_pack(v[0], v[1]), bf16x2_pack(v[2], v[3]));
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / extend on the task map.  Persistent workgroup j drains bin j of a
+// map built with query blocks (lbsa_plan_varlen): each descriptor is one query
+// block of one (request, KV head) over a range of its KV tiles, computed by the
+// same block loop as the grid kernel above.  A descriptor that covers its whole
+// segment writes the bf16 output rows of its block; a cut one -- only a bin's
+// first or last descriptor can be cut -- writes its partial (normalised O,
+// natural-log LSE) to slot 2 j (first) or 2 j + 1 (last), and
+// varlen_combine_kernel merges the chunks of each cut segment.
+// ---------------------------------------------------------------------------
+struct VarlenArgs {
+    const uint16_t* q;           // packed [total_q][Hq][128]
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const int32_t* page_table;   // [B][max_pages]
+    float* part_lse;             // [2 P][128]: row p * 8 + g of a slot
+    float* part_o;               // [2 P][128][128]
+    uint16_t* out;               // packed like q
+    int64_t num_pages;
+    int32_t Hq, max_pages, total_q;
+    float scale_log2;
+};
+
+// Four fp32 -> four bf16 (round to nearest even) in one 8-byte store.
+__device__ inline void store_bf16x4(uint16_t* p, f32x4 v) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(bf16x2_pack(v[0], v[1]), bf16x2_pack(v[2], v[3]));
+}
+
+__device__ inline int varlen_extent(int L, int q, int k) {   // tiles the block's last query sees
+    return (L - q + min(q, kQBlock * (k + 1)) + kTile - 1) / kTile;
+}
+
+__global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8_t* map, int B, int Hkv, int P,
+                                                                     int nq_max, VarlenArgs a) {
+    __shared__ __attribute__((aligned(16))) char ring_mem[kPfStages * kPfStageBytes];
+    lds_char* const ring = (lds_char*)ring_mem;
+    constexpr int CB = 2, kPosWave = 2 * CB;
+    static_assert(kWaves * kPosWave == kQBlock, "one workgroup holds one query block");
+    const VarlenMapLayout ML = varlen_map_layout(B, Hkv, P, nq_max);
+    const int j = blockIdx.x;
+    const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
+    const auto* bdb = uniform_ptr<int32_t>(map + ML.bin_desc_begin);
+    const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
+    const int d0 = bdb[j], d1 = bdb[j + 1];
+    const int cap = Hkv * nq_max + P;
+    if (h_err != 0 || h_p != P || h_b != B || h_hkv != Hkv || d0 < 0 || d1 < d0 || d1 > cap) return;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    for (int d = d0; d < d1; ++d) {
+        const auto* rec = uniform_ptr<int32_t>(map + ML.desc) + (size_t)kVarlenDescWords * d;
+        const int h = rec[VD_H], b = rec[VD_B], k = rec[VD_K], t0 = rec[VD_T0], t1 = rec[VD_T1];
+        const int L = rec[VD_L], q = rec[VD_Q], qs = rec[VD_QS];
+        // a record this map cannot hold (corrupt map): skipped, nothing read out of bounds
+        if (h < 0 || h >= Hkv || b < 0 || b >= B || L < 0 || L > a.max_pages * kTile || q < 1 || q > L ||
+            k < 0 || kQBlock * k >= q || qs < 0 || qs > a.total_q - q || t0 < 0 || t1 <= t0 ||
+            t1 > varlen_extent(L, q, k))
+            continue;
+        QBlock blk;
+        blk.q0 = a.q + (size_t)(qs + kQBlock * k) * a.Hq * kHeadDim;
+        blk.k_cache = a.k_cache;
+        blk.v_cache = a.v_cache;
+        blk.pt = a.page_table + (size_t)b * a.max_pages;
+        blk.num_pages = a.num_pages;
+        blk.Hq = a.Hq;
+        blk.Hkv = Hkv;
+        blk.h = h;
+        blk.L = L;
+        blk.live = min(kQBlock, q - kQBlock * k);
+        blk.off = L - q + kQBlock * k;
+        blk.scale_log2 = a.scale_log2;
+        QBlockState<CB> st;
+        st.bad = false;
+        attend_qblock<CB>(blk, ring, t0, t1, st);
+        const bool whole = t0 == 0 && t1 == varlen_extent(L, q, k);
+        const int slot = 2 * j + (d == d0 ? 0 : 1);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int p = w * kPosWave + 2 * cb + (r >> 3), gg = r & 7;
+            if (p >= blk.live) continue;
+            const float lt = st.l[cb][0];
+            float inv = lt > 0.f ? 1.f / lt : 0.f;        // a query that sees none of these tokens: O = 0
+            if (st.bad) inv = __builtin_nanf("");
+            if (whole) {
+                uint16_t* o = a.out + ((size_t)(qs + kQBlock * k + p) * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + 4 * g;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const f32x4 v = st.acc[cb][db] * inv;
+                    *reinterpret_cast<uint2*>(o + 16 * db) = make_uint2(bf16x2_pack(v[0], v[1]), bf16x2_pack(v[2], v[3]));
+                }
+            } else {
+                const size_t row = (size_t)slot * kVarlenRows + p * kGroup + gg;
+                float* o = a.part_o + row * kHeadDim + 4 * g;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[cb][db] * inv;
+                if (g == 0) {
+                    float lse = lt > 0.f ? (st.m[cb] + __builtin_log2f(lt)) * kLn2 : kNegInf;
+                    if (st.bad) lse = __builtin_nanf("");
+                    a.part_lse[row] = lse;
+                }
+            }
+        }
+        lds_barrier();   // every wave is done with the ring before the next descriptor's loads
+    }
+}
+
+// The chunks of cut segments, merged: workgroup (h, u) takes segment
+// s = h * NQ + u (query block u of KV head h) when it has two or more chunks.
+// Chunk c sits in slot slot0 (c = 0) or 2 (bin of chunk 0 + c): a cut
+// segment's chunks lie in consecutive bins, each after the first starting its
+// bin.  256 threads: 8 rows at a time (row p * 8 + g of the block), 32 threads
+// x 4 dims per row; the loads of up to 8 chunks are issued before the merge.
+constexpr int kVarlenCombineUnroll = 8;
+
+__global__ __launch_bounds__(kCombineThreads) void varlen_combine_kernel(const uint8_t* map, int B, int Hkv, int P,
+                                                                         int nq_max, VarlenArgs a) {
+    const VarlenMapLayout ML = varlen_map_layout(B, Hkv, P, nq_max);
+    const int h = (int)(blockIdx.x / (unsigned)nq_max), u = (int)(blockIdx.x % (unsigned)nq_max);
+    const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
+    const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
+    const int NQ = hdr[14];
+    const int tid = threadIdx.x, d4 = (tid & 31) * 4;
+    if (h_err != 0 || h_p != P || h_b != B || h_hkv != Hkv || NQ < 0 || NQ > nq_max) {
+        // a map built for another shape or from invalid lengths: every output row
+        // is NaN (packed rows u, u + nq_max, ... of the group's heads here)
+        const float nan = __builtin_nanf("");
+        for (int t = u; t < a.total_q; t += nq_max)
+            for (int gg = tid >> 5; gg < kGroup; gg += kCombineThreads / 32)
+                store_bf16x4(a.out + ((size_t)t * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + d4,
+                             f32x4{nan, nan, nan, nan});
+        return;
+    }
+    if (u >= NQ) return;
+    const int s = h * NQ + u;
+    const int sd0 = uniform_ptr<int32_t>(map + ML.seg_first_desc)[s];
+    const int n = uniform_ptr<int32_t>(map + ML.seg_num_chunks)[s];
+    const int slot0 = uniform_ptr<int32_t>(map + ML.seg_slot0)[s];
+    const int b = uniform_ptr<int32_t>(map + ML.blk_req)[u];
+    const int k = uniform_ptr<int32_t>(map + ML.blk_k)[u];
+    if (n < 2) return;                                  // one chunk: written by the split kernel
+    if (b < 0 || b >= B || slot0 < 0 || (slot0 >> 1) + n > P || sd0 < 0) return;   // corrupt map
+    const int q = uniform_ptr<int32_t>(map + ML.qlens)[b];
+    const int qs = uniform_ptr<int32_t>(map + ML.qstart)[b];
+    const int live = min(kQBlock, q - kQBlock * k);
+    if (live <= 0 || qs < 0 || qs + kQBlock * k + live > a.total_q) return;
+    const int bin0 = slot0 >> 1;
+    for (int row = tid >> 5; row < kVarlenRows; row += kCombineThreads / 32) {
+        const int p = row >> 3, gg = row & 7;
+        if (p >= live) break;                           // rows are position-major: the rest are dead too
+        float m = kNegInf, wsum = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        bool nan_seen = false;
+        for (int c0 = 0; c0 < n; c0 += kVarlenCombineUnroll) {
+            float l[kVarlenCombineUnroll];
+            f32x4 x[kVarlenCombineUnroll];
+#pragma unroll
+            for (int i = 0; i < kVarlenCombineUnroll; ++i) {
+                const int c = c0 + i;
+                if (c < n) {
+                    const size_t pr = (size_t)(c == 0 ? slot0 : 2 * (bin0 + c)) * kVarlenRows + row;
+                    l[i] = a.part_lse[pr];
+                    x[i] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kHeadDim + d4);
+                } else {
+                    l[i] = kNegInf;
+                    x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kVarlenCombineUnroll; ++i) {
+                if (l[i] != l[i]) { nan_seen = true; continue; }
+                if (l[i] == kNegInf) continue;
+                if (l[i] > m) {
+                    const float sc = exp2_fast((m - l[i]) * kLog2e);   // 0 when m = -inf
+                    wsum *= sc;
+                    o *= sc;
+                    m = l[i];
+                }
+                const float wgt = exp2_fast((l[i] - m) * kLog2e);
+                wsum += wgt;
+                o += wgt * x[i];
+            }
+        }
+        o *= wsum > 0.f ? 1.f / wsum : 0.f;
+        if (nan_seen) {
+            const float nan = __builtin_nanf("");
+            o = f32x4{nan, nan, nan, nan};
+        }
+        store_bf16x4(a.out + ((size_t)(qs + kQBlock * k + p) * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + d4, o);
     }
 }
 
@@ -334,6 +573,35 @@ hipError_t launch_cb(PrefillArgs a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_varlen(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
+                         const void* map, int B, int Hq, int Hkv, int P, int64_t nq_max, int max_pages,
+                         int64_t num_pages, int64_t total_q, float scale_log2, float* part_lse, float* part_o,
+                         void* out, hipStream_t stream) {
+    VarlenArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint16_t*>(k_cache);
+    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.page_table = page_table;
+    a.part_lse = part_lse;
+    a.part_o = part_o;
+    a.out = static_cast<uint16_t*>(out);
+    a.num_pages = num_pages;
+    a.Hq = Hq;
+    a.max_pages = max_pages;
+    a.total_q = (int32_t)total_q;
+    a.scale_log2 = scale_log2;
+    const uint8_t* m = static_cast<const uint8_t*>(map);
+    hipError_t e = launch(varlen_split_kernel, dim3(P), dim3(kSplitThreads), 0, stream, m, B, Hkv, P, (int)nq_max, a);
+    if (e != hipSuccess) return e;
+    const long long grid = (long long)nq_max * Hkv;
+    return launch(varlen_combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, m, B, Hkv, P,
+                  (int)nq_max, a);
+}
+
+hipError_t varlen_occupancy(int* blocks_per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, varlen_split_kernel, kSplitThreads, 0);
+}
 
 hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                           const int32_t* seqlens, int B, int QL, int Hq, int Hkv, int max_pages,

@@ -38,6 +38,12 @@ class _MapLayout(ctypes.Structure):
                  "desc_len", "total")]
 
 
+class _VarlenMapLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("header", "bin_desc_begin", "desc", "seg_first_desc", "seg_num_chunks", "seg_slot0", "blk_req",
+                 "blk_k", "qbase", "qstart", "seqlens", "qlens", "total")]
+
+
 class _WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("part_lse", "part_o", "total")]
 
@@ -71,6 +77,13 @@ def lib() -> ctypes.CDLL:
         L.lbsa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, i64, i32, f32, vp, sz, vp, vp]
         L.lbsa_prefill.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32, vp, vp]
+        L.lbsa_varlen_task_map_layout_get.argtypes = [i32, i32, i32, i64, ctypes.POINTER(_VarlenMapLayout)]
+        L.lbsa_varlen_task_map_bytes.argtypes = [i32, i32, i32, i64, ctypes.POINTER(sz)]
+        L.lbsa_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.lbsa_varlen_default_workgroups.argtypes = [ctypes.c_int, ctypes.POINTER(i32)]
+        L.lbsa_plan_varlen.argtypes = [vp, vp, i32, i32, i32, i32, i32, i64, i32, i32, vp, sz, vp]
+        L.lbsa_attend_varlen.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32, f32, vp, sz,
+                                         vp, sz, vp, vp]
         L.lbsa_router_split_weights.argtypes = [vp, i32, i32, vp, vp, vp]
         L.lbsa_router_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.lbsa_router_gemm.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -83,7 +96,9 @@ def lib() -> ctypes.CDLL:
                    "lbsa_plan", "lbsa_decode", "lbsa_decode_noalloc", "lbsa_decode_split", "lbsa_decode_combine",
                    "lbsa_decode_static", "lbsa_prefill", "lbsa_router_split_weights",
                    "lbsa_router_workspace_bytes", "lbsa_router_gemm", "lbsa_time_next_kernel",
-                   "lbsa_time_next_kernels"):
+                   "lbsa_time_next_kernels", "lbsa_varlen_task_map_layout_get", "lbsa_varlen_task_map_bytes",
+                   "lbsa_varlen_workspace_bytes", "lbsa_varlen_default_workgroups", "lbsa_plan_varlen",
+                   "lbsa_attend_varlen"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -354,6 +369,112 @@ def prefill(q, k_cache, v_cache, page_table, seqlens, softmax_scale: float, out=
     _check("lbsa_prefill", lib().lbsa_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), KV_BF16, _ptr(page_table),
                                               _ptr(seqlens), B, QL, Hq, Hkv, D, page, int(page_table.shape[1]),
                                               int(num_pages), float(softmax_scale), _ptr(out), _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# prefill / extend / decode rows on one task map (query blocks of 16 positions)
+# ---------------------------------------------------------------------------
+
+QBLOCK = 16
+
+
+def varlen_task_map_layout(batch: int, num_kv_heads: int, P: int, total_q: int) -> dict:
+    lay = _VarlenMapLayout()
+    _check("lbsa_varlen_task_map_layout_get",
+           lib().lbsa_varlen_task_map_layout_get(batch, num_kv_heads, P, total_q, ctypes.byref(lay)))
+    return {n: int(getattr(lay, n)) for n, _ in lay._fields_}
+
+
+def varlen_task_map_bytes(batch: int, num_kv_heads: int, P: int, total_q: int) -> int:
+    out = ctypes.c_size_t()
+    _check("lbsa_varlen_task_map_bytes",
+           lib().lbsa_varlen_task_map_bytes(batch, num_kv_heads, P, total_q, ctypes.byref(out)))
+    return out.value
+
+
+def varlen_workspace_bytes(num_heads: int, num_kv_heads: int, P: int) -> int:
+    out = ctypes.c_size_t()
+    _check("lbsa_varlen_workspace_bytes",
+           lib().lbsa_varlen_workspace_bytes(num_heads, num_kv_heads, HEAD_DIM, P, ctypes.byref(out)))
+    return out.value
+
+
+def varlen_default_workgroups(device: int = 0) -> int:
+    out = ctypes.c_int32()
+    _check("lbsa_varlen_default_workgroups", lib().lbsa_varlen_default_workgroups(device, ctypes.byref(out)))
+    return out.value
+
+
+def plan_varlen(seqlens: torch.Tensor, qlens: torch.Tensor, num_heads: int, num_kv_heads: int, max_pages: int,
+                num_workgroups: int, min_tiles_per_bin: int = 0, total_q: int | None = None,
+                task_map: torch.Tensor | None = None):
+    """Task map with query blocks for requests bringing qlens[b] new tokens each
+    (packed q rows in request order); total_q = sum(qlens) (read from the device
+    tensor when not given)."""
+    B = int(seqlens.numel())
+    assert qlens.numel() == B and seqlens.dtype == torch.int32 and qlens.dtype == torch.int32
+    assert seqlens.is_contiguous() and qlens.is_contiguous()
+    if total_q is None:
+        total_q = int(qlens.sum())
+    nbytes = varlen_task_map_bytes(B, num_kv_heads, num_workgroups, total_q)
+    if task_map is None:
+        task_map = torch.empty(nbytes, dtype=torch.uint8, device=seqlens.device)
+    _check("lbsa_plan_varlen", lib().lbsa_plan_varlen(
+        _ptr(seqlens), _ptr(qlens), B, num_heads, num_kv_heads, PAGE_SIZE, max_pages, total_q, num_workgroups,
+        min_tiles_per_bin, _ptr(task_map), task_map.numel() * task_map.element_size(), _stream(seqlens.device)))
+    return task_map
+
+
+def attend_varlen(q, k_cache, v_cache, page_table, task_map, num_workgroups: int, softmax_scale: float, B: int,
+                  workspace=None, out=None):
+    """Attention of packed queries q bf16 [total_q, Hq, D] on a map from plan_varlen;
+    returns bf16 [total_q, Hq, D]."""
+    assert q.dtype == torch.bfloat16 and k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16
+    for t in (q, k_cache, v_cache, page_table, task_map):
+        assert t.is_contiguous()
+    total_q, Hq, D = q.shape
+    num_pages, page, Hkv, D2 = k_cache.shape
+    assert page == PAGE_SIZE and D2 == D and tuple(v_cache.shape) == tuple(k_cache.shape)
+    assert page_table.dtype == torch.int32 and page_table.shape[0] == B
+    if workspace is None:
+        workspace = torch.empty(varlen_workspace_bytes(Hq, Hkv, num_workgroups), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, q)
+    _check("lbsa_attend_varlen", lib().lbsa_attend_varlen(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), B, Hq, Hkv, D, page, int(page_table.shape[1]),
+        int(num_pages), total_q, num_workgroups, float(softmax_scale), _ptr(task_map),
+        task_map.numel() * task_map.element_size(), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(out), _stream(q.device)))
+    return out
+
+
+def read_varlen_task_map(task_map: torch.Tensor, batch: int, num_kv_heads: int, P: int, total_q: int) -> dict:
+    """Copy a query-block task map to the host and split it into its arrays."""
+    lay = varlen_task_map_layout(batch, num_kv_heads, P, total_q)
+    raw = task_map.detach().cpu().numpy()[:lay["total"]]
+
+    def arr(off, n, shape=None):
+        a = raw[off:off + 4 * n].view(np.int32).copy()
+        return a if shape is None else a.reshape(shape)
+
+    header = arr(lay["header"], 16)
+    nq_max = batch + total_q // QBLOCK
+    cap = num_kv_heads * nq_max + P
+    NQ = int(header[14])
+    S = num_kv_heads * NQ
+    out = {"header": header, "bin_desc_begin": arr(lay["bin_desc_begin"], P + 1),
+           "desc_all": arr(lay["desc"], 8 * cap, (cap, 8)),
+           "seg_first_desc": arr(lay["seg_first_desc"], S), "seg_num_chunks": arr(lay["seg_num_chunks"], S),
+           "seg_slot0": arr(lay["seg_slot0"], S), "blk_req": arr(lay["blk_req"], NQ), "blk_k": arr(lay["blk_k"], NQ),
+           "qbase": arr(lay["qbase"], batch + 1), "qstart": arr(lay["qstart"], batch + 1),
+           "seqlens": arr(lay["seqlens"], batch), "qlens": arr(lay["qlens"], batch)}
+    for i, name in enumerate(HEADER_FIELDS):
+        out[name] = int(header[i])
+    out["NQ"], out["QB"] = NQ, int(header[15])
+    out["desc"] = out["desc_all"][:max(0, min(out["Ndesc"], cap))].copy()
     return out
 
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 204
+    assert lbsa.lib().lbsa_version() == 205
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -201,3 +201,53 @@ def test_timing_hook_arms_and_disarms_without_a_gpu():
     assert L.lbsa_time_next_kernels(2, None, arr) == lbsa.ERR_INVALID_ARGUMENT
     assert L.lbsa_time_next_kernels(2, arr, arr) == 0       # NULL events: armed, nothing stamped
     lbsa.time_next_kernels([])
+
+
+def test_varlen_map_layout_and_workspace():
+    """Query-block maps: 32-byte descriptors for Hkv * (B + total_q / 16) + P
+    slots, every array after the descriptors, and 2 P partial slots of 128 rows."""
+    for B, Hkv, P, tq in [(2, 1, 4, 21), (64, 8, 512, 8255), (1, 8, 512, 8192)]:
+        lay = lbsa.varlen_task_map_layout(B, Hkv, P, tq)
+        nq = B + tq // 16
+        S, cap = Hkv * nq, Hkv * nq + P
+        assert lay["header"] == 0 and lay["bin_desc_begin"] == 64
+        assert lay["desc"] % 32 == 0 and lay["desc"] >= 64 + 4 * (P + 1)
+        assert lay["seg_first_desc"] == lay["desc"] + 32 * cap
+        assert lay["seg_num_chunks"] == lay["seg_first_desc"] + 4 * S
+        assert lay["seg_slot0"] == lay["seg_num_chunks"] + 4 * S
+        assert lay["blk_req"] == lay["seg_slot0"] + 4 * S and lay["blk_k"] == lay["blk_req"] + 4 * nq
+        assert lay["qbase"] == lay["blk_k"] + 4 * nq and lay["qstart"] == lay["qbase"] + 4 * (B + 1)
+        assert lay["seqlens"] == lay["qstart"] + 4 * (B + 1) and lay["qlens"] == lay["seqlens"] + 4 * B
+        assert lay["total"] >= lay["qlens"] + 4 * B and lay["total"] % 256 == 0
+        assert lbsa.varlen_task_map_bytes(B, Hkv, P, tq) == lay["total"]
+    ws = lbsa.varlen_workspace_bytes(64, 8, 512)
+    assert ws >= 2 * 512 * 128 * (128 + 1) * 4 and ws < 2 * 512 * 128 * (128 + 1) * 4 + 512
+
+
+def test_varlen_host_argument_errors():
+    L = lbsa.lib()
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t()
+    assert L.lbsa_varlen_task_map_bytes(4, 1, 32, 3, ctypes.byref(sz)) == lbsa.ERR_INVALID_ARGUMENT   # total_q < B
+    assert L.lbsa_varlen_task_map_bytes(1, 8, 512, 1 << 20, ctypes.byref(sz)) == lbsa.ERR_UNSUPPORTED  # LDS
+    ok = dict(sl=vp(16), ql=vp(32), B=2, Hq=8, Hkv=1, page=64, mp=4, tq=21, P=4, F=0, map=vp(256), nb=1 << 20)
+
+    def plan(**kw):
+        a = dict(ok, **kw)
+        return L.lbsa_plan_varlen(a["sl"], a["ql"], a["B"], a["Hq"], a["Hkv"], a["page"], a["mp"], a["tq"], a["P"],
+                                  a["F"], a["map"], a["nb"], None)
+    assert plan(ql=None) == lbsa.ERR_INVALID_ARGUMENT
+    assert plan(nb=64) == lbsa.ERR_INVALID_ARGUMENT                 # map too small
+    assert plan(page=32) == lbsa.ERR_UNSUPPORTED
+    assert plan(map=vp(272)) == lbsa.ERR_INVALID_ARGUMENT           # 32-byte descriptors need 32-byte alignment
+
+    def attend(**kw):
+        a = dict(q=vp(256), k=vp(256), v=vp(256), pt=vp(256), B=2, Hq=8, Hkv=1, D=128, page=64, mp=4, np_=8, tq=21,
+                 P=4, sc=0.088, map=vp(256), mb=1 << 20, ws=vp(256), wb=1 << 30, out=vp(256))
+        a.update(kw)
+        return L.lbsa_attend_varlen(a["q"], a["k"], a["v"], a["pt"], a["B"], a["Hq"], a["Hkv"], a["D"], a["page"],
+                                    a["mp"], a["np_"], a["tq"], a["P"], a["sc"], a["map"], a["mb"], a["ws"], a["wb"],
+                                    a["out"], None)
+    assert attend(sc=0.0) == lbsa.ERR_INVALID_ARGUMENT
+    assert attend(wb=1024) == lbsa.ERR_INVALID_ARGUMENT              # workspace too small
+    assert attend(out=None) == lbsa.ERR_INVALID_ARGUMENT
+    assert attend(D=64) == lbsa.ERR_UNSUPPORTED
