@@ -440,6 +440,119 @@ def table4(args):
     print(json.dumps({"table4": rows, "unit": "us", "flush": args.flush}), flush=True)
 
 
+def _timed(run, steps, warmup, flush):
+    """Mean event time (us) of run() with one event pair per call, the flush outside."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        flush(i)
+        run()
+    torch.cuda.synchronize()
+    ev = _pairs(steps)
+    for i in range(steps):
+        flush(i)
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return summarize([1000.0 * a.elapsed_time(b) for a, b in ev])["mean"]
+
+
+def varlen_bench(args):
+    """Prefill / extend and decode rows on one task map (query-block segments)
+    against the grid path: lbsa_prefill for the requests with new tokens and the
+    decode task map for the decode rows.  Workloads: the mixed batch (one 8K
+    extend of an 8K context beside 63 decode rows, 64/8 heads) and a q8k prefill
+    alone.  Per path: the step (with its plans) and the layer (plans reused),
+    event pairs with the read flush before each; the map path's kernels also by
+    their own stamps."""
+    import torch
+
+    from load_balanced_split_assign_amd import lbsa
+    from load_balanced_split_assign_amd import workload as wl
+    flush = make_flush(args.flush)
+    rows = []
+    cases = {"mixed_extend": dict(wl.MIXED_EXTEND),
+             "q8k_prefill": dict(wl.MIXED_EXTEND, extend_len=8192, extend_q=8192, decode_rows=0)}
+    for name, cfg in cases.items():
+        sl, ql = wl.mixed_extend_lengths(**cfg)
+        b = wl.make_batch(seqlens=sl, qlens=ql, num_heads=64, num_kv_heads=8, kv_dtype="bf16", seed=cfg["seed"],
+                          tail="normal", device="cuda:0")
+        tq = int(sum(ql))
+        B, mp = b["B"], b["max_pages"]
+        P = args.workgroups or lbsa.varlen_default_workgroups(0)
+        tm = torch.empty(lbsa.varlen_task_map_bytes(B, 8, P, tq), dtype=torch.uint8, device="cuda:0")
+        ws = torch.empty(lbsa.varlen_workspace_bytes(64, 8, P), dtype=torch.uint8, device="cuda:0")
+        out = torch.empty_like(b["q"])
+
+        def vplan():
+            lbsa.plan_varlen(b["seqlens"], b["qlens"], 64, 8, mp, P, 0, total_q=tq, task_map=tm)
+
+        def vattend():
+            lbsa.attend_varlen(b["q"], b["k_cache"], b["v_cache"], b["page_table"], tm, P, b["softmax_scale"], B,
+                               workspace=ws, out=out)
+        vplan()
+        layer = _timed(vattend, args.steps, args.warmup, flush)
+        step = _timed(lambda: (vplan(), vattend()), args.steps, args.warmup, flush)
+        kev = [_pairs(2) for _ in range(args.steps)]
+        for e in kev:
+            for x, y in e:
+                x.record(); y.record()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            flush(i)
+            lbsa.time_next_kernels(kev[i])
+            vattend()
+        torch.cuda.synchronize()
+        split_k = statistics.fmean(1000.0 * e[0][0].elapsed_time(e[0][1]) for e in kev)
+        comb_k = statistics.fmean(1000.0 * e[1][0].elapsed_time(e[1][1]) for e in kev)
+        m = lbsa.read_varlen_task_map(tm, B, 8, P, tq)
+
+        # the grid path: lbsa_prefill for the request with new tokens, the decode map for the rest
+        eq = ql[0]
+        ext_q = b["q"][:eq].reshape(1, eq, 64, 128)
+        ext_out = torch.empty_like(ext_q)
+        ext_pt = b["page_table"][:1].contiguous()
+        ext_sl = b["seqlens"][:1].contiguous()
+        nd = B - 1
+        if nd:
+            dec = {"q": b["q"][eq:].contiguous(), "k_cache": b["k_cache"], "v_cache": b["v_cache"],
+                   "k_scale": None, "v_scale": None, "q_scale": None, "page_table": b["page_table"][1:].contiguous(),
+                   "seqlens": b["seqlens"][1:].contiguous(), "num_heads": 64, "num_kv_heads": 8, "B": nd,
+                   "max_pages": mp, "softmax_scale": b["softmax_scale"], "q_len": 1}
+            dpath = Path(dec, lbsa.default_workgroups(0, "bf16"))
+            dpath.assign()
+
+        def grid_layer():
+            lbsa.prefill(ext_q, b["k_cache"], b["v_cache"], ext_pt, ext_sl, b["softmax_scale"], out=ext_out)
+            if nd:
+                dpath.layer()
+
+        def grid_step():
+            if nd:
+                dpath.assign()
+            grid_layer()
+        g_layer = _timed(grid_layer, args.steps, args.warmup, flush)
+        g_step = _timed(grid_step, args.steps, args.warmup, flush)
+        flops = causal_flops(1, eq, sl[0], 64) + sum(4 * 64 * 128 * L for L in sl[1:])
+        rows.append({"workload": name, "batch": B, "total_q": tq, "extend": {"L": sl[0], "q": eq},
+                     "decode_rows": nd, "P": P, "T": m["T"], "K": m["K"], "Ndesc": m["Ndesc"],
+                     "cut_segments": int((m["seg_num_chunks"] > 1).sum()), "flops": flops,
+                     "map_layer_us": round(layer, 2), "map_step_us": round(step, 2),
+                     "map_split_kernel_us": round(split_k, 2), "map_combine_kernel_us": round(comb_k, 2),
+                     "grid_layer_us": round(g_layer, 2), "grid_step_us": round(g_step, 2),
+                     "map_layer_TFLOPs": round(flops / layer / 1e6, 1),
+                     "map_layer_pct_of_mfma_peak": round(100 * flops / layer / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
+                     "grid_layer_TFLOPs": round(flops / g_layer / 1e6, 1),
+                     "speedup_map_vs_grid_layer": round(g_layer / layer, 3),
+                     "speedup_map_vs_grid_step": round(g_step / step, 3)})
+        del b, tm, ws, out
+        if nd:
+            del dpath, dec
+        torch.cuda.empty_cache()
+    print(json.dumps({"varlen": rows, "unit": "us", "flush": args.flush}), flush=True)
+
+
 ROUTER_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
 
 
@@ -755,6 +868,8 @@ def main():
                     help="instead of the headline line: the fused QK-Norm/RoPE/KV-write prologue")
     ap.add_argument("--graph", action="store_true",
                     help="eager launches against one HIP graph of assign + split + combine (step times)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="instead of the headline line: prefill / extend / decode rows on one task map vs the grid")
     ap.add_argument("--table3", action="store_true",
                     help="instead of the headline line: the six fp8 KV-length mixes, dynamic vs static")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -784,6 +899,9 @@ def main():
 
     if args.table3:
         table3(args)
+        return
+    if args.varlen:
+        varlen_bench(args)
         return
     if args.prologue:
         prologue_bench(args)

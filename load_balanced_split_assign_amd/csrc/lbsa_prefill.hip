@@ -108,7 +108,7 @@ struct QBlockState {
 
 template <int CB>
 __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock& a, lds_char* ring, int t0, int t1,
-                                                                    QBlockState<CB>& st) {
+                                                                    QBlockState<CB>& st, int first_page = -1) {
     constexpr int kPosWave = 2 * CB;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
@@ -166,8 +166,7 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
         dead_off[s] = 16u * (uint32_t)(lane & 15);    // row 0 of the page: always live
     }
     const auto* pt = uniform_ptr<int32_t>(a.pt);
-    auto issue = [&](int t, lds_char* stg) {
-        int64_t page = pt[t];
+    auto issue_page = [&](int64_t page, int t, lds_char* stg) {
         if (page < 0 || page >= a.num_pages) {
             st.bad = true;
             page = 0;
@@ -184,7 +183,10 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
             dma16(vb + (live ? live_off_v[s] : dead_off[s]), stg + kPfHalf + w * kPfSlice + 1024 * s);
         }
     };
-    for (int u = 0; u < kPfStages - 1; ++u) issue(min(t0 + u, t1 - 1), ring + u * kPfStageBytes);
+    auto issue = [&](int t, lds_char* stg) { issue_page(pt[t], t, stg); };
+    static_assert(kPfStages == 2, "one tile issued ahead");
+    // the first tile, with its page id from the caller when it has one
+    issue_page(first_page >= 0 ? (int64_t)first_page : (int64_t)pt[t0], t0, ring);
 
     // lane parts of the ring read addresses (stage 0, first 16 rows); the
     // stage and the 16-row sub-tile are the reads' immediate offsets
@@ -413,7 +415,12 @@ __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8
     constexpr int CB = 2, kPosWave = 2 * CB;
     static_assert(kWaves * kPosWave == kQBlock, "one workgroup holds one query block");
     const VarlenMapLayout ML = varlen_map_layout(B, Hkv, P, nq_max);
-    const int j = blockIdx.x;
+    // Consecutive bins hold consecutive query blocks of one (request, KV head),
+    // which re-read the same K/V: they go to workgroups of one XCD (workgroups
+    // are dispatched to the 8 XCDs in turn), so that K/V stays in that XCD's L2.
+    // Bin j runs on workgroup (j mod P/8) * 8 + j / (P/8) when 8 divides P.
+    const int w_id = blockIdx.x;
+    const int j = P % 8 == 0 ? (w_id % 8) * (P / 8) + w_id / 8 : w_id;
     const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
     const auto* bdb = uniform_ptr<int32_t>(map + ML.bin_desc_begin);
     const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
@@ -422,15 +429,38 @@ __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8
     if (h_err != 0 || h_p != P || h_b != B || h_hkv != Hkv || d0 < 0 || d1 < d0 || d1 > cap) return;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
+    const auto* descs = uniform_ptr<int32_t>(map + ML.desc);
+    const auto* ptab = uniform_ptr<int32_t>(a.page_table);
+    // A descriptor switch costs one round trip, not three: the record of the
+    // next descriptor is loaded while this one computes, and the page id of its
+    // first tile before this one's epilogue (both used in the next iteration, so
+    // the loads are not moved down to their use).
+    auto record = [&](int d, int (&x)[kVarlenDescWords]) {
+#pragma unroll
+        for (int i = 0; i < kVarlenDescWords; ++i) x[i] = descs[(size_t)kVarlenDescWords * d + i];
+    };
+    auto first_page_of = [&](const int (&x)[kVarlenDescWords]) {
+        const int b = min(max(x[VD_B], 0), B - 1), t = min(max(x[VD_T0], 0), a.max_pages - 1);
+        return (int)ptab[(size_t)b * a.max_pages + t];           // clamped: checked with the record below
+    };
+    int cur[kVarlenDescWords];
+    record(d0 < d1 ? d0 : 0, cur);
+    int cur_page = first_page_of(cur);
     for (int d = d0; d < d1; ++d) {
-        const auto* rec = uniform_ptr<int32_t>(map + ML.desc) + (size_t)kVarlenDescWords * d;
-        const int h = rec[VD_H], b = rec[VD_B], k = rec[VD_K], t0 = rec[VD_T0], t1 = rec[VD_T1];
-        const int L = rec[VD_L], q = rec[VD_Q], qs = rec[VD_QS];
+        int nx[kVarlenDescWords];
+        record(d + 1 < d1 ? d + 1 : d, nx);
+        const int h = cur[VD_H], b = cur[VD_B], k = cur[VD_K], t0 = cur[VD_T0], t1 = cur[VD_T1];
+        const int L = cur[VD_L], q = cur[VD_Q], qs = cur[VD_QS];
+        const int page0 = cur_page;
+#pragma unroll
+        for (int i = 0; i < kVarlenDescWords; ++i) cur[i] = nx[i];
         // a record this map cannot hold (corrupt map): skipped, nothing read out of bounds
         if (h < 0 || h >= Hkv || b < 0 || b >= B || L < 0 || L > a.max_pages * kTile || q < 1 || q > L ||
             k < 0 || kQBlock * k >= q || qs < 0 || qs > a.total_q - q || t0 < 0 || t1 <= t0 ||
-            t1 > varlen_extent(L, q, k))
+            t1 > varlen_extent(L, q, k)) {
+            cur_page = first_page_of(cur);
             continue;
+        }
         QBlock blk;
         blk.q0 = a.q + (size_t)(qs + kQBlock * k) * a.Hq * kHeadDim;
         blk.k_cache = a.k_cache;
@@ -446,7 +476,8 @@ __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8
         blk.scale_log2 = a.scale_log2;
         QBlockState<CB> st;
         st.bad = false;
-        attend_qblock<CB>(blk, ring, t0, t1, st);
+        attend_qblock<CB>(blk, ring, t0, t1, st, page0);
+        cur_page = first_page_of(cur);
         const bool whole = t0 == 0 && t1 == varlen_extent(L, q, k);
         const int slot = 2 * j + (d == d0 ? 0 : 1);
 #pragma unroll
