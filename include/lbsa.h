@@ -323,28 +323,36 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
  *                  bytes: header (words as lbsa_plan's, plus 14 = query blocks
  *                  per KV head NQ, 15 = LBSA_QBLOCK), bin CSR, 32-byte
  *                  descriptors (kv_head, request, block, tile_begin, tile_end,
- *                  L, q, first packed row), per segment s = h * NQ + block (of
- *                  all requests in order) its first descriptor, chunk count and
- *                  first partial slot, per block its request and index, the
- *                  prefixes of blocks and of qlens, and the two length copies
+ *                  L, q, first packed row), per descriptor its partial slot,
+ *                  the claim order (per group of bins, requests in walk order,
+ *                  each from its last descriptor back), per segment
+ *                  s = h * NQ + block (of all requests in order)
+ *                  its first descriptor, chunk count and first partial slot,
+ *                  per block its request and index, the prefixes of blocks and
+ *                  of qlens, and the two length copies
  *                  (lbsa_varlen_task_map_layout_get)
  *   workspace      lbsa_varlen_workspace_bytes(num_heads, num_kv_heads, 128, P):
+ *                  256 bytes of claim counters (cleared by every call), then
  *                  2 P partial slots of 16 x 8 rows (position x head), fp32 LSE
  *                  [2 P][128] then O [2 P][128][128]; only a bin's first and last
  *                  descriptors can cut a segment, so slot 2 j + (0 first, 1 last)
- * lbsa_attend_varlen is two launches: a persistent workgroup per bin computes
- * each descriptor's query block over its tiles (MFMA, K/V through LDS), writing
- * the bf16 rows of a segment it holds whole and a partial otherwise; then one
- * workgroup per (KV head, block) merges the chunks of the cut segments.
+ * lbsa_attend_varlen is three launches on the stream: a one-workgroup kernel
+ * clears the claim counters; persistent workgroups (as many as stay resident)
+ * claim the descriptors of 8 groups of consecutive bins, one group per XCD,
+ * in the map's claim order, and compute each descriptor's
+ * query block over its tiles (MFMA, K/V through LDS), writing the bf16 rows of
+ * a segment it holds whole and a partial otherwise; then one workgroup per
+ * (KV head, block) merges the chunks of the cut segments.  Calls that share a
+ * workspace must not overlap.
  * Errors: shapes as lbsa_plan and lbsa_prefill (bf16 only); maps larger than
  * one assign workgroup's LDS (about 16K segments) give LBSA_ERR_UNSUPPORTED.
  * A length or q out of range on the device sets the error word: every output
- * row is then NaN.  Default P: lbsa_varlen_default_workgroups.
+ * row is then NaN.  Default P (bins): lbsa_varlen_default_workgroups.
  */
 #define LBSA_QBLOCK 16
 typedef struct {
-    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seg_slot0, blk_req, blk_k, qbase,
-        qstart, seqlens, qlens, total;
+    size_t header, bin_desc_begin, desc, desc_slot, claim_order, seg_first_desc, seg_num_chunks, seg_slot0,
+        blk_req, blk_k, qbase, qstart, seqlens, qlens, total;
 } lbsa_varlen_task_map_layout;
 int lbsa_varlen_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32_t P, int64_t total_q,
                                     lbsa_varlen_task_map_layout* out);

@@ -4,6 +4,7 @@
 #include <limits.h>
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "lbsa_internal.h"
@@ -104,7 +105,7 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 205; }
+LBSA_API int lbsa_version(void) { return 206; }
 
 namespace {
 // Events armed for the next launches on this host thread, used in order.
@@ -491,6 +492,8 @@ LBSA_API int lbsa_varlen_task_map_layout_get(int32_t batch, int32_t num_kv_heads
     out->header = m.header;
     out->bin_desc_begin = m.bin_desc_begin;
     out->desc = m.desc;
+    out->desc_slot = m.desc_slot;
+    out->claim_order = m.claim_order;
     out->seg_first_desc = m.seg_first_desc;
     out->seg_num_chunks = m.seg_num_chunks;
     out->seg_slot0 = m.seg_slot0;
@@ -518,7 +521,28 @@ LBSA_API int lbsa_varlen_workspace_bytes(int32_t num_heads, int32_t num_kv_heads
     if (!out_bytes || P <= 0) return LBSA_ERR_INVALID_ARGUMENT;
     const int s = check_shape(1, num_heads, num_kv_heads, head_dim, kTile);
     if (s != LBSA_OK) return s;
-    *out_bytes = align_up(2 * (size_t)P * kVarlenSlotBytesLse, 256) + 2 * (size_t)P * kVarlenSlotBytesO;
+    *out_bytes = kVarlenCounterBytes + align_up(2 * (size_t)P * kVarlenSlotBytesLse, 256) +
+                 2 * (size_t)P * kVarlenSlotBytesO;
+    return LBSA_OK;
+}
+
+// Workgroups the varlen split kernel keeps resident on a device (its
+// occupancy times the compute units), cached per device.
+static int varlen_resident_workgroups(int device, int* out) {
+    static std::atomic<int> cached[64];
+    if (device >= 0 && device < 64) {
+        const int c = cached[device].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return LBSA_OK;
+        }
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return LBSA_ERR_HIP;
+    if (varlen_occupancy(&per_cu) != hipSuccess || per_cu <= 0 || cus <= 0) return LBSA_ERR_HIP;
+    *out = cus * per_cu;
+    if (device >= 0 && device < 64) cached[device].store(*out, std::memory_order_relaxed);
     return LBSA_OK;
 }
 
@@ -581,13 +605,23 @@ LBSA_API int lbsa_attend_varlen(const void* q_d, const void* k_cache_d, const vo
     s = lbsa_varlen_workspace_bytes(num_heads, num_kv_heads, head_dim, num_workgroups, &ws_need);
     if (s != LBSA_OK) return s;
     if (task_map_bytes < map_need || workspace_bytes < ws_need) return LBSA_ERR_INVALID_ARGUMENT;
-    float* part_lse = static_cast<float*>(workspace_d);
-    float* part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace_d) +
+    int device = 0, resident = 0;
+    if (hipGetDevice(&device) != hipSuccess) return LBSA_ERR_HIP;
+    s = varlen_resident_workgroups(device, &resident);
+    if (s != LBSA_OK) return s;
+    // no more workgroups than the map can hold descriptors
+    const int64_t nq = varlen_max_blocks(batch, total_q);
+    const int64_t cap = (int64_t)num_kv_heads * nq + num_workgroups;
+    const int workgroups = (int)(cap < resident ? cap : resident);
+    uint8_t* ws = static_cast<uint8_t*>(workspace_d);
+    int32_t* counters = reinterpret_cast<int32_t*>(ws);
+    float* part_lse = reinterpret_cast<float*>(ws + kVarlenCounterBytes);
+    float* part_o = reinterpret_cast<float*>(ws + kVarlenCounterBytes +
                                              align_up(2 * (size_t)num_workgroups * kVarlenSlotBytesLse, 256));
     return hip_status(launch_varlen(q_d, k_cache_d, v_cache_d, page_table_d, task_map_d, batch, num_heads,
-                                    num_kv_heads, num_workgroups, varlen_max_blocks(batch, total_q),
-                                    max_pages_per_seq, num_pages > INT32_MAX ? INT32_MAX : num_pages, total_q,
-                                    softmax_scale * kLog2eHost, part_lse, part_o, out_d,
+                                    num_kv_heads, num_workgroups, nq, max_pages_per_seq,
+                                    num_pages > INT32_MAX ? INT32_MAX : num_pages, total_q,
+                                    softmax_scale * kLog2eHost, counters, part_lse, part_o, out_d, workgroups,
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -253,6 +253,8 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
     int32_t* hdr = reinterpret_cast<int32_t*>(map + L.header);
     int32_t* bdb = reinterpret_cast<int32_t*>(map + L.bin_desc_begin);
     int32_t* desc = reinterpret_cast<int32_t*>(map + L.desc);
+    int32_t* dslot = reinterpret_cast<int32_t*>(map + L.desc_slot);
+    int32_t* order = reinterpret_cast<int32_t*>(map + L.claim_order);
     int32_t* sfd_g = reinterpret_cast<int32_t*>(map + L.seg_first_desc);
     int32_t* snc_g = reinterpret_cast<int32_t*>(map + L.seg_num_chunks);
     int32_t* slot0_g = reinterpret_cast<int32_t*>(map + L.seg_slot0);
@@ -386,6 +388,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
                 int32_t* rec = desc + (size_t)kVarlenDescWords * d;
                 *reinterpret_cast<int4*>(rec) = make_int4(h, b, u - qbase[b], x - a);
                 *reinterpret_cast<int4*>(rec + 4) = make_int4(t1 - a, lens[b], qls[b], qstart[b]);
+                dslot[d] = 2 * j + (d != v ? 1 : 0);
                 if (t1 >= xe) break;
                 x = t1;                                       // blocks are never empty: the next one
                 if (++u == NQ) { u = 0; ++h; }
@@ -393,6 +396,22 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
             }
         }
         bdb[j] = v;
+    }
+    __syncthreads();   // records and bin starts written by this workgroup
+
+    // ---- claim order: in each group of bins, the requests in walk order and
+    // each request's descriptors from the last back (its query blocks with the
+    // most tiles first); a request's descriptors for one KV head are
+    // contiguous in the walk, [first of its first block, first of the next)
+    for (int d = tid; d < ndesc; d += kAssignThreads) {
+        const int32_t* rec = desc + (size_t)kVarlenDescWords * d;
+        const int h = rec[VD_H], b = rec[VD_B], j = dslot[d] >> 1;
+        int x = 0;
+        while (x + 1 < kVarlenGroups && (int)((int64_t)(x + 1) * P / kVarlenGroups) <= j) ++x;
+        const int lo = bdb[(int)((int64_t)x * P / kVarlenGroups)];
+        const int hi = bdb[(int)((int64_t)(x + 1) * P / kVarlenGroups)];
+        const int r_lo = max(lo, sfd[h * NQ + qbase[b]]), r_hi = min(hi, sfd[h * NQ + qbase[b + 1]]);
+        order[r_lo + r_hi - 1 - d] = d;
     }
 
     if (tid == 0) {

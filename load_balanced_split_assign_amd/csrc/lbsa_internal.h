@@ -84,10 +84,16 @@ constexpr int kVarlenRows = kQBlock * kGroup;   // partial rows per slot: positi
 __host__ __device__ inline int64_t varlen_max_blocks(int B, int64_t total_q) { return B + total_q / kQBlock; }
 
 // Byte offsets of a prefill / extend task map for B requests, Hkv KV heads, P
-// bins and at most NQ query blocks per KV head.
+// bins and at most NQ query blocks per KV head.  desc_slot[d] is the partial
+// slot of descriptor d: 2 j for the first descriptor of bin j, 2 j + 1 for
+// the others (only a bin's first and last descriptors can be cut).
+// claim_order lists the descriptors of each group of bins (kVarlenGroups
+// groups of consecutive bins, group x = bins [x P / 8, (x + 1) P / 8)) in the
+// order the split kernel's workgroups claim them: the group's requests in walk
+// order, each request's descriptors from its last back.
 struct VarlenMapLayout {
-    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seg_slot0, blk_req, blk_k, qbase,
-        qstart, seqlens, qlens, total;
+    size_t header, bin_desc_begin, desc, desc_slot, claim_order, seg_first_desc, seg_num_chunks, seg_slot0,
+        blk_req, blk_k, qbase, qstart, seqlens, qlens, total;
 };
 
 __host__ __device__ inline VarlenMapLayout varlen_map_layout(int B, int Hkv, int P, int64_t NQ) {
@@ -97,7 +103,9 @@ __host__ __device__ inline VarlenMapLayout varlen_map_layout(int B, int Hkv, int
     m.header = 0;
     m.bin_desc_begin = 64;
     m.desc = align_up(m.bin_desc_begin + 4 * ((size_t)P + 1), 32);
-    m.seg_first_desc = m.desc + 4 * kVarlenDescWords * cap;
+    m.desc_slot = m.desc + 4 * kVarlenDescWords * cap;
+    m.claim_order = m.desc_slot + 4 * cap;
+    m.seg_first_desc = m.claim_order + 4 * cap;
     m.seg_num_chunks = m.seg_first_desc + 4 * S;
     m.seg_slot0 = m.seg_num_chunks + 4 * S;
     m.blk_req = m.seg_slot0 + 4 * S;
@@ -109,6 +117,12 @@ __host__ __device__ inline VarlenMapLayout varlen_map_layout(int B, int Hkv, int
     m.total = align_up(m.qlens + 4 * (size_t)B, 256);
     return m;
 }
+
+// The varlen workspace starts with the claim counters of the split kernel's
+// workgroups, one per group of bins (a group per XCD), cleared before every
+// launch; the partial slots follow.
+constexpr int kVarlenGroups = 8;
+constexpr size_t kVarlenCounterBytes = 256;
 
 // LDS words the varlen assign kernel needs: lengths, q lengths, their two
 // prefixes, the tile prefix over query blocks and the chunk prefix over
@@ -168,8 +182,8 @@ hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t strea
 hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu);
 hipError_t launch_varlen(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                          const void* map, int B, int Hq, int Hkv, int P, int64_t nq_max, int max_pages,
-                         int64_t num_pages, int64_t total_q, float scale_log2, float* part_lse, float* part_o,
-                         void* out, hipStream_t stream);
+                         int64_t num_pages, int64_t total_q, float scale_log2, int32_t* counters, float* part_lse,
+                         float* part_o, void* out, int workgroups, hipStream_t stream);
 hipError_t varlen_occupancy(int* blocks_per_cu);
 hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                           const int32_t* seqlens, int B, int QL, int Hq, int Hkv, int max_pages,

@@ -377,20 +377,33 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill / extend on the task map.  Persistent workgroup j drains bin j of a
-// map built with query blocks (lbsa_plan_varlen): each descriptor is one query
-// block of one (request, KV head) over a range of its KV tiles, computed by the
-// same block loop as the grid kernel above.  A descriptor that covers its whole
-// segment writes the bf16 output rows of its block; a cut one -- only a bin's
-// first or last descriptor can be cut -- writes its partial (normalised O,
-// natural-log LSE) to slot 2 j (first) or 2 j + 1 (last), and
+// Prefill / extend on the task map.  A map built with query blocks
+// (lbsa_plan_varlen) holds descriptors: one query block of one (request, KV
+// head) over a range of its KV tiles, each computed by the same block loop as
+// the grid kernel above.  A descriptor that covers its whole segment writes the
+// bf16 output rows of its block; a cut one -- only a bin's first or last
+// descriptor can be cut -- writes its partial (normalised O, natural-log LSE)
+// to the slot the map gives it (2 j first, 2 j + 1 last, for bin j), and
 // varlen_combine_kernel merges the chunks of each cut segment.
+//
+// Execution order on gfx950.  The bins fix where segments are cut; the
+// persistent workgroups then claim the descriptors one at a time.  A
+// workgroup per bin would leave the last-dispatched of the two workgroups of a
+// compute unit behind (the older one wins issue arbitration), and its bin
+// would end last, alone on the unit.  The P bins form 8 groups of consecutive
+// bins, group x for the workgroups of XCD x (workgroups are dispatched to the
+// 8 XCDs in turn), so the K/V of a group's query blocks stays in one L2; a
+// workgroup claims its group's descriptors in the map's claim order (each
+// request's query blocks with the most tiles first, as the grid kernel orders
+// them: workgroups that claim together stream the same tiles together, and
+// the last claims are short), then helps the other groups.
 // ---------------------------------------------------------------------------
 struct VarlenArgs {
     const uint16_t* q;           // packed [total_q][Hq][128]
     const uint16_t* k_cache;
     const uint16_t* v_cache;
     const int32_t* page_table;   // [B][max_pages]
+    int32_t* counters;           // [kVarlenGroups] claim counters, zero at launch
     float* part_lse;             // [2 P][128]: row p * 8 + g of a slot
     float* part_o;               // [2 P][128][128]
     uint16_t* out;               // packed like q
@@ -408,105 +421,121 @@ __device__ inline int varlen_extent(int L, int q, int k) {   // tiles the block'
     return (L - q + min(q, kQBlock * (k + 1)) + kTile - 1) / kTile;
 }
 
+// The claim counters of one launch start at zero (a fill kernel, not a
+// memset, so the launches can be captured in a graph).
+__global__ void varlen_reset_kernel(int32_t* counters) {
+    if (threadIdx.x < kVarlenGroups) counters[threadIdx.x] = 0;
+}
+
 __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8_t* map, int B, int Hkv, int P,
                                                                      int nq_max, VarlenArgs a) {
     __shared__ __attribute__((aligned(16))) char ring_mem[kPfStages * kPfStageBytes];
+    __shared__ int claim_lds;
     lds_char* const ring = (lds_char*)ring_mem;
     constexpr int CB = 2, kPosWave = 2 * CB;
     static_assert(kWaves * kPosWave == kQBlock, "one workgroup holds one query block");
     const VarlenMapLayout ML = varlen_map_layout(B, Hkv, P, nq_max);
-    // Consecutive bins hold consecutive query blocks of one (request, KV head),
-    // which re-read the same K/V: they go to workgroups of one XCD (workgroups
-    // are dispatched to the 8 XCDs in turn), so that K/V stays in that XCD's L2.
-    // Bin j runs on workgroup (j mod P/8) * 8 + j / (P/8) when 8 divides P.
-    const int w_id = blockIdx.x;
-    const int j = P % 8 == 0 ? (w_id % 8) * (P / 8) + w_id / 8 : w_id;
     const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
     const auto* bdb = uniform_ptr<int32_t>(map + ML.bin_desc_begin);
     const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
-    const int d0 = bdb[j], d1 = bdb[j + 1];
+    const int ndesc = hdr[LBSA_HDR_NDESC];
     const int cap = Hkv * nq_max + P;
-    if (h_err != 0 || h_p != P || h_b != B || h_hkv != Hkv || d0 < 0 || d1 < d0 || d1 > cap) return;
+    if (h_err != 0 || h_p != P || h_b != B || h_hkv != Hkv || ndesc < 0 || ndesc > cap) return;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const auto* descs = uniform_ptr<int32_t>(map + ML.desc);
+    const auto* dslot = uniform_ptr<int32_t>(map + ML.desc_slot);
+    const auto* order = uniform_ptr<int32_t>(map + ML.claim_order);
     const auto* ptab = uniform_ptr<int32_t>(a.page_table);
-    // A descriptor switch costs one round trip, not three: the record of the
-    // next descriptor is loaded while this one computes, and the page id of its
-    // first tile before this one's epilogue (both used in the next iteration, so
-    // the loads are not moved down to their use).
-    auto record = [&](int d, int (&x)[kVarlenDescWords]) {
+
+    // ---- claims: group gx's descriptors are [lo, hi), claim i takes order[lo + i]
+    int gx = (int)(blockIdx.x % kVarlenGroups), tried = 0, lo = 0, hi = 0;
+    auto group_bounds = [&]() {
+        const int l = bdb[(int)((int64_t)gx * P / kVarlenGroups)];
+        const int e = bdb[(int)((int64_t)(gx + 1) * P / kVarlenGroups)];
+        const bool ok = 0 <= l && l <= e && e <= ndesc;              // a corrupt map: the group is skipped
+        lo = ok ? l : 0;
+        hi = ok ? e : 0;
+    };
+    // thread 0 adds to the counter; the value reaches the other waves through LDS
+    auto claim_issue = [&]() { return threadIdx.x == 0 ? atomicAdd(a.counters + gx, 1) : 0; };
+    // the descriptor of claim v (thread 0's), or of the next claims once this
+    // group is drained; -1 when every group is
+    auto claim_take = [&](int v) {
+        while (true) {
+            if (threadIdx.x == 0) claim_lds = v;
+            lds_barrier();
+            const int i = __builtin_amdgcn_readfirstlane(claim_lds);
+            lds_barrier();                                              // read before thread 0 writes again
+            if (i < hi - lo) {
+                const int d = order[lo + i];
+                return d >= lo && d < hi ? d : hi - 1 - i;    // a corrupt order: the index itself
+            }
+            if (++tried == kVarlenGroups) return -1;
+            gx = gx + 1 == kVarlenGroups ? 0 : gx + 1;
+            group_bounds();
+            v = claim_issue();
+        }
+    };
+    group_bounds();
+    int d = claim_take(claim_issue());
+    while (d >= 0) {
+        // the next claim is in flight while this descriptor computes
+        const int v_next = claim_issue();
+        int x[kVarlenDescWords];
 #pragma unroll
         for (int i = 0; i < kVarlenDescWords; ++i) x[i] = descs[(size_t)kVarlenDescWords * d + i];
-    };
-    auto first_page_of = [&](const int (&x)[kVarlenDescWords]) {
-        const int b = min(max(x[VD_B], 0), B - 1), t = min(max(x[VD_T0], 0), a.max_pages - 1);
-        return (int)ptab[(size_t)b * a.max_pages + t];           // clamped: checked with the record below
-    };
-    int cur[kVarlenDescWords];
-    record(d0 < d1 ? d0 : 0, cur);
-    int cur_page = first_page_of(cur);
-    for (int d = d0; d < d1; ++d) {
-        int nx[kVarlenDescWords];
-        record(d + 1 < d1 ? d + 1 : d, nx);
-        const int h = cur[VD_H], b = cur[VD_B], k = cur[VD_K], t0 = cur[VD_T0], t1 = cur[VD_T1];
-        const int L = cur[VD_L], q = cur[VD_Q], qs = cur[VD_QS];
-        const int page0 = cur_page;
-#pragma unroll
-        for (int i = 0; i < kVarlenDescWords; ++i) cur[i] = nx[i];
+        const int slot = dslot[d];
+        const int h = x[VD_H], b = x[VD_B], k = x[VD_K], t0 = x[VD_T0], t1 = x[VD_T1];
+        const int L = x[VD_L], q = x[VD_Q], qs = x[VD_QS];
         // a record this map cannot hold (corrupt map): skipped, nothing read out of bounds
-        if (h < 0 || h >= Hkv || b < 0 || b >= B || L < 0 || L > a.max_pages * kTile || q < 1 || q > L ||
-            k < 0 || kQBlock * k >= q || qs < 0 || qs > a.total_q - q || t0 < 0 || t1 <= t0 ||
-            t1 > varlen_extent(L, q, k)) {
-            cur_page = first_page_of(cur);
-            continue;
-        }
-        QBlock blk;
-        blk.q0 = a.q + (size_t)(qs + kQBlock * k) * a.Hq * kHeadDim;
-        blk.k_cache = a.k_cache;
-        blk.v_cache = a.v_cache;
-        blk.pt = a.page_table + (size_t)b * a.max_pages;
-        blk.num_pages = a.num_pages;
-        blk.Hq = a.Hq;
-        blk.Hkv = Hkv;
-        blk.h = h;
-        blk.L = L;
-        blk.live = min(kQBlock, q - kQBlock * k);
-        blk.off = L - q + kQBlock * k;
-        blk.scale_log2 = a.scale_log2;
-        QBlockState<CB> st;
-        st.bad = false;
-        attend_qblock<CB>(blk, ring, t0, t1, st, page0);
-        cur_page = first_page_of(cur);
-        const bool whole = t0 == 0 && t1 == varlen_extent(L, q, k);
-        const int slot = 2 * j + (d == d0 ? 0 : 1);
+        const bool rec_ok = h >= 0 && h < Hkv && b >= 0 && b < B && L >= 0 && L <= a.max_pages * kTile && q >= 1 &&
+                            q <= L && k >= 0 && kQBlock * k < q && qs >= 0 && qs <= a.total_q - q && t0 >= 0 &&
+                            t1 > t0 && t1 <= varlen_extent(L, q, k);
+        const bool whole = rec_ok && t0 == 0 && t1 == varlen_extent(L, q, k);
+        if (rec_ok && (whole || (slot >= 0 && slot < 2 * P))) {
+            QBlock blk;
+            blk.q0 = a.q + (size_t)(qs + kQBlock * k) * a.Hq * kHeadDim;
+            blk.k_cache = a.k_cache;
+            blk.v_cache = a.v_cache;
+            blk.pt = a.page_table + (size_t)b * a.max_pages;
+            blk.num_pages = a.num_pages;
+            blk.Hq = a.Hq;
+            blk.Hkv = Hkv;
+            blk.h = h;
+            blk.L = L;
+            blk.live = min(kQBlock, q - kQBlock * k);
+            blk.off = L - q + kQBlock * k;
+            blk.scale_log2 = a.scale_log2;
+            QBlockState<CB> st;
+            st.bad = false;
+            attend_qblock<CB>(blk, ring, t0, t1, st, ptab[(size_t)b * a.max_pages + t0]);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int p = w * kPosWave + 2 * cb + (r >> 3), gg = r & 7;
-            if (p >= blk.live) continue;
-            const float lt = st.l[cb][0];
-            float inv = lt > 0.f ? 1.f / lt : 0.f;        // a query that sees none of these tokens: O = 0
-            if (st.bad) inv = __builtin_nanf("");
-            if (whole) {
-                uint16_t* o = a.out + ((size_t)(qs + kQBlock * k + p) * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + 4 * g;
+            for (int cb = 0; cb < CB; ++cb) {
+                const int p = w * kPosWave + 2 * cb + (r >> 3), gg = r & 7;
+                if (p >= blk.live) continue;
+                const float lt = st.l[cb][0];
+                float inv = lt > 0.f ? 1.f / lt : 0.f;        // a query that sees none of these tokens: O = 0
+                if (st.bad) inv = __builtin_nanf("");
+                if (whole) {
+                    uint16_t* o =
+                        a.out + ((size_t)(qs + kQBlock * k + p) * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + 4 * g;
 #pragma unroll
-                for (int db = 0; db < 8; ++db) {
-                    const f32x4 v = st.acc[cb][db] * inv;
-                    *reinterpret_cast<uint2*>(o + 16 * db) = make_uint2(bf16x2_pack(v[0], v[1]), bf16x2_pack(v[2], v[3]));
-                }
-            } else {
-                const size_t row = (size_t)slot * kVarlenRows + p * kGroup + gg;
-                float* o = a.part_o + row * kHeadDim + 4 * g;
+                    for (int db = 0; db < 8; ++db) store_bf16x4(o + 16 * db, st.acc[cb][db] * inv);
+                } else {
+                    const size_t row = (size_t)slot * kVarlenRows + p * kGroup + gg;
+                    float* o = a.part_o + row * kHeadDim + 4 * g;
 #pragma unroll
-                for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[cb][db] * inv;
-                if (g == 0) {
-                    float lse = lt > 0.f ? (st.m[cb] + __builtin_log2f(lt)) * kLn2 : kNegInf;
-                    if (st.bad) lse = __builtin_nanf("");
-                    a.part_lse[row] = lse;
+                    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[cb][db] * inv;
+                    if (g == 0) {
+                        float lse = lt > 0.f ? (st.m[cb] + __builtin_log2f(lt)) * kLn2 : kNegInf;
+                        if (st.bad) lse = __builtin_nanf("");
+                        a.part_lse[row] = lse;
+                    }
                 }
             }
         }
-        lds_barrier();   // every wave is done with the ring before the next descriptor's loads
+        d = claim_take(v_next);   // its barriers also keep the ring until every wave is done with it
     }
 }
 
@@ -607,13 +636,14 @@ hipError_t launch_cb(PrefillArgs a, hipStream_t stream) {
 
 hipError_t launch_varlen(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
                          const void* map, int B, int Hq, int Hkv, int P, int64_t nq_max, int max_pages,
-                         int64_t num_pages, int64_t total_q, float scale_log2, float* part_lse, float* part_o,
-                         void* out, hipStream_t stream) {
+                         int64_t num_pages, int64_t total_q, float scale_log2, int32_t* counters, float* part_lse,
+                         float* part_o, void* out, int workgroups, hipStream_t stream) {
     VarlenArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k_cache = static_cast<const uint16_t*>(k_cache);
     a.v_cache = static_cast<const uint16_t*>(v_cache);
     a.page_table = page_table;
+    a.counters = counters;
     a.part_lse = part_lse;
     a.part_o = part_o;
     a.out = static_cast<uint16_t*>(out);
@@ -623,7 +653,13 @@ hipError_t launch_varlen(const void* q, const void* k_cache, const void* v_cache
     a.total_q = (int32_t)total_q;
     a.scale_log2 = scale_log2;
     const uint8_t* m = static_cast<const uint8_t*>(map);
-    hipError_t e = launch(varlen_split_kernel, dim3(P), dim3(kSplitThreads), 0, stream, m, B, Hkv, P, (int)nq_max, a);
+    // the counter reset stays outside the kernel timing hook, which stamps
+    // the split and combine kernels
+    hipLaunchKernelGGL(varlen_reset_kernel, dim3(1), dim3(64), 0, stream, counters);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch(varlen_split_kernel, dim3((unsigned)workgroups), dim3(kSplitThreads), 0, stream, m, B, Hkv, P,
+               (int)nq_max, a);
     if (e != hipSuccess) return e;
     const long long grid = (long long)nq_max * Hkv;
     return launch(varlen_combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, m, B, Hkv, P,

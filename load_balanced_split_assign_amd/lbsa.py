@@ -40,7 +40,7 @@ class _MapLayout(ctypes.Structure):
 
 class _VarlenMapLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("header", "bin_desc_begin", "desc", "seg_first_desc", "seg_num_chunks", "seg_slot0", "blk_req",
+                ("header", "bin_desc_begin", "desc", "desc_slot", "claim_order", "seg_first_desc", "seg_num_chunks", "seg_slot0", "blk_req",
                  "blk_k", "qbase", "qstart", "seqlens", "qlens", "total")]
 
 
@@ -474,7 +474,10 @@ def read_varlen_task_map(task_map: torch.Tensor, batch: int, num_kv_heads: int, 
     for i, name in enumerate(HEADER_FIELDS):
         out[name] = int(header[i])
     out["NQ"], out["QB"] = NQ, int(header[15])
-    out["desc"] = out["desc_all"][:max(0, min(out["Ndesc"], cap))].copy()
+    nd = max(0, min(out["Ndesc"], cap))
+    out["desc"] = out["desc_all"][:nd].copy()
+    out["desc_slot"] = arr(lay["desc_slot"], cap)[:nd].copy()
+    out["claim_order"] = arr(lay["claim_order"], cap)[:nd].copy()
     return out
 
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 205
+    assert lbsa.lib().lbsa_version() == 206
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -205,14 +205,17 @@ def test_timing_hook_arms_and_disarms_without_a_gpu():
 
 def test_varlen_map_layout_and_workspace():
     """Query-block maps: 32-byte descriptors for Hkv * (B + total_q / 16) + P
-    slots, every array after the descriptors, and 2 P partial slots of 128 rows."""
+    slots, their partial-slot words and claim order, every array after them; the workspace:
+    256 bytes of claim counters, then 2 P partial slots of 128 rows."""
     for B, Hkv, P, tq in [(2, 1, 4, 21), (64, 8, 512, 8255), (1, 8, 512, 8192)]:
         lay = lbsa.varlen_task_map_layout(B, Hkv, P, tq)
         nq = B + tq // 16
         S, cap = Hkv * nq, Hkv * nq + P
         assert lay["header"] == 0 and lay["bin_desc_begin"] == 64
         assert lay["desc"] % 32 == 0 and lay["desc"] >= 64 + 4 * (P + 1)
-        assert lay["seg_first_desc"] == lay["desc"] + 32 * cap
+        assert lay["desc_slot"] == lay["desc"] + 32 * cap
+        assert lay["claim_order"] == lay["desc_slot"] + 4 * cap
+        assert lay["seg_first_desc"] == lay["claim_order"] + 4 * cap
         assert lay["seg_num_chunks"] == lay["seg_first_desc"] + 4 * S
         assert lay["seg_slot0"] == lay["seg_num_chunks"] + 4 * S
         assert lay["blk_req"] == lay["seg_slot0"] + 4 * S and lay["blk_k"] == lay["blk_req"] + 4 * nq
@@ -221,7 +224,7 @@ def test_varlen_map_layout_and_workspace():
         assert lay["total"] >= lay["qlens"] + 4 * B and lay["total"] % 256 == 0
         assert lbsa.varlen_task_map_bytes(B, Hkv, P, tq) == lay["total"]
     ws = lbsa.varlen_workspace_bytes(64, 8, 512)
-    assert ws >= 2 * 512 * 128 * (128 + 1) * 4 and ws < 2 * 512 * 128 * (128 + 1) * 4 + 512
+    assert ws >= 256 + 2 * 512 * 128 * (128 + 1) * 4 and ws < 2 * 512 * 128 * (128 + 1) * 4 + 768
 
 
 def test_varlen_host_argument_errors():

@@ -45,13 +45,27 @@ def expected_extras(o, sl, ql, P):
     qbase = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     qstart = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
     bdb = np.asarray(o["bin_desc_begin"], np.int64)
-    slot0 = []
-    for d0 in o["seg_first_desc"]:
-        j0 = int(np.searchsorted(bdb[:P], d0, side="right") - 1)   # the bin holding descriptor d0
-        slot0.append(2 * j0 + (0 if bdb[j0] == d0 else 1))
+    def slot_of(d):
+        j = int(np.searchsorted(bdb[:P], d, side="right") - 1)     # the bin holding descriptor d
+        return 2 * j + (0 if bdb[j] == d else 1)
+    slot0 = [slot_of(d0) for d0 in o["seg_first_desc"]]
+    desc_slot = [slot_of(d) for d in range(len(o["desc"]))]
+    # claim order: 8 groups of consecutive bins, each listing its requests in
+    # walk order with every request's run of descriptors reversed
+    order = []
+    for x in range(8):
+        lo, hi = int(bdb[x * P // 8]), int(bdb[(x + 1) * P // 8])
+        d = lo
+        while d < hi:
+            e = d
+            while e < hi and tuple(o["desc"][e][:2]) == tuple(o["desc"][d][:2]):
+                e += 1
+            order += list(range(e - 1, d - 1, -1))
+            d = e
     blk_req = np.repeat(np.arange(len(ql)), nq).astype(np.int32)
     blk_k = np.concatenate([np.arange(n) for n in nq]).astype(np.int32)
-    return dict(qbase=qbase, qstart=qstart, slot0=np.asarray(slot0, np.int32), blk_req=blk_req, blk_k=blk_k)
+    return dict(qbase=qbase, qstart=qstart, slot0=np.asarray(slot0, np.int32), blk_req=blk_req, blk_k=blk_k,
+                desc_slot=np.asarray(desc_slot, np.int32), claim_order=np.asarray(order, np.int32))
 
 
 def assert_same_varlen_map(oracle_mod, sl, ql, Hkv, P, F, mp, what=""):
@@ -75,6 +89,8 @@ def assert_same_varlen_map(oracle_mod, sl, ql, Hkv, P, F, mp, what=""):
     if o["error"] == 0:
         e = expected_extras(o, sl, ql, P)
         np.testing.assert_array_equal(g["seg_slot0"], e["slot0"], err_msg=ctx)
+        np.testing.assert_array_equal(g["desc_slot"], e["desc_slot"], err_msg=ctx)
+        np.testing.assert_array_equal(g["claim_order"], e["claim_order"], err_msg=ctx)
         np.testing.assert_array_equal(g["blk_req"], e["blk_req"], err_msg=ctx)
         np.testing.assert_array_equal(g["blk_k"], e["blk_k"], err_msg=ctx)
         np.testing.assert_array_equal(g["qbase"], e["qbase"], err_msg=ctx)
