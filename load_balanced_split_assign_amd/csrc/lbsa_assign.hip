@@ -399,19 +399,71 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
     }
     __syncthreads();   // records and bin starts written by this workgroup
 
-    // ---- claim order: in each group of bins, the requests in walk order and
-    // each request's descriptors from the last back (its query blocks with the
-    // most tiles first); a request's descriptors for one KV head are
-    // contiguous in the walk, [first of its first block, first of the next)
-    for (int d = tid; d < ndesc; d += kAssignThreads) {
+    // ---- claim order: in each group of bins, the descriptors by decreasing
+    // tile count (lengths of kLenClasses tiles and more share the last class),
+    // equal counts by decreasing index.  A counting sort over the LDS, free
+    // once the walk is done: a histogram per (group, length), its exclusive
+    // scan in (group, decreasing length) order -- the groups are consecutive
+    // descriptor ranges from 0, so the scan gives claim positions -- then a
+    // stable scatter in decreasing index order.
+    int* hist = smem;                                   // [kVarlenGroups * kLenClasses]
+    constexpr int kKeys = kVarlenGroups * kLenClasses;
+    auto key_of = [&](int d) {
         const int32_t* rec = desc + (size_t)kVarlenDescWords * d;
-        const int h = rec[VD_H], b = rec[VD_B], j = dslot[d] >> 1;
+        const int len = min(rec[VD_T1] - rec[VD_T0], kLenClasses - 1);
+        const int j = dslot[d] >> 1;
         int x = 0;
         while (x + 1 < kVarlenGroups && (int)((int64_t)(x + 1) * P / kVarlenGroups) <= j) ++x;
-        const int lo = bdb[(int)((int64_t)x * P / kVarlenGroups)];
-        const int hi = bdb[(int)((int64_t)(x + 1) * P / kVarlenGroups)];
-        const int r_lo = max(lo, sfd[h * NQ + qbase[b]]), r_hi = min(hi, sfd[h * NQ + qbase[b + 1]]);
-        order[r_lo + r_hi - 1 - d] = d;
+        return x * kLenClasses + (kLenClasses - 1 - max(len, 0));
+    };
+    for (int i = tid; i < kKeys; i += kAssignThreads) hist[i] = 0;
+    __syncthreads();
+    for (int d = tid; d < ndesc; d += kAssignThreads) atomicAdd(&hist[key_of(d)], 1);
+    __syncthreads();
+    {
+        constexpr int per_t = kKeys / kAssignThreads;
+        static_assert(kKeys % kAssignThreads == 0, "keys split evenly over the threads");
+        int sum = 0;
+        for (int i = 0; i < per_t; ++i) sum += hist[tid * per_t + i];
+        int total;
+        int pre = block_exclusive_scan(sum, red[0], &total);
+        for (int i = 0; i < per_t; ++i) {
+            const int c = hist[tid * per_t + i];
+            hist[tid * per_t + i] = pre;
+            pre += c;
+        }
+    }
+    __syncthreads();
+    {
+        const int lane = tid & 63, wv = tid >> 6;
+        const uint64_t lt_mask = (1ull << lane) - 1;
+        for (int c0 = 0; c0 < ndesc; c0 += kAssignThreads) {
+            const int d = ndesc - 1 - (c0 + tid);           // decreasing index: thread order = scatter order
+            const bool valid = d >= 0;
+            const int key = valid ? key_of(d) : -1;
+            // rank among the lanes of this wave with the same key, and their count
+            int rank = 0, count = 0;
+            uint64_t pending = __builtin_amdgcn_ballot_w64(valid);
+            while (pending) {
+                const int leader = __builtin_ctzll(pending);
+                const int lk = __builtin_amdgcn_readlane(key, leader);
+                const uint64_t m = __builtin_amdgcn_ballot_w64(valid && key == lk);
+                if (valid && key == lk) {
+                    rank = __builtin_popcountll(m & lt_mask);
+                    count = __builtin_popcountll(m);
+                }
+                pending &= ~m;
+            }
+            // the waves take their positions in turn
+            for (int t = 0; t < kAssignThreads / 64; ++t) {
+                if (wv == t && valid) {
+                    const int base = hist[key];
+                    order[base + rank] = d;
+                    if (rank == count - 1) hist[key] = base + count;   // the key's last lane moves it on
+                }
+                __syncthreads();
+            }
+        }
     }
 
     if (tid == 0) {
@@ -438,7 +490,9 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
 
 hipError_t launch_assign_varlen(const int32_t* seqlens, const int32_t* qlens, int B, int Hq, int Hkv, int P, int F,
                                 int max_pages, int64_t total_q, int64_t nq_max, void* map, hipStream_t stream) {
-    const size_t lds = sizeof(int) * varlen_assign_lds_words(B, Hkv, nq_max);
+    const size_t words = varlen_assign_lds_words(B, Hkv, nq_max);
+    const size_t lds = sizeof(int) * (words > (size_t)kVarlenGroups * kLenClasses ? words
+                                                                                 : (size_t)kVarlenGroups * kLenClasses);
     return launch(assign_varlen_kernel, dim3(1), dim3(kAssignThreads), (uint32_t)lds, stream, seqlens, qlens, B, Hq,
                   Hkv, P, F, max_pages, (int)total_q, (int)nq_max, static_cast<uint8_t*>(map));
 }

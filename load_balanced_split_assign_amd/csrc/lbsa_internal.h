@@ -89,8 +89,8 @@ __host__ __device__ inline int64_t varlen_max_blocks(int B, int64_t total_q) { r
 // the others (only a bin's first and last descriptors can be cut).
 // claim_order lists the descriptors of each group of bins (kVarlenGroups
 // groups of consecutive bins, group x = bins [x P / 8, (x + 1) P / 8)) in the
-// order the split kernel's workgroups claim them: the group's requests in walk
-// order, each request's descriptors from its last back.
+// order the split kernel's workgroups claim them: by decreasing tile count
+// (counts of 1023 and more tie), equal counts by decreasing index.
 struct VarlenMapLayout {
     size_t header, bin_desc_begin, desc, desc_slot, claim_order, seg_first_desc, seg_num_chunks, seg_slot0,
         blk_req, blk_k, qbase, qstart, seqlens, qlens, total;
@@ -123,6 +123,7 @@ __host__ __device__ inline VarlenMapLayout varlen_map_layout(int B, int Hkv, int
 // launch; the partial slots follow.
 constexpr int kVarlenGroups = 8;
 constexpr size_t kVarlenCounterBytes = 256;
+constexpr int kLenClasses = 1024;           // claim-order sort keys per group: tile counts 0 .. 1023+
 
 // LDS words the varlen assign kernel needs: lengths, q lengths, their two
 // prefixes, the tile prefix over query blocks and the chunk prefix over

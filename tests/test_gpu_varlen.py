@@ -50,18 +50,13 @@ def expected_extras(o, sl, ql, P):
         return 2 * j + (0 if bdb[j] == d else 1)
     slot0 = [slot_of(d0) for d0 in o["seg_first_desc"]]
     desc_slot = [slot_of(d) for d in range(len(o["desc"]))]
-    # claim order: 8 groups of consecutive bins, each listing its requests in
-    # walk order with every request's run of descriptors reversed
+    # claim order: 8 groups of consecutive bins, each by decreasing tile count
+    # (1023 and more tie), equal counts by decreasing descriptor index
     order = []
     for x in range(8):
         lo, hi = int(bdb[x * P // 8]), int(bdb[(x + 1) * P // 8])
-        d = lo
-        while d < hi:
-            e = d
-            while e < hi and tuple(o["desc"][e][:2]) == tuple(o["desc"][d][:2]):
-                e += 1
-            order += list(range(e - 1, d - 1, -1))
-            d = e
+        length = lambda d: min(int(o["desc"][d][4] - o["desc"][d][3]), 1023)
+        order += sorted(range(lo, hi), key=lambda d: (-length(d), -d))
     blk_req = np.repeat(np.arange(len(ql)), nq).astype(np.int32)
     blk_k = np.concatenate([np.arange(n) for n in nq]).astype(np.int32)
     return dict(qbase=qbase, qstart=qstart, slot0=np.asarray(slot0, np.int32), blk_req=blk_req, blk_k=blk_k,
