@@ -458,14 +458,44 @@ def _timed(run, steps, warmup, flush):
     return summarize([1000.0 * a.elapsed_time(b) for a, b in ev])["mean"]
 
 
+def _timed_alternating(runs, steps, warmup, flush):
+    """Mean event time (us) of each closure in `runs` (name -> run), the
+    closures taking turns within every round (flush before each call, outside
+    its event pair), so that every one meets the same clock and cache history;
+    `warmup` untimed rounds first."""
+    import torch
+    stream = torch.cuda.current_stream()
+    names = list(runs)
+    k = 0
+    for _ in range(warmup):
+        for n in names:
+            flush(k)
+            k += 1
+            runs[n]()
+    torch.cuda.synchronize()
+    ev = {n: _pairs(steps) for n in names}
+    for i in range(steps):
+        for n in names:
+            flush(k)
+            k += 1
+            ev[n][i][0].record(stream)
+            runs[n]()
+            ev[n][i][1].record(stream)
+    torch.cuda.synchronize()
+    return {n: summarize([1000.0 * a.elapsed_time(b) for a, b in ev[n]])["mean"] for n in names}
+
+
 def varlen_bench(args):
     """Prefill / extend and decode rows on one task map (query-block segments)
     against the grid path: lbsa_prefill for the requests with new tokens and the
     decode task map for the decode rows.  Workloads: the mixed batch (one 8K
     extend of an 8K context beside 63 decode rows, 64/8 heads) and a q8k prefill
     alone.  Per path: the step (with its plans) and the layer (plans reused),
-    event pairs with the read flush before each; the map path's kernels also by
-    their own stamps."""
+    event pairs with the read flush before each; the map path's split kernel
+    (which also merges the cut segments) also by its own stamps.  The paths
+    take turns in every round after at least 10 warm-up rounds: the clocks
+    still rise over the first tens of milliseconds of load, and timing one path
+    after the other favours the second."""
     import torch
 
     from load_balanced_split_assign_amd import lbsa
@@ -492,20 +522,15 @@ def varlen_bench(args):
             lbsa.attend_varlen(b["q"], b["k_cache"], b["v_cache"], b["page_table"], tm, P, b["softmax_scale"], B,
                                workspace=ws, out=out)
         vplan()
-        layer = _timed(vattend, args.steps, args.warmup, flush)
-        step = _timed(lambda: (vplan(), vattend()), args.steps, args.warmup, flush)
-        kev = [_pairs(2) for _ in range(args.steps)]
-        for e in kev:
-            for x, y in e:
-                x.record(); y.record()
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            flush(i)
-            lbsa.time_next_kernels(kev[i])
+        stamps = []
+
+        def vattend_stamped():
+            e = _pairs(1)
+            e[0][0].record()
+            e[0][1].record()
+            lbsa.time_next_kernels(e)
             vattend()
-        torch.cuda.synchronize()
-        split_k = statistics.fmean(1000.0 * e[0][0].elapsed_time(e[0][1]) for e in kev)
-        comb_k = statistics.fmean(1000.0 * e[1][0].elapsed_time(e[1][1]) for e in kev)
+            stamps.append(e[0])
         m = lbsa.read_varlen_task_map(tm, B, 8, P, tq)
 
         # the grid path: lbsa_prefill for the request with new tokens, the decode map for the rest
@@ -532,14 +557,18 @@ def varlen_bench(args):
             if nd:
                 dpath.assign()
             grid_layer()
-        g_layer = _timed(grid_layer, args.steps, args.warmup, flush)
-        g_step = _timed(grid_step, args.steps, args.warmup, flush)
+        t = _timed_alternating({"map_layer": vattend, "grid_layer": grid_layer, "map_step": lambda: (vplan(), vattend()),
+                                "grid_step": grid_step, "map_stamped": vattend_stamped},
+                               args.steps, max(args.warmup, 10), flush)
+        torch.cuda.synchronize()
+        layer, step, g_layer, g_step = t["map_layer"], t["map_step"], t["grid_layer"], t["grid_step"]
+        split_k = statistics.fmean(1000.0 * x.elapsed_time(y) for x, y in stamps[-args.steps:])
         flops = causal_flops(1, eq, sl[0], 64) + sum(4 * 64 * 128 * L for L in sl[1:])
         rows.append({"workload": name, "batch": B, "total_q": tq, "extend": {"L": sl[0], "q": eq},
                      "decode_rows": nd, "P": P, "T": m["T"], "K": m["K"], "Ndesc": m["Ndesc"],
                      "cut_segments": int((m["seg_num_chunks"] > 1).sum()), "flops": flops,
                      "map_layer_us": round(layer, 2), "map_step_us": round(step, 2),
-                     "map_split_kernel_us": round(split_k, 2), "map_combine_kernel_us": round(comb_k, 2),
+                     "map_split_kernel_us": round(split_k, 2),
                      "grid_layer_us": round(g_layer, 2), "grid_step_us": round(g_step, 2),
                      "map_layer_TFLOPs": round(flops / layer / 1e6, 1),
                      "map_layer_pct_of_mfma_peak": round(100 * flops / layer / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),

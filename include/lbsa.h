@@ -332,18 +332,19 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
  *                  of qlens, and the two length copies
  *                  (lbsa_varlen_task_map_layout_get)
  *   workspace      lbsa_varlen_workspace_bytes(num_heads, num_kv_heads, 128, P):
- *                  256 bytes of claim counters (cleared by every call), then
- *                  2 P partial slots of 16 x 8 rows (position x head), fp32 LSE
- *                  [2 P][128] then O [2 P][128][128]; only a bin's first and last
- *                  descriptors can cut a segment, so slot 2 j + (0 first, 1 last)
- * lbsa_attend_varlen is three launches on the stream: a one-workgroup kernel
- * clears the claim counters; persistent workgroups (as many as stay resident)
- * claim the descriptors of 8 groups of consecutive bins, one group per XCD,
- * in the map's claim order, and compute each descriptor's
- * query block over its tiles (MFMA, K/V through LDS), writing the bf16 rows of
- * a segment it holds whole and a partial otherwise; then one workgroup per
- * (KV head, block) merges the chunks of the cut segments.  Calls that share a
- * workspace must not overlap.
+ *                  int32 counters (8 claim, then P arrival; cleared by every
+ *                  call), padded to 256 bytes, then 2 P partial slots of
+ *                  16 x 8 rows (position x head), fp32 LSE [2 P][128] then O
+ *                  [2 P][128][128]; only a bin's first and last descriptors can
+ *                  cut a segment, so slot 2 j + (0 first, 1 last)
+ * lbsa_attend_varlen is two launches on the stream: a small kernel clears the
+ * counters; persistent workgroups (as many as stay resident) claim the
+ * descriptors of 8 groups of consecutive bins, one group per XCD, in the
+ * map's claim order, and compute each descriptor's query block over its tiles
+ * (MFMA, K/V through LDS), writing the bf16 rows of a segment it holds whole
+ * and a partial otherwise; the workgroup that writes a cut segment's last
+ * chunk merges its chunks into the output rows.  Calls that share a workspace
+ * must not overlap.
  * Errors: shapes as lbsa_plan and lbsa_prefill (bf16 only); maps larger than
  * one assign workgroup's LDS (about 16K segments) give LBSA_ERR_UNSUPPORTED.
  * A length or q out of range on the device sets the error word: every output

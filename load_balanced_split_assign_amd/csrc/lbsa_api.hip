@@ -475,7 +475,8 @@ static int varlen_shape(int32_t batch, int32_t num_kv_heads, int32_t P, int64_t 
     if (batch <= 0 || num_kv_heads <= 0 || P <= 0 || total_q < batch) return LBSA_ERR_INVALID_ARGUMENT;
     if (total_q > (1 << 24) || P >= (1 << 24)) return LBSA_ERR_UNSUPPORTED;
     // the single assign workgroup keeps every prefix in LDS
-    if (varlen_assign_lds_words(batch, num_kv_heads, varlen_max_blocks(batch, total_q)) > (size_t)kMaxAssignLdsWords)
+    if (varlen_assign_lds_words(batch, num_kv_heads, varlen_max_blocks(batch, total_q)) >
+        (size_t)kMaxAssignLdsWords + kVarlenClaimHistWords)
         return LBSA_ERR_UNSUPPORTED;
     return LBSA_OK;
 }
@@ -521,7 +522,7 @@ LBSA_API int lbsa_varlen_workspace_bytes(int32_t num_heads, int32_t num_kv_heads
     if (!out_bytes || P <= 0) return LBSA_ERR_INVALID_ARGUMENT;
     const int s = check_shape(1, num_heads, num_kv_heads, head_dim, kTile);
     if (s != LBSA_OK) return s;
-    *out_bytes = kVarlenCounterBytes + align_up(2 * (size_t)P * kVarlenSlotBytesLse, 256) +
+    *out_bytes = varlen_counter_bytes(P) + align_up(2 * (size_t)P * kVarlenSlotBytesLse, 256) +
                  2 * (size_t)P * kVarlenSlotBytesO;
     return LBSA_OK;
 }
@@ -615,9 +616,9 @@ LBSA_API int lbsa_attend_varlen(const void* q_d, const void* k_cache_d, const vo
     const int workgroups = (int)(cap < resident ? cap : resident);
     uint8_t* ws = static_cast<uint8_t*>(workspace_d);
     int32_t* counters = reinterpret_cast<int32_t*>(ws);
-    float* part_lse = reinterpret_cast<float*>(ws + kVarlenCounterBytes);
-    float* part_o = reinterpret_cast<float*>(ws + kVarlenCounterBytes +
-                                             align_up(2 * (size_t)num_workgroups * kVarlenSlotBytesLse, 256));
+    const size_t cb = varlen_counter_bytes(num_workgroups);
+    float* part_lse = reinterpret_cast<float*>(ws + cb);
+    float* part_o = reinterpret_cast<float*>(ws + cb + align_up(2 * (size_t)num_workgroups * kVarlenSlotBytesLse, 256));
     return hip_status(launch_varlen(q_d, k_cache_d, v_cache_d, page_table_d, task_map_d, batch, num_heads,
                                     num_kv_heads, num_workgroups, nq, max_pages_per_seq,
                                     num_pages > INT32_MAX ? INT32_MAX : num_pages, total_q,

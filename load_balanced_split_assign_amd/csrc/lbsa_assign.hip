@@ -21,6 +21,8 @@
 // each bin's descriptors are emitted by one thread walking the bin's tile range
 // from its first slot.  Every step is a scan, a search or a short walk, so the
 // 256 threads share the work.
+#include <mutex>
+
 #include "lbsa_internal.h"
 
 namespace lbsa {
@@ -59,6 +61,30 @@ __device__ int block_exclusive_scan(int v, int* red, int* total) {
     }
     *total = all;
     return before + x - v;
+}
+
+// Group of bin j: the largest x with floor(x P / 8) <= j.
+__device__ inline int group_of_bin(int j, int P) {
+    int x = 0;
+    while (x + 1 < kVarlenGroups && (int)((int64_t)(x + 1) * P / kVarlenGroups) <= j) ++x;
+    return x;
+}
+
+// Claim-order sort key of a descriptor of `len` tiles in group x: groups in
+// order, lengths decreasing by class (exact below 8 tiles, then four classes
+// per power of two).
+constexpr int kLenClasses = 64;
+constexpr int kClaimKeys = kVarlenGroups * kLenClasses;
+constexpr int kWaveQuarters = kAssignThreads / 64;
+static_assert(kClaimKeys * kWaveQuarters == kVarlenClaimHistWords, "LDS words reserved for the claim order");
+__device__ inline int claim_key(int x, int len) {
+    int c = len;
+    if (len >= 8) {
+        const int e = 31 - __builtin_clz((unsigned)len);            // floor(log2 len) >= 3
+        c = 8 + 4 * (e - 3) + ((len >> (e - 2)) & 3);              // the two bits below the leading one
+    }
+    c = min(max(c, 0), kLenClasses - 1);
+    return x * kLenClasses + (kLenClasses - 1 - c);
 }
 
 struct Bins {
@@ -344,85 +370,76 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
         bins.r = T % bins.K;
     }
 
-    // ---- chunks per segment s = h * NQ + u, their prefix, first-chunk slots --
+    // ---- chunks per segment s = h * NQ + u and their prefix ------------------
+    // (counts in LDS with interleaved segments, then a scan over contiguous
+    // ranges of them)
     const int S = Hkv * NQ;
+    for (int s = tid; s < S; s += kAssignThreads) {
+        const int h = s / NQ, u = s - h * NQ;
+        const int a = h * N + tpre[u], n = tpre[u + 1] - tpre[u];
+        sfd[s] = n ? bins.of(a + n - 1) - bins.of(a) + 1 : 0;
+    }
+    __syncthreads();
     const int sper = (S + kAssignThreads - 1) / kAssignThreads;
     const int s0 = min(S, tid * sper), s1 = min(S, s0 + sper);
     int c_local = 0;
-    for (int s = s0; s < s1; ++s) {
-        const int h = s / NQ, u = s - h * NQ;
-        const int a = h * N + tpre[u], n = tpre[u + 1] - tpre[u];
-        const int c = n ? bins.of(a + n - 1) - bins.of(a) + 1 : 0;
-        sfd[s] = c;
-        c_local += c;
-        const int j0 = n ? bins.of(a) : 0;
-        slot0_g[s] = 2 * j0 + (n && a != bins.start(j0) ? 1 : 0);
-    }
+    for (int s = s0; s < s1; ++s) c_local += sfd[s];
     int ndesc;
     run = block_exclusive_scan(c_local, red[3], &ndesc);
     for (int s = s0; s < s1; ++s) {
         const int c = sfd[s];
         sfd[s] = run;
-        sfd_g[s] = run;
-        snc_g[s] = c;
         run += c;
     }
     if (tid == 0) sfd[S] = ndesc;
+    // claim-order histogram: per sort key and per wave's quarter of the
+    // descriptors (the quarters in decreasing index order: wave 0 the highest)
+    int* hist = sfd + (size_t)Hkv * nq_max + 1;        // [kClaimKeys][kWaveQuarters], after sfd's words
+    for (int i = tid; i < kClaimKeys * kWaveQuarters; i += kAssignThreads) hist[i] = 0;
+    const int quarter = (ndesc + kWaveQuarters - 1) / kWaveQuarters;
     __syncthreads();
 
-    // ---- bins: thread j walks bin j's tile range segment by segment ---------
-    for (int j = tid; j <= P; j += kAssignThreads) {
-        int v = ndesc;
-        if (j < bins.K) {
-            int x = bins.start(j);
-            const int xe = bins.start(j + 1);
-            int h = x / N;
-            int u = upper_bound(tpre, NQ, x - h * N) - 1;
-            int a = h * N + tpre[u];
-            v = sfd[h * NQ + u] + (j - bins.of(a));
-            const int cap = S + P;
-            for (int d = v; d < cap; ++d) {
-                const int e = h * N + tpre[u + 1];            // end of segment (h, u)
-                const int t1 = min(e, xe);
-                const int b = upper_bound(qbase, B, u) - 1;
-                int32_t* rec = desc + (size_t)kVarlenDescWords * d;
-                *reinterpret_cast<int4*>(rec) = make_int4(h, b, u - qbase[b], x - a);
-                *reinterpret_cast<int4*>(rec + 4) = make_int4(t1 - a, lens[b], qls[b], qstart[b]);
-                dslot[d] = 2 * j + (d != v ? 1 : 0);
-                if (t1 >= xe) break;
-                x = t1;                                       // blocks are never empty: the next one
-                if (++u == NQ) { u = 0; ++h; }
-                a = h * N + tpre[u];
-            }
+    // ---- descriptors, segment by segment: chunk c of segment s is descriptor
+    // sfd[s] + c, its part of bin bins.of(a) + c (the same numbering as a walk
+    // of every bin in order).  Neighbouring threads take neighbouring
+    // segments, so the records of one-chunk segments are written together.
+    // The chunk that starts at its bin's first tile is the bin's first
+    // descriptor: exactly one per bin below K. ----------------------------------
+    for (int s = tid; s < S; s += kAssignThreads) {
+        const int h = s / NQ, u = s - h * NQ;
+        const int a = h * N + tpre[u], n = tpre[u + 1] - tpre[u];
+        const int d0 = sfd[s], nc = sfd[s + 1] - d0;
+        const int j0 = n ? bins.of(a) : 0;
+        sfd_g[s] = d0;
+        snc_g[s] = nc;
+        slot0_g[s] = 2 * j0 + (n && a != bins.start(j0) ? 1 : 0);
+        const int b = upper_bound(qbase, B, u) - 1;
+        const int k = u - qbase[b], L = lens[b], q = qls[b], qs = qstart[b];
+        for (int c = 0; c < nc; ++c) {
+            const int j = j0 + c, d = d0 + c;
+            const int bs = bins.start(j);
+            const int ts = max(a, bs), te = min(a + n, bins.start(j + 1));
+            int32_t* rec = desc + (size_t)kVarlenDescWords * d;
+            *reinterpret_cast<int4*>(rec) = make_int4(h, b, k, ts - a);
+            *reinterpret_cast<int4*>(rec + 4) = make_int4(te - a, L, q, qs);
+            dslot[d] = 2 * j + (ts != bs ? 1 : 0);
+            if (ts == bs) bdb[j] = d;
+            atomicAdd(&hist[claim_key(group_of_bin(j, P), te - ts) * kWaveQuarters + (ndesc - 1 - d) / quarter], 1);
         }
-        bdb[j] = v;
     }
+    for (int j = bins.K + tid; j <= P; j += kAssignThreads) bdb[j] = ndesc;
     __syncthreads();   // records and bin starts written by this workgroup
 
     // ---- claim order: in each group of bins, the descriptors by decreasing
-    // tile count (lengths of kLenClasses tiles and more share the last class),
-    // equal counts by decreasing index.  A counting sort over the LDS, free
-    // once the walk is done: a histogram per (group, length), its exclusive
-    // scan in (group, decreasing length) order -- the groups are consecutive
-    // descriptor ranges from 0, so the scan gives claim positions -- then a
-    // stable scatter in decreasing index order.
-    int* hist = smem;                                   // [kVarlenGroups * kLenClasses]
-    constexpr int kKeys = kVarlenGroups * kLenClasses;
-    auto key_of = [&](int d) {
-        const int32_t* rec = desc + (size_t)kVarlenDescWords * d;
-        const int len = min(rec[VD_T1] - rec[VD_T0], kLenClasses - 1);
-        const int j = dslot[d] >> 1;
-        int x = 0;
-        while (x + 1 < kVarlenGroups && (int)((int64_t)(x + 1) * P / kVarlenGroups) <= j) ++x;
-        return x * kLenClasses + (kLenClasses - 1 - max(len, 0));
-    };
-    for (int i = tid; i < kKeys; i += kAssignThreads) hist[i] = 0;
-    __syncthreads();
-    for (int d = tid; d < ndesc; d += kAssignThreads) atomicAdd(&hist[key_of(d)], 1);
-    __syncthreads();
+    // length class (claim_key), equal classes by decreasing index.  The walk
+    // counted them per (key, quarter); the exclusive scan in (key, quarter)
+    // order gives each wave the first position of every key in its quarter (the
+    // groups are consecutive descriptor ranges from 0, so positions are claim
+    // positions); then wave w places its quarter, highest index first, 64 at a
+    // time, ranking equal keys by lane.
     {
-        constexpr int per_t = kKeys / kAssignThreads;
-        static_assert(kKeys % kAssignThreads == 0, "keys split evenly over the threads");
+        constexpr int per_t = kClaimKeys * kWaveQuarters / kAssignThreads;
+        static_assert((kClaimKeys * kWaveQuarters) % kAssignThreads == 0, "entries split evenly over the threads");
         int sum = 0;
         for (int i = 0; i < per_t; ++i) sum += hist[tid * per_t + i];
         int total;
@@ -437,11 +454,15 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
     {
         const int lane = tid & 63, wv = tid >> 6;
         const uint64_t lt_mask = (1ull << lane) - 1;
-        for (int c0 = 0; c0 < ndesc; c0 += kAssignThreads) {
-            const int d = ndesc - 1 - (c0 + tid);           // decreasing index: thread order = scatter order
-            const bool valid = d >= 0;
-            const int key = valid ? key_of(d) : -1;
-            // rank among the lanes of this wave with the same key, and their count
+        const int top = ndesc - 1 - wv * quarter, bottom = max(ndesc - (wv + 1) * quarter, 0);
+        for (int c0 = top; c0 >= bottom; c0 -= 64) {
+            const int d = c0 - lane;
+            const bool valid = d >= bottom;
+            int key = -1;
+            if (valid) {
+                const int32_t* rec = desc + (size_t)kVarlenDescWords * d;
+                key = claim_key(group_of_bin(dslot[d] >> 1, P), rec[VD_T1] - rec[VD_T0]);
+            }
             int rank = 0, count = 0;
             uint64_t pending = __builtin_amdgcn_ballot_w64(valid);
             while (pending) {
@@ -454,14 +475,11 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
                 }
                 pending &= ~m;
             }
-            // the waves take their positions in turn
-            for (int t = 0; t < kAssignThreads / 64; ++t) {
-                if (wv == t && valid) {
-                    const int base = hist[key];
-                    order[base + rank] = d;
-                    if (rank == count - 1) hist[key] = base + count;   // the key's last lane moves it on
-                }
-                __syncthreads();
+            if (valid) {
+                int* slot = &hist[key * kWaveQuarters + wv];
+                const int base = *slot;
+                order[base + rank] = d;
+                if (rank == count - 1) *slot = base + count;   // the key's last lane moves it on
             }
         }
     }
@@ -490,9 +508,17 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
 
 hipError_t launch_assign_varlen(const int32_t* seqlens, const int32_t* qlens, int B, int Hq, int Hkv, int P, int F,
                                 int max_pages, int64_t total_q, int64_t nq_max, void* map, hipStream_t stream) {
-    const size_t words = varlen_assign_lds_words(B, Hkv, nq_max);
-    const size_t lds = sizeof(int) * (words > (size_t)kVarlenGroups * kLenClasses ? words
-                                                                                 : (size_t)kVarlenGroups * kLenClasses);
+    const size_t lds = sizeof(int) * varlen_assign_lds_words(B, Hkv, nq_max);
+    // the prefixes may take 64 KiB and the claim-order histogram comes on top:
+    // allow the kernel gfx950's larger LDS once per process
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&assign_varlen_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)(sizeof(int) * ((size_t)kMaxAssignLdsWords + kVarlenClaimHistWords)));
+    });
+    if (attr != hipSuccess) return attr;
     return launch(assign_varlen_kernel, dim3(1), dim3(kAssignThreads), (uint32_t)lds, stream, seqlens, qlens, B, Hq,
                   Hkv, P, F, max_pages, (int)total_q, (int)nq_max, static_cast<uint8_t*>(map));
 }

@@ -89,8 +89,9 @@ __host__ __device__ inline int64_t varlen_max_blocks(int B, int64_t total_q) { r
 // the others (only a bin's first and last descriptors can be cut).
 // claim_order lists the descriptors of each group of bins (kVarlenGroups
 // groups of consecutive bins, group x = bins [x P / 8, (x + 1) P / 8)) in the
-// order the split kernel's workgroups claim them: by decreasing tile count
-// (counts of 1023 and more tie), equal counts by decreasing index.
+// order the split kernel's workgroups claim them: by decreasing length class
+// (the tile count below 8, then four classes per power of two), equal classes
+// by decreasing index.
 struct VarlenMapLayout {
     size_t header, bin_desc_begin, desc, desc_slot, claim_order, seg_first_desc, seg_num_chunks, seg_slot0,
         blk_req, blk_k, qbase, qstart, seqlens, qlens, total;
@@ -118,18 +119,19 @@ __host__ __device__ inline VarlenMapLayout varlen_map_layout(int B, int Hkv, int
     return m;
 }
 
-// The varlen workspace starts with the claim counters of the split kernel's
-// workgroups, one per group of bins (a group per XCD), cleared before every
-// launch; the partial slots follow.
+// The varlen workspace starts with the counters of the split kernel, cleared
+// before every launch: one claim counter per group of bins (a group per XCD),
+// then an arrival counter per bin (for the cut segment whose first chunk the
+// bin holds); the partial slots follow.
 constexpr int kVarlenGroups = 8;
-constexpr size_t kVarlenCounterBytes = 256;
-constexpr int kLenClasses = 1024;           // claim-order sort keys per group: tile counts 0 .. 1023+
+__host__ __device__ inline size_t varlen_counter_bytes(int P) { return align_up(4 * ((size_t)kVarlenGroups + P), 256); }
 
 // LDS words the varlen assign kernel needs: lengths, q lengths, their two
-// prefixes, the tile prefix over query blocks and the chunk prefix over
-// segments.
+// prefixes, the tile prefix over query blocks, the chunk prefix over
+// segments and the claim-order histogram.
+constexpr int kVarlenClaimHistWords = 2048;
 __host__ __device__ inline size_t varlen_assign_lds_words(int B, int Hkv, int64_t NQ) {
-    return 4 * (size_t)B + 2 + ((size_t)NQ + 1) + ((size_t)Hkv * NQ + 1);
+    return 4 * (size_t)B + 2 + ((size_t)NQ + 1) + ((size_t)Hkv * NQ + 1) + kVarlenClaimHistWords;
 }
 
 // Byte offsets of the partial buffers for `slots` partials of (q_len x G) x D

@@ -383,8 +383,10 @@ __global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
 // the grid kernel above.  A descriptor that covers its whole segment writes the
 // bf16 output rows of its block; a cut one -- only a bin's first or last
 // descriptor can be cut -- writes its partial (normalised O, natural-log LSE)
-// to the slot the map gives it (2 j first, 2 j + 1 last, for bin j), and
-// varlen_combine_kernel merges the chunks of each cut segment.
+// to the slot the map gives it (2 j first, 2 j + 1 last, for bin j), and the
+// workgroup that writes the last of a cut segment's chunks merges them all
+// into the output rows (an arrival counter per cut segment, indexed by the bin
+// of its first chunk: a bin starts at most one cut segment).
 //
 // Execution order on gfx950.  The bins fix where segments are cut; the
 // persistent workgroups then claim the descriptors one at a time.  A
@@ -403,7 +405,7 @@ struct VarlenArgs {
     const uint16_t* k_cache;
     const uint16_t* v_cache;
     const int32_t* page_table;   // [B][max_pages]
-    int32_t* counters;           // [kVarlenGroups] claim counters, zero at launch
+    int32_t* counters;           // kVarlenGroups claim counters, then P arrival counters; zero at launch
     float* part_lse;             // [2 P][128]: row p * 8 + g of a slot
     float* part_o;               // [2 P][128][128]
     uint16_t* out;               // packed like q
@@ -421,16 +423,72 @@ __device__ inline int varlen_extent(int L, int q, int k) {   // tiles the block'
     return (L - q + min(q, kQBlock * (k + 1)) + kTile - 1) / kTile;
 }
 
-// The claim counters of one launch start at zero (a fill kernel, not a
-// memset, so the launches can be captured in a graph).
-__global__ void varlen_reset_kernel(int32_t* counters) {
-    if (threadIdx.x < kVarlenGroups) counters[threadIdx.x] = 0;
+// The claim and arrival counters of one launch start at zero (a fill kernel,
+// not a memset, so the launches can be captured in a graph).
+__global__ void varlen_reset_kernel(int32_t* counters, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) counters[i] = 0;
+}
+
+// Merge of the n >= 2 chunks of one cut segment into its bf16 output rows, by
+// the whole workgroup: 8 rows at a time (row p * 8 + g of the block), 32
+// threads x 4 dims per row, the loads of up to 8 chunks issued before the
+// merge.  Chunk c sits in slot slot0 (c = 0) or 2 (bin0 + c): a cut
+// segment's chunks lie in consecutive bins, each after the first starting its
+// bin.  A NaN LSE (an invalid page) makes the row NaN.
+constexpr int kVarlenMergeUnroll = 8;
+
+__device__ inline void merge_cut_segment(const VarlenArgs& a, int slot0, int n, uint16_t* out_rows, int live) {
+    const int tid = threadIdx.x, d4 = (tid & 31) * 4;
+    const int bin0 = slot0 >> 1;
+    for (int row = tid >> 5; row < kVarlenRows; row += kSplitThreads / 32) {
+        const int p = row >> 3, gg = row & 7;
+        if (p >= live) break;                           // rows are position-major: the rest are dead too
+        float m = kNegInf, wsum = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        bool nan_seen = false;
+        for (int c0 = 0; c0 < n; c0 += kVarlenMergeUnroll) {
+            float l[kVarlenMergeUnroll];
+            f32x4 x[kVarlenMergeUnroll];
+#pragma unroll
+            for (int i = 0; i < kVarlenMergeUnroll; ++i) {
+                const int c = c0 + i;
+                if (c < n) {
+                    const size_t pr = (size_t)(c == 0 ? slot0 : 2 * (bin0 + c)) * kVarlenRows + row;
+                    l[i] = a.part_lse[pr];
+                    x[i] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kHeadDim + d4);
+                } else {
+                    l[i] = kNegInf;
+                    x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kVarlenMergeUnroll; ++i) {
+                if (l[i] != l[i]) { nan_seen = true; continue; }
+                if (l[i] == kNegInf) continue;
+                if (l[i] > m) {
+                    const float sc = exp2_fast((m - l[i]) * kLog2e);   // 0 when m = -inf
+                    wsum *= sc;
+                    o *= sc;
+                    m = l[i];
+                }
+                const float wgt = exp2_fast((l[i] - m) * kLog2e);
+                wsum += wgt;
+                o += wgt * x[i];
+            }
+        }
+        o *= wsum > 0.f ? 1.f / wsum : 0.f;
+        if (nan_seen) {
+            const float nan = __builtin_nanf("");
+            o = f32x4{nan, nan, nan, nan};
+        }
+        store_bf16x4(out_rows + ((size_t)p * a.Hq + gg) * kHeadDim + d4, o);
+    }
 }
 
 __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8_t* map, int B, int Hkv, int P,
                                                                      int nq_max, VarlenArgs a) {
     __shared__ __attribute__((aligned(16))) char ring_mem[kPfStages * kPfStageBytes];
-    __shared__ int claim_lds;
+    __shared__ int claim_lds, arrive_lds;
     lds_char* const ring = (lds_char*)ring_mem;
     constexpr int CB = 2, kPosWave = 2 * CB;
     static_assert(kWaves * kPosWave == kQBlock, "one workgroup holds one query block");
@@ -438,14 +496,26 @@ __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8
     const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
     const auto* bdb = uniform_ptr<int32_t>(map + ML.bin_desc_begin);
     const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
-    const int ndesc = hdr[LBSA_HDR_NDESC];
+    const int ndesc = hdr[LBSA_HDR_NDESC], NQ = hdr[14];
     const int cap = Hkv * nq_max + P;
-    if (h_err != 0 || h_p != P || h_b != B || h_hkv != Hkv || ndesc < 0 || ndesc > cap) return;
+    if (h_err != 0 || h_p != P || h_b != B || h_hkv != Hkv || ndesc < 0 || ndesc > cap || NQ < 0 || NQ > nq_max) {
+        // a map built for another shape or from invalid lengths: every output
+        // row is NaN (packed rows of all heads, spread over the workgroups)
+        const float nan = __builtin_nanf("");
+        const size_t n4 = (size_t)a.total_q * a.Hq * (kHeadDim / 4);
+        for (size_t i = (size_t)blockIdx.x * kSplitThreads + threadIdx.x; i < n4; i += (size_t)gridDim.x * kSplitThreads)
+            store_bf16x4(a.out + 4 * i, f32x4{nan, nan, nan, nan});
+        return;
+    }
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const auto* descs = uniform_ptr<int32_t>(map + ML.desc);
     const auto* dslot = uniform_ptr<int32_t>(map + ML.desc_slot);
     const auto* order = uniform_ptr<int32_t>(map + ML.claim_order);
+    const auto* qbase = uniform_ptr<int32_t>(map + ML.qbase);
+    const auto* snc = uniform_ptr<int32_t>(map + ML.seg_num_chunks);
+    const auto* sslot0 = uniform_ptr<int32_t>(map + ML.seg_slot0);
+    int32_t* const arrive = a.counters + kVarlenGroups;
     const auto* ptab = uniform_ptr<int32_t>(a.page_table);
 
     // ---- claims: group gx's descriptors are [lo, hi), claim i takes order[lo + i]
@@ -534,93 +604,29 @@ __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8
                     }
                 }
             }
+            if (!whole) {
+                // the segment's chunk count and first slot (s = h * NQ + its block)
+                const int u = qbase[b] + k;
+                const int sg = h * NQ + (u >= 0 && u < NQ ? u : 0);
+                const int n = snc[sg], slot0 = sslot0[sg];
+                const bool seg_ok = u >= 0 && u < NQ && n >= 2 && slot0 >= 0 && (slot0 >> 1) + n <= P;
+                // every wave's partial stores are done before thread 0 counts the
+                // chunk in; the acquire-release add publishes them at device scope
+                // and, for the last arrival, makes the other chunks visible
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    arrive_lds = seg_ok ? __hip_atomic_fetch_add(arrive + (slot0 >> 1), 1, __ATOMIC_ACQ_REL,
+                                                                 __HIP_MEMORY_SCOPE_AGENT)
+                                        : -1;
+                __syncthreads();
+                if (seg_ok && __builtin_amdgcn_readfirstlane(arrive_lds) == n - 1) {
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    merge_cut_segment(a, slot0, n, a.out + ((size_t)(qs + kQBlock * k) * a.Hq + (size_t)h * kGroup) * kHeadDim,
+                                      blk.live);
+                }
+            }
         }
         d = claim_take(v_next);   // its barriers also keep the ring until every wave is done with it
-    }
-}
-
-// The chunks of cut segments, merged: workgroup (h, u) takes segment
-// s = h * NQ + u (query block u of KV head h) when it has two or more chunks.
-// Chunk c sits in slot slot0 (c = 0) or 2 (bin of chunk 0 + c): a cut
-// segment's chunks lie in consecutive bins, each after the first starting its
-// bin.  256 threads: 8 rows at a time (row p * 8 + g of the block), 32 threads
-// x 4 dims per row; the loads of up to 8 chunks are issued before the merge.
-constexpr int kVarlenCombineUnroll = 8;
-
-__global__ __launch_bounds__(kCombineThreads) void varlen_combine_kernel(const uint8_t* map, int B, int Hkv, int P,
-                                                                         int nq_max, VarlenArgs a) {
-    const VarlenMapLayout ML = varlen_map_layout(B, Hkv, P, nq_max);
-    const int h = (int)(blockIdx.x / (unsigned)nq_max), u = (int)(blockIdx.x % (unsigned)nq_max);
-    const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
-    const int h_err = hdr[LBSA_HDR_ERROR], h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
-    const int NQ = hdr[14];
-    const int tid = threadIdx.x, d4 = (tid & 31) * 4;
-    if (h_err != 0 || h_p != P || h_b != B || h_hkv != Hkv || NQ < 0 || NQ > nq_max) {
-        // a map built for another shape or from invalid lengths: every output row
-        // is NaN (packed rows u, u + nq_max, ... of the group's heads here)
-        const float nan = __builtin_nanf("");
-        for (int t = u; t < a.total_q; t += nq_max)
-            for (int gg = tid >> 5; gg < kGroup; gg += kCombineThreads / 32)
-                store_bf16x4(a.out + ((size_t)t * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + d4,
-                             f32x4{nan, nan, nan, nan});
-        return;
-    }
-    if (u >= NQ) return;
-    const int s = h * NQ + u;
-    const int sd0 = uniform_ptr<int32_t>(map + ML.seg_first_desc)[s];
-    const int n = uniform_ptr<int32_t>(map + ML.seg_num_chunks)[s];
-    const int slot0 = uniform_ptr<int32_t>(map + ML.seg_slot0)[s];
-    const int b = uniform_ptr<int32_t>(map + ML.blk_req)[u];
-    const int k = uniform_ptr<int32_t>(map + ML.blk_k)[u];
-    if (n < 2) return;                                  // one chunk: written by the split kernel
-    if (b < 0 || b >= B || slot0 < 0 || (slot0 >> 1) + n > P || sd0 < 0) return;   // corrupt map
-    const int q = uniform_ptr<int32_t>(map + ML.qlens)[b];
-    const int qs = uniform_ptr<int32_t>(map + ML.qstart)[b];
-    const int live = min(kQBlock, q - kQBlock * k);
-    if (live <= 0 || qs < 0 || qs + kQBlock * k + live > a.total_q) return;
-    const int bin0 = slot0 >> 1;
-    for (int row = tid >> 5; row < kVarlenRows; row += kCombineThreads / 32) {
-        const int p = row >> 3, gg = row & 7;
-        if (p >= live) break;                           // rows are position-major: the rest are dead too
-        float m = kNegInf, wsum = 0.f;
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        bool nan_seen = false;
-        for (int c0 = 0; c0 < n; c0 += kVarlenCombineUnroll) {
-            float l[kVarlenCombineUnroll];
-            f32x4 x[kVarlenCombineUnroll];
-#pragma unroll
-            for (int i = 0; i < kVarlenCombineUnroll; ++i) {
-                const int c = c0 + i;
-                if (c < n) {
-                    const size_t pr = (size_t)(c == 0 ? slot0 : 2 * (bin0 + c)) * kVarlenRows + row;
-                    l[i] = a.part_lse[pr];
-                    x[i] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kHeadDim + d4);
-                } else {
-                    l[i] = kNegInf;
-                    x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < kVarlenCombineUnroll; ++i) {
-                if (l[i] != l[i]) { nan_seen = true; continue; }
-                if (l[i] == kNegInf) continue;
-                if (l[i] > m) {
-                    const float sc = exp2_fast((m - l[i]) * kLog2e);   // 0 when m = -inf
-                    wsum *= sc;
-                    o *= sc;
-                    m = l[i];
-                }
-                const float wgt = exp2_fast((l[i] - m) * kLog2e);
-                wsum += wgt;
-                o += wgt * x[i];
-            }
-        }
-        o *= wsum > 0.f ? 1.f / wsum : 0.f;
-        if (nan_seen) {
-            const float nan = __builtin_nanf("");
-            o = f32x4{nan, nan, nan, nan};
-        }
-        store_bf16x4(a.out + ((size_t)(qs + kQBlock * k + p) * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + d4, o);
     }
 }
 
@@ -654,15 +660,13 @@ hipError_t launch_varlen(const void* q, const void* k_cache, const void* v_cache
     a.scale_log2 = scale_log2;
     const uint8_t* m = static_cast<const uint8_t*>(map);
     // the counter reset stays outside the kernel timing hook, which stamps
-    // the split and combine kernels
-    hipLaunchKernelGGL(varlen_reset_kernel, dim3(1), dim3(64), 0, stream, counters);
+    // the split kernel
+    const int words = kVarlenGroups + P;
+    const int blocks = min((words + 255) / 256, 64);
+    hipLaunchKernelGGL(varlen_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, counters, words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch(varlen_split_kernel, dim3((unsigned)workgroups), dim3(kSplitThreads), 0, stream, m, B, Hkv, P,
-               (int)nq_max, a);
-    if (e != hipSuccess) return e;
-    const long long grid = (long long)nq_max * Hkv;
-    return launch(varlen_combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, m, B, Hkv, P,
+    return launch(varlen_split_kernel, dim3((unsigned)workgroups), dim3(kSplitThreads), 0, stream, m, B, Hkv, P,
                   (int)nq_max, a);
 }
 

@@ -206,7 +206,7 @@ def test_timing_hook_arms_and_disarms_without_a_gpu():
 def test_varlen_map_layout_and_workspace():
     """Query-block maps: 32-byte descriptors for Hkv * (B + total_q / 16) + P
     slots, their partial-slot words and claim order, every array after them; the workspace:
-    256 bytes of claim counters, then 2 P partial slots of 128 rows."""
+    8 claim and P arrival counters, then 2 P partial slots of 128 rows."""
     for B, Hkv, P, tq in [(2, 1, 4, 21), (64, 8, 512, 8255), (1, 8, 512, 8192)]:
         lay = lbsa.varlen_task_map_layout(B, Hkv, P, tq)
         nq = B + tq // 16
@@ -223,8 +223,10 @@ def test_varlen_map_layout_and_workspace():
         assert lay["seqlens"] == lay["qstart"] + 4 * (B + 1) and lay["qlens"] == lay["seqlens"] + 4 * B
         assert lay["total"] >= lay["qlens"] + 4 * B and lay["total"] % 256 == 0
         assert lbsa.varlen_task_map_bytes(B, Hkv, P, tq) == lay["total"]
-    ws = lbsa.varlen_workspace_bytes(64, 8, 512)
-    assert ws >= 256 + 2 * 512 * 128 * (128 + 1) * 4 and ws < 2 * 512 * 128 * (128 + 1) * 4 + 768
+    for P in (1, 512, 1000):
+        counters = -(-4 * (8 + P) // 256) * 256            # 8 claim + P arrival counters, 256-aligned
+        lse = -(-2 * P * 128 * 4 // 256) * 256
+        assert lbsa.varlen_workspace_bytes(64, 8, P) == counters + lse + 2 * P * 128 * 128 * 4
 
 
 def test_varlen_host_argument_errors():

@@ -50,13 +50,20 @@ def expected_extras(o, sl, ql, P):
         return 2 * j + (0 if bdb[j] == d else 1)
     slot0 = [slot_of(d0) for d0 in o["seg_first_desc"]]
     desc_slot = [slot_of(d) for d in range(len(o["desc"]))]
-    # claim order: 8 groups of consecutive bins, each by decreasing tile count
-    # (1023 and more tie), equal counts by decreasing descriptor index
+    # claim order: 8 groups of consecutive bins, each by decreasing length
+    # class (the tile count below 8, then four classes per power of two: the
+    # octave and the two bits below its leading one), equal classes by
+    # decreasing descriptor index
+    def length_class(d):
+        n = int(o["desc"][d][4] - o["desc"][d][3])
+        if n < 8:
+            return n
+        e = n.bit_length() - 1
+        return min(8 + 4 * (e - 3) + ((n >> (e - 2)) & 3), 63)
     order = []
     for x in range(8):
         lo, hi = int(bdb[x * P // 8]), int(bdb[(x + 1) * P // 8])
-        length = lambda d: min(int(o["desc"][d][4] - o["desc"][d][3]), 1023)
-        order += sorted(range(lo, hi), key=lambda d: (-length(d), -d))
+        order += sorted(range(lo, hi), key=lambda d: (-length_class(d), -d))
     blk_req = np.repeat(np.arange(len(ql)), nq).astype(np.int32)
     blk_k = np.concatenate([np.arange(n) for n in nq]).astype(np.int32)
     return dict(qbase=qbase, qstart=qstart, slot0=np.asarray(slot0, np.int32), blk_req=blk_req, blk_k=blk_k,
@@ -168,6 +175,43 @@ def test_small_mixes_full_parity(oracle_mod, name, P, F):
     out = attend(b, tm, P)
     ref, _ = oracle_mod.attention_varlen(b)
     H.check(b, H.out_np(out), ref, f"{name} P={P} F={F} (cut segments: {int((m['seg_num_chunks'] > 1).sum())})")
+
+
+def test_many_chunk_segments_merged_in_the_split_kernel(oracle_mod):
+    """A decode row of 128 tiles spread over dozens of bins (more chunks than
+    the merge loads at once) beside a prefill cut at many bin edges: every
+    row against the oracle."""
+    b = varlen_batch([8192, 100, 3000], [1, 100, 40], Hq=8, Hkv=1, seed=74)
+    P = 64
+    tm = plan(b, P, 1)
+    m = lbsa.read_varlen_task_map(tm, b["B"], 1, P, b["total_q"])
+    assert m["seg_num_chunks"].max() > 16 and (m["seg_num_chunks"] > 1).sum() >= 4
+    out = attend(b, tm, P)
+    ref, _ = oracle_mod.attention_varlen(b)
+    H.check(b, H.out_np(out), ref, f"many-chunk segments (max {int(m['seg_num_chunks'].max())} chunks)")
+
+
+def test_repeated_calls_on_one_workspace_are_bit_identical(oracle_mod):
+    """The counters are cleared by every call, and the result does not depend on
+    which workgroup claims which descriptor: three calls on one workspace, with
+    another map's call in between, give the same bits."""
+    b = varlen_batch([2000, 777, 129, 4000], [1500, 700, 16, 1], Hq=16, Hkv=2, seed=75)
+    P = 100
+    tm = plan(b, P, 1)
+    ws = torch.empty(lbsa.varlen_workspace_bytes(16, 2, P), dtype=torch.uint8, device="cuda:0")
+    run = lambda: lbsa.attend_varlen(b["q"], b["k_cache"], b["v_cache"], b["page_table"], tm, P, b["softmax_scale"],
+                                     b["B"], workspace=ws)
+    first = run().clone()
+    second = run().clone()
+    other = varlen_batch([300, 64], [30, 64], Hq=16, Hkv=2, seed=76)
+    lbsa.attend_varlen(other["q"], other["k_cache"], other["v_cache"], other["page_table"], plan(other, P), P,
+                       other["softmax_scale"], other["B"], workspace=ws)
+    third = run().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), second.view(torch.int16))
+    assert torch.equal(first.view(torch.int16), third.view(torch.int16))
+    ref, _ = oracle_mod.attention_varlen(b)
+    H.check(b, H.out_np(first), ref, "repeated calls")
 
 
 def test_decode_rows_match_the_decode_path(oracle_mod):
