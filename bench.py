@@ -557,9 +557,9 @@ def varlen_bench(args):
             if nd:
                 dpath.assign()
             grid_layer()
-        t = _timed_alternating({"map_layer": vattend, "grid_layer": grid_layer, "map_step": lambda: (vplan(), vattend()),
-                                "grid_step": grid_step, "map_stamped": vattend_stamped},
-                               args.steps, max(args.warmup, 10), flush)
+        runs = {"map_layer": vattend, "grid_layer": grid_layer, "map_step": lambda: (vplan(), vattend()),
+                "grid_step": grid_step, "map_stamped": vattend_stamped}
+        t = _timed_alternating(runs, args.steps, max(args.warmup, 10), flush)
         torch.cuda.synchronize()
         layer, step, g_layer, g_step = t["map_layer"], t["map_step"], t["grid_layer"], t["grid_step"]
         split_k = statistics.fmean(1000.0 * x.elapsed_time(y) for x, y in stamps[-args.steps:])

@@ -503,7 +503,8 @@ __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8
         // row is NaN (packed rows of all heads, spread over the workgroups)
         const float nan = __builtin_nanf("");
         const size_t n4 = (size_t)a.total_q * a.Hq * (kHeadDim / 4);
-        for (size_t i = (size_t)blockIdx.x * kSplitThreads + threadIdx.x; i < n4; i += (size_t)gridDim.x * kSplitThreads)
+        const size_t stride = (size_t)gridDim.x * kSplitThreads;
+        for (size_t i = (size_t)blockIdx.x * kSplitThreads + threadIdx.x; i < n4; i += stride)
             store_bf16x4(a.out + 4 * i, f32x4{nan, nan, nan, nan});
         return;
     }
@@ -621,8 +622,8 @@ __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8
                 __syncthreads();
                 if (seg_ok && __builtin_amdgcn_readfirstlane(arrive_lds) == n - 1) {
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                    merge_cut_segment(a, slot0, n, a.out + ((size_t)(qs + kQBlock * k) * a.Hq + (size_t)h * kGroup) * kHeadDim,
-                                      blk.live);
+                    uint16_t* rows = a.out + ((size_t)(qs + kQBlock * k) * a.Hq + (size_t)h * kGroup) * kHeadDim;
+                    merge_cut_segment(a, slot0, n, rows, blk.live);
                 }
             }
         }

@@ -40,8 +40,8 @@ class _MapLayout(ctypes.Structure):
 
 class _VarlenMapLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("header", "bin_desc_begin", "desc", "desc_slot", "claim_order", "seg_first_desc", "seg_num_chunks", "seg_slot0", "blk_req",
-                 "blk_k", "qbase", "qstart", "seqlens", "qlens", "total")]
+                ("header", "bin_desc_begin", "desc", "desc_slot", "claim_order", "seg_first_desc", "seg_num_chunks",
+                 "seg_slot0", "blk_req", "blk_k", "qbase", "qstart", "seqlens", "qlens", "total")]
 
 
 class _WsLayout(ctypes.Structure):
