@@ -38,3 +38,39 @@ def test_graph_replays_match_eager(kv):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+
+
+def test_varlen_graph_replays_match_eager():
+    """Prefill / extend / decode rows on the task map: plan_varlen + attend_varlen
+    (the counter-clearing kernel, the split kernel with its in-kernel merges)
+    captured once; before every replay the workspace is filled with garbage,
+    so the claim and arrival counters must be cleared inside the graph."""
+    from load_balanced_split_assign_amd import workload as wl
+    sl, ql = [2000, 777, 129, 4000], [1500, 700, 16, 1]
+    b = wl.make_batch(seqlens=sl, qlens=ql, num_heads=16, num_kv_heads=2, kv_dtype="bf16", seed=42, device="cpu")
+    b = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
+    tq, P = sum(ql), 100
+    tm = torch.empty(lbsa.varlen_task_map_bytes(b["B"], 2, P, tq), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(lbsa.varlen_workspace_bytes(16, 2, P), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(b["q"])
+
+    def step():
+        lbsa.plan_varlen(b["seqlens"], b["qlens"], 16, 2, b["max_pages"], P, 1, total_q=tq, task_map=tm)
+        lbsa.attend_varlen(b["q"], b["k_cache"], b["v_cache"], b["page_table"], tm, P, b["softmax_scale"], b["B"],
+                           workspace=ws, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    m = lbsa.read_varlen_task_map(tm, b["B"], 2, P, tq)
+    assert (m["seg_num_chunks"] > 1).sum() >= 2            # the merges run inside the graph too
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
