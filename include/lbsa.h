@@ -344,7 +344,9 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
  * (MFMA, K/V through LDS), writing the bf16 rows of a segment it holds whole
  * and a partial otherwise; the workgroup that writes a cut segment's last
  * chunk merges its chunks into the output rows.  Calls that share a workspace
- * must not overlap.
+ * must not overlap.  The first lbsa_plan_varlen call in a process sets the assign
+ * kernel's dynamic-LDS limit (a kernel attribute): make it before capturing the
+ * calls in a graph.
  * Errors: shapes as lbsa_plan and lbsa_prefill (bf16 only); maps larger than
  * one assign workgroup's LDS (about 16K segments) give LBSA_ERR_UNSUPPORTED.
  * A length or q out of range on the device sets the error word: every output
