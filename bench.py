@@ -486,6 +486,12 @@ def _timed_alternating(runs, steps, warmup, flush):
 
 
 def varlen_bench(args):
+    """The --varlen mode: varlen_rows with the command line's steps, warm-up, flush and P."""
+    rows = varlen_rows(args.steps, args.warmup, make_flush(args.flush), args.workgroups)
+    print(json.dumps({"varlen": rows, "unit": "us", "flush": args.flush}), flush=True)
+
+
+def varlen_rows(steps, warmup, flush, P_arg=0):
     """Prefill / extend and decode rows on one task map (query-block segments)
     against the grid path: lbsa_prefill for the requests with new tokens and the
     decode task map for the decode rows.  Workloads: the mixed batch (one 8K
@@ -500,7 +506,6 @@ def varlen_bench(args):
 
     from load_balanced_split_assign_amd import lbsa
     from load_balanced_split_assign_amd import workload as wl
-    flush = make_flush(args.flush)
     rows = []
     cases = {"mixed_extend": dict(wl.MIXED_EXTEND),
              "q8k_prefill": dict(wl.MIXED_EXTEND, extend_len=8192, extend_q=8192, decode_rows=0)}
@@ -510,7 +515,7 @@ def varlen_bench(args):
                           tail="normal", device="cuda:0")
         tq = int(sum(ql))
         B, mp = b["B"], b["max_pages"]
-        P = args.workgroups or lbsa.varlen_default_workgroups(0)
+        P = P_arg or lbsa.varlen_default_workgroups(0)
         tm = torch.empty(lbsa.varlen_task_map_bytes(B, 8, P, tq), dtype=torch.uint8, device="cuda:0")
         ws = torch.empty(lbsa.varlen_workspace_bytes(64, 8, P), dtype=torch.uint8, device="cuda:0")
         out = torch.empty_like(b["q"])
@@ -559,10 +564,10 @@ def varlen_bench(args):
             grid_layer()
         runs = {"map_layer": vattend, "grid_layer": grid_layer, "map_step": lambda: (vplan(), vattend()),
                 "grid_step": grid_step, "map_stamped": vattend_stamped}
-        t = _timed_alternating(runs, args.steps, max(args.warmup, 10), flush)
+        t = _timed_alternating(runs, steps, max(warmup, 10), flush)
         torch.cuda.synchronize()
         layer, step, g_layer, g_step = t["map_layer"], t["map_step"], t["grid_layer"], t["grid_step"]
-        split_k = statistics.fmean(1000.0 * x.elapsed_time(y) for x, y in stamps[-args.steps:])
+        split_k = statistics.fmean(1000.0 * x.elapsed_time(y) for x, y in stamps[-steps:])
         flops = causal_flops(1, eq, sl[0], 64) + sum(4 * 64 * 128 * L for L in sl[1:])
         rows.append({"workload": name, "batch": B, "total_q": tq, "extend": {"L": sl[0], "q": eq},
                      "decode_rows": nd, "P": P, "T": m["T"], "K": m["K"], "Ndesc": m["Ndesc"],
@@ -579,7 +584,7 @@ def varlen_bench(args):
         if nd:
             del dpath, dec
         torch.cuda.empty_cache()
-    print(json.dumps({"varlen": rows, "unit": "us", "flush": args.flush}), flush=True)
+    return rows
 
 
 ROUTER_M = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
@@ -880,6 +885,7 @@ def main():
                     help="time the headline workload alone (no other configs, static sweep or CPU baseline)")
     ap.add_argument("--workgroups", type=int, default=0, help="persistent workgroups (0 = CUs x occupancy)")
     ap.add_argument("--no-static", action="store_true", help="skip the static split-KV comparison")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the prefill-on-map block of the default line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
                     help="cache eviction before each timed step")
@@ -996,6 +1002,11 @@ def main():
             del b2, p2
             torch.cuda.empty_cache()
         rec["configs"] = configs
+
+    if not args.no_varlen and not args.only:
+        # prefill / extend and decode rows on one task map against the grid path
+        # (the --varlen mode's measurement, fewer rounds)
+        rec["prefill_on_map"] = {"unit": "us", "rows": varlen_rows(min(args.steps, 20), 10, flush)}
 
     if not args.no_static and not args.only:
         sk = gpu_batch("skewed")
