@@ -476,7 +476,7 @@ static int varlen_shape(int32_t batch, int32_t num_kv_heads, int32_t P, int64_t 
     if (total_q > (1 << 24) || P >= (1 << 24)) return LBSA_ERR_UNSUPPORTED;
     // the single assign workgroup keeps every prefix in LDS
     if (varlen_assign_lds_words(batch, num_kv_heads, varlen_max_blocks(batch, total_q)) >
-        (size_t)kMaxAssignLdsWords + kVarlenClaimHistWords)
+        (size_t)kMaxVarlenAssignLdsWords)
         return LBSA_ERR_UNSUPPORTED;
     return LBSA_OK;
 }

@@ -509,14 +509,14 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
 hipError_t launch_assign_varlen(const int32_t* seqlens, const int32_t* qlens, int B, int Hq, int Hkv, int P, int F,
                                 int max_pages, int64_t total_q, int64_t nq_max, void* map, hipStream_t stream) {
     const size_t lds = sizeof(int) * varlen_assign_lds_words(B, Hkv, nq_max);
-    // the prefixes may take 64 KiB and the claim-order histogram comes on top:
-    // allow the kernel gfx950's larger LDS once per process
+    // the prefixes and the histogram take up to 152 KiB: allow the kernel
+    // gfx950's larger LDS once per process
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
         attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&assign_varlen_kernel),
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)(sizeof(int) * ((size_t)kMaxAssignLdsWords + kVarlenClaimHistWords)));
+                                   (int)(sizeof(int) * (size_t)kMaxVarlenAssignLdsWords));
     });
     if (attr != hipSuccess) return attr;
     return launch(assign_varlen_kernel, dim3(1), dim3(kAssignThreads), (uint32_t)lds, stream, seqlens, qlens, B, Hq,

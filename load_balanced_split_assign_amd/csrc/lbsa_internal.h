@@ -130,6 +130,9 @@ __host__ __device__ inline size_t varlen_counter_bytes(int P) { return align_up(
 // prefixes, the tile prefix over query blocks, the chunk prefix over
 // segments and the claim-order histogram.
 constexpr int kVarlenClaimHistWords = 2048;
+// The varlen assign runs in one workgroup with every prefix in LDS: up to
+// 144 KiB of prefixes plus the histogram (gfx950 gives a workgroup 160 KiB).
+constexpr int kMaxVarlenAssignLdsWords = 36864 + kVarlenClaimHistWords;
 __host__ __device__ inline size_t varlen_assign_lds_words(int B, int Hkv, int64_t NQ) {
     return 4 * (size_t)B + 2 + ((size_t)NQ + 1) + ((size_t)Hkv * NQ + 1) + kVarlenClaimHistWords;
 }
