@@ -348,8 +348,8 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
  * kernel's dynamic-LDS limit (a kernel attribute): make it before capturing the
  * calls in a graph.
  * Errors: shapes as lbsa_plan and lbsa_prefill (bf16 only); maps larger than
- * one assign workgroup's LDS give LBSA_ERR_UNSUPPORTED: 4 B + 9 NQ words over
- * 36 864 with 8 KV heads (NQ = batch + total_q / 16), about 60K query tokens.
+ * one assign workgroup's LDS give LBSA_ERR_UNSUPPORTED: 4 B + 10 NQ words over
+ * 36 864 with 8 KV heads (NQ = batch + total_q / 16), about 58K query tokens.
  * A length or q out of range on the device sets the error word: every output
  * row is then NaN.  Default P (bins): lbsa_varlen_default_workgroups.
  */

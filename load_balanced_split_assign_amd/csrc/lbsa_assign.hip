@@ -297,6 +297,8 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
     int* qstart = qbase + B + 1;       // [B + 1] exclusive prefix of q_b (packed query rows)
     int* tpre = qstart + B + 1;        // [nq_max + 1] exclusive prefix of the blocks' tiles
     int* sfd = tpre + nq_max + 1;      // [Hkv * nq_max + 1] exclusive prefix of chunks(s)
+    int* hist = sfd + (size_t)Hkv * nq_max + 1;        // [kClaimKeys][kWaveQuarters] claim-order histogram
+    int* blkreq = hist + kClaimKeys * kWaveQuarters;   // [nq_max] request of each query block
     const int tid = threadIdx.x;
 
     // ---- lengths, validation, query blocks and packed rows per request -----
@@ -344,6 +346,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
         const int b = upper_bound(qbase, B, u) - 1;
         const int k = u - qbase[b];
         breq_g[u] = b;
+        blkreq[u] = b;
         bk_g[u] = k;
         const int seen = lens[b] - qls[b] + min(qls[b], kQBlock * (k + 1));
         const int nt = (seen + kTile - 1) / kTile;
@@ -394,7 +397,6 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
     if (tid == 0) sfd[S] = ndesc;
     // claim-order histogram: per sort key and per wave's quarter of the
     // descriptors (the quarters in decreasing index order: wave 0 the highest)
-    int* hist = sfd + (size_t)Hkv * nq_max + 1;        // [kClaimKeys][kWaveQuarters], after sfd's words
     for (int i = tid; i < kClaimKeys * kWaveQuarters; i += kAssignThreads) hist[i] = 0;
     const int quarter = (ndesc + kWaveQuarters - 1) / kWaveQuarters;
     __syncthreads();
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
         sfd_g[s] = d0;
         snc_g[s] = nc;
         slot0_g[s] = 2 * j0 + (n && a != bins.start(j0) ? 1 : 0);
-        const int b = upper_bound(qbase, B, u) - 1;
+        const int b = blkreq[u];
         const int k = u - qbase[b], L = lens[b], q = qls[b], qs = qstart[b];
         for (int c = 0; c < nc; ++c) {
             const int j = j0 + c, d = d0 + c;
@@ -455,14 +457,24 @@ __global__ __launch_bounds__(kAssignThreads) void assign_varlen_kernel(
         const int lane = tid & 63, wv = tid >> 6;
         const uint64_t lt_mask = (1ull << lane) - 1;
         const int top = ndesc - 1 - wv * quarter, bottom = max(ndesc - (wv + 1) * quarter, 0);
+        // the next 64 descriptors' tile range and slot are loaded while these are placed
+        int n_t0 = 0, n_t1 = 0, n_slot = 0;
+        auto fetch = [&](int c) {
+            const int dd = c - lane;
+            if (dd >= bottom) {
+                const int32_t* rec = desc + (size_t)kVarlenDescWords * dd;
+                n_t0 = rec[VD_T0];
+                n_t1 = rec[VD_T1];
+                n_slot = dslot[dd];
+            }
+        };
+        fetch(top);
         for (int c0 = top; c0 >= bottom; c0 -= 64) {
+            const int t0v = n_t0, t1v = n_t1, slv = n_slot;
+            fetch(c0 - 64);
             const int d = c0 - lane;
             const bool valid = d >= bottom;
-            int key = -1;
-            if (valid) {
-                const int32_t* rec = desc + (size_t)kVarlenDescWords * d;
-                key = claim_key(group_of_bin(dslot[d] >> 1, P), rec[VD_T1] - rec[VD_T0]);
-            }
+            const int key = valid ? claim_key(group_of_bin(slv >> 1, P), t1v - t0v) : -1;
             int rank = 0, count = 0;
             uint64_t pending = __builtin_amdgcn_ballot_w64(valid);
             while (pending) {

@@ -128,13 +128,13 @@ __host__ __device__ inline size_t varlen_counter_bytes(int P) { return align_up(
 
 // LDS words the varlen assign kernel needs: lengths, q lengths, their two
 // prefixes, the tile prefix over query blocks, the chunk prefix over
-// segments and the claim-order histogram.
+// segments, the claim-order histogram and each query block's request.
 constexpr int kVarlenClaimHistWords = 2048;
 // The varlen assign runs in one workgroup with every prefix in LDS: up to
 // 144 KiB of prefixes plus the histogram (gfx950 gives a workgroup 160 KiB).
 constexpr int kMaxVarlenAssignLdsWords = 36864 + kVarlenClaimHistWords;
 __host__ __device__ inline size_t varlen_assign_lds_words(int B, int Hkv, int64_t NQ) {
-    return 4 * (size_t)B + 2 + ((size_t)NQ + 1) + ((size_t)Hkv * NQ + 1) + kVarlenClaimHistWords;
+    return 4 * (size_t)B + 2 + ((size_t)NQ + 1) + ((size_t)Hkv * NQ + 1) + kVarlenClaimHistWords + (size_t)NQ;
 }
 
 // Byte offsets of the partial buffers for `slots` partials of (q_len x G) x D
