@@ -108,6 +108,14 @@ class Path:
                                  out=self.out, q_len=self.q_len)
 
 
+def auto_P(batch, q_len=None):
+    """lbsa_auto_workgroups for a batch built on this host (its lengths are known here)."""
+    from load_balanced_split_assign_amd import lbsa
+    sl = [int(x) for x in batch["seqlens"].cpu()]
+    kv = batch.get("kv_dtype") or ("fp8" if batch.get("k_scale") is not None else "bf16")
+    return lbsa.auto_workgroups(sl, batch["num_kv_heads"], kv, q_len or batch.get("q_len", 1) or 1)
+
+
 def make_flush(mode):
     """Evicts K/V of the previous step from L2 and the Infinity Cache.  'read'
     streams a 512 MiB buffer through a reduction (the caches are left holding
@@ -211,7 +219,7 @@ def graph_bench(args):
     rows = []
     for name in ("tp8_share", "t3_64x0.5K", "skewed"):
         b = gpu_batch(name)
-        path = Path(b, lbsa.default_workgroups(0, b["kv_dtype"]))
+        path = Path(b, auto_P(b))
         eager = summarize(time_steps(path, args.steps, args.warmup, flush)["step"])["median"]
         graph = summarize(time_steps_graph(path, args.steps, args.warmup, flush))["median"]
         rows.append({"workload": name, "eager_step_us": round(eager, 2), "graph_step_us": round(graph, 2)})
@@ -312,7 +320,7 @@ def table3(args):
     for name in wl.TABLE3:
         b = gpu_batch(name)
         w = wl.WORKLOADS[name]
-        P = args.workgroups or lbsa.default_workgroups(0, w.kv_dtype)
+        P = args.workgroups or auto_P(b)
         sl = [int(x) for x in b["seqlens"].cpu()]
         ab = alg_bytes(sl, b["num_heads"], b["num_kv_heads"], 128, w.kv_dtype)
         path = Path(b, P)
@@ -354,7 +362,7 @@ def mtp_bench(args):
         w = wl.WORKLOADS[name]
         row = {"workload": name, "kv_dtype": w.kv_dtype, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads}
         for ql in (1, 2):
-            P = args.workgroups or w.num_workgroups or lbsa.default_workgroups(0, w.kv_dtype, ql)
+            P = args.workgroups or w.num_workgroups or auto_P(b, ql)
             row[f"q{ql}_P"] = P
             b = wl.make_batch(name, tail="normal", device="cuda:0", q_len=ql)
             sl = [int(x) for x in b["seqlens"].cpu()]
@@ -403,7 +411,7 @@ def table4(args):
         row = {"shape": name, "kind": kind, "batch": B, "q_len": QL, "kv_len": L,
                "pages_h20_ms": TABLE4_H20_MS[name]}
         if kind == "decode":
-            P = args.workgroups or lbsa.default_workgroups(0, "bf16")
+            P = args.workgroups or auto_P(b)
             path = Path(b, P)
             t = time_layer(path, args.steps, args.warmup, flush, with_assign=True)["mean"]
             ab = alg_bytes([L] * B, 64, 8, 128, "bf16")
@@ -550,7 +558,7 @@ def varlen_rows(steps, warmup, flush, P_arg=0):
                    "k_scale": None, "v_scale": None, "q_scale": None, "page_table": b["page_table"][1:].contiguous(),
                    "seqlens": b["seqlens"][1:].contiguous(), "num_heads": 64, "num_kv_heads": 8, "B": nd,
                    "max_pages": mp, "softmax_scale": b["softmax_scale"], "q_len": 1}
-            dpath = Path(dec, lbsa.default_workgroups(0, "bf16"))
+            dpath = Path(dec, auto_P(dec))
             dpath.assign()
 
         def grid_layer():
@@ -804,13 +812,13 @@ def _load_traffic():
     return rec.get("workloads", {})
 
 
-def write_traffic(fetch_dir, write_dir, workload):
+def write_traffic(fetch_dir, write_dir, workload, P):
     """HBM bytes per split launch on `workload` = FETCH_SIZE + WRITE_SIZE of the
     split kernel, each scaled by CALIB_BYTES / what the same counter reads for
     the calibration copy (the first device-to-device copy dispatch of a
     --calib-copy run).  The file keeps one entry per workload, each stamped with
-    the kernel source it was taken on."""
-    rec = {"source_sha256": source_sha(SPLIT_SRC), "kernel": "split_kernel", "workload": workload,
+    the kernel source it was taken on and the number of bins P of that run."""
+    rec = {"source_sha256": source_sha(SPLIT_SRC), "kernel": "split_kernel", "workload": workload, "P": P,
            "calib_bytes": CALIB_BYTES}
     total = 0.0
     for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
@@ -833,11 +841,12 @@ def write_traffic(fetch_dir, write_dir, workload):
     print(json.dumps(rec))
 
 
-def traffic_from_profile(workload):
+def traffic_from_profile(workload, P):
     """HBM bytes per split launch from committed PMC counters, if they were taken
-    on the current kernel source and on this workload (else None)."""
+    on the current kernel source, on this workload and with the same number of
+    bins (else None)."""
     rec = _load_traffic().get(workload)
-    if not rec or rec.get("source_sha256") != source_sha(SPLIT_SRC):
+    if not rec or rec.get("source_sha256") != source_sha(SPLIT_SRC) or rec.get("P") != P:
         return None
     return rec.get("bytes_per_launch")
 
@@ -848,7 +857,7 @@ def measure_workload(name, steps, warmup, flush, workgroups=0):
     from load_balanced_split_assign_amd import workload as wl
     w = wl.WORKLOADS[name]
     batch = gpu_batch(name)
-    P = workgroups or w.num_workgroups or lbsa.default_workgroups(0, w.kv_dtype)
+    P = workgroups or w.num_workgroups or auto_P(batch)
     sl = [int(x) for x in batch["seqlens"].cpu()]
     ab = alg_bytes(sl, batch["num_heads"], batch["num_kv_heads"], 128, w.kv_dtype)
     path = Path(batch, P)
@@ -912,7 +921,9 @@ def main():
                          "--calib-copy) into the split kernel's HBM bytes per launch")
     args = ap.parse_args()
     if args.traffic_from:
-        write_traffic(*args.traffic_from, args.workload)
+        if not args.workgroups:
+            ap.error("--traffic-from needs --workgroups: the P of the profiled run")
+        write_traffic(*args.traffic_from, args.workload, args.workgroups)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path needs no collectives; "
@@ -982,7 +993,7 @@ def main():
         "partial_bytes": head["partial_bytes"],
         "roofline": {"kernel": "split_kernel", "bound": "hbm", "achieved": round(split_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(name), "alg_bytes_per_launch": ab["split"],
+                     "traffic": traffic_from_profile(name, P), "alg_bytes_per_launch": ab["split"],
                      "avg_launch_us": round(split_us, 3), "workload": name,
                      "timing": "kernel start/end events (hipExtLaunchKernel), live in this run"},
     }
@@ -1010,11 +1021,12 @@ def main():
 
     if not args.no_static and not args.only:
         sk = gpu_batch("skewed")
-        Pk = lbsa.default_workgroups(0, "bf16")
-        dyn = time_layer(Path(sk, Pk), 20, 3, flush)
+        Pk = lbsa.default_workgroups(0, "bf16")            # the heuristic S is defined on the resident count
+        Pd = auto_P(sk)
+        dyn = time_layer(Path(sk, Pd), 20, 3, flush)
         heur, heur_t, best_S, sweep = static_sweep(sk, Pk, 10, 2, flush)
         rec["static_baseline"] = {
-            "workload": "skewed", "P": Pk, "dynamic_layer_us": round(dyn["mean"], 2),
+            "workload": "skewed", "P": Pd, "P_resident": Pk, "dynamic_layer_us": round(dyn["mean"], 2),
             "static_heuristic_S": heur, "static_heuristic_us": round(heur_t, 2),
             "static_best_S": best_S, "static_best_us": round(sweep[best_S], 2),
             "static_sweep_us": {str(k): round(v, 2) for k, v in sweep.items()},

@@ -151,6 +151,20 @@ int lbsa_time_next_kernel(void* start_event, void* stop_event);
  * P than resident runs in waves of workgroups.  Writes *out_P. */
 int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t q_len, int32_t* out_P);
 
+/* Number of bins (P) for a batch of total_tiles = sum over KV heads and
+ * requests of ceil(L / 64), known to a serving engine on the host: twice the
+ * resident workgroups when num_kv_heads > 1 and there are at least 32 tiles
+ * per resident workgroup, else lbsa_default_workgroups.  The second wave of
+ * bins goes to the workgroups that finish first.  On MI355X equal bins do not
+ * finish together when several KV heads share the batch: a bin's speed
+ * depends on which KV head it streams (measured: 179-241 us across the 8
+ * heads of a 64-request fp8 batch, 92-111 us on the skewed bf16 batch), and
+ * with two waves those batches ran 4-6% faster; with one KV head, or a few
+ * tiles per workgroup, the extra bins' start-up cost more than they
+ * balanced.  Writes *out_P. */
+int lbsa_auto_workgroups(int device, int32_t kv_dtype, int32_t q_len, int32_t num_kv_heads, int64_t total_tiles,
+                         int32_t* out_P);
+
 /* Layout and size of the task map for (batch, num_kv_heads, P). */
 int lbsa_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32_t P,
                              lbsa_task_map_layout* out);

@@ -105,7 +105,7 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 206; }
+LBSA_API int lbsa_version(void) { return 207; }
 
 namespace {
 // Events armed for the next launches on this host thread, used in order.
@@ -170,6 +170,19 @@ LBSA_API int lbsa_default_workgroups(int device, int32_t kv_dtype, int32_t q_len
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess || per_cu <= 0 || cus <= 0) return LBSA_ERR_HIP;
     *out_P = cus * per_cu;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_auto_workgroups(int device, int32_t kv_dtype, int32_t q_len, int32_t num_kv_heads,
+                                  int64_t total_tiles, int32_t* out_P) {
+    if (!out_P || num_kv_heads <= 0 || total_tiles < 0) return LBSA_ERR_INVALID_ARGUMENT;
+    int32_t resident = 0;
+    const int s = lbsa_default_workgroups(device, kv_dtype, q_len, &resident);
+    if (s != LBSA_OK) return s;
+    // a second wave of bins when several KV heads share the batch and every
+    // resident workgroup has at least kAutoTilesPerWorkgroup tiles to stream
+    const bool two_waves = num_kv_heads > 1 && total_tiles >= (int64_t)kAutoTilesPerWorkgroup * resident;
+    *out_P = two_waves ? 2 * resident : resident;
     return LBSA_OK;
 }
 

@@ -17,6 +17,7 @@ constexpr int kSplitThreads = 256;   // 4 wave64 per split workgroup
 constexpr int kAssignThreads = 256;
 constexpr int kCombineThreads = 256;
 constexpr int kMaxAssignLdsWords = 16384;  // (B + 1) + (Hkv*B + 1) + B int32 in 64 KiB
+constexpr int kAutoTilesPerWorkgroup = 32;  // lbsa_auto_workgroups: tiles per resident workgroup for two waves
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.lbsa_status_string.restype = ctypes.c_char_p
         L.lbsa_version.restype = ctypes.c_int
         L.lbsa_default_workgroups.argtypes = [ctypes.c_int, i32, i32, ctypes.POINTER(i32)]
+        L.lbsa_auto_workgroups.argtypes = [ctypes.c_int, i32, i32, i32, i64, ctypes.POINTER(i32)]
         L.lbsa_task_map_layout_get.argtypes = [i32, i32, i32, ctypes.POINTER(_MapLayout)]
         L.lbsa_task_map_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         L.lbsa_workspace_layout_get.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(_WsLayout)]
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
         L.lbsa_time_next_kernels.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.lbsa_prologue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, f32, i32, i32, i32, i32, i32, i32,
                                     vp, vp, vp, vp, vp, vp, i64, vp]
-        for fn in ("lbsa_default_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes", "lbsa_prologue",
+        for fn in ("lbsa_default_workgroups", "lbsa_auto_workgroups", "lbsa_task_map_layout_get", "lbsa_task_map_bytes", "lbsa_prologue",
                    "lbsa_workspace_layout_get", "lbsa_workspace_bytes", "lbsa_static_workspace_bytes",
                    "lbsa_plan", "lbsa_decode", "lbsa_decode_noalloc", "lbsa_decode_split", "lbsa_decode_combine",
                    "lbsa_decode_static", "lbsa_prefill", "lbsa_router_split_weights",
@@ -162,6 +163,15 @@ def default_workgroups(device: int = 0, kv_dtype: str = "bf16", q_len: int = 1) 
     out = ctypes.c_int32()
     _check("lbsa_default_workgroups", lib().lbsa_default_workgroups(int(device), kv_dtype_code(kv_dtype),
                                                                     int(q_len), ctypes.byref(out)))
+    return int(out.value)
+
+
+def auto_workgroups(seqlens, num_kv_heads: int, kv_dtype: str = "bf16", q_len: int = 1, device: int = 0) -> int:
+    """lbsa_auto_workgroups for host-side lengths (a sequence of ints)."""
+    total_tiles = int(num_kv_heads) * sum(-(-int(x) // 64) for x in seqlens if int(x) > 0)
+    out = ctypes.c_int32()
+    _check("lbsa_auto_workgroups", lib().lbsa_auto_workgroups(int(device), kv_dtype_code(kv_dtype), int(q_len),
+                                                              int(num_kv_heads), total_tiles, ctypes.byref(out)))
     return int(out.value)
 
 

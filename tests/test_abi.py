@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 206
+    assert lbsa.lib().lbsa_version() == 207
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -185,6 +185,10 @@ def test_default_workgroups_rejects_bad_arguments_on_host():
     assert L.lbsa_default_workgroups(0, 0, 0, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT
     assert L.lbsa_default_workgroups(0, 7, 1, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT     # kv dtype
     assert L.lbsa_default_workgroups(0, 0, 1, None) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_auto_workgroups(0, 0, 1, 0, 1000, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT    # no KV head
+    assert L.lbsa_auto_workgroups(0, 0, 1, 8, -1, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT      # tiles
+    assert L.lbsa_auto_workgroups(0, 0, 3, 8, 1000, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT    # q_len
+    assert L.lbsa_auto_workgroups(0, 0, 1, 8, 1000, None) == lbsa.ERR_INVALID_ARGUMENT
 
 
 def test_timing_hook_arms_and_disarms_without_a_gpu():

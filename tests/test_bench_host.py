@@ -41,19 +41,20 @@ def test_summarize_statistics():
     assert s["p90"] == 9.0                                  # 9th of 10 sorted values
 
 
-def test_traffic_reported_only_for_its_source_and_workload(tmp_path, monkeypatch):
+def test_traffic_reported_only_for_its_source_workload_and_P(tmp_path, monkeypatch):
     ok = bench.source_sha(bench.SPLIT_SRC)
     f = tmp_path / "traffic.json"
     doc = {"kernel": "split_kernel", "workloads": {
-        "long": {"source_sha256": ok, "workload": "long", "bytes_per_launch": 123},
-        "tp8_share": {"source_sha256": "0" * 64, "workload": "tp8_share", "bytes_per_launch": 7}}}
+        "long": {"source_sha256": ok, "workload": "long", "P": 512, "bytes_per_launch": 123},
+        "tp8_share": {"source_sha256": "0" * 64, "workload": "tp8_share", "P": 256, "bytes_per_launch": 7}}}
     f.write_text(json.dumps(doc))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.traffic_from_profile("long") == 123
-    assert bench.traffic_from_profile("tp8_share") is None      # taken on another kernel source
-    assert bench.traffic_from_profile("skewed") is None         # never taken
+    assert bench.traffic_from_profile("long", 512) == 123
+    assert bench.traffic_from_profile("long", 256) is None       # taken with another number of bins
+    assert bench.traffic_from_profile("tp8_share", 256) is None  # taken on another kernel source
+    assert bench.traffic_from_profile("skewed", 256) is None     # never taken
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
-    assert bench.traffic_from_profile("long") is None
+    assert bench.traffic_from_profile("long", 512) is None
 
 
 def test_write_traffic_keeps_one_entry_per_workload(tmp_path, monkeypatch):
@@ -73,13 +74,14 @@ def test_write_traffic_keeps_one_entry_per_workload(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     calib = bench.CALIB_BYTES / 1024.0
     bench.write_traffic(run_dir("fetch", "FETCH_SIZE", 2 * calib, 1000.0),
-                        run_dir("write", "WRITE_SIZE", calib, 10.0), "long")
+                        run_dir("write", "WRITE_SIZE", calib, 10.0), "long", 512)
     doc = json.loads(f.read_text())
     assert set(doc["workloads"]) == {"tp8_share", "long"}
     e = doc["workloads"]["long"]
     assert e["fetch"]["factor"] == 0.5 and e["write"]["factor"] == 1.0
     assert e["bytes_per_launch"] == round(1000.0 * 1024 * 0.5 + 10.0 * 1024)
-    assert bench.traffic_from_profile("long") == e["bytes_per_launch"]
+    assert e["P"] == 512
+    assert bench.traffic_from_profile("long", 512) == e["bytes_per_launch"]
 
 
 def test_more_than_one_gpu_is_refused():

@@ -243,3 +243,14 @@ def test_mismatched_map_poisons_output():
     big[:tm.numel()] = tm                                          # map built for P = 16, used with P = 32
     out = H.out_np(H.decode(batch, big, 32))
     assert np.isnan(out).all()
+
+
+def test_auto_workgroups_rule():
+    """lbsa_auto_workgroups: the resident count, doubled for batches of several KV
+    heads with at least 32 tiles per resident workgroup."""
+    for kv in ("bf16", "fp8"):
+        res = lbsa.default_workgroups(0, kv)
+        assert lbsa.auto_workgroups([64 * 32] * res, 1, kv) == res                 # one KV head: never doubled
+        assert lbsa.auto_workgroups([64 * 32] * (res // 8), 8, kv) == 2 * res      # exactly 32 tiles each
+        assert lbsa.auto_workgroups([64 * 31] * (res // 8), 8, kv) == res          # 31 tiles each
+        assert lbsa.auto_workgroups([], 8, kv) == res
