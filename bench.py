@@ -362,9 +362,9 @@ def mtp_bench(args):
         w = wl.WORKLOADS[name]
         row = {"workload": name, "kv_dtype": w.kv_dtype, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads}
         for ql in (1, 2):
+            b = wl.make_batch(name, tail="normal", device="cuda:0", q_len=ql)
             P = args.workgroups or w.num_workgroups or auto_P(b, ql)
             row[f"q{ql}_P"] = P
-            b = wl.make_batch(name, tail="normal", device="cuda:0", q_len=ql)
             sl = [int(x) for x in b["seqlens"].cpu()]
             ab = alg_bytes(sl, b["num_heads"], b["num_kv_heads"], 128, w.kv_dtype, q_len=ql)
             t = time_layer(Path(b, P), args.steps, args.warmup, flush)["mean"]
