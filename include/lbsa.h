@@ -91,6 +91,7 @@ extern "C" {
 #define LBSA_HDR_N 11       /* tiles per KV head = sum_b ceil(L_b / 64) */
 #define LBSA_HDR_MAX_PAGES 12
 #define LBSA_HDR_PAGE_SIZE 13
+#define LBSA_HDR_NLONG 14   /* segments of more than 8 chunks, listed in long_seg */
 #define LBSA_HDR_WORDS 16
 
 /* Byte offsets of the arrays inside a task map (all from the map base). */
@@ -107,6 +108,11 @@ typedef struct {
                                the bin's descriptor count, the request's length, 0; all zero
                                but the index (= Ndesc) for a bin without descriptors */
     size_t desc_len;        /* int32[Hkv*B + P]: length of descriptor d's request */
+    size_t long_seg;        /* int32x4[(Hkv*B + P) / 9]: (h*B + b, first descriptor, chunks, 0)
+                               of each segment with more than 8 chunks, in segment order;
+                               the first header[LBSA_HDR_NLONG] records are valid.  The
+                               combine merges such a segment one output row per workgroup,
+                               a shorter one whole in one workgroup. */
     size_t total;           /* bytes */
 } lbsa_task_map_layout;
 

@@ -105,7 +105,7 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 207; }
+LBSA_API int lbsa_version(void) { return 208; }
 
 namespace {
 // Events armed for the next launches on this host thread, used in order.
@@ -198,6 +198,7 @@ LBSA_API int lbsa_task_map_layout_get(int32_t batch, int32_t num_kv_heads, int32
     out->seqlens = m.seqlens;
     out->bin_head = m.bin_head;
     out->desc_len = m.desc_len;
+    out->long_seg = m.long_seg;
     out->total = m.total;
     return LBSA_OK;
 }

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     const int32_t* __restrict__ seqlens, int B, int Hq, int Hkv, int P, int F, int max_pages,
     uint8_t* __restrict__ map) {
     extern __shared__ int smem[];
-    __shared__ int red[2][kAssignThreads / 64];
+    __shared__ int red[3][kAssignThreads / 64];
     // every kernel argument in one round trip, before anything uses one (else the
     // compiler fetches them in several dependent rounds)
     __asm__ volatile("" ::"s"(seqlens), "s"(map), "s"(B), "s"(Hq), "s"(Hkv), "s"(P), "s"(F), "s"(max_pages));
@@ -124,6 +124,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     int32_t* sl_g = reinterpret_cast<int32_t*>(map + L.seqlens);
     int4* head = reinterpret_cast<int4*>(map + L.bin_head);
     int32_t* dlen = reinterpret_cast<int32_t*>(map + L.desc_len);
+    int4* long_seg = reinterpret_cast<int4*>(map + L.long_seg);
 
     const int S = Hkv * B;
     int* prefix = smem;            // [B + 1]  exclusive prefix of n_b
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
     const int sper = (S + kAssignThreads - 1) / kAssignThreads;
     const int s0 = min(S, tid * sper), s1 = min(S, s0 + sper);
     local = 0;
+    int nlong_local = 0;
     for (int s = s0; s < s1; ++s) {
         const int h = s / B, b = s - h * B;
         const int a = h * N + prefix[b];
@@ -180,14 +182,19 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
         const int c = n ? bins.of(a + n - 1) - bins.of(a) + 1 : 0;
         sfd[s] = c;
         local += c;
+        nlong_local += c > kCombineSegChunks;
     }
-    int ndesc;
+    int ndesc, nlong;
     run = block_exclusive_scan(local, red[1], &ndesc);
+    // the long segments (more than kCombineSegChunks chunks) in segment order,
+    // for the combine; at most max_long_segments(S + P) of them
+    int lrun = block_exclusive_scan(nlong_local, red[2], &nlong);
     for (int s = s0; s < s1; ++s) {
         const int c = sfd[s];
         sfd[s] = run;
         sfd_g[s] = run;
         snc_g[s] = c;
+        if (c > kCombineSegChunks) long_seg[lrun++] = make_int4(s, run, c, 0);
         run += c;
     }
     if (tid == 0) sfd[S] = ndesc;
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(
         hdr[11] = N;
         hdr[12] = max_pages;
         hdr[13] = kTile;
-        hdr[14] = 0;
+        hdr[14] = nlong;
         hdr[15] = 0;
     }
 }

@@ -794,80 +794,42 @@ __device__ inline void merge_chunk(float l, f32x4 x, float& m, float& wsum, f32x
     o += wgt * x;
 }
 
-// One workgroup per output row (request, query token, query head).  Its 256
-// threads form 8 slices of 32 (4 consecutive d per thread); slice c0 merges
-// chunks c0, c0 + 8, ... of the row with a running (max LSE, weight sum,
-// weighted O).  The loads of up to kCombineUnroll chunks per slice (64 per
-// row) are all issued before the first of them is used, so a row of up to 64
-// chunks costs one round trip to the partials after the one to the map (16
-// per slice needed more registers, and the lower occupancy cost more than the
-// round trips it saved).  The 8
-// slice states are then merged through LDS under the global maximum.  With
-// a.direct_out, a row whose segment has a single chunk was written by the split
-// kernel, and its workgroup stops after reading the chunk count.
+// Merge of chunks [d0, d0 + n) of partial row rr (R rows per slot) into the
+// bf16 output row dst by one workgroup of 256 threads.  They form 8 slices of
+// 32 (4 consecutive dims per thread); slice z merges chunks z, z + 8, ... with
+// a running (max LSE, weight sum, weighted O).  The loads of up to UNROLL
+// chunks per slice (8 UNROLL per row) are all issued before the first of them
+// is used, so a row of up to 8 UNROLL chunks costs one round trip to the
+// partials.  The 8 slice states are then merged through LDS under the global
+// maximum.  A poisoned row is written as NaN.  The static combine, one
+// workgroup per output row of every request, takes UNROLL = 8 (16 needed more
+// registers, and the lower occupancy cost more than the round trips it
+// saved); the long segments of the task-map combine, a few workgroups with
+// up to hundreds of chunks each, take 16.
 constexpr int kCombineUnroll = 8;
-template <bool STATIC>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint8_t* map, int B, int Hkv, int P, int Hq,
-                                                                   int QL, AttnArgs a) {
+struct RowMergeLds {
+    float m[8];
+    float w[8];
+    int nan;
+    __attribute__((aligned(16))) float o[8][kHeadDim];
+};
+template <int UNROLL = kCombineUnroll>
+__device__ inline void merge_row(const AttnArgs& a, int64_t d0, int n, int R, int rr, uint16_t* dst, bool poison,
+                                 RowMergeLds& red) {
     constexpr int kSlices = 8;
-    __shared__ float red_m[kSlices];
-    __shared__ float red_w[kSlices];
-    __shared__ int red_nan;
-    __shared__ __attribute__((aligned(16))) float red_o[kSlices][kHeadDim];
-    // every kernel argument in one round trip, before anything uses one
-    const int row = blockIdx.x;                         // (b * QL + query) * Hq + hq
-    const int bq = row / Hq, hq = row - bq * Hq;
-    const int b = bq / QL, qi = bq - b * QL;
-    const int h = hq / kGroup, gq = hq - h * kGroup;
-    const int R = kGroup * QL;                        // partial rows per slot
-    const int64_t seg = (int64_t)h * B + b;
     const int tid = threadIdx.x, slice = tid >> 5, d4 = (tid & 31) * 4;
-
-    int64_t d0 = 0;
-    int n = 0;
-    bool poison = false;
-    if constexpr (STATIC) {
-        d0 = seg * P;
-        n = P;
-    } else {
-        // the header words and the segment's chunk range: independent loads in
-        // one round trip, checked together (the segment index is in range for
-        // any map of this shape)
-        const MapLayout ML = map_layout(B, Hkv, P);
-        const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
-        const int h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
-        const int h_err = hdr[LBSA_HDR_ERROR];
-        const int sd0 = uniform_ptr<int32_t>(map + ML.seg_first_desc)[seg];
-        const int sn = uniform_ptr<int32_t>(map + ML.seg_num_chunks)[seg];
-        const int cap = Hkv * B + P;
-        // a map built for another shape, or one whose lengths were invalid (the
-        // split kernel computed nothing): every row is NaN
-        poison = (h_p != P) | (h_b != B) | (h_hkv != Hkv) | (h_err != 0) | (sd0 < 0) | (sn < 0) |
-                 (sn > cap - sd0);
-        // the remaining kernel arguments go out with the map loads (map, B, Hkv,
-        // P, Hq and QL arrive preloaded in SGPRs): one round trip for both
-        __asm__ volatile("" ::"s"(a.part_lse), "s"(a.part_o), "s"(a.out), "s"(a.direct_out));
-        keep(sd0);
-        keep(sn);
-        if (!poison) {
-            d0 = sd0;
-            n = sn;
-            if (a.direct_out && n == 1) return;         // the split kernel wrote this row
-        }
-    }
-    if (tid == 0) red_nan = 0;
-
+    if (tid == 0) red.nan = 0;
     float m = kNegInf, wsum = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     bool nan_seen = false;
-    auto pr = [&](int c) { return (d0 + c) * R + kGroup * qi + gq; };
-    for (int c0 = slice; c0 < n; c0 += kCombineUnroll * kSlices) {
-        float l[kCombineUnroll];
-        f32x4 x[kCombineUnroll];
+    auto pr = [&](int c) { return (d0 + c) * R + rr; };
+    for (int c0 = slice; c0 < n; c0 += UNROLL * kSlices) {
+        float l[UNROLL];
+        f32x4 x[UNROLL];
         // every load first (a slice past the row's last chunk loads nothing), then
         // the merges
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) {
+        for (int u = 0; u < UNROLL; ++u) {
             const int c = c0 + u * kSlices;
             if (c < n) {
                 l[u] = a.part_lse[pr(c)];
@@ -878,36 +840,157 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint8_t*
             }
         }
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) merge_chunk(l[u], x[u], m, wsum, o, nan_seen);
+        for (int u = 0; u < UNROLL; ++u) merge_chunk(l[u], x[u], m, wsum, o, nan_seen);
     }
-    __syncthreads();                                    // red_nan initialised
-    if (nan_seen) red_nan = 1;
+    __syncthreads();                                    // red.nan initialised
+    if (nan_seen) red.nan = 1;
     if ((tid & 31) == 0) {
-        red_m[slice] = m;
-        red_w[slice] = wsum;
+        red.m[slice] = m;
+        red.w[slice] = wsum;
     }
-    *reinterpret_cast<f32x4*>(&red_o[slice][d4]) = o;
+    *reinterpret_cast<f32x4*>(&red.o[slice][d4]) = o;
     __syncthreads();
     if (slice == 0) {
         float M = kNegInf;
 #pragma unroll
-        for (int i = 0; i < kSlices; ++i) M = fmaxf(M, red_m[i]);
+        for (int i = 0; i < kSlices; ++i) M = fmaxf(M, red.m[i]);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         float W = 0.f;
         if (M != kNegInf) {
 #pragma unroll
             for (int i = 0; i < kSlices; ++i) {
-                const float sc = exp2_fast((red_m[i] - M) * kLog2e);   // 0 for empty slices
-                W += sc * red_w[i];
-                acc += sc * *reinterpret_cast<const f32x4*>(&red_o[i][d4]);
+                const float sc = exp2_fast((red.m[i] - M) * kLog2e);   // 0 for empty slices
+                W += sc * red.w[i];
+                acc += sc * *reinterpret_cast<const f32x4*>(&red.o[i][d4]);
             }
             acc *= 1.f / W;
         }
-        if (poison || red_nan) {
+        if (poison || red.nan) {
             const float nan = __builtin_nanf("");
             acc = f32x4{nan, nan, nan, nan};
         }
-        store_bf16x4(static_cast<uint16_t*>(a.out) + (size_t)row * kHeadDim + d4, acc);
+        store_bf16x4(dst + d4, acc);
+    }
+}
+
+// The combine of the static split: one workgroup per output row (request,
+// query token, query head), merging the row's P chunks (slots seg * P + s).
+__global__ __launch_bounds__(kCombineThreads) void combine_static_kernel(int B, int P, int Hq, int QL, AttnArgs a) {
+    __shared__ RowMergeLds red;
+    const int row = blockIdx.x;                         // (b * QL + query) * Hq + hq
+    const int bq = row / Hq, hq = row - bq * Hq;
+    const int b = bq / QL, qi = bq - b * QL;
+    const int h = hq / kGroup, gq = hq - h * kGroup;
+    const int64_t seg = (int64_t)h * B + b;
+    merge_row(a, seg * P, P, kGroup * QL, kGroup * qi + gq, static_cast<uint16_t*>(a.out) + (size_t)row * kHeadDim,
+              false, red);
+}
+
+// The combine of the task-map path, over the map's segments (KV head h,
+// request b) and their 8 * QL rows rr = 8 * query token + head of the group.
+//  - Workgroups [0, E), E = 8 QL max_long_segments(Hkv*B + P): workgroup e
+//    takes row e mod 8 QL of the (e / 8 QL)-th long segment of the map's list
+//    (more than kCombineSegChunks chunks) and merges it with merge_row; past
+//    the list's end it returns.  They come first so that the largest merges
+//    start first.
+//  - Workgroups [E, E + Hkv*B): one per segment; thread t holds 4 dims of row
+//    t / 32 (and of row t / 32 + 8 when QL = 2) and merges the segment's up to
+//    kCombineSegChunks chunks from registers, all loaded in one round trip.  A
+//    segment with one chunk was written by the split kernel when direct_out is
+//    set: its workgroup returns after the map words; a long one is left to the
+//    first range.
+// A map built for another shape, or one whose lengths were invalid (the split
+// kernel computed nothing), poisons the call: every output row is NaN (written
+// by the segment workgroups).  Against one workgroup per output row (most of
+// which would only read a chunk count), a batch of 64 requests with 64 query
+// heads launches 2-3x fewer workgroups, and each row of a long segment still
+// has a workgroup of its own.
+template <int QL>
+__global__ __launch_bounds__(kCombineThreads) void combine_map_kernel(const uint8_t* map, int B, int Hkv, int P, int Hq,
+                                                                       AttnArgs a) {
+    __shared__ RowMergeLds red;
+    constexpr int R = kGroup * QL;                      // partial rows per slot
+    const MapLayout ML = map_layout(B, Hkv, P);
+    const int S = Hkv * B, cap = S + P;
+    const int E = R * max_long_segments(cap);
+    const int tid = threadIdx.x, d4 = (tid & 31) * 4;
+    const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
+    auto out_row = [&](int h, int b, int rr) {
+        const int qi = rr >> 3, gq = rr & 7;
+        return static_cast<uint16_t*>(a.out) + ((size_t)(b * QL + qi) * Hq + (size_t)h * kGroup + gq) * kHeadDim;
+    };
+    if ((int)blockIdx.x < E) {
+        const int k = (int)blockIdx.x / R, rr = (int)blockIdx.x - k * R;
+        // the record and the header words in one round trip, with the kernel
+        // arguments still to come (k < max_long_segments(cap): in bounds)
+        const auto* ent = uniform_ptr<int32_t>(map + ML.long_seg) + 4 * k;
+        const int seg = ent[0], d0 = ent[1], n = ent[2];
+        const int h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
+        const int h_err = hdr[LBSA_HDR_ERROR], h_nlong = hdr[LBSA_HDR_NLONG];
+        __asm__ volatile("" ::"s"(a.part_lse), "s"(a.part_o), "s"(a.out));
+        keep(seg);
+        keep(d0);
+        keep(n);
+        keep(h_nlong);
+        // a poisoned map is written as NaN by the segment workgroups; a record
+        // that does not describe a long segment of this map is not merged
+        const bool bad_map = (h_p != P) | (h_b != B) | (h_hkv != Hkv) | (h_err != 0);
+        if (bad_map || k >= h_nlong || seg < 0 || seg >= S || d0 < 0 || n <= kCombineSegChunks || n > cap - d0)
+            return;
+        const int h = seg / B, b = seg - h * B;
+        merge_row<2 * kCombineUnroll>(a, d0, n, R, rr, out_row(h, b, rr), false, red);
+        return;
+    }
+    const int seg = (int)blockIdx.x - E, h = seg / B, b = seg - h * B;
+    const int d0 = uniform_ptr<int32_t>(map + ML.seg_first_desc)[seg];
+    const int n = uniform_ptr<int32_t>(map + ML.seg_num_chunks)[seg];
+    const int h_p = hdr[LBSA_HDR_P], h_b = hdr[LBSA_HDR_B], h_hkv = hdr[LBSA_HDR_HKV];
+    const int h_err = hdr[LBSA_HDR_ERROR];
+    __asm__ volatile("" ::"s"(a.part_lse), "s"(a.part_o), "s"(a.out), "s"(a.direct_out));
+    keep(d0);
+    keep(n);
+    keep(h_err);
+    const int r0 = tid >> 5;
+    const bool bad_map = (h_p != P) | (h_b != B) | (h_hkv != Hkv) | (h_err != 0);
+    if (bad_map | (d0 < 0) | (n < 0) | (n > cap - d0)) {
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int i = 0; i < QL; ++i) store_bf16x4(out_row(h, b, r0 + kGroup * i) + d4, f32x4{nan, nan, nan, nan});
+        return;
+    }
+    if ((a.direct_out && n == 1) || n > kCombineSegChunks) return;
+    if (n == 0) {                                       // an empty request: O = 0
+#pragma unroll
+        for (int i = 0; i < QL; ++i) store_bf16x4(out_row(h, b, r0 + kGroup * i) + d4, f32x4{0.f, 0.f, 0.f, 0.f});
+        return;
+    }
+    // every load first, branch-free: a chunk past the segment's last re-reads
+    // the last one (same cache lines) and is dropped by its -inf LSE
+    float l[QL][kCombineSegChunks];
+    f32x4 x[QL][kCombineSegChunks];
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+#pragma unroll
+        for (int c = 0; c < kCombineSegChunks; ++c) {
+            const size_t pr = (size_t)(d0 + min(c, n - 1)) * R + r0 + kGroup * i;
+            const float lv = a.part_lse[pr];
+            l[i][c] = c < n ? lv : kNegInf;
+            x[i][c] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kHeadDim + d4);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+        float m = kNegInf, wsum = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        bool nan_seen = false;
+#pragma unroll
+        for (int c = 0; c < kCombineSegChunks; ++c) merge_chunk(l[i][c], x[i][c], m, wsum, o, nan_seen);
+        if (m != kNegInf) o *= 1.f / wsum;
+        if (nan_seen) {
+            const float nan = __builtin_nanf("");
+            o = f32x4{nan, nan, nan, nan};
+        }
+        store_bf16x4(out_row(h, b, r0 + kGroup * i) + d4, o);
     }
 }
 
@@ -932,12 +1015,16 @@ hipError_t launch_static(const AttnArgs& a, bool fp8, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const AttnArgs& a, bool static_mode, hipStream_t stream) {
-    const long long grid = (long long)a.B * a.QL * a.Hq;
     if (static_mode)
-        return launch(combine_kernel<true>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a.map, a.B, a.Hkv,
-                      a.P, a.Hq, a.QL, a);
-    return launch(combine_kernel<false>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a.map, a.B, a.Hkv,
-                  a.P, a.Hq, a.QL, a);
+        return launch(combine_static_kernel, dim3((unsigned)((long long)a.B * a.QL * a.Hq)), dim3(kCombineThreads), 0,
+                      stream, a.B, a.P, a.Hq, a.QL, a);
+    const long long S = (long long)a.B * a.Hkv;
+    const long long grid = (long long)kGroup * a.QL * max_long_segments(S + a.P) + S;
+    if (a.QL == 2)
+        return launch(combine_map_kernel<2>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a.map, a.B, a.Hkv,
+                      a.P, a.Hq, a);
+    return launch(combine_map_kernel<1>, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, a.map, a.B, a.Hkv,
+                  a.P, a.Hq, a);
 }
 
 hipError_t split_occupancy(bool fp8, int q_len, int* blocks_per_cu) {

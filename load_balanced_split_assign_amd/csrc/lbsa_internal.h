@@ -43,8 +43,17 @@ inline hipError_t launch(F kernel, dim3 grid, dim3 block, uint32_t lds_bytes, hi
 
 // Byte offsets of the task-map arrays for (B, Hkv, P).
 struct MapLayout {
-    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seqlens, bin_head, desc_len, total;
+    size_t header, bin_desc_begin, desc, seg_first_desc, seg_num_chunks, seqlens, bin_head, desc_len, long_seg,
+        total;
 };
+
+// A segment of more than kCombineSegChunks chunks is "long": the assign lists
+// it as (segment, first descriptor, chunks, 0), and the combine merges each of
+// its rows in a workgroup of its own; shorter segments are merged whole by one
+// workgroup.  With at most Hkv*B + P descriptors there are at most
+// max_long_segments of them.
+constexpr int kCombineSegChunks = 8;
+__host__ __device__ inline int max_long_segments(int64_t cap) { return (int)(cap / (kCombineSegChunks + 1)); }
 
 // Words of one bin_head record: the bin's first descriptor, its slot, the
 // bin's descriptor count and the request's length (everything a split
@@ -64,7 +73,8 @@ __host__ __device__ inline MapLayout map_layout(int B, int Hkv, int P) {
     m.seqlens = m.seg_num_chunks + 4 * S;
     m.bin_head = align_up(m.seqlens + 4 * (size_t)B, 32);
     m.desc_len = m.bin_head + 4 * kBinHeadWords * (size_t)P;
-    m.total = align_up(m.desc_len + 4 * cap, 256);
+    m.long_seg = align_up(m.desc_len + 4 * cap, 16);
+    m.total = align_up(m.long_seg + 16 * (size_t)max_long_segments((int64_t)cap), 256);
     return m;
 }
 

@@ -22,6 +22,9 @@ KV_BF16, KV_FP8_E4M3 = 0, 1
 PAGE_SIZE, HEAD_DIM, GROUP, DEFAULT_MIN_TILES = 64, 128, 8, 2
 HEADER_FIELDS = ("T", "K", "q", "r", "Ndesc", "P", "F", "B", "Hq", "Hkv",
                  "error", "N", "max_pages", "page_size")
+# a decode segment with more chunks than this is listed in the map's long_seg
+# records and merged one output row per combine workgroup
+LONG_SEGMENT_CHUNKS = 8
 
 _lib = None
 
@@ -35,7 +38,7 @@ class LbsaError(RuntimeError):
 class _MapLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("header", "bin_desc_begin", "desc", "seg_first_desc", "seg_num_chunks", "seqlens", "bin_head",
-                 "desc_len", "total")]
+                 "desc_len", "long_seg", "total")]
 
 
 class _VarlenMapLayout(ctypes.Structure):
@@ -574,6 +577,9 @@ def read_task_map(task_map: torch.Tensor, batch: int, num_kv_heads: int, P: int)
     nd = max(0, min(out["Ndesc"], cap))
     out["desc"] = out["desc_all"][:nd].copy()
     out["desc_len"] = out["desc_len_all"][:nd].copy()
+    max_long = cap // (LONG_SEGMENT_CHUNKS + 1)
+    out["nlong"] = int(header[14])
+    out["long_seg"] = arr(lay["long_seg"], 4 * max_long, (max_long, 4))[:max(0, min(out["nlong"], max_long))].copy()
     return out
 
 

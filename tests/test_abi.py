@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 207
+    assert lbsa.lib().lbsa_version() == 208
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -46,7 +46,8 @@ def test_task_map_layout_is_aligned_and_sized():
         assert lay["seqlens"] == lay["seg_num_chunks"] + 4 * S
         assert lay["bin_head"] % 32 == 0 and lay["bin_head"] >= lay["seqlens"] + 4 * B
         assert lay["desc_len"] == lay["bin_head"] + 32 * P
-        assert lay["total"] >= lay["desc_len"] + 4 * cap and lay["total"] % 256 == 0
+        assert lay["long_seg"] % 16 == 0 and lay["long_seg"] >= lay["desc_len"] + 4 * cap
+        assert lay["total"] >= lay["long_seg"] + 16 * (cap // 9) and lay["total"] % 256 == 0
         assert lbsa.task_map_bytes(B, Hkv, P) == lay["total"]
 
 

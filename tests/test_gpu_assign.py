@@ -1,9 +1,11 @@
 """GPU assign kernel vs the oracle's assign: the task map must be bit-exact.
 
 Compared: header words 0..13, bin CSR (P + 1 entries), descriptors [0, Ndesc),
-per-segment first descriptor and chunk count, the length copy, and the per-bin
-head records (expected values built from the oracle's descriptors and CSR).
-Slots of the descriptor array past Ndesc are unspecified and not compared.
+per-segment first descriptor and chunk count, the length copy, the per-bin
+head records (expected values built from the oracle's descriptors and CSR), and
+the combine's list of long segments (more than 8 chunks, header word 14),
+built here from the oracle's chunk counts.  Slots of the descriptor array past
+Ndesc are unspecified and not compared.
 """
 import numpy as np
 import pytest
@@ -37,7 +39,19 @@ def assert_same_map(oracle_mod, seqlens, Hq, Hkv, P, F, max_pages, what=""):
     np.testing.assert_array_equal(g["bin_head"], expected_bin_head(o, P, sl), err_msg=str(ctx))
     np.testing.assert_array_equal(g["desc_len"], sl[np.asarray(o["desc"], np.int64)[:, 1]] if len(o["desc"]) else
                                   np.zeros(0, np.int32), err_msg=str(ctx))
+    want = expected_long_segments(o)
+    assert g["nlong"] == len(want), ctx
+    np.testing.assert_array_equal(g["long_seg"], want, err_msg=str(ctx))
     return g
+
+
+def expected_long_segments(o):
+    """(segment, first descriptor, chunks, 0) of each segment with more than
+    lbsa.LONG_SEGMENT_CHUNKS chunks in the oracle's map, in segment order."""
+    snc = np.asarray(o["seg_num_chunks"], np.int64)
+    sfd = np.asarray(o["seg_first_desc"], np.int64)
+    s = np.nonzero(snc > lbsa.LONG_SEGMENT_CHUNKS)[0]
+    return np.stack([s, sfd[s], snc[s], np.zeros_like(s)], axis=1).astype(np.int32).reshape(-1, 4)
 
 
 def expected_bin_head(o, P, seqlens):

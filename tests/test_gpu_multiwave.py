@@ -2,7 +2,7 @@
 multiple of compute units x occupancy): the split grid then runs in several
 waves of workgroups.  Checked against the fp64 oracle (the bar of
 tests/parity.py) and for run-to-run bit equality, and the map's reserved
-header words stay zero.
+header word stays zero.
 """
 import numpy as np
 import pytest
@@ -14,7 +14,7 @@ from load_balanced_split_assign_amd import lbsa
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
-HDR_RESERVED = (14, 15)
+HDR_RESERVED = (15,)
 
 
 def resident(batch):
@@ -37,12 +37,12 @@ def test_multiwave_matches_oracle_and_repeats(oracle_mod, mult):
                                 num_heads=16, num_kv_heads=2, kv_dtype="bf16", seed=41))
     P = mult * resident(batch)
     tm = H.plan(batch, P)
-    assert reserved_words(tm) == (0, 0)
+    assert reserved_words(tm) == (0,)
     outs = []
     for _ in range(3):
         outs.append(H.decode(batch, tm, P).clone())
         torch.cuda.synchronize()
-        assert reserved_words(tm) == (0, 0)
+        assert reserved_words(tm) == (0,)
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     check(oracle_mod, batch, outs[0], f"multiwave x{mult}")
@@ -55,7 +55,7 @@ def test_multiwave_fp8(oracle_mod):
     tm = H.plan(batch, P)
     out = H.decode(batch, tm, P)
     torch.cuda.synchronize()
-    assert reserved_words(tm) == (0, 0)
+    assert reserved_words(tm) == (0,)
     check(oracle_mod, batch, out, "multiwave fp8")
 
 
@@ -68,7 +68,7 @@ def test_multiwave_full_size(oracle_mod, name):
         tm = H.plan(batch, P)
         out = H.decode(batch, tm, P)
         torch.cuda.synchronize()
-        assert reserved_words(tm) == (0, 0), (name, P)
+        assert reserved_words(tm) == (0,), (name, P)
         H.check(batch, H.out_np(out), ref, (name, P))
 
 
@@ -92,4 +92,4 @@ def test_multiwave_partials_repeat_bitwise():
     for a, b in zip(p1, p2):
         assert np.isfinite(a).all()
         assert np.array_equal(a.view(np.int32), b.view(np.int32))
-    assert reserved_words(tm) == (0, 0)
+    assert reserved_words(tm) == (0,)
