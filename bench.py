@@ -130,6 +130,9 @@ def make_flush(mode):
     return lambda i: None
 
 
+MIN_WARM_S = 0.25   # seconds of untimed steps before any timed pass of time_steps
+
+
 def _pairs(n):
     import torch
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -147,10 +150,16 @@ def time_steps(path, steps, warmup, flush):
 
     from load_balanced_split_assign_amd import lbsa
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
+    # at least `warmup` steps and MIN_WARM_S of busy GPU: after an idle stretch
+    # (the CPU leg, a batch built on the host) the clocks take tens of ms of
+    # load to come back up, and a few short steps do not cover that
+    t_end = time.perf_counter() + MIN_WARM_S
+    i = 0
+    while i < warmup or time.perf_counter() < t_end:
         flush(i)
         path.assign(); path.layer()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        i += 1
     whole = _pairs(steps)
     for i in range(steps):
         flush(i)
