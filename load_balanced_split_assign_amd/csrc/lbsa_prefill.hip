@@ -13,13 +13,16 @@
 // columns:
 //   * A workgroup (4 wave64) owns one KV head of one request and a block of
 //     query positions; every query column is a (position, head of the group)
-//     pair, 16 columns per MFMA block, CB blocks per wave (CB = 1 or 2, i.e.
-//     2 or 4 positions per wave).  Q stays in registers for the whole run.
+//     pair, 16 columns per MFMA block, CB blocks per wave (CB = 1, 2 or 3,
+//     i.e. 2, 4 or 6 positions per wave).  Q stays in registers for the whole
+//     run.  Every wave reads each K/V element from LDS once for all its
+//     columns, so the LDS bytes per MFMA fall as 1 / CB: at CB = 2 the LDS
+//     reads take about as long as the MFMAs.
 //   * The 64-token K/V tiles (one page of the KV head) stream through a
 //     2-stage LDS ring (64 KiB) shared by the 4 waves: each wave issues the
 //     async global->LDS loads of 16 of the 64 rows, waits for them with its
 //     own vmcnt, and one workgroup barrier per tile publishes the tile and
-//     frees the stage written next.  At 64 KiB of LDS and under 256 VGPRs two
+//     frees the stage written next.  At 64 KiB of LDS and up to 256 VGPRs two
 //     workgroups share a compute unit, so one's softmax (VALU) overlaps the
 //     other's MFMAs; that overlap outweighs the larger K/V reuse of 4 blocks
 //     per wave or a deeper ring, which both leave one wave per SIMD.
@@ -28,7 +31,11 @@
 //     blocks), an online softmax per column in the exp2 domain with a lazy
 //     running max, then O^T += V^T P^T with MFMA 16x16x32 bf16 over the 32
 //     tokens (V^T through ds_read_b64_tr_b16, P straight from the S^T
-//     accumulators).  Half-tiles that reach a column's limit set the scores
+//     accumulators; P of every block first, then the MFMAs, each V^T operand
+//     shared by the blocks).  At CB = 3 the operands of a half-tile pass
+//     through the same registers one after another (K of one 16-token
+//     sub-tile, then the other, then V^T, read while the S MFMAs run), which
+//     keeps the kernel at 256 VGPRs and two waves per SIMD.  Half-tiles that reach a column's limit set the scores
 //     above it to -inf; the softmax scale folds into one fma before each
 //     exp2; the denominator is one more MFMA with an all-ones A operand over
 //     the same bf16 P as the numerator.
@@ -77,6 +84,65 @@ struct PrefillArgs {
 
 __device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// The K rows of one 16-token sub-tile at ring byte OFF (A operands of S^T),
+// complete on return.
+template <int OFF>
+__device__ inline void lds_read_k16_at(uint4 (&k)[4], const uint32_t (&ka)[4]) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
+    u32x4 k0, k1, k2, k3;
+    __asm__ volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\t"
+        "ds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\t"
+        "ds_read_b128 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3)
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "i"(OFF)
+        : "memory");
+    k[0] = __builtin_bit_cast(uint4, k0);
+    k[1] = __builtin_bit_cast(uint4, k1);
+    k[2] = __builtin_bit_cast(uint4, k2);
+    k[3] = __builtin_bit_cast(uint4, k3);
+}
+
+// The transposed V reads of the same half-tile (V^T operands of PV), complete
+// on return.
+template <int OFF>
+__device__ inline void lds_read_vt32_at(s16x4 (&va)[2][8], const uint32_t (&vaddr)[8]) {
+    static_assert(OFF >= 0 && OFF + 16 * kPfRow < 65536, "DS offset field");
+    typedef short s16x4_v __attribute__((ext_vector_type(4)));
+    s16x4_v o[16];
+    __asm__ volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+          "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]),
+          "=&v"(o[15])
+        : "v"(vaddr[0]), "v"(vaddr[1]), "v"(vaddr[2]), "v"(vaddr[3]), "v"(vaddr[4]), "v"(vaddr[5]), "v"(vaddr[6]),
+          "v"(vaddr[7]), "i"(OFF), "i"(OFF + 16 * kPfRow)
+        : "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        va[0][i] = __builtin_bit_cast(s16x4, o[i]);
+        va[1][i] = __builtin_bit_cast(s16x4, o[8 + i]);
+    }
+}
+
 
 
 // One query block of one (request, KV head) over the KV tiles [t0, t1) of the
@@ -110,6 +176,9 @@ template <int CB>
 __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock& a, lds_char* ring, int t0, int t1,
                                                                     QBlockState<CB>& st, int first_page = -1) {
     constexpr int kPosWave = 2 * CB;
+    // three blocks per wave fit two waves per SIMD only with the K and V^T
+    // operands of a half-tile in registers one after the other
+    constexpr bool kLateV = CB >= 3;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int L = a.L;
@@ -210,22 +279,40 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
         // sub-tiles, shared by all CB blocks
         uint4 kk[2][4];
         s16x4 va[2][8];
-        lds_read_tile_bf16_at<OFF>(kk[0], va[0], ka, vaddr);
-        lds_read_tile_bf16_at<OFF + 16 * kPfRow>(kk[1], va[1], ka, vaddr);
+        if constexpr (!kLateV) {
+            lds_read_tile_bf16_at<OFF>(kk[0], va[0], ka, vaddr);
+            lds_read_tile_bf16_at<OFF + 16 * kPfRow>(kk[1], va[1], ka, vaddr);
+        }
 
         // ---- S^T = K Q^T: s[cb][sub][i] is token t32 + 16 sub + 4 g + i
         f32x4 s[CB][2];
+        auto s_mfmas = [&](int sub, const uint4 (&k)[4]) {
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
+            for (int cb = 0; cb < CB; ++cb) {
                 f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][1]), as_bf16x8(q[cb][1]), sa, 0, 0, 0);
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[sub][3]), as_bf16x8(q[cb][3]), sa, 0, 0, 0);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[0]), as_bf16x8(q[cb][0]), sa, 0, 0, 0);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[1]), as_bf16x8(q[cb][1]), sa, 0, 0, 0);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[2]), as_bf16x8(q[cb][2]), sa, 0, 0, 0);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k[3]), as_bf16x8(q[cb][3]), sa, 0, 0, 0);
                 s[cb][sub] = sa;
             }
+        };
+        if constexpr (kLateV) {
+            // one 16-token sub-tile of K in registers at a time
+            lds_read_k16_at<OFF>(kk[0], ka);
+            s_mfmas(0, kk[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_read_k16_at<OFF + 16 * kPfRow>(kk[0], ka);
+            s_mfmas(1, kk[0]);
+        } else {
+            s_mfmas(0, kk[0]);
+            s_mfmas(1, kk[1]);
+        }
+        // the V^T reads go out while the S MFMAs run, into the registers the
+        // K operands have just left
+        if constexpr (kLateV) {
+            __builtin_amdgcn_sched_barrier(0);   // the S MFMAs stay above: kk is dead before va
+            lds_read_vt32_at<OFF>(va, vaddr);
         }
 
         // ---- online softmax over the 8 scores of this lane per block.  Half-
@@ -274,28 +361,33 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
 
         // ---- P and O^T += V^T P^T with MFMA 16x16x32: k = the 32 tokens,
         // lane group g holding tokens 4g .. 4g + 3 of both sub-tiles, in the
-        // same order in the V^T operand (two transposed reads) and in P
+        // same order in the V^T operand (two transposed reads) and in P.  P of
+        // every block first (the scores die there), then the MFMAs, each V^T
+        // operand shared by the blocks
+        bf16x8 pb[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             const float mref = st.m[cb] == kNegInf ? 0.f : st.m[cb];
             float p[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(s[cb][j >> 2][j & 3], a.scale_log2, -mref));
-            const bf16x8 pb = __builtin_bit_cast(
+            pb[cb] = __builtin_bit_cast(
                 bf16x8, make_uint4(bf16x2_pack(p[0], p[1]), bf16x2_pack(p[2], p[3]),
                                    bf16x2_pack(p[4], p[5]), bf16x2_pack(p[6], p[7])));
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const bf16x8 vt = __builtin_bit_cast(
-                    bf16x8, make_uint4(__builtin_bit_cast(uint2, va[0][db]).x,
-                                       __builtin_bit_cast(uint2, va[0][db]).y,
-                                       __builtin_bit_cast(uint2, va[1][db]).x,
-                                       __builtin_bit_cast(uint2, va[1][db]).y));
-                st.acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, st.acc[cb][db], 0, 0, 0);
-            }
-            // the softmax denominator over the same bf16 P as the numerator
-            st.l[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, st.l[cb], 0, 0, 0);
         }
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const bf16x8 vt = __builtin_bit_cast(
+                bf16x8, make_uint4(__builtin_bit_cast(uint2, va[0][db]).x, __builtin_bit_cast(uint2, va[0][db]).y,
+                                   __builtin_bit_cast(uint2, va[1][db]).x, __builtin_bit_cast(uint2, va[1][db]).y));
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                st.acc[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb[cb], st.acc[cb][db], 0, 0, 0);
+        }
+        // the softmax denominator over the same bf16 P as the numerator
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            st.l[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[cb], st.l[cb], 0, 0, 0);
     };
 
     // tile k sits in ring stage U = (k - t0) % 2.  Every tile issues the same
@@ -320,7 +412,7 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
 }
 
 template <int CB>
-__global__ __launch_bounds__(kSplitThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kSplitThreads, 2) void prefill_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char ring_mem[kPfStages * kPfStageBytes];
     lds_char* const ring = (lds_char*)ring_mem;         // stage u at u * kPfStageBytes
     constexpr int kPosWave = 2 * CB, kPosBlock = kWaves * kPosWave;
@@ -694,11 +786,17 @@ hipError_t launch_prefill(const void* q, const void* k_cache, const void* v_cach
     a.qblocks = 0;
     a.scale_log2 = scale_log2;
     if (cb <= 0) {
-        // two query blocks per wave (K/V reuse) while that still leaves two
-        // workgroups per compute unit in the grid, else one
+        // the widest block (most K/V reuse per LDS read) whose grid still
+        // fills the device: 3 blocks per wave from two full rounds of two
+        // workgroups per compute unit (with fewer, a grid of equal blocks
+        // leaves the last round partly idle and 2 blocks per wave are as
+        // fast), 2 from one round
         const long long bh = (long long)B * Hkv;
-        cb = bh * ((QL + kWaves * 4 - 1) / (kWaves * 4)) >= 512 ? 2 : 1;
+        cb = bh * ((QL + kWaves * 6 - 1) / (kWaves * 6)) >= 1024  ? 3
+             : bh * ((QL + kWaves * 4 - 1) / (kWaves * 4)) >= 512 ? 2
+                                                                  : 1;
     }
+    if (cb == 3) return launch_cb<3>(a, stream);
     return cb == 2 ? launch_cb<2>(a, stream) : launch_cb<1>(a, stream);
 }
 

@@ -5,8 +5,9 @@ Prefill and extend are causal attention of each request's q_len new tokens
 Table 4 measures the backend on such shapes.  Tolerance: max |out - oracle|
 <= 2e-2 (bf16 KV, bf16 output), as for decode.  Inputs carry NaN in every
 tail slot past L of each last page, so a leak past a request's length shows.
-The query-block width CB (1 or 2 MFMA column blocks per wave) is chosen on the
-host from the grid size; the shapes below reach both.
+The query-block width CB (1, 2 or 3 MFMA column blocks per wave, 8, 16 or 24
+query positions per workgroup) is chosen on the host from the grid size; the
+shapes below reach all three, the widest with a ragged last block.
 """
 import numpy as np
 import pytest
@@ -28,6 +29,8 @@ def run(batch):
 
 def cb_of(B, Hkv, QL):
     """The host's choice of column blocks per wave (mirrors the launch rule)."""
+    if B * Hkv * -(-QL // 24) >= 1024:
+        return 3
     return 2 if B * Hkv * -(-QL // 16) >= 512 else 1
 
 
@@ -52,7 +55,7 @@ def test_prefill_matches_oracle(oracle_mod, sl, ql, Hq, Hkv):
     H.check(batch, got, ref, ("prefill", ql, Hq, Hkv))
 
 
-@pytest.mark.parametrize("B,Hkv,QL,expect_cb", [(4, 8, 256, 2), (8, 8, 100, 1), (2, 2, 96, 1)])
+@pytest.mark.parametrize("B,Hkv,QL,expect_cb", [(4, 8, 770, 3), (2, 8, 770, 2), (4, 8, 256, 2), (8, 8, 100, 1), (2, 2, 96, 1)])
 def test_prefill_each_block_width(oracle_mod, B, Hkv, QL, expect_cb):
     assert cb_of(B, Hkv, QL) == expect_cb
     sl = [QL + 37 * i for i in range(B)]                      # extend with different prefixes
