@@ -369,11 +369,11 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
  * calls in a graph.
  * Errors: shapes as lbsa_plan and lbsa_prefill (bf16 only); maps larger than
  * one assign workgroup's LDS give LBSA_ERR_UNSUPPORTED: 4 B + 10 NQ words over
- * 36 864 with 8 KV heads (NQ = batch + total_q / 16), about 58K query tokens.
+ * 36 864 with 8 KV heads (NQ = batch + total_q / 24), about 88K query tokens.
  * A length or q out of range on the device sets the error word: every output
  * row is then NaN.  Default P (bins): lbsa_varlen_default_workgroups.
  */
-#define LBSA_QBLOCK 16
+#define LBSA_QBLOCK 24   /* 4 waves x 3 MFMA column blocks of 2 positions (x 8 heads) */
 typedef struct {
     size_t header, bin_desc_begin, desc, desc_slot, claim_order, seg_first_desc, seg_num_chunks, seg_slot0,
         blk_req, blk_k, qbase, qstart, seqlens, qlens, total;

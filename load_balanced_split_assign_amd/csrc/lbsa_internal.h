@@ -86,12 +86,14 @@ __host__ __device__ inline MapLayout map_layout(int B, int Hkv, int P) {
 // block innermost, with the decode budget, fill and spill.  Q and out are
 // packed [sum q_b][Hq][128].
 // ---------------------------------------------------------------------------
-constexpr int kQBlock = 16;                 // query positions per block (one split workgroup's columns)
+constexpr int kQBlock = 24;                 // query positions per block (one split workgroup's columns:
+                                            // 4 waves x 3 MFMA column blocks of 2 positions x 8 heads)
+static_assert(kQBlock == LBSA_QBLOCK, "the public block size");
 constexpr int kVarlenDescWords = 8;         // h, b, k, t0, t1, L, q, qstart: one 32-byte record
 enum { VD_H = 0, VD_B = 1, VD_K = 2, VD_T0 = 3, VD_T1 = 4, VD_L = 5, VD_Q = 6, VD_QS = 7 };
 constexpr int kVarlenRows = kQBlock * kGroup;   // partial rows per slot: position p, head g -> p * 8 + g
 
-// Query blocks a map must hold: sum_b ceil(q_b / 16) <= B + total_q / 16.
+// Query blocks a map must hold: sum_b ceil(q_b / 24) <= B + total_q / 24.
 __host__ __device__ inline int64_t varlen_max_blocks(int B, int64_t total_q) { return B + total_q / kQBlock; }
 
 // Byte offsets of a prefill / extend task map for B requests, Hkv KV heads, P

@@ -84,6 +84,14 @@ struct PrefillArgs {
 
 __device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// x, through an empty asm that the compiler must assume changes it: values
+// derived from the result are computed where it is taken, not hoisted out of an
+// enclosing loop (where they would occupy registers across the whole loop).
+__device__ inline int opaque(int x) {
+    __asm__ volatile("" : "+v"(x));
+    return x;
+}
+
 // The K rows of one 16-token sub-tile at ring byte OFF (A operands of S^T),
 // complete on return.
 template <int OFF>
@@ -174,12 +182,15 @@ struct QBlockState {
 
 template <int CB>
 __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock& a, lds_char* ring, int t0, int t1,
-                                                                    QBlockState<CB>& st, int first_page = -1) {
+                                                                    QBlockState<CB>& st, int tid, int first_page = -1) {
     constexpr int kPosWave = 2 * CB;
     // three blocks per wave fit two waves per SIMD only with the K and V^T
     // operands of a half-tile in registers one after the other
     constexpr bool kLateV = CB >= 3;
-    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // tid: the thread index (the task-map kernel passes it through opaque(), so
+    // that the lane values below are formed per descriptor, not held across its
+    // claim loop)
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int L = a.L;
 
@@ -221,19 +232,15 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
     wait_vmcnt<0>();
 
     // this lane's 4 K and 4 V chunks of every tile: rows 16 w + 4 s + lane / 16,
-    // chunk lane % 16, XOR-swizzled by the row inside the wave's 16
-    uint32_t live_off[4], live_off_v[4], dead_off[4];
-    int lrow[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        lrow[s] = 4 * s + (lane >> 4);
-        const uint32_t chunk = 16u * (uint32_t)((lane & 15) ^ lrow[s]);
-        const uint32_t chunk_v = 16u * (uint32_t)((lane & 15) ^ swz_v(lrow[s]));
-        const uint32_t row_off = (uint32_t)(16 * w + lrow[s]) * (uint32_t)a.Hkv * kPfRow;
-        live_off[s] = row_off + chunk;
-        live_off_v[s] = row_off + chunk_v;
-        dead_off[s] = 16u * (uint32_t)(lane & 15);    // row 0 of the page: always live
-    }
+    // chunk lane % 16, XOR-swizzled by the row inside the wave's 16.  With row =
+    // 4 s + lane / 16 each swizzle is a lane part XOR an s part (K: chunk ^ row;
+    // V: swz_v(4 s + g4) = swz_v(g4) ^ swz_v(4 s)), so the 8 offsets are formed
+    // at each tile from three lane registers, laundered there so that the
+    // compiler does not hoist 8 precomputed offsets out of the tile loop
+    const int g4 = lane >> 4;
+    const uint32_t ck0 = (uint32_t)((lane & 15) ^ g4);
+    const uint32_t cv0 = (uint32_t)((lane & 15) ^ swz_v(g4));
+    const uint32_t lrow0 = (uint32_t)(16 * w + g4) * (uint32_t)a.Hkv * kPfRow;
     const auto* pt = uniform_ptr<int32_t>(a.pt);
     auto issue_page = [&](int64_t page, int t, lds_char* stg) {
         if (page < 0 || page >= a.num_pages) {
@@ -245,11 +252,17 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
         const char* vb = reinterpret_cast<const char*>(a.v_cache) + pbase;
         const int tok0 = kTile * t + 16 * w;
         const bool full = tok0 + 16 <= L;
+        uint32_t ck = ck0, cv = cv0, lr = lrow0;
+        __asm__ volatile("" : "+v"(ck), "+v"(cv), "+v"(lr));
+        const uint32_t dead = 16u * (uint32_t)(lane & 15);   // row 0 of the page: always live
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const bool live = full || tok0 + lrow[s] < L;
-            dma16(kb + (live ? live_off[s] : dead_off[s]), stg + w * kPfSlice + 1024 * s);
-            dma16(vb + (live ? live_off_v[s] : dead_off[s]), stg + kPfHalf + w * kPfSlice + 1024 * s);
+            const bool live = full || tok0 + 4 * s + g4 < L;
+            const uint32_t row_off = lr + (uint32_t)(4 * s) * (uint32_t)a.Hkv * kPfRow;
+            const uint32_t ko = row_off + 16u * (ck ^ (uint32_t)(4 * s));
+            const uint32_t vo = row_off + 16u * (cv ^ (uint32_t)swz_v(4 * s));
+            dma16(kb + (live ? ko : dead), stg + w * kPfSlice + 1024 * s);
+            dma16(vb + (live ? vo : dead), stg + kPfHalf + w * kPfSlice + 1024 * s);
         }
     };
     auto issue = [&](int t, lds_char* stg) { issue_page(pt[t], t, stg); };
@@ -449,7 +462,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void prefill_kernel(PrefillArgs a
 
     QBlockState<CB> st;
     st.bad = !len_ok;
-    attend_qblock<CB>(blk, ring, 0, ntiles, st);
+    attend_qblock<CB>(blk, ring, 0, ntiles, st, (int)threadIdx.x);
 
     // ---- normalise and store: lane (g, r) holds dims 16 db + 4 g .. + 3 of column r
 #pragma unroll
@@ -530,7 +543,7 @@ __global__ void varlen_reset_kernel(int32_t* counters, int n) {
 constexpr int kVarlenMergeUnroll = 8;
 
 __device__ inline void merge_cut_segment(const VarlenArgs& a, int slot0, int n, uint16_t* out_rows, int live) {
-    const int tid = threadIdx.x, d4 = (tid & 31) * 4;
+    const int tid = opaque((int)threadIdx.x), d4 = (tid & 31) * 4;
     const int bin0 = slot0 >> 1;
     for (int row = tid >> 5; row < kVarlenRows; row += kSplitThreads / 32) {
         const int p = row >> 3, gg = row & 7;
@@ -577,12 +590,12 @@ __device__ inline void merge_cut_segment(const VarlenArgs& a, int slot0, int n, 
     }
 }
 
-__global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8_t* map, int B, int Hkv, int P,
+__global__ __launch_bounds__(kSplitThreads, 2) void varlen_split_kernel(const uint8_t* map, int B, int Hkv, int P,
                                                                      int nq_max, VarlenArgs a) {
     __shared__ __attribute__((aligned(16))) char ring_mem[kPfStages * kPfStageBytes];
     __shared__ int claim_lds, arrive_lds;
     lds_char* const ring = (lds_char*)ring_mem;
-    constexpr int CB = 2, kPosWave = 2 * CB;
+    constexpr int CB = 3, kPosWave = 2 * CB;
     static_assert(kWaves * kPosWave == kQBlock, "one workgroup holds one query block");
     const VarlenMapLayout ML = varlen_map_layout(B, Hkv, P, nq_max);
     const auto* hdr = uniform_ptr<int32_t>(map + ML.header);
@@ -672,25 +685,26 @@ __global__ __launch_bounds__(kSplitThreads) void varlen_split_kernel(const uint8
             blk.scale_log2 = a.scale_log2;
             QBlockState<CB> st;
             st.bad = false;
-            attend_qblock<CB>(blk, ring, t0, t1, st, ptab[(size_t)b * a.max_pages + t0]);
+            attend_qblock<CB>(blk, ring, t0, t1, st, opaque((int)threadIdx.x), ptab[(size_t)b * a.max_pages + t0]);
+            const int el = opaque((int)threadIdx.x) & 63, er = el & 15, eg = el >> 4;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                const int p = w * kPosWave + 2 * cb + (r >> 3), gg = r & 7;
+                const int p = w * kPosWave + 2 * cb + (er >> 3), gg = er & 7;
                 if (p >= blk.live) continue;
                 const float lt = st.l[cb][0];
                 float inv = lt > 0.f ? 1.f / lt : 0.f;        // a query that sees none of these tokens: O = 0
                 if (st.bad) inv = __builtin_nanf("");
                 if (whole) {
                     uint16_t* o =
-                        a.out + ((size_t)(qs + kQBlock * k + p) * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + 4 * g;
+                        a.out + ((size_t)(qs + kQBlock * k + p) * a.Hq + (size_t)h * kGroup + gg) * kHeadDim + 4 * eg;
 #pragma unroll
                     for (int db = 0; db < 8; ++db) store_bf16x4(o + 16 * db, st.acc[cb][db] * inv);
                 } else {
                     const size_t row = (size_t)slot * kVarlenRows + p * kGroup + gg;
-                    float* o = a.part_o + row * kHeadDim + 4 * g;
+                    float* o = a.part_o + row * kHeadDim + 4 * eg;
 #pragma unroll
                     for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[cb][db] * inv;
-                    if (g == 0) {
+                    if (eg == 0) {
                         float lse = lt > 0.f ? (st.m[cb] + __builtin_log2f(lt)) * kLn2 : kNegInf;
                         if (st.bad) lse = __builtin_nanf("");
                         a.part_lse[row] = lse;

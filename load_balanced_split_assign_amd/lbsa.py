@@ -386,10 +386,10 @@ def prefill(q, k_cache, v_cache, page_table, seqlens, softmax_scale: float, out=
 
 
 # ---------------------------------------------------------------------------
-# prefill / extend / decode rows on one task map (query blocks of 16 positions)
+# prefill / extend / decode rows on one task map (query blocks of 24 positions)
 # ---------------------------------------------------------------------------
 
-QBLOCK = 16
+QBLOCK = 24   # the library's query positions per block (header word 15 of a built map)
 
 
 def varlen_task_map_layout(batch: int, num_kv_heads: int, P: int, total_q: int) -> dict:

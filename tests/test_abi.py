@@ -209,12 +209,13 @@ def test_timing_hook_arms_and_disarms_without_a_gpu():
 
 
 def test_varlen_map_layout_and_workspace():
-    """Query-block maps: 32-byte descriptors for Hkv * (B + total_q / 16) + P
-    slots, their partial-slot words and claim order, every array after them; the workspace:
-    8 claim and P arrival counters, then 2 P partial slots of 128 rows."""
+    """Query-block maps (24 positions per block): 32-byte descriptors for
+    Hkv * (B + total_q / 24) + P slots, their partial-slot words and claim order,
+    every array after them; the workspace: 8 claim and P arrival counters, then
+    2 P partial slots of 24 * 8 = 192 rows."""
     for B, Hkv, P, tq in [(2, 1, 4, 21), (64, 8, 512, 8255), (1, 8, 512, 8192)]:
         lay = lbsa.varlen_task_map_layout(B, Hkv, P, tq)
-        nq = B + tq // 16
+        nq = B + tq // lbsa.QBLOCK
         S, cap = Hkv * nq, Hkv * nq + P
         assert lay["header"] == 0 and lay["bin_desc_begin"] == 64
         assert lay["desc"] % 32 == 0 and lay["desc"] >= 64 + 4 * (P + 1)
@@ -230,8 +231,9 @@ def test_varlen_map_layout_and_workspace():
         assert lbsa.varlen_task_map_bytes(B, Hkv, P, tq) == lay["total"]
     for P in (1, 512, 1000):
         counters = -(-4 * (8 + P) // 256) * 256            # 8 claim + P arrival counters, 256-aligned
-        lse = -(-2 * P * 128 * 4 // 256) * 256
-        assert lbsa.varlen_workspace_bytes(64, 8, P) == counters + lse + 2 * P * 128 * 128 * 4
+        rows = 8 * lbsa.QBLOCK
+        lse = -(-2 * P * rows * 4 // 256) * 256
+        assert lbsa.varlen_workspace_bytes(64, 8, P) == counters + lse + 2 * P * rows * 128 * 4
 
 
 def test_varlen_host_argument_errors():
@@ -261,3 +263,12 @@ def test_varlen_host_argument_errors():
     assert attend(wb=1024) == lbsa.ERR_INVALID_ARGUMENT              # workspace too small
     assert attend(out=None) == lbsa.ERR_INVALID_ARGUMENT
     assert attend(D=64) == lbsa.ERR_UNSUPPORTED
+
+
+def test_query_block_size_matches_the_header():
+    """The binding's query-block size is the public header's LBSA_QBLOCK (the
+    library asserts the same of its own constant at compile time)."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "lbsa.h")).read()
+    assert int(re.search(r"#define LBSA_QBLOCK (\d+)", hdr).group(1)) == lbsa.QBLOCK

@@ -41,7 +41,7 @@ def attend(batch, tm, P):
 
 def expected_extras(o, sl, ql, P):
     """GPU-only arrays of the map, from the oracle's map and the lengths."""
-    nq = [-(-q // 16) for q in ql]
+    nq = [-(-q // lbsa.QBLOCK) for q in ql]
     qbase = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     qstart = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
     bdb = np.asarray(o["bin_desc_begin"], np.int64)
@@ -75,7 +75,8 @@ def assert_same_varlen_map(oracle_mod, sl, ql, Hkv, P, F, mp, what=""):
     ql_t = torch.tensor(ql, dtype=torch.int32, device="cuda:0")
     tm = lbsa.plan_varlen(sl_t, ql_t, 8 * Hkv, Hkv, mp, P, F, total_q=int(sum(ql)))
     g = lbsa.read_varlen_task_map(tm, len(sl), Hkv, P, int(sum(ql)))
-    o = oracle_mod.assign_varlen(np.asarray(sl, np.int32), np.asarray(ql, np.int32), 8 * Hkv, Hkv, P, F or 2, mp)
+    o = oracle_mod.assign_varlen(np.asarray(sl, np.int32), np.asarray(ql, np.int32), 8 * Hkv, Hkv, P, F or 2, mp,
+                                 lbsa.QBLOCK)
     ctx = str((what, len(sl), Hkv, P, F))
     np.testing.assert_array_equal(g["header"], o["header"], err_msg=ctx)
     np.testing.assert_array_equal(g["bin_desc_begin"], o["bin_desc_begin"], err_msg=ctx)
@@ -102,7 +103,8 @@ def assert_same_varlen_map(oracle_mod, sl, ql, Hkv, P, F, mp, what=""):
 
 def test_worked_example_map(oracle_mod):
     g = assert_same_varlen_map(oracle_mod, [100, 50], [20, 1], 1, 4, 2, 4)
-    assert g["Ndesc"] == 4 and g["NQ"] == 3
+    assert g["QB"] == lbsa.QBLOCK == 24
+    assert g["Ndesc"] == 2 and g["NQ"] == 2        # one block per request, 3 tiles in one bin (F = 2)
 
 
 def test_mixed_extend_map_bitexact(oracle_mod):
@@ -131,21 +133,21 @@ def test_random_varlen_maps_bitexact(oracle_mod):
 
 def test_maps_near_the_lds_limit(oracle_mod):
     """The single assign workgroup keeps its prefixes in up to 144 KiB of LDS:
-    a 56000-token prefill and a mix of long extends, 8 KV heads, bit-exact
+    an 88000-token prefill and a mix of long extends, 8 KV heads, bit-exact
     against the oracle; then the prefill's attention on sampled rows."""
-    for sl, ql in [([56000], [56000]), ([20000, 16000, 30000, 9000], [14000, 16000, 12000, 1])]:
+    for sl, ql in [([88000], [88000]), ([40000, 30000, 45000, 9000], [30000, 30000, 27000, 1])]:
         mp = max(-(-x // 64) for x in sl)
         assert_same_varlen_map(oracle_mod, sl, ql, 8, 512, 0, mp, "near the LDS limit")
-    b = wl.make_batch(seqlens=[56000], qlens=[56000], num_heads=64, num_kv_heads=8, kv_dtype="bf16", seed=78,
+    b = wl.make_batch(seqlens=[88000], qlens=[88000], num_heads=64, num_kv_heads=8, kv_dtype="bf16", seed=78,
                       tail="nan", device="cuda:0")
-    b["total_q"] = 56000
+    b["total_q"] = 88000
     P = lbsa.varlen_default_workgroups(0)
     out = H.out_np(attend(b, plan(b, P), P))
-    rows = [(t, hq) for t in (0, 15, 16, 30001, 55999) for hq in (0, 9, 63)]
+    rows = [(t, hq) for t in (0, 23, 24, 30001, 87999) for hq in (0, 9, 63)]
     bc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
     ref, _ = oracle_mod.attention_varlen_rows(bc, rows)
     got = np.stack([out[t, hq] for t, hq in rows])
-    H.check(b, got, ref, "56000-token prefill, sampled rows")
+    H.check(b, got, ref, "88000-token prefill, sampled rows")
 
 
 def test_one_query_per_request_gives_the_decode_map(oracle_mod):
@@ -200,7 +202,7 @@ def test_many_chunk_segments_merged_in_the_split_kernel(oracle_mod):
     """A decode row of 128 tiles spread over dozens of bins (more chunks than
     the merge loads at once) beside a prefill cut at many bin edges: every
     row against the oracle."""
-    b = varlen_batch([8192, 100, 3000], [1, 100, 40], Hq=8, Hkv=1, seed=74)
+    b = varlen_batch([8192, 200, 3000], [1, 200, 40], Hq=8, Hkv=1, seed=74)
     P = 64
     tm = plan(b, P, 1)
     m = lbsa.read_varlen_task_map(tm, b["B"], 1, P, b["total_q"])
@@ -259,7 +261,7 @@ def test_mixed_extend_full_size_sampled_parity(oracle_mod):
     out = H.out_np(attend(b, tm, P))
     eq = int(b["qlens"][0])
     rng = np.random.default_rng(5)
-    pos = np.unique(np.concatenate([[0, 15, 16, 4095, eq - 1], rng.integers(0, eq, 43)]))
+    pos = np.unique(np.concatenate([[0, 23, 24, 4095, eq - 1], rng.integers(0, eq, 43)]))
     rows = [(int(t), hq) for t in pos for hq in range(64)] + [(eq + i, hq) for i in range(63) for hq in range(64)]
     bc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in b.items()}
     ref, _ = oracle_mod.attention_varlen_rows(bc, rows)

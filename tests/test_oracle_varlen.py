@@ -84,7 +84,7 @@ def test_one_query_per_request_is_the_decode_map(oracle_mod):
         np.testing.assert_array_equal(v["seg_num_chunks"], d["seg_num_chunks"])
 
 
-@pytest.mark.parametrize("QB", [4, 16])
+@pytest.mark.parametrize("QB", [4, 16, 24])
 def test_brute_force_small_cases(oracle_mod, QB):
     rng = np.random.default_rng(12 + QB)
     cases = 0
