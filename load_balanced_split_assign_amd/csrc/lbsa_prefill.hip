@@ -180,7 +180,10 @@ struct QBlockState {
     bool bad;
 };
 
-template <int CB>
+// LEAN: form the 8 DMA offsets of a tile at each tile from three lane registers
+// instead of holding them (the task-map kernel, whose claim loop needs the
+// registers); the grid kernel holds them and saves the VALU work.
+template <int CB, bool LEAN = false>
 __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock& a, lds_char* ring, int t0, int t1,
                                                                     QBlockState<CB>& st, int tid, int first_page = -1) {
     constexpr int kPosWave = 2 * CB;
@@ -234,9 +237,9 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
     // this lane's 4 K and 4 V chunks of every tile: rows 16 w + 4 s + lane / 16,
     // chunk lane % 16, XOR-swizzled by the row inside the wave's 16.  With row =
     // 4 s + lane / 16 each swizzle is a lane part XOR an s part (K: chunk ^ row;
-    // V: swz_v(4 s + g4) = swz_v(g4) ^ swz_v(4 s)), so the 8 offsets are formed
-    // at each tile from three lane registers, laundered there so that the
-    // compiler does not hoist 8 precomputed offsets out of the tile loop
+    // V: swz_v(4 s + g4) = swz_v(g4) ^ swz_v(4 s)); LEAN launders the three lane
+    // registers at each tile, so that the compiler forms the 8 offsets there
+    // rather than hoisting them out of the tile loop
     const int g4 = lane >> 4;
     const uint32_t ck0 = (uint32_t)((lane & 15) ^ g4);
     const uint32_t cv0 = (uint32_t)((lane & 15) ^ swz_v(g4));
@@ -253,7 +256,7 @@ __device__ __attribute__((always_inline)) inline void attend_qblock(const QBlock
         const int tok0 = kTile * t + 16 * w;
         const bool full = tok0 + 16 <= L;
         uint32_t ck = ck0, cv = cv0, lr = lrow0;
-        __asm__ volatile("" : "+v"(ck), "+v"(cv), "+v"(lr));
+        if constexpr (LEAN) __asm__ volatile("" : "+v"(ck), "+v"(cv), "+v"(lr));
         const uint32_t dead = 16u * (uint32_t)(lane & 15);   // row 0 of the page: always live
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -685,7 +688,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void varlen_split_kernel(const ui
             blk.scale_log2 = a.scale_log2;
             QBlockState<CB> st;
             st.bad = false;
-            attend_qblock<CB>(blk, ring, t0, t1, st, opaque((int)threadIdx.x), ptab[(size_t)b * a.max_pages + t0]);
+            attend_qblock<CB, true>(blk, ring, t0, t1, st, opaque((int)threadIdx.x), ptab[(size_t)b * a.max_pages + t0]);
             const int el = opaque((int)threadIdx.x) & 63, er = el & 15, eg = el >> 4;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
