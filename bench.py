@@ -532,7 +532,7 @@ def varlen_rows(steps, warmup, flush, P_arg=0):
                           tail="normal", device="cuda:0")
         tq = int(sum(ql))
         B, mp = b["B"], b["max_pages"]
-        P = P_arg or lbsa.varlen_default_workgroups(0)
+        P = P_arg or lbsa.varlen_auto_workgroups(ql, 8)
         tm = torch.empty(lbsa.varlen_task_map_bytes(B, 8, P, tq), dtype=torch.uint8, device="cuda:0")
         ws = torch.empty(lbsa.varlen_workspace_bytes(64, 8, P), dtype=torch.uint8, device="cuda:0")
         out = torch.empty_like(b["q"])

@@ -371,7 +371,8 @@ int lbsa_prefill(const void* q_d, const void* k_cache_d, const void* v_cache_d, 
  * one assign workgroup's LDS give LBSA_ERR_UNSUPPORTED: 4 B + 10 NQ words over
  * 36 864 with 8 KV heads (NQ = batch + total_q / 24), about 88K query tokens.
  * A length or q out of range on the device sets the error word: every output
- * row is then NaN.  Default P (bins): lbsa_varlen_default_workgroups.
+ * row is then NaN.  P (bins): lbsa_varlen_auto_workgroups, or
+ * lbsa_varlen_default_workgroups (one bin per resident workgroup).
  */
 #define LBSA_QBLOCK 24   /* 4 waves x 3 MFMA column blocks of 2 positions (x 8 heads) */
 typedef struct {
@@ -384,6 +385,16 @@ int lbsa_varlen_task_map_bytes(int32_t batch, int32_t num_kv_heads, int32_t P, i
 int lbsa_varlen_workspace_bytes(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t P,
                                 size_t* out_bytes);
 int lbsa_varlen_default_workgroups(int device, int32_t* out_P);
+/* P (bins) for a prefill / extend map from the host's copy of the q counts
+ * (qlens_host: int32[batch], HOST memory): a quarter of the resident count when
+ * the batch has at least 4 segments (Hkv x query blocks) per resident workgroup,
+ * else the resident count.  The split kernel's workgroups claim descriptors, so
+ * with many segments fewer bins only cut fewer of them: on MI355X the 8K extend
+ * beside 63 decode rows and a q8k prefill took 2-4% less at a quarter of the
+ * bins.  Errors: LBSA_ERR_INVALID_ARGUMENT for a NULL pointer or batch,
+ * num_kv_heads < 1; LBSA_ERR_HIP when the device cannot be queried. */
+int lbsa_varlen_auto_workgroups(int device, const int32_t* qlens_host, int32_t batch, int32_t num_kv_heads,
+                                int32_t* out_P);
 int lbsa_plan_varlen(const int32_t* seqlens_d, const int32_t* qlens_d, int32_t batch, int32_t num_heads,
                      int32_t num_kv_heads, int32_t page_size, int32_t max_pages_per_seq, int64_t total_q,
                      int32_t num_workgroups, int32_t min_tiles_per_bin, void* task_map_d, size_t task_map_bytes,

@@ -105,7 +105,7 @@ LBSA_API const char* lbsa_status_string(int status) {
     }
 }
 
-LBSA_API int lbsa_version(void) { return 208; }
+LBSA_API int lbsa_version(void) { return 209; }
 
 namespace {
 // Events armed for the next launches on this host thread, used in order.
@@ -568,6 +568,21 @@ LBSA_API int lbsa_varlen_default_workgroups(int device, int32_t* out_P) {
         return LBSA_ERR_HIP;
     if (varlen_occupancy(&per_cu) != hipSuccess || per_cu <= 0) return LBSA_ERR_HIP;
     *out_P = cus * per_cu;
+    return LBSA_OK;
+}
+
+LBSA_API int lbsa_varlen_auto_workgroups(int device, const int32_t* qlens_host, int32_t batch, int32_t num_kv_heads,
+                                         int32_t* out_P) {
+    if (!out_P || !qlens_host || batch <= 0 || num_kv_heads <= 0) return LBSA_ERR_INVALID_ARGUMENT;
+    int resident = 0;
+    const int s = varlen_resident_workgroups(device, &resident);
+    if (s != LBSA_OK) return s;
+    int64_t nq = 0;   // query blocks; out-of-range q count none (the map marks them)
+    for (int b = 0; b < batch; ++b) nq += qlens_host[b] >= 1 ? (qlens_host[b] + kQBlock - 1) / kQBlock : 0;
+    // with at least 4 segments per resident workgroup the claims balance the
+    // load without the extra cuts of one bin per workgroup: a quarter of the
+    // bins cuts fewer segments (fewer partials and merges)
+    *out_P = (int64_t)num_kv_heads * nq >= 4LL * resident ? (resident + 3) / 4 : resident;
     return LBSA_OK;
 }
 

@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         L.lbsa_varlen_task_map_bytes.argtypes = [i32, i32, i32, i64, ctypes.POINTER(sz)]
         L.lbsa_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.lbsa_varlen_default_workgroups.argtypes = [ctypes.c_int, ctypes.POINTER(i32)]
+        L.lbsa_varlen_auto_workgroups.argtypes = [ctypes.c_int, ctypes.POINTER(i32), i32, i32, ctypes.POINTER(i32)]
         L.lbsa_plan_varlen.argtypes = [vp, vp, i32, i32, i32, i32, i32, i64, i32, i32, vp, sz, vp]
         L.lbsa_attend_varlen.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32, f32, vp, sz,
                                          vp, sz, vp, vp]
@@ -101,7 +102,8 @@ def lib() -> ctypes.CDLL:
                    "lbsa_decode_static", "lbsa_prefill", "lbsa_router_split_weights",
                    "lbsa_router_workspace_bytes", "lbsa_router_gemm", "lbsa_time_next_kernel",
                    "lbsa_time_next_kernels", "lbsa_varlen_task_map_layout_get", "lbsa_varlen_task_map_bytes",
-                   "lbsa_varlen_workspace_bytes", "lbsa_varlen_default_workgroups", "lbsa_plan_varlen",
+                   "lbsa_varlen_workspace_bytes", "lbsa_varlen_default_workgroups", "lbsa_varlen_auto_workgroups",
+                   "lbsa_plan_varlen",
                    "lbsa_attend_varlen"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -416,6 +418,16 @@ def varlen_workspace_bytes(num_heads: int, num_kv_heads: int, P: int) -> int:
 def varlen_default_workgroups(device: int = 0) -> int:
     out = ctypes.c_int32()
     _check("lbsa_varlen_default_workgroups", lib().lbsa_varlen_default_workgroups(device, ctypes.byref(out)))
+    return out.value
+
+
+def varlen_auto_workgroups(qlens, num_kv_heads: int, device: int = 0) -> int:
+    """P for a prefill / extend map from the q counts (host values)."""
+    q = np.ascontiguousarray(np.asarray(qlens, dtype=np.int32).ravel())
+    out = ctypes.c_int32()
+    _check("lbsa_varlen_auto_workgroups",
+           lib().lbsa_varlen_auto_workgroups(int(device), q.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                            int(q.size), int(num_kv_heads), ctypes.byref(out)))
     return out.value
 
 

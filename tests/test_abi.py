@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lbsa.lib().lbsa_version() == 208
+    assert lbsa.lib().lbsa_version() == 209
     assert lbsa.status_string(0) == "ok"
     assert "invalid" in lbsa.status_string(-1)
     assert "unsupported" in lbsa.status_string(-2)
@@ -272,3 +272,15 @@ def test_query_block_size_matches_the_header():
     import re
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "lbsa.h")).read()
     assert int(re.search(r"#define LBSA_QBLOCK (\d+)", hdr).group(1)) == lbsa.QBLOCK
+
+
+def test_varlen_auto_workgroups_argument_errors():
+    """Rejected on the host before any device query."""
+    L = lbsa.lib()
+    i32 = ctypes.c_int32
+    q = (i32 * 2)(8192, 1)
+    out = i32()
+    assert L.lbsa_varlen_auto_workgroups(0, None, 2, 8, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_varlen_auto_workgroups(0, q, 0, 8, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_varlen_auto_workgroups(0, q, 2, 0, ctypes.byref(out)) == lbsa.ERR_INVALID_ARGUMENT
+    assert L.lbsa_varlen_auto_workgroups(0, q, 2, 8, None) == lbsa.ERR_INVALID_ARGUMENT

@@ -267,3 +267,17 @@ def test_mixed_extend_full_size_sampled_parity(oracle_mod):
     ref, _ = oracle_mod.attention_varlen_rows(bc, rows)
     got = np.stack([out[t, hq] for t, hq in rows])
     H.check(b, got, ref, f"mixed extend: {len(pos)} extend positions + 63 decode rows, all heads")
+
+
+def test_varlen_auto_workgroups_rule():
+    """A quarter of the resident bins once the batch has 4 segments (KV heads x
+    query blocks) per resident workgroup, else one bin per resident workgroup."""
+    res = lbsa.varlen_default_workgroups(0)
+    qb = lbsa.QBLOCK
+    enough = -(-4 * res // 8) * qb                      # one request, 8 KV heads: 4 res segments
+    assert lbsa.varlen_auto_workgroups([enough], 8) == -(-res // 4)
+    assert lbsa.varlen_auto_workgroups([enough - qb], 8) == res
+    _, ql = wl.mixed_extend_lengths()
+    nq = sum(-(-q // qb) for q in ql)
+    assert lbsa.varlen_auto_workgroups(ql, 8) == (-(-res // 4) if 8 * nq >= 4 * res else res)
+    assert lbsa.varlen_auto_workgroups([0, -5, 1], 1) == res   # q out of range counts no block
