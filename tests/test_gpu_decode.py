@@ -254,3 +254,43 @@ def test_auto_workgroups_rule():
         assert lbsa.auto_workgroups([64 * 32] * (res // 8), 8, kv) == 2 * res      # exactly 32 tiles each
         assert lbsa.auto_workgroups([64 * 31] * (res // 8), 8, kv) == res          # 31 tiles each
         assert lbsa.auto_workgroups([], 8, kv) == res
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_combine_segment_forms(oracle_mod, q_len):
+    """The combine's two forms side by side: segments of 0, 1 and 2..8 chunks
+    (merged whole, one workgroup per segment; a single chunk written by the
+    split kernel) and of 9 and 11 (one workgroup per output row, from the map's
+    long-segment list); every row against the oracle, both query counts."""
+    sl = [4629, 3196, 4561, 120, 2544, 1590, 553, 3552, 5776, 1142, 255, 0]
+    batch = H.batch_on_gpu(dict(seqlens=sl, num_heads=16, num_kv_heads=2, kv_dtype="bf16", seed=61, q_len=q_len))
+    P = 96
+    tm = H.plan(batch, P, 1)
+    m = lbsa.read_task_map(tm, len(sl), 2, P)
+    snc = m["seg_num_chunks"]
+    assert {0, 1, 8, 9}.issubset(set(snc.tolist()))
+    assert m["nlong"] == int((snc > lbsa.LONG_SEGMENT_CHUNKS).sum()) > 0
+    out = H.decode(batch, tm, P)
+    check_full(oracle_mod, batch, out, ("combine segment forms", q_len))
+
+
+def test_combine_long_list_at_its_bound(oracle_mod):
+    """One request, 8 KV heads, 72 bins of 2 tiles: every head's segment has 9
+    chunks, so the long-segment list is full ((8 + 72) / 9 = 8 records)."""
+    batch = H.batch_on_gpu(dict(seqlens=[1152], num_heads=64, num_kv_heads=8, kv_dtype="bf16", seed=62))
+    P = 72
+    tm = H.plan(batch, P, 1)
+    m = lbsa.read_task_map(tm, 1, 8, P)
+    assert (m["seg_num_chunks"] == 9).all() and m["nlong"] == (8 + P) // 9 == 8
+    check_full(oracle_mod, batch, H.decode(batch, tm, P), "long list at its bound")
+
+
+def test_combine_row_of_hundreds_of_chunks(oracle_mod):
+    """One 100000-token request over 512 bins, 8 query heads on one KV head: each
+    output row merges 512 chunks, four rounds of the long form's loads."""
+    batch = H.batch_on_gpu(dict(seqlens=[100000], num_heads=8, num_kv_heads=1, kv_dtype="bf16", seed=63))
+    P = 512
+    tm = H.plan(batch, P, 1)
+    m = lbsa.read_task_map(tm, 1, 1, P)
+    assert int(m["seg_num_chunks"][0]) == 512 and m["nlong"] == 1
+    check_full(oracle_mod, batch, H.decode(batch, tm, P), "512-chunk rows")
