@@ -130,7 +130,22 @@ def make_flush(mode):
     return lambda i: None
 
 
-MIN_WARM_S = 0.25   # seconds of untimed steps before any timed pass of time_steps
+MIN_WARM_S = 0.25   # seconds of untimed steps before any timed pass
+
+
+def _warm(run_once, warmup, flush):
+    """At least `warmup` untimed runs and MIN_WARM_S of busy GPU (synchronised
+    one by one): after an idle stretch (the CPU leg, a batch built on the host)
+    the clocks take tens of ms of load to come back up, and a few short runs do
+    not cover that."""
+    import torch
+    t_end = time.perf_counter() + MIN_WARM_S
+    i = 0
+    while i < warmup or time.perf_counter() < t_end:
+        flush(i)
+        run_once()
+        torch.cuda.synchronize()
+        i += 1
 
 
 def _pairs(n):
@@ -150,16 +165,7 @@ def time_steps(path, steps, warmup, flush):
 
     from load_balanced_split_assign_amd import lbsa
     stream = torch.cuda.current_stream()
-    # at least `warmup` steps and MIN_WARM_S of busy GPU: after an idle stretch
-    # (the CPU leg, a batch built on the host) the clocks take tens of ms of
-    # load to come back up, and a few short steps do not cover that
-    t_end = time.perf_counter() + MIN_WARM_S
-    i = 0
-    while i < warmup or time.perf_counter() < t_end:
-        flush(i)
-        path.assign(); path.layer()
-        torch.cuda.synchronize()
-        i += 1
+    _warm(lambda: (path.assign(), path.layer()), warmup, flush)
     whole = _pairs(steps)
     for i in range(steps):
         flush(i)
@@ -203,10 +209,7 @@ def time_steps_graph(path, steps, warmup, flush):
     with torch.cuda.graph(g):
         path.assign(); path.layer()
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        flush(i)
-        g.replay()
-    torch.cuda.synchronize()
+    _warm(g.replay, warmup, flush)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         flush(i)
@@ -252,10 +255,7 @@ def time_static(batch, S, steps, warmup, flush, stamps=False):
                            S, batch["softmax_scale"], q_scale=batch["q_scale"], k_scale=batch["k_scale"],
                            v_scale=batch["v_scale"], workspace=ws, out=out)
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        flush(i)
-        run()
-    torch.cuda.synchronize()
+    _warm(run, warmup, flush)
     ev = _pairs(steps)
     for i in range(steps):
         flush(i)
@@ -292,10 +292,7 @@ def time_layer(path, steps, warmup, flush, with_assign=False):
             path.assign()
         path.layer()
     path.assign()            # the map the layers reuse
-    for i in range(warmup):
-        flush(i)
-        run()
-    torch.cuda.synchronize()
+    _warm(run, warmup, flush)
     ev = _pairs(steps)
     for i in range(steps):
         flush(i)
@@ -376,8 +373,11 @@ def mtp_bench(args):
             row[f"q{ql}_P"] = P
             sl = [int(x) for x in b["seqlens"].cpu()]
             ab = alg_bytes(sl, b["num_heads"], b["num_kv_heads"], 128, w.kv_dtype, q_len=ql)
-            t = time_layer(Path(b, P), args.steps, args.warmup, flush)["mean"]
+            tl = time_layer(Path(b, P), args.steps, args.warmup, flush)
+            t = tl["mean"]
             row[f"q{ql}_layer_us"] = round(t, 2)
+            row[f"q{ql}_layer_median_us"] = round(tl["median"], 2)
+            row[f"q{ql}_layer_p90_us"] = round(tl["p90"], 2)
             row[f"q{ql}_GBps"] = round(ab["layer"] / t / 1e3, 1)
             row["batch"] = b["B"]
             del b
@@ -461,10 +461,7 @@ def _timed(run, steps, warmup, flush):
     """Mean event time (us) of run() with one event pair per call, the flush outside."""
     import torch
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        flush(i)
-        run()
-    torch.cuda.synchronize()
+    _warm(run, warmup, flush)
     ev = _pairs(steps)
     for i in range(steps):
         flush(i)
@@ -484,12 +481,11 @@ def _timed_alternating(runs, steps, warmup, flush):
     stream = torch.cuda.current_stream()
     names = list(runs)
     k = 0
-    for _ in range(warmup):
+
+    def round_once():
         for n in names:
-            flush(k)
-            k += 1
             runs[n]()
-    torch.cuda.synchronize()
+    _warm(round_once, warmup, flush)
     ev = {n: _pairs(steps) for n in names}
     for i in range(steps):
         for n in names:
